@@ -1,0 +1,145 @@
+"""CPU oracle of the SDM hot path -- TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg
+of ``bench.py`` may import this package. The product path never does.
+
+Thin numpy/ctypes wrapper over ``liboracle_sdm.so`` (plain C, see
+``oracle_sdm.c``). Inputs are converted to contiguous fp32 / int32 host arrays
+(bf16 tensors are widened exactly); outputs are fresh numpy arrays.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional, Tuple
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "liboracle_sdm.so")
+SRC = os.path.join(HERE, "oracle_sdm.c")
+
+EQ4 = 0
+FIG2 = 1
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile liboracle_sdm.so with gcc (no fast-math, no FMA contraction)."""
+    if force or not os.path.exists(LIB_PATH):
+        tmp = LIB_PATH + ".tmp"
+        cmd = ["gcc", "-O2", "-std=c11", "-Wall", "-ffp-contract=off", "-fno-fast-math",
+               "-fPIC", "-shared", "-pthread", SRC, "-o", tmp, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            build()
+        lib = ctypes.CDLL(LIB_PATH)
+        P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        lib.oracle_half_scores.argtypes = [P, P, I64, I64, I64, I64, I64, P, I]
+        lib.oracle_select.argtypes = [P, I64, I64, I64, I64, I64, P, P, P, P, I]
+        lib.oracle_scan.argtypes = [P, P, I64, P, P, I64, P, P, P, P, P,
+                                    I64, I64, I64, I64, I64, I, I]
+        for f in (lib.oracle_half_scores, lib.oracle_select, lib.oracle_scan):
+            f.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _f32(x) -> np.ndarray:
+    try:
+        import torch
+        if isinstance(x, torch.Tensor):
+            x = x.detach().to("cpu", torch.float32).numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    return np.ascontiguousarray(x, dtype=np.float32)
+
+
+def _i32(x) -> np.ndarray:
+    try:
+        import torch
+        if isinstance(x, torch.Tensor):
+            x = x.detach().to("cpu", torch.int32).numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    return np.ascontiguousarray(x, dtype=np.int32)
+
+
+def _p(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _check(rc: int, what: str):
+    if rc != 0:
+        raise ValueError(f"oracle {what} rejected its arguments (code {rc})")
+
+
+def default_threads() -> int:
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def half_scores(q, subkeys, nthreads: Optional[int] = None) -> np.ndarray:
+    """A1: q [B,H,T,2,dh], subkeys [H,2,n,dh] -> half-scores [B,H,T,2,n] fp32."""
+    q = _f32(q); K = _f32(subkeys)
+    B, H, T, two, dh = q.shape
+    assert two == 2 and K.shape[0] == H and K.shape[1] == 2 and K.shape[3] == dh
+    n = K.shape[2]
+    out = np.empty((B, H, T, 2, n), np.float32)
+    _check(_load().oracle_half_scores(_p(q), _p(K), B, H, T, n, dh, _p(out),
+                                      nthreads or default_threads()), "half_scores")
+    return out
+
+
+def select(half, k: int, nthreads: Optional[int] = None
+           ) -> Tuple[np.ndarray, np.ndarray, np.ndarray, np.ndarray]:
+    """A2-A4 on half-scores [B,H,T,2,n]: returns (idx, wt, score, score_next)."""
+    half = _f32(half)
+    B, H, T, two, n = half.shape
+    assert two == 2
+    idx = np.empty((B, H, T, k), np.int32)
+    wt = np.empty((B, H, T, k), np.float32)
+    sc = np.empty((B, H, T, k), np.float32)
+    nxt = np.empty((B, H, T), np.float32)
+    _check(_load().oracle_select(_p(half), B, H, T, n, k, _p(idx), _p(wt), _p(sc), _p(nxt),
+                                 nthreads or default_threads()), "select")
+    return idx, wt, sc, nxt
+
+
+def address(q, subkeys, k: int, nthreads: Optional[int] = None):
+    """A1-A4: product-key addressing of one branch. Returns (idx, wt, score, score_next)."""
+    return select(half_scores(q, subkeys, nthreads), k, nthreads)
+
+
+def scan(idx_w, wt_w, idx_r, wt_r, alpha, beta, v, M_in, form: int = EQ4,
+         nthreads: Optional[int] = None) -> Tuple[np.ndarray, np.ndarray]:
+    """A5-A6 over all tokens. M_in [B,H,N,dv] is not modified.
+
+    Returns (M_out [B,H,N,dv], y [B,H,T,dv]).
+    """
+    iw = _i32(idx_w); ww = _f32(wt_w); ir = _i32(idx_r); wr = _f32(wt_r)
+    a = _f32(alpha); b = _f32(beta); vv = _f32(v)
+    M = np.array(_f32(M_in), dtype=np.float32, copy=True, order="C")
+    B, H, T, W = iw.shape
+    R = ir.shape[3]
+    N, dv = M.shape[2], M.shape[3]
+    assert M.shape[:2] == (B, H) and vv.shape == (B, H, T, dv)
+    y = np.empty((B, H, T, dv), np.float32)
+    _check(_load().oracle_scan(_p(iw), _p(ww), W, _p(ir), _p(wr), R, _p(a), _p(b), _p(vv),
+                               _p(M), _p(y), B, H, T, N, dv, form,
+                               nthreads or default_threads()), "scan")
+    return M, y
+
+
+def broadcast_state(M0, B: int) -> np.ndarray:
+    """The per-sequence initial state: M0 [H,N,dv] copied for each of B sequences."""
+    M0 = _f32(M0)
+    return np.ascontiguousarray(np.broadcast_to(M0[None], (B,) + M0.shape))

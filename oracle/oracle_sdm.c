@@ -1,0 +1,278 @@
+/*
+ * oracle_sdm.c -- plain, slow CPU reference of the SDM hot path.
+ *
+ * TEST INFRASTRUCTURE ONLY (see oracle_sdm.h). Written from the pages:
+ *   [SDM]   "Sparse Delta Memory：中文精读笔记"
+ *   [FwPKM] "Fast-weight Product Key Memory：中文精读笔记"
+ *
+ * Readings where the pages leave a step open (each is pinned by a test):
+ *   - slot (a, b) of the outer sum is row a*n + b, a from half 0;
+ *   - when k > n each half keeps all n sub-scores (k_h = min(k, n));
+ *   - ties are broken by the lower index: per half by sub-index, in the final
+ *     selection by slot index;
+ *   - half-scores are rounded to fp32 and a slot score is one fp32 add;
+ *   - the weights are a plain softmax over the selected fp32 slot scores;
+ *   - within one token all write rows are updated first, then the read sees
+ *     the updated table (read-after-write).
+ *
+ * Build: gcc -O2 -std=c11 -ffp-contract=off -fPIC -shared -pthread
+ * (no fast-math, no FMA contraction: every double operation is rounded as
+ * written).
+ */
+#include "oracle_sdm.h"
+
+#include <math.h>
+#include <pthread.h>
+#include <stdlib.h>
+#include <string.h>
+
+int oracle_version(void) { return 1; }
+
+/* ------------------------------------------------------------------ */
+/* a tiny "run f(i) for i in [0, count) on nthreads threads" helper.   */
+/* Work items are independent, so results never depend on nthreads.   */
+/* ------------------------------------------------------------------ */
+typedef void (*item_fn)(void* ctx, int64_t item);
+typedef struct {
+    item_fn fn;
+    void* ctx;
+    int64_t count;
+    int tid, nthreads;
+} par_arg;
+
+static void* par_body(void* p) {
+    par_arg* a = (par_arg*)p;
+    for (int64_t i = a->tid; i < a->count; i += a->nthreads) a->fn(a->ctx, i);
+    return NULL;
+}
+
+static void parallel_for(item_fn fn, void* ctx, int64_t count, int nthreads) {
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > 256) nthreads = 256;
+    if (nthreads == 1 || count <= 1) {
+        for (int64_t i = 0; i < count; ++i) fn(ctx, i);
+        return;
+    }
+    pthread_t th[256];
+    par_arg args[256];
+    for (int t = 0; t < nthreads; ++t) {
+        args[t].fn = fn; args[t].ctx = ctx; args[t].count = count;
+        args[t].tid = t; args[t].nthreads = nthreads;
+        pthread_create(&th[t], NULL, par_body, &args[t]);
+    }
+    for (int t = 0; t < nthreads; ++t) pthread_join(th[t], NULL);
+}
+
+/* ------------------------------------------------------------------ */
+/* A1 -- half-scores [SDM §2.3; FwPKM §2.2]: each half-query is scored  */
+/* against the n subkeys of its half by a dot product.                 */
+/* ------------------------------------------------------------------ */
+typedef struct {
+    const float *q, *K;
+    int64_t H, T, n, dh;
+    float* out;
+} hs_ctx;
+
+static void hs_item(void* p, int64_t bht) {
+    hs_ctx* c = (hs_ctx*)p;
+    int64_t h = (bht / c->T) % c->H;
+    for (int j = 0; j < 2; ++j) {
+        const float* qj = c->q + (bht * 2 + j) * c->dh;
+        for (int64_t a = 0; a < c->n; ++a) {
+            const float* ka = c->K + ((h * 2 + j) * c->n + a) * c->dh;
+            double acc = 0.0;
+            for (int64_t i = 0; i < c->dh; ++i) acc += (double)qj[i] * (double)ka[i];
+            c->out[(bht * 2 + j) * c->n + a] = (float)acc;
+        }
+    }
+}
+
+int oracle_half_scores(const float* q, const float* subkeys, int64_t B, int64_t H,
+                       int64_t T, int64_t n, int64_t dh, float* out, int nthreads) {
+    if (!q || !subkeys || !out) return -1;
+    if (B < 0 || H < 0 || T < 0 || n < 1 || dh < 1) return -2;
+    hs_ctx c = {q, subkeys, H, T, n, dh, out};
+    parallel_for(hs_item, &c, B * H * T, nthreads);
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* A2-A4 -- product-key selection [SDM §2.3; FwPKM §2.2].              */
+/* ------------------------------------------------------------------ */
+typedef struct {
+    float s;
+    int64_t id;
+} scored;
+
+/* order: higher score first; equal scores -> lower index first */
+static int by_score_then_index(const void* x, const void* y) {
+    const scored* a = (const scored*)x;
+    const scored* b = (const scored*)y;
+    if (a->s > b->s) return -1;
+    if (a->s < b->s) return 1;
+    return (a->id > b->id) - (a->id < b->id);
+}
+
+/* Top-k slots of one token-branch by product keys. h0, h1: the n half-scores
+ * of half 0 and half 1. Writes kk slots (kk <= n*n) with their fp32 scores,
+ * ordered by (score desc, slot asc). */
+static void pkm_topk(const float* h0, const float* h1, int64_t n, int64_t kk,
+                     int64_t* slot_out, float* score_out) {
+    int64_t kh = kk < n ? kk : n;             /* per-half keep count */
+    scored* best0 = (scored*)malloc((size_t)n * sizeof(scored));
+    scored* best1 = (scored*)malloc((size_t)n * sizeof(scored));
+    scored* cand = (scored*)malloc((size_t)(kh * kh) * sizeof(scored));
+    /* A2: per-half top-kh, each half ordered by (score desc, sub-index asc) */
+    for (int64_t a = 0; a < n; ++a) { best0[a].s = h0[a]; best0[a].id = a; }
+    for (int64_t b = 0; b < n; ++b) { best1[b].s = h1[b]; best1[b].id = b; }
+    qsort(best0, (size_t)n, sizeof(scored), by_score_then_index);
+    qsort(best1, (size_t)n, sizeof(scored), by_score_then_index);
+    /* A3: all kh*kh outer sums; slot score = one fp32 add; slot = a*n + b */
+    int64_t m = 0;
+    for (int64_t i = 0; i < kh; ++i)
+        for (int64_t j = 0; j < kh; ++j) {
+            float s = best0[i].s + best1[j].s;
+            cand[m].s = s;
+            cand[m].id = best0[i].id * n + best1[j].id;
+            ++m;
+        }
+    qsort(cand, (size_t)m, sizeof(scored), by_score_then_index);
+    for (int64_t i = 0; i < kk; ++i) { slot_out[i] = cand[i].id; score_out[i] = cand[i].s; }
+    free(cand); free(best1); free(best0);
+}
+
+typedef struct {
+    const float* half;
+    int64_t n, k;
+    int32_t* idx;
+    float *wt, *score, *score_next;
+} sel_ctx;
+
+static void sel_item(void* p, int64_t bht) {
+    sel_ctx* c = (sel_ctx*)p;
+    int64_t n = c->n, k = c->k, N = n * n;
+    const float* h0 = c->half + bht * 2 * n;
+    const float* h1 = h0 + n;
+    int64_t kn = k < N ? k + 1 : k;
+    int64_t* slots = (int64_t*)malloc((size_t)kn * sizeof(int64_t));
+    float* sc = (float*)malloc((size_t)kn * sizeof(float));
+
+    pkm_topk(h0, h1, n, k, slots, sc);
+    /* A4: softmax over the k selected fp32 scores, max-subtracted, in double */
+    double mx = (double)sc[0], sum = 0.0;
+    double* e = (double*)malloc((size_t)k * sizeof(double));
+    for (int64_t i = 0; i < k; ++i) { e[i] = exp((double)sc[i] - mx); sum += e[i]; }
+    for (int64_t i = 0; i < k; ++i) {
+        c->idx[bht * k + i] = (int32_t)slots[i];
+        c->wt[bht * k + i] = (float)(e[i] / sum);
+        if (c->score) c->score[bht * k + i] = sc[i];
+    }
+    if (c->score_next) {
+        if (k < N) {
+            /* the (k+1)-th slot score may lie outside the k x k grid: rerun with k+1 */
+            pkm_topk(h0, h1, n, k + 1, slots, sc);
+            c->score_next[bht] = sc[k];
+        } else {
+            c->score_next[bht] = -INFINITY;
+        }
+    }
+    free(e); free(sc); free(slots);
+}
+
+int oracle_select(const float* half, int64_t B, int64_t H, int64_t T, int64_t n,
+                  int64_t k, int32_t* idx, float* wt, float* score, float* score_next,
+                  int nthreads) {
+    if (!half || !idx || !wt) return -1;
+    if (B < 0 || H < 0 || T < 0 || n < 1 || k < 1 || k > n * n) return -2;
+    sel_ctx c = {half, n, k, idx, wt, score, score_next};
+    parallel_for(sel_item, &c, B * H * T, nthreads);
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* A5-A6 -- sparse gated delta write, then sparse read                 */
+/* [SDM §2.4 Eq. (3)-(5); §2.5 Fig. 2 form].                           */
+/* ------------------------------------------------------------------ */
+typedef struct {
+    const int32_t* idx_w; const float* wt_w; int64_t W;
+    const int32_t* idx_r; const float* wt_r; int64_t R;
+    const float *alpha, *beta, *v;
+    float *M, *y;
+    int64_t T, N, dv;
+    int form;
+} scan_ctx;
+
+static void scan_item(void* p, int64_t s) {      /* s = b*H + h: one sequence-head */
+    scan_ctx* c = (scan_ctx*)p;
+    int64_t W = c->W, R = c->R, dv = c->dv;
+    float* Ms = c->M + s * c->N * dv;
+    double* vhat = (double*)malloc((size_t)dv * sizeof(double));
+    for (int64_t t = 0; t < c->T; ++t) {
+        int64_t st = s * c->T + t;
+        const int32_t* iw = c->idx_w + st * W;
+        const float* ww = c->wt_w + st * W;
+        const int32_t* ir = c->idx_r + st * R;
+        const float* wr = c->wt_r + st * R;
+        const float* vt = c->v + st * dv;
+        double a = (double)c->alpha[st], b = (double)c->beta[st];
+
+        if (c->form == ORACLE_FIG2) {
+            /* shared prediction from the decayed pre-token rows:
+               vhat = sum_j k^(j) * alpha * M[j] */
+            for (int64_t col = 0; col < dv; ++col) vhat[col] = 0.0;
+            for (int64_t j = 0; j < W; ++j) {
+                const float* row = Ms + (int64_t)iw[j] * dv;
+                for (int64_t col = 0; col < dv; ++col)
+                    vhat[col] += (double)ww[j] * (a * (double)row[col]);
+            }
+        }
+        /* Eq. (3): decay the selected rows; Eq. (4) or Fig. 2: delta-correct them.
+           Unselected rows are not touched at all. */
+        for (int64_t j = 0; j < W; ++j) {
+            float* row = Ms + (int64_t)iw[j] * dv;
+            double kw = (double)ww[j];
+            for (int64_t col = 0; col < dv; ++col) {
+                double mt = a * (double)row[col];
+                double pred = (c->form == ORACLE_FIG2) ? vhat[col] : mt;
+                row[col] = (float)(mt + b * kw * ((double)vt[col] - pred));
+            }
+        }
+        /* Eq. (5): weighted read of the R selected rows of the updated table */
+        float* yt = c->y + st * dv;
+        for (int64_t col = 0; col < dv; ++col) {
+            double acc = 0.0;
+            for (int64_t j = 0; j < R; ++j)
+                acc += (double)wr[j] * (double)Ms[(int64_t)ir[j] * dv + col];
+            yt[col] = (float)acc;
+        }
+    }
+    free(vhat);
+}
+
+int oracle_scan(const int32_t* idx_w, const float* wt_w, int64_t W,
+                const int32_t* idx_r, const float* wt_r, int64_t R,
+                const float* alpha, const float* beta, const float* v,
+                float* M, float* y, int64_t B, int64_t H, int64_t T, int64_t N,
+                int64_t dv, int form, int nthreads) {
+    if (!idx_w || !wt_w || !idx_r || !wt_r || !alpha || !beta || !v || !M || !y) return -1;
+    if (B < 0 || H < 0 || T < 0 || N < 1 || dv < 1 || W < 1 || R < 1 || W > N || R > N) return -2;
+    if (form != ORACLE_EQ4 && form != ORACLE_FIG2) return -2;
+    /* preconditions: indices in range, write indices of one token distinct */
+    int64_t ntok = B * H * T;
+    unsigned char* seen = (unsigned char*)calloc((size_t)N, 1);
+    for (int64_t st = 0; st < ntok; ++st) {
+        for (int64_t j = 0; j < R; ++j)
+            if (idx_r[st * R + j] < 0 || idx_r[st * R + j] >= N) { free(seen); return -3; }
+        for (int64_t j = 0; j < W; ++j) {
+            int32_t i = idx_w[st * W + j];
+            if (i < 0 || i >= N) { free(seen); return -3; }
+            if (seen[i]) { free(seen); return -4; }
+            seen[i] = 1;
+        }
+        for (int64_t j = 0; j < W; ++j) seen[idx_w[st * W + j]] = 0;
+    }
+    free(seen);
+    scan_ctx c = {idx_w, wt_w, W, idx_r, wt_r, R, alpha, beta, v, M, y, T, N, dv, form};
+    parallel_for(scan_item, &c, B * H, nthreads);
+    return 0;
+}

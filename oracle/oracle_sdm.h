@@ -1,0 +1,65 @@
+/*
+ * oracle_sdm.h -- plain, slow CPU reference of the SDM hot path.
+ *
+ * TEST INFRASTRUCTURE ONLY. Only the test suite, the smoke check and the CPU
+ * baseline leg of the benchmark may load this library. The product path
+ * (libsdm.so and its Python binding) never calls it, and the two share no
+ * code, headers, helpers or tables.
+ *
+ * Sources (page titles; sections as printed on the pages):
+ *   [SDM]   "Sparse Delta Memory：中文精读笔记" (close-reading notes on
+ *           arXiv 2607.07386v1): §2.2 notation, §2.3 product-key addressing,
+ *           §2.4 Eq. (3)-(5) write / read, §2.5 Fig. 2 shared-residual form
+ *           and the worked counter-example, §2.1 Eq. (2) gated delta rule.
+ *   [FwPKM] "Fast-weight Product Key Memory：中文精读笔记", §2.2
+ *           (per-half top-k, k^2 candidates, softmax over the selection).
+ *
+ * Conventions: all arrays are host memory, row-major and contiguous, fp32 for
+ * every floating-point tensor (bf16 inputs are widened exactly by the
+ * caller). Accumulations run in double; every stored value is rounded once to
+ * fp32. Functions return 0 on success and a negative code on invalid
+ * arguments (nothing is written then).
+ *
+ * Every function has a pin in tests/test_oracle_pins.py; none is unpinned.
+ */
+#ifndef ORACLE_SDM_H
+#define ORACLE_SDM_H
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ORACLE_EQ4 0   /* per-slot residual, Eq. (4) as printed   */
+#define ORACLE_FIG2 1  /* shared residual read off Fig. 2         */
+
+/* A1: half-scores. q [B,H,T,2,dh], subkeys [H,2,n,dh] -> out [B,H,T,2,n].
+ * out[..,j,a] = fp32( sum_c q[..,j,c] * K[h,j,a,c] ), summed in double in c order. */
+int oracle_half_scores(const float* q, const float* subkeys, int64_t B, int64_t H,
+                       int64_t T, int64_t n, int64_t dh, float* out, int nthreads);
+
+/* A2-A4 from given half-scores half [B,H,T,2,n], for k selected slots.
+ * idx/wt/score [B,H,T,k]: slots ordered by (score desc, slot asc), softmax
+ * weights, fp32 slot scores. score_next [B,H,T] (may be NULL): the (k+1)-th
+ * slot score found by the same procedure with k+1, or -INFINITY when k == n*n. */
+int oracle_select(const float* half, int64_t B, int64_t H, int64_t T, int64_t n,
+                  int64_t k, int32_t* idx, float* wt, float* score, float* score_next,
+                  int nthreads);
+
+/* A5-A6: the sparse gated delta scan over tokens 0..T-1, in place on M.
+ * idx_w/wt_w [B,H,T,W], idx_r/wt_r [B,H,T,R], alpha/beta [B,H,T], v [B,H,T,dv],
+ * M [B,H,N,dv] (in: state before token 0, out: after token T-1), y [B,H,T,dv].
+ * form: ORACLE_EQ4 or ORACLE_FIG2. Returns -3 on an out-of-range index and
+ * -4 on a repeated write index within one token (checked before any write). */
+int oracle_scan(const int32_t* idx_w, const float* wt_w, int64_t W,
+                const int32_t* idx_r, const float* wt_r, int64_t R,
+                const float* alpha, const float* beta, const float* v,
+                float* M, float* y, int64_t B, int64_t H, int64_t T, int64_t N,
+                int64_t dv, int form, int nthreads);
+
+int oracle_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif
