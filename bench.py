@@ -1,0 +1,185 @@
+#!/usr/bin/env python3
+"""Benchmark of the SDM hot path on one MI355X.
+
+One step = one pass of the whole hot path over one batch of synthetic input:
+per-sequence table init from M0, product-key addressing of both branches, and
+the sparse gated delta scan (planner + scan kernels). Inputs are resident in
+HBM before the timed region; outputs are preallocated.
+
+Prints ONE JSON line: throughput (tokens/s = B*T per step), the scan's roofline
+entry (algorithmic slot-row bytes B*H*T*(2W+R)*d_v*4 per launch over the
+launch's average duration from HIP events) and the CPU oracle timed on a
+bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import subprocess
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "SDM scan tokens/s and slot-row HBM GB/s at N=65536,W=R=64,d_v=128"
+HBM_PEAK_GBPS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scan_traffic_gdn_matched.json")
+SCAN_SRC = os.path.join(ROOT, "sparse_memory_linear_amd", "csrc", "scan.hip")
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--workload", default="gdn_matched")
+    p.add_argument("--form", default="eq4", choices=["eq4", "fig2"])
+    p.add_argument("--cpu-seconds", type=float, default=15.0,
+                   help="target CPU time of the oracle baseline sample")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    return p.parse_args()
+
+
+def host_cpu() -> str:
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True).stdout
+        for line in out.splitlines():
+            if line.startswith("Model name"):
+                return line.split(":", 1)[1].strip()
+    except Exception:
+        pass
+    return platform.processor() or "unknown"
+
+
+def measured_traffic():
+    """HBM bytes per scan launch from the committed counter summary, if it was
+    taken on the current scan kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+        sha = hashlib.sha256(open(SCAN_SRC, "rb").read()).hexdigest()
+        if rec.get("scan_source_sha256") == sha:
+            return rec.get("traffic_bytes_per_launch")
+    except (OSError, ValueError):
+        pass
+    return None
+
+
+def cpu_baseline(wl, x, target_s: float):
+    """The oracle as it is (addressing of both branches + scan), on the first
+    T' tokens of sequence b=0 with all H heads; T' sized to ~target_s."""
+    import numpy as np
+    import oracle
+
+    nthreads = oracle.default_threads()
+
+    def run(Tp):
+        sl = lambda t: t[:1, :, :Tp].contiguous()
+        t0 = time.perf_counter()
+        iw, ww, _, _ = oracle.address(sl(x["q_w"]), x["subkeys"], wl.W, nthreads)
+        ir, wr, _, _ = oracle.address(sl(x["q_r"]), x["subkeys"], wl.R, nthreads)
+        oracle.scan(iw, ww, ir, wr, sl(x["alpha"]), sl(x["beta"]), sl(x["v"]),
+                    x["M0"][None].numpy(), oracle.EQ4, nthreads)
+        return time.perf_counter() - t0
+
+    Tc = min(wl.T, 32)
+    tc = run(Tc)
+    Tp = int(min(wl.T, max(Tc, Tc * target_s / max(tc, 1e-3))))
+    ts = run(Tp) if Tp > Tc else tc
+    return {"value": Tp / ts, "unit": "tokens/s", "cores": nthreads, "kind": "oracle",
+            "sample": f"sequence b=0 of {wl.name}, all {wl.H} heads, first {Tp} of {wl.T} tokens "
+                      f"(addressing of both branches + {'EQ4'} scan), {ts:.1f} s wall",
+            "host_cpu": host_cpu()}
+
+
+def main():
+    a = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if a.gpus > 1 or world > 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(the per-(sequence, head) streams would shard with no exchange; "
+              "see the design notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import sparse_memory_linear_amd as sdm
+    from sparse_memory_linear_amd import inputs
+
+    dev = torch.device("cuda:0")
+    wl = inputs.get(a.workload)
+    x = inputs.make_inputs(wl)
+    g = {k: v.to(dev) for k, v in x.items()}
+    B, H, T, N, dv, W, R = wl.B, wl.H, wl.T, wl.N, wl.d_v, wl.W, wl.R
+    addr_out = (torch.empty((B, H, T, W), dtype=torch.int32, device=dev),
+                torch.empty((B, H, T, W), dtype=torch.float32, device=dev),
+                torch.empty((B, H, T, R), dtype=torch.int32, device=dev),
+                torch.empty((B, H, T, R), dtype=torch.float32, device=dev))
+    M = torch.empty((B, H, N, dv), dtype=torch.float32, device=dev)
+    y = torch.empty((B, H, T, dv), dtype=torch.float32, device=dev)
+    ws = torch.empty((sdm.sdm_scan_workspace_bytes(B, H, T, W, R, dv),), dtype=torch.uint8, device=dev)
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    def step(marks=None):
+        if marks:
+            marks[0].record()
+        sdm.sdm_state_init(g["M0"], B, out=M)
+        if marks:
+            marks[1].record()
+        iw, ww, ir, wr = sdm.sdm_address(g["q_w"], g["q_r"], g["subkeys"], g["subkeys"], W, R, out=addr_out)
+        if marks:
+            marks[2].record()
+        sdm.sdm_scan_forward(iw, ww, ir, wr, g["alpha"], g["beta"], g["v"], M, a.form, y=y, workspace=ws)
+        if marks:
+            marks[3].record()
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    marks = [[ev() for _ in range(4)] for _ in range(a.steps)]
+    t0 = time.perf_counter()
+    for i in range(a.steps):
+        step(marks[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = 1e3 * wall / a.steps
+    init_ms = sum(m[0].elapsed_time(m[1]) for m in marks) / a.steps
+    addr_ms = sum(m[1].elapsed_time(m[2]) for m in marks) / a.steps
+    scan_ms = sum(m[2].elapsed_time(m[3]) for m in marks) / a.steps
+
+    row_bytes = B * H * T * (2 * W + R) * dv * 4
+    scan_gbps = row_bytes / (scan_ms * 1e-3) / 1e9
+    rec = {
+        "metric": METRIC,
+        "value": B * T / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "B": B, "H": H, "T": T, "N": N, "W": W, "R": R,
+                   "d_v": dv, "d_h": wl.d_h, "form": a.form,
+                   "inputs": "bf16 q/v/subkeys, fp32 table/gates" if wl.bf16_inputs else "fp32"},
+        "breakdown_ms": {"state_init": init_ms, "address": addr_ms, "scan": scan_ms},
+        "scan_tokens_per_s": B * T / (scan_ms * 1e-3),
+        "slot_row_GBps": scan_gbps,
+        "roofline": {"bound": "hbm", "achieved": scan_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": scan_gbps / HBM_PEAK_GBPS, "traffic": measured_traffic(),
+                     "kernel": "sdm_scan_forward (planner + scan kernels)",
+                     "algorithmic_bytes_per_launch": row_bytes},
+    }
+    if not a.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(wl, x, a.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

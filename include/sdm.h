@@ -1,0 +1,154 @@
+/*
+ * sdm.h -- C ABI of the Sparse Delta Memory (SDM) hot path on MI355X (gfx950).
+ *
+ * The operations follow "Sparse Delta Memory：中文精读笔记" (close-reading notes
+ * on arXiv 2607.07386v1), cited below as [SDM], and the product-key
+ * addressing of "Fast-weight Product Key Memory：中文精读笔记" §2.2, cited as
+ * [FwPKM].
+ *
+ * Common conventions
+ *   - Every tensor pointer is a DEVICE pointer owned by the caller. Tensors are
+ *     row-major and contiguous; shapes are given in the comments. Sizes are
+ *     int64_t. The library never frees or retains caller memory.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream). All
+ *     compute calls are asynchronous and ordered on that stream; results are
+ *     visible after the caller synchronises it.
+ *   - Every call validates its arguments on the host before any launch. On
+ *     failure it returns a non-zero sdm_status, writes nothing and launches
+ *     nothing; sdm_last_error() then describes the failure (thread-local).
+ *     A failed launch returns SDM_ERR_HIP. Faults inside a kernel surface at
+ *     the caller's next synchronisation. No C++ exception crosses the ABI.
+ *   - Pointers to device tensors must be 16-byte aligned (SDM_ERR_ALIGN).
+ *   - Empty work (B, H or T equal to 0) is valid and launches nothing.
+ */
+#ifndef SDM_H
+#define SDM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SDM_ABI_VERSION 1
+
+typedef enum sdm_status {
+    SDM_OK = 0,
+    SDM_ERR_NULL = 1,         /* a required pointer is NULL                      */
+    SDM_ERR_SHAPE = 2,        /* a size is negative or sizes are inconsistent    */
+    SDM_ERR_DTYPE = 3,        /* unknown dtype or delta form                     */
+    SDM_ERR_ALIGN = 4,        /* a device pointer is not 16-byte aligned         */
+    SDM_ERR_UNSUPPORTED = 5,  /* valid but outside the sizes the kernels cover   */
+    SDM_ERR_HIP = 6,          /* a HIP launch failed                             */
+    SDM_ERR_WORKSPACE = 7     /* workspace missing or too small                  */
+} sdm_status;
+
+typedef enum sdm_dtype { SDM_F32 = 0, SDM_BF16 = 1 } sdm_dtype;
+
+/* The two write rules the notes keep side by side ([SDM] §2.4-§2.5):
+ *   SDM_DELTA_EQ4:  M[i] <- a M[i] + b w_i (v - a M[i])         (Eq. (4), per slot)
+ *   SDM_DELTA_FIG2: vhat = sum_j w_j a M[j];  M[i] <- a M[i] + b w_i (v - vhat)
+ *                   (shared residual read off Fig. 2; equals the gated delta
+ *                   rule Eq. (2) when every slot is selected).            */
+typedef enum sdm_delta_form { SDM_DELTA_EQ4 = 0, SDM_DELTA_FIG2 = 1 } sdm_delta_form;
+
+/* SDM_ABI_VERSION of the loaded library. */
+int sdm_abi_version(void);
+
+/* Static text for a status code. */
+const char* sdm_status_string(int status);
+
+/* Detail of the last failing call on the calling thread ("" if none). */
+const char* sdm_last_error(void);
+
+/*
+ * sdm_address -- product-key addressing of both branches ([SDM] §2.3, §2.2
+ * notation; [FwPKM] §2.2).
+ *
+ * For each (b, h, t) and each branch (write with k = W, read with k = R):
+ *   half-scores  s_j[a] = <q[.., j, :], subkeys[h, j, a, :]>, j in {0, 1}, a < n_sub
+ *                (MFMA contraction, fp32 accumulation);
+ *   per half     keep the k_h = min(k, n_sub) best, ordered (score desc, index asc);
+ *   combine      slot (a, b) -> row a*n_sub + b with score fp32(s_0[a] + s_1[b]);
+ *                the k best candidate slots, ordered (score desc, slot asc);
+ *   weights      softmax over the k selected slot scores.
+ *
+ *   q_w, q_r             [B, H, T, 2, dh]   q_dtype (half 0 then half 1)
+ *   subkeys_w, subkeys_r [H, 2, n_sub, dh]  k_dtype == q_dtype (may alias)
+ *   idx_w, wt_w          [B, H, T, W]       int32 slots, fp32 weights (out)
+ *   idx_r, wt_r          [B, H, T, R]       (out)
+ *   score_w, score_r     [B, H, T, W|R]     optional (NULL): fp32 slot scores
+ *
+ * Supported: q_dtype in {SDM_F32, SDM_BF16}; n_sub a multiple of 16 up to 512;
+ * dh a multiple of 8 (fp32) or 32 (bf16) up to 256; 1 <= W, R <= min(64, n_sub^2).
+ */
+int sdm_address(const void* q_w, const void* q_r, int q_dtype,
+                const void* subkeys_w, const void* subkeys_r, int k_dtype,
+                int64_t B, int64_t H, int64_t T, int64_t n_sub, int64_t dh,
+                int64_t W, int64_t R,
+                int32_t* idx_w, float* wt_w, int32_t* idx_r, float* wt_r,
+                float* score_w, float* score_r, void* stream);
+
+/*
+ * sdm_debug_half_scores -- test hook: only the half-score contraction of
+ * sdm_address (same kernel code), for one branch.
+ *   q [B, H, T, 2, dh], subkeys [H, 2, n_sub, dh], half [B, H, T, 2, n_sub] fp32 (out).
+ * Same support as sdm_address.
+ */
+int sdm_debug_half_scores(const void* q, int q_dtype, const void* subkeys, int k_dtype,
+                          int64_t B, int64_t H, int64_t T, int64_t n_sub, int64_t dh,
+                          float* half, void* stream);
+
+/*
+ * sdm_state_init -- per-sequence initial table from the (learned) initial
+ * state M0 ([SDM] §2.6): M[b] = M0 for every b.
+ *   M0 [H, N, dv] fp32, M [B, H, N, dv] fp32 (out). dv must be a multiple of 4.
+ */
+int sdm_state_init(const float* M0, float* M, int64_t B, int64_t H, int64_t N,
+                   int64_t dv, void* stream);
+
+/*
+ * sdm_scan_workspace_bytes -- device workspace sdm_scan_forward needs for these
+ * sizes (0 when there is no work, -1 when the sizes are invalid).
+ */
+int64_t sdm_scan_workspace_bytes(int64_t B, int64_t H, int64_t T, int64_t W, int64_t R,
+                                 int64_t dv);
+
+/*
+ * sdm_scan_forward -- the sparse gated delta recurrence with its sparse read,
+ * sequential in t for each (b, h) ([SDM] §2.4 Eq. (3)-(5), §2.5 Fig. 2):
+ *   for t = 0 .. T-1:
+ *     for i in idx_w[b,h,t,:]:  Mt = alpha[b,h,t] * M[b,h,i,:]              (Eq. 3)
+ *                               M[b,h,i,:] = Mt + beta * wt_w_i * (v - P_i)
+ *                               P_i = Mt (EQ4)  or  sum_j wt_w_j * alpha * M[b,h,j,:] (FIG2)
+ *     y[b,h,t,:] = sum_i wt_r_i * M[b,h,idx_r_i,:]   (after this token's writes, Eq. 5)
+ *   Rows that no token selects for writing are never touched (bit-identical).
+ *
+ *   idx_w, wt_w  [B, H, T, W]   int32 / fp32     idx_r, wt_r [B, H, T, R]
+ *   alpha, beta  [B, H, T]      fp32 gates
+ *   v            [B, H, T, dv]  v_dtype (SDM_F32 or SDM_BF16)
+ *   M            [B, H, N, dv]  fp32, in: state before token 0, out: after token T-1
+ *   y            [B, H, T, dv]  fp32 (out)
+ *   workspace    device buffer of >= sdm_scan_workspace_bytes(B,H,T,W,R,dv) bytes,
+ *                16-byte aligned; its contents on entry do not matter.
+ *
+ * The state is in/out, so a sequence split over several calls gives the same
+ * result as one call. Preconditions: indices in [0, N) and the W write indices
+ * of one token distinct (sdm_address guarantees both). Entries that break the
+ * first are skipped (memory-safe, result unspecified); the second gives an
+ * unspecified result. Weights are used as given.
+ * Supported: 1 <= W, R <= 256, N <= 2^18, dv a multiple of 4.
+ */
+int sdm_scan_forward(const int32_t* idx_w, const float* wt_w, int64_t W,
+                     const int32_t* idx_r, const float* wt_r, int64_t R,
+                     const float* alpha, const float* beta,
+                     const void* v, int v_dtype,
+                     float* M, float* y,
+                     int64_t B, int64_t H, int64_t T, int64_t N, int64_t dv,
+                     int form, void* workspace, int64_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SDM_H */

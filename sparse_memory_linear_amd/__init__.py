@@ -1,0 +1,9 @@
+"""SDM (Sparse Delta Memory) hot path on MI355X: product-key addressing and the
+sparse gated delta scan as hand-written HIP kernels behind a C ABI
+(include/sdm.h). This package holds the Python binding (``binding``), the
+in-tree build (``build``) and the seeded synthetic inputs (``inputs``)."""
+from . import inputs  # noqa: F401
+from .binding import (SDM_BF16, SDM_DELTA_EQ4, SDM_DELTA_FIG2, SDM_F32,  # noqa: F401
+                      SdmError, sdm_abi_version, sdm_address, sdm_debug_half_scores,
+                      sdm_last_error, sdm_scan_forward, sdm_scan_workspace_bytes,
+                      sdm_state_init, sdm_status_string)

@@ -1,0 +1,213 @@
+"""Thin Python binding of libsdm.so (include/sdm.h), same names as the C ABI.
+
+Argument marshalling only: tensors are checked (device, dtype, shape,
+contiguity), outputs are allocated with torch on the tensors' device, and the
+raw device pointers plus the current torch stream are handed to the C ABI.
+Every step of the hot path runs in the library's HIP kernels; there is no
+fallback. If the library is missing, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsdm.so")
+
+SDM_F32, SDM_BF16 = 0, 1
+SDM_DELTA_EQ4, SDM_DELTA_FIG2 = 0, 1
+FORMS = {"eq4": SDM_DELTA_EQ4, "fig2": SDM_DELTA_FIG2}
+
+# int sdm_*(...) signatures, in the order of include/sdm.h
+_P, _I64, _I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+_SIGS = {
+    "sdm_abi_version": (_I, []),
+    "sdm_status_string": (ctypes.c_char_p, [_I]),
+    "sdm_last_error": (ctypes.c_char_p, []),
+    "sdm_address": (_I, [_P, _P, _I, _P, _P, _I, _I64, _I64, _I64, _I64, _I64, _I64, _I64,
+                         _P, _P, _P, _P, _P, _P, _P]),
+    "sdm_debug_half_scores": (_I, [_P, _I, _P, _I, _I64, _I64, _I64, _I64, _I64, _P, _P]),
+    "sdm_state_init": (_I, [_P, _P, _I64, _I64, _I64, _I64, _P]),
+    "sdm_scan_workspace_bytes": (_I64, [_I64, _I64, _I64, _I64, _I64, _I64]),
+    "sdm_scan_forward": (_I, [_P, _P, _I64, _P, _P, _I64, _P, _P, _P, _I, _P, _P,
+                              _I64, _I64, _I64, _I64, _I64, _I, _P, _I64, _P]),
+}
+
+_lib = None
+
+
+class SdmError(RuntimeError):
+    def __init__(self, fn: str, code: int, detail: str):
+        super().__init__(f"{fn} failed with status {code}: {detail}")
+        self.code = code
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libsdm.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -c 'import __graft_entry__ as g; g.build()'`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(fn: str, rc: int):
+    if rc != 0:
+        raise SdmError(fn, rc, lib().sdm_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(dev: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _dev(*ts: torch.Tensor) -> torch.device:
+    d = ts[0].device
+    for t in ts:
+        if t.device.type != "cuda" or t.device != d:
+            raise ValueError("all tensors must be on the same GPU")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+    return d
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return SDM_F32
+    if t.dtype == torch.bfloat16:
+        return SDM_BF16
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+def sdm_abi_version() -> int:
+    return lib().sdm_abi_version()
+
+
+def sdm_status_string(code: int) -> str:
+    return lib().sdm_status_string(code).decode()
+
+
+def sdm_last_error() -> str:
+    return lib().sdm_last_error().decode()
+
+
+def sdm_address(q_w: torch.Tensor, q_r: torch.Tensor, subkeys_w: torch.Tensor,
+                subkeys_r: torch.Tensor, W: int, R: int, return_scores: bool = False,
+                out: Optional[Tuple[torch.Tensor, ...]] = None):
+    """Product-key addressing of both branches.
+
+    q_w, q_r [B,H,T,2,dh]; subkeys [H,2,n_sub,dh] (same dtype, fp32 or bf16).
+    Returns (idx_w, wt_w, idx_r, wt_r) and, with return_scores, (score_w, score_r).
+    ``out`` may pass preallocated (idx_w, wt_w, idx_r, wt_r) tensors.
+    """
+    d = _dev(q_w, q_r, subkeys_w, subkeys_r)
+    B, H, T, two, dh = q_w.shape
+    n = subkeys_w.shape[2]
+    if two != 2 or q_r.shape != q_w.shape or subkeys_w.shape != (H, 2, n, dh) \
+            or subkeys_r.shape != subkeys_w.shape:
+        raise ValueError("shape mismatch in sdm_address")
+    kw = dict(device=d)
+    if out is not None:
+        idx_w, wt_w, idx_r, wt_r = out
+        for t, shp, dt in ((idx_w, (B, H, T, W), torch.int32), (wt_w, (B, H, T, W), torch.float32),
+                           (idx_r, (B, H, T, R), torch.int32), (wt_r, (B, H, T, R), torch.float32)):
+            if tuple(t.shape) != shp or t.dtype != dt:
+                raise ValueError("preallocated address output has the wrong shape or dtype")
+        _dev(q_w, idx_w, wt_w, idx_r, wt_r)
+    else:
+        idx_w = torch.empty((B, H, T, W), dtype=torch.int32, **kw)
+        wt_w = torch.empty((B, H, T, W), dtype=torch.float32, **kw)
+        idx_r = torch.empty((B, H, T, R), dtype=torch.int32, **kw)
+        wt_r = torch.empty((B, H, T, R), dtype=torch.float32, **kw)
+    sc_w = torch.empty((B, H, T, W), dtype=torch.float32, **kw) if return_scores else None
+    sc_r = torch.empty((B, H, T, R), dtype=torch.float32, **kw) if return_scores else None
+    _check("sdm_address", lib().sdm_address(
+        _ptr(q_w), _ptr(q_r), _dtype_code(q_w), _ptr(subkeys_w), _ptr(subkeys_r),
+        _dtype_code(subkeys_w), B, H, T, n, dh, W, R, _ptr(idx_w), _ptr(wt_w), _ptr(idx_r),
+        _ptr(wt_r), _ptr(sc_w), _ptr(sc_r), _stream(d)))
+    out = (idx_w, wt_w, idx_r, wt_r)
+    return out + (sc_w, sc_r) if return_scores else out
+
+
+def sdm_debug_half_scores(q: torch.Tensor, subkeys: torch.Tensor) -> torch.Tensor:
+    """Half-scores [B,H,T,2,n_sub] fp32 of one branch (the contraction of sdm_address)."""
+    d = _dev(q, subkeys)
+    B, H, T, _, dh = q.shape
+    n = subkeys.shape[2]
+    half = torch.empty((B, H, T, 2, n), dtype=torch.float32, device=d)
+    _check("sdm_debug_half_scores", lib().sdm_debug_half_scores(
+        _ptr(q), _dtype_code(q), _ptr(subkeys), _dtype_code(subkeys), B, H, T, n, dh,
+        _ptr(half), _stream(d)))
+    return half
+
+
+def sdm_state_init(M0: torch.Tensor, B: int, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Per-sequence table [B,H,N,dv] initialised from M0 [H,N,dv]."""
+    d = _dev(M0)
+    H, N, dv = M0.shape
+    M = out if out is not None else torch.empty((B, H, N, dv), dtype=torch.float32, device=d)
+    if M.shape != (B, H, N, dv) or M.dtype != torch.float32:
+        raise ValueError("state tensor has the wrong shape or dtype")
+    _dev(M0, M)
+    _check("sdm_state_init", lib().sdm_state_init(_ptr(M0), _ptr(M), B, H, N, dv, _stream(d)))
+    return M
+
+
+def sdm_scan_workspace_bytes(B: int, H: int, T: int, W: int, R: int, dv: int) -> int:
+    n = lib().sdm_scan_workspace_bytes(B, H, T, W, R, dv)
+    if n < 0:
+        raise ValueError("invalid sizes for the scan workspace")
+    return n
+
+
+def sdm_scan_forward(idx_w: torch.Tensor, wt_w: torch.Tensor, idx_r: torch.Tensor,
+                     wt_r: torch.Tensor, alpha: torch.Tensor, beta: torch.Tensor,
+                     v: torch.Tensor, M: torch.Tensor, form: str = "eq4",
+                     y: Optional[torch.Tensor] = None,
+                     workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Sparse gated delta scan over all T tokens; M [B,H,N,dv] is updated in place.
+
+    Returns y [B,H,T,dv] fp32.
+    """
+    d = _dev(idx_w, wt_w, idx_r, wt_r, alpha, beta, v, M)
+    B, H, T, W = idx_w.shape
+    R = idx_r.shape[3]
+    N, dv = M.shape[2], M.shape[3]
+    shapes = {"wt_w": (wt_w, (B, H, T, W)), "idx_r": (idx_r, (B, H, T, R)),
+              "wt_r": (wt_r, (B, H, T, R)), "alpha": (alpha, (B, H, T)),
+              "beta": (beta, (B, H, T)), "v": (v, (B, H, T, dv)), "M": (M, (B, H, N, dv))}
+    for name, (t, shp) in shapes.items():
+        if tuple(t.shape) != shp:
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {shp}")
+    if idx_w.dtype != torch.int32 or idx_r.dtype != torch.int32 or wt_w.dtype != torch.float32 \
+            or wt_r.dtype != torch.float32 or alpha.dtype != torch.float32 \
+            or beta.dtype != torch.float32 or M.dtype != torch.float32:
+        raise ValueError("dtype mismatch in sdm_scan_forward")
+    if y is None:
+        y = torch.empty((B, H, T, dv), dtype=torch.float32, device=d)
+    elif tuple(y.shape) != (B, H, T, dv) or y.dtype != torch.float32:
+        raise ValueError("y has the wrong shape or dtype")
+    _dev(M, y)
+    nbytes = sdm_scan_workspace_bytes(B, H, T, W, R, dv)
+    if workspace is None:
+        workspace = torch.empty((max(nbytes, 16),), dtype=torch.uint8, device=d)
+    elif workspace.dtype != torch.uint8 or workspace.dim() != 1:
+        raise ValueError("workspace must be a 1-D uint8 tensor")
+    _dev(M, workspace)
+    _check("sdm_scan_forward", lib().sdm_scan_forward(
+        _ptr(idx_w), _ptr(wt_w), W, _ptr(idx_r), _ptr(wt_r), R, _ptr(alpha), _ptr(beta),
+        _ptr(v), _dtype_code(v), _ptr(M), _ptr(y), B, H, T, N, dv, FORMS[form],
+        _ptr(workspace), workspace.numel(), _stream(d)))
+    return y

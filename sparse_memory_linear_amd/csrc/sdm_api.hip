@@ -1,0 +1,191 @@
+// sdm_api.hip -- the C ABI (include/sdm.h): host-side validation and dispatch.
+// Every check runs before any HIP call; a failing call writes nothing,
+// launches nothing and records a thread-local message.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "sdm.h"
+#include "sdm_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+int ok() {
+    g_err[0] = '\0';
+    return SDM_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int hip_fail(hipError_t e, const char* what) {
+    return fail(SDM_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+int check_address_sizes(int q_dtype, int k_dtype, int64_t B, int64_t H, int64_t T, int64_t n_sub,
+                        int64_t dh) {
+    if (q_dtype != SDM_F32 && q_dtype != SDM_BF16) return fail(SDM_ERR_DTYPE, "unknown q dtype %d", q_dtype);
+    if (k_dtype != q_dtype) return fail(SDM_ERR_DTYPE, "subkey dtype %d differs from q dtype %d", k_dtype, q_dtype);
+    if (B < 0 || H < 0 || T < 0) return fail(SDM_ERR_SHAPE, "negative B/H/T (%lld, %lld, %lld)",
+                                             (long long)B, (long long)H, (long long)T);
+    if (n_sub < 1 || dh < 1) return fail(SDM_ERR_SHAPE, "n_sub and dh must be >= 1");
+    if (n_sub % 16 != 0 || n_sub > 512)
+        return fail(SDM_ERR_UNSUPPORTED, "n_sub=%lld: kernels cover multiples of 16 up to 512", (long long)n_sub);
+    const int64_t step = q_dtype == SDM_BF16 ? 32 : 8;
+    if (dh % step != 0 || dh > 256)
+        return fail(SDM_ERR_UNSUPPORTED, "dh=%lld: kernels cover multiples of %lld up to 256", (long long)dh,
+                    (long long)step);
+    const int64_t ntile = (T + 15) / 16;
+    if (ntile * B * H > 0x7FFFFFFFll) return fail(SDM_ERR_UNSUPPORTED, "too many token tiles for one launch");
+    return SDM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sdm_abi_version(void) { return SDM_ABI_VERSION; }
+
+const char* sdm_status_string(int s) {
+    switch (s) {
+        case SDM_OK: return "ok";
+        case SDM_ERR_NULL: return "null pointer";
+        case SDM_ERR_SHAPE: return "invalid shape";
+        case SDM_ERR_DTYPE: return "invalid dtype or form";
+        case SDM_ERR_ALIGN: return "pointer not 16-byte aligned";
+        case SDM_ERR_UNSUPPORTED: return "unsupported size";
+        case SDM_ERR_HIP: return "HIP error";
+        case SDM_ERR_WORKSPACE: return "workspace missing or too small";
+        default: return "unknown status";
+    }
+}
+
+const char* sdm_last_error(void) { return g_err; }
+
+int sdm_address(const void* q_w, const void* q_r, int q_dtype, const void* subkeys_w, const void* subkeys_r,
+                int k_dtype, int64_t B, int64_t H, int64_t T, int64_t n_sub, int64_t dh, int64_t W, int64_t R,
+                int32_t* idx_w, float* wt_w, int32_t* idx_r, float* wt_r, float* score_w, float* score_r,
+                void* stream) {
+    if (!q_w || !q_r || !subkeys_w || !subkeys_r || !idx_w || !wt_w || !idx_r || !wt_r)
+        return fail(SDM_ERR_NULL, "sdm_address: a required pointer is NULL");
+    int rc = check_address_sizes(q_dtype, k_dtype, B, H, T, n_sub, dh);
+    if (rc) return rc;
+    const int64_t N = n_sub * n_sub;
+    if (W < 1 || R < 1 || W > N || R > N)
+        return fail(SDM_ERR_SHAPE, "W=%lld, R=%lld must lie in [1, N=%lld]", (long long)W, (long long)R,
+                    (long long)N);
+    if (W > 64 || R > 64) return fail(SDM_ERR_UNSUPPORTED, "W, R <= 64 on the GPU (W=%lld, R=%lld)",
+                                      (long long)W, (long long)R);
+    const void* ptrs[] = {q_w, q_r, subkeys_w, subkeys_r, idx_w, wt_w, idx_r, wt_r};
+    for (const void* p : ptrs)
+        if (!aligned16(p)) return fail(SDM_ERR_ALIGN, "sdm_address: pointer %p not 16-byte aligned", p);
+    if ((score_w && !aligned16(score_w)) || (score_r && !aligned16(score_r)))
+        return fail(SDM_ERR_ALIGN, "sdm_address: score pointer not 16-byte aligned");
+    if (B == 0 || H == 0 || T == 0) return ok();
+    sdm::AddressArgs a{};
+    a.q[0] = q_w; a.q[1] = q_r;
+    a.K[0] = subkeys_w; a.K[1] = subkeys_r;
+    a.idx[0] = idx_w; a.idx[1] = idx_r;
+    a.wt[0] = wt_w; a.wt[1] = wt_r;
+    a.score[0] = score_w; a.score[1] = score_r;
+    a.k[0] = (int)W; a.k[1] = (int)R;
+    a.half_out = nullptr;
+    a.B = B; a.H = H; a.T = T; a.n = (int)n_sub; a.dh = (int)dh;
+    a.nbranch = 2;
+    a.bf16 = q_dtype == SDM_BF16;
+    hipError_t e = sdm::launch_address(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "sdm_address launch");
+    return ok();
+}
+
+int sdm_debug_half_scores(const void* q, int q_dtype, const void* subkeys, int k_dtype, int64_t B, int64_t H,
+                          int64_t T, int64_t n_sub, int64_t dh, float* half, void* stream) {
+    if (!q || !subkeys || !half) return fail(SDM_ERR_NULL, "sdm_debug_half_scores: NULL pointer");
+    int rc = check_address_sizes(q_dtype, k_dtype, B, H, T, n_sub, dh);
+    if (rc) return rc;
+    if (!aligned16(q) || !aligned16(subkeys) || !aligned16(half))
+        return fail(SDM_ERR_ALIGN, "sdm_debug_half_scores: pointer not 16-byte aligned");
+    if (B == 0 || H == 0 || T == 0) return ok();
+    sdm::AddressArgs a{};
+    a.q[0] = q; a.K[0] = subkeys;
+    a.k[0] = 1;
+    a.half_out = half;
+    a.B = B; a.H = H; a.T = T; a.n = (int)n_sub; a.dh = (int)dh;
+    a.nbranch = 1;
+    a.bf16 = q_dtype == SDM_BF16;
+    hipError_t e = sdm::launch_address(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "sdm_debug_half_scores launch");
+    return ok();
+}
+
+int sdm_state_init(const float* M0, float* M, int64_t B, int64_t H, int64_t N, int64_t dv, void* stream) {
+    if (!M0 || !M) return fail(SDM_ERR_NULL, "sdm_state_init: NULL pointer");
+    if (B < 0 || H < 0 || N < 1 || dv < 1) return fail(SDM_ERR_SHAPE, "sdm_state_init: invalid sizes");
+    if (dv % 4 != 0) return fail(SDM_ERR_UNSUPPORTED, "sdm_state_init: dv must be a multiple of 4");
+    if (!aligned16(M0) || !aligned16(M)) return fail(SDM_ERR_ALIGN, "sdm_state_init: pointer not 16-byte aligned");
+    if (B == 0 || H == 0) return ok();
+    hipError_t e = sdm::launch_state_init(M0, M, B, H * N * dv, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "sdm_state_init launch");
+    return ok();
+}
+
+int64_t sdm_scan_workspace_bytes(int64_t B, int64_t H, int64_t T, int64_t W, int64_t R, int64_t dv) {
+    if (B < 0 || H < 0 || T < 0 || W < 1 || R < 1 || W > 256 || R > 256 || dv < 4 || dv % 4) return -1;
+    if (B == 0 || H == 0 || T == 0) return 0;
+    return sdm::scan_workspace_bytes(B * H, T, (int)W, (int)R, (int)dv);
+}
+
+int sdm_scan_forward(const int32_t* idx_w, const float* wt_w, int64_t W, const int32_t* idx_r, const float* wt_r,
+                     int64_t R, const float* alpha, const float* beta, const void* v, int v_dtype, float* M,
+                     float* y, int64_t B, int64_t H, int64_t T, int64_t N, int64_t dv, int form, void* workspace,
+                     int64_t workspace_bytes, void* stream) {
+    if (!idx_w || !wt_w || !idx_r || !wt_r || !alpha || !beta || !v || !M || !y)
+        return fail(SDM_ERR_NULL, "sdm_scan_forward: a required pointer is NULL");
+    if (v_dtype != SDM_F32 && v_dtype != SDM_BF16) return fail(SDM_ERR_DTYPE, "unknown v dtype %d", v_dtype);
+    if (form != SDM_DELTA_EQ4 && form != SDM_DELTA_FIG2) return fail(SDM_ERR_DTYPE, "unknown delta form %d", form);
+    if (B < 0 || H < 0 || T < 0 || N < 1 || dv < 1)
+        return fail(SDM_ERR_SHAPE, "sdm_scan_forward: invalid sizes");
+    if (W < 1 || R < 1 || W > N || R > N)
+        return fail(SDM_ERR_SHAPE, "W=%lld, R=%lld must lie in [1, N=%lld]", (long long)W, (long long)R,
+                    (long long)N);
+    if (W > 256 || R > 256) return fail(SDM_ERR_UNSUPPORTED, "W, R <= 256 on the GPU");
+    if (N > (1 << 18)) return fail(SDM_ERR_UNSUPPORTED, "N=%lld: at most 2^18 slots", (long long)N);
+    if (dv % 4 != 0) return fail(SDM_ERR_UNSUPPORTED, "dv=%lld must be a multiple of 4", (long long)dv);
+    if (!sdm::scan_geometry((int)W, (int)R, (int)dv, nullptr, nullptr))
+        return fail(SDM_ERR_UNSUPPORTED, "no scan kernel covers W=%lld, R=%lld, dv=%lld", (long long)W,
+                    (long long)R, (long long)dv);
+    const void* ptrs[] = {idx_w, wt_w, idx_r, wt_r, alpha, beta, v, M, y};
+    for (const void* p : ptrs)
+        if (!aligned16(p)) return fail(SDM_ERR_ALIGN, "sdm_scan_forward: pointer %p not 16-byte aligned", p);
+    if (B == 0 || H == 0 || T == 0) return ok();
+    const int64_t need = sdm::scan_workspace_bytes(B * H, T, (int)W, (int)R, (int)dv);
+    if (!workspace || workspace_bytes < need)
+        return fail(SDM_ERR_WORKSPACE, "workspace of %lld bytes needed, %lld given", (long long)need,
+                    (long long)(workspace ? workspace_bytes : 0));
+    if (!aligned16(workspace)) return fail(SDM_ERR_ALIGN, "workspace not 16-byte aligned");
+    if ((B * H + 7) / 8 * 8 * (dv / 4) > 0x7FFFFFFFll)
+        return fail(SDM_ERR_UNSUPPORTED, "too many streams for one launch");
+    sdm::ScanArgs a{};
+    a.idx_w = idx_w; a.wt_w = wt_w; a.W = (int)W;
+    a.idx_r = idx_r; a.wt_r = wt_r; a.R = (int)R;
+    a.alpha = alpha; a.beta = beta;
+    a.v = v; a.v_bf16 = v_dtype == SDM_BF16;
+    a.M = M; a.y = y;
+    a.NS = B * H; a.T = T; a.N = N; a.dv = (int)dv;
+    a.form = form;
+    a.workspace = workspace;
+    hipError_t e = sdm::launch_scan(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "sdm_scan_forward launch");
+    return ok();
+}
+
+}  // extern "C"

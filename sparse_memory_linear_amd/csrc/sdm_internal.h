@@ -1,0 +1,43 @@
+// Internal launch interface between the C ABI (sdm_api.hip) and the kernels.
+// Not installed, not part of the ABI.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sdm {
+
+struct AddressArgs {
+    const void* q[2];        // per branch: [B,H,T,2,dh]
+    const void* K[2];        // per branch: [H,2,n,dh]
+    int32_t* idx[2];         // [B,H,T,k]
+    float* wt[2];
+    float* score[2];         // optional
+    int k[2];
+    float* half_out;         // debug: [B,H,T,2,n]; when set only half-scores are written
+    int64_t B, H, T;
+    int n, dh;
+    int nbranch;             // 1 or 2
+    bool bf16;
+};
+hipError_t launch_address(const AddressArgs& a, hipStream_t st);
+
+struct ScanArgs {
+    const int32_t* idx_w; const float* wt_w; int W;
+    const int32_t* idx_r; const float* wt_r; int R;
+    const float* alpha; const float* beta;
+    const void* v; bool v_bf16;
+    float* M; float* y;
+    int64_t NS;              // B*H streams
+    int64_t T, N;
+    int dv;
+    int form;                // 0 = per-slot Eq. (4), 1 = Fig. 2 shared residual
+    void* workspace;
+};
+// Chooses the kernel instance; returns false if no instance covers (W, R, dv).
+bool scan_geometry(int W, int R, int dv, int* slab, int* rec_bytes);
+int64_t scan_workspace_bytes(int64_t NS, int64_t T, int W, int R, int dv);
+hipError_t launch_scan(const ScanArgs& a, hipStream_t st);
+
+hipError_t launch_state_init(const float* M0, float* M, int64_t B, int64_t per_seq, hipStream_t st);
+
+}  // namespace sdm

@@ -1,0 +1,109 @@
+"""Host-side checks of the C ABI (no GPU): the library loads, exports every
+declared symbol, and rejects invalid arguments before any launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from sparse_memory_linear_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sdm.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sdm_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(binding.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    return binding.lib()
+
+
+def test_header_declares_the_hot_path_calls():
+    names = declared_functions()
+    for f in ("sdm_address", "sdm_scan_forward", "sdm_state_init", "sdm_debug_half_scores",
+              "sdm_scan_workspace_bytes", "sdm_status_string", "sdm_last_error", "sdm_abi_version"):
+        assert f in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert set(binding._SIGS) == set(declared_functions())
+
+
+def test_abi_version_and_status_strings(lib):
+    assert binding.sdm_abi_version() == 1
+    assert binding.sdm_status_string(0) == "ok"
+    assert binding.sdm_status_string(7).startswith("workspace")
+    assert binding.sdm_status_string(99) == "unknown status"
+
+
+def test_workspace_size_is_pure_host_logic(lib):
+    # W = R = 64, dv = 128: 16-byte header + 32 rows x 4 groups x 8 bytes per token
+    # record, plus one 16-byte sink per lane of each of the 8*ceil(32/8)*16 wavefronts
+    assert binding.sdm_scan_workspace_bytes(4, 8, 8192, 64, 64, 128) == 32 * 8192 * 1040 + 512 * 64 * 16
+    assert binding.sdm_scan_workspace_bytes(0, 8, 8192, 64, 64, 128) == 0
+    assert lib.sdm_scan_workspace_bytes(1, 1, 1, 0, 1, 16) == -1
+    assert lib.sdm_scan_workspace_bytes(1, 1, 1, 300, 1, 16) == -1
+
+
+P = ctypes.c_void_p
+
+
+def test_address_rejects_bad_arguments_before_launch(lib):
+    fake = P(4096)  # never dereferenced: every call below fails validation first
+    args = lambda **kw: dict(dict(q_w=fake, q_r=fake, qd=1, kw=fake, kr=fake, kd=1, B=1, H=1, T=16,
+                                  n=256, dh=64, W=64, R=64, iw=fake, ww=fake, ir=fake, wr=fake,
+                                  sw=None, sr=None, st=None), **kw)
+    call = lambda a: lib.sdm_address(*a.values())
+    assert call(args(q_w=None)) == 1
+    assert call(args(qd=5)) == 3
+    assert call(args(kd=0)) == 3                 # subkey dtype must match q
+    assert call(args(T=-1)) == 2
+    assert call(args(n=250)) == 5                # not a multiple of 16
+    assert call(args(dh=48)) == 5                # bf16 needs multiples of 32
+    assert call(args(W=0)) == 2
+    assert call(args(W=65)) == 5                 # GPU covers k <= 64
+    assert call(args(iw=P(4100))) == 4           # misaligned
+    assert "aligned" in binding.sdm_last_error()
+
+
+def test_scan_rejects_bad_arguments_before_launch(lib):
+    fake = P(4096)
+    base = dict(iw=fake, ww=fake, W=64, ir=fake, wr=fake, R=64, a=fake, b=fake, v=fake, vd=1,
+                M=fake, y=fake, B=1, H=1, T=8, N=65536, dv=128, form=0, ws=fake, wsb=1 << 30,
+                st=None)
+    call = lambda **kw: lib.sdm_scan_forward(*dict(base, **kw).values())
+    assert call(iw=None) == 1
+    assert call(vd=2) == 3
+    assert call(form=2) == 3
+    assert call(W=65537) == 2                    # W > N
+    assert call(N=(1 << 18) + 1, W=64) == 5
+    assert call(dv=130) == 5
+    assert call(ws=None) == 7
+    assert call(wsb=100) == 7
+    assert call(y=P(4104)) == 4
+    assert "workspace" in binding.sdm_last_error() or "aligned" in binding.sdm_last_error()
+
+
+def test_state_init_rejects_bad_arguments(lib):
+    fake = P(4096)
+    assert lib.sdm_state_init(None, fake, 1, 1, 16, 16, None) == 1
+    assert lib.sdm_state_init(fake, fake, 1, 1, 16, 18, None) == 5
+    assert lib.sdm_state_init(fake, fake, -1, 1, 16, 16, None) == 2
+
+
+def test_binding_refuses_cpu_tensors(lib):
+    import torch
+    x = torch.zeros(1, 1, 16, 2, 64, dtype=torch.bfloat16)
+    k = torch.zeros(1, 2, 256, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        binding.sdm_address(x, x, k, k, 8, 8)

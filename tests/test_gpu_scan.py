@@ -1,0 +1,172 @@
+"""GPU parity of the sparse gated delta scan against the CPU oracle, through the C ABI.
+
+Both sides receive identical indices, weights, gates, values and initial table
+(bit for bit), so y and the final table must agree to fp32 rounding; rows no
+token writes must stay bit-identical to M0.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_memory_linear_amd as sdm
+from sparse_memory_linear_amd import inputs
+from parity import TOL_BF16, TOL_F32, max_rel_err, say
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+FORMS = [("eq4", oracle.EQ4), ("fig2", oracle.FIG2)]
+
+
+def _run_gpu(idx_w, wt_w, idx_r, wt_r, alpha, beta, v, M_in, form):
+    t = lambda a, dt=None: (a if isinstance(a, torch.Tensor) else torch.from_numpy(np.ascontiguousarray(a))).to(DEV)
+    M = t(M_in).float().contiguous().clone()
+    y = sdm.sdm_scan_forward(t(idx_w).int(), t(wt_w).float(), t(idx_r).int(), t(wt_r).float(),
+                             t(alpha).float(), t(beta).float(), t(v), M, form)
+    torch.cuda.synchronize()
+    return M.cpu().numpy(), y.cpu().numpy()
+
+
+def _check(name, Mg, yg, Mo, yo, M_in, idx_w, tol):
+    ey, em = max_rel_err(yg, yo), max_rel_err(Mg, Mo)
+    say(f"  {name}: max rel err y {ey:.2e}, M {em:.2e}")
+    assert ey <= tol and em <= tol
+    # rows never selected for writing are bit-identical to the initial table
+    M_in = np.asarray(M_in)
+    iw = np.asarray(idx_w)
+    B, H = iw.shape[:2]
+    for b in range(B):
+        for h in range(H):
+            written = np.zeros(M_in.shape[2], bool)
+            written[iw[b, h].reshape(-1)] = True
+            assert np.array_equal(Mg[b, h, ~written].view(np.uint32), M_in[b, h, ~written].view(np.uint32))
+
+
+CASES = [("tiny", {}), ("tiny_dense", {}), ("small", {}),
+         ("gdn_matched", dict(B=1, H=2, T=1000)), ("long_context", dict(H=2, T=3000)),
+         ("large_table", dict(T=1500))]
+
+
+_ADDR = {}
+
+
+def _oracle_inputs(name, over):
+    key = (name, tuple(sorted(over.items())))
+    if key not in _ADDR:
+        wl = inputs.get(name, **over)
+        x = inputs.make_inputs(wl)
+        iw, ww, _, _ = oracle.address(x["q_w"], x["subkeys"], wl.W)
+        ir, wr, _, _ = oracle.address(x["q_r"], x["subkeys"], wl.R)
+        _ADDR.clear()
+        _ADDR[key] = (wl, x, iw, ww, ir, wr)
+    return _ADDR[key]
+
+
+@pytest.mark.parametrize("name,over", CASES, ids=[c[0] for c in CASES])
+@pytest.mark.parametrize("form,oform", FORMS, ids=["eq4", "fig2"])
+def test_scan_matches_oracle(name, over, form, oform):
+    say(f"[scan] {name} {over} form={form}")
+    wl, x, iw, ww, ir, wr = _oracle_inputs(name, over)
+    M_in = oracle.broadcast_state(x["M0"], wl.B)
+    Mo, yo = oracle.scan(iw, ww, ir, wr, x["alpha"], x["beta"], x["v"], M_in, oform)
+    Mg, yg = _run_gpu(iw, ww, ir, wr, x["alpha"], x["beta"], x["v"], M_in, form)
+    _check(name, Mg, yg, Mo, yo, M_in, iw, TOL_BF16 if wl.bf16_inputs else TOL_F32)
+
+
+def _random_case(seed, B, H, T, N, dv, W, R, bf16=False):
+    rng = np.random.default_rng(seed)
+    iw = np.stack([rng.permutation(N)[:W] for _ in range(B * H * T)]).reshape(B, H, T, W).astype(np.int32)
+    ir = np.stack([rng.permutation(N)[:R] for _ in range(B * H * T)]).reshape(B, H, T, R).astype(np.int32)
+    ww = rng.dirichlet(np.ones(W), size=(B, H, T)).astype(np.float32)
+    wr = rng.dirichlet(np.ones(R), size=(B, H, T)).astype(np.float32)
+    a = (1 / (1 + np.exp(-rng.normal(2, .5, (B, H, T))))).astype(np.float32)
+    b = (1 / (1 + np.exp(-rng.normal(0, 1, (B, H, T))))).astype(np.float32)
+    v = torch.from_numpy(rng.standard_normal((B, H, T, dv)).astype(np.float32))
+    if bf16:
+        v = v.to(torch.bfloat16)
+    M0 = (rng.standard_normal((B, H, N, dv)) * 0.02).astype(np.float32)
+    return dict(idx_w=iw, wt_w=ww, idx_r=ir, wt_r=wr, alpha=a, beta=b, v=v, M_in=M0)
+
+
+HAZARD = [  # small tables: rows are rewritten by nearby tokens all the time
+    dict(B=1, H=3, T=700, N=256, dv=128, W=64, R=64, bf16=True),   # 64-slot sets in 256 rows
+    dict(B=2, H=1, T=400, N=64, dv=32, W=16, R=16),                  # every other token overlaps
+    dict(B=1, H=1, T=300, N=16, dv=512, W=8, R=8),
+    dict(B=1, H=2, T=500, N=300, dv=16, W=200, R=256),              # wide sets, one slab
+]
+
+
+@pytest.mark.parametrize("case", HAZARD, ids=[f"N{c['N']}W{c['W']}dv{c['dv']}" for c in HAZARD])
+@pytest.mark.parametrize("form,oform", FORMS, ids=["eq4", "fig2"])
+def test_scan_hazard_stress(case, form, oform):
+    """Heavy row reuse: read-after-write within a token and across every
+    prefetch distance must be forwarded correctly."""
+    say(f"[scan hazards] {case} form={form}")
+    c = _random_case(1, **case)
+    Mo, yo = oracle.scan(**c, form=oform)
+    Mg, yg = _run_gpu(**c, form=form)
+    _check("hazard", Mg, yg, Mo, yo, c["M_in"], c["idx_w"], TOL_F32)
+
+
+@pytest.mark.parametrize("T", [1, 2, 5, 6, 7, 10, 11, 13, 61])
+def test_scan_short_and_ragged_sequences(T):
+    say(f"[scan ragged] T={T}")
+    for case in (dict(B=3, H=1, N=128, dv=128, W=64, R=64), dict(B=1, H=5, N=64, dv=64, W=16, R=16)):
+        c = _random_case(T, T=T, **case)
+        for form, oform in FORMS:
+            Mo, yo = oracle.scan(**c, form=oform)
+            Mg, yg = _run_gpu(**c, form=form)
+            _check(f"T={T} {form}", Mg, yg, Mo, yo, c["M_in"], c["idx_w"], TOL_F32)
+
+
+def test_scan_empty_sequence_is_a_no_op():
+    c = _random_case(0, B=1, H=1, T=1, N=64, dv=16, W=4, R=4)
+    z = {k: (v[:, :, :0] if k != "M_in" else v) for k, v in c.items()}
+    Mg, yg = _run_gpu(**z, form="eq4")
+    assert yg.shape == (1, 1, 0, 16) and np.array_equal(Mg, c["M_in"])
+
+
+def test_scan_deterministic_split_and_column_permutation():
+    c = _random_case(3, B=2, H=2, T=500, N=512, dv=128, W=64, R=64, bf16=True)
+    for form in ("eq4", "fig2"):
+        M1, y1 = _run_gpu(**c, form=form)
+        M2, y2 = _run_gpu(**c, form=form)
+        assert np.array_equal(M1, M2) and np.array_equal(y1, y2)          # bit-exact rerun
+        t1 = 211
+        first = {k: (v[:, :, :t1] if k != "M_in" else v) for k, v in c.items()}
+        Ma, ya = _run_gpu(**first, form=form)
+        second = {k: (v[:, :, t1:] if k != "M_in" else Ma) for k, v in c.items()}
+        Mb, yb = _run_gpu(**second, form=form)
+        assert np.array_equal(Mb, M1) and np.array_equal(np.concatenate([ya, yb], 2), y1)
+        perm = np.random.default_rng(0).permutation(128)
+        cp = dict(c); cp["v"] = c["v"][..., torch.from_numpy(perm)].contiguous()
+        cp["M_in"] = np.ascontiguousarray(c["M_in"][..., perm])
+        Mp, yp = _run_gpu(**cp, form=form)
+        assert np.array_equal(Mp, M1[..., perm]) and np.array_equal(yp, y1[..., perm])
+
+
+def test_state_init_broadcasts_M0():
+    M0 = torch.randn(3, 1000, 64)
+    M = sdm.sdm_state_init(M0.to(DEV), 5).cpu()
+    assert all(torch.equal(M[b], M0) for b in range(5))
+
+
+@pytest.mark.parametrize("name,streams", [("gdn_matched", [(0, 0), (3, 7)]), ("long_context", [(0, 5)])])
+def test_full_pipeline_full_size_sampled_streams(name, streams):
+    """The whole hot path at full size, in the benchmark's launch configuration
+    (state init, addressing, scan); sampled (b, h) streams are checked in full
+    against the oracle scan fed with the GPU's slots and weights."""
+    wl = inputs.get(name)
+    say(f"[pipeline full size] {name} B={wl.B} H={wl.H} T={wl.T} streams={streams}")
+    x = inputs.make_inputs(wl)
+    g = {k: v.to(DEV) for k, v in x.items()}
+    iw, ww, ir, wr = sdm.sdm_address(g["q_w"], g["q_r"], g["subkeys"], g["subkeys"], wl.W, wl.R)
+    M = sdm.sdm_state_init(g["M0"], wl.B)
+    y = sdm.sdm_scan_forward(iw, ww, ir, wr, g["alpha"], g["beta"], g["v"], M, "eq4")
+    torch.cuda.synchronize()
+    for (b, h) in streams:
+        sl = lambda t: t[b:b + 1, h:h + 1].cpu()
+        Mo, yo = oracle.scan(sl(iw), sl(ww), sl(ir), sl(wr), sl(x["alpha"]), sl(x["beta"]), sl(x["v"]),
+                             x["M0"][h:h + 1][None].numpy(), oracle.EQ4)
+        _check(f"stream ({b},{h})", sl(M).numpy(), sl(y).numpy(), Mo, yo,
+               x["M0"][h:h + 1][None].numpy(), sl(iw).numpy(), TOL_BF16)
