@@ -19,7 +19,8 @@
  *     A failed launch returns SDM_ERR_HIP. Faults inside a kernel surface at
  *     the caller's next synchronisation. No C++ exception crosses the ABI.
  *   - Pointers to device tensors must be 16-byte aligned (SDM_ERR_ALIGN).
- *   - Empty work (B, H or T equal to 0) is valid and launches nothing.
+ *   - Empty work (B, H or T equal to 0) is valid, launches nothing and accepts
+ *     NULL tensor pointers (empty tensors need not have storage).
  */
 #ifndef SDM_H
 #define SDM_H

@@ -75,8 +75,6 @@ int sdm_address(const void* q_w, const void* q_r, int q_dtype, const void* subke
                 int k_dtype, int64_t B, int64_t H, int64_t T, int64_t n_sub, int64_t dh, int64_t W, int64_t R,
                 int32_t* idx_w, float* wt_w, int32_t* idx_r, float* wt_r, float* score_w, float* score_r,
                 void* stream) {
-    if (!q_w || !q_r || !subkeys_w || !subkeys_r || !idx_w || !wt_w || !idx_r || !wt_r)
-        return fail(SDM_ERR_NULL, "sdm_address: a required pointer is NULL");
     int rc = check_address_sizes(q_dtype, k_dtype, B, H, T, n_sub, dh);
     if (rc) return rc;
     const int64_t N = n_sub * n_sub;
@@ -85,12 +83,14 @@ int sdm_address(const void* q_w, const void* q_r, int q_dtype, const void* subke
                     (long long)N);
     if (W > 64 || R > 64) return fail(SDM_ERR_UNSUPPORTED, "W, R <= 64 on the GPU (W=%lld, R=%lld)",
                                       (long long)W, (long long)R);
+    if (B == 0 || H == 0 || T == 0) return ok();  // empty tensors may have NULL data
+    if (!q_w || !q_r || !subkeys_w || !subkeys_r || !idx_w || !wt_w || !idx_r || !wt_r)
+        return fail(SDM_ERR_NULL, "sdm_address: a required pointer is NULL");
     const void* ptrs[] = {q_w, q_r, subkeys_w, subkeys_r, idx_w, wt_w, idx_r, wt_r};
     for (const void* p : ptrs)
         if (!aligned16(p)) return fail(SDM_ERR_ALIGN, "sdm_address: pointer %p not 16-byte aligned", p);
     if ((score_w && !aligned16(score_w)) || (score_r && !aligned16(score_r)))
         return fail(SDM_ERR_ALIGN, "sdm_address: score pointer not 16-byte aligned");
-    if (B == 0 || H == 0 || T == 0) return ok();
     sdm::AddressArgs a{};
     a.q[0] = q_w; a.q[1] = q_r;
     a.K[0] = subkeys_w; a.K[1] = subkeys_r;
@@ -109,12 +109,12 @@ int sdm_address(const void* q_w, const void* q_r, int q_dtype, const void* subke
 
 int sdm_debug_half_scores(const void* q, int q_dtype, const void* subkeys, int k_dtype, int64_t B, int64_t H,
                           int64_t T, int64_t n_sub, int64_t dh, float* half, void* stream) {
-    if (!q || !subkeys || !half) return fail(SDM_ERR_NULL, "sdm_debug_half_scores: NULL pointer");
     int rc = check_address_sizes(q_dtype, k_dtype, B, H, T, n_sub, dh);
     if (rc) return rc;
+    if (B == 0 || H == 0 || T == 0) return ok();
+    if (!q || !subkeys || !half) return fail(SDM_ERR_NULL, "sdm_debug_half_scores: NULL pointer");
     if (!aligned16(q) || !aligned16(subkeys) || !aligned16(half))
         return fail(SDM_ERR_ALIGN, "sdm_debug_half_scores: pointer not 16-byte aligned");
-    if (B == 0 || H == 0 || T == 0) return ok();
     sdm::AddressArgs a{};
     a.q[0] = q; a.K[0] = subkeys;
     a.k[0] = 1;
@@ -128,11 +128,11 @@ int sdm_debug_half_scores(const void* q, int q_dtype, const void* subkeys, int k
 }
 
 int sdm_state_init(const float* M0, float* M, int64_t B, int64_t H, int64_t N, int64_t dv, void* stream) {
-    if (!M0 || !M) return fail(SDM_ERR_NULL, "sdm_state_init: NULL pointer");
     if (B < 0 || H < 0 || N < 1 || dv < 1) return fail(SDM_ERR_SHAPE, "sdm_state_init: invalid sizes");
     if (dv % 4 != 0) return fail(SDM_ERR_UNSUPPORTED, "sdm_state_init: dv must be a multiple of 4");
-    if (!aligned16(M0) || !aligned16(M)) return fail(SDM_ERR_ALIGN, "sdm_state_init: pointer not 16-byte aligned");
     if (B == 0 || H == 0) return ok();
+    if (!M0 || !M) return fail(SDM_ERR_NULL, "sdm_state_init: NULL pointer");
+    if (!aligned16(M0) || !aligned16(M)) return fail(SDM_ERR_ALIGN, "sdm_state_init: pointer not 16-byte aligned");
     hipError_t e = sdm::launch_state_init(M0, M, B, H * N * dv, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "sdm_state_init launch");
     return ok();
@@ -148,8 +148,6 @@ int sdm_scan_forward(const int32_t* idx_w, const float* wt_w, int64_t W, const i
                      int64_t R, const float* alpha, const float* beta, const void* v, int v_dtype, float* M,
                      float* y, int64_t B, int64_t H, int64_t T, int64_t N, int64_t dv, int form, void* workspace,
                      int64_t workspace_bytes, void* stream) {
-    if (!idx_w || !wt_w || !idx_r || !wt_r || !alpha || !beta || !v || !M || !y)
-        return fail(SDM_ERR_NULL, "sdm_scan_forward: a required pointer is NULL");
     if (v_dtype != SDM_F32 && v_dtype != SDM_BF16) return fail(SDM_ERR_DTYPE, "unknown v dtype %d", v_dtype);
     if (form != SDM_DELTA_EQ4 && form != SDM_DELTA_FIG2) return fail(SDM_ERR_DTYPE, "unknown delta form %d", form);
     if (B < 0 || H < 0 || T < 0 || N < 1 || dv < 1)
@@ -163,10 +161,12 @@ int sdm_scan_forward(const int32_t* idx_w, const float* wt_w, int64_t W, const i
     if (!sdm::scan_geometry((int)W, (int)R, (int)dv, nullptr, nullptr))
         return fail(SDM_ERR_UNSUPPORTED, "no scan kernel covers W=%lld, R=%lld, dv=%lld", (long long)W,
                     (long long)R, (long long)dv);
+    if (B == 0 || H == 0 || T == 0) return ok();  // empty tensors may have NULL data
+    if (!idx_w || !wt_w || !idx_r || !wt_r || !alpha || !beta || !v || !M || !y)
+        return fail(SDM_ERR_NULL, "sdm_scan_forward: a required pointer is NULL");
     const void* ptrs[] = {idx_w, wt_w, idx_r, wt_r, alpha, beta, v, M, y};
     for (const void* p : ptrs)
         if (!aligned16(p)) return fail(SDM_ERR_ALIGN, "sdm_scan_forward: pointer %p not 16-byte aligned", p);
-    if (B == 0 || H == 0 || T == 0) return ok();
     const int64_t need = sdm::scan_workspace_bytes(B * H, T, (int)W, (int)R, (int)dv);
     if (!workspace || workspace_bytes < need)
         return fail(SDM_ERR_WORKSPACE, "workspace of %lld bytes needed, %lld given", (long long)need,

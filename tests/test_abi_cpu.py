@@ -83,6 +83,7 @@ def test_scan_rejects_bad_arguments_before_launch(lib):
                 st=None)
     call = lambda **kw: lib.sdm_scan_forward(*dict(base, **kw).values())
     assert call(iw=None) == 1
+    assert call(iw=None, ww=None, M=None, T=0) == 0                     # empty: valid no-op
     assert call(vd=2) == 3
     assert call(form=2) == 3
     assert call(W=65537) == 2                    # W > N
@@ -97,6 +98,7 @@ def test_scan_rejects_bad_arguments_before_launch(lib):
 def test_state_init_rejects_bad_arguments(lib):
     fake = P(4096)
     assert lib.sdm_state_init(None, fake, 1, 1, 16, 16, None) == 1
+    assert lib.sdm_state_init(None, None, 0, 1, 16, 16, None) == 0      # empty: no storage needed
     assert lib.sdm_state_init(fake, fake, 1, 1, 16, 18, None) == 5
     assert lib.sdm_state_init(fake, fake, -1, 1, 16, 16, None) == 2
 
