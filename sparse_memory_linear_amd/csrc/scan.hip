@@ -6,27 +6,30 @@
 //       EQ4:  M[i] = Mt_i + beta_t w_i (v_t - Mt_i)
 //       FIG2: M[i] = Mt_i + beta_t w_i (v_t - sum_j w_j Mt_j)
 //   y_t = sum over the read rows of wr_i M[i]  (after this token's writes).
-// Rows that are not selected for writing are never loaded for writing nor
-// stored, so they stay bit-identical.
+// Rows that are not selected for writing are never stored, so they stay
+// bit-identical.
 //
 // Design. The columns of the table never interact (both forms are per column),
-// so one wavefront owns one (stream, column slab of S floats) and runs the whole
-// token loop on the device. All indices are known before the scan (they are the
-// addressing output), so a planner kernel first resolves every read-after-write
-// hazard from the indices alone:
-//   * the scan issues the row loads of token t+D while it processes token t
-//     (a register ring, D tokens deep), so a row written by a token in
-//     [t+D-D, t+D) is stale in HBM at load time; the planner marks such an
-//     access "forward from token t+D-d, write position p" and the scan takes the
-//     value from an LDS ring of recently written rows instead;
-//   * a read of a row written by the same token forwards with d = 0.
-// Everything else is ordered by the single wavefront: its loads and stores of
-// one address are performed in program order, so a load issued after a store
-// (any lane) returns the stored value. No barriers are needed.
+// so one workgroup owns one (stream, column slab of S floats) and runs the
+// whole token loop on the device. Inside it, "writer" wavefronts own the W
+// write accesses of every token (G rows each) and "reader" wavefronts the R
+// read accesses. One workgroup barrier per token orders them (two for FIG2,
+// whose shared prediction sums over all writers); on gfx950 a workgroup-scope
+// barrier does not drain the memory counters, so each wavefront keeps D tokens
+// of row loads in flight across it.
+//
+// All indices are known before the scan (they are the addressing output), so
+// a planner kernel first resolves every read-after-write hazard from the
+// indices alone. A wavefront issues the loads of token t+D while it is at
+// token t, after the barrier that closed token t-1; stores of tokens < t are
+// visible to those loads, rows written by tokens in [t, t+D) are not. The
+// planner marks such accesses "forward from token t+D-d, write position p" and
+// the scan takes them from an LDS ring of recently written rows; a read of a
+// row written by the same token forwards with d = 0 (after the token's barrier).
 //
 // Placement: workgroups are dealt to the 8 XCDs round-robin, so blockIdx is
 // remapped to put every slab of a stream on the same XCD; the slabs of a row
-// then share that XCD's L2 lines, and HBM sees whole 128-byte lines.
+// then share that XCD's L2 lines.
 #include "sdm_internal.h"
 
 namespace sdm {
@@ -39,25 +42,31 @@ constexpr uint32_t ROW_MASK = (1u << 18) - 1u;
 constexpr int POS_SHIFT = 18;               // write position of the source (8 bits)
 constexpr int DIST_SHIFT = 26;              // token distance of the source (4 bits)
 
-// Lane layout of a slab of S fp32 columns: L = S/4 lanes per row segment
-// (16 B each), G = 64/L rows per wavefront-wide load, NGX groups of G rows per
-// branch; per token the plan record is a 16-byte header (alpha, beta) followed
-// by entries [r][g] for r < G, g < 2*NGX (g < NGX: write p = g*G + r, else read
-// p = (g-NGX)*G + r).
-constexpr int rec_bytes(int S, int NGX) { return 16 + (64 / (S / 4)) * 2 * NGX * 8; }
+constexpr int D_PF = 10;  // tokens of row loads in flight per wavefront
+constexpr int D_MT = 10;  // extra lead of the plan-entry loads; memory counters complete in
+                          // order, so waiting on an entry also waits on every older row load:
+                          // the lead must be >= D_PF to keep D_PF tokens of rows in flight
+constexpr int MAX_WAVES = 8;
 
-struct Inst {
-    int S, NGX, D, DM;
+// Geometry of a slab of S fp32 columns: L = S/4 lanes per row segment (16 B
+// each), G = 64/L rows per wavefront; NWW = ceil(W/G) writer and NWR = ceil(R/G)
+// reader wavefronts. Plan record per token: a 16-byte header (alpha, beta)
+// then entries [wave][G] (int2 each): writer wave w, lane row r -> write
+// access w*G + r; reader wave NWW+w -> read access w*G + r.
+struct Geom {
+    int S, G, NWW, NWR;
+    int nw() const { return NWW + NWR; }
+    int64_t rec() const { return 16 + (int64_t)nw() * G * 8; }
 };
-// Instances: the prefetch depth D and the plan lead DM are set by the VGPR
-// budget of each geometry.
-constexpr Inst kInst[] = {
-    {32, 1, 6, 3},  // W, R <= 8
-    {16, 1, 6, 3},  // W, R <= 16
-    {8, 2, 3, 2},   // W, R <= 64
-    {4, 1, 6, 3},   // W, R <= 64, 16-byte segments (more wavefronts per stream)
-    {4, 4, 2, 1},   // W, R <= 256
-};
+
+Geom make_geom(int S, int W, int R) {
+    Geom g;
+    g.S = S;
+    g.G = 64 / (S / 4);
+    g.NWW = (W + g.G - 1) / g.G;
+    g.NWR = (R + g.G - 1) / g.G;
+    return g;
+}
 
 // ------------------------------------------------------------------ planner
 constexpr int HT_CAP = 8192;  // LDS hash table entries (64-bit)
@@ -69,7 +78,7 @@ __global__ __launch_bounds__(256) void plan_kernel(
     const int32_t* __restrict__ idx_w, const float* __restrict__ wt_w, int W,
     const int32_t* __restrict__ idx_r, const float* __restrict__ wt_r, int R,
     const float* __restrict__ alpha, const float* __restrict__ beta,
-    uint8_t* __restrict__ plan, int64_t T, int64_t N, int D, int G, int NGX, int TT,
+    uint8_t* __restrict__ plan, int64_t T, int64_t N, int D, int G, int NWW, int NWR, int TT,
     int64_t ntile) {
     __shared__ unsigned long long ht[HT_CAP];
     const int tid = threadIdx.x;
@@ -77,8 +86,8 @@ __global__ __launch_bounds__(256) void plan_kernel(
     const int64_t t0 = (blockIdx.x % ntile) * TT;
     const int64_t t1 = t0 + TT < T ? t0 + TT : T;
     const int64_t h0 = t0 - D > 0 ? t0 - D : 0;
-    const int NG = 2 * NGX;
-    const int64_t REC = 16 + (int64_t)G * NG * 8;
+    const int NW = NWW + NWR;
+    const int64_t REC = 16 + (int64_t)NW * G * 8;
     const int32_t* iw = idx_w + s * T * W;
     const float* ww = wt_w + s * T * W;
     const int32_t* ir = idx_r + s * T * R;
@@ -101,14 +110,14 @@ __global__ __launch_bounds__(256) void plan_kernel(
     }
     __syncthreads();
 
-    const int per_tok = G * NG;
+    const int per_tok = NW * G;
     const int64_t nent = (t1 - t0) * per_tok;
     for (int64_t e = tid; e < nent; e += 256) {
         const int64_t tt = t0 + e / per_tok;
         const int rem = (int)(e % per_tok);
-        const int rr = rem / NG, g = rem % NG;
-        const bool isw = g < NGX;
-        const int p = (isw ? g : g - NGX) * G + rr;
+        const int wv = rem / G, rr = rem % G;
+        const bool isw = wv < NWW;
+        const int p = (isw ? wv : wv - NWW) * G + rr;
         uint32_t packed = ENT_INVALID;
         float w = 0.f;
         if (p < (isw ? W : R)) {
@@ -136,8 +145,7 @@ __global__ __launch_bounds__(256) void plan_kernel(
                     packed |= ENT_FWD | ((uint32_t)(tt - best) << DIST_SHIFT) | (bp << POS_SHIFT);
             }
         }
-        *reinterpret_cast<int2*>(P + tt * REC + 16 + (int64_t)(rr * NG + g) * 8) =
-            make_int2((int)packed, __float_as_int(w));
+        *reinterpret_cast<int2*>(P + tt * REC + 16 + (int64_t)rem * 8) = make_int2((int)packed, __float_as_int(w));
     }
     for (int64_t tt = t0 + tid; tt < t1; tt += 256)
         *reinterpret_cast<float4*>(P + tt * REC) = make_float4(alpha[s * T + tt], beta[s * T + tt], 0.f, 0.f);
@@ -175,189 +183,237 @@ __device__ __forceinline__ float4 f4_fma(float s, float4 a, float4 c) {  // s*a 
 __device__ __forceinline__ float4 f4_sub(float4 a, float4 b) {
     return make_float4(a.x - b.x, a.y - b.y, a.z - b.z, a.w - b.w);
 }
-__device__ __forceinline__ float4 f4_xor(float4 a, int m) {
-    return make_float4(__shfl_xor(a.x, m), __shfl_xor(a.y, m), __shfl_xor(a.z, m), __shfl_xor(a.w, m));
-}
 __device__ __forceinline__ float4 f4_add(float4 a, float4 b) {
     return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
 }
 
-template <int S, int NGX, int D, int DM, int FORM, bool VBF16>
-__global__ __launch_bounds__(64) void scan_kernel(const uint8_t* __restrict__ plan, const void* __restrict__ v,
-                                                  float* M, float* __restrict__ y, float* sink_base, int64_t T,
-                                                  int64_t N, int dv, int nslab, int64_t NS) {
-    constexpr int L = S / 4, G = 64 / L, NG = 2 * NGX, U = D + DM + 1;
-    constexpr int REC = rec_bytes(S, NGX);
+// x + (x rotated by N lanes within each row of 16): DPP row_ror
+template <int N>
+__device__ __forceinline__ float ror_add(float x) {
+    return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x120 + N, 0xF, 0xF, false));
+}
+// x + its partner 16 (resp. 32) lanes away: the two halves returned by the
+// gfx950 permlane swaps of (x, x) are {x, partner} in some order on every lane.
+__device__ __forceinline__ float xor16_add(float x) {
+    auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+__device__ __forceinline__ float xor32_add(float x) {
+    auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+// Sum over the G row-lanes that share a column chunk (lanes with equal lane % L);
+// every lane ends with its chunk's sum, bit-identical across those lanes.
+template <int L>
+__device__ __forceinline__ float row_sum(float x) {
+    if constexpr (L <= 8) x = ror_add<8>(x);
+    if constexpr (L <= 4) x = ror_add<4>(x);
+    if constexpr (L <= 2) x = ror_add<2>(x);
+    if constexpr (L <= 1) x = ror_add<1>(x);
+    x = xor16_add(x);
+    return xor32_add(x);
+}
+template <int L>
+__device__ __forceinline__ float4 row_sum4(float4 a) {
+    return make_float4(row_sum<L>(a.x), row_sum<L>(a.y), row_sum<L>(a.z), row_sum<L>(a.w));
+}
+
+template <int S, int FORM, bool VBF16>
+__global__ __launch_bounds__(MAX_WAVES * 64) void scan_kernel(
+    const uint8_t* __restrict__ plan, const void* __restrict__ v, float* M, float* __restrict__ y,
+    float* sink_base, int T, int64_t N, int dv, int nslab, int64_t NS, int NWW, int NWR) {
+    constexpr int L = S / 4, G = 64 / L;
+    constexpr int D = D_PF, DM = D_MT;
+    constexpr int U = D + DM + 1;   // register ring depth = unroll factor
+    constexpr int UR = D + 2;       // LDS ring of written rows (see the ring-reuse note below)
     using VL = VLoad<VBF16>;
     using V4 = typename VL::T4;
-    __shared__ float4 ring[U][NGX * G][L];
+    extern __shared__ float4 lds[];
+    const int NW = NWW + NWR;
+    float4* ring = lds;                                  // [UR][NWW*G][L]
+    float4* ybuf = lds + UR * NWW * G * L;               // [2][NWR][L]
+    float4* vbuf = ybuf + 2 * NWR * L;                   // [NWW][L]
 
-    const int lane = threadIdx.x, r = lane / L, cc = lane % L;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane / L, cc = lane % L;
     const int b = blockIdx.x, xcd = b & 7, kq = b >> 3;
     const int64_t s = (int64_t)(kq / nslab) * 8 + xcd;
     const int slab = kq % nslab;
-    if (s >= NS) return;
+    if (s >= NS) return;  // uniform over the workgroup
     const int col = slab * S + cc * 4;
-    float* Ms = M + s * N * dv + col;
-    const uint8_t* Ps = plan + s * T * REC + 16 + r * NG * 8;
-    const float2* Hs = reinterpret_cast<const float2*>(plan + s * T * REC);
-    const int64_t voff = s * T * dv + col;
-    float* ys = y + s * T * dv + col;
-    float* sink = sink_base + ((int64_t)blockIdx.x * 64 + lane) * 4;
+    const float* Mr = M + s * N * dv;                    // this stream's table (row base)
+    float* Mw = M + s * N * dv;
+    const int64_t REC = 16 + (int64_t)NW * G * 8;
+    const uint8_t* Pe = plan + s * (int64_t)T * REC + 16 + (int64_t)(wave * G + r) * 8;
+    const uint8_t* Ph = plan + s * (int64_t)T * REC;
+    const int64_t voff = s * (int64_t)T * dv + col;
+    float* ys = y + s * (int64_t)T * dv + col;
+    float* sink = sink_base + ((int64_t)blockIdx.x * (MAX_WAVES * 64) + threadIdx.x) * 4;
+    const bool writer = wave < NWW;
+    const int pos = wave * G + r;                        // write position of a writer lane
+    const int rw = wave - NWW;                           // reader index
 
-    struct Meta {
-        float2 ab;
-        int2 e[NG];
+    auto ring_at = [&](int slot, int p) -> float4& { return ring[((int64_t)slot * NWW * G + p) * L + cc]; };
+    auto load_entry = [&](int t) -> int2 { return *reinterpret_cast<const int2*>(Pe + (int64_t)t * REC); };
+    auto load_ab = [&](int t) -> float2 { return *reinterpret_cast<const float2*>(Ph + (int64_t)t * REC); };
+    auto load_row = [&](int2 e) -> float4 {
+        const uint32_t off = (((uint32_t)e.x & ROW_MASK) * (uint32_t)dv + (uint32_t)col);
+        return *reinterpret_cast<const float4*>(Mr + off);
     };
-    auto load_meta = [&](int64_t t, Meta& m) {
-        m.ab = Hs[t * (REC / 8)];
-        const int4* ep = reinterpret_cast<const int4*>(Ps + t * REC);
-#pragma unroll
-        for (int q = 0; q < NG / 2; ++q) {
-            const int4 w4 = ep[q];
-            m.e[2 * q] = make_int2(w4.x, w4.y);
-            m.e[2 * q + 1] = make_int2(w4.z, w4.w);
+    auto source = [&](int t, int2 e, float4 pre) -> float4 {
+        // forwarded rows come from the LDS ring; the ballot keeps the common
+        // no-forward case free of LDS traffic
+        const uint32_t pk = (uint32_t)e.x;
+        const bool f = (pk & (ENT_FWD | ENT_INVALID)) == ENT_FWD;
+        if (__ballot(f) != 0ull && f) {
+            const int d = (int)((pk >> DIST_SHIFT) & 15u);
+            const int p = (int)((pk >> POS_SHIFT) & 255u);
+            pre = ring_at((t - d) % UR, p);
         }
+        return pre;
     };
-    auto load_rows = [&](int64_t t, const Meta& m, float4 (&rw)[NG], V4& vt) {
-#pragma unroll
-        for (int g = 0; g < NG; ++g) {
-            const uint32_t row = (uint32_t)m.e[g].x & ROW_MASK;
-            rw[g] = *reinterpret_cast<const float4*>(Ms + (int64_t)row * dv);
-        }
-        vt = VL::load(v, voff + t * dv);
-    };
-    auto fwd_src = [&](int64_t t, uint32_t pk) -> float4 {
-        const int d = (int)((pk >> DIST_SHIFT) & 15u);
-        const int pos = (int)((pk >> POS_SHIFT) & 255u);
-        return ring[(int)((t - d) % U)][pos][cc];
-    };
-    auto process = [&](int64_t t, int slot, const Meta& m, const float4 (&rw)[NG], const V4& vt) {
-        const float alpha = m.ab.x, beta = m.ab.y;
-        const float4 vf = VL::f(vt);
-        // ---- write rows: decay (Eq. 3), delta correction (Eq. 4 or Fig. 2)
-        float4 src[NGX];
-        bool fw = false;
-#pragma unroll
-        for (int g = 0; g < NGX; ++g) {
-            src[g] = rw[g];
-            fw |= ((uint32_t)m.e[g].x & (ENT_FWD | ENT_INVALID)) == ENT_FWD;
-        }
-        if (__ballot(fw) != 0ull) {
-#pragma unroll
-            for (int g = 0; g < NGX; ++g) {
-                const uint32_t pk = (uint32_t)m.e[g].x;
-                if ((pk & (ENT_FWD | ENT_INVALID)) == ENT_FWD) src[g] = fwd_src(t, pk);
-            }
-        }
-        float4 mt[NGX];
-#pragma unroll
-        for (int g = 0; g < NGX; ++g) mt[g] = f4_scale(alpha, src[g]);
-        float4 vhat = make_float4(0.f, 0.f, 0.f, 0.f);
+
+    // one token of a writer wavefront (barriers: [B'_t], B_t)
+    auto write_token = [&](int t, int2 e, float2 ab, float4 pre, V4 vt) {
+        const uint32_t pk = (uint32_t)e.x;
+        const bool ok = (pk & ENT_INVALID) == 0u;
+        const float w = __int_as_float(e.y);
+        const float4 mt = f4_scale(ab.x, source(t, e, pre));
+        float4 pred = mt;
         if constexpr (FORM == 1) {
+            const float4 part = row_sum4<L>(f4_scale(ok ? w : 0.f, mt));
+            if (r == 0) vbuf[wave * L + cc] = part;
+            __syncthreads();
+            pred = vbuf[cc];
 #pragma unroll
-            for (int g = 0; g < NGX; ++g) {
-                const bool ok = ((uint32_t)m.e[g].x & ENT_INVALID) == 0u;
-                vhat = f4_fma(ok ? __int_as_float(m.e[g].y) : 0.f, mt[g], vhat);
-            }
-#pragma unroll
-            for (int msk = L; msk < 64; msk <<= 1) vhat = f4_add(vhat, f4_xor(vhat, msk));
+            for (int q = 1; q < MAX_WAVES; ++q)
+                if (q < NWW) pred = f4_add(pred, vbuf[q * L + cc]);
         }
+        const float4 nv = f4_fma(ab.y * w, f4_sub(VL::f(vt), pred), mt);
+        float* dst = ok ? Mw + (((pk & ROW_MASK) * (uint32_t)dv + (uint32_t)col)) : sink;
+        *reinterpret_cast<float4*>(dst) = nv;
+        ring_at(t % UR, pos) = nv;
+        __syncthreads();
+    };
+    // one token of a reader wavefront (barriers: [B'_t], B_t); the partial sums
+    // of token t are combined by reader 0 after the next barrier
+    auto read_token = [&](int t, int2 e, float4 pre) {
+        if constexpr (FORM == 1) __syncthreads();
+        __syncthreads();
+        const uint32_t pk = (uint32_t)e.x;
+        const float w = (pk & ENT_INVALID) == 0u ? __int_as_float(e.y) : 0.f;
+        const float4 part = row_sum4<L>(f4_scale(w, source(t, e, pre)));
+        if (r == 0) ybuf[((t & 1) * NWR + rw) * L + cc] = part;
+        // every reader sums the previous token's partials; reader 0 stores the
+        // result, the others (and token 0, which has no predecessor) hit the sink
+        const int pb = (t - 1) & 1;
+        float4 acc = ybuf[(pb * NWR) * L + cc];
 #pragma unroll
-        for (int g = 0; g < NGX; ++g) {
-            const uint32_t pk = (uint32_t)m.e[g].x;
-            const float bw = beta * __int_as_float(m.e[g].y);
-            const float4 res = f4_sub(vf, FORM == 1 ? vhat : mt[g]);
-            const float4 nv = f4_fma(bw, res, mt[g]);
-            // masked lanes store into this wavefront's sink instead of branching, so
-            // every iteration issues the same memory operations (exact vmcnt waits)
-            float* dst = (pk & ENT_INVALID) == 0u ? Ms + (int64_t)(pk & ROW_MASK) * dv : sink;
-            *reinterpret_cast<float4*>(dst) = nv;
-            ring[slot][g * G + r][cc] = nv;
-        }
-        // ---- read rows (Eq. 5), after this token's writes
-        float4 rs[NGX];
-        bool fr = false;
-#pragma unroll
-        for (int g = 0; g < NGX; ++g) {
-            rs[g] = rw[NGX + g];
-            fr |= ((uint32_t)m.e[NGX + g].x & (ENT_FWD | ENT_INVALID)) == ENT_FWD;
-        }
-        if (__ballot(fr) != 0ull) {
-#pragma unroll
-            for (int g = 0; g < NGX; ++g) {
-                const uint32_t pk = (uint32_t)m.e[NGX + g].x;
-                if ((pk & (ENT_FWD | ENT_INVALID)) == ENT_FWD) rs[g] = fwd_src(t, pk);
-            }
-        }
-        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-        for (int g = 0; g < NGX; ++g) {
-            const bool ok = ((uint32_t)m.e[NGX + g].x & ENT_INVALID) == 0u;
-            acc = f4_fma(ok ? __int_as_float(m.e[NGX + g].y) : 0.f, rs[g], acc);
-        }
-#pragma unroll
-        for (int msk = L; msk < 64; msk <<= 1) acc = f4_add(acc, f4_xor(acc, msk));
-        // the butterfly leaves the same sum on every lane of a column chunk: all store it
-        *reinterpret_cast<float4*>(ys + t * dv) = acc;
+        for (int q = 1; q < MAX_WAVES; ++q)
+            if (q < NWR) acc = f4_add(acc, ybuf[(pb * NWR + q) * L + cc]);
+        float* dst = (rw == 0 && t > 0) ? ys + (int64_t)(t - 1) * dv : sink;
+        *reinterpret_cast<float4*>(dst) = acc;
     };
 
-    int64_t t_done = 0;
+    // Main loop: U tokens per trip, fully unrolled so that the register rings
+    // are statically indexed. Each role gets its own prologue that issues the
+    // steady-state sequence of loads (with a sink store standing in for each
+    // token's store), so that the loop header merges like states and the
+    // compiler's memory waits stay D tokens deep.
+    int t_done = 0;
     if (T >= U) {
-        Meta meta[U];
-        float4 rows[U][NG];
-        V4 vv[U];
+        int2 ent[U];
+        float4 pre[U];
+        if (writer) {
+            float2 ab[U];
+            V4 vv[U];
 #pragma unroll
-        for (int q = 0; q < D + DM; ++q) load_meta(q < T ? q : T - 1, meta[q]);
-        // keep the plan loads ahead of the row loads: the first loop iteration then
-        // waits only for its own data, as every later one does
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int q = 0; q < D; ++q) load_rows(q, meta[q], rows[q], vv[q]);
-        __builtin_amdgcn_sched_barrier(0);
-        for (int64_t t0 = 0; t0 + U <= T; t0 += U) {
-#pragma unroll
-            for (int j = 0; j < U; ++j) {
-                const int64_t t = t0 + j;
-                const int64_t tm = t + D + DM < T ? t + D + DM : T - 1;
-                load_meta(tm, meta[(j + D + DM) % U]);
-                const int64_t tr = t + D < T ? t + D : T - 1;
-                load_rows(tr, meta[(j + D) % U], rows[(j + D) % U], vv[(j + D) % U]);
-                process(t, j, meta[j], rows[j], vv[j]);
+            for (int q = 0; q < D + DM; ++q) {
+                ent[q] = load_entry(q);
+                ab[q] = load_ab(q);
+                if (q >= DM) {
+                    pre[q - DM] = load_row(ent[q - DM]);
+                    vv[q - DM] = VL::load(v, voff + (int64_t)(q - DM) * dv);
+                }
+                *reinterpret_cast<float4*>(sink) = make_float4(0.f, 0.f, 0.f, 0.f);
             }
-            t_done = t0 + U;
+            for (int t0 = 0; t0 + U <= T; t0 += U) {
+#pragma unroll
+                for (int j = 0; j < U; ++j) {
+                    const int t = t0 + j;
+                    const int tm = t + D + DM < T ? t + D + DM : T - 1;
+                    ent[(j + D + DM) % U] = load_entry(tm);
+                    ab[(j + D + DM) % U] = load_ab(tm);
+                    const int tr = t + D < T ? t + D : T - 1;
+                    pre[(j + D) % U] = load_row(ent[(j + D) % U]);
+                    vv[(j + D) % U] = VL::load(v, voff + (int64_t)tr * dv);
+                    write_token(t, ent[j], ab[j], pre[j], vv[j]);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int q = 0; q < D + DM; ++q) {
+                ent[q] = load_entry(q);
+                if (q >= DM) pre[q - DM] = load_row(ent[q - DM]);
+                *reinterpret_cast<float4*>(sink) = make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+            for (int t0 = 0; t0 + U <= T; t0 += U) {
+#pragma unroll
+                for (int j = 0; j < U; ++j) {
+                    const int t = t0 + j;
+                    const int tm = t + D + DM < T ? t + D + DM : T - 1;
+                    ent[(j + D + DM) % U] = load_entry(tm);
+                    pre[(j + D) % U] = load_row(ent[(j + D) % U]);
+                    read_token(t, ent[j], pre[j]);
+                }
+            }
         }
+        t_done = (T / U) * U;
     }
     // tail (and short sequences): loads right before use; forwarding stays valid
-    for (int64_t t = t_done; t < T; ++t) {
-        Meta m;
-        float4 rw[NG];
-        V4 vt;
-        load_meta(t, m);
-        load_rows(t, m, rw, vt);
-        process(t, (int)(t % U), m, rw, vt);
+    for (int t = t_done; t < T; ++t) {
+        const int2 e = load_entry(t);
+        const float4 pre = load_row(e);
+        if (writer) write_token(t, e, load_ab(t), pre, VL::load(v, voff + (int64_t)t * dv));
+        else read_token(t, e, pre);
+    }
+    // the last token's partial sums
+    __syncthreads();
+    if (!writer && rw == 0 && T > 0) {
+        const int pb = (T - 1) & 1;
+        float4 acc = ybuf[(pb * NWR) * L + cc];
+        for (int q = 1; q < NWR; ++q) acc = f4_add(acc, ybuf[(pb * NWR + q) * L + cc]);
+        *reinterpret_cast<float4*>(ys + (int64_t)(T - 1) * dv) = acc;
     }
 }
+// Ring reuse: the writer of token t overwrites slot t % UR, last used by token
+// t - UR; its readers (tokens up to t - UR + D) have finished once every
+// wavefront passed barrier B_{t-1}, which needs t - UR + D <= t - 2, so UR = D + 2.
 
-template <int S, int NGX, int D, int DM>
-hipError_t launch_scan_inst(const ScanArgs& a, hipStream_t st) {
-    const int G = 64 / (S / 4);
+size_t scan_lds_bytes(const Geom& g) {
+    const int L = g.S / 4;
+    return ((size_t)(D_PF + 2) * g.NWW * g.G * L + 2 * g.NWR * L + g.NWW * L) * 16;
+}
+
+template <int S>
+hipError_t launch_scan_slab(const ScanArgs& a, const Geom& g, hipStream_t st) {
     // planner: tiles of TT tokens; the hash table holds the writes of TT + D tokens at load <= 1/2
-    int TT = HT_CAP / (2 * a.W) - D;
+    int TT = HT_CAP / (2 * a.W) - D_PF;
     if (TT < 1) TT = 1;
     const int64_t ntile = (a.T + TT - 1) / TT;
     uint8_t* plan = static_cast<uint8_t*>(a.workspace);
     hipLaunchKernelGGL(plan_kernel, dim3((unsigned)(ntile * a.NS)), dim3(256), 0, st, a.idx_w, a.wt_w, a.W,
-                       a.idx_r, a.wt_r, a.R, a.alpha, a.beta, plan, a.T, a.N, D, G, NGX, TT, ntile);
+                       a.idx_r, a.wt_r, a.R, a.alpha, a.beta, plan, a.T, a.N, D_PF, g.G, g.NWW, g.NWR, TT,
+                       ntile);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int nslab = a.dv / S;
     const int64_t nblk = ((a.NS + 7) / 8) * 8 * nslab;
-    float* sink = reinterpret_cast<float*>(plan + a.NS * a.T * rec_bytes(S, NGX));
-    dim3 grid((unsigned)nblk);
-#define SDM_LAUNCH(FORM, VB)                                                                            \
-    hipLaunchKernelGGL((scan_kernel<S, NGX, D, DM, FORM, VB>), grid, dim3(64), 0, st, plan, a.v, a.M, \
-                       a.y, sink, a.T, a.N, a.dv, nslab, a.NS)
+    float* sink = reinterpret_cast<float*>(plan + a.NS * a.T * g.rec());
+    const size_t lds = scan_lds_bytes(g);
+    dim3 grid((unsigned)nblk), block((unsigned)(g.nw() * 64));
+#define SDM_LAUNCH(FORM, VB)                                                                          \
+    hipLaunchKernelGGL((scan_kernel<S, FORM, VB>), grid, block, lds, st, plan, a.v, a.M, a.y, sink, \
+                       (int)a.T, a.N, a.dv, nslab, a.NS, g.NWW, g.NWR)
     if (a.form == 0) {
         if (a.v_bf16) SDM_LAUNCH(0, true); else SDM_LAUNCH(0, false);
     } else {
@@ -367,27 +423,34 @@ hipError_t launch_scan_inst(const ScanArgs& a, hipStream_t st) {
     return hipGetLastError();
 }
 
-int pick_instance(int W, int R, int dv) {
-    const int K = W > R ? W : R;
+// Slab width: SDM_SCAN_SLAB forces one; otherwise the widest slab (fewest
+// requests per byte) whose groups of G rows tile W and R without padding, then
+// the one with the least padding.
+int pick_slab(int W, int R, int dv) {
     int forced = 0;
     if (const char* e = getenv("SDM_SCAN_SLAB")) forced = atoi(e);
-    for (int i = 0; i < (int)(sizeof(kInst) / sizeof(kInst[0])); ++i) {
-        const Inst& in = kInst[i];
-        const int G = 64 / (in.S / 4);
-        if (K > in.NGX * G || dv % in.S != 0) continue;
-        if (forced && forced != in.S) continue;
-        return i;
+    int best = 0;
+    long best_waste = -1;
+    for (int S : {32, 16, 8, 4}) {
+        if (dv % S != 0 || (forced && forced != S)) continue;
+        const Geom g = make_geom(S, W, R);
+        if (g.nw() > MAX_WAVES) continue;
+        const long waste = (long)g.NWW * g.G - W + (long)g.NWR * g.G - R;
+        if (best_waste < 0 || waste < best_waste) {
+            best = S;
+            best_waste = waste;
+        }
     }
-    return -1;
+    return best;
 }
 
 }  // namespace
 
 bool scan_geometry(int W, int R, int dv, int* slab, int* rec) {
-    const int i = pick_instance(W, R, dv);
-    if (i < 0) return false;
-    if (slab) *slab = kInst[i].S;
-    if (rec) *rec = rec_bytes(kInst[i].S, kInst[i].NGX);
+    const int S = pick_slab(W, R, dv);
+    if (S == 0) return false;
+    if (slab) *slab = S;
+    if (rec) *rec = (int)make_geom(S, W, R).rec();
     return true;
 }
 
@@ -395,17 +458,18 @@ int64_t scan_workspace_bytes(int64_t NS, int64_t T, int W, int R, int dv) {
     int rec = 0, S = 0;
     if (!scan_geometry(W, R, dv, &S, &rec)) return -1;
     const int64_t nblk = ((NS + 7) / 8) * 8 * (dv / S);
-    return NS * T * rec + nblk * 64 * 16;  // plan records + one 16-byte sink per lane
+    return NS * T * rec + nblk * MAX_WAVES * 64 * 16;  // plan records + one 16-byte sink per thread
 }
 
 hipError_t launch_scan(const ScanArgs& a, hipStream_t st) {
-    switch (pick_instance(a.W, a.R, a.dv)) {
-        case 0: return launch_scan_inst<32, 1, 6, 3>(a, st);
-        case 1: return launch_scan_inst<16, 1, 6, 3>(a, st);
-        case 2: return launch_scan_inst<8, 2, 3, 2>(a, st);
-        case 3: return launch_scan_inst<4, 1, 6, 3>(a, st);
-        case 4: return launch_scan_inst<4, 4, 2, 1>(a, st);
-        default: return hipErrorInvalidValue;
+    const int S = pick_slab(a.W, a.R, a.dv);
+    if (S == 0) return hipErrorInvalidValue;
+    const Geom g = make_geom(S, a.W, a.R);
+    switch (S) {
+        case 32: return launch_scan_slab<32>(a, g, st);
+        case 16: return launch_scan_slab<16>(a, g, st);
+        case 8: return launch_scan_slab<8>(a, g, st);
+        default: return launch_scan_slab<4>(a, g, st);
     }
 }
 

@@ -47,9 +47,10 @@ def test_abi_version_and_status_strings(lib):
 
 
 def test_workspace_size_is_pure_host_logic(lib):
-    # W = R = 64, dv = 128: 16-byte header + 32 rows x 4 groups x 8 bytes per token
-    # record, plus one 16-byte sink per lane of each of the 8*ceil(32/8)*16 wavefronts
-    assert binding.sdm_scan_workspace_bytes(4, 8, 8192, 64, 64, 128) == 32 * 8192 * 1040 + 512 * 64 * 16
+    # W = R = 64, dv = 128 -> 16-column slabs: 16 rows per wavefront, 4 writer + 4
+    # reader wavefronts; a token record is a 16-byte header + 8 x 16 entries of 8
+    # bytes, plus a 16-byte sink per thread of the 8*ceil(32/8)*8 workgroups of 512
+    assert binding.sdm_scan_workspace_bytes(4, 8, 8192, 64, 64, 128) == 32 * 8192 * 1040 + 256 * 512 * 16
     assert binding.sdm_scan_workspace_bytes(0, 8, 8192, 64, 64, 128) == 0
     assert lib.sdm_scan_workspace_bytes(1, 1, 1, 0, 1, 16) == -1
     assert lib.sdm_scan_workspace_bytes(1, 1, 1, 300, 1, 16) == -1
