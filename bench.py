@@ -41,6 +41,9 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="target CPU time of the oracle baseline sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                   help="run one plain device copy of BYTES bytes before the benchmark "
+                        "(a known-size kernel that calibrates HBM byte counters)")
     return p.parse_args()
 
 
@@ -110,6 +113,12 @@ def main():
     from sparse_memory_linear_amd import inputs
 
     dev = torch.device("cuda:0")
+    if a.copy_probe > 0:
+        src = torch.ones(a.copy_probe // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     wl = inputs.get(a.workload)
     x = inputs.make_inputs(wl)
     g = {k: v.to(dev) for k, v in x.items()}

@@ -42,11 +42,22 @@ constexpr uint32_t ROW_MASK = (1u << 18) - 1u;
 constexpr int POS_SHIFT = 18;               // write position of the source (8 bits)
 constexpr int DIST_SHIFT = 26;              // token distance of the source (4 bits)
 
-constexpr int D_PF = 10;  // tokens of row loads in flight per wavefront
-constexpr int D_MT = 10;  // extra lead of the plan-entry loads; memory counters complete in
-                          // order, so waiting on an entry also waits on every older row load:
-                          // the lead must be >= D_PF to keep D_PF tokens of rows in flight
-constexpr int MAX_WAVES = 8;
+// Per slab width: D = tokens of row loads in flight per wavefront; the plan
+// entries lead by another D + 1 tokens (memory counters complete in order, so
+// waiting on an entry also waits on every older row load: a lead >= D keeps D
+// tokens of rows in flight); NWMAX = wavefronts per workgroup (sets the VGPR
+// budget: 8 -> 256, 16 -> 128). 32-column slabs move whole 128-byte lines per
+// row: on MI355X random 128-byte accesses sustain ~1.4x the bandwidth of 64-byte
+// ones.
+template <int S>
+struct SlabCfg {
+    static constexpr int D = 10, NWMAX = 8;
+};
+template <>
+struct SlabCfg<32> {
+    static constexpr int D = 6, NWMAX = 16;
+};
+constexpr int MAX_WAVES = 16;   // largest NWMAX
 
 // Geometry of a slab of S fp32 columns: L = S/4 lanes per row segment (16 B
 // each), G = 64/L rows per wavefront; NWW = ceil(W/G) writer and NWR = ceil(R/G)
@@ -219,12 +230,16 @@ __device__ __forceinline__ float4 row_sum4(float4 a) {
 }
 
 template <int S, int FORM, bool VBF16>
-__global__ __launch_bounds__(MAX_WAVES * 64) void scan_kernel(
+__global__ __launch_bounds__(SlabCfg<S>::NWMAX * 64) void scan_kernel(
     const uint8_t* __restrict__ plan, const void* __restrict__ v, float* M, float* __restrict__ y,
     float* sink_base, int T, int64_t N, int dv, int nslab, int64_t NS, int NWW, int NWR) {
     constexpr int L = S / 4, G = 64 / L;
-    constexpr int D = D_PF, DM = D_MT;
-    constexpr int U = D + DM + 1;   // register ring depth = unroll factor
+    constexpr int D = SlabCfg<S>::D, NWMAX = SlabCfg<S>::NWMAX;
+    constexpr int DM = D + 1;       // plan-entry lead beyond D
+    constexpr int UP = D + 1;       // row / value register rings: D in flight + the one in use
+    constexpr int U = D + DM + 1;   // plan-entry ring = unroll factor (a multiple of UP, so
+                                    // every ring index is static in the unrolled loop)
+    static_assert(U % UP == 0, "ring sizes");
     constexpr int UR = D + 2;       // LDS ring of written rows (see the ring-reuse note below)
     using VL = VLoad<VBF16>;
     using V4 = typename VL::T4;
@@ -285,7 +300,7 @@ __global__ __launch_bounds__(MAX_WAVES * 64) void scan_kernel(
             __syncthreads();
             pred = vbuf[cc];
 #pragma unroll
-            for (int q = 1; q < MAX_WAVES; ++q)
+            for (int q = 1; q < NWMAX; ++q)
                 if (q < NWW) pred = f4_add(pred, vbuf[q * L + cc]);
         }
         const float4 nv = f4_fma(ab.y * w, f4_sub(VL::f(vt), pred), mt);
@@ -308,7 +323,7 @@ __global__ __launch_bounds__(MAX_WAVES * 64) void scan_kernel(
         const int pb = (t - 1) & 1;
         float4 acc = ybuf[(pb * NWR) * L + cc];
 #pragma unroll
-        for (int q = 1; q < MAX_WAVES; ++q)
+        for (int q = 1; q < NWMAX; ++q)
             if (q < NWR) acc = f4_add(acc, ybuf[(pb * NWR + q) * L + cc]);
         float* dst = (rw == 0 && t > 0) ? ys + (int64_t)(t - 1) * dv : sink;
         *reinterpret_cast<float4*>(dst) = acc;
@@ -322,10 +337,10 @@ __global__ __launch_bounds__(MAX_WAVES * 64) void scan_kernel(
     int t_done = 0;
     if (T >= U) {
         int2 ent[U];
-        float4 pre[U];
+        float4 pre[UP];
         if (writer) {
             float2 ab[U];
-            V4 vv[U];
+            V4 vv[UP];
 #pragma unroll
             for (int q = 0; q < D + DM; ++q) {
                 ent[q] = load_entry(q);
@@ -344,9 +359,9 @@ __global__ __launch_bounds__(MAX_WAVES * 64) void scan_kernel(
                     ent[(j + D + DM) % U] = load_entry(tm);
                     ab[(j + D + DM) % U] = load_ab(tm);
                     const int tr = t + D < T ? t + D : T - 1;
-                    pre[(j + D) % U] = load_row(ent[(j + D) % U]);
-                    vv[(j + D) % U] = VL::load(v, voff + (int64_t)tr * dv);
-                    write_token(t, ent[j], ab[j], pre[j], vv[j]);
+                    pre[(j + D) % UP] = load_row(ent[(j + D) % U]);
+                    vv[(j + D) % UP] = VL::load(v, voff + (int64_t)tr * dv);
+                    write_token(t, ent[j], ab[j], pre[j % UP], vv[j % UP]);
                 }
             }
         } else {
@@ -362,8 +377,8 @@ __global__ __launch_bounds__(MAX_WAVES * 64) void scan_kernel(
                     const int t = t0 + j;
                     const int tm = t + D + DM < T ? t + D + DM : T - 1;
                     ent[(j + D + DM) % U] = load_entry(tm);
-                    pre[(j + D) % U] = load_row(ent[(j + D) % U]);
-                    read_token(t, ent[j], pre[j]);
+                    pre[(j + D) % UP] = load_row(ent[(j + D) % U]);
+                    read_token(t, ent[j], pre[j % UP]);
                 }
             }
         }
@@ -389,27 +404,30 @@ __global__ __launch_bounds__(MAX_WAVES * 64) void scan_kernel(
 // t - UR; its readers (tokens up to t - UR + D) have finished once every
 // wavefront passed barrier B_{t-1}, which needs t - UR + D <= t - 2, so UR = D + 2.
 
+template <int S>
 size_t scan_lds_bytes(const Geom& g) {
-    const int L = g.S / 4;
-    return ((size_t)(D_PF + 2) * g.NWW * g.G * L + 2 * g.NWR * L + g.NWW * L) * 16;
+    const int L = S / 4;
+    return ((size_t)(SlabCfg<S>::D + 2) * g.NWW * g.G * L + 2 * g.NWR * L + g.NWW * L) * 16;
 }
 
 template <int S>
 hipError_t launch_scan_slab(const ScanArgs& a, const Geom& g, hipStream_t st) {
+    constexpr int D = SlabCfg<S>::D;
+    static_assert(D <= 15, "the plan stores forward distances in 4 bits");
     // planner: tiles of TT tokens; the hash table holds the writes of TT + D tokens at load <= 1/2
-    int TT = HT_CAP / (2 * a.W) - D_PF;
+    int TT = HT_CAP / (2 * a.W) - D;
     if (TT < 1) TT = 1;
     const int64_t ntile = (a.T + TT - 1) / TT;
     uint8_t* plan = static_cast<uint8_t*>(a.workspace);
     hipLaunchKernelGGL(plan_kernel, dim3((unsigned)(ntile * a.NS)), dim3(256), 0, st, a.idx_w, a.wt_w, a.W,
-                       a.idx_r, a.wt_r, a.R, a.alpha, a.beta, plan, a.T, a.N, D_PF, g.G, g.NWW, g.NWR, TT,
+                       a.idx_r, a.wt_r, a.R, a.alpha, a.beta, plan, a.T, a.N, D, g.G, g.NWW, g.NWR, TT,
                        ntile);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int nslab = a.dv / S;
     const int64_t nblk = ((a.NS + 7) / 8) * 8 * nslab;
     float* sink = reinterpret_cast<float*>(plan + a.NS * a.T * g.rec());
-    const size_t lds = scan_lds_bytes(g);
+    const size_t lds = scan_lds_bytes<S>(g);
     dim3 grid((unsigned)nblk), block((unsigned)(g.nw() * 64));
 #define SDM_LAUNCH(FORM, VB)                                                                          \
     hipLaunchKernelGGL((scan_kernel<S, FORM, VB>), grid, block, lds, st, plan, a.v, a.M, a.y, sink, \
@@ -423,31 +441,48 @@ hipError_t launch_scan_slab(const ScanArgs& a, const Geom& g, hipStream_t st) {
     return hipGetLastError();
 }
 
-// Slab width: SDM_SCAN_SLAB forces one; otherwise the widest slab (fewest
-// requests per byte) whose groups of G rows tile W and R without padding, then
-// the one with the least padding.
-int pick_slab(int W, int R, int dv) {
+int slab_nwmax(int S) { return S == 32 ? SlabCfg<32>::NWMAX : SlabCfg<16>::NWMAX; }
+
+// Slab width: SDM_SCAN_SLAB forces one. Otherwise, among the widths whose groups
+// of G rows tile W and R without padding and that need at most 8 wavefronts
+// (the 16-wavefront form has a shallower pipeline), the widest one that still
+// gives at least 128 workgroups (half the CUs): wider slabs move longer row
+// segments, narrower ones give more independent workgroups. Failing that, the
+// width with the most workgroups, then the one with the least padding.
+// (Measured on the N=65536, W=R=64, d_v=128 shapes: 32 streams -> 16 columns,
+// 8 streams -> 8 columns.)
+int pick_slab(int64_t NS, int W, int R, int dv) {
     int forced = 0;
     if (const char* e = getenv("SDM_SCAN_SLAB")) forced = atoi(e);
-    int best = 0;
-    long best_waste = -1;
+    struct Cand {
+        int S;
+        long waste, units;
+        int nw;
+    };
+    auto better = [](const Cand& a, const Cand& b) {
+        if ((a.waste == 0) != (b.waste == 0)) return a.waste == 0;
+        if ((a.nw <= 8) != (b.nw <= 8)) return a.nw <= 8;
+        const bool ea = a.units >= 128, eb = b.units >= 128;
+        if (ea != eb) return ea;
+        if (ea) return a.S > b.S;
+        if (a.units != b.units) return a.units > b.units;
+        return a.waste < b.waste;
+    };
+    Cand best{0, 0, 0, 0};
     for (int S : {32, 16, 8, 4}) {
         if (dv % S != 0 || (forced && forced != S)) continue;
         const Geom g = make_geom(S, W, R);
-        if (g.nw() > MAX_WAVES) continue;
-        const long waste = (long)g.NWW * g.G - W + (long)g.NWR * g.G - R;
-        if (best_waste < 0 || waste < best_waste) {
-            best = S;
-            best_waste = waste;
-        }
+        if (g.nw() > slab_nwmax(S)) continue;
+        const Cand c{S, (long)g.NWW * g.G - W + (long)g.NWR * g.G - R, (long)NS * (dv / S), g.nw()};
+        if (best.S == 0 || better(c, best)) best = c;
     }
-    return best;
+    return best.S;
 }
 
 }  // namespace
 
-bool scan_geometry(int W, int R, int dv, int* slab, int* rec) {
-    const int S = pick_slab(W, R, dv);
+bool scan_geometry(int64_t NS, int W, int R, int dv, int* slab, int* rec) {
+    const int S = pick_slab(NS, W, R, dv);
     if (S == 0) return false;
     if (slab) *slab = S;
     if (rec) *rec = (int)make_geom(S, W, R).rec();
@@ -456,13 +491,13 @@ bool scan_geometry(int W, int R, int dv, int* slab, int* rec) {
 
 int64_t scan_workspace_bytes(int64_t NS, int64_t T, int W, int R, int dv) {
     int rec = 0, S = 0;
-    if (!scan_geometry(W, R, dv, &S, &rec)) return -1;
+    if (!scan_geometry(NS, W, R, dv, &S, &rec)) return -1;
     const int64_t nblk = ((NS + 7) / 8) * 8 * (dv / S);
     return NS * T * rec + nblk * MAX_WAVES * 64 * 16;  // plan records + one 16-byte sink per thread
 }
 
 hipError_t launch_scan(const ScanArgs& a, hipStream_t st) {
-    const int S = pick_slab(a.W, a.R, a.dv);
+    const int S = pick_slab(a.NS, a.W, a.R, a.dv);
     if (S == 0) return hipErrorInvalidValue;
     const Geom g = make_geom(S, a.W, a.R);
     switch (S) {

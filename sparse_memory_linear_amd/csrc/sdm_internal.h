@@ -34,7 +34,7 @@ struct ScanArgs {
     void* workspace;
 };
 // Chooses the kernel instance; returns false if no instance covers (W, R, dv).
-bool scan_geometry(int W, int R, int dv, int* slab, int* rec_bytes);
+bool scan_geometry(int64_t NS, int W, int R, int dv, int* slab, int* rec_bytes);
 int64_t scan_workspace_bytes(int64_t NS, int64_t T, int W, int R, int dv);
 hipError_t launch_scan(const ScanArgs& a, hipStream_t st);
 
