@@ -8,7 +8,7 @@
 // candidates are selected and weighted by a softmax over their scores.
 // Ties go to the lower index (sub-index per half, slot index at the end).
 //
-// Design (one wavefront per workgroup, 16 tokens of one (b, h, branch)):
+// Design (one workgroup of NWA = 4 wavefronts per 16 tokens of one (b, h, branch)):
 //   a1  half-scores: a [16 tokens x d_h] x [d_h x 16 subkeys] MFMA tile per
 //       step (v_mfma_f32_16x16x32_bf16 for bf16 inputs, 16x16x4 f32 for fp32),
 //       fp32 accumulation, staged in LDS as [token][half][subkey].
@@ -26,12 +26,20 @@
 //       score (a tie that the slot order could decide differently), the token
 //       is redone over the full k_h x k_h grid.
 //   a4  softmax in fp32 (max-subtracted, expf), butterfly sum.
+// The wavefronts share the MFMA tiles of a1; then each selects TG = 4 tokens.
+// The selection is a chain of dependent wave-wide steps, so the 4 tokens are
+// carried through it together (independent chains interleave), and every
+// cross-lane exchange uses DPP or the gfx950 permlane swaps instead of LDS.
+// Two workgroups fit a CU's LDS, i.e. two wavefronts per SIMD, so one
+// wavefront's scalar (ballot/popcount) work overlaps another's vector work.
 #include "sdm_internal.h"
 
 namespace sdm {
 namespace {
 
-constexpr int TOK = 16;       // tokens per wavefront = one MFMA M tile
+constexpr int TOK = 16;       // tokens per workgroup = one MFMA M tile
+constexpr int TG = 4;         // tokens selected together by one wavefront
+constexpr int NWA = TOK / TG; // wavefronts per workgroup
 constexpr int EC = 5;         // candidate chunks per lane: sum_{i<=64} floor(64/i) = 280 <= 320
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
@@ -55,91 +63,160 @@ __device__ __forceinline__ int lanes_below(uint64_t m) {
                                           __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t x, int m) {
-    const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)x, m);
-    const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(x >> 32), m);
-    return ((uint64_t)hi << 32) | lo;
+// Value of lane (lane ^ M), without LDS: DPP quad permutes (1, 2), DPP row
+// shifts (4), DPP row rotate (8), gfx950 permlane swaps (16, 32).
+template <int M>
+__device__ __forceinline__ uint32_t xlane(uint32_t x, int lane) {
+    if constexpr (M == 1) {
+        return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, false);  // quad_perm 1,0,3,2
+    } else if constexpr (M == 2) {
+        return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x4E, 0xF, 0xF, false);  // quad_perm 2,3,0,1
+    } else if constexpr (M == 4) {
+        const uint32_t up = (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x104, 0xF, 0xF, false);  // row_shl:4
+        const uint32_t dn = (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x114, 0xF, 0xF, false);  // row_shr:4
+        return (lane & 4) ? dn : up;
+    } else if constexpr (M == 8) {
+        return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x128, 0xF, 0xF, false);  // row_ror:8
+    } else if constexpr (M == 16) {
+        auto p = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+        return (lane & 16) ? p[0] : p[1];
+    } else {
+        auto p = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+        return (lane & 32) ? p[0] : p[1];
+    }
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
+template <int M>
+__device__ __forceinline__ uint64_t xlane64(uint64_t x, int lane) {
+    return ((uint64_t)xlane<M>((uint32_t)(x >> 32), lane) << 32) | xlane<M>((uint32_t)x, lane);
+}
+
+template <int M>
+__device__ __forceinline__ float xlanef(float x, int lane) {
+    return __uint_as_float(xlane<M>(__float_as_uint(x), lane));
+}
+
+__device__ __forceinline__ float wave_sum(float v, int lane) {
+    v += xlanef<32>(v, lane);
+    v += xlanef<16>(v, lane);
+    v += xlanef<8>(v, lane);
+    v += xlanef<4>(v, lane);
+    v += xlanef<2>(v, lane);
+    v += xlanef<1>(v, lane);
     return v;  // the butterfly adds the same pairs on every lane: identical on all lanes
 }
 
-// Select the k best candidates (larger key first, then smaller id) among
-// candidates c = e*64 + lane, e < nch, read through get(e, key, id). Key 0
-// marks an absent candidate; ids are below 2^18. Exactly k winners (k <= number
-// of present candidates) are written in candidate order to okey/oid[0..k).
-template <int NCH, typename Get>
-__device__ void wave_select(Get get, int nch_rt, int k, uint32_t* okey, uint32_t* oid, int lane) {
+// Select, for each of the NT token-chains g, the k best candidates (larger key
+// first, then smaller id) among candidates c = e*64 + lane, e < nch, read
+// through get(g, e, key, id). Key 0 marks an absent candidate; ids are below
+// 2^18. Exactly k winners (k <= number of present candidates) are written in
+// candidate order to okey/oid[g*64 + 0..k).
+template <int NT, int NCH, typename Get>
+__device__ __forceinline__ void wave_select(Get get, int nch_rt, int k, uint32_t* okey, uint32_t* oid,
+                                            int lane) {
     const int nch = NCH > 0 ? NCH : nch_rt;
-    uint32_t tau = 0u;
+    uint32_t tau[NT];
+#pragma unroll
+    for (int g = 0; g < NT; ++g) tau[g] = 0u;
     for (int bit = 31; bit >= 0; --bit) {
-        const uint32_t cand = tau | (1u << bit);
-        int cnt = 0;
+        int cnt[NT];
+#pragma unroll
+        for (int g = 0; g < NT; ++g) cnt[g] = 0;
+#pragma unroll
+        for (int e = 0; e < nch; ++e) {
+#pragma unroll
+            for (int g = 0; g < NT; ++g) {
+                uint32_t kk, ii;
+                get(g, e, kk, ii);
+                cnt[g] += popc(__ballot(kk >= (tau[g] | (1u << bit))));
+            }
+        }
+#pragma unroll
+        for (int g = 0; g < NT; ++g)
+            if (cnt[g] >= k) tau[g] |= 1u << bit;
+    }
+    int need[NT];
+    bool cut[NT], any_cut = false;
+#pragma unroll
+    for (int g = 0; g < NT; ++g) {
+        int gt = 0, eq = 0;
 #pragma unroll
         for (int e = 0; e < nch; ++e) {
             uint32_t kk, ii;
-            get(e, kk, ii);
-            cnt += popc(__ballot(kk >= cand));
+            get(g, e, kk, ii);
+            gt += popc(__ballot(kk > tau[g]));
+            eq += popc(__ballot(kk == tau[g]));
         }
-        if (cnt >= k) tau = cand;
+        need[g] = k - gt;
+        cut[g] = eq > need[g];  // more ties at the threshold than places left
+        any_cut |= cut[g];
     }
-    int gt = 0, eq = 0;
+    uint32_t sig[NT];
 #pragma unroll
-    for (int e = 0; e < nch; ++e) {
-        uint32_t kk, ii;
-        get(e, kk, ii);
-        gt += popc(__ballot(kk > tau));
-        eq += popc(__ballot(kk == tau));
-    }
-    const int need = k - gt;
-    const bool cut = eq > need;  // more ties at the threshold than places left
-    uint32_t sig = 0u;
-    if (cut) {
+    for (int g = 0; g < NT; ++g) sig[g] = 0u;
+    if (any_cut) {  // rare: exact ties at the threshold; keep the lowest ids
         for (int bit = 17; bit >= 0; --bit) {
-            const uint32_t cand = sig | (1u << bit);
-            int cnt = 0;
+            int cnt[NT];
+#pragma unroll
+            for (int g = 0; g < NT; ++g) cnt[g] = 0;
 #pragma unroll
             for (int e = 0; e < nch; ++e) {
-                uint32_t kk, ii;
-                get(e, kk, ii);
-                cnt += popc(__ballot(kk == tau && (0x3FFFFu - ii) >= cand));
+#pragma unroll
+                for (int g = 0; g < NT; ++g) {
+                    uint32_t kk, ii;
+                    get(g, e, kk, ii);
+                    cnt[g] += popc(__ballot(kk == tau[g] && (0x3FFFFu - ii) >= (sig[g] | (1u << bit))));
+                }
             }
-            if (cnt >= need) sig = cand;
+#pragma unroll
+            for (int g = 0; g < NT; ++g)
+                if (cnt[g] >= need[g]) sig[g] |= 1u << bit;
         }
     }
-    int base = 0;
 #pragma unroll
-    for (int e = 0; e < nch; ++e) {
-        uint32_t kk, ii;
-        get(e, kk, ii);
-        const bool sel = kk > tau || (kk == tau && (!cut || (0x3FFFFu - ii) >= sig));
-        const uint64_t m = __ballot(sel);
-        if (sel) {
-            const int pos = base + lanes_below(m);
-            okey[pos] = kk;
-            oid[pos] = ii;
+    for (int g = 0; g < NT; ++g) {
+        int base = 0;
+#pragma unroll
+        for (int e = 0; e < nch; ++e) {
+            uint32_t kk, ii;
+            get(g, e, kk, ii);
+            const bool sel = kk > tau[g] || (kk == tau[g] && (!cut[g] || (0x3FFFFu - ii) >= sig[g]));
+            const uint64_t m = __ballot(sel);
+            if (sel) {
+                const int pos = base + lanes_below(m);
+                okey[g * 64 + pos] = kk;
+                oid[g * 64 + pos] = ii;
+            }
+            base += popc(m);
         }
-        base += popc(m);
     }
 }
 
-// Bitonic sort across the 64 lanes, one 64-bit key per lane, descending.
-__device__ __forceinline__ uint64_t wave_sort_desc(uint64_t x, int lane) {
+template <int J, int NT>
+__device__ __forceinline__ void sort_stage(uint64_t (&x)[NT], int lane, int k) {
 #pragma unroll
-    for (int k = 2; k <= 64; k <<= 1) {
-#pragma unroll
-        for (int j = k >> 1; j > 0; j >>= 1) {
-            const uint64_t o = shfl_xor_u64(x, j);
-            const bool keep_max = (((lane & j) == 0) == ((lane & k) == 0));
-            const uint64_t mx = x > o ? x : o;
-            const uint64_t mn = x > o ? o : x;
-            x = keep_max ? mx : mn;
-        }
+    for (int g = 0; g < NT; ++g) {
+        const uint64_t o = xlane64<J>(x[g], lane);
+        const bool keep_max = (((lane & J) == 0) == ((lane & k) == 0));
+        const uint64_t mx = x[g] > o ? x[g] : o;
+        const uint64_t mn = x[g] > o ? o : x[g];
+        x[g] = keep_max ? mx : mn;
     }
-    return x;
+}
+
+// Bitonic sort across the 64 lanes, one 64-bit key per lane, descending, for
+// NT independent sequences at once.
+template <int NT>
+__device__ __forceinline__ void wave_sort_desc(uint64_t (&x)[NT], int lane) {
+    sort_stage<1>(x, lane, 2);
+    sort_stage<2>(x, lane, 4); sort_stage<1>(x, lane, 4);
+    sort_stage<4>(x, lane, 8); sort_stage<2>(x, lane, 8); sort_stage<1>(x, lane, 8);
+    sort_stage<8>(x, lane, 16); sort_stage<4>(x, lane, 16); sort_stage<2>(x, lane, 16);
+    sort_stage<1>(x, lane, 16);
+    sort_stage<16>(x, lane, 32); sort_stage<8>(x, lane, 32); sort_stage<4>(x, lane, 32);
+    sort_stage<2>(x, lane, 32); sort_stage<1>(x, lane, 32);
+    sort_stage<32>(x, lane, 64); sort_stage<16>(x, lane, 64); sort_stage<8>(x, lane, 64);
+    sort_stage<4>(x, lane, 64); sort_stage<2>(x, lane, 64); sort_stage<1>(x, lane, 64);
 }
 
 __device__ __forceinline__ uint64_t composite(uint32_t key, uint32_t id) {
@@ -147,9 +224,9 @@ __device__ __forceinline__ uint64_t composite(uint32_t key, uint32_t id) {
 }
 
 template <bool BF16, int EH>
-__global__ __launch_bounds__(64) void address_kernel(AddressArgs a) {
+__global__ __launch_bounds__(NWA * 64) void address_kernel(AddressArgs a) {
     extern __shared__ __align__(16) uint32_t smem[];
-    const int lane = threadIdx.x;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int n = a.n, dh = a.dh;
     const int64_t ntile = (a.T + TOK - 1) / TOK;
     const int64_t bh = blockIdx.x / ntile;
@@ -158,18 +235,21 @@ __global__ __launch_bounds__(64) void address_kernel(AddressArgs a) {
     const int h = (int)(bh % a.H);
 
     float* sc = reinterpret_cast<float*>(smem);      // [TOK][2][n]
-    float* ls = sc + TOK * 2 * n;                     // [2][64] sorted half scores
-    uint32_t* lid = reinterpret_cast<uint32_t*>(ls + 128);  // [2][64] their sub-indices
-    uint32_t* bkey = lid + 128;                       // [64] select output
-    uint32_t* bid = bkey + 64;                        // [64]
-    uint32_t* pairs = bid + 64;                       // [EC*64] pruned rank pairs
+    uint32_t* pairs = reinterpret_cast<uint32_t*>(sc + TOK * 2 * n);  // [EC*64] pruned rank pairs
+    float* ls = reinterpret_cast<float*>(pairs + EC * 64) + wave * (TG * 128 * 2 + TG * 64 * 2);
+    uint32_t* lid = reinterpret_cast<uint32_t*>(ls + TG * 128);  // [TG][2][64] their sub-indices
+    uint32_t* bkey = lid + TG * 128;                  // [TG][64] select output
+    uint32_t* bid = bkey + TG * 64;                   // [TG][64]
+    // ls: [TG][2][64] sorted half scores of this wavefront's tokens
 
     // ---------------- a1: half-scores on MFMA ----------------
     const int m16 = lane & 15, g4 = lane >> 4;
     const int64_t tq = t0 + m16;
     const bool tok_ok = tq < a.T;
-    for (int j = 0; j < 2; ++j) {
-        for (int a0 = 0; a0 < n; a0 += 16) {
+    // the 2 * n/16 subkey tiles are dealt round-robin to the wavefronts
+    for (int tile = wave; tile < 2 * (n / 16); tile += NWA) {
+        const int j = tile / (n / 16), a0 = (tile % (n / 16)) * 16;
+        {
             f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
             if constexpr (BF16) {
                 const uint16_t* q = static_cast<const uint16_t*>(a.q[br]) +
@@ -204,7 +284,7 @@ __global__ __launch_bounds__(64) void address_kernel(AddressArgs a) {
     __syncthreads();
 
     if (a.half_out) {  // test hook: the contraction only
-        for (int e = lane; e < TOK * 2 * n; e += 64) {
+        for (int e = threadIdx.x; e < TOK * 2 * n; e += NWA * 64) {
             const int m = e / (2 * n);
             if (t0 + m < a.T) a.half_out[(bh * a.T + t0) * 2 * n + e] = sc[e];
         }
@@ -225,93 +305,122 @@ __global__ __launch_bounds__(64) void address_kernel(AddressArgs a) {
         const int o = __shfl_up(incl, d);
         if (lane >= d) incl += o;
     }
-    const int C = __shfl(incl, 63);
-    for (int jj = 0, off = incl - len; jj < len; ++jj) pairs[off + jj] = ((uint32_t)lane << 8) | (uint32_t)jj;
+    const int C = __builtin_amdgcn_readlane(incl, 63);
+    if (wave == 0)
+        for (int jj = 0, off = incl - len; jj < len; ++jj) pairs[off + jj] = ((uint32_t)lane << 8) | (uint32_t)jj;
     __syncthreads();
 
     int32_t* idx_out = a.idx[br];
     float* wt_out = a.wt[br];
     float* sc_out = a.score[br];
 
-    for (int m = 0; m < TOK; ++m) {
-        const int64_t t = t0 + m;
-        if (t >= a.T) break;
+    {
+        const int m0 = wave * TG;
+        if (t0 + m0 >= a.T) return;
+        // tokens past T run on the zero scores of their masked rows; nothing is stored
 
         // ---------------- a2: per-half top-k_h, sorted ----------------
         for (int j = 0; j < 2; ++j) {
-            const float* s = sc + (m * 2 + j) * n;
-            uint32_t key[EH], id[EH];
+            uint32_t key[TG][EH];
 #pragma unroll
-            for (int e = 0; e < EH; ++e) {
-                const int aa = e * 64 + lane;
-                key[e] = aa < n ? ord_key(s[aa]) : 0u;
-                id[e] = (uint32_t)aa;
+            for (int g = 0; g < TG; ++g) {
+                const float* s = sc + ((m0 + g) * 2 + j) * n;
+#pragma unroll
+                for (int e = 0; e < EH; ++e) {
+                    const int aa = e * 64 + lane;
+                    key[g][e] = aa < n ? ord_key(s[aa]) : 0u;
+                }
             }
-            wave_select<EH>([&](int e, uint32_t& kk, uint32_t& ii) { kk = key[e]; ii = id[e]; },
-                            EH, kh, bkey, bid, lane);
-            uint64_t x = lane < kh ? composite(bkey[lane], bid[lane]) : 0ull;
-            x = wave_sort_desc(x, lane);
-            if (lane < kh) {
-                ls[j * 64 + lane] = key_float((uint32_t)(x >> 32));
-                lid[j * 64 + lane] = 0xFFFFFFFFu - (uint32_t)x;
-            }
+            wave_select<TG, EH>(
+                [&](int g, int e, uint32_t& kk, uint32_t& ii) {
+                    kk = key[g][e];
+                    ii = (uint32_t)(e * 64 + lane);
+                },
+                EH, kh, bkey, bid, lane);
+            uint64_t x[TG];
+#pragma unroll
+            for (int g = 0; g < TG; ++g) x[g] = lane < kh ? composite(bkey[g * 64 + lane], bid[g * 64 + lane]) : 0ull;
+            wave_sort_desc<TG>(x, lane);
+#pragma unroll
+            for (int g = 0; g < TG; ++g)
+                if (lane < kh) {
+                    ls[(g * 2 + j) * 64 + lane] = key_float((uint32_t)(x[g] >> 32));
+                    lid[(g * 2 + j) * 64 + lane] = 0xFFFFFFFFu - (uint32_t)x[g];
+                }
         }
 
         // ---------------- a3: combine over the pruned pairs ----------------
-        uint32_t ck[EC], ci[EC];
+        uint32_t ck[TG][EC], ci[TG][EC];
 #pragma unroll
         for (int e = 0; e < EC; ++e) {
             const int c = e * 64 + lane;
-            ck[e] = 0u;
-            ci[e] = 0u;
-            if (c < C) {
-                const uint32_t p = pairs[c];
-                const int i = (int)(p >> 8), jj = (int)(p & 255u);
-                ck[e] = ord_key(ls[i] + ls[64 + jj]);
-                ci[e] = lid[i] * (uint32_t)n + lid[64 + jj];
+            const uint32_t p = c < C ? pairs[c] : 0u;
+            const int i = (int)(p >> 8), jj = (int)(p & 255u);
+#pragma unroll
+            for (int g = 0; g < TG; ++g) {
+                ck[g][e] = c < C ? ord_key(ls[(g * 2) * 64 + i] + ls[(g * 2 + 1) * 64 + jj]) : 0u;
+                ci[g][e] = lid[(g * 2) * 64 + i] * (uint32_t)n + lid[(g * 2 + 1) * 64 + jj];
             }
         }
-        wave_select<EC>([&](int e, uint32_t& kk, uint32_t& ii) { kk = ck[e]; ii = ci[e]; },
-                        EC, k, bkey, bid, lane);
-        uint64_t x = lane < k ? composite(bkey[lane], bid[lane]) : 0ull;
-        x = wave_sort_desc(x, lane);
+        wave_select<TG, EC>(
+            [&](int g, int e, uint32_t& kk, uint32_t& ii) {
+                kk = ck[g][e];
+                ii = ci[g][e];
+            },
+            EC, k, bkey, bid, lane);
+        uint64_t x[TG];
+#pragma unroll
+        for (int g = 0; g < TG; ++g) x[g] = lane < k ? composite(bkey[g * 64 + lane], bid[g * 64 + lane]) : 0ull;
+        wave_sort_desc<TG>(x, lane);
 
         // certificate: every pruned pair must score strictly below the k-th winner
-        const uint32_t kth = (uint32_t)(__shfl((int)(uint32_t)(x >> 32), k - 1));
-        uint32_t bnd = 0u;
-        if (lane < kh) {
-            const int jb = k / (lane + 1);
-            if (jb < kh) bnd = ord_key(ls[lane] + ls[64 + jb]);
-        }
-        if (__ballot(bnd != 0u && bnd >= kth) != 0ull) {
-            const int full = kh * kh;
-            wave_select<0>(
-                [&](int e, uint32_t& kk, uint32_t& ii) {
-                    const int c = e * 64 + lane;
-                    kk = 0u;
-                    ii = 0u;
-                    if (c < full) {
-                        const int i = c / kh, jj = c - (c / kh) * kh;
-                        kk = ord_key(ls[i] + ls[64 + jj]);
-                        ii = lid[i] * (uint32_t)n + lid[64 + jj];
-                    }
-                },
-                (full + 63) / 64, k, bkey, bid, lane);
-            x = lane < k ? composite(bkey[lane], bid[lane]) : 0ull;
-            x = wave_sort_desc(x, lane);
+#pragma unroll
+        for (int g = 0; g < TG; ++g) {
+            const uint32_t kth = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(x[g] >> 32), k - 1);
+            uint32_t bnd = 0u;
+            if (lane < kh) {
+                const int jb = k / (lane + 1);
+                if (jb < kh) bnd = ord_key(ls[(g * 2) * 64 + lane] + ls[(g * 2 + 1) * 64 + jb]);
+            }
+            if (t0 + m0 + g < a.T && __ballot(bnd != 0u && bnd >= kth) != 0ull) {
+                const int full = kh * kh;
+                const float* l0 = ls + (g * 2) * 64;
+                const float* l1 = ls + (g * 2 + 1) * 64;
+                const uint32_t* i0 = lid + (g * 2) * 64;
+                const uint32_t* i1 = lid + (g * 2 + 1) * 64;
+                wave_select<1, 0>(
+                    [&](int, int e, uint32_t& kk, uint32_t& ii) {
+                        const int c = e * 64 + lane;
+                        kk = 0u;
+                        ii = 0u;
+                        if (c < full) {
+                            const int i = c / kh, jj = c - (c / kh) * kh;
+                            kk = ord_key(l0[i] + l1[jj]);
+                            ii = i0[i] * (uint32_t)n + i1[jj];
+                        }
+                    },
+                    (full + 63) / 64, k, bkey + g * 64, bid + g * 64, lane);
+                uint64_t y1[1] = {lane < k ? composite(bkey[g * 64 + lane], bid[g * 64 + lane]) : 0ull};
+                wave_sort_desc<1>(y1, lane);
+                x[g] = y1[0];
+            }
         }
 
         // ---------------- a4: softmax over the k winners ----------------
-        const float S = key_float((uint32_t)(x >> 32));
-        const uint32_t slot = 0xFFFFFFFFu - (uint32_t)x;
-        const float mx = __shfl(S, 0);
-        const float ex = lane < k ? expf(S - mx) : 0.f;
-        const float sum = wave_sum(ex);
-        if (lane < k) {
-            const int64_t o = (bh * a.T + t) * k + lane;
-            idx_out[o] = (int32_t)slot;
-            wt_out[o] = ex / sum;
-            if (sc_out) sc_out[o] = S;
+#pragma unroll
+        for (int g = 0; g < TG; ++g) {
+            const int64_t t = t0 + m0 + g;
+            const float S = key_float((uint32_t)(x[g] >> 32));
+            const uint32_t slot = 0xFFFFFFFFu - (uint32_t)x[g];
+            const float mx = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(S), 0));
+            const float ex = lane < k ? expf(S - mx) : 0.f;
+            const float sum = wave_sum(ex, lane);
+            if (lane < k && t < a.T) {
+                const int64_t o = (bh * a.T + t) * k + lane;
+                idx_out[o] = (int32_t)slot;
+                wt_out[o] = ex / sum;
+                if (sc_out) sc_out[o] = S;
+            }
         }
     }
 }
@@ -319,9 +428,9 @@ __global__ __launch_bounds__(64) void address_kernel(AddressArgs a) {
 template <bool BF16, int EH>
 hipError_t launch_inst(const AddressArgs& a, hipStream_t st) {
     const int64_t ntile = (a.T + TOK - 1) / TOK;
-    const size_t lds = (size_t)TOK * 2 * a.n * 4 + (128 + 128 + 64 + 64 + EC * 64) * 4;
+    const size_t lds = (size_t)TOK * 2 * a.n * 4 + EC * 64 * 4 + (size_t)NWA * (TG * 128 * 2 + TG * 64 * 2) * 4;
     dim3 grid((unsigned)(ntile * a.B * a.H), (unsigned)a.nbranch);
-    hipLaunchKernelGGL((address_kernel<BF16, EH>), grid, dim3(64), lds, st, a);
+    hipLaunchKernelGGL((address_kernel<BF16, EH>), grid, dim3(NWA * 64), lds, st, a);
     return hipGetLastError();
 }
 
