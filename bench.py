@@ -38,7 +38,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default="gdn_matched")
     p.add_argument("--form", default="eq4", choices=["eq4", "fig2"])
-    p.add_argument("--cpu-seconds", type=float, default=15.0,
+    p.add_argument("--cpu-seconds", type=float, default=20.0,
                    help="target CPU time of the oracle baseline sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
@@ -73,29 +73,37 @@ def measured_traffic():
 
 
 def cpu_baseline(wl, x, target_s: float):
-    """The oracle as it is (addressing of both branches + scan), on the first
-    T' tokens of sequence b=0 with all H heads; T' sized to ~target_s."""
-    import numpy as np
+    """The oracle as it is (addressing of both branches + scan) on a bounded
+    sample of the same workload: the first B' sequences with all H heads, or
+    the first T' tokens of one sequence when a whole one already exceeds the
+    target; the sample is sized from a short calibration run to ~target_s."""
+    import math
     import oracle
 
     nthreads = oracle.default_threads()
 
-    def run(Tp):
-        sl = lambda t: t[:1, :, :Tp].contiguous()
+    def run(nb, Tp):
+        sl = lambda t: t[:nb, :, :Tp].contiguous()
         t0 = time.perf_counter()
         iw, ww, _, _ = oracle.address(sl(x["q_w"]), x["subkeys"], wl.W, nthreads)
         ir, wr, _, _ = oracle.address(sl(x["q_r"]), x["subkeys"], wl.R, nthreads)
         oracle.scan(iw, ww, ir, wr, sl(x["alpha"]), sl(x["beta"]), sl(x["v"]),
-                    x["M0"][None].numpy(), oracle.EQ4, nthreads)
+                    oracle.broadcast_state(x["M0"].numpy(), nb), oracle.EQ4, nthreads)
         return time.perf_counter() - t0
 
-    Tc = min(wl.T, 32)
-    tc = run(Tc)
-    Tp = int(min(wl.T, max(Tc, Tc * target_s / max(tc, 1e-3))))
-    ts = run(Tp) if Tp > Tc else tc
-    return {"value": Tp / ts, "unit": "tokens/s", "cores": nthreads, "kind": "oracle",
-            "sample": f"sequence b=0 of {wl.name}, all {wl.H} heads, first {Tp} of {wl.T} tokens "
-                      f"(addressing of both branches + {'EQ4'} scan), {ts:.1f} s wall",
+    # two calibration points separate the per-call fixed cost from the per-token cost
+    T1, T2 = min(wl.T, 64), min(wl.T, 512)
+    t1, t2 = run(1, T1), run(1, T2)
+    per_tok = max((t2 - t1) / max(T2 - T1, 1), t2 / T2 * 0.1, 1e-6)
+    want = max(target_s - max(t1 - T1 * per_tok, 0.0), 0.0) / per_tok
+    if want <= wl.T:
+        nb, Tp = 1, max(T2, int(want))
+    else:
+        nb, Tp = min(wl.B, max(1, math.ceil(want / wl.T))), wl.T
+    ts = run(nb, Tp) if (nb, Tp) != (1, T2) else t2
+    return {"value": nb * Tp / ts, "unit": "tokens/s", "cores": nthreads, "kind": "oracle",
+            "sample": f"{nb} of {wl.B} sequences of {wl.name}, all {wl.H} heads, first {Tp} of "
+                      f"{wl.T} tokens (addressing of both branches + EQ4 scan), {ts:.1f} s wall",
             "host_cpu": host_cpu()}
 
 
