@@ -139,7 +139,8 @@ int64_t sdm_scan_workspace_bytes(int64_t B, int64_t H, int64_t T, int64_t W, int
  * of one token distinct (sdm_address guarantees both). Entries that break the
  * first are skipped (memory-safe, result unspecified); the second gives an
  * unspecified result. Weights are used as given.
- * Supported: 1 <= W, R <= 256, N <= 2^18, dv a multiple of 4.
+ * Supported: 1 <= W, R <= 256, N <= 2^18, dv a multiple of 4, N * dv * 4 < 2^31
+ * (one stream's table below 2 GiB).
  */
 int sdm_scan_forward(const int32_t* idx_w, const float* wt_w, int64_t W,
                      const int32_t* idx_r, const float* wt_r, int64_t R,

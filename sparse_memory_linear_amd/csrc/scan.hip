@@ -27,6 +27,13 @@
 // the scan takes them from an LDS ring of recently written rows; a read of a
 // row written by the same token forwards with d = 0 (after the token's barrier).
 //
+// The token loop is bound by instruction issue as much as by memory, so every
+// memory access is a buffer instruction with a 32-bit lane offset and the
+// token's offset in a scalar register; an access that must not happen (padding
+// lanes, the y store of all but one wavefront) gets an offset past the end of
+// its buffer, which the hardware drops (loads return 0). Writer entries carry
+// alpha and beta next to the weight, so a writer issues one plan load per token.
+//
 // Placement: workgroups are dealt to the 8 XCDs round-robin, so blockIdx is
 // remapped to put every slab of a stream on the same XCD; the slabs of a row
 // then share that XCD's L2 lines.
@@ -35,7 +42,7 @@
 namespace sdm {
 namespace {
 
-// Plan entry, one per (token, access): .x = packed, .y = weight bits.
+// Plan entry word: row, flags and the forward source.
 constexpr uint32_t ENT_INVALID = 1u << 31;  // padding or out-of-range index: no access
 constexpr uint32_t ENT_FWD = 1u << 30;      // value comes from the LDS ring
 constexpr uint32_t ROW_MASK = (1u << 18) - 1u;
@@ -46,28 +53,43 @@ constexpr int DIST_SHIFT = 26;              // token distance of the source (4 b
 // entries lead by another D + 1 tokens (memory counters complete in order, so
 // waiting on an entry also waits on every older row load: a lead >= D keeps D
 // tokens of rows in flight); NWMAX = wavefronts per workgroup (sets the VGPR
-// budget: 8 -> 256, 16 -> 128). 32-column slabs move whole 128-byte lines per
-// row: on MI355X random 128-byte accesses sustain ~1.4x the bandwidth of 64-byte
-// ones.
+// budget: 8 -> 256, 16 -> 128).
+#ifndef SDM_SCAN_DEPTH
+#define SDM_SCAN_DEPTH 10
+#endif
+#ifndef SDM_SCAN_DEPTH32
+#define SDM_SCAN_DEPTH32 6
+#endif
 template <int S>
 struct SlabCfg {
-    static constexpr int D = 10, NWMAX = 8;
+    static constexpr int D = SDM_SCAN_DEPTH, NWMAX = 8;
+};
+#ifndef SDM_SCAN_DEPTH8
+#define SDM_SCAN_DEPTH8 SDM_SCAN_DEPTH
+#endif
+#ifndef SDM_SCAN_NW8
+#define SDM_SCAN_NW8 8
+#endif
+template <>
+struct SlabCfg<8> {
+    static constexpr int D = SDM_SCAN_DEPTH8, NWMAX = SDM_SCAN_NW8;
 };
 template <>
 struct SlabCfg<32> {
-    static constexpr int D = 6, NWMAX = 16;
+    static constexpr int D = SDM_SCAN_DEPTH32, NWMAX = 16;
 };
-constexpr int MAX_WAVES = 16;   // largest NWMAX
 
 // Geometry of a slab of S fp32 columns: L = S/4 lanes per row segment (16 B
 // each), G = 64/L rows per wavefront; NWW = ceil(W/G) writer and NWR = ceil(R/G)
-// reader wavefronts. Plan record per token: a 16-byte header (alpha, beta)
-// then entries [wave][G] (int2 each): writer wave w, lane row r -> write
-// access w*G + r; reader wave NWW+w -> read access w*G + r.
+// reader wavefronts. Plan record per token: writer entries [NWW][G] of 16 bytes
+// (packed word, weight, alpha, beta), then reader entries [NWR][G] of 8 bytes
+// (packed word, weight): writer wave w, lane row r -> write access w*G + r,
+// reader wave w -> read access w*G + r.
 struct Geom {
     int S, G, NWW, NWR;
-    int nw() const { return NWW + NWR; }
-    int64_t rec() const { return 16 + (int64_t)nw() * G * 8; }
+    __host__ __device__ int nw() const { return NWW + NWR; }
+    __host__ __device__ int64_t wbytes() const { return (int64_t)NWW * G * 16; }
+    __host__ __device__ int64_t rec() const { return wbytes() + (int64_t)NWR * G * 8; }
 };
 
 Geom make_geom(int S, int W, int R) {
@@ -79,109 +101,211 @@ Geom make_geom(int S, int W, int R) {
     return g;
 }
 
+// Readers summed by reader 0 per token: the largest reader count a slab width
+// can have (R <= 256, at most NWMAX wavefronts in all); partial-sum slots of
+// absent readers stay zero.
+template <int S>
+constexpr int nrmax() {
+    constexpr int g = 64 / (S / 4), byr = 256 / g, nwm = SlabCfg<S>::NWMAX;
+    return byr < nwm ? byr : nwm;
+}
+
 // ------------------------------------------------------------------ planner
-constexpr int HT_CAP = 8192;  // LDS hash table entries (64-bit)
-constexpr unsigned long long HT_EMPTY = ~0ull;
+// One workgroup per (stream, tile of TT tokens). An LDS hash table holds every
+// write of tokens [t0 - D, t0 + TT) as a 32-bit entry (row << 14 | tok << pb | p)
+// with tok the token relative to t0 - D and p the write position (pb bits);
+// the table is kept at most half full. A bitmap over all N rows marks the rows
+// written anywhere in the tile, so the common access (no writer nearby) is
+// settled by one LDS read; the others look up the latest writer of their row
+// inside their window. Global loads are issued in batches of PB independent
+// loads per thread, so their latency is paid once per batch rather than once
+// per element.
+constexpr int HT_CAP = 16384;              // LDS hash table entries (32-bit): 64 KiB
+constexpr int HT_BITS = 14;
+constexpr int HT_WRITES = HT_CAP / 2;      // writes held per tile (load factor <= 1/2)
+constexpr uint32_t HT_EMPTY = ~0u;         // never a valid entry (see the launch)
+constexpr int PB = 8;                      // loads in flight per thread
+constexpr int PLAN_THREADS = 512;
 
-__device__ __forceinline__ uint32_t ht_hash(uint32_t row) { return (row * 2654435761u) >> (32 - 13); }
+__device__ __forceinline__ uint32_t ht_hash(uint32_t row) { return (row * 2654435761u) >> (32 - HT_BITS); }
 
-__global__ __launch_bounds__(256) void plan_kernel(
-    const int32_t* __restrict__ idx_w, const float* __restrict__ wt_w, int W,
-    const int32_t* __restrict__ idx_r, const float* __restrict__ wt_r, int R,
-    const float* __restrict__ alpha, const float* __restrict__ beta,
-    uint8_t* __restrict__ plan, int64_t T, int64_t N, int D, int G, int NWW, int NWR, int TT,
-    int64_t ntile) {
-    __shared__ unsigned long long ht[HT_CAP];
+// Sizes of one launch over a chunk of Tc tokens taken from streams of TS tokens.
+struct PlanArgs {
+    const int32_t* idx_w; const float* wt_w; int W;
+    const int32_t* idx_r; const float* wt_r; int R;
+    const float* alpha; const float* beta;
+    uint8_t* plan;
+    int64_t Tc, TS, N;
+    int D, G, NWW, NWR, TT, pb;
+    int64_t ntile;
+};
+
+__global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(PlanArgs a) {
+    __shared__ uint32_t ht[HT_CAP];
+    extern __shared__ uint32_t bm[];          // ceil(N / 32) words
     const int tid = threadIdx.x;
-    const int64_t s = blockIdx.x / ntile;
-    const int64_t t0 = (blockIdx.x % ntile) * TT;
-    const int64_t t1 = t0 + TT < T ? t0 + TT : T;
+    const int W = a.W, R = a.R, D = a.D, G = a.G, NWW = a.NWW, pb = a.pb;
+    const int64_t T = a.Tc, N = a.N;
+    const int64_t s = blockIdx.x / a.ntile;
+    const int64_t t0 = (blockIdx.x % a.ntile) * a.TT;
+    const int64_t t1 = t0 + a.TT < T ? t0 + a.TT : T;
     const int64_t h0 = t0 - D > 0 ? t0 - D : 0;
-    const int NW = NWW + NWR;
-    const int64_t REC = 16 + (int64_t)NW * G * 8;
-    const int32_t* iw = idx_w + s * T * W;
-    const float* ww = wt_w + s * T * W;
-    const int32_t* ir = idx_r + s * T * R;
-    const float* wr = wt_r + s * T * R;
-    uint8_t* P = plan + s * T * REC;
+    const int64_t WB = (int64_t)NWW * G * 16;
+    const int64_t REC = WB + (int64_t)a.NWR * G * 8;
+    const int32_t* iw = a.idx_w + s * a.TS * W;
+    const float* ww = a.wt_w + s * a.TS * W;
+    const int32_t* ir = a.idx_r + s * a.TS * R;
+    const float* wr = a.wt_r + s * a.TS * R;
+    const float* al = a.alpha + s * a.TS;
+    const float* be = a.beta + s * a.TS;
+    uint8_t* P = a.plan + s * T * REC;
 
-    for (int i = tid; i < HT_CAP; i += 256) ht[i] = HT_EMPTY;
+    for (int i = tid; i < HT_CAP / 4; i += PLAN_THREADS)
+        reinterpret_cast<uint4*>(ht)[i] = make_uint4(HT_EMPTY, HT_EMPTY, HT_EMPTY, HT_EMPTY);
+    const int nbm = (int)((N + 31) >> 5);
+    for (int i = tid; i < nbm; i += PLAN_THREADS) bm[i] = 0u;
     __syncthreads();
-    // every write of tokens [h0, t1): key = row, value = (token - h0, position)
-    const int64_t nins = (t1 - h0) * W;
-    for (int64_t e = tid; e < nins; e += 256) {
-        const int64_t tt = h0 + e / W;
-        const int p = (int)(e % W);
-        const int32_t row = iw[tt * W + p];
-        if (row < 0 || row >= N) continue;
-        const unsigned long long ent = ((unsigned long long)(uint32_t)row << 32) |
-                                       ((unsigned long long)(tt - h0) << 16) | (unsigned)p;
-        uint32_t hsh = ht_hash((uint32_t)row);
-        while (atomicCAS(&ht[hsh], HT_EMPTY, ent) != HT_EMPTY) hsh = (hsh + 1) & (HT_CAP - 1);
+    // writes of tokens [h0, t1), contiguous in idx_w
+    const int nins = (int)(t1 - h0) * W;
+    const int32_t* iw0 = iw + h0 * W;
+    for (int base = 0; base < nins; base += PLAN_THREADS * PB) {
+        int32_t row[PB];
+#pragma unroll
+        for (int u = 0; u < PB; ++u) {
+            const int e = base + u * PLAN_THREADS + tid;
+            row[u] = e < nins ? iw0[e] : -1;
+        }
+#pragma unroll
+        for (int u = 0; u < PB; ++u) {
+            const int e = base + u * PLAN_THREADS + tid;
+            if (row[u] < 0 || row[u] >= N) continue;
+            const int tok = e / W, p = e - tok * W;
+            const uint32_t ent = ((uint32_t)row[u] << HT_BITS) | ((uint32_t)tok << pb) | (uint32_t)p;
+            atomicOr(&bm[row[u] >> 5], 1u << (row[u] & 31));
+            uint32_t h = ht_hash((uint32_t)row[u]);
+            while (atomicCAS(&ht[h], HT_EMPTY, ent) != HT_EMPTY) h = (h + 1) & (HT_CAP - 1);
+        }
     }
     __syncthreads();
 
-    const int per_tok = NW * G;
-    const int64_t nent = (t1 - t0) * per_tok;
-    for (int64_t e = tid; e < nent; e += 256) {
-        const int64_t tt = t0 + e / per_tok;
-        const int rem = (int)(e % per_tok);
-        const int wv = rem / G, rr = rem % G;
-        const bool isw = wv < NWW;
-        const int p = (isw ? wv : wv - NWW) * G + rr;
-        uint32_t packed = ENT_INVALID;
-        float w = 0.f;
-        if (p < (isw ? W : R)) {
-            const int32_t row = isw ? iw[tt * W + p] : ir[tt * R + p];
-            if (row >= 0 && row < N) {
-                w = isw ? ww[tt * W + p] : wr[tt * R + p];
-                packed = (uint32_t)row;
-                // latest writer of this row in [tt-D, tt-1] (writes) or [tt-D, tt] (reads)
-                const int64_t lo = tt - D, hi = isw ? tt - 1 : tt;
-                int64_t best = -1;
-                uint32_t bp = 0;
-                uint32_t hsh = ht_hash((uint32_t)row);
-                unsigned long long ent;
-                while ((ent = ht[hsh]) != HT_EMPTY) {
-                    if ((uint32_t)(ent >> 32) == (uint32_t)row) {
-                        const int64_t tw = h0 + (int64_t)((ent >> 16) & 0xFFFFu);
-                        if (tw >= lo && tw <= hi && tw > best) {
-                            best = tw;
-                            bp = (uint32_t)(ent & 0xFFFFu);
-                        }
-                    }
-                    hsh = (hsh + 1) & (HT_CAP - 1);
-                }
-                if (best >= 0)
-                    packed |= ENT_FWD | ((uint32_t)(tt - best) << DIST_SHIFT) | (bp << POS_SHIFT);
+    const int per_tok = (NWW + a.NWR) * G;
+    const int nent = (int)(t1 - t0) * per_tok;
+    const uint32_t pmask = (1u << pb) - 1u;
+    for (int base = 0; base < nent; base += PLAN_THREADS * PB) {
+        int32_t row[PB];
+        float w[PB];
+        bool isw[PB];
+#pragma unroll
+        for (int u = 0; u < PB; ++u) {
+            const int e = base + u * PLAN_THREADS + tid;
+            const int tl = e / per_tok, rem = e - tl * per_tok;
+            const int wv = rem / G, rr = rem - wv * G;
+            isw[u] = wv < NWW;
+            const int p = (isw[u] ? wv : wv - NWW) * G + rr;
+            const int64_t tt = t0 + tl;
+            row[u] = -1;
+            w[u] = 0.f;
+            if (e < nent && p < (isw[u] ? W : R)) {
+                row[u] = isw[u] ? iw[tt * W + p] : ir[tt * R + p];
+                w[u] = isw[u] ? ww[tt * W + p] : wr[tt * R + p];
             }
         }
-        *reinterpret_cast<int2*>(P + tt * REC + 16 + (int64_t)rem * 8) = make_int2((int)packed, __float_as_int(w));
+#pragma unroll
+        for (int u = 0; u < PB; ++u) {
+            const int e = base + u * PLAN_THREADS + tid;
+            if (e >= nent) break;
+            const int tl = e / per_tok, rem = e - tl * per_tok;
+            const int64_t tt = t0 + tl;
+            uint32_t packed = ENT_INVALID;
+            float wv = 0.f;
+            if (row[u] >= 0 && row[u] < N) {
+                wv = w[u];
+                packed = (uint32_t)row[u];
+            }
+            if (packed != ENT_INVALID && (bm[row[u] >> 5] >> (row[u] & 31)) & 1u) {
+                // latest writer of this row in [tt-D, tt-1] (writes) or [tt-D, tt] (reads),
+                // as a token index relative to h0
+                const int lo = (int)(tt - D - h0), hi = (int)(tt - h0) - (isw[u] ? 1 : 0);
+                int best = -1;
+                uint32_t bp = 0;
+                uint32_t h = ht_hash((uint32_t)row[u]);
+                uint32_t ent;
+                while ((ent = ht[h]) != HT_EMPTY) {
+                    if ((ent >> HT_BITS) == (uint32_t)row[u]) {
+                        const int tw = (int)((ent & ((1u << HT_BITS) - 1u)) >> pb);
+                        if (tw >= lo && tw <= hi && tw > best) {
+                            best = tw;
+                            bp = ent & pmask;
+                        }
+                    }
+                    h = (h + 1) & (HT_CAP - 1);
+                }
+                if (best >= 0)
+                    packed |= ENT_FWD | ((uint32_t)(tt - h0 - best) << DIST_SHIFT) | (bp << POS_SHIFT);
+            }
+            uint8_t* rec = P + tt * REC;
+            if (isw[u])  // writer entries come first, in access order
+                *reinterpret_cast<int4*>(rec + (int64_t)rem * 16) =
+                    make_int4((int)packed, __float_as_int(wv), __float_as_int(al[tt]), __float_as_int(be[tt]));
+            else
+                *reinterpret_cast<int2*>(rec + WB + (int64_t)(rem - NWW * G) * 8) =
+                    make_int2((int)packed, __float_as_int(wv));
+        }
     }
-    for (int64_t tt = t0 + tid; tt < t1; tt += 256)
-        *reinterpret_cast<float4*>(P + tt * REC) = make_float4(alpha[s * T + tt], beta[s * T + tt], 0.f, 0.f);
 }
 
 // ------------------------------------------------------------------ scan
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+using rsrc_t = __amdgpu_buffer_rsrc_t;
+// A buffer offset beyond every buffer the scan addresses (each is < 2 GiB): the
+// hardware's range check drops the access and a load returns zeros.
+constexpr uint32_t OOB = 0x80000000u;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* p, int64_t bytes) {
+    // raw buffer: stride 0, num_records = size in bytes, 32-bit data format (gfx9 word 3)
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ int4 ld_i4(rsrc_t r, uint32_t vo, uint32_t so) {
+    const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(r, (int)vo, (int)so, 0);
+    return make_int4((int)x.x, (int)x.y, (int)x.z, (int)x.w);
+}
+__device__ __forceinline__ int2 ld_i2(rsrc_t r, uint32_t vo, uint32_t so) {
+    const u32x2 x = __builtin_amdgcn_raw_buffer_load_b64(r, (int)vo, (int)so, 0);
+    return make_int2((int)x.x, (int)x.y);
+}
+__device__ __forceinline__ float4 ld_f4(rsrc_t r, uint32_t vo, uint32_t so) {
+    const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(r, (int)vo, (int)so, 0);
+    return make_float4(__uint_as_float(x.x), __uint_as_float(x.y), __uint_as_float(x.z), __uint_as_float(x.w));
+}
+__device__ __forceinline__ void st_f4(float4 v, rsrc_t r, uint32_t vo, uint32_t so) {
+    u32x4 x;
+    x.x = __float_as_uint(v.x); x.y = __float_as_uint(v.y); x.z = __float_as_uint(v.z); x.w = __float_as_uint(v.w);
+    __builtin_amdgcn_raw_buffer_store_b128(x, r, (int)vo, (int)so, 0);
+}
+__device__ __forceinline__ void st_f1(float v, rsrc_t r, uint32_t vo, uint32_t so) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, (int)vo, (int)so, 0);
+}
+
+// v_t of this lane's 4 columns.
 template <bool BF16>
 struct VLoad;
 template <>
 struct VLoad<false> {
     using T4 = float4;
-    __device__ static T4 load(const void* base, int64_t off) {
-        return *reinterpret_cast<const float4*>(static_cast<const float*>(base) + off);
-    }
+    static constexpr int ESZ = 4;
+    __device__ static T4 load(rsrc_t r, uint32_t vo, uint32_t so) { return ld_f4(r, vo, so); }
     __device__ static float4 f(const T4& x) { return x; }
 };
 template <>
 struct VLoad<true> {
-    using T4 = uint2;
-    __device__ static T4 load(const void* base, int64_t off) {
-        return *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(base) + off);
-    }
+    using T4 = int2;
+    static constexpr int ESZ = 2;
+    __device__ static T4 load(rsrc_t r, uint32_t vo, uint32_t so) { return ld_i2(r, vo, so); }
     __device__ static float4 f(const T4& x) {
-        return make_float4(__uint_as_float(x.x << 16), __uint_as_float(x.x & 0xFFFF0000u),
-                           __uint_as_float(x.y << 16), __uint_as_float(x.y & 0xFFFF0000u));
+        const uint32_t a = (uint32_t)x.x, b = (uint32_t)x.y;
+        return make_float4(__uint_as_float(a << 16), __uint_as_float(a & 0xFFFF0000u),
+                           __uint_as_float(b << 16), __uint_as_float(b & 0xFFFF0000u));
     }
 };
 
@@ -203,182 +327,188 @@ template <int N>
 __device__ __forceinline__ float ror_add(float x) {
     return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x120 + N, 0xF, 0xF, false));
 }
-// x + its partner 16 (resp. 32) lanes away: the two halves returned by the
-// gfx950 permlane swaps of (x, x) are {x, partner} in some order on every lane.
-__device__ __forceinline__ float xor16_add(float x) {
-    auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
-}
-__device__ __forceinline__ float xor32_add(float x) {
-    auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
-}
-// Sum over the G row-lanes that share a column chunk (lanes with equal lane % L);
-// every lane ends with its chunk's sum, bit-identical across those lanes.
+// Sum over the G rows of a wavefront (lane = row * L + chunk), as a
+// reduce-scatter: the gfx950 permlane swaps exchange one register between lane
+// halves (32) and quarter pairs (16), so each swap + add halves the number of
+// components a lane carries. Lane l ends with component l / 16 of column chunk
+// l % L summed over all rows; lanes that share (l / 16, l % L) hold equal bits.
+//   swap32(A, B): lanes < 32 get {A[l], A[l+32]}, lanes >= 32 get {B[l-32], B[l]}
+//   swap16(A, B): the same between even and odd rows of 16 lanes
 template <int L>
-__device__ __forceinline__ float row_sum(float x) {
-    if constexpr (L <= 8) x = ror_add<8>(x);
-    if constexpr (L <= 4) x = ror_add<4>(x);
-    if constexpr (L <= 2) x = ror_add<2>(x);
-    if constexpr (L <= 1) x = ror_add<1>(x);
-    x = xor16_add(x);
-    return xor32_add(x);
-}
-template <int L>
-__device__ __forceinline__ float4 row_sum4(float4 a) {
-    return make_float4(row_sum<L>(a.x), row_sum<L>(a.y), row_sum<L>(a.z), row_sum<L>(a.w));
+__device__ __forceinline__ float rows_reduce(float4 x) {
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x.x), __float_as_uint(x.z), false, false);
+    const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(x.y), __float_as_uint(x.w), false, false);
+    const float a = __uint_as_float(p[0]) + __uint_as_float(p[1]);  // comp 0 (lanes < 32) or 2
+    const float b = __uint_as_float(q[0]) + __uint_as_float(q[1]);  // comp 1 (lanes < 32) or 3
+    const auto u = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    float c = __uint_as_float(u[0]) + __uint_as_float(u[1]);        // comp lane / 16
+    if constexpr (L <= 8) c = ror_add<8>(c);
+    if constexpr (L <= 4) c = ror_add<4>(c);
+    if constexpr (L <= 2) c = ror_add<2>(c);
+    if constexpr (L <= 1) c = ror_add<1>(c);
+    return c;
 }
 
+struct ScanKArgs {
+    const uint8_t* plan;
+    const void* v;
+    float* M;
+    float* y;
+    int T;          // tokens in this launch
+    int64_t TS;     // tokens per stream in v and y (stream stride)
+    int64_t N;
+    int dv, nslab;
+    int64_t NS;
+    int NWW, NWR;
+};
+
 template <int S, int FORM, bool VBF16>
-__global__ __launch_bounds__(SlabCfg<S>::NWMAX * 64) void scan_kernel(
-    const uint8_t* __restrict__ plan, const void* __restrict__ v, float* M, float* __restrict__ y,
-    float* sink_base, int T, int64_t N, int dv, int nslab, int64_t NS, int NWW, int NWR) {
+__global__ __launch_bounds__(SlabCfg<S>::NWMAX * 64) void scan_kernel(ScanKArgs a) {
     constexpr int L = S / 4, G = 64 / L;
-    constexpr int D = SlabCfg<S>::D, NWMAX = SlabCfg<S>::NWMAX;
+    constexpr int D = SlabCfg<S>::D, NWMAX = SlabCfg<S>::NWMAX, NRMAX = nrmax<S>();
     constexpr int DM = D + 1;       // plan-entry lead beyond D
     constexpr int UP = D + 1;       // row / value register rings: D in flight + the one in use
     constexpr int U = D + DM + 1;   // plan-entry ring = unroll factor (a multiple of UP, so
                                     // every ring index is static in the unrolled loop)
     static_assert(U % UP == 0, "ring sizes");
-    constexpr int UR = D + 2;       // LDS ring of written rows (see the ring-reuse note below)
+    constexpr int UR = U;           // LDS ring of written rows: token t uses slot t % U, a
+                                    // constant in the unrolled loop (reuse needs UR >= D + 2)
     using VL = VLoad<VBF16>;
     using V4 = typename VL::T4;
+    const int NWW = a.NWW, NWR = a.NWR, T = a.T, dv = a.dv;
     extern __shared__ float4 lds[];
-    const int NW = NWW + NWR;
-    float4* ring = lds;                                  // [UR][NWW*G][L]
-    float4* ybuf = lds + UR * NWW * G * L;               // [2][NWR][L]
-    float4* vbuf = ybuf + 2 * NWR * L;                   // [NWW][L]
+    float4* ring = lds;                                              // [UR][NWW*G][L]
+    float* ybuf = reinterpret_cast<float*>(lds + UR * NWW * G * L);  // [2][NRMAX][S]
+    float4* vbuf = reinterpret_cast<float4*>(ybuf + 2 * NRMAX * S);  // [NWW][L] (FIG2)
 
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane / L, cc = lane % L;
     const int b = blockIdx.x, xcd = b & 7, kq = b >> 3;
-    const int64_t s = (int64_t)(kq / nslab) * 8 + xcd;
-    const int slab = kq % nslab;
-    if (s >= NS) return;  // uniform over the workgroup
+    const int64_t s = (int64_t)(kq / a.nslab) * 8 + xcd;
+    const int slab = kq % a.nslab;
+    if (s >= a.NS) return;  // uniform over the workgroup
     const int col = slab * S + cc * 4;
-    const float* Mr = M + s * N * dv;                    // this stream's table (row base)
-    float* Mw = M + s * N * dv;
-    const int64_t REC = 16 + (int64_t)NW * G * 8;
-    const uint8_t* Pe = plan + s * (int64_t)T * REC + 16 + (int64_t)(wave * G + r) * 8;
-    const uint8_t* Ph = plan + s * (int64_t)T * REC;
-    const int64_t voff = s * (int64_t)T * dv + col;
-    float* ys = y + s * (int64_t)T * dv + col;
-    float* sink = sink_base + ((int64_t)blockIdx.x * (MAX_WAVES * 64) + threadIdx.x) * 4;
+    const Geom geo{S, G, NWW, NWR};
+    const uint32_t REC = (uint32_t)geo.rec();
+    const rsrc_t Rp = make_rsrc(a.plan + s * (int64_t)T * REC, (int64_t)T * REC);
+    const rsrc_t Rm = make_rsrc(a.M + s * a.N * dv, a.N * dv * 4);
+    const rsrc_t Rv = make_rsrc(static_cast<const char*>(a.v) + s * a.TS * dv * VL::ESZ, (int64_t)T * dv * VL::ESZ);
+    const rsrc_t Ry = make_rsrc(a.y + s * a.TS * dv, (int64_t)T * dv * 4);
     const bool writer = wave < NWW;
     const int pos = wave * G + r;                        // write position of a writer lane
     const int rw = wave - NWW;                           // reader index
+    const uint32_t e_off = writer ? (uint32_t)pos * 16u : (uint32_t)geo.wbytes() + (uint32_t)(rw * G + r) * 8u;
+    const uint32_t dv4 = (uint32_t)dv * 4u, col4 = (uint32_t)col * 4u;
+    const uint32_t v_off = (uint32_t)col * VL::ESZ;
+    const uint32_t vstride = (uint32_t)dv * VL::ESZ;
+    // reader 0's first S lanes store y[t-1] (one column each); every other y store is dropped
+    const uint32_t y_off = (!writer && rw == 0 && lane < S) ? (uint32_t)(slab * S + lane) * 4u : OOB;
+    const int ylane = lane < S ? lane : 0;
 
-    auto ring_at = [&](int slot, int p) -> float4& { return ring[((int64_t)slot * NWW * G + p) * L + cc]; };
-    auto load_entry = [&](int t) -> int2 { return *reinterpret_cast<const int2*>(Pe + (int64_t)t * REC); };
-    auto load_ab = [&](int t) -> float2 { return *reinterpret_cast<const float2*>(Ph + (int64_t)t * REC); };
-    auto load_row = [&](int2 e) -> float4 {
-        const uint32_t off = (((uint32_t)e.x & ROW_MASK) * (uint32_t)dv + (uint32_t)col);
-        return *reinterpret_cast<const float4*>(Mr + off);
+    // partial sums of absent readers stay zero (made visible by the first barrier)
+    for (int i = threadIdx.x; i < 2 * NRMAX * S; i += blockDim.x) ybuf[i] = 0.f;
+
+    auto row_off = [&](uint32_t pk) -> uint32_t {
+        return (pk & ENT_INVALID) ? OOB : __umul24(pk & ROW_MASK, dv4) + col4;
     };
-    auto source = [&](int t, int2 e, float4 pre) -> float4 {
+    auto load_went = [&](int t) -> int4 { return ld_i4(Rp, e_off, (uint32_t)t * REC); };
+    auto load_rent = [&](int t) -> int2 { return ld_i2(Rp, e_off, (uint32_t)t * REC); };
+    auto load_row = [&](uint32_t pk) -> float4 { return ld_f4(Rm, row_off(pk), 0u); };
+    auto load_v = [&](int t) -> V4 { return VL::load(Rv, v_off, (uint32_t)t * vstride); };
+    auto ring_at = [&](int slot, int p) -> float4& { return ring[((int64_t)slot * NWW * G + p) * L + cc]; };
+    auto source = [&](int slot, uint32_t pk, float4 pre) -> float4 {
         // forwarded rows come from the LDS ring; the ballot keeps the common
         // no-forward case free of LDS traffic
-        const uint32_t pk = (uint32_t)e.x;
         const bool f = (pk & (ENT_FWD | ENT_INVALID)) == ENT_FWD;
         if (__ballot(f) != 0ull && f) {
-            const int d = (int)((pk >> DIST_SHIFT) & 15u);
-            const int p = (int)((pk >> POS_SHIFT) & 255u);
-            pre = ring_at((t - d) % UR, p);
+            int sl = slot - (int)((pk >> DIST_SHIFT) & 15u);
+            if (sl < 0) sl += UR;
+            pre = ring_at(sl, (int)((pk >> POS_SHIFT) & 255u));
         }
         return pre;
     };
 
     // one token of a writer wavefront (barriers: [B'_t], B_t)
-    auto write_token = [&](int t, int2 e, float2 ab, float4 pre, V4 vt) {
+    auto write_token = [&](int slot, int4 e, float4 pre, V4 vt) {
         const uint32_t pk = (uint32_t)e.x;
-        const bool ok = (pk & ENT_INVALID) == 0u;
-        const float w = __int_as_float(e.y);
-        const float4 mt = f4_scale(ab.x, source(t, e, pre));
+        const float w = __int_as_float(e.y), al = __int_as_float(e.z), be = __int_as_float(e.w);
+        const float4 mt = f4_scale(al, source(slot, pk, pre));
         float4 pred = mt;
         if constexpr (FORM == 1) {
-            const float4 part = row_sum4<L>(f4_scale(ok ? w : 0.f, mt));
-            if (r == 0) vbuf[wave * L + cc] = part;
+            const float part = rows_reduce<L>(f4_scale(w, mt));
+            if ((lane & 15) < L) reinterpret_cast<float*>(vbuf)[wave * S + 4 * (lane & 15) + (lane >> 4)] = part;
             __syncthreads();
             pred = vbuf[cc];
 #pragma unroll
             for (int q = 1; q < NWMAX; ++q)
                 if (q < NWW) pred = f4_add(pred, vbuf[q * L + cc]);
         }
-        const float4 nv = f4_fma(ab.y * w, f4_sub(VL::f(vt), pred), mt);
-        float* dst = ok ? Mw + (((pk & ROW_MASK) * (uint32_t)dv + (uint32_t)col)) : sink;
-        *reinterpret_cast<float4*>(dst) = nv;
-        ring_at(t % UR, pos) = nv;
+        const float4 nv = f4_fma(be * w, f4_sub(VL::f(vt), pred), mt);
+        st_f4(nv, Rm, row_off(pk), 0u);
+        ring_at(slot, pos) = nv;
         __syncthreads();
     };
     // one token of a reader wavefront (barriers: [B'_t], B_t); the partial sums
     // of token t are combined by reader 0 after the next barrier
-    auto read_token = [&](int t, int2 e, float4 pre) {
+    auto read_token = [&](int t, int slot, int2 e, float4 pre) {
         if constexpr (FORM == 1) __syncthreads();
         __syncthreads();
         const uint32_t pk = (uint32_t)e.x;
-        const float w = (pk & ENT_INVALID) == 0u ? __int_as_float(e.y) : 0.f;
-        const float4 part = row_sum4<L>(f4_scale(w, source(t, e, pre)));
-        if (r == 0) ybuf[((t & 1) * NWR + rw) * L + cc] = part;
-        // every reader sums the previous token's partials; reader 0 stores the
-        // result, the others (and token 0, which has no predecessor) hit the sink
-        const int pb = (t - 1) & 1;
-        float4 acc = ybuf[(pb * NWR) * L + cc];
+        const float part = rows_reduce<L>(f4_scale(__int_as_float(e.y), source(slot, pk, pre)));
+        if ((lane & 15) < L) ybuf[((t & 1) * NRMAX + rw) * S + 4 * (lane & 15) + (lane >> 4)] = part;
+        float acc = 0.f;
+        if (rw == 0) {  // uniform per wavefront; no memory operation inside
+            const float* pb = ybuf + ((t - 1) & 1) * NRMAX * S + ylane;
 #pragma unroll
-        for (int q = 1; q < NWMAX; ++q)
-            if (q < NWR) acc = f4_add(acc, ybuf[(pb * NWR + q) * L + cc]);
-        float* dst = (rw == 0 && t > 0) ? ys + (int64_t)(t - 1) * dv : sink;
-        *reinterpret_cast<float4*>(dst) = acc;
+            for (int q = 0; q < NRMAX; ++q) acc += pb[q * S];
+        }
+        st_f1(acc, Ry, t > 0 ? y_off : OOB, (uint32_t)(t > 0 ? t - 1 : 0) * dv4);
     };
 
     // Main loop: U tokens per trip, fully unrolled so that the register rings
     // are statically indexed. Each role gets its own prologue that issues the
-    // steady-state sequence of loads (with a sink store standing in for each
-    // token's store), so that the loop header merges like states and the
-    // compiler's memory waits stay D tokens deep.
+    // steady-state sequence of memory operations (with a dropped store standing
+    // in for each token's store), so that the loop header merges like states and
+    // the compiler's memory waits stay D tokens deep.
     int t_done = 0;
     if (T >= U) {
-        int2 ent[U];
         float4 pre[UP];
         if (writer) {
-            float2 ab[U];
+            int4 ent[U];
             V4 vv[UP];
 #pragma unroll
             for (int q = 0; q < D + DM; ++q) {
-                ent[q] = load_entry(q);
-                ab[q] = load_ab(q);
+                ent[q] = load_went(q);
                 if (q >= DM) {
-                    pre[q - DM] = load_row(ent[q - DM]);
-                    vv[q - DM] = VL::load(v, voff + (int64_t)(q - DM) * dv);
+                    pre[q - DM] = load_row((uint32_t)ent[q - DM].x);
+                    vv[q - DM] = load_v(q - DM);
                 }
-                *reinterpret_cast<float4*>(sink) = make_float4(0.f, 0.f, 0.f, 0.f);
+                st_f4(make_float4(0.f, 0.f, 0.f, 0.f), Rm, OOB, 0u);
             }
             for (int t0 = 0; t0 + U <= T; t0 += U) {
 #pragma unroll
                 for (int j = 0; j < U; ++j) {
                     const int t = t0 + j;
-                    const int tm = t + D + DM < T ? t + D + DM : T - 1;
-                    ent[(j + D + DM) % U] = load_entry(tm);
-                    ab[(j + D + DM) % U] = load_ab(tm);
-                    const int tr = t + D < T ? t + D : T - 1;
-                    pre[(j + D) % UP] = load_row(ent[(j + D) % U]);
-                    vv[(j + D) % UP] = VL::load(v, voff + (int64_t)tr * dv);
-                    write_token(t, ent[j], ab[j], pre[j % UP], vv[j % UP]);
+                    ent[(j + D + DM) % U] = load_went(t + D + DM < T ? t + D + DM : T - 1);
+                    pre[(j + D) % UP] = load_row((uint32_t)ent[(j + D) % U].x);
+                    vv[(j + D) % UP] = load_v(t + D < T ? t + D : T - 1);
+                    write_token(j, ent[j], pre[j % UP], vv[j % UP]);
                 }
             }
         } else {
+            int2 ent[U];
 #pragma unroll
             for (int q = 0; q < D + DM; ++q) {
-                ent[q] = load_entry(q);
-                if (q >= DM) pre[q - DM] = load_row(ent[q - DM]);
-                *reinterpret_cast<float4*>(sink) = make_float4(0.f, 0.f, 0.f, 0.f);
+                ent[q] = load_rent(q);
+                if (q >= DM) pre[q - DM] = load_row((uint32_t)ent[q - DM].x);
+                st_f1(0.f, Ry, OOB, 0u);
             }
             for (int t0 = 0; t0 + U <= T; t0 += U) {
 #pragma unroll
                 for (int j = 0; j < U; ++j) {
                     const int t = t0 + j;
-                    const int tm = t + D + DM < T ? t + D + DM : T - 1;
-                    ent[(j + D + DM) % U] = load_entry(tm);
-                    pre[(j + D) % UP] = load_row(ent[(j + D) % U]);
-                    read_token(t, ent[j], pre[j % UP]);
+                    ent[(j + D + DM) % U] = load_rent(t + D + DM < T ? t + D + DM : T - 1);
+                    pre[(j + D) % UP] = load_row((uint32_t)ent[(j + D) % U].x);
+                    read_token(t, j, ent[j], pre[j % UP]);
                 }
             }
         }
@@ -386,62 +516,100 @@ __global__ __launch_bounds__(SlabCfg<S>::NWMAX * 64) void scan_kernel(
     }
     // tail (and short sequences): loads right before use; forwarding stays valid
     for (int t = t_done; t < T; ++t) {
-        const int2 e = load_entry(t);
-        const float4 pre = load_row(e);
-        if (writer) write_token(t, e, load_ab(t), pre, VL::load(v, voff + (int64_t)t * dv));
-        else read_token(t, e, pre);
+        if (writer) {
+            const int4 e = load_went(t);
+            write_token(t % U, e, load_row((uint32_t)e.x), load_v(t));
+        } else {
+            const int2 e = load_rent(t);
+            read_token(t, t % U, e, load_row((uint32_t)e.x));
+        }
     }
     // the last token's partial sums
     __syncthreads();
     if (!writer && rw == 0 && T > 0) {
-        const int pb = (T - 1) & 1;
-        float4 acc = ybuf[(pb * NWR) * L + cc];
-        for (int q = 1; q < NWR; ++q) acc = f4_add(acc, ybuf[(pb * NWR + q) * L + cc]);
-        *reinterpret_cast<float4*>(ys + (int64_t)(T - 1) * dv) = acc;
+        const float* pb = ybuf + ((T - 1) & 1) * NRMAX * S + ylane;
+        float acc = 0.f;
+        for (int q = 0; q < NRMAX; ++q) acc += pb[q * S];
+        st_f1(acc, Ry, y_off, (uint32_t)(T - 1) * dv4);
     }
 }
 // Ring reuse: the writer of token t overwrites slot t % UR, last used by token
 // t - UR; its readers (tokens up to t - UR + D) have finished once every
-// wavefront passed barrier B_{t-1}, which needs t - UR + D <= t - 2, so UR = D + 2.
+// wavefront passed barrier B_{t-1}, which needs t - UR + D <= t - 2, i.e.
+// UR >= D + 2 (here UR = 2D + 2).
 
 template <int S>
 size_t scan_lds_bytes(const Geom& g) {
-    const int L = S / 4;
-    return ((size_t)(SlabCfg<S>::D + 2) * g.NWW * g.G * L + 2 * g.NWR * L + g.NWW * L) * 16;
+    constexpr int D = SlabCfg<S>::D, UR = 2 * D + 2, L = S / 4;
+    return (size_t)UR * g.NWW * g.G * L * 16 + (size_t)2 * nrmax<S>() * S * 4 + (size_t)g.NWW * L * 16;
+}
+
+// Tokens per launch: every buffer one stream spans in a launch (plan records, v,
+// y) stays below 2 GiB, so 32-bit offsets and the dropped-access offset work.
+int64_t chunk_tokens(int64_t T, const Geom& g, int dv) {
+    const int64_t per_tok = g.rec() > (int64_t)dv * 4 ? g.rec() : (int64_t)dv * 4;
+    const int64_t cap = (int64_t)0x7FFFFFFF / per_tok;
+    return T < cap ? T : cap;
 }
 
 template <int S>
 hipError_t launch_scan_slab(const ScanArgs& a, const Geom& g, hipStream_t st) {
     constexpr int D = SlabCfg<S>::D;
     static_assert(D <= 15, "the plan stores forward distances in 4 bits");
-    // planner: tiles of TT tokens; the hash table holds the writes of TT + D tokens at load <= 1/2
-    int TT = HT_CAP / (2 * a.W) - D;
+    // planner: tiles of TT tokens; the hash table holds the writes of TT + D tokens
+    // at load <= 1/2. With pb = ceil(log2 W) (so 2^pb < 2W), the entry ids
+    // tok << pb | p stay below (TT + D) << pb < 2 * HT_WRITES = 2^14, and the
+    // largest one is at most 2^14 - 2, so no entry equals HT_EMPTY.
+    int pb = 0;
+    while ((1 << pb) < a.W) ++pb;
+    int TT = HT_WRITES / a.W - D;
     if (TT < 1) TT = 1;
-    const int64_t ntile = (a.T + TT - 1) / TT;
-    uint8_t* plan = static_cast<uint8_t*>(a.workspace);
-    hipLaunchKernelGGL(plan_kernel, dim3((unsigned)(ntile * a.NS)), dim3(256), 0, st, a.idx_w, a.wt_w, a.W,
-                       a.idx_r, a.wt_r, a.R, a.alpha, a.beta, plan, a.T, a.N, D, g.G, g.NWW, g.NWR, TT,
-                       ntile);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    const int64_t Tc = chunk_tokens(a.T, g, a.dv);
     const int nslab = a.dv / S;
     const int64_t nblk = ((a.NS + 7) / 8) * 8 * nslab;
-    float* sink = reinterpret_cast<float*>(plan + a.NS * a.T * g.rec());
     const size_t lds = scan_lds_bytes<S>(g);
-    dim3 grid((unsigned)nblk), block((unsigned)(g.nw() * 64));
-#define SDM_LAUNCH(FORM, VB)                                                                          \
-    hipLaunchKernelGGL((scan_kernel<S, FORM, VB>), grid, block, lds, st, plan, a.v, a.M, a.y, sink, \
-                       (int)a.T, a.N, a.dv, nslab, a.NS, g.NWW, g.NWR)
-    if (a.form == 0) {
-        if (a.v_bf16) SDM_LAUNCH(0, true); else SDM_LAUNCH(0, false);
-    } else {
-        if (a.v_bf16) SDM_LAUNCH(1, true); else SDM_LAUNCH(1, false);
+    const size_t bm_bytes = (size_t)((a.N + 31) / 32) * 4;
+    const int esz = a.v_bf16 ? 2 : 4;
+    for (int64_t c0 = 0; c0 < a.T; c0 += Tc) {
+        const int64_t Tn = a.T - c0 < Tc ? a.T - c0 : Tc;
+        PlanArgs p{};
+        p.idx_w = a.idx_w + c0 * a.W; p.wt_w = a.wt_w + c0 * a.W; p.W = a.W;
+        p.idx_r = a.idx_r + c0 * a.R; p.wt_r = a.wt_r + c0 * a.R; p.R = a.R;
+        p.alpha = a.alpha + c0; p.beta = a.beta + c0;
+        p.plan = static_cast<uint8_t*>(a.workspace);
+        p.Tc = Tn; p.TS = a.T; p.N = a.N;
+        p.D = D; p.G = g.G; p.NWW = g.NWW; p.NWR = g.NWR; p.TT = TT; p.pb = pb;
+        p.ntile = (Tn + TT - 1) / TT;
+        hipLaunchKernelGGL(plan_kernel, dim3((unsigned)(p.ntile * a.NS)), dim3(PLAN_THREADS), bm_bytes, st, p);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        ScanKArgs k{};
+        k.plan = p.plan;
+        k.v = static_cast<const char*>(a.v) + c0 * a.dv * esz;
+        k.M = a.M;
+        k.y = a.y + c0 * a.dv;
+        k.T = (int)Tn; k.TS = a.T; k.N = a.N; k.dv = a.dv; k.nslab = nslab; k.NS = a.NS;
+        k.NWW = g.NWW; k.NWR = g.NWR;
+        dim3 grid((unsigned)nblk), block((unsigned)(g.nw() * 64));
+        if (a.form == 0) {
+            if (a.v_bf16) hipLaunchKernelGGL((scan_kernel<S, 0, true>), grid, block, lds, st, k);
+            else hipLaunchKernelGGL((scan_kernel<S, 0, false>), grid, block, lds, st, k);
+        } else {
+            if (a.v_bf16) hipLaunchKernelGGL((scan_kernel<S, 1, true>), grid, block, lds, st, k);
+            else hipLaunchKernelGGL((scan_kernel<S, 1, false>), grid, block, lds, st, k);
+        }
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
     }
-#undef SDM_LAUNCH
-    return hipGetLastError();
+    return hipSuccess;
 }
 
-int slab_nwmax(int S) { return S == 32 ? SlabCfg<32>::NWMAX : SlabCfg<16>::NWMAX; }
+int slab_nwmax(int S) {
+    return S == 32 ? SlabCfg<32>::NWMAX : S == 16 ? SlabCfg<16>::NWMAX : S == 8 ? SlabCfg<8>::NWMAX : SlabCfg<4>::NWMAX;
+}
+int slab_nrmax(int S) {
+    return S == 32 ? nrmax<32>() : S == 16 ? nrmax<16>() : S == 8 ? nrmax<8>() : nrmax<4>();
+}
 
 // Slab width: SDM_SCAN_SLAB forces one. Otherwise, among the widths whose groups
 // of G rows tile W and R without padding and that need at most 8 wavefronts
@@ -472,7 +640,7 @@ int pick_slab(int64_t NS, int W, int R, int dv) {
     for (int S : {32, 16, 8, 4}) {
         if (dv % S != 0 || (forced && forced != S)) continue;
         const Geom g = make_geom(S, W, R);
-        if (g.nw() > slab_nwmax(S)) continue;
+        if (g.nw() > slab_nwmax(S) || g.NWR > slab_nrmax(S)) continue;
         const Cand c{S, (long)g.NWW * g.G - W + (long)g.NWR * g.G - R, (long)NS * (dv / S), g.nw()};
         if (best.S == 0 || better(c, best)) best = c;
     }
@@ -490,10 +658,10 @@ bool scan_geometry(int64_t NS, int W, int R, int dv, int* slab, int* rec) {
 }
 
 int64_t scan_workspace_bytes(int64_t NS, int64_t T, int W, int R, int dv) {
-    int rec = 0, S = 0;
-    if (!scan_geometry(NS, W, R, dv, &S, &rec)) return -1;
-    const int64_t nblk = ((NS + 7) / 8) * 8 * (dv / S);
-    return NS * T * rec + nblk * MAX_WAVES * 64 * 16;  // plan records + one 16-byte sink per thread
+    int S = 0;
+    if (!scan_geometry(NS, W, R, dv, &S, nullptr)) return -1;
+    const Geom g = make_geom(S, W, R);
+    return NS * chunk_tokens(T, g, dv) * g.rec();  // plan records of one launch
 }
 
 hipError_t launch_scan(const ScanArgs& a, hipStream_t st) {

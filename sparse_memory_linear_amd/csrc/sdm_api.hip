@@ -158,6 +158,9 @@ int sdm_scan_forward(const int32_t* idx_w, const float* wt_w, int64_t W, const i
     if (W > 256 || R > 256) return fail(SDM_ERR_UNSUPPORTED, "W, R <= 256 on the GPU");
     if (N > (1 << 18)) return fail(SDM_ERR_UNSUPPORTED, "N=%lld: at most 2^18 slots", (long long)N);
     if (dv % 4 != 0) return fail(SDM_ERR_UNSUPPORTED, "dv=%lld must be a multiple of 4", (long long)dv);
+    if (N * dv * 4 >= (1ll << 31))
+        return fail(SDM_ERR_UNSUPPORTED, "one stream's table (N*dv*4 = %lld bytes) must stay below 2 GiB",
+                    (long long)(N * dv * 4));
     if (!sdm::scan_geometry(B * H > 0 ? B * H : 1, (int)W, (int)R, (int)dv, nullptr, nullptr))
         return fail(SDM_ERR_UNSUPPORTED, "no scan kernel covers W=%lld, R=%lld, dv=%lld", (long long)W,
                     (long long)R, (long long)dv);

@@ -48,13 +48,12 @@ def test_abi_version_and_status_strings(lib):
 
 def test_workspace_size_is_pure_host_logic(lib):
     # W = R = 64, dv = 128, 32 streams -> 16-column slabs: 16 rows per wavefront,
-    # 4 writer + 4 reader wavefronts; a token record is a 16-byte header + 8 x 16
-    # entries of 8 bytes, plus a 16-byte sink for each of the 1024 thread slots of
-    # the 8*ceil(32/8)*8 workgroups
-    assert binding.sdm_scan_workspace_bytes(4, 8, 8192, 64, 64, 128) == 32 * 8192 * 1040 + 256 * 1024 * 16
+    # 4 writer + 4 reader wavefronts; a token record holds 64 writer entries of
+    # 16 bytes and 64 reader entries of 8 bytes
+    assert binding.sdm_scan_workspace_bytes(4, 8, 8192, 64, 64, 128) == 32 * 8192 * 1536
     # 8 streams (the long-context shape) -> 8-column slabs: 32 rows per wavefront,
-    # 2 + 2 wavefronts, 16 + 4*32*8 bytes per token, 8*1*16 workgroups
-    assert binding.sdm_scan_workspace_bytes(1, 8, 1000, 64, 64, 128) == 8 * 1000 * 1040 + 128 * 1024 * 16
+    # 2 + 2 wavefronts, the same 64 + 64 entries per token
+    assert binding.sdm_scan_workspace_bytes(1, 8, 1000, 64, 64, 128) == 8 * 1000 * 1536
     assert binding.sdm_scan_workspace_bytes(0, 8, 8192, 64, 64, 128) == 0
     assert lib.sdm_scan_workspace_bytes(1, 1, 1, 0, 1, 16) == -1
     assert lib.sdm_scan_workspace_bytes(1, 1, 1, 300, 1, 16) == -1
@@ -94,6 +93,7 @@ def test_scan_rejects_bad_arguments_before_launch(lib):
     assert call(W=65537) == 2                    # W > N
     assert call(N=(1 << 18) + 1, W=64) == 5
     assert call(dv=130) == 5
+    assert call(N=1 << 18, W=64, dv=2048) == 5   # one stream's table would reach 2 GiB
     assert call(ws=None) == 7
     assert call(wsb=100) == 7
     assert call(y=P(4104)) == 4
