@@ -111,145 +111,197 @@ constexpr int nrmax() {
 }
 
 // ------------------------------------------------------------------ planner
+// The rows of a stream's table may be split into P partitions (a hash of the
+// row index), each scanned by its own workgroups: every partition gets its own
+// plan records, in which the accesses of a token that fall into it are packed
+// to the front in access order (their "rank"); the rest is padding.
+//
 // One workgroup per (stream, tile of TT tokens). An LDS hash table holds every
-// write of tokens [t0 - D, t0 + TT) as a 32-bit entry (row << 14 | tok << pb | p)
-// with tok the token relative to t0 - D and p the write position (pb bits);
-// the table is kept at most half full. A bitmap over all N rows marks the rows
-// written anywhere in the tile, so the common access (no writer nearby) is
-// settled by one LDS read; the others look up the latest writer of their row
-// inside their window. Global loads are issued in batches of PB independent
-// loads per thread, so their latency is paid once per batch rather than once
-// per element.
+// write of tokens [t0 - D, t0 + TT) as a 32-bit entry (row << 14 | tok << pb |
+// rank) with tok the token relative to t0 - D; the table is kept at most half
+// full. A bitmap over all N rows marks the rows written anywhere in the tile,
+// so the common access (no writer nearby) is settled by one LDS read; the
+// others look up the latest writer of their row inside their window. Each
+// wavefront handles whole tokens (lanes = access positions, ranks by ballot)
+// and issues the index loads of PNB tokens together.
 constexpr int HT_CAP = 16384;              // LDS hash table entries (32-bit): 64 KiB
 constexpr int HT_BITS = 14;
 constexpr int HT_WRITES = HT_CAP / 2;      // writes held per tile (load factor <= 1/2)
 constexpr uint32_t HT_EMPTY = ~0u;         // never a valid entry (see the launch)
-constexpr int PB = 8;                      // loads in flight per thread
-constexpr int PLAN_THREADS = 512;
+constexpr int PLAN_WAVES = 8;
+constexpr int PLAN_THREADS = PLAN_WAVES * 64;
+constexpr int PNB = 2;                     // tokens whose loads a wavefront issues together (keeps the
+                                           // planner under 128 VGPRs: two workgroups per CU)
+constexpr int MAX_PARTS = 8;
 
 __device__ __forceinline__ uint32_t ht_hash(uint32_t row) { return (row * 2654435761u) >> (32 - HT_BITS); }
+__device__ __forceinline__ int row_part(uint32_t row, int pshift) {
+    return pshift == 0 ? 0 : (int)((row * 0x9E3779B1u) >> (32 - pshift));
+}
 
-// Sizes of one launch over a chunk of Tc tokens taken from streams of TS tokens.
+// One launch over a chunk of Tc tokens taken from streams of TS tokens.
 struct PlanArgs {
     const int32_t* idx_w; const float* wt_w; int W;
     const int32_t* idx_r; const float* wt_r; int R;
     const float* alpha; const float* beta;
-    uint8_t* plan;
+    uint8_t* plan;                         // [NS][P][Tc][rec]
     int64_t Tc, TS, N;
-    int D, G, NWW, NWR, TT, pb;
+    int D, G, NWW, NWR, TT, pb, P, pshift;
     int64_t ntile;
 };
+
+// Rank of this lane's access among the valid accesses of its partition at
+// lower positions, given the counts cnt[q] of the chunks before; updates cnt.
+__device__ __forceinline__ int part_rank(bool ok, int part, int P, uint64_t below, int (&cnt)[MAX_PARTS]) {
+    int rank = 0;
+#pragma unroll
+    for (int q = 0; q < MAX_PARTS; ++q) {
+        if (q < P) {
+            const uint64_t m = __ballot(ok && part == q);
+            if (ok && part == q) rank = cnt[q] + __popcll(m & below);
+            cnt[q] += __popcll(m);
+        }
+    }
+    return rank;
+}
+
+// Forward bits of an access of `row` at token cur (relative to the window
+// start): the latest write of the row at a token in [lo, hi], or 0.
+__device__ __forceinline__ uint32_t fwd_bits(const uint32_t* ht, const uint32_t* bm, uint32_t row, int cur,
+                                             int lo, int hi, int pb) {
+    if (!((bm[row >> 5] >> (row & 31)) & 1u)) return 0u;
+    int best = -1;
+    uint32_t bp = 0;
+    uint32_t h = ht_hash(row), ent;
+    while ((ent = ht[h]) != HT_EMPTY) {
+        if ((ent >> HT_BITS) == row) {
+            const int tw = (int)((ent & ((1u << HT_BITS) - 1u)) >> pb);
+            if (tw >= lo && tw <= hi && tw > best) {
+                best = tw;
+                bp = ent & ((1u << pb) - 1u);
+            }
+        }
+        h = (h + 1) & (HT_CAP - 1);
+    }
+    return best < 0 ? 0u : ENT_FWD | ((uint32_t)(cur - best) << DIST_SHIFT) | (bp << POS_SHIFT);
+}
 
 __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(PlanArgs a) {
     __shared__ uint32_t ht[HT_CAP];
     extern __shared__ uint32_t bm[];          // ceil(N / 32) words
-    const int tid = threadIdx.x;
-    const int W = a.W, R = a.R, D = a.D, G = a.G, NWW = a.NWW, pb = a.pb;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const uint64_t below = (1ull << lane) - 1ull;
+    const int W = a.W, R = a.R, D = a.D, G = a.G, NWW = a.NWW, NWR = a.NWR, pb = a.pb, P = a.P, psh = a.pshift;
     const int64_t T = a.Tc, N = a.N;
     const int64_t s = blockIdx.x / a.ntile;
     const int64_t t0 = (blockIdx.x % a.ntile) * a.TT;
     const int64_t t1 = t0 + a.TT < T ? t0 + a.TT : T;
     const int64_t h0 = t0 - D > 0 ? t0 - D : 0;
     const int64_t WB = (int64_t)NWW * G * 16;
-    const int64_t REC = WB + (int64_t)a.NWR * G * 8;
+    const int64_t REC = WB + (int64_t)NWR * G * 8;
     const int32_t* iw = a.idx_w + s * a.TS * W;
     const float* ww = a.wt_w + s * a.TS * W;
     const int32_t* ir = a.idx_r + s * a.TS * R;
     const float* wr = a.wt_r + s * a.TS * R;
     const float* al = a.alpha + s * a.TS;
     const float* be = a.beta + s * a.TS;
-    uint8_t* P = a.plan + s * T * REC;
+    uint8_t* Ps = a.plan + s * P * T * REC;   // this stream's records [P][Tc][rec]
 
     for (int i = tid; i < HT_CAP / 4; i += PLAN_THREADS)
         reinterpret_cast<uint4*>(ht)[i] = make_uint4(HT_EMPTY, HT_EMPTY, HT_EMPTY, HT_EMPTY);
     const int nbm = (int)((N + 31) >> 5);
     for (int i = tid; i < nbm; i += PLAN_THREADS) bm[i] = 0u;
     __syncthreads();
-    // writes of tokens [h0, t1), contiguous in idx_w
-    const int nins = (int)(t1 - h0) * W;
-    const int32_t* iw0 = iw + h0 * W;
-    for (int base = 0; base < nins; base += PLAN_THREADS * PB) {
-        int32_t row[PB];
+
+    // phase 1: the writes of tokens [h0, t1), with their rank inside their partition
+    const int n1 = (int)(t1 - h0);
+    for (int k0 = wave; k0 < n1; k0 += PLAN_WAVES * PNB) {
+        int cnt[PNB][MAX_PARTS] = {};
+        for (int c = 0; c < W; c += 64) {
+            int32_t row[PNB];
 #pragma unroll
-        for (int u = 0; u < PB; ++u) {
-            const int e = base + u * PLAN_THREADS + tid;
-            row[u] = e < nins ? iw0[e] : -1;
-        }
+            for (int u = 0; u < PNB; ++u) {
+                const int tk = k0 + u * PLAN_WAVES, p = c + lane;
+                row[u] = (tk < n1 && p < W) ? iw[(h0 + tk) * W + p] : -1;
+            }
 #pragma unroll
-        for (int u = 0; u < PB; ++u) {
-            const int e = base + u * PLAN_THREADS + tid;
-            if (row[u] < 0 || row[u] >= N) continue;
-            const int tok = e / W, p = e - tok * W;
-            const uint32_t ent = ((uint32_t)row[u] << HT_BITS) | ((uint32_t)tok << pb) | (uint32_t)p;
-            atomicOr(&bm[row[u] >> 5], 1u << (row[u] & 31));
-            uint32_t h = ht_hash((uint32_t)row[u]);
-            while (atomicCAS(&ht[h], HT_EMPTY, ent) != HT_EMPTY) h = (h + 1) & (HT_CAP - 1);
+            for (int u = 0; u < PNB; ++u) {
+                const int tk = k0 + u * PLAN_WAVES;
+                if (tk >= n1) break;  // uniform
+                const bool ok = row[u] >= 0 && row[u] < N;
+                const int part = ok ? row_part((uint32_t)row[u], psh) : 0;
+                const int rank = part_rank(ok, part, P, below, cnt[u]);
+                if (ok) {
+                    atomicOr(&bm[row[u] >> 5], 1u << (row[u] & 31));
+                    const uint32_t ent = ((uint32_t)row[u] << HT_BITS) | ((uint32_t)tk << pb) | (uint32_t)rank;
+                    uint32_t h = ht_hash((uint32_t)row[u]);
+                    while (atomicCAS(&ht[h], HT_EMPTY, ent) != HT_EMPTY) h = (h + 1) & (HT_CAP - 1);
+                }
+            }
         }
     }
     __syncthreads();
 
-    const int per_tok = (NWW + a.NWR) * G;
-    const int nent = (int)(t1 - t0) * per_tok;
-    const uint32_t pmask = (1u << pb) - 1u;
-    for (int base = 0; base < nent; base += PLAN_THREADS * PB) {
-        int32_t row[PB];
-        float w[PB];
-        bool isw[PB];
+    // phase 2: the records of tokens [t0, t1): writes, then reads, then padding
+    const int n2 = (int)(t1 - t0);
+    for (int k0 = wave; k0 < n2; k0 += PLAN_WAVES * PNB) {
+        for (int br = 0; br < 2; ++br) {
+            const bool isw = br == 0;
+            const int K = isw ? W : R;
+            const int32_t* ix = isw ? iw : ir;
+            const float* wx = isw ? ww : wr;
+            int cnt[PNB][MAX_PARTS] = {};
+            for (int c = 0; c < K; c += 64) {
+                int32_t row[PNB];
+                float w[PNB];
 #pragma unroll
-        for (int u = 0; u < PB; ++u) {
-            const int e = base + u * PLAN_THREADS + tid;
-            const int tl = e / per_tok, rem = e - tl * per_tok;
-            const int wv = rem / G, rr = rem - wv * G;
-            isw[u] = wv < NWW;
-            const int p = (isw[u] ? wv : wv - NWW) * G + rr;
-            const int64_t tt = t0 + tl;
-            row[u] = -1;
-            w[u] = 0.f;
-            if (e < nent && p < (isw[u] ? W : R)) {
-                row[u] = isw[u] ? iw[tt * W + p] : ir[tt * R + p];
-                w[u] = isw[u] ? ww[tt * W + p] : wr[tt * R + p];
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < PB; ++u) {
-            const int e = base + u * PLAN_THREADS + tid;
-            if (e >= nent) break;
-            const int tl = e / per_tok, rem = e - tl * per_tok;
-            const int64_t tt = t0 + tl;
-            uint32_t packed = ENT_INVALID;
-            float wv = 0.f;
-            if (row[u] >= 0 && row[u] < N) {
-                wv = w[u];
-                packed = (uint32_t)row[u];
-            }
-            if (packed != ENT_INVALID && (bm[row[u] >> 5] >> (row[u] & 31)) & 1u) {
-                // latest writer of this row in [tt-D, tt-1] (writes) or [tt-D, tt] (reads),
-                // as a token index relative to h0
-                const int lo = (int)(tt - D - h0), hi = (int)(tt - h0) - (isw[u] ? 1 : 0);
-                int best = -1;
-                uint32_t bp = 0;
-                uint32_t h = ht_hash((uint32_t)row[u]);
-                uint32_t ent;
-                while ((ent = ht[h]) != HT_EMPTY) {
-                    if ((ent >> HT_BITS) == (uint32_t)row[u]) {
-                        const int tw = (int)((ent & ((1u << HT_BITS) - 1u)) >> pb);
-                        if (tw >= lo && tw <= hi && tw > best) {
-                            best = tw;
-                            bp = ent & pmask;
-                        }
-                    }
-                    h = (h + 1) & (HT_CAP - 1);
+                for (int u = 0; u < PNB; ++u) {
+                    const int tk = k0 + u * PLAN_WAVES, p = c + lane;
+                    const bool in = tk < n2 && p < K;
+                    row[u] = in ? ix[(t0 + tk) * K + p] : -1;
+                    w[u] = in ? wx[(t0 + tk) * K + p] : 0.f;
                 }
-                if (best >= 0)
-                    packed |= ENT_FWD | ((uint32_t)(tt - h0 - best) << DIST_SHIFT) | (bp << POS_SHIFT);
+#pragma unroll
+                for (int u = 0; u < PNB; ++u) {
+                    const int tk = k0 + u * PLAN_WAVES;
+                    if (tk >= n2) break;  // uniform
+                    const int64_t tt = t0 + tk;
+                    const bool ok = row[u] >= 0 && row[u] < N;
+                    const int part = ok ? row_part((uint32_t)row[u], psh) : 0;
+                    const int rank = part_rank(ok, part, P, below, cnt[u]);
+                    if (!ok) continue;
+                    // latest writer of this row in [tt-D, tt-1] (writes) or [tt-D, tt] (reads)
+                    const int cur = (int)(tt - h0);
+                    const uint32_t packed =
+                        (uint32_t)row[u] | fwd_bits(ht, bm, (uint32_t)row[u], cur, cur - D, cur - (isw ? 1 : 0), pb);
+                    uint8_t* rec = Ps + ((int64_t)part * T + tt) * REC;
+                    if (isw)
+                        *reinterpret_cast<int4*>(rec + (int64_t)rank * 16) = make_int4(
+                            (int)packed, __float_as_int(w[u]), __float_as_int(al[tt]), __float_as_int(be[tt]));
+                    else
+                        *reinterpret_cast<int2*>(rec + WB + (int64_t)rank * 8) =
+                            make_int2((int)packed, __float_as_int(w[u]));
+                }
             }
-            uint8_t* rec = P + tt * REC;
-            if (isw[u])  // writer entries come first, in access order
-                *reinterpret_cast<int4*>(rec + (int64_t)rem * 16) =
-                    make_int4((int)packed, __float_as_int(wv), __float_as_int(al[tt]), __float_as_int(be[tt]));
-            else
-                *reinterpret_cast<int2*>(rec + WB + (int64_t)(rem - NWW * G) * 8) =
-                    make_int2((int)packed, __float_as_int(wv));
+            // padding: slots past each partition's count
+            const int cap = (isw ? NWW : NWR) * G;
+#pragma unroll
+            for (int u = 0; u < PNB; ++u) {
+                const int tk = k0 + u * PLAN_WAVES;
+                if (tk >= n2) break;
+                const int64_t tt = t0 + tk;
+#pragma unroll
+                for (int q = 0; q < MAX_PARTS; ++q) {
+                    if (q >= P) break;
+                    uint8_t* rec = Ps + ((int64_t)q * T + tt) * REC;
+                    for (int k = cnt[u][q] + lane; k < cap; k += 64) {
+                        if (isw)
+                            *reinterpret_cast<int4*>(rec + (int64_t)k * 16) = make_int4((int)ENT_INVALID, 0, 0, 0);
+                        else
+                            *reinterpret_cast<int2*>(rec + WB + (int64_t)k * 8) = make_int2((int)ENT_INVALID, 0);
+                    }
+                }
+            }
         }
     }
 }
@@ -350,14 +402,15 @@ __device__ __forceinline__ float rows_reduce(float4 x) {
 }
 
 struct ScanKArgs {
-    const uint8_t* plan;
+    const uint8_t* plan;  // [NS][P][T][rec]
     const void* v;
     float* M;
-    float* y;
+    float* y;       // y of (stream s, partition p) at y + s * ys + p * yp
+    int64_t ys, yp;
     int T;          // tokens in this launch
-    int64_t TS;     // tokens per stream in v and y (stream stride)
+    int64_t TS;     // tokens per stream in v (stream stride)
     int64_t N;
-    int dv, nslab;
+    int dv, nslab, P;
     int64_t NS;
     int NWW, NWR;
 };
@@ -382,17 +435,17 @@ __global__ __launch_bounds__(SlabCfg<S>::NWMAX * 64) void scan_kernel(ScanKArgs 
     float4* vbuf = reinterpret_cast<float4*>(ybuf + 2 * NRMAX * S);  // [NWW][L] (FIG2)
 
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane / L, cc = lane % L;
-    const int b = blockIdx.x, xcd = b & 7, kq = b >> 3;
-    const int64_t s = (int64_t)(kq / a.nslab) * 8 + xcd;
-    const int slab = kq % a.nslab;
+    const int b = blockIdx.x, xcd = b & 7, kq = b >> 3, units = a.nslab * a.P;
+    const int64_t s = (int64_t)(kq / units) * 8 + xcd;
+    const int slab = kq % a.nslab, part = (kq % units) / a.nslab;
     if (s >= a.NS) return;  // uniform over the workgroup
     const int col = slab * S + cc * 4;
     const Geom geo{S, G, NWW, NWR};
     const uint32_t REC = (uint32_t)geo.rec();
-    const rsrc_t Rp = make_rsrc(a.plan + s * (int64_t)T * REC, (int64_t)T * REC);
+    const rsrc_t Rp = make_rsrc(a.plan + (s * a.P + part) * (int64_t)T * REC, (int64_t)T * REC);
     const rsrc_t Rm = make_rsrc(a.M + s * a.N * dv, a.N * dv * 4);
     const rsrc_t Rv = make_rsrc(static_cast<const char*>(a.v) + s * a.TS * dv * VL::ESZ, (int64_t)T * dv * VL::ESZ);
-    const rsrc_t Ry = make_rsrc(a.y + s * a.TS * dv, (int64_t)T * dv * 4);
+    const rsrc_t Ry = make_rsrc(a.y + s * a.ys + part * a.yp, (int64_t)T * dv * 4);
     const bool writer = wave < NWW;
     const int pos = wave * G + r;                        // write position of a writer lane
     const int rw = wave - NWW;                           // reader index
@@ -544,6 +597,18 @@ size_t scan_lds_bytes(const Geom& g) {
     return (size_t)UR * g.NWW * g.G * L * 16 + (size_t)2 * nrmax<S>() * S * 4 + (size_t)g.NWW * L * 16;
 }
 
+// Partial y of P row partitions summed in partition order: y[s, t] = sum_p yp[p, s, t].
+__global__ __launch_bounds__(256) void ypart_reduce(const float4* __restrict__ yp, float4* __restrict__ y, int P,
+                                                    int64_t NS, int64_t Tc, int64_t TS, int64_t dq) {
+    const int64_t per_s = Tc * dq, n = NS * per_s;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t st = i / per_s, rem = i - st * per_s;
+        float4 acc = yp[i];
+        for (int q = 1; q < P; ++q) acc = f4_add(acc, yp[q * n + i]);
+        y[st * TS * dq + rem] = acc;
+    }
+}
+
 // Tokens per launch: every buffer one stream spans in a launch (plan records, v,
 // y) stays below 2 GiB, so 32-bit offsets and the dropped-access offset work.
 int64_t chunk_tokens(int64_t T, const Geom& g, int dv) {
@@ -552,43 +617,71 @@ int64_t chunk_tokens(int64_t T, const Geom& g, int dv) {
     return T < cap ? T : cap;
 }
 
+// A scan configuration: slab width S, row partitions P and the wavefront layout.
+struct Cfg {
+    int S = 0, P = 1;
+    Geom g{};
+};
+
+// Bytes of workspace one launch needs: plan records, then (P > 1) partial y.
+struct WsLayout {
+    int64_t plan_bytes, ypart_off, total;
+};
+WsLayout ws_layout(const Cfg& c, int64_t NS, int64_t Tc, int dv) {
+    WsLayout w;
+    w.plan_bytes = NS * c.P * Tc * c.g.rec();
+    w.ypart_off = (w.plan_bytes + 255) / 256 * 256;
+    w.total = c.P > 1 ? w.ypart_off + (int64_t)c.P * NS * Tc * dv * 4 : w.plan_bytes;
+    return w;
+}
+
 template <int S>
-hipError_t launch_scan_slab(const ScanArgs& a, const Geom& g, hipStream_t st) {
+hipError_t launch_scan_slab(const ScanArgs& a, const Cfg& c, hipStream_t st) {
     constexpr int D = SlabCfg<S>::D;
     static_assert(D <= 15, "the plan stores forward distances in 4 bits");
+    const Geom& g = c.g;
     // planner: tiles of TT tokens; the hash table holds the writes of TT + D tokens
     // at load <= 1/2. With pb = ceil(log2 W) (so 2^pb < 2W), the entry ids
-    // tok << pb | p stay below (TT + D) << pb < 2 * HT_WRITES = 2^14, and the
+    // tok << pb | rank stay below (TT + D) << pb < 2 * HT_WRITES = 2^14, and the
     // largest one is at most 2^14 - 2, so no entry equals HT_EMPTY.
     int pb = 0;
     while ((1 << pb) < a.W) ++pb;
+    int psh = 0;
+    while ((1 << psh) < c.P) ++psh;
     int TT = HT_WRITES / a.W - D;
     if (TT < 1) TT = 1;
     const int64_t Tc = chunk_tokens(a.T, g, a.dv);
+    const WsLayout wl = ws_layout(c, a.NS, Tc, a.dv);
     const int nslab = a.dv / S;
-    const int64_t nblk = ((a.NS + 7) / 8) * 8 * nslab;
+    const int64_t nblk = ((a.NS + 7) / 8) * 8 * nslab * c.P;
     const size_t lds = scan_lds_bytes<S>(g);
     const size_t bm_bytes = (size_t)((a.N + 31) / 32) * 4;
     const int esz = a.v_bf16 ? 2 : 4;
+    uint8_t* plan = static_cast<uint8_t*>(a.workspace);
+    float* ypart = reinterpret_cast<float*>(plan + wl.ypart_off);
     for (int64_t c0 = 0; c0 < a.T; c0 += Tc) {
         const int64_t Tn = a.T - c0 < Tc ? a.T - c0 : Tc;
         PlanArgs p{};
         p.idx_w = a.idx_w + c0 * a.W; p.wt_w = a.wt_w + c0 * a.W; p.W = a.W;
         p.idx_r = a.idx_r + c0 * a.R; p.wt_r = a.wt_r + c0 * a.R; p.R = a.R;
         p.alpha = a.alpha + c0; p.beta = a.beta + c0;
-        p.plan = static_cast<uint8_t*>(a.workspace);
+        p.plan = plan;
         p.Tc = Tn; p.TS = a.T; p.N = a.N;
-        p.D = D; p.G = g.G; p.NWW = g.NWW; p.NWR = g.NWR; p.TT = TT; p.pb = pb;
+        p.D = D; p.G = g.G; p.NWW = g.NWW; p.NWR = g.NWR; p.TT = TT; p.pb = pb; p.P = c.P; p.pshift = psh;
         p.ntile = (Tn + TT - 1) / TT;
         hipLaunchKernelGGL(plan_kernel, dim3((unsigned)(p.ntile * a.NS)), dim3(PLAN_THREADS), bm_bytes, st, p);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         ScanKArgs k{};
-        k.plan = p.plan;
+        k.plan = plan;
         k.v = static_cast<const char*>(a.v) + c0 * a.dv * esz;
         k.M = a.M;
-        k.y = a.y + c0 * a.dv;
-        k.T = (int)Tn; k.TS = a.T; k.N = a.N; k.dv = a.dv; k.nslab = nslab; k.NS = a.NS;
+        if (c.P > 1) {
+            k.y = ypart; k.ys = Tn * a.dv; k.yp = a.NS * Tn * a.dv;
+        } else {
+            k.y = a.y + c0 * a.dv; k.ys = a.T * a.dv; k.yp = 0;
+        }
+        k.T = (int)Tn; k.TS = a.T; k.N = a.N; k.dv = a.dv; k.nslab = nslab; k.P = c.P; k.NS = a.NS;
         k.NWW = g.NWW; k.NWR = g.NWR;
         dim3 grid((unsigned)nblk), block((unsigned)(g.nw() * 64));
         if (a.form == 0) {
@@ -600,6 +693,15 @@ hipError_t launch_scan_slab(const ScanArgs& a, const Geom& g, hipStream_t st) {
         }
         e = hipGetLastError();
         if (e != hipSuccess) return e;
+        if (c.P > 1) {
+            const int64_t n4 = a.NS * Tn * (a.dv / 4);
+            const int64_t nb = (n4 + 255) / 256 < 4096 ? (n4 + 255) / 256 : 4096;
+            hipLaunchKernelGGL(ypart_reduce, dim3((unsigned)nb), dim3(256), 0, st,
+                               reinterpret_cast<const float4*>(ypart), reinterpret_cast<float4*>(a.y + c0 * a.dv),
+                               c.P, a.NS, Tn, a.T, (int64_t)(a.dv / 4));
+            e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
     }
     return hipSuccess;
 }
@@ -610,18 +712,25 @@ int slab_nwmax(int S) {
 int slab_nrmax(int S) {
     return S == 32 ? nrmax<32>() : S == 16 ? nrmax<16>() : S == 8 ? nrmax<8>() : nrmax<4>();
 }
+bool slab_fits(int S, int W, int R, int dv) {
+    if (dv % S != 0) return false;
+    const Geom g = make_geom(S, W, R);
+    return g.nw() <= slab_nwmax(S) && g.NWR <= slab_nrmax(S);
+}
 
-// Slab width: SDM_SCAN_SLAB forces one. Otherwise, among the widths whose groups
-// of G rows tile W and R without padding and that need at most 8 wavefronts
-// (the 16-wavefront form has a shallower pipeline), the widest one that still
-// gives at least 128 workgroups (half the CUs): wider slabs move longer row
-// segments, narrower ones give more independent workgroups. Failing that, the
-// width with the most workgroups, then the one with the least padding.
-// (Measured on the N=65536, W=R=64, d_v=128 shapes: 32 streams -> 16 columns,
-// 8 streams -> 8 columns.)
-int pick_slab(int64_t NS, int W, int R, int dv) {
-    int forced = 0;
-    if (const char* e = getenv("SDM_SCAN_SLAB")) forced = atoi(e);
+int env_int(const char* name) {
+    const char* e = getenv(name);
+    return e ? atoi(e) : 0;
+}
+
+// Slab width without row partitions: among the widths whose groups of G rows
+// tile W and R without padding and that need at most 8 wavefronts (the
+// 16-wavefront form has a shallower pipeline), the widest one that still gives
+// at least 128 workgroups (half the CUs): wider slabs move longer row segments,
+// narrower ones give more independent workgroups. Failing that, the width with
+// the most workgroups, then the one with the least padding. (Measured on the
+// N=65536, W=R=64, d_v=128 shapes: 32 streams -> 16 columns, 8 streams -> 8.)
+int pick_slab(int64_t NS, int W, int R, int dv, int forced) {
     struct Cand {
         int S;
         long waste, units;
@@ -638,41 +747,74 @@ int pick_slab(int64_t NS, int W, int R, int dv) {
     };
     Cand best{0, 0, 0, 0};
     for (int S : {32, 16, 8, 4}) {
-        if (dv % S != 0 || (forced && forced != S)) continue;
+        if ((forced && forced != S) || !slab_fits(S, W, R, dv)) continue;
         const Geom g = make_geom(S, W, R);
-        if (g.nw() > slab_nwmax(S) || g.NWR > slab_nrmax(S)) continue;
         const Cand c{S, (long)g.NWW * g.G - W + (long)g.NWR * g.G - R, (long)NS * (dv / S), g.nw()};
         if (best.S == 0 || better(c, best)) best = c;
     }
     return best.S;
 }
 
+// The per-slot form (EQ4) never couples two rows, so it may split the rows into
+// partitions; then every workgroup reads and writes whole 128-byte lines
+// (32-column slabs) and the partitions supply the workgroups that narrower
+// slabs would: P is the smallest power of two (at most 8) that gives 256
+// workgroups. The per-CU count of outstanding line misses is what bounds the
+// scan, so a line that carries 128 useful bytes instead of 32 or 64 is worth
+// more than the extra padding lanes of a partitioned record. The shared-residual
+// form (FIG2) couples all rows of a token and keeps P = 1.
+// SDM_SCAN_SLAB and SDM_SCAN_PARTS force a width and a partition count.
+Cfg choose_cfg(int64_t NS, int W, int R, int dv, int form) {
+    Cfg c;
+    const int fs = env_int("SDM_SCAN_SLAB"), fp = env_int("SDM_SCAN_PARTS");
+    if (form == 0 && (fs == 0 || fs == 32) && slab_fits(32, W, R, dv) && fp != 1) {
+        c.S = 32;
+    } else {
+        c.S = pick_slab(NS, W, R, dv, fs);
+        if (c.S == 0) return c;
+    }
+    if (form == 0) {
+        if (fp == 1 || fp == 2 || fp == 4 || fp == 8) {
+            c.P = fp;
+        } else {
+            const int64_t units = (NS > 0 ? NS : 1) * (dv / c.S);
+            while (c.P < MAX_PARTS && units * c.P < 256) c.P *= 2;
+        }
+    }
+    c.g = make_geom(c.S, W, R);
+    return c;
+}
+
 }  // namespace
 
 bool scan_geometry(int64_t NS, int W, int R, int dv, int* slab, int* rec) {
-    const int S = pick_slab(NS, W, R, dv);
-    if (S == 0) return false;
-    if (slab) *slab = S;
-    if (rec) *rec = (int)make_geom(S, W, R).rec();
+    for (int form = 0; form < 2; ++form)
+        if (choose_cfg(NS, W, R, dv, form).S == 0) return false;
+    const Cfg c = choose_cfg(NS, W, R, dv, 0);
+    if (slab) *slab = c.S;
+    if (rec) *rec = (int)c.g.rec();
     return true;
 }
 
 int64_t scan_workspace_bytes(int64_t NS, int64_t T, int W, int R, int dv) {
-    int S = 0;
-    if (!scan_geometry(NS, W, R, dv, &S, nullptr)) return -1;
-    const Geom g = make_geom(S, W, R);
-    return NS * chunk_tokens(T, g, dv) * g.rec();  // plan records of one launch
+    int64_t need = 0;
+    for (int form = 0; form < 2; ++form) {
+        const Cfg c = choose_cfg(NS, W, R, dv, form);
+        if (c.S == 0) return -1;
+        const int64_t b = ws_layout(c, NS, chunk_tokens(T, c.g, dv), dv).total;
+        if (b > need) need = b;
+    }
+    return need;
 }
 
 hipError_t launch_scan(const ScanArgs& a, hipStream_t st) {
-    const int S = pick_slab(a.NS, a.W, a.R, a.dv);
-    if (S == 0) return hipErrorInvalidValue;
-    const Geom g = make_geom(S, a.W, a.R);
-    switch (S) {
-        case 32: return launch_scan_slab<32>(a, g, st);
-        case 16: return launch_scan_slab<16>(a, g, st);
-        case 8: return launch_scan_slab<8>(a, g, st);
-        default: return launch_scan_slab<4>(a, g, st);
+    const Cfg c = choose_cfg(a.NS, a.W, a.R, a.dv, a.form);
+    switch (c.S) {
+        case 32: return launch_scan_slab<32>(a, c, st);
+        case 16: return launch_scan_slab<16>(a, c, st);
+        case 8: return launch_scan_slab<8>(a, c, st);
+        case 4: return launch_scan_slab<4>(a, c, st);
+        default: return hipErrorInvalidValue;
     }
 }
 

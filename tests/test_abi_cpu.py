@@ -47,13 +47,18 @@ def test_abi_version_and_status_strings(lib):
 
 
 def test_workspace_size_is_pure_host_logic(lib):
-    # W = R = 64, dv = 128, 32 streams -> 16-column slabs: 16 rows per wavefront,
-    # 4 writer + 4 reader wavefronts; a token record holds 64 writer entries of
-    # 16 bytes and 64 reader entries of 8 bytes
-    assert binding.sdm_scan_workspace_bytes(4, 8, 8192, 64, 64, 128) == 32 * 8192 * 1536
-    # 8 streams (the long-context shape) -> 8-column slabs: 32 rows per wavefront,
-    # 2 + 2 wavefronts, the same 64 + 64 entries per token
-    assert binding.sdm_scan_workspace_bytes(1, 8, 1000, 64, 64, 128) == 8 * 1000 * 1536
+    # W = R = 64, dv = 128, 32 streams. The per-slot form uses 32-column slabs
+    # (8 rows per wavefront, 8 writer + 8 reader wavefronts; a token record holds
+    # 64 writer entries of 16 bytes and 64 reader entries of 8 bytes) with the
+    # rows split into 2 partitions (32 * 4 slabs * 2 = 256 workgroups), plus the
+    # two partitions' partial y. The shared-residual form (16-column slabs, one
+    # partition) needs less, and the workspace covers both.
+    rec = 64 * 16 + 64 * 8
+    assert binding.sdm_scan_workspace_bytes(4, 8, 8192, 64, 64, 128) == \
+        32 * 2 * 8192 * rec + 2 * 32 * 8192 * 128 * 4
+    # 8 streams (the long-context shape): 8 partitions
+    assert binding.sdm_scan_workspace_bytes(1, 8, 1000, 64, 64, 128) == \
+        8 * 8 * 1000 * rec + 8 * 8 * 1000 * 128 * 4
     assert binding.sdm_scan_workspace_bytes(0, 8, 8192, 64, 64, 128) == 0
     assert lib.sdm_scan_workspace_bytes(1, 1, 1, 0, 1, 16) == -1
     assert lib.sdm_scan_workspace_bytes(1, 1, 1, 300, 1, 16) == -1
