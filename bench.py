@@ -190,7 +190,7 @@ def main():
         "slot_row_GBps": scan_gbps,
         "roofline": {"bound": "hbm", "achieved": scan_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": scan_gbps / HBM_PEAK_GBPS, "traffic": measured_traffic(),
-                     "kernel": "sdm_scan_forward (planner + scan kernels)",
+                     "kernel": "sdm_scan_forward (plan_kernel + scan_kernel + ypart_reduce)",
                      "algorithmic_bytes_per_launch": row_bytes},
     }
     if not a.no_cpu_baseline:

@@ -108,6 +108,27 @@ def test_scan_hazard_stress(case, form, oform):
     _check("hazard", Mg, yg, Mo, yo, c["M_in"], c["idx_w"], TOL_F32)
 
 
+# (slab width, row partitions) forced through the library's tuning variables;
+# every form of the launch must give the oracle's result
+SWEEP = [(32, 1), (32, 2), (32, 4), (32, 8), (16, 2), (16, 8), (8, 4), (4, 8)]
+
+
+@pytest.mark.parametrize("slab,parts", SWEEP, ids=[f"S{s}P{p}" for s, p in SWEEP])
+def test_scan_slabs_and_row_partitions_match_oracle(slab, parts, monkeypatch):
+    monkeypatch.setenv("SDM_SCAN_SLAB", str(slab))
+    monkeypatch.setenv("SDM_SCAN_PARTS", str(parts))
+    say(f"[scan slab/partitions] S={slab} P={parts}")
+    for case in (HAZARD[0], dict(B=2, H=1, T=300, N=64, dv=32, W=16, R=16), dict(B=1, H=2, T=77, N=4096, dv=64, W=64, R=32)):
+        if case["dv"] % slab:
+            continue
+        c = _random_case(7, **case)
+        Mo, yo = oracle.scan(**c, form=oracle.EQ4)
+        Mg, yg = _run_gpu(**c, form="eq4")
+        _check(f"S={slab} P={parts} N={case['N']}", Mg, yg, Mo, yo, c["M_in"], c["idx_w"], TOL_F32)
+        M2, y2 = _run_gpu(**c, form="eq4")
+        assert np.array_equal(M2, Mg) and np.array_equal(y2, yg)       # bit-exact rerun
+
+
 @pytest.mark.parametrize("T", [1, 2, 5, 6, 7, 10, 11, 13, 61])
 def test_scan_short_and_ragged_sequences(T):
     say(f"[scan ragged] T={T}")
