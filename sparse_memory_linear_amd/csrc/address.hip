@@ -115,9 +115,19 @@ template <int NT, int NCH, typename Get>
 __device__ __forceinline__ void wave_select(Get get, int nch_rt, int k, uint32_t* okey, uint32_t* oid,
                                             int lane) {
     const int nch = NCH > 0 ? NCH : nch_rt;
+    // Radix select of the k-th largest key, most significant bit first: tau
+    // keeps the bits fixed so far with count(key >= tau) >= k. As soon as some
+    // prefix has exactly k keys at or above it, the winners are known and the
+    // lower bits cannot change them, so a token stops there (the loop ends when
+    // every token has); with distinct keys that happens once the prefix
+    // separates the k-th from the (k+1)-th key, after about half the bits.
     uint32_t tau[NT];
+    bool done[NT];
 #pragma unroll
-    for (int g = 0; g < NT; ++g) tau[g] = 0u;
+    for (int g = 0; g < NT; ++g) {
+        tau[g] = 0u;
+        done[g] = false;
+    }
     for (int bit = 31; bit >= 0; --bit) {
         int cnt[NT];
 #pragma unroll
@@ -131,9 +141,16 @@ __device__ __forceinline__ void wave_select(Get get, int nch_rt, int k, uint32_t
                 cnt[g] += popc(__ballot(kk >= (tau[g] | (1u << bit))));
             }
         }
+        bool all = true;
 #pragma unroll
-        for (int g = 0; g < NT; ++g)
-            if (cnt[g] >= k) tau[g] |= 1u << bit;
+        for (int g = 0; g < NT; ++g) {
+            if (!done[g] && cnt[g] >= k) {
+                tau[g] |= 1u << bit;
+                done[g] = cnt[g] == k;
+            }
+            all = all && done[g];
+        }
+        if (all) break;
     }
     int need[NT];
     bool cut[NT], any_cut = false;
@@ -219,6 +236,13 @@ __device__ __forceinline__ void wave_sort_desc(uint64_t (&x)[NT], int lane) {
     sort_stage<4>(x, lane, 64); sort_stage<2>(x, lane, 64); sort_stage<1>(x, lane, 64);
 }
 
+// Floats per wavefront block of LDS: the half-scores of TG tokens or the sorted
+// lists + select buffers, whichever is larger.
+__host__ __device__ inline int block_floats(int n) {
+    const int scores = TG * 2 * n, lists = TG * (128 * 2 + 64 * 2);
+    return scores > lists ? scores : lists;
+}
+
 __device__ __forceinline__ uint64_t composite(uint32_t key, uint32_t id) {
     return ((uint64_t)key << 32) | (uint64_t)(0xFFFFFFFFu - id);
 }
@@ -234,13 +258,19 @@ __global__ __launch_bounds__(NWA * 64) void address_kernel(AddressArgs a) {
     const int br = blockIdx.y;
     const int h = (int)(bh % a.H);
 
-    float* sc = reinterpret_cast<float*>(smem);      // [TOK][2][n]
-    uint32_t* pairs = reinterpret_cast<uint32_t*>(sc + TOK * 2 * n);  // [EC*64] pruned rank pairs
-    float* ls = reinterpret_cast<float*>(pairs + EC * 64) + wave * (TG * 128 * 2 + TG * 64 * 2);
+    // LDS: one block of pw floats per wavefront, then the pruned rank pairs. A
+    // block first holds the half-scores [TG][2][n] of the wavefront's tokens;
+    // once the wavefront has them in registers it reuses the block for its
+    // sorted half lists and select buffers, so a workgroup needs little more
+    // than its score tile and four workgroups fit a CU.
+    const int pw = block_floats(n);
+    float* smf = reinterpret_cast<float*>(smem);
+    auto sc_tok = [&](int m) -> float* { return smf + (m / TG) * pw + (m % TG) * 2 * n; };  // [2][n]
+    uint32_t* pairs = reinterpret_cast<uint32_t*>(smf + NWA * pw);  // [EC*64] pruned rank pairs
+    float* ls = smf + wave * pw;                      // [TG][2][64] sorted half scores
     uint32_t* lid = reinterpret_cast<uint32_t*>(ls + TG * 128);  // [TG][2][64] their sub-indices
     uint32_t* bkey = lid + TG * 128;                  // [TG][64] select output
     uint32_t* bid = bkey + TG * 64;                   // [TG][64]
-    // ls: [TG][2][64] sorted half scores of this wavefront's tokens
 
     // ---------------- a1: half-scores on MFMA ----------------
     const int m16 = lane & 15, g4 = lane >> 4;
@@ -278,7 +308,7 @@ __global__ __launch_bounds__(NWA * 64) void address_kernel(AddressArgs a) {
             }
             // D layout: lane holds tokens 4*(lane/16)+i of subkey column lane%16
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sc[((g4 * 4 + i) * 2 + j) * n + a0 + m16] = acc[i];
+            for (int i = 0; i < 4; ++i) sc_tok(g4 * 4 + i)[j * n + a0 + m16] = acc[i];
         }
     }
     __syncthreads();
@@ -286,7 +316,7 @@ __global__ __launch_bounds__(NWA * 64) void address_kernel(AddressArgs a) {
     if (a.half_out) {  // test hook: the contraction only
         for (int e = threadIdx.x; e < TOK * 2 * n; e += NWA * 64) {
             const int m = e / (2 * n);
-            if (t0 + m < a.T) a.half_out[(bh * a.T + t0) * 2 * n + e] = sc[e];
+            if (t0 + m < a.T) a.half_out[(bh * a.T + t0) * 2 * n + e] = sc_tok(m)[e - m * 2 * n];
         }
         return;
     }
@@ -320,20 +350,24 @@ __global__ __launch_bounds__(NWA * 64) void address_kernel(AddressArgs a) {
         // tokens past T run on the zero scores of their masked rows; nothing is stored
 
         // ---------------- a2: per-half top-k_h, sorted ----------------
-        for (int j = 0; j < 2; ++j) {
-            uint32_t key[TG][EH];
+        // both halves' scores into registers first: the block is reused below
+        uint32_t keys[2][TG][EH];
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int g = 0; g < TG; ++g) {
-                const float* s = sc + ((m0 + g) * 2 + j) * n;
+                const float* s = sc_tok(m0 + g) + j * n;
 #pragma unroll
                 for (int e = 0; e < EH; ++e) {
                     const int aa = e * 64 + lane;
-                    key[g][e] = aa < n ? ord_key(s[aa]) : 0u;
+                    keys[j][g][e] = aa < n ? ord_key(s[aa]) : 0u;
                 }
             }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
             wave_select<TG, EH>(
                 [&](int g, int e, uint32_t& kk, uint32_t& ii) {
-                    kk = key[g][e];
+                    kk = keys[j][g][e];
                     ii = (uint32_t)(e * 64 + lane);
                 },
                 EH, kh, bkey, bid, lane);
@@ -428,7 +462,7 @@ __global__ __launch_bounds__(NWA * 64) void address_kernel(AddressArgs a) {
 template <bool BF16, int EH>
 hipError_t launch_inst(const AddressArgs& a, hipStream_t st) {
     const int64_t ntile = (a.T + TOK - 1) / TOK;
-    const size_t lds = (size_t)TOK * 2 * a.n * 4 + EC * 64 * 4 + (size_t)NWA * (TG * 128 * 2 + TG * 64 * 2) * 4;
+    const size_t lds = (size_t)NWA * block_floats(a.n) * 4 + EC * 64 * 4;
     dim3 grid((unsigned)(ntile * a.B * a.H), (unsigned)a.nbranch);
     hipLaunchKernelGGL((address_kernel<BF16, EH>), grid, dim3(NWA * 64), lds, st, a);
     return hipGetLastError();
