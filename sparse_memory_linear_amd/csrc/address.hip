@@ -30,8 +30,9 @@
 // The selection is a chain of dependent wave-wide steps, so the 4 tokens are
 // carried through it together (independent chains interleave), and every
 // cross-lane exchange uses DPP or the gfx950 permlane swaps instead of LDS.
-// Two workgroups fit a CU's LDS, i.e. two wavefronts per SIMD, so one
-// wavefront's scalar (ballot/popcount) work overlaps another's vector work.
+// A wavefront reuses the LDS block of its own scores for its sorted lists, so a
+// workgroup needs ~33 KB (n = 256) and four fit a CU: four wavefronts per SIMD,
+// whose scalar (ballot/popcount) and vector work overlap.
 #include "sdm_internal.h"
 
 namespace sdm {
