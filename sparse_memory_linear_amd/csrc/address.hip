@@ -8,7 +8,7 @@
 // candidates are selected and weighted by a softmax over their scores.
 // Ties go to the lower index (sub-index per half, slot index at the end).
 //
-// Design (one workgroup of NWA = 4 wavefronts per 16 tokens of one (b, h, branch)):
+// Design (one workgroup of NWA = 8 wavefronts per 16 tokens of one (b, h, branch)):
 //   a1  half-scores: a [16 tokens x d_h] x [d_h x 16 subkeys] MFMA tile per
 //       step (v_mfma_f32_16x16x32_bf16 for bf16 inputs, 16x16x4 f32 for fp32),
 //       fp32 accumulation, staged in LDS as [token][half][subkey].
@@ -26,20 +26,21 @@
 //       score (a tie that the slot order could decide differently), the token
 //       is redone over the full k_h x k_h grid.
 //   a4  softmax in fp32 (max-subtracted, expf), butterfly sum.
-// The wavefronts share the MFMA tiles of a1; then each selects TG = 4 tokens.
-// The selection is a chain of dependent wave-wide steps, so the 4 tokens are
+// The wavefronts share the MFMA tiles of a1; then each selects TG = 2 tokens.
+// The selection is a chain of dependent wave-wide steps, so the 2 tokens are
 // carried through it together (independent chains interleave), and every
 // cross-lane exchange uses DPP or the gfx950 permlane swaps instead of LDS.
 // A wavefront reuses the LDS block of its own scores for its sorted lists, so a
-// workgroup needs ~33 KB (n = 256) and four fit a CU: four wavefronts per SIMD,
-// whose scalar (ballot/popcount) and vector work overlap.
+// workgroup needs ~33 KB (n = 256) and four fit a CU: eight wavefronts per
+// SIMD, whose scalar (ballot/popcount) and vector work overlap. (Measured at
+// n = 256, k = 64: 2 tokens per wavefront beat 1, 4 and 8.)
 #include "sdm_internal.h"
 
 namespace sdm {
 namespace {
 
 constexpr int TOK = 16;       // tokens per workgroup = one MFMA M tile
-constexpr int TG = 4;         // tokens selected together by one wavefront
+constexpr int TG = 2;         // tokens selected together by one wavefront
 constexpr int NWA = TOK / TG; // wavefronts per workgroup
 constexpr int EC = 5;         // candidate chunks per lane: sum_{i<=64} floor(64/i) = 280 <= 320
 
