@@ -145,6 +145,7 @@ struct PlanArgs {
     const int32_t* idx_r; const float* wt_r; int R;
     const float* alpha; const float* beta;
     uint8_t* plan;                         // [NS][P][Tc][rec]
+    uint32_t* maxc;                        // [NS][P][2]: most writes / reads of one token (zeroed)
     int64_t Tc, TS, N;
     int D, G, NWW, NWR, TT, pb, P, pshift;
     int64_t ntile;
@@ -186,8 +187,9 @@ __device__ __forceinline__ uint32_t fwd_bits(const uint32_t* ht, const uint32_t*
     return best < 0 ? 0u : ENT_FWD | ((uint32_t)(cur - best) << DIST_SHIFT) | (bp << POS_SHIFT);
 }
 
-__global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(PlanArgs a) {
+__global__ __launch_bounds__(PLAN_THREADS) __attribute__((amdgpu_waves_per_eu(4))) void plan_kernel(PlanArgs a) {
     __shared__ uint32_t ht[HT_CAP];
+    __shared__ uint32_t smax[2][MAX_PARTS];   // this tile's largest per-partition counts
     extern __shared__ uint32_t bm[];          // ceil(N / 32) words
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const uint64_t below = (1ull << lane) - 1ull;
@@ -211,6 +213,7 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(PlanArgs a) {
         reinterpret_cast<uint4*>(ht)[i] = make_uint4(HT_EMPTY, HT_EMPTY, HT_EMPTY, HT_EMPTY);
     const int nbm = (int)((N + 31) >> 5);
     for (int i = tid; i < nbm; i += PLAN_THREADS) bm[i] = 0u;
+    if (tid < 2 * MAX_PARTS) smax[tid / MAX_PARTS][tid % MAX_PARTS] = 0u;
     __syncthreads();
 
     // phase 1: the writes of tokens [h0, t1), with their rank inside their partition
@@ -242,7 +245,8 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(PlanArgs a) {
     }
     __syncthreads();
 
-    // phase 2: the records of tokens [t0, t1): writes, then reads, then padding
+    // phase 2: the records of tokens [t0, t1): writes, then reads, then padding;
+    // the largest per-partition counts are collected in LDS
     const int n2 = (int)(t1 - t0);
     for (int k0 = wave; k0 < n2; k0 += PLAN_WAVES * PNB) {
         for (int br = 0; br < 2; ++br) {
@@ -293,6 +297,7 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(PlanArgs a) {
 #pragma unroll
                 for (int q = 0; q < MAX_PARTS; ++q) {
                     if (q >= P) break;
+                    if (lane == 0) atomicMax(&smax[br][q], (uint32_t)cnt[u][q]);
                     uint8_t* rec = Ps + ((int64_t)q * T + tt) * REC;
                     for (int k = cnt[u][q] + lane; k < cap; k += 64) {
                         if (isw)
@@ -304,6 +309,12 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(PlanArgs a) {
             }
         }
     }
+    __syncthreads();
+    if (tid < 2 * P) atomicMax(&a.maxc[(s * P + tid / 2) * 2 + tid % 2], smax[tid % 2][tid / 2]);
+}
+
+__global__ void zero_u32(uint32_t* p, int n) {
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0u;
 }
 
 // ------------------------------------------------------------------ scan
@@ -403,6 +414,7 @@ __device__ __forceinline__ float rows_reduce(float4 x) {
 
 struct ScanKArgs {
     const uint8_t* plan;  // [NS][P][T][rec]
+    const uint32_t* maxc; // [NS][P][2]: most writes / reads of one token in a partition
     const void* v;
     float* M;
     float* y;       // y of (stream s, partition p) at y + s * ys + p * yp
@@ -459,6 +471,20 @@ __global__ __launch_bounds__(SlabCfg<S>::NWMAX * 64) void scan_kernel(ScanKArgs 
 
     // partial sums of absent readers stay zero (made visible by the first barrier)
     for (int i = threadIdx.x; i < 2 * NRMAX * S; i += blockDim.x) ybuf[i] = 0.f;
+
+    // The planner packs a partition's accesses to the front of its records, so
+    // wavefronts whose slots no token of this launch reaches have nothing to do:
+    // they only keep the barrier count (one barrier per token, one at the end).
+    // Reader 0 always runs (it stores y); the shared-residual form uses all
+    // writers' partial sums and runs every wavefront.
+    if constexpr (FORM == 0) {
+        const uint32_t* mc = a.maxc + (s * a.P + part) * 2;
+        const bool idle = writer ? (uint32_t)(wave * G) >= mc[0] : (rw > 0 && (uint32_t)(rw * G) >= mc[1]);
+        if (idle) {
+            for (int t = 0; t <= T; ++t) __syncthreads();
+            return;
+        }
+    }
 
     auto row_off = [&](uint32_t pk) -> uint32_t {
         return (pk & ENT_INVALID) ? OOB : __umul24(pk & ROW_MASK, dv4) + col4;
@@ -625,13 +651,15 @@ struct Cfg {
 
 // Bytes of workspace one launch needs: plan records, then (P > 1) partial y.
 struct WsLayout {
-    int64_t plan_bytes, ypart_off, total;
+    int64_t plan_bytes, ypart_off, maxc_off, total;
 };
 WsLayout ws_layout(const Cfg& c, int64_t NS, int64_t Tc, int dv) {
     WsLayout w;
     w.plan_bytes = NS * c.P * Tc * c.g.rec();
     w.ypart_off = (w.plan_bytes + 255) / 256 * 256;
-    w.total = c.P > 1 ? w.ypart_off + (int64_t)c.P * NS * Tc * dv * 4 : w.plan_bytes;
+    const int64_t yend = c.P > 1 ? w.ypart_off + (int64_t)c.P * NS * Tc * dv * 4 : w.plan_bytes;
+    w.maxc_off = (yend + 255) / 256 * 256;
+    w.total = w.maxc_off + NS * c.P * 2 * 4;
     return w;
 }
 
@@ -659,13 +687,17 @@ hipError_t launch_scan_slab(const ScanArgs& a, const Cfg& c, hipStream_t st) {
     const int esz = a.v_bf16 ? 2 : 4;
     uint8_t* plan = static_cast<uint8_t*>(a.workspace);
     float* ypart = reinterpret_cast<float*>(plan + wl.ypart_off);
+    uint32_t* maxc = reinterpret_cast<uint32_t*>(plan + wl.maxc_off);
+    const int nmax = (int)(a.NS * c.P * 2);
     for (int64_t c0 = 0; c0 < a.T; c0 += Tc) {
         const int64_t Tn = a.T - c0 < Tc ? a.T - c0 : Tc;
+        hipLaunchKernelGGL(zero_u32, dim3((unsigned)((nmax + 255) / 256)), dim3(256), 0, st, maxc, nmax);
         PlanArgs p{};
         p.idx_w = a.idx_w + c0 * a.W; p.wt_w = a.wt_w + c0 * a.W; p.W = a.W;
         p.idx_r = a.idx_r + c0 * a.R; p.wt_r = a.wt_r + c0 * a.R; p.R = a.R;
         p.alpha = a.alpha + c0; p.beta = a.beta + c0;
         p.plan = plan;
+        p.maxc = maxc;
         p.Tc = Tn; p.TS = a.T; p.N = a.N;
         p.D = D; p.G = g.G; p.NWW = g.NWW; p.NWR = g.NWR; p.TT = TT; p.pb = pb; p.P = c.P; p.pshift = psh;
         p.ntile = (Tn + TT - 1) / TT;
@@ -674,6 +706,7 @@ hipError_t launch_scan_slab(const ScanArgs& a, const Cfg& c, hipStream_t st) {
         if (e != hipSuccess) return e;
         ScanKArgs k{};
         k.plan = plan;
+        k.maxc = maxc;
         k.v = static_cast<const char*>(a.v) + c0 * a.dv * esz;
         k.M = a.M;
         if (c.P > 1) {

@@ -53,12 +53,13 @@ def test_workspace_size_is_pure_host_logic(lib):
     # rows split into 2 partitions (32 * 4 slabs * 2 = 256 workgroups), plus the
     # two partitions' partial y. The shared-residual form (16-column slabs, one
     # partition) needs less, and the workspace covers both.
+    # and the largest per-token count of each (stream, partition, branch)
     rec = 64 * 16 + 64 * 8
     assert binding.sdm_scan_workspace_bytes(4, 8, 8192, 64, 64, 128) == \
-        32 * 2 * 8192 * rec + 2 * 32 * 8192 * 128 * 4
+        32 * 2 * 8192 * rec + 2 * 32 * 8192 * 128 * 4 + 32 * 2 * 2 * 4
     # 8 streams (the long-context shape): 8 partitions
     assert binding.sdm_scan_workspace_bytes(1, 8, 1000, 64, 64, 128) == \
-        8 * 8 * 1000 * rec + 8 * 8 * 1000 * 128 * 4
+        8 * 8 * 1000 * rec + 8 * 8 * 1000 * 128 * 4 + 8 * 8 * 2 * 4
     assert binding.sdm_scan_workspace_bytes(0, 8, 8192, 64, 64, 128) == 0
     assert lib.sdm_scan_workspace_bytes(1, 1, 1, 0, 1, 16) == -1
     assert lib.sdm_scan_workspace_bytes(1, 1, 1, 300, 1, 16) == -1
