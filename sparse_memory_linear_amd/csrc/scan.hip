@@ -412,6 +412,24 @@ __device__ __forceinline__ float rows_reduce(float4 x) {
     return c;
 }
 
+// Sum of the first Q partial-sum slots (stride S) as a balanced tree. Slots of
+// readers that do not run hold zero, so any power of two Q >= the number of
+// running readers gives the same sum: the tree over 2Q adds a zero subtree.
+template <int Q, int S>
+__device__ __forceinline__ float tree_sum(const float* p) {
+    if constexpr (Q == 1) return p[0];
+    else return tree_sum<Q / 2, S>(p) + tree_sum<Q / 2, S>(p + (Q / 2) * S);
+}
+template <int NRMAX, int S>
+__device__ __forceinline__ float readers_sum(const float* p, int nra) {
+    if (nra <= 1) return tree_sum<1, S>(p);
+    if (nra <= 2) return tree_sum<2, S>(p);
+    if constexpr (NRMAX >= 4) if (nra <= 4) return tree_sum<4, S>(p);
+    if constexpr (NRMAX >= 8) if (nra <= 8) return tree_sum<8, S>(p);
+    if constexpr (NRMAX >= 16) return tree_sum<16, S>(p);
+    return tree_sum<NRMAX, S>(p);
+}
+
 struct ScanKArgs {
     const uint8_t* plan;  // [NS][P][T][rec]
     const uint32_t* maxc; // [NS][P][2]: most writes / reads of one token in a partition
@@ -477,6 +495,8 @@ __global__ __launch_bounds__(SlabCfg<S>::NWMAX * 64) void scan_kernel(ScanKArgs 
     // they only keep the barrier count (one barrier per token, one at the end).
     // Reader 0 always runs (it stores y); the shared-residual form uses all
     // writers' partial sums and runs every wavefront.
+    // nra: reader wavefronts whose partial sums reader 0 adds (a power of two)
+    int nra = NWR;
     if constexpr (FORM == 0) {
         const uint32_t* mc = a.maxc + (s * a.P + part) * 2;
         const bool idle = writer ? (uint32_t)(wave * G) >= mc[0] : (rw > 0 && (uint32_t)(rw * G) >= mc[1]);
@@ -484,6 +504,12 @@ __global__ __launch_bounds__(SlabCfg<S>::NWMAX * 64) void scan_kernel(ScanKArgs 
             for (int t = 0; t <= T; ++t) __syncthreads();
             return;
         }
+        nra = ((int)mc[1] + G - 1) / G;
+    }
+    {
+        int q = 1;
+        while (q < nra) q *= 2;
+        nra = q;
     }
 
     auto row_off = [&](uint32_t pk) -> uint32_t {
@@ -531,15 +557,14 @@ __global__ __launch_bounds__(SlabCfg<S>::NWMAX * 64) void scan_kernel(ScanKArgs 
     auto read_token = [&](int t, int slot, int2 e, float4 pre) {
         if constexpr (FORM == 1) __syncthreads();
         __syncthreads();
+        // reader 0 first sums the previous token's partials (complete since
+        // this token's barrier), so their LDS reads overlap the row sum below
+        float acc = 0.f;
+        if (rw == 0)  // uniform per wavefront; no memory operation inside
+            acc = readers_sum<NRMAX, S>(ybuf + ((t - 1) & 1) * NRMAX * S + ylane, nra);
         const uint32_t pk = (uint32_t)e.x;
         const float part = rows_reduce<L>(f4_scale(__int_as_float(e.y), source(slot, pk, pre)));
         if ((lane & 15) < L) ybuf[((t & 1) * NRMAX + rw) * S + 4 * (lane & 15) + (lane >> 4)] = part;
-        float acc = 0.f;
-        if (rw == 0) {  // uniform per wavefront; no memory operation inside
-            const float* pb = ybuf + ((t - 1) & 1) * NRMAX * S + ylane;
-#pragma unroll
-            for (int q = 0; q < NRMAX; ++q) acc += pb[q * S];
-        }
         st_f1(acc, Ry, t > 0 ? y_off : OOB, (uint32_t)(t > 0 ? t - 1 : 0) * dv4);
     };
 
@@ -606,9 +631,7 @@ __global__ __launch_bounds__(SlabCfg<S>::NWMAX * 64) void scan_kernel(ScanKArgs 
     // the last token's partial sums
     __syncthreads();
     if (!writer && rw == 0 && T > 0) {
-        const float* pb = ybuf + ((T - 1) & 1) * NRMAX * S + ylane;
-        float acc = 0.f;
-        for (int q = 0; q < NRMAX; ++q) acc += pb[q * S];
+        const float acc = readers_sum<NRMAX, S>(ybuf + ((T - 1) & 1) * NRMAX * S + ylane, nra);
         st_f1(acc, Ry, y_off, (uint32_t)(T - 1) * dv4);
     }
 }
