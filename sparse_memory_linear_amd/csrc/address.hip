@@ -215,11 +215,11 @@ template <int J, int NT>
 __device__ __forceinline__ void sort_stage(uint64_t (&x)[NT], int lane, int k) {
 #pragma unroll
     for (int g = 0; g < NT; ++g) {
+        // keep the larger of (x, partner) where the lane keeps the maximum, the
+        // smaller elsewhere: one compare, one mask operation, one select
         const uint64_t o = xlane64<J>(x[g], lane);
         const bool keep_max = (((lane & J) == 0) == ((lane & k) == 0));
-        const uint64_t mx = x[g] > o ? x[g] : o;
-        const uint64_t mn = x[g] > o ? o : x[g];
-        x[g] = keep_max ? mx : mn;
+        x[g] = ((x[g] > o) == keep_max) ? x[g] : o;
     }
 }
 
@@ -275,42 +275,73 @@ __global__ __launch_bounds__(NWA * 64) void address_kernel(AddressArgs a) {
     uint32_t* bid = bkey + TG * 64;                   // [TG][64]
 
     // ---------------- a1: half-scores on MFMA ----------------
+    // The 2 * n/16 subkey tiles are dealt round-robin to the wavefronts. For each
+    // k-step a wavefront loads its tokens' half-queries once and the subkeys of
+    // all its tiles together, so the loads of a step are in flight at once.
+    constexpr int TPW = (2 * (64 * EH / 16) + NWA - 1) / NWA;  // most tiles per wavefront
+    const int nt16 = n / 16, ntiles = 2 * nt16;
     const int m16 = lane & 15, g4 = lane >> 4;
     const int64_t tq = t0 + m16;
     const bool tok_ok = tq < a.T;
-    // the 2 * n/16 subkey tiles are dealt round-robin to the wavefronts
-    for (int tile = wave; tile < 2 * (n / 16); tile += NWA) {
-        const int j = tile / (n / 16), a0 = (tile % (n / 16)) * 16;
-        {
-            f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-            if constexpr (BF16) {
-                const uint16_t* q = static_cast<const uint16_t*>(a.q[br]) +
-                                    ((bh * a.T + (tok_ok ? tq : 0)) * 2 + j) * dh;
-                const uint16_t* kp = static_cast<const uint16_t*>(a.K[br]) +
-                                     (((int64_t)h * 2 + j) * n + a0 + m16) * dh;
-                for (int c0 = 0; c0 < dh; c0 += 32) {
-                    uint4 qa = tok_ok ? *reinterpret_cast<const uint4*>(q + c0 + g4 * 8)
-                                      : make_uint4(0u, 0u, 0u, 0u);
-                    uint4 kb = *reinterpret_cast<const uint4*>(kp + c0 + g4 * 8);
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        __builtin_bit_cast(bf16x8_t, qa), __builtin_bit_cast(bf16x8_t, kb), acc, 0, 0, 0);
-                }
-            } else {
-                const float* q = static_cast<const float*>(a.q[br]) +
-                                 ((bh * a.T + (tok_ok ? tq : 0)) * 2 + j) * dh;
-                const float* kp = static_cast<const float*>(a.K[br]) +
-                                  (((int64_t)h * 2 + j) * n + a0 + m16) * dh;
-                for (int c0 = 0; c0 < dh; c0 += 8) {
-                    float2 qa = tok_ok ? *reinterpret_cast<const float2*>(q + c0 + g4 * 2)
-                                       : make_float2(0.f, 0.f);
-                    float2 kb = *reinterpret_cast<const float2*>(kp + c0 + g4 * 2);
-                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qa.x, kb.x, acc, 0, 0, 0);
-                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qa.y, kb.y, acc, 0, 0, 0);
+    f32x4_t acc[TPW];
+    int64_t krow[TPW];  // element offset of this lane's subkey row of each tile
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+        acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        const int tile = wave + i * NWA, j = tile / nt16, a0 = (tile % nt16) * 16;
+        krow[i] = (((int64_t)h * 2 + j) * n + a0 + m16) * dh;
+    }
+    const int64_t qrow = (bh * a.T + (tok_ok ? tq : 0)) * 2 * dh;  // half 0; half 1 follows
+    if constexpr (BF16) {
+        const uint16_t* q = static_cast<const uint16_t*>(a.q[br]) + qrow;
+        const uint16_t* kp = static_cast<const uint16_t*>(a.K[br]);
+        for (int c0 = 0; c0 < dh; c0 += 32) {
+            uint4 qa[2], kb[TPW];
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj)
+                qa[jj] = tok_ok ? *reinterpret_cast<const uint4*>(q + jj * dh + c0 + g4 * 8) : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+            for (int i = 0; i < TPW; ++i)
+                if (wave + i * NWA < ntiles) kb[i] = *reinterpret_cast<const uint4*>(kp + krow[i] + c0 + g4 * 8);
+#pragma unroll
+            for (int i = 0; i < TPW; ++i) {
+                const int tile = wave + i * NWA;
+                if (tile < ntiles)
+                    acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(bf16x8_t, tile < nt16 ? qa[0] : qa[1]), __builtin_bit_cast(bf16x8_t, kb[i]),
+                        acc[i], 0, 0, 0);
+            }
+        }
+    } else {
+        const float* q = static_cast<const float*>(a.q[br]) + qrow;
+        const float* kp = static_cast<const float*>(a.K[br]);
+        for (int c0 = 0; c0 < dh; c0 += 8) {
+            float2 qa[2], kb[TPW];
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj)
+                qa[jj] = tok_ok ? *reinterpret_cast<const float2*>(q + jj * dh + c0 + g4 * 2) : make_float2(0.f, 0.f);
+#pragma unroll
+            for (int i = 0; i < TPW; ++i)
+                if (wave + i * NWA < ntiles) kb[i] = *reinterpret_cast<const float2*>(kp + krow[i] + c0 + g4 * 2);
+#pragma unroll
+            for (int i = 0; i < TPW; ++i) {
+                const int tile = wave + i * NWA;
+                if (tile < ntiles) {
+                    const float2 qv = tile < nt16 ? qa[0] : qa[1];
+                    acc[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(qv.x, kb[i].x, acc[i], 0, 0, 0);
+                    acc[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(qv.y, kb[i].y, acc[i], 0, 0, 0);
                 }
             }
-            // D layout: lane holds tokens 4*(lane/16)+i of subkey column lane%16
+        }
+    }
+    // D layout: lane holds tokens 4*(lane/16)+i of subkey column lane%16
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sc_tok(g4 * 4 + i)[j * n + a0 + m16] = acc[i];
+    for (int i = 0; i < TPW; ++i) {
+        const int tile = wave + i * NWA;
+        if (tile < ntiles) {
+            const int j = tile / nt16, a0 = (tile % nt16) * 16;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sc_tok(g4 * 4 + r)[j * n + a0 + m16] = acc[i][r];
         }
     }
     __syncthreads();
