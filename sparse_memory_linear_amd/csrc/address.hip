@@ -217,9 +217,28 @@ __device__ __forceinline__ void sort_stage(uint64_t (&x)[NT], int lane, int k) {
     for (int g = 0; g < NT; ++g) {
         // keep the larger of (x, partner) where the lane keeps the maximum, the
         // smaller elsewhere: one compare, one mask operation, one select
-        const uint64_t o = xlane64<J>(x[g], lane);
         const bool keep_max = (((lane & J) == 0) == ((lane & k) == 0));
-        x[g] = ((x[g] > o) == keep_max) ? x[g] : o;
+        if constexpr (J >= 16) {
+            // a permlane swap of (v, v) returns {v, partner's v} in an order that
+            // depends only on the lane half, the same order for both words; max
+            // and min of the pair are then the same on both lanes
+            const uint32_t lo = (uint32_t)x[g], hi = (uint32_t)(x[g] >> 32);
+            uint32_t l0, l1, h0, h1;
+            if constexpr (J == 16) {
+                const auto pl = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+                const auto ph = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+                l0 = pl[0]; l1 = pl[1]; h0 = ph[0]; h1 = ph[1];
+            } else {
+                const auto pl = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+                const auto ph = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+                l0 = pl[0]; l1 = pl[1]; h0 = ph[0]; h1 = ph[1];
+            }
+            const uint64_t a0 = ((uint64_t)h0 << 32) | l0, a1 = ((uint64_t)h1 << 32) | l1;
+            x[g] = ((a0 > a1) == keep_max) ? a0 : a1;
+        } else {
+            const uint64_t o = xlane64<J>(x[g], lane);
+            x[g] = ((x[g] > o) == keep_max) ? x[g] : o;
+        }
     }
 }
 
@@ -267,7 +286,9 @@ __global__ __launch_bounds__(NWA * 64) void address_kernel(AddressArgs a) {
     // than its score tile and four workgroups fit a CU.
     const int pw = block_floats(n);
     float* smf = reinterpret_cast<float*>(smem);
-    auto sc_tok = [&](int m) -> float* { return smf + (m / TG) * pw + (m % TG) * 2 * n; };  // [2][n]
+    auto sc_tok = [&](int m) -> float* {  // [2][n]
+        return smf + __umul24((uint32_t)(m / TG), (uint32_t)pw) + __umul24((uint32_t)(m % TG), (uint32_t)(2 * n));
+    };
     uint32_t* pairs = reinterpret_cast<uint32_t*>(smf + NWA * pw);  // [EC*64] pruned rank pairs
     float* ls = smf + wave * pw;                      // [TG][2][64] sorted half scores
     uint32_t* lid = reinterpret_cast<uint32_t*>(ls + TG * 128);  // [TG][2][64] their sub-indices
@@ -426,7 +447,7 @@ __global__ __launch_bounds__(NWA * 64) void address_kernel(AddressArgs a) {
 #pragma unroll
             for (int g = 0; g < TG; ++g) {
                 ck[g][e] = c < C ? ord_key(ls[(g * 2) * 64 + i] + ls[(g * 2 + 1) * 64 + jj]) : 0u;
-                ci[g][e] = lid[(g * 2) * 64 + i] * (uint32_t)n + lid[(g * 2 + 1) * 64 + jj];
+                ci[g][e] = __umul24(lid[(g * 2) * 64 + i], (uint32_t)n) + lid[(g * 2 + 1) * 64 + jj];
             }
         }
         wave_select<TG, EC>(
