@@ -635,6 +635,113 @@ __global__ __launch_bounds__(SlabCfg<S>::NWMAX * 64) void scan_kernel(ScanKArgs 
         st_f1(acc, Ry, y_off, (uint32_t)(T - 1) * dv4);
     }
 }
+// ------------------------------------------------------------------ short scans
+// For a few tokens per call (decoding: one token per sequence and call, the
+// table kept between calls) the prefetch pipeline and its planner cost more
+// than they hide. The direct form reads the indices itself and issues a
+// token's row loads only after the barrier that closes the previous token, so
+// every load sees every earlier store (same workgroup, same CU) and nothing is
+// forwarded. Per token: writers load, update and store their rows; barrier;
+// readers load theirs (after this token's writes) and reduce; barrier; reader
+// 0 sums the readers' partials and stores y. The indices, weights, gates and v
+// of the next token are loaded while the current one runs.
+struct DirectArgs {
+    const int32_t* idx_w; const float* wt_w; int W;
+    const int32_t* idx_r; const float* wt_r; int R;
+    const float* alpha; const float* beta;
+    const void* v;
+    float* M;
+    float* y;
+    int T;
+    int64_t N;
+    int dv, nslab;
+    int64_t NS;
+    int NWW, NWR;
+};
+
+template <int S, int FORM, bool VBF16>
+__global__ __launch_bounds__(SlabCfg<S>::NWMAX * 64) void scan_direct_kernel(DirectArgs a) {
+    constexpr int L = S / 4, G = 64 / L;
+    constexpr int NWMAX = SlabCfg<S>::NWMAX, NRMAX = nrmax<S>();
+    using VL = VLoad<VBF16>;
+    using V4 = typename VL::T4;
+    const int NWW = a.NWW, NWR = a.NWR, T = a.T, dv = a.dv, W = a.W, R = a.R;
+    __shared__ float ybuf[NRMAX * S];
+    __shared__ float4 vbuf[NWMAX * L];
+
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane / L, cc = lane % L;
+    const int b = blockIdx.x, xcd = b & 7, kq = b >> 3;
+    const int64_t s = (int64_t)(kq / a.nslab) * 8 + xcd;
+    const int slab = kq % a.nslab;
+    if (s >= a.NS) return;  // uniform over the workgroup
+    const int col = slab * S + cc * 4;
+    const bool writer = wave < NWW;
+    const int rw = wave - NWW;
+    const int pos = writer ? wave * G + r : rw * G + r;  // access position of this lane's row
+    const int K = writer ? W : R;
+    const bool has = pos < K;
+    const int32_t* ix = (writer ? a.idx_w : a.idx_r) + s * (int64_t)T * K;
+    const float* wx = (writer ? a.wt_w : a.wt_r) + s * (int64_t)T * K;
+    const rsrc_t Rm = make_rsrc(a.M + s * a.N * dv, a.N * dv * 4);
+    const rsrc_t Rv = make_rsrc(static_cast<const char*>(a.v) + s * (int64_t)T * dv * VL::ESZ,
+                                (int64_t)T * dv * VL::ESZ);
+    const rsrc_t Ry = make_rsrc(a.y + s * (int64_t)T * dv, (int64_t)T * dv * 4);
+    const uint32_t dv4 = (uint32_t)dv * 4u, col4 = (uint32_t)col * 4u;
+    const uint32_t y_off = (!writer && rw == 0 && lane < S) ? (uint32_t)(slab * S + lane) * 4u : OOB;
+    const int ylane = lane < S ? lane : 0;
+    int nra = 1;
+    while (nra < NWR) nra *= 2;
+    for (int i = threadIdx.x; i < NRMAX * S; i += blockDim.x) ybuf[i] = 0.f;
+    __syncthreads();
+
+    auto off_of = [&](int32_t row) -> uint32_t {
+        return (row >= 0 && row < a.N) ? __umul24((uint32_t)row, dv4) + col4 : OOB;
+    };
+    // this lane's access of token t: row offset and weight (0 when absent)
+    int32_t row_n = has ? ix[pos] : -1;
+    float w_n = has ? wx[pos] : 0.f;
+    float al_n = a.alpha[s * (int64_t)T], be_n = a.beta[s * (int64_t)T];
+    V4 v_n = VL::load(Rv, (uint32_t)col * VL::ESZ, 0u);
+    for (int t = 0; t < T; ++t) {
+        const uint32_t off = off_of(row_n);
+        const float w = off == OOB ? 0.f : w_n, al = al_n, be = be_n;
+        const V4 vt = v_n;
+        if (t + 1 < T) {  // uniform: the next token's indices, weights, gates and v
+            const int64_t o = (int64_t)(t + 1) * K + pos;
+            row_n = has ? ix[o] : -1;
+            w_n = has ? wx[o] : 0.f;
+            al_n = a.alpha[s * (int64_t)T + t + 1];
+            be_n = a.beta[s * (int64_t)T + t + 1];
+            v_n = VL::load(Rv, (uint32_t)col * VL::ESZ, (uint32_t)(t + 1) * (uint32_t)dv * VL::ESZ);
+        }
+        if (writer) {
+            const float4 pre = ld_f4(Rm, off, 0u);  // after the barrier that closed token t-1
+            const float4 mt = f4_scale(al, pre);
+            float4 pred = mt;
+            if constexpr (FORM == 1) {
+                const float part = rows_reduce<L>(f4_scale(w, mt));
+                if ((lane & 15) < L) reinterpret_cast<float*>(vbuf)[wave * S + 4 * (lane & 15) + (lane >> 4)] = part;
+                __syncthreads();
+                pred = vbuf[cc];
+                for (int q = 1; q < NWW; ++q) pred = f4_add(pred, vbuf[q * L + cc]);
+            }
+            st_f4(f4_fma(be * w, f4_sub(VL::f(vt), pred), mt), Rm, off, 0u);
+            __syncthreads();  // B1: this token's rows are written
+            __syncthreads();  // B2
+        } else {
+            if constexpr (FORM == 1) __syncthreads();
+            __syncthreads();  // B1
+            const float4 cur = ld_f4(Rm, off, 0u);  // the rows after this token's writes
+            const float part = rows_reduce<L>(f4_scale(w, cur));
+            if ((lane & 15) < L) ybuf[rw * S + 4 * (lane & 15) + (lane >> 4)] = part;
+            __syncthreads();  // B2: all partial sums are in
+            float acc = 0.f;
+            if (rw == 0) acc = readers_sum<NRMAX, S>(ybuf + ylane, nra);
+            st_f1(acc, Ry, y_off, (uint32_t)t * dv4);
+        }
+    }
+}
+
 // Ring reuse: the writer of token t overwrites slot t % UR, last used by token
 // t - UR; its readers (tokens up to t - UR + D) have finished once every
 // wavefront passed barrier B_{t-1}, which needs t - UR + D <= t - 2, i.e.
@@ -762,6 +869,27 @@ hipError_t launch_scan_slab(const ScanArgs& a, const Cfg& c, hipStream_t st) {
     return hipSuccess;
 }
 
+template <int S>
+hipError_t launch_scan_direct(const ScanArgs& a, hipStream_t st) {
+    const Geom g = make_geom(S, a.W, a.R);
+    DirectArgs d{};
+    d.idx_w = a.idx_w; d.wt_w = a.wt_w; d.W = a.W;
+    d.idx_r = a.idx_r; d.wt_r = a.wt_r; d.R = a.R;
+    d.alpha = a.alpha; d.beta = a.beta; d.v = a.v; d.M = a.M; d.y = a.y;
+    d.T = (int)a.T; d.N = a.N; d.dv = a.dv; d.nslab = a.dv / S; d.NS = a.NS;
+    d.NWW = g.NWW; d.NWR = g.NWR;
+    const int64_t nblk = ((a.NS + 7) / 8) * 8 * d.nslab;
+    dim3 grid((unsigned)nblk), block((unsigned)(g.nw() * 64));
+    if (a.form == 0) {
+        if (a.v_bf16) hipLaunchKernelGGL((scan_direct_kernel<S, 0, true>), grid, block, 0, st, d);
+        else hipLaunchKernelGGL((scan_direct_kernel<S, 0, false>), grid, block, 0, st, d);
+    } else {
+        if (a.v_bf16) hipLaunchKernelGGL((scan_direct_kernel<S, 1, true>), grid, block, 0, st, d);
+        else hipLaunchKernelGGL((scan_direct_kernel<S, 1, false>), grid, block, 0, st, d);
+    }
+    return hipGetLastError();
+}
+
 int slab_nwmax(int S) {
     return S == 32 ? SlabCfg<32>::NWMAX : S == 16 ? SlabCfg<16>::NWMAX : S == 8 ? SlabCfg<8>::NWMAX : SlabCfg<4>::NWMAX;
 }
@@ -863,7 +991,23 @@ int64_t scan_workspace_bytes(int64_t NS, int64_t T, int W, int R, int dv) {
     return need;
 }
 
+// Calls of at most this many tokens take the direct form (SDM_SCAN_DIRECT_T
+// overrides; 0 turns it off).
+int64_t direct_max_tokens() {
+    const char* e = getenv("SDM_SCAN_DIRECT_T");
+    return e ? atoll(e) : 8;
+}
+
 hipError_t launch_scan(const ScanArgs& a, hipStream_t st) {
+    if (a.T <= direct_max_tokens() && a.T * (int64_t)a.dv * 4 < 0x7FFFFFFF) {
+        switch (pick_slab(a.NS, a.W, a.R, a.dv, env_int("SDM_SCAN_SLAB"))) {
+            case 32: return launch_scan_direct<32>(a, st);
+            case 16: return launch_scan_direct<16>(a, st);
+            case 8: return launch_scan_direct<8>(a, st);
+            case 4: return launch_scan_direct<4>(a, st);
+            default: break;
+        }
+    }
     const Cfg c = choose_cfg(a.NS, a.W, a.R, a.dv, a.form);
     switch (c.S) {
         case 32: return launch_scan_slab<32>(a, c, st);

@@ -129,6 +129,39 @@ def test_scan_slabs_and_row_partitions_match_oracle(slab, parts, monkeypatch):
         assert np.array_equal(M2, Mg) and np.array_equal(y2, yg)       # bit-exact rerun
 
 
+@pytest.mark.parametrize("case", HAZARD + [dict(B=2, H=2, T=130, N=4096, dv=64, W=64, R=32, bf16=True)],
+                         ids=[f"N{c['N']}W{c['W']}dv{c['dv']}" for c in HAZARD] + ["N4096W64dv64"])
+@pytest.mark.parametrize("form,oform", FORMS, ids=["eq4", "fig2"])
+def test_direct_short_scan_matches_oracle(case, form, oform, monkeypatch):
+    """The planner-free form used for short calls, forced for whole sequences:
+    every token's loads follow the previous token's barrier, so heavy row
+    reuse must still give the oracle's result."""
+    monkeypatch.setenv("SDM_SCAN_DIRECT_T", "100000")
+    say(f"[scan direct] {case} form={form}")
+    c = _random_case(5, **case)
+    Mo, yo = oracle.scan(**c, form=oform)
+    Mg, yg = _run_gpu(**c, form=form)
+    _check("direct", Mg, yg, Mo, yo, c["M_in"], c["idx_w"], TOL_F32)
+
+
+def test_decode_one_token_per_call_matches_one_scan():
+    """Decoding: T = 1 per call, the table carried between calls, equals the
+    oracle's scan over the whole sequence."""
+    c = _random_case(9, B=8, H=2, T=40, N=4096, dv=64, W=16, R=16, bf16=True)
+    Mo, yo = oracle.scan(**c, form=oracle.EQ4)
+    t = lambda a: (a if isinstance(a, torch.Tensor) else torch.from_numpy(np.ascontiguousarray(a))).to(DEV)
+    M = t(c["M_in"]).float().contiguous().clone()
+    ys = []
+    for k in range(40):
+        sl = lambda a: t(a)[:, :, k:k + 1].contiguous()
+        ys.append(sdm.sdm_scan_forward(sl(c["idx_w"]).int(), sl(c["wt_w"]).float(), sl(c["idx_r"]).int(),
+                                       sl(c["wt_r"]).float(), sl(c["alpha"]).float(), sl(c["beta"]).float(),
+                                       sl(c["v"]), M, "eq4"))
+    torch.cuda.synchronize()
+    yg = torch.cat(ys, 2).cpu().numpy()
+    _check("decode", M.cpu().numpy(), yg, Mo, yo, c["M_in"], c["idx_w"], TOL_F32)
+
+
 @pytest.mark.parametrize("T", [1, 2, 5, 6, 7, 10, 11, 13, 61])
 def test_scan_short_and_ragged_sequences(T):
     say(f"[scan ragged] T={T}")
