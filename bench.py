@@ -107,6 +107,72 @@ def cpu_baseline(wl, x, target_s: float):
             "host_cpu": host_cpu()}
 
 
+def decode_bench(a, wl, x, dev):
+    """Decoding: each step feeds one token of every sequence through addressing
+    and the scan (a call with T = 1), the state staying resident between steps."""
+    import torch
+    import sparse_memory_linear_amd as sdm
+
+    B, H, N, dv, W, R = wl.B, wl.H, wl.N, wl.d_v, wl.W, wl.R
+    nsteps = a.warmup + a.steps
+    if nsteps > wl.T:
+        sys.exit(f"decode: warmup + steps must be at most {wl.T}")
+    sub = x["subkeys"].to(dev)
+    tok = lambda key, k: x[key][:, :, k:k + 1].contiguous().to(dev)
+    per = [{key: tok(key, k) for key in ("q_w", "q_r", "alpha", "beta", "v")} for k in range(nsteps)]
+    M = sdm.sdm_state_init(x["M0"].to(dev), B)
+    addr_out = (torch.empty((B, H, 1, W), dtype=torch.int32, device=dev),
+                torch.empty((B, H, 1, W), dtype=torch.float32, device=dev),
+                torch.empty((B, H, 1, R), dtype=torch.int32, device=dev),
+                torch.empty((B, H, 1, R), dtype=torch.float32, device=dev))
+    y = torch.empty((B, H, 1, dv), dtype=torch.float32, device=dev)
+    ws = torch.empty((sdm.sdm_scan_workspace_bytes(B, H, 1, W, R, dv),), dtype=torch.uint8, device=dev)
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    def step(k, marks=None):
+        i = per[k]
+        if marks:
+            marks[0].record()
+        iw, ww, ir, wr = sdm.sdm_address(i["q_w"], i["q_r"], sub, sub, W, R, out=addr_out)
+        if marks:
+            marks[1].record()
+        sdm.sdm_scan_forward(iw, ww, ir, wr, i["alpha"], i["beta"], i["v"], M, a.form, y=y, workspace=ws)
+        if marks:
+            marks[2].record()
+
+    for k in range(a.warmup):
+        step(k)
+    torch.cuda.synchronize()
+    marks = [[ev() for _ in range(3)] for _ in range(a.steps)]
+    t0 = time.perf_counter()
+    for i in range(a.steps):
+        step(a.warmup + i, marks[i])
+    torch.cuda.synchronize()
+    ms_step = 1e3 * (time.perf_counter() - t0) / a.steps
+    addr_ms = sum(m[0].elapsed_time(m[1]) for m in marks) / a.steps
+    scan_ms = sum(m[1].elapsed_time(m[2]) for m in marks) / a.steps
+    row_bytes = B * H * (2 * W + R) * dv * 4
+    gbps = row_bytes / (scan_ms * 1e-3) / 1e9
+    rec = {
+        "metric": "SDM decode tokens/s at N=65536,W=R=64,d_v=128 (one token per sequence per step)",
+        "value": B / (ms_step * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": a.steps,
+        "warmup": a.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": wl.name, "B": B, "H": H, "T_per_step": 1, "N": N, "W": W, "R": R, "d_v": dv,
+                   "d_h": wl.d_h, "form": a.form, "inputs": "bf16 q/v/subkeys, fp32 table/gates",
+                   "state_GiB": B * H * N * dv * 4 / 2**30},
+        "breakdown_ms": {"address": addr_ms, "scan": scan_ms},
+        "slot_row_GBps": gbps,
+        "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": gbps / HBM_PEAK_GBPS, "traffic": None,
+                     "kernel": "sdm_scan_forward (direct short-call form)",
+                     "algorithmic_bytes_per_launch": row_bytes},
+    }
+    if not a.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(wl, x, a.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     a = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -129,6 +195,8 @@ def main():
         del src, dst
     wl = inputs.get(a.workload)
     x = inputs.make_inputs(wl)
+    if wl.name == "decode":
+        return decode_bench(a, wl, x, dev)
     g = {k: v.to(dev) for k, v in x.items()}
     B, H, T, N, dv, W, R = wl.B, wl.H, wl.T, wl.N, wl.d_v, wl.W, wl.R
     addr_out = (torch.empty((B, H, T, W), dtype=torch.int32, device=dev),

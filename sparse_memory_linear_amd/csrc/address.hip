@@ -273,11 +273,19 @@ __global__ __launch_bounds__(NWA * 64) void address_kernel(AddressArgs a) {
     extern __shared__ __align__(16) uint32_t smem[];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int n = a.n, dh = a.dh;
-    const int64_t ntile = (a.T + TOK - 1) / TOK;
-    const int64_t bh = blockIdx.x / ntile;
-    const int64_t t0 = (blockIdx.x % ntile) * TOK;
+    // A tile is TOK consecutive tokens of one head in (sequence, position)
+    // order, u = b * T + t: within a sequence for long calls, across sequences
+    // when a call carries few tokens per sequence (decoding). Every token of a
+    // tile uses the same subkeys.
+    const int64_t UT = a.B * a.T;
+    const int64_t ntile = (UT + TOK - 1) / TOK;
+    const int h = (int)(blockIdx.x / ntile);
+    const int64_t u0 = (blockIdx.x % ntile) * TOK;
     const int br = blockIdx.y;
-    const int h = (int)(bh % a.H);
+    auto row_of = [&](int64_t u) -> int64_t {  // row of token u in the [B, H, T] layout
+        const int64_t b = u / a.T;
+        return (b * a.H + h) * a.T + (u - b * a.T);
+    };
 
     // LDS: one block of pw floats per wavefront, then the pruned rank pairs. A
     // block first holds the half-scores [TG][2][n] of the wavefront's tokens;
@@ -302,8 +310,8 @@ __global__ __launch_bounds__(NWA * 64) void address_kernel(AddressArgs a) {
     constexpr int TPW = (2 * (64 * EH / 16) + NWA - 1) / NWA;  // most tiles per wavefront
     const int nt16 = n / 16, ntiles = 2 * nt16;
     const int m16 = lane & 15, g4 = lane >> 4;
-    const int64_t tq = t0 + m16;
-    const bool tok_ok = tq < a.T;
+    const int64_t tq = u0 + m16;
+    const bool tok_ok = tq < UT;
     f32x4_t acc[TPW];
     int64_t krow[TPW];  // element offset of this lane's subkey row of each tile
 #pragma unroll
@@ -312,7 +320,7 @@ __global__ __launch_bounds__(NWA * 64) void address_kernel(AddressArgs a) {
         const int tile = wave + i * NWA, j = tile / nt16, a0 = (tile % nt16) * 16;
         krow[i] = (((int64_t)h * 2 + j) * n + a0 + m16) * dh;
     }
-    const int64_t qrow = (bh * a.T + (tok_ok ? tq : 0)) * 2 * dh;  // half 0; half 1 follows
+    const int64_t qrow = row_of(tok_ok ? tq : 0) * 2 * dh;  // half 0; half 1 follows
     if constexpr (BF16) {
         const uint16_t* q = static_cast<const uint16_t*>(a.q[br]) + qrow;
         const uint16_t* kp = static_cast<const uint16_t*>(a.K[br]);
@@ -370,7 +378,7 @@ __global__ __launch_bounds__(NWA * 64) void address_kernel(AddressArgs a) {
     if (a.half_out) {  // test hook: the contraction only
         for (int e = threadIdx.x; e < TOK * 2 * n; e += NWA * 64) {
             const int m = e / (2 * n);
-            if (t0 + m < a.T) a.half_out[(bh * a.T + t0) * 2 * n + e] = sc_tok(m)[e - m * 2 * n];
+            if (u0 + m < UT) a.half_out[row_of(u0 + m) * 2 * n + (e - m * 2 * n)] = sc_tok(m)[e - m * 2 * n];
         }
         return;
     }
@@ -400,7 +408,7 @@ __global__ __launch_bounds__(NWA * 64) void address_kernel(AddressArgs a) {
 
     {
         const int m0 = wave * TG;
-        if (t0 + m0 >= a.T) return;
+        if (u0 + m0 >= UT) return;
         // tokens past T run on the zero scores of their masked rows; nothing is stored
 
         // ---------------- a2: per-half top-k_h, sorted ----------------
@@ -470,7 +478,7 @@ __global__ __launch_bounds__(NWA * 64) void address_kernel(AddressArgs a) {
                 const int jb = k / (lane + 1);
                 if (jb < kh) bnd = ord_key(ls[(g * 2) * 64 + lane] + ls[(g * 2 + 1) * 64 + jb]);
             }
-            if (t0 + m0 + g < a.T && __ballot(bnd != 0u && bnd >= kth) != 0ull) {
+            if (u0 + m0 + g < UT && __ballot(bnd != 0u && bnd >= kth) != 0ull) {
                 const int full = kh * kh;
                 const float* l0 = ls + (g * 2) * 64;
                 const float* l1 = ls + (g * 2 + 1) * 64;
@@ -497,14 +505,14 @@ __global__ __launch_bounds__(NWA * 64) void address_kernel(AddressArgs a) {
         // ---------------- a4: softmax over the k winners ----------------
 #pragma unroll
         for (int g = 0; g < TG; ++g) {
-            const int64_t t = t0 + m0 + g;
+            const int64_t u = u0 + m0 + g;
             const float S = key_float((uint32_t)(x[g] >> 32));
             const uint32_t slot = 0xFFFFFFFFu - (uint32_t)x[g];
             const float mx = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(S), 0));
             const float ex = lane < k ? expf(S - mx) : 0.f;
             const float sum = wave_sum(ex, lane);
-            if (lane < k && t < a.T) {
-                const int64_t o = (bh * a.T + t) * k + lane;
+            if (lane < k && u < UT) {
+                const int64_t o = row_of(u) * k + lane;
                 idx_out[o] = (int32_t)slot;
                 wt_out[o] = ex / sum;
                 if (sc_out) sc_out[o] = S;
@@ -515,9 +523,9 @@ __global__ __launch_bounds__(NWA * 64) void address_kernel(AddressArgs a) {
 
 template <bool BF16, int EH>
 hipError_t launch_inst(const AddressArgs& a, hipStream_t st) {
-    const int64_t ntile = (a.T + TOK - 1) / TOK;
+    const int64_t ntile = (a.B * a.T + TOK - 1) / TOK;
     const size_t lds = (size_t)NWA * block_floats(a.n) * 4 + EC * 64 * 4;
-    dim3 grid((unsigned)(ntile * a.B * a.H), (unsigned)a.nbranch);
+    dim3 grid((unsigned)(ntile * a.H), (unsigned)a.nbranch);
     hipLaunchKernelGGL((address_kernel<BF16, EH>), grid, dim3(NWA * 64), lds, st, a);
     return hipGetLastError();
 }

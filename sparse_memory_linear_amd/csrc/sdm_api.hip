@@ -44,8 +44,8 @@ int check_address_sizes(int q_dtype, int k_dtype, int64_t B, int64_t H, int64_t 
     if (dh % step != 0 || dh > 256)
         return fail(SDM_ERR_UNSUPPORTED, "dh=%lld: kernels cover multiples of %lld up to 256", (long long)dh,
                     (long long)step);
-    const int64_t ntile = (T + 15) / 16;
-    if (ntile * B * H > 0x7FFFFFFFll) return fail(SDM_ERR_UNSUPPORTED, "too many token tiles for one launch");
+    const int64_t ntile = (B * T + 15) / 16;
+    if (ntile * H > 0x7FFFFFFFll) return fail(SDM_ERR_UNSUPPORTED, "too many token tiles for one launch");
     return SDM_OK;
 }
 

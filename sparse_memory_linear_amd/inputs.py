@@ -76,6 +76,9 @@ WORKLOADS: Dict[str, Workload] = {
                              n_centroids=1024, sigma=0.5),
     # large table at the FwPKM value-table size (512 MB fp32 table)
     "large_table": Workload("large_table", 1, 1, 65536, 512, 512, 256, 8, 8, False, 0.02, 3.0, 4),
+    # decoding: 256 sequences of the GDN-matched layer, one token per sequence
+    # per call (T = the number of calls), the 64 GiB state kept between calls
+    "decode": Workload("decode", 256, 8, 32, 256, 128, 64, 64, 64, True, 0.02, 2.0, 5),
 }
 
 

@@ -116,6 +116,26 @@ def test_ragged_token_counts(T):
     assert np.array_equal(ir.cpu().numpy(), oi)
 
 
+@pytest.mark.parametrize("B,T", [(40, 1), (7, 3), (3, 17)])
+def test_token_tiles_span_sequences(B, T):
+    """Short calls pack tokens of several sequences of a head into one tile
+    (decoding: T = 1); the half-scores, the selection and where each token's
+    result lands must not depend on that."""
+    wl = inputs.get("gdn_matched", B=B, H=2, T=T)
+    say(f"[address tiles across sequences] B={B} T={T}")
+    x = inputs.make_inputs(wl)
+    g = _gpu(x)
+    iw, ww, ir, wr = sdm.sdm_address(g["q_w"], g["q_r"], g["subkeys"], g["subkeys"], wl.W, wl.R)
+    for q, idx, wt, k in ((g["q_w"], iw, ww, wl.W), (g["q_r"], ir, wr, wl.R)):
+        half = sdm.sdm_debug_half_scores(q, g["subkeys"]).cpu()
+        ref = oracle.half_scores(q.cpu(), x["subkeys"])
+        assert np.all(np.abs(half.numpy().astype(np.float64) - ref) <= _half_bound(q.cpu(), x["subkeys"]))
+        oi, ow, _, _ = oracle.select(half, k)
+        assert np.array_equal(idx.cpu().numpy(), oi)
+        gw = wt.cpu().numpy()
+        assert np.max(np.abs(gw - ow) / np.maximum(ow, 1e-30)) < 2e-6 or np.abs(gw - ow).max() < 1e-7
+
+
 def test_empty_input_is_a_no_op():
     wl = inputs.get("small", B=1, H=1, T=0)
     x = inputs.make_inputs(wl)
