@@ -48,7 +48,10 @@ def _load():
         lib.oracle_select.argtypes = [P, I64, I64, I64, I64, I64, P, P, P, P, I]
         lib.oracle_scan.argtypes = [P, P, I64, P, P, I64, P, P, P, P, P,
                                     I64, I64, I64, I64, I64, I, I]
-        for f in (lib.oracle_half_scores, lib.oracle_select, lib.oracle_scan):
+        lib.oracle_scan_backward.argtypes = [P, P, I64, P, P, I64, P, P, P, P, P, P,
+                                             P, P, P, P, P, P, I64, I64, I64, I64, I64, I, I]
+        for f in (lib.oracle_half_scores, lib.oracle_select, lib.oracle_scan,
+                  lib.oracle_scan_backward):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -137,6 +140,35 @@ def scan(idx_w, wt_w, idx_r, wt_r, alpha, beta, v, M_in, form: int = EQ4,
                                _p(M), _p(y), B, H, T, N, dv, form,
                                nthreads or default_threads()), "scan")
     return M, y
+
+
+def scan_backward(idx_w, wt_w, idx_r, wt_r, alpha, beta, v, M_in, dy, dM_out=None,
+                  form: int = EQ4, nthreads: Optional[int] = None) -> dict:
+    """Reverse-mode derivatives of the scan ([SDM] §2.9 Appendix A: the tokens in
+    reverse, each written row restored from its pre-image).
+
+    M_in [B,H,N,dv] is the state before token 0, dy [B,H,T,dv] the gradient of y
+    and dM_out [B,H,N,dv] (or None: zero) that of the final state. Returns a dict
+    with dv [B,H,T,dv], dalpha, dbeta [B,H,T], dwt_w [B,H,T,W], dwt_r [B,H,T,R]
+    and dM_in [B,H,N,dv]; inputs are not modified.
+    """
+    iw = _i32(idx_w); ww = _f32(wt_w); ir = _i32(idx_r); wr = _f32(wt_r)
+    a = _f32(alpha); b = _f32(beta); vv = _f32(v); M = _f32(M_in); g = _f32(dy)
+    gM = None if dM_out is None else _f32(dM_out)
+    B, H, T, W = iw.shape
+    R = ir.shape[3]
+    N, dv = M.shape[2], M.shape[3]
+    assert M.shape[:2] == (B, H) and vv.shape == (B, H, T, dv) and g.shape == vv.shape
+    assert gM is None or gM.shape == M.shape
+    out = {"dv": np.empty((B, H, T, dv), np.float32), "dalpha": np.empty((B, H, T), np.float32),
+           "dbeta": np.empty((B, H, T), np.float32), "dwt_w": np.empty((B, H, T, W), np.float32),
+           "dwt_r": np.empty((B, H, T, R), np.float32), "dM_in": np.empty((B, H, N, dv), np.float32)}
+    _check(_load().oracle_scan_backward(
+        _p(iw), _p(ww), W, _p(ir), _p(wr), R, _p(a), _p(b), _p(vv), _p(M), _p(g),
+        None if gM is None else _p(gM), _p(out["dv"]), _p(out["dalpha"]), _p(out["dbeta"]),
+        _p(out["dwt_w"]), _p(out["dwt_r"]), _p(out["dM_in"]), B, H, T, N, dv, form,
+        nthreads or default_threads()), "scan_backward")
+    return out
 
 
 def broadcast_state(M0, B: int) -> np.ndarray:

@@ -26,7 +26,7 @@
 #include <stdlib.h>
 #include <string.h>
 
-int oracle_version(void) { return 1; }
+int oracle_version(void) { return 2; }
 
 /* ------------------------------------------------------------------ */
 /* a tiny "run f(i) for i in [0, count) on nthreads threads" helper.   */
@@ -249,16 +249,10 @@ static void scan_item(void* p, int64_t s) {      /* s = b*H + h: one sequence-he
     free(vhat);
 }
 
-int oracle_scan(const int32_t* idx_w, const float* wt_w, int64_t W,
-                const int32_t* idx_r, const float* wt_r, int64_t R,
-                const float* alpha, const float* beta, const float* v,
-                float* M, float* y, int64_t B, int64_t H, int64_t T, int64_t N,
-                int64_t dv, int form, int nthreads) {
-    if (!idx_w || !wt_w || !idx_r || !wt_r || !alpha || !beta || !v || !M || !y) return -1;
-    if (B < 0 || H < 0 || T < 0 || N < 1 || dv < 1 || W < 1 || R < 1 || W > N || R > N) return -2;
-    if (form != ORACLE_EQ4 && form != ORACLE_FIG2) return -2;
-    /* preconditions: indices in range, write indices of one token distinct */
-    int64_t ntok = B * H * T;
+/* preconditions of the scan: indices in range, write indices of one token
+   distinct. 0, or -3 (out of range) / -4 (repeated write index). */
+static int check_indices(const int32_t* idx_w, int64_t W, const int32_t* idx_r, int64_t R,
+                         int64_t ntok, int64_t N) {
     unsigned char* seen = (unsigned char*)calloc((size_t)N, 1);
     for (int64_t st = 0; st < ntok; ++st) {
         for (int64_t j = 0; j < R; ++j)
@@ -272,7 +266,186 @@ int oracle_scan(const int32_t* idx_w, const float* wt_w, int64_t W,
         for (int64_t j = 0; j < W; ++j) seen[idx_w[st * W + j]] = 0;
     }
     free(seen);
+    return 0;
+}
+
+int oracle_scan(const int32_t* idx_w, const float* wt_w, int64_t W,
+                const int32_t* idx_r, const float* wt_r, int64_t R,
+                const float* alpha, const float* beta, const float* v,
+                float* M, float* y, int64_t B, int64_t H, int64_t T, int64_t N,
+                int64_t dv, int form, int nthreads) {
+    if (!idx_w || !wt_w || !idx_r || !wt_r || !alpha || !beta || !v || !M || !y) return -1;
+    if (B < 0 || H < 0 || T < 0 || N < 1 || dv < 1 || W < 1 || R < 1 || W > N || R > N) return -2;
+    if (form != ORACLE_EQ4 && form != ORACLE_FIG2) return -2;
+    int rc = check_indices(idx_w, W, idx_r, R, B * H * T, N);
+    if (rc) return rc;
     scan_ctx c = {idx_w, wt_w, W, idx_r, wt_r, R, alpha, beta, v, M, y, T, N, dv, form};
     parallel_for(scan_item, &c, B * H, nthreads);
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* Backward of A5-A6: reverse-mode derivatives of the scan              */
+/* [SDM §2.4 Eq. (3)-(5), §2.5 Fig. 2 form; §2.9 Appendix A: the        */
+/*  forward writes in place and the backward walks the tokens in        */
+/*  reverse, restoring each written row from its pre-image].            */
+/*                                                                      */
+/* Per token the forward computes, for write rows i_p with pre-images   */
+/* m_p = M_{t-1}[i_p] and read rows j_q:                                */
+/*   EQ4:  M_t[i_p] = a m_p + b w_p (v - a m_p)                         */
+/*   FIG2: M_t[i_p] = a m_p + b w_p (v - a s),  s = sum_p w_p m_p       */
+/*   y_t = sum_q r_q M_t[j_q]                                           */
+/* With G = dL/dM_t (the adjoint table), token t in reverse order:      */
+/*   reads:  dr_q = <dy_t, M_t[j_q]>;  G[j_q] += r_q dy_t                */
+/*   writes, with g_p = G[i_p] (after the reads), u = v - a m_p (EQ4)   */
+/*   or u = v - a s (FIG2), gh = sum_p w_p g_p:                          */
+/*   EQ4:  dv += b w_p g_p;  da += (1 - b w_p) <g_p, m_p>;              */
+/*         db += w_p <g_p, u>;  dw_p = b <g_p, u>;                       */
+/*         G[i_p] = a (1 - b w_p) g_p                                    */
+/*   FIG2: dv = b gh;  da = sum_p <g_p, m_p> - b <gh, s>;  db = <gh, u>; */
+/*         dw_p = b <g_p, u> - a b <gh, m_p>;  G[i_p] = a g_p - a b w_p gh */
+/*   and M[i_p] = m_p (the undo). After token 0, G = dL/dM_0.            */
+/* Here the pre-images are recorded by running the forward first (same  */
+/* arithmetic as oracle_scan); G and every sum are kept in double and    */
+/* the outputs rounded once to fp32.                                     */
+/* ------------------------------------------------------------------ */
+typedef struct {
+    const int32_t* idx_w; const float* wt_w; int64_t W;
+    const int32_t* idx_r; const float* wt_r; int64_t R;
+    const float *alpha, *beta, *v, *M_in, *dy, *dM_out;
+    float *dv_, *dalpha, *dbeta, *dwt_w, *dwt_r, *dM_in;
+    int64_t T, N, dv;
+    int form;
+} bwd_ctx;
+
+static void bwd_item(void* p, int64_t s) {      /* s = b*H + h: one sequence-head */
+    bwd_ctx* c = (bwd_ctx*)p;
+    const int64_t W = c->W, R = c->R, dv = c->dv, T = c->T, N = c->N;
+    float* Ms = (float*)malloc((size_t)(N * dv) * sizeof(float));
+    float* pre = (float*)malloc((size_t)(T * W * dv + 1) * sizeof(float));
+    float* yscr = (float*)malloc((size_t)(T * dv + 1) * sizeof(float));
+    double* G = (double*)malloc((size_t)(N * dv) * sizeof(double));
+    double* g = (double*)malloc((size_t)(W * dv) * sizeof(double));
+    double* gh = (double*)malloc((size_t)dv * sizeof(double));
+    double* sm = (double*)malloc((size_t)dv * sizeof(double));
+    memcpy(Ms, c->M_in + s * N * dv, (size_t)(N * dv) * sizeof(float));
+
+    /* forward pass, recording the pre-image of every written row */
+    for (int64_t t = 0; t < T; ++t) {
+        const int32_t* iw = c->idx_w + (s * T + t) * W;
+        for (int64_t p = 0; p < W; ++p)
+            memcpy(pre + (t * W + p) * dv, Ms + (int64_t)iw[p] * dv, (size_t)dv * sizeof(float));
+        scan_ctx f = {c->idx_w + (s * T + t) * W, c->wt_w + (s * T + t) * W, W,
+                      c->idx_r + (s * T + t) * R, c->wt_r + (s * T + t) * R, R,
+                      c->alpha + s * T + t, c->beta + s * T + t, c->v + (s * T + t) * dv,
+                      Ms, yscr + t * dv, 1, N, dv, c->form};
+        scan_item(&f, 0);
+    }
+
+    for (int64_t k = 0; k < N * dv; ++k) G[k] = c->dM_out ? (double)c->dM_out[s * N * dv + k] : 0.0;
+    for (int64_t t = T - 1; t >= 0; --t) {
+        const int64_t st = s * T + t;
+        const int32_t* iw = c->idx_w + st * W;
+        const float* ww = c->wt_w + st * W;
+        const int32_t* ir = c->idx_r + st * R;
+        const float* wr = c->wt_r + st * R;
+        const float* vt = c->v + st * dv;
+        const float* dyt = c->dy + st * dv;
+        const double a = (double)c->alpha[st], b = (double)c->beta[st];
+
+        /* Eq. (5) read of M_t: weight gradients, then the read's adjoint */
+        for (int64_t q = 0; q < R; ++q) {
+            const float* row = Ms + (int64_t)ir[q] * dv;
+            double acc = 0.0;
+            for (int64_t col = 0; col < dv; ++col) acc += (double)dyt[col] * (double)row[col];
+            c->dwt_r[st * R + q] = (float)acc;
+        }
+        for (int64_t q = 0; q < R; ++q) {
+            double* Gr = G + (int64_t)ir[q] * dv;
+            for (int64_t col = 0; col < dv; ++col) Gr[col] += (double)wr[q] * (double)dyt[col];
+        }
+
+        /* the write's adjoint, from the pre-images m_p */
+        for (int64_t p = 0; p < W; ++p)
+            memcpy(g + p * dv, G + (int64_t)iw[p] * dv, (size_t)dv * sizeof(double));
+        double da = 0.0, db = 0.0;
+        if (c->form == ORACLE_FIG2) {
+            for (int64_t col = 0; col < dv; ++col) { gh[col] = 0.0; sm[col] = 0.0; }
+            for (int64_t p = 0; p < W; ++p) {
+                const float* m = pre + (t * W + p) * dv;
+                for (int64_t col = 0; col < dv; ++col) {
+                    gh[col] += (double)ww[p] * g[p * dv + col];
+                    sm[col] += (double)ww[p] * (double)m[col];
+                }
+            }
+            double ghs = 0.0;
+            for (int64_t col = 0; col < dv; ++col) {
+                const double u = (double)vt[col] - a * sm[col];
+                c->dv_[st * dv + col] = (float)(b * gh[col]);
+                db += gh[col] * u;
+                ghs += gh[col] * sm[col];
+            }
+            da = -b * ghs;
+            for (int64_t p = 0; p < W; ++p) {
+                const float* m = pre + (t * W + p) * dv;
+                double gm = 0.0, gu = 0.0, hm = 0.0;
+                for (int64_t col = 0; col < dv; ++col) {
+                    const double u = (double)vt[col] - a * sm[col];
+                    gm += g[p * dv + col] * (double)m[col];
+                    gu += g[p * dv + col] * u;
+                    hm += gh[col] * (double)m[col];
+                }
+                da += gm;
+                c->dwt_w[st * W + p] = (float)(b * gu - a * b * hm);
+                double* Gw = G + (int64_t)iw[p] * dv;
+                for (int64_t col = 0; col < dv; ++col)
+                    Gw[col] = a * g[p * dv + col] - a * b * (double)ww[p] * gh[col];
+            }
+        } else {
+            for (int64_t col = 0; col < dv; ++col) gh[col] = 0.0;   /* dv accumulator */
+            for (int64_t p = 0; p < W; ++p) {
+                const float* m = pre + (t * W + p) * dv;
+                const double kw = (double)ww[p];
+                double gm = 0.0, gu = 0.0;
+                for (int64_t col = 0; col < dv; ++col) {
+                    const double gc = g[p * dv + col];
+                    gm += gc * (double)m[col];
+                    gu += gc * ((double)vt[col] - a * (double)m[col]);
+                    gh[col] += b * kw * gc;
+                }
+                da += (1.0 - b * kw) * gm;
+                db += kw * gu;
+                c->dwt_w[st * W + p] = (float)(b * gu);
+                double* Gw = G + (int64_t)iw[p] * dv;
+                for (int64_t col = 0; col < dv; ++col) Gw[col] = a * (1.0 - b * kw) * g[p * dv + col];
+            }
+            for (int64_t col = 0; col < dv; ++col) c->dv_[st * dv + col] = (float)gh[col];
+        }
+        c->dalpha[st] = (float)da;
+        c->dbeta[st] = (float)db;
+        /* the undo: rows of token t back to their pre-images (M_{t-1}) */
+        for (int64_t p = 0; p < W; ++p)
+            memcpy(Ms + (int64_t)iw[p] * dv, pre + (t * W + p) * dv, (size_t)dv * sizeof(float));
+    }
+    for (int64_t k = 0; k < N * dv; ++k) c->dM_in[s * N * dv + k] = (float)G[k];
+    free(Ms); free(pre); free(yscr); free(G); free(g); free(gh); free(sm);
+}
+
+int oracle_scan_backward(const int32_t* idx_w, const float* wt_w, int64_t W,
+                         const int32_t* idx_r, const float* wt_r, int64_t R,
+                         const float* alpha, const float* beta, const float* v,
+                         const float* M_in, const float* dy, const float* dM_out,
+                         float* dv_, float* dalpha, float* dbeta, float* dwt_w, float* dwt_r,
+                         float* dM_in, int64_t B, int64_t H, int64_t T, int64_t N, int64_t dv,
+                         int form, int nthreads) {
+    if (!idx_w || !wt_w || !idx_r || !wt_r || !alpha || !beta || !v || !M_in || !dy ||
+        !dv_ || !dalpha || !dbeta || !dwt_w || !dwt_r || !dM_in) return -1;
+    if (B < 0 || H < 0 || T < 0 || N < 1 || dv < 1 || W < 1 || R < 1 || W > N || R > N) return -2;
+    if (form != ORACLE_EQ4 && form != ORACLE_FIG2) return -2;
+    int rc = check_indices(idx_w, W, idx_r, R, B * H * T, N);
+    if (rc) return rc;
+    bwd_ctx c = {idx_w, wt_w, W, idx_r, wt_r, R, alpha, beta, v, M_in, dy, dM_out,
+                 dv_, dalpha, dbeta, dwt_w, dwt_r, dM_in, T, N, dv, form};
+    parallel_for(bwd_item, &c, B * H, nthreads);
     return 0;
 }

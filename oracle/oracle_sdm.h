@@ -57,6 +57,23 @@ int oracle_scan(const int32_t* idx_w, const float* wt_w, int64_t W,
                 float* M, float* y, int64_t B, int64_t H, int64_t T, int64_t N,
                 int64_t dv, int form, int nthreads);
 
+/* Backward of A5-A6 by reverse-mode differentiation of the whole scan, the
+ * tokens walked in reverse with each written row restored from its pre-image
+ * ([SDM] §2.9 Appendix A, backward memory). Same index/weight/gate/v inputs as
+ * oracle_scan; M_in [B,H,N,dv] is the state before token 0 (not modified);
+ * dy [B,H,T,dv] the gradient of y; dM_out [B,H,N,dv] that of the final state
+ * (NULL: zero). Outputs: dv_ [B,H,T,dv], dalpha/dbeta [B,H,T], dwt_w [B,H,T,W],
+ * dwt_r [B,H,T,R], dM_in [B,H,N,dv] (the gradient of the state before token 0).
+ * Derivatives are those of the exact recurrence at the fp32 values the forward
+ * stores; the adjoint table and every sum are kept in double. */
+int oracle_scan_backward(const int32_t* idx_w, const float* wt_w, int64_t W,
+                         const int32_t* idx_r, const float* wt_r, int64_t R,
+                         const float* alpha, const float* beta, const float* v,
+                         const float* M_in, const float* dy, const float* dM_out,
+                         float* dv_, float* dalpha, float* dbeta, float* dwt_w, float* dwt_r,
+                         float* dM_in, int64_t B, int64_t H, int64_t T, int64_t N, int64_t dv,
+                         int form, int nthreads);
+
 int oracle_version(void);
 
 #ifdef __cplusplus
