@@ -32,7 +32,7 @@
 extern "C" {
 #endif
 
-#define SDM_ABI_VERSION 1
+#define SDM_ABI_VERSION 2
 
 typedef enum sdm_status {
     SDM_OK = 0,
@@ -149,6 +149,81 @@ int sdm_scan_forward(const int32_t* idx_w, const float* wt_w, int64_t W,
                      float* M, float* y,
                      int64_t B, int64_t H, int64_t T, int64_t N, int64_t dv,
                      int form, void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
+ * Training: the forward with pre-images, then the backward that undoes it.
+ * ([SDM] §2.9 Appendix A, backward memory: the forward writes the table in
+ * place; the backward walks the tokens in reverse and restores each written
+ * row from its stored pre-image, so the memory is O(N*dv + T*W*dv) instead of
+ * one table per step.)
+ */
+
+/*
+ * sdm_scan_snapshot_bytes -- bytes of the pre-image buffer for these sizes:
+ * B*H*T*W*dv*4 (-1 when the sizes are invalid).
+ */
+int64_t sdm_scan_snapshot_bytes(int64_t B, int64_t H, int64_t T, int64_t W, int64_t dv);
+
+/*
+ * sdm_scan_forward_save -- sdm_scan_forward (same arguments; M bit-identical
+ * to it, y equal up to the order in which the read rows are added) that also
+ * stores, for every write, the row as it was before this token's decay:
+ *   snap [B, H, T, W, dv] fp32 (out): snap[b,h,t,p,:] = M_{t-1}[b,h,idx_w[b,h,t,p],:]
+ * The workspace is the one sdm_scan_workspace_bytes gives. Same support as
+ * sdm_scan_forward.
+ */
+int sdm_scan_forward_save(const int32_t* idx_w, const float* wt_w, int64_t W,
+                          const int32_t* idx_r, const float* wt_r, int64_t R,
+                          const float* alpha, const float* beta,
+                          const void* v, int v_dtype,
+                          float* M, float* y, float* snap,
+                          int64_t B, int64_t H, int64_t T, int64_t N, int64_t dv,
+                          int form, void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
+ * sdm_scan_backward_workspace_bytes -- device workspace sdm_scan_backward needs
+ * (per-slab partial sums of the weight and gate gradients); 0 when there is no
+ * work, -1 when the sizes are invalid.
+ */
+int64_t sdm_scan_backward_workspace_bytes(int64_t B, int64_t H, int64_t T, int64_t W, int64_t R,
+                                          int64_t dv);
+
+/*
+ * sdm_scan_backward -- reverse-mode derivatives of one sdm_scan_forward_save
+ * call, tokens T-1 .. 0, with the forward's writes undone in place.
+ *   idx_w, wt_w, idx_r, wt_r, alpha, beta, v, form: as given to the forward call
+ *   snap  [B, H, T, W, dv] fp32: the forward call's pre-images
+ *   dy    [B, H, T, dv] fp32: dL/dy
+ *   M     [B, H, N, dv] fp32, in: the state after the forward call;
+ *         out: the state before it (bit-identical to what the forward got)
+ *   dM    [B, H, N, dv] fp32, in: dL/dM after the call (zeros if the final state
+ *         does not enter the loss); out: dL/dM before the call
+ *   dv_out [B, H, T, dv], dalpha, dbeta [B, H, T], dwt_w [B, H, T, W],
+ *   dwt_r [B, H, T, R]: fp32 gradients (out)
+ *   workspace: >= sdm_scan_backward_workspace_bytes(B,H,T,W,R,dv) bytes, 16-byte aligned
+ * A sequence split into forward calls is differentiated call by call, last
+ * call first, passing M and dM along. Preconditions: those of the forward, and
+ * also the R read indices of one token distinct (sdm_address guarantees it).
+ * Supported: as sdm_scan_forward; W, R <= 256 with ceil(W/G) + ceil(R/G) <= 16
+ * wavefronts for some slab width (G = 64 / (S / 4) rows per wavefront, S in
+ * {4, 8, 16, 32} dividing dv).
+ */
+int sdm_scan_backward(const int32_t* idx_w, const float* wt_w, int64_t W,
+                      const int32_t* idx_r, const float* wt_r, int64_t R,
+                      const float* alpha, const float* beta,
+                      const void* v, int v_dtype, const float* snap, const float* dy,
+                      float* M, float* dM,
+                      float* dv_out, float* dalpha, float* dbeta, float* dwt_w, float* dwt_r,
+                      int64_t B, int64_t H, int64_t T, int64_t N, int64_t dv,
+                      int form, void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
+ * sdm_state_init_backward -- adjoint of sdm_state_init: the gradient of the
+ * shared initial state, dM0[h] = sum over b of dM[b, h] (added in b order).
+ *   dM [B, H, N, dv] fp32, dM0 [H, N, dv] fp32 (out). dv a multiple of 4.
+ */
+int sdm_state_init_backward(const float* dM, float* dM0, int64_t B, int64_t H, int64_t N,
+                            int64_t dv, void* stream);
 
 #ifdef __cplusplus
 }

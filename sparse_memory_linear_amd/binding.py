@@ -33,6 +33,13 @@ _SIGS = {
     "sdm_scan_workspace_bytes": (_I64, [_I64, _I64, _I64, _I64, _I64, _I64]),
     "sdm_scan_forward": (_I, [_P, _P, _I64, _P, _P, _I64, _P, _P, _P, _I, _P, _P,
                               _I64, _I64, _I64, _I64, _I64, _I, _P, _I64, _P]),
+    "sdm_scan_snapshot_bytes": (_I64, [_I64, _I64, _I64, _I64, _I64]),
+    "sdm_scan_forward_save": (_I, [_P, _P, _I64, _P, _P, _I64, _P, _P, _P, _I, _P, _P, _P,
+                                   _I64, _I64, _I64, _I64, _I64, _I, _P, _I64, _P]),
+    "sdm_scan_backward_workspace_bytes": (_I64, [_I64, _I64, _I64, _I64, _I64, _I64]),
+    "sdm_scan_backward": (_I, [_P, _P, _I64, _P, _P, _I64, _P, _P, _P, _I, _P, _P, _P, _P,
+                               _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I, _P, _I64, _P]),
+    "sdm_state_init_backward": (_I, [_P, _P, _I64, _I64, _I64, _I64, _P]),
 }
 
 _lib = None
@@ -172,15 +179,7 @@ def sdm_scan_workspace_bytes(B: int, H: int, T: int, W: int, R: int, dv: int) ->
     return n
 
 
-def sdm_scan_forward(idx_w: torch.Tensor, wt_w: torch.Tensor, idx_r: torch.Tensor,
-                     wt_r: torch.Tensor, alpha: torch.Tensor, beta: torch.Tensor,
-                     v: torch.Tensor, M: torch.Tensor, form: str = "eq4",
-                     y: Optional[torch.Tensor] = None,
-                     workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Sparse gated delta scan over all T tokens; M [B,H,N,dv] is updated in place.
-
-    Returns y [B,H,T,dv] fp32.
-    """
+def _scan_inputs(fn, idx_w, wt_w, idx_r, wt_r, alpha, beta, v, M):
     d = _dev(idx_w, wt_w, idx_r, wt_r, alpha, beta, v, M)
     B, H, T, W = idx_w.shape
     R = idx_r.shape[3]
@@ -194,20 +193,124 @@ def sdm_scan_forward(idx_w: torch.Tensor, wt_w: torch.Tensor, idx_r: torch.Tenso
     if idx_w.dtype != torch.int32 or idx_r.dtype != torch.int32 or wt_w.dtype != torch.float32 \
             or wt_r.dtype != torch.float32 or alpha.dtype != torch.float32 \
             or beta.dtype != torch.float32 or M.dtype != torch.float32:
-        raise ValueError("dtype mismatch in sdm_scan_forward")
-    if y is None:
-        y = torch.empty((B, H, T, dv), dtype=torch.float32, device=d)
-    elif tuple(y.shape) != (B, H, T, dv) or y.dtype != torch.float32:
-        raise ValueError("y has the wrong shape or dtype")
-    _dev(M, y)
-    nbytes = sdm_scan_workspace_bytes(B, H, T, W, R, dv)
-    if workspace is None:
-        workspace = torch.empty((max(nbytes, 16),), dtype=torch.uint8, device=d)
-    elif workspace.dtype != torch.uint8 or workspace.dim() != 1:
+        raise ValueError(f"dtype mismatch in {fn}")
+    return d, (B, H, T, W, R, N, dv)
+
+
+def _f32_out(t: Optional[torch.Tensor], shape, d, name: str) -> torch.Tensor:
+    if t is None:
+        return torch.empty(shape, dtype=torch.float32, device=d)
+    if tuple(t.shape) != tuple(shape) or t.dtype != torch.float32:
+        raise ValueError(f"{name} has the wrong shape or dtype")
+    _dev(t)
+    if t.device != d:
+        raise ValueError("all tensors must be on the same GPU")
+    return t
+
+
+def _workspace(ws: Optional[torch.Tensor], nbytes: int, d) -> torch.Tensor:
+    if ws is None:
+        return torch.empty((max(nbytes, 16),), dtype=torch.uint8, device=d)
+    if ws.dtype != torch.uint8 or ws.dim() != 1:
         raise ValueError("workspace must be a 1-D uint8 tensor")
-    _dev(M, workspace)
+    _dev(ws)
+    return ws
+
+
+def sdm_scan_forward(idx_w: torch.Tensor, wt_w: torch.Tensor, idx_r: torch.Tensor,
+                     wt_r: torch.Tensor, alpha: torch.Tensor, beta: torch.Tensor,
+                     v: torch.Tensor, M: torch.Tensor, form: str = "eq4",
+                     y: Optional[torch.Tensor] = None,
+                     workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Sparse gated delta scan over all T tokens; M [B,H,N,dv] is updated in place.
+
+    Returns y [B,H,T,dv] fp32.
+    """
+    d, (B, H, T, W, R, N, dv) = _scan_inputs("sdm_scan_forward", idx_w, wt_w, idx_r, wt_r,
+                                             alpha, beta, v, M)
+    y = _f32_out(y, (B, H, T, dv), d, "y")
+    workspace = _workspace(workspace, sdm_scan_workspace_bytes(B, H, T, W, R, dv), d)
     _check("sdm_scan_forward", lib().sdm_scan_forward(
         _ptr(idx_w), _ptr(wt_w), W, _ptr(idx_r), _ptr(wt_r), R, _ptr(alpha), _ptr(beta),
         _ptr(v), _dtype_code(v), _ptr(M), _ptr(y), B, H, T, N, dv, FORMS[form],
         _ptr(workspace), workspace.numel(), _stream(d)))
     return y
+
+
+def sdm_scan_snapshot_bytes(B: int, H: int, T: int, W: int, dv: int) -> int:
+    n = lib().sdm_scan_snapshot_bytes(B, H, T, W, dv)
+    if n < 0:
+        raise ValueError("invalid sizes for the pre-image buffer")
+    return n
+
+
+def sdm_scan_forward_save(idx_w: torch.Tensor, wt_w: torch.Tensor, idx_r: torch.Tensor,
+                          wt_r: torch.Tensor, alpha: torch.Tensor, beta: torch.Tensor,
+                          v: torch.Tensor, M: torch.Tensor, form: str = "eq4",
+                          y: Optional[torch.Tensor] = None, snap: Optional[torch.Tensor] = None,
+                          workspace: Optional[torch.Tensor] = None
+                          ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """The training forward: sdm_scan_forward that also stores the pre-image of
+    every write. M is updated in place. Returns (y [B,H,T,dv], snap [B,H,T,W,dv])."""
+    d, (B, H, T, W, R, N, dv) = _scan_inputs("sdm_scan_forward_save", idx_w, wt_w, idx_r, wt_r,
+                                             alpha, beta, v, M)
+    y = _f32_out(y, (B, H, T, dv), d, "y")
+    snap = _f32_out(snap, (B, H, T, W, dv), d, "snap")
+    workspace = _workspace(workspace, sdm_scan_workspace_bytes(B, H, T, W, R, dv), d)
+    _check("sdm_scan_forward_save", lib().sdm_scan_forward_save(
+        _ptr(idx_w), _ptr(wt_w), W, _ptr(idx_r), _ptr(wt_r), R, _ptr(alpha), _ptr(beta),
+        _ptr(v), _dtype_code(v), _ptr(M), _ptr(y), _ptr(snap), B, H, T, N, dv, FORMS[form],
+        _ptr(workspace), workspace.numel(), _stream(d)))
+    return y, snap
+
+
+def sdm_scan_backward_workspace_bytes(B: int, H: int, T: int, W: int, R: int, dv: int) -> int:
+    n = lib().sdm_scan_backward_workspace_bytes(B, H, T, W, R, dv)
+    if n < 0:
+        raise ValueError("invalid sizes for the backward workspace")
+    return n
+
+
+def sdm_scan_backward(idx_w: torch.Tensor, wt_w: torch.Tensor, idx_r: torch.Tensor,
+                      wt_r: torch.Tensor, alpha: torch.Tensor, beta: torch.Tensor,
+                      v: torch.Tensor, snap: torch.Tensor, dy: torch.Tensor, M: torch.Tensor,
+                      dM: torch.Tensor, form: str = "eq4", out: Optional[dict] = None,
+                      workspace: Optional[torch.Tensor] = None) -> dict:
+    """Backward of one sdm_scan_forward_save call, undoing its writes in place.
+
+    M [B,H,N,dv] (in: after the forward call, out: before it) and dM (in: dL/dM
+    after the call, out: before it) are updated in place. Returns a dict with dv
+    [B,H,T,dv], dalpha, dbeta [B,H,T], dwt_w [B,H,T,W], dwt_r [B,H,T,R]; ``out``
+    may pass those tensors preallocated.
+    """
+    d, (B, H, T, W, R, N, dv) = _scan_inputs("sdm_scan_backward", idx_w, wt_w, idx_r, wt_r,
+                                             alpha, beta, v, M)
+    for name, t, shp in (("snap", snap, (B, H, T, W, dv)), ("dy", dy, (B, H, T, dv)),
+                         ("dM", dM, (B, H, N, dv))):
+        if tuple(t.shape) != shp or t.dtype != torch.float32:
+            raise ValueError(f"{name} has the wrong shape or dtype")
+        _dev(M, t)
+    out = dict(out or {})
+    shapes = {"dv": (B, H, T, dv), "dalpha": (B, H, T), "dbeta": (B, H, T),
+              "dwt_w": (B, H, T, W), "dwt_r": (B, H, T, R)}
+    for k, shp in shapes.items():
+        out[k] = _f32_out(out.get(k), shp, d, k)
+    workspace = _workspace(workspace, sdm_scan_backward_workspace_bytes(B, H, T, W, R, dv), d)
+    _check("sdm_scan_backward", lib().sdm_scan_backward(
+        _ptr(idx_w), _ptr(wt_w), W, _ptr(idx_r), _ptr(wt_r), R, _ptr(alpha), _ptr(beta),
+        _ptr(v), _dtype_code(v), _ptr(snap), _ptr(dy), _ptr(M), _ptr(dM), _ptr(out["dv"]),
+        _ptr(out["dalpha"]), _ptr(out["dbeta"]), _ptr(out["dwt_w"]), _ptr(out["dwt_r"]),
+        B, H, T, N, dv, FORMS[form], _ptr(workspace), workspace.numel(), _stream(d)))
+    return out
+
+
+def sdm_state_init_backward(dM: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Gradient of the shared initial state: dM0 [H,N,dv] = sum over b of dM [B,H,N,dv]."""
+    d = _dev(dM)
+    B, H, N, dv = dM.shape
+    if dM.dtype != torch.float32:
+        raise ValueError("dM must be fp32")
+    dM0 = _f32_out(out, (H, N, dv), d, "dM0")
+    _check("sdm_state_init_backward", lib().sdm_state_init_backward(
+        _ptr(dM), _ptr(dM0), B, H, N, dv, _stream(d)))
+    return dM0

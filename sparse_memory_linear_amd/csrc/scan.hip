@@ -37,6 +37,7 @@
 // Placement: workgroups are dealt to the 8 XCDs round-robin, so blockIdx is
 // remapped to put every slab of a stream on the same XCD; the slabs of a row
 // then share that XCD's L2 lines.
+#include "sdm_buffer.h"
 #include "sdm_internal.h"
 
 namespace sdm {
@@ -318,100 +319,6 @@ __global__ void zero_u32(uint32_t* p, int n) {
 }
 
 // ------------------------------------------------------------------ scan
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-using rsrc_t = __amdgpu_buffer_rsrc_t;
-// A buffer offset beyond every buffer the scan addresses (each is < 2 GiB): the
-// hardware's range check drops the access and a load returns zeros.
-constexpr uint32_t OOB = 0x80000000u;
-
-__device__ __forceinline__ rsrc_t make_rsrc(const void* p, int64_t bytes) {
-    // raw buffer: stride 0, num_records = size in bytes, 32-bit data format (gfx9 word 3)
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
-}
-__device__ __forceinline__ int4 ld_i4(rsrc_t r, uint32_t vo, uint32_t so) {
-    const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(r, (int)vo, (int)so, 0);
-    return make_int4((int)x.x, (int)x.y, (int)x.z, (int)x.w);
-}
-__device__ __forceinline__ int2 ld_i2(rsrc_t r, uint32_t vo, uint32_t so) {
-    const u32x2 x = __builtin_amdgcn_raw_buffer_load_b64(r, (int)vo, (int)so, 0);
-    return make_int2((int)x.x, (int)x.y);
-}
-__device__ __forceinline__ float4 ld_f4(rsrc_t r, uint32_t vo, uint32_t so) {
-    const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(r, (int)vo, (int)so, 0);
-    return make_float4(__uint_as_float(x.x), __uint_as_float(x.y), __uint_as_float(x.z), __uint_as_float(x.w));
-}
-__device__ __forceinline__ void st_f4(float4 v, rsrc_t r, uint32_t vo, uint32_t so) {
-    u32x4 x;
-    x.x = __float_as_uint(v.x); x.y = __float_as_uint(v.y); x.z = __float_as_uint(v.z); x.w = __float_as_uint(v.w);
-    __builtin_amdgcn_raw_buffer_store_b128(x, r, (int)vo, (int)so, 0);
-}
-__device__ __forceinline__ void st_f1(float v, rsrc_t r, uint32_t vo, uint32_t so) {
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, (int)vo, (int)so, 0);
-}
-
-// v_t of this lane's 4 columns.
-template <bool BF16>
-struct VLoad;
-template <>
-struct VLoad<false> {
-    using T4 = float4;
-    static constexpr int ESZ = 4;
-    __device__ static T4 load(rsrc_t r, uint32_t vo, uint32_t so) { return ld_f4(r, vo, so); }
-    __device__ static float4 f(const T4& x) { return x; }
-};
-template <>
-struct VLoad<true> {
-    using T4 = int2;
-    static constexpr int ESZ = 2;
-    __device__ static T4 load(rsrc_t r, uint32_t vo, uint32_t so) { return ld_i2(r, vo, so); }
-    __device__ static float4 f(const T4& x) {
-        const uint32_t a = (uint32_t)x.x, b = (uint32_t)x.y;
-        return make_float4(__uint_as_float(a << 16), __uint_as_float(a & 0xFFFF0000u),
-                           __uint_as_float(b << 16), __uint_as_float(b & 0xFFFF0000u));
-    }
-};
-
-__device__ __forceinline__ float4 f4_scale(float s, float4 a) {
-    return make_float4(s * a.x, s * a.y, s * a.z, s * a.w);
-}
-__device__ __forceinline__ float4 f4_fma(float s, float4 a, float4 c) {  // s*a + c
-    return make_float4(fmaf(s, a.x, c.x), fmaf(s, a.y, c.y), fmaf(s, a.z, c.z), fmaf(s, a.w, c.w));
-}
-__device__ __forceinline__ float4 f4_sub(float4 a, float4 b) {
-    return make_float4(a.x - b.x, a.y - b.y, a.z - b.z, a.w - b.w);
-}
-__device__ __forceinline__ float4 f4_add(float4 a, float4 b) {
-    return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
-}
-
-// x + (x rotated by N lanes within each row of 16): DPP row_ror
-template <int N>
-__device__ __forceinline__ float ror_add(float x) {
-    return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x120 + N, 0xF, 0xF, false));
-}
-// Sum over the G rows of a wavefront (lane = row * L + chunk), as a
-// reduce-scatter: the gfx950 permlane swaps exchange one register between lane
-// halves (32) and quarter pairs (16), so each swap + add halves the number of
-// components a lane carries. Lane l ends with component l / 16 of column chunk
-// l % L summed over all rows; lanes that share (l / 16, l % L) hold equal bits.
-//   swap32(A, B): lanes < 32 get {A[l], A[l+32]}, lanes >= 32 get {B[l-32], B[l]}
-//   swap16(A, B): the same between even and odd rows of 16 lanes
-template <int L>
-__device__ __forceinline__ float rows_reduce(float4 x) {
-    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x.x), __float_as_uint(x.z), false, false);
-    const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(x.y), __float_as_uint(x.w), false, false);
-    const float a = __uint_as_float(p[0]) + __uint_as_float(p[1]);  // comp 0 (lanes < 32) or 2
-    const float b = __uint_as_float(q[0]) + __uint_as_float(q[1]);  // comp 1 (lanes < 32) or 3
-    const auto u = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
-    float c = __uint_as_float(u[0]) + __uint_as_float(u[1]);        // comp lane / 16
-    if constexpr (L <= 8) c = ror_add<8>(c);
-    if constexpr (L <= 4) c = ror_add<4>(c);
-    if constexpr (L <= 2) c = ror_add<2>(c);
-    if constexpr (L <= 1) c = ror_add<1>(c);
-    return c;
-}
-
 // Sum of the first Q partial-sum slots (stride S) as a balanced tree. Slots of
 // readers that do not run hold zero, so any power of two Q >= the number of
 // running readers gives the same sum: the tree over 2Q adds a zero subtree.
@@ -443,9 +350,16 @@ struct ScanKArgs {
     int dv, nslab, P;
     int64_t NS;
     int NWW, NWR;
+    float* snap;    // SAVE: pre-images of stream s at snap + s * snap_s, [T][W][dv]
+    int64_t snap_s;
+    int W;
 };
 
-template <int S, int FORM, bool VBF16>
+// SAVE (training forward): every write also stores its row as it was before
+// this token's decay (the pre-image M_{t-1}[i]) at [t][write position][col],
+// which the backward uses to undo the write. It runs with one row partition,
+// so a writer's rank in its token is the write position.
+template <int S, int FORM, bool VBF16, bool SAVE>
 __global__ __launch_bounds__(SlabCfg<S>::NWMAX * 64) void scan_kernel(ScanKArgs a) {
     constexpr int L = S / 4, G = 64 / L;
     constexpr int D = SlabCfg<S>::D, NWMAX = SlabCfg<S>::NWMAX, NRMAX = nrmax<S>();
@@ -476,6 +390,7 @@ __global__ __launch_bounds__(SlabCfg<S>::NWMAX * 64) void scan_kernel(ScanKArgs 
     const rsrc_t Rm = make_rsrc(a.M + s * a.N * dv, a.N * dv * 4);
     const rsrc_t Rv = make_rsrc(static_cast<const char*>(a.v) + s * a.TS * dv * VL::ESZ, (int64_t)T * dv * VL::ESZ);
     const rsrc_t Ry = make_rsrc(a.y + s * a.ys + part * a.yp, (int64_t)T * dv * 4);
+    const rsrc_t Rs = make_rsrc(SAVE ? a.snap + s * a.snap_s : a.M, SAVE ? (int64_t)T * a.W * dv * 4 : 0);
     const bool writer = wave < NWW;
     const int pos = wave * G + r;                        // write position of a writer lane
     const int rw = wave - NWW;                           // reader index
@@ -483,6 +398,8 @@ __global__ __launch_bounds__(SlabCfg<S>::NWMAX * 64) void scan_kernel(ScanKArgs 
     const uint32_t dv4 = (uint32_t)dv * 4u, col4 = (uint32_t)col * 4u;
     const uint32_t v_off = (uint32_t)col * VL::ESZ;
     const uint32_t vstride = (uint32_t)dv * VL::ESZ;
+    const uint32_t sstride = (uint32_t)a.W * dv4;                    // snapshot bytes per token
+    const uint32_t s_lane = (uint32_t)pos * dv4 + col4;
     // reader 0's first S lanes store y[t-1] (one column each); every other y store is dropped
     const uint32_t y_off = (!writer && rw == 0 && lane < S) ? (uint32_t)(slab * S + lane) * 4u : OOB;
     const int ylane = lane < S ? lane : 0;
@@ -533,10 +450,12 @@ __global__ __launch_bounds__(SlabCfg<S>::NWMAX * 64) void scan_kernel(ScanKArgs 
     };
 
     // one token of a writer wavefront (barriers: [B'_t], B_t)
-    auto write_token = [&](int slot, int4 e, float4 pre, V4 vt) {
+    auto write_token = [&](int t, int slot, int4 e, float4 pre, V4 vt) {
         const uint32_t pk = (uint32_t)e.x;
         const float w = __int_as_float(e.y), al = __int_as_float(e.z), be = __int_as_float(e.w);
-        const float4 mt = f4_scale(al, source(slot, pk, pre));
+        const float4 old = source(slot, pk, pre);
+        if constexpr (SAVE) st_f4(old, Rs, (pk & ENT_INVALID) ? OOB : s_lane, (uint32_t)t * sstride);
+        const float4 mt = f4_scale(al, old);
         float4 pred = mt;
         if constexpr (FORM == 1) {
             const float part = rows_reduce<L>(f4_scale(w, mt));
@@ -587,6 +506,7 @@ __global__ __launch_bounds__(SlabCfg<S>::NWMAX * 64) void scan_kernel(ScanKArgs 
                     vv[q - DM] = load_v(q - DM);
                 }
                 st_f4(make_float4(0.f, 0.f, 0.f, 0.f), Rm, OOB, 0u);
+                if constexpr (SAVE) st_f4(make_float4(0.f, 0.f, 0.f, 0.f), Rs, OOB, 0u);
             }
             for (int t0 = 0; t0 + U <= T; t0 += U) {
 #pragma unroll
@@ -595,7 +515,7 @@ __global__ __launch_bounds__(SlabCfg<S>::NWMAX * 64) void scan_kernel(ScanKArgs 
                     ent[(j + D + DM) % U] = load_went(t + D + DM < T ? t + D + DM : T - 1);
                     pre[(j + D) % UP] = load_row((uint32_t)ent[(j + D) % U].x);
                     vv[(j + D) % UP] = load_v(t + D < T ? t + D : T - 1);
-                    write_token(j, ent[j], pre[j % UP], vv[j % UP]);
+                    write_token(t, j, ent[j], pre[j % UP], vv[j % UP]);
                 }
             }
         } else {
@@ -622,7 +542,7 @@ __global__ __launch_bounds__(SlabCfg<S>::NWMAX * 64) void scan_kernel(ScanKArgs 
     for (int t = t_done; t < T; ++t) {
         if (writer) {
             const int4 e = load_went(t);
-            write_token(t % U, e, load_row((uint32_t)e.x), load_v(t));
+            write_token(t, t % U, e, load_row((uint32_t)e.x), load_v(t));
         } else {
             const int2 e = load_rent(t);
             read_token(t, t % U, e, load_row((uint32_t)e.x));
@@ -657,9 +577,10 @@ struct DirectArgs {
     int dv, nslab;
     int64_t NS;
     int NWW, NWR;
+    float* snap;    // SAVE: [NS][T][W][dv] pre-images
 };
 
-template <int S, int FORM, bool VBF16>
+template <int S, int FORM, bool VBF16, bool SAVE>
 __global__ __launch_bounds__(SlabCfg<S>::NWMAX * 64) void scan_direct_kernel(DirectArgs a) {
     constexpr int L = S / 4, G = 64 / L;
     constexpr int NWMAX = SlabCfg<S>::NWMAX, NRMAX = nrmax<S>();
@@ -686,6 +607,7 @@ __global__ __launch_bounds__(SlabCfg<S>::NWMAX * 64) void scan_direct_kernel(Dir
     const rsrc_t Rv = make_rsrc(static_cast<const char*>(a.v) + s * (int64_t)T * dv * VL::ESZ,
                                 (int64_t)T * dv * VL::ESZ);
     const rsrc_t Ry = make_rsrc(a.y + s * (int64_t)T * dv, (int64_t)T * dv * 4);
+    const rsrc_t Rs = make_rsrc(SAVE ? a.snap + s * (int64_t)T * W * dv : a.M, SAVE ? (int64_t)T * W * dv * 4 : 0);
     const uint32_t dv4 = (uint32_t)dv * 4u, col4 = (uint32_t)col * 4u;
     const uint32_t y_off = (!writer && rw == 0 && lane < S) ? (uint32_t)(slab * S + lane) * 4u : OOB;
     const int ylane = lane < S ? lane : 0;
@@ -716,6 +638,8 @@ __global__ __launch_bounds__(SlabCfg<S>::NWMAX * 64) void scan_direct_kernel(Dir
         }
         if (writer) {
             const float4 pre = ld_f4(Rm, off, 0u);  // after the barrier that closed token t-1
+            if constexpr (SAVE)
+                st_f4(pre, Rs, off == OOB ? OOB : (uint32_t)pos * dv4 + col4, (uint32_t)t * (uint32_t)W * dv4);
             const float4 mt = f4_scale(al, pre);
             float4 pred = mt;
             if constexpr (FORM == 1) {
@@ -767,8 +691,9 @@ __global__ __launch_bounds__(256) void ypart_reduce(const float4* __restrict__ y
 
 // Tokens per launch: every buffer one stream spans in a launch (plan records, v,
 // y) stays below 2 GiB, so 32-bit offsets and the dropped-access offset work.
-int64_t chunk_tokens(int64_t T, const Geom& g, int dv) {
-    const int64_t per_tok = g.rec() > (int64_t)dv * 4 ? g.rec() : (int64_t)dv * 4;
+int64_t chunk_tokens(int64_t T, const Geom& g, int dv, int save_w = 0) {
+    int64_t per_tok = g.rec() > (int64_t)dv * 4 ? g.rec() : (int64_t)dv * 4;
+    if ((int64_t)save_w * dv * 4 > per_tok) per_tok = (int64_t)save_w * dv * 4;
     const int64_t cap = (int64_t)0x7FFFFFFF / per_tok;
     return T < cap ? T : cap;
 }
@@ -808,7 +733,8 @@ hipError_t launch_scan_slab(const ScanArgs& a, const Cfg& c, hipStream_t st) {
     while ((1 << psh) < c.P) ++psh;
     int TT = HT_WRITES / a.W - D;
     if (TT < 1) TT = 1;
-    const int64_t Tc = chunk_tokens(a.T, g, a.dv);
+    const bool save = a.snap != nullptr;
+    const int64_t Tc = chunk_tokens(a.T, g, a.dv, save ? a.W : 0);
     const WsLayout wl = ws_layout(c, a.NS, Tc, a.dv);
     const int nslab = a.dv / S;
     const int64_t nblk = ((a.NS + 7) / 8) * 8 * nslab * c.P;
@@ -846,13 +772,20 @@ hipError_t launch_scan_slab(const ScanArgs& a, const Cfg& c, hipStream_t st) {
         }
         k.T = (int)Tn; k.TS = a.T; k.N = a.N; k.dv = a.dv; k.nslab = nslab; k.P = c.P; k.NS = a.NS;
         k.NWW = g.NWW; k.NWR = g.NWR;
+        k.W = a.W;
+        k.snap = save ? a.snap + c0 * a.W * a.dv : nullptr;
+        k.snap_s = a.T * a.W * a.dv;
         dim3 grid((unsigned)nblk), block((unsigned)(g.nw() * 64));
-        if (a.form == 0) {
-            if (a.v_bf16) hipLaunchKernelGGL((scan_kernel<S, 0, true>), grid, block, lds, st, k);
-            else hipLaunchKernelGGL((scan_kernel<S, 0, false>), grid, block, lds, st, k);
-        } else {
-            if (a.v_bf16) hipLaunchKernelGGL((scan_kernel<S, 1, true>), grid, block, lds, st, k);
-            else hipLaunchKernelGGL((scan_kernel<S, 1, false>), grid, block, lds, st, k);
+        const int sel = (a.form ? 4 : 0) | (a.v_bf16 ? 2 : 0) | (save ? 1 : 0);
+        switch (sel) {
+            case 0: hipLaunchKernelGGL((scan_kernel<S, 0, false, false>), grid, block, lds, st, k); break;
+            case 1: hipLaunchKernelGGL((scan_kernel<S, 0, false, true>), grid, block, lds, st, k); break;
+            case 2: hipLaunchKernelGGL((scan_kernel<S, 0, true, false>), grid, block, lds, st, k); break;
+            case 3: hipLaunchKernelGGL((scan_kernel<S, 0, true, true>), grid, block, lds, st, k); break;
+            case 4: hipLaunchKernelGGL((scan_kernel<S, 1, false, false>), grid, block, lds, st, k); break;
+            case 5: hipLaunchKernelGGL((scan_kernel<S, 1, false, true>), grid, block, lds, st, k); break;
+            case 6: hipLaunchKernelGGL((scan_kernel<S, 1, true, false>), grid, block, lds, st, k); break;
+            default: hipLaunchKernelGGL((scan_kernel<S, 1, true, true>), grid, block, lds, st, k); break;
         }
         e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -878,14 +811,19 @@ hipError_t launch_scan_direct(const ScanArgs& a, hipStream_t st) {
     d.alpha = a.alpha; d.beta = a.beta; d.v = a.v; d.M = a.M; d.y = a.y;
     d.T = (int)a.T; d.N = a.N; d.dv = a.dv; d.nslab = a.dv / S; d.NS = a.NS;
     d.NWW = g.NWW; d.NWR = g.NWR;
+    d.snap = a.snap;
     const int64_t nblk = ((a.NS + 7) / 8) * 8 * d.nslab;
     dim3 grid((unsigned)nblk), block((unsigned)(g.nw() * 64));
-    if (a.form == 0) {
-        if (a.v_bf16) hipLaunchKernelGGL((scan_direct_kernel<S, 0, true>), grid, block, 0, st, d);
-        else hipLaunchKernelGGL((scan_direct_kernel<S, 0, false>), grid, block, 0, st, d);
-    } else {
-        if (a.v_bf16) hipLaunchKernelGGL((scan_direct_kernel<S, 1, true>), grid, block, 0, st, d);
-        else hipLaunchKernelGGL((scan_direct_kernel<S, 1, false>), grid, block, 0, st, d);
+    const int sel = (a.form ? 4 : 0) | (a.v_bf16 ? 2 : 0) | (a.snap ? 1 : 0);
+    switch (sel) {
+        case 0: hipLaunchKernelGGL((scan_direct_kernel<S, 0, false, false>), grid, block, 0, st, d); break;
+        case 1: hipLaunchKernelGGL((scan_direct_kernel<S, 0, false, true>), grid, block, 0, st, d); break;
+        case 2: hipLaunchKernelGGL((scan_direct_kernel<S, 0, true, false>), grid, block, 0, st, d); break;
+        case 3: hipLaunchKernelGGL((scan_direct_kernel<S, 0, true, true>), grid, block, 0, st, d); break;
+        case 4: hipLaunchKernelGGL((scan_direct_kernel<S, 1, false, false>), grid, block, 0, st, d); break;
+        case 5: hipLaunchKernelGGL((scan_direct_kernel<S, 1, false, true>), grid, block, 0, st, d); break;
+        case 6: hipLaunchKernelGGL((scan_direct_kernel<S, 1, true, false>), grid, block, 0, st, d); break;
+        default: hipLaunchKernelGGL((scan_direct_kernel<S, 1, true, true>), grid, block, 0, st, d); break;
     }
     return hipGetLastError();
 }
@@ -948,9 +886,11 @@ int pick_slab(int64_t NS, int W, int R, int dv, int forced) {
 // more than the extra padding lanes of a partitioned record. The shared-residual
 // form (FIG2) couples all rows of a token and keeps P = 1.
 // SDM_SCAN_SLAB and SDM_SCAN_PARTS force a width and a partition count.
-Cfg choose_cfg(int64_t NS, int W, int R, int dv, int form) {
+// The training forward (snapshots) keeps P = 1 for both forms, so that a
+// writer's rank is its write position.
+Cfg choose_cfg(int64_t NS, int W, int R, int dv, int form, bool save = false) {
     Cfg c;
-    const int fs = env_int("SDM_SCAN_SLAB"), fp = env_int("SDM_SCAN_PARTS");
+    const int fs = env_int("SDM_SCAN_SLAB"), fp = save ? 1 : env_int("SDM_SCAN_PARTS");
     if (form == 0 && (fs == 0 || fs == 32) && slab_fits(32, W, R, dv) && fp != 1) {
         c.S = 32;
     } else {
@@ -999,7 +939,8 @@ int64_t direct_max_tokens() {
 }
 
 hipError_t launch_scan(const ScanArgs& a, hipStream_t st) {
-    if (a.T <= direct_max_tokens() && a.T * (int64_t)a.dv * 4 < 0x7FFFFFFF) {
+    const int64_t per_tok = (int64_t)a.dv * 4 * (a.snap ? (a.W > 1 ? a.W : 1) : 1);
+    if (a.T <= direct_max_tokens() && a.T * per_tok < 0x7FFFFFFF) {
         switch (pick_slab(a.NS, a.W, a.R, a.dv, env_int("SDM_SCAN_SLAB"))) {
             case 32: return launch_scan_direct<32>(a, st);
             case 16: return launch_scan_direct<16>(a, st);
@@ -1008,7 +949,7 @@ hipError_t launch_scan(const ScanArgs& a, hipStream_t st) {
             default: break;
         }
     }
-    const Cfg c = choose_cfg(a.NS, a.W, a.R, a.dv, a.form);
+    const Cfg c = choose_cfg(a.NS, a.W, a.R, a.dv, a.form, a.snap != nullptr);
     switch (c.S) {
         case 32: return launch_scan_slab<32>(a, c, st);
         case 16: return launch_scan_slab<16>(a, c, st);

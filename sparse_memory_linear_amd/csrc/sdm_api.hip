@@ -5,6 +5,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <initializer_list>
+
 #include "sdm.h"
 #include "sdm_internal.h"
 
@@ -144,14 +146,20 @@ int64_t sdm_scan_workspace_bytes(int64_t B, int64_t H, int64_t T, int64_t W, int
     return sdm::scan_workspace_bytes(B * H, T, (int)W, (int)R, (int)dv);
 }
 
-int sdm_scan_forward(const int32_t* idx_w, const float* wt_w, int64_t W, const int32_t* idx_r, const float* wt_r,
-                     int64_t R, const float* alpha, const float* beta, const void* v, int v_dtype, float* M,
-                     float* y, int64_t B, int64_t H, int64_t T, int64_t N, int64_t dv, int form, void* workspace,
-                     int64_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared checks of the scan entry points (sizes, dtypes, pointers, alignment,
+// workspace). 0 when the call may launch; NO_WORK when there is no work (the
+// call succeeds and launches nothing); otherwise the status code.
+constexpr int NO_WORK = -1;
+int check_scan(const char* fn, const int32_t* idx_w, const float* wt_w, int64_t W, const int32_t* idx_r,
+               const float* wt_r, int64_t R, const float* alpha, const float* beta, const void* v, int v_dtype,
+               int64_t B, int64_t H, int64_t T, int64_t N, int64_t dv, int form) {
     if (v_dtype != SDM_F32 && v_dtype != SDM_BF16) return fail(SDM_ERR_DTYPE, "unknown v dtype %d", v_dtype);
     if (form != SDM_DELTA_EQ4 && form != SDM_DELTA_FIG2) return fail(SDM_ERR_DTYPE, "unknown delta form %d", form);
-    if (B < 0 || H < 0 || T < 0 || N < 1 || dv < 1)
-        return fail(SDM_ERR_SHAPE, "sdm_scan_forward: invalid sizes");
+    if (B < 0 || H < 0 || T < 0 || N < 1 || dv < 1) return fail(SDM_ERR_SHAPE, "%s: invalid sizes", fn);
     if (W < 1 || R < 1 || W > N || R > N)
         return fail(SDM_ERR_SHAPE, "W=%lld, R=%lld must lie in [1, N=%lld]", (long long)W, (long long)R,
                     (long long)N);
@@ -164,19 +172,45 @@ int sdm_scan_forward(const int32_t* idx_w, const float* wt_w, int64_t W, const i
     if (!sdm::scan_geometry(B * H > 0 ? B * H : 1, (int)W, (int)R, (int)dv, nullptr, nullptr))
         return fail(SDM_ERR_UNSUPPORTED, "no scan kernel covers W=%lld, R=%lld, dv=%lld", (long long)W,
                     (long long)R, (long long)dv);
-    if (B == 0 || H == 0 || T == 0) return ok();  // empty tensors may have NULL data
-    if (!idx_w || !wt_w || !idx_r || !wt_r || !alpha || !beta || !v || !M || !y)
-        return fail(SDM_ERR_NULL, "sdm_scan_forward: a required pointer is NULL");
-    const void* ptrs[] = {idx_w, wt_w, idx_r, wt_r, alpha, beta, v, M, y};
+    if ((B * H + 7) / 8 * 8 * (dv / 4) > 0x7FFFFFFFll)
+        return fail(SDM_ERR_UNSUPPORTED, "too many streams for one launch");
+    if (B == 0 || H == 0 || T == 0) return NO_WORK;  // empty tensors may have NULL data
+    if (!idx_w || !wt_w || !idx_r || !wt_r || !alpha || !beta || !v)
+        return fail(SDM_ERR_NULL, "%s: a required pointer is NULL", fn);
+    const void* ptrs[] = {idx_w, wt_w, idx_r, wt_r, alpha, beta, v};
     for (const void* p : ptrs)
-        if (!aligned16(p)) return fail(SDM_ERR_ALIGN, "sdm_scan_forward: pointer %p not 16-byte aligned", p);
-    const int64_t need = sdm::scan_workspace_bytes(B * H, T, (int)W, (int)R, (int)dv);
+        if (!aligned16(p)) return fail(SDM_ERR_ALIGN, "%s: pointer %p not 16-byte aligned", fn, p);
+    return 0;
+}
+
+int check_buffers(const char* fn, std::initializer_list<const void*> ptrs) {
+    for (const void* p : ptrs) {
+        if (!p) return fail(SDM_ERR_NULL, "%s: a required pointer is NULL", fn);
+        if (!aligned16(p)) return fail(SDM_ERR_ALIGN, "%s: pointer %p not 16-byte aligned", fn, p);
+    }
+    return 0;
+}
+
+int check_workspace(void* workspace, int64_t workspace_bytes, int64_t need) {
     if (!workspace || workspace_bytes < need)
         return fail(SDM_ERR_WORKSPACE, "workspace of %lld bytes needed, %lld given", (long long)need,
                     (long long)(workspace ? workspace_bytes : 0));
     if (!aligned16(workspace)) return fail(SDM_ERR_ALIGN, "workspace not 16-byte aligned");
-    if ((B * H + 7) / 8 * 8 * (dv / 4) > 0x7FFFFFFFll)
-        return fail(SDM_ERR_UNSUPPORTED, "too many streams for one launch");
+    return 0;
+}
+
+int scan_forward_impl(const char* fn, const int32_t* idx_w, const float* wt_w, int64_t W, const int32_t* idx_r,
+                      const float* wt_r, int64_t R, const float* alpha, const float* beta, const void* v,
+                      int v_dtype, float* M, float* y, float* snap, bool save, int64_t B, int64_t H, int64_t T,
+                      int64_t N, int64_t dv, int form, void* workspace, int64_t workspace_bytes, void* stream) {
+    int rc = check_scan(fn, idx_w, wt_w, W, idx_r, wt_r, R, alpha, beta, v, v_dtype, B, H, T, N, dv, form);
+    if (rc == NO_WORK) return ok();
+    if (rc) return rc;
+    if ((rc = check_buffers(fn, {M, y}))) return rc;
+    if (save && (rc = check_buffers(fn, {snap}))) return rc;
+    if ((rc = check_workspace(workspace, workspace_bytes,
+                              sdm::scan_workspace_bytes(B * H, T, (int)W, (int)R, (int)dv))))
+        return rc;
     sdm::ScanArgs a{};
     a.idx_w = idx_w; a.wt_w = wt_w; a.W = (int)W;
     a.idx_r = idx_r; a.wt_r = wt_r; a.R = (int)R;
@@ -186,8 +220,84 @@ int sdm_scan_forward(const int32_t* idx_w, const float* wt_w, int64_t W, const i
     a.NS = B * H; a.T = T; a.N = N; a.dv = (int)dv;
     a.form = form;
     a.workspace = workspace;
+    a.snap = save ? snap : nullptr;
     hipError_t e = sdm::launch_scan(a, static_cast<hipStream_t>(stream));
-    if (e != hipSuccess) return hip_fail(e, "sdm_scan_forward launch");
+    if (e != hipSuccess) return hip_fail(e, fn);
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int sdm_scan_forward(const int32_t* idx_w, const float* wt_w, int64_t W, const int32_t* idx_r, const float* wt_r,
+                     int64_t R, const float* alpha, const float* beta, const void* v, int v_dtype, float* M,
+                     float* y, int64_t B, int64_t H, int64_t T, int64_t N, int64_t dv, int form, void* workspace,
+                     int64_t workspace_bytes, void* stream) {
+    return scan_forward_impl("sdm_scan_forward", idx_w, wt_w, W, idx_r, wt_r, R, alpha, beta, v, v_dtype, M, y,
+                             nullptr, false, B, H, T, N, dv, form, workspace, workspace_bytes, stream);
+}
+
+int64_t sdm_scan_snapshot_bytes(int64_t B, int64_t H, int64_t T, int64_t W, int64_t dv) {
+    if (B < 0 || H < 0 || T < 0 || W < 1 || dv < 1) return -1;
+    return B * H * T * W * dv * 4;
+}
+
+int sdm_scan_forward_save(const int32_t* idx_w, const float* wt_w, int64_t W, const int32_t* idx_r,
+                          const float* wt_r, int64_t R, const float* alpha, const float* beta, const void* v,
+                          int v_dtype, float* M, float* y, float* snap, int64_t B, int64_t H, int64_t T, int64_t N,
+                          int64_t dv, int form, void* workspace, int64_t workspace_bytes, void* stream) {
+    return scan_forward_impl("sdm_scan_forward_save", idx_w, wt_w, W, idx_r, wt_r, R, alpha, beta, v, v_dtype, M,
+                             y, snap, true, B, H, T, N, dv, form, workspace, workspace_bytes, stream);
+}
+
+int64_t sdm_scan_backward_workspace_bytes(int64_t B, int64_t H, int64_t T, int64_t W, int64_t R, int64_t dv) {
+    if (B < 0 || H < 0 || T < 0 || W < 1 || R < 1 || W > 256 || R > 256 || dv < 4 || dv % 4) return -1;
+    if (B == 0 || H == 0 || T == 0) return 0;
+    return sdm::scan_backward_workspace_bytes(B * H, T, (int)W, (int)R, (int)dv);
+}
+
+int sdm_scan_backward(const int32_t* idx_w, const float* wt_w, int64_t W, const int32_t* idx_r, const float* wt_r,
+                      int64_t R, const float* alpha, const float* beta, const void* v, int v_dtype,
+                      const float* snap, const float* dy, float* M, float* dM, float* dv_out, float* dalpha,
+                      float* dbeta, float* dwt_w, float* dwt_r, int64_t B, int64_t H, int64_t T, int64_t N,
+                      int64_t dv, int form, void* workspace, int64_t workspace_bytes, void* stream) {
+    const char* fn = "sdm_scan_backward";
+    int rc = check_scan(fn, idx_w, wt_w, W, idx_r, wt_r, R, alpha, beta, v, v_dtype, B, H, T, N, dv, form);
+    if (rc == NO_WORK) return ok();
+    if (rc) return rc;
+    if (!sdm::scan_backward_geometry(B * H, (int)W, (int)R, (int)dv))
+        return fail(SDM_ERR_UNSUPPORTED, "no backward kernel covers W=%lld, R=%lld, dv=%lld", (long long)W,
+                    (long long)R, (long long)dv);
+    if ((rc = check_buffers(fn, {snap, dy, M, dM, dv_out, dalpha, dbeta, dwt_w, dwt_r}))) return rc;
+    if ((rc = check_workspace(workspace, workspace_bytes,
+                              sdm::scan_backward_workspace_bytes(B * H, T, (int)W, (int)R, (int)dv))))
+        return rc;
+    sdm::BwdArgs a{};
+    a.idx_w = idx_w; a.wt_w = wt_w; a.W = (int)W;
+    a.idx_r = idx_r; a.wt_r = wt_r; a.R = (int)R;
+    a.alpha = alpha; a.beta = beta;
+    a.v = v; a.v_bf16 = v_dtype == SDM_BF16;
+    a.snap = snap; a.dy = dy; a.M = M; a.dM = dM;
+    a.dv_out = dv_out; a.dalpha = dalpha; a.dbeta = dbeta; a.dwt_w = dwt_w; a.dwt_r = dwt_r;
+    a.NS = B * H; a.T = T; a.N = N; a.dv = (int)dv;
+    a.form = form;
+    a.workspace = workspace;
+    hipError_t e = sdm::launch_scan_backward(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, fn);
+    return ok();
+}
+
+int sdm_state_init_backward(const float* dM, float* dM0, int64_t B, int64_t H, int64_t N, int64_t dv,
+                            void* stream) {
+    if (B < 0 || H < 0 || N < 1 || dv < 1) return fail(SDM_ERR_SHAPE, "sdm_state_init_backward: invalid sizes");
+    if (dv % 4 != 0) return fail(SDM_ERR_UNSUPPORTED, "sdm_state_init_backward: dv must be a multiple of 4");
+    if (H == 0) return ok();
+    if (B == 0) return fail(SDM_ERR_SHAPE, "sdm_state_init_backward: B must be >= 1");
+    int rc = check_buffers("sdm_state_init_backward", {dM, dM0});
+    if (rc) return rc;
+    hipError_t e = sdm::launch_state_init_backward(dM, dM0, B, H * N * dv, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "sdm_state_init_backward launch");
     return ok();
 }
 

@@ -32,11 +32,34 @@ struct ScanArgs {
     int dv;
     int form;                // 0 = per-slot Eq. (4), 1 = Fig. 2 shared residual
     void* workspace;
+    float* snap;             // optional [NS][T][W][dv]: pre-image of every write (training forward)
 };
 // Chooses the kernel instance; returns false if no instance covers (W, R, dv).
 bool scan_geometry(int64_t NS, int W, int R, int dv, int* slab, int* rec_bytes);
 int64_t scan_workspace_bytes(int64_t NS, int64_t T, int W, int R, int dv);
 hipError_t launch_scan(const ScanArgs& a, hipStream_t st);
+
+struct BwdArgs {
+    const int32_t* idx_w; const float* wt_w; int W;
+    const int32_t* idx_r; const float* wt_r; int R;
+    const float* alpha; const float* beta;
+    const void* v; bool v_bf16;
+    const float* snap;       // [NS][T][W][dv] from the training forward
+    const float* dy;         // [NS][T][dv]
+    float* M;                // in: state after token T-1; out: before token 0 (restored)
+    float* dM;               // in: dL/dM after token T-1; out: dL/dM before token 0
+    float* dv_out;           // [NS][T][dv]
+    float* dalpha; float* dbeta;   // [NS][T]
+    float* dwt_w; float* dwt_r;    // [NS][T][W], [NS][T][R]
+    int64_t NS, T, N;
+    int dv;
+    int form;
+    void* workspace;
+};
+int64_t scan_backward_workspace_bytes(int64_t NS, int64_t T, int W, int R, int dv);
+bool scan_backward_geometry(int64_t NS, int W, int R, int dv);
+hipError_t launch_scan_backward(const BwdArgs& a, hipStream_t st);
+hipError_t launch_state_init_backward(const float* dM, float* dM0, int64_t B, int64_t per_seq, hipStream_t st);
 
 hipError_t launch_state_init(const float* M0, float* M, int64_t B, int64_t per_seq, hipStream_t st);
 

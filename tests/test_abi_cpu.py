@@ -29,7 +29,9 @@ def lib():
 def test_header_declares_the_hot_path_calls():
     names = declared_functions()
     for f in ("sdm_address", "sdm_scan_forward", "sdm_state_init", "sdm_debug_half_scores",
-              "sdm_scan_workspace_bytes", "sdm_status_string", "sdm_last_error", "sdm_abi_version"):
+              "sdm_scan_workspace_bytes", "sdm_status_string", "sdm_last_error", "sdm_abi_version",
+              "sdm_scan_forward_save", "sdm_scan_snapshot_bytes", "sdm_scan_backward",
+              "sdm_scan_backward_workspace_bytes", "sdm_state_init_backward"):
         assert f in names
 
 
@@ -40,7 +42,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert binding.sdm_abi_version() == 1
+    assert binding.sdm_abi_version() == 2
     assert binding.sdm_status_string(0) == "ok"
     assert binding.sdm_status_string(7).startswith("workspace")
     assert binding.sdm_status_string(99) == "unknown status"
@@ -104,6 +106,48 @@ def test_scan_rejects_bad_arguments_before_launch(lib):
     assert call(wsb=100) == 7
     assert call(y=P(4104)) == 4
     assert "workspace" in binding.sdm_last_error() or "aligned" in binding.sdm_last_error()
+
+
+def test_training_sizes_are_pure_host_logic(lib):
+    # pre-images: one fp32 row per write
+    assert binding.sdm_scan_snapshot_bytes(4, 8, 8192, 64, 128) == 4 * 8 * 8192 * 64 * 128 * 4
+    assert lib.sdm_scan_snapshot_bytes(1, 1, 1, 0, 16) == -1
+    # backward partial sums: per slab, per (stream, token) W + R + 2 floats. 32 streams:
+    # 16-column slabs (the widest with 256 workgroups), 8 slabs
+    assert binding.sdm_scan_backward_workspace_bytes(4, 8, 8192, 64, 64, 128) == 8 * 32 * 8192 * 130 * 4
+    # 8 streams: 4-column slabs (32 per stream); chunks of at most 2^31 / (W dv 4) tokens
+    assert binding.sdm_scan_backward_workspace_bytes(1, 8, 1000, 64, 64, 128) == 32 * 8 * 1000 * 130 * 4
+    assert binding.sdm_scan_backward_workspace_bytes(1, 8, 131072, 64, 64, 128) == \
+        32 * 8 * (0x7FFFFFFF // (64 * 128 * 4)) * 130 * 4
+    assert binding.sdm_scan_backward_workspace_bytes(0, 8, 100, 64, 64, 128) == 0
+    assert lib.sdm_scan_backward_workspace_bytes(1, 1, 1, 300, 1, 16) == -1
+
+
+def test_training_calls_reject_bad_arguments_before_launch(lib):
+    fake = P(4096)
+    fwd = dict(iw=fake, ww=fake, W=64, ir=fake, wr=fake, R=64, a=fake, b=fake, v=fake, vd=1,
+               M=fake, y=fake, snap=fake, B=1, H=1, T=8, N=65536, dv=128, form=0, ws=fake,
+               wsb=1 << 30, st=None)
+    call = lambda **kw: lib.sdm_scan_forward_save(*dict(fwd, **kw).values())
+    assert call(snap=None) == 1
+    assert call(snap=P(4100)) == 4
+    assert call(snap=None, T=0) == 0
+    assert call(form=3) == 3
+    bwd = dict(iw=fake, ww=fake, W=64, ir=fake, wr=fake, R=64, a=fake, b=fake, v=fake, vd=1,
+               snap=fake, dy=fake, M=fake, dM=fake, dv=fake, da=fake, db=fake, dww=fake, dwr=fake,
+               B=1, H=1, T=8, N=65536, dvs=128, form=0, ws=fake, wsb=1 << 30, st=None)
+    callb = lambda **kw: lib.sdm_scan_backward(*dict(bwd, **kw).values())
+    for k in ("snap", "dy", "M", "dM", "dv", "da", "db", "dww", "dwr"):
+        assert callb(**{k: None}) == 1, k
+    assert callb(dy=P(4104)) == 4
+    assert callb(ws=None) == 7
+    assert callb(wsb=16) == 7
+    assert callb(dvs=130) == 5
+    assert callb(W=0) == 2
+    assert callb(snap=None, dy=None, T=0) == 0
+    assert lib.sdm_state_init_backward(None, fake, 2, 1, 16, 16, None) == 1
+    assert lib.sdm_state_init_backward(fake, fake, 0, 1, 16, 16, None) == 2
+    assert lib.sdm_state_init_backward(fake, fake, 2, 1, 16, 18, None) == 5
 
 
 def test_state_init_rejects_bad_arguments(lib):
