@@ -41,6 +41,8 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=20.0,
                    help="target CPU time of the oracle baseline sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--train", action="store_true",
+                   help="training step: addressing, forward with pre-images, backward with undo")
     p.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                    help="run one plain device copy of BYTES bytes before the benchmark "
                         "(a known-size kernel that calibrates HBM byte counters)")
@@ -105,6 +107,114 @@ def cpu_baseline(wl, x, target_s: float):
             "sample": f"{nb} of {wl.B} sequences of {wl.name}, all {wl.H} heads, first {Tp} of "
                       f"{wl.T} tokens (addressing of both branches + EQ4 scan), {ts:.1f} s wall",
             "host_cpu": host_cpu()}
+
+
+def cpu_baseline_train(wl, x, dy, target_s: float):
+    """The oracle's training step (addressing of both branches + its backward,
+    which runs its forward first) on a bounded sample: the first T' tokens of
+    the first sequence, all heads, T' sized from a calibration run."""
+    import oracle
+
+    nthreads = oracle.default_threads()
+
+    def run(Tp):
+        sl = lambda t: t[:1, :, :Tp].contiguous()
+        t0 = time.perf_counter()
+        iw, ww, _, _ = oracle.address(sl(x["q_w"]), x["subkeys"], wl.W, nthreads)
+        ir, wr, _, _ = oracle.address(sl(x["q_r"]), x["subkeys"], wl.R, nthreads)
+        oracle.scan_backward(iw, ww, ir, wr, sl(x["alpha"]), sl(x["beta"]), sl(x["v"]),
+                             oracle.broadcast_state(x["M0"].numpy(), 1), dy[:1, :, :Tp],
+                             None, oracle.EQ4, nthreads)
+        return time.perf_counter() - t0
+
+    T1, T2 = min(wl.T, 64), min(wl.T, 512)
+    t1, t2 = run(T1), run(T2)
+    per_tok = max((t2 - t1) / max(T2 - T1, 1), t2 / T2 * 0.1, 1e-6)
+    Tp = int(min(wl.T, max(T2, (target_s - max(t1 - T1 * per_tok, 0.0)) / per_tok)))
+    ts = run(Tp) if Tp != T2 else t2
+    return {"value": Tp / ts, "unit": "tokens/s", "cores": nthreads, "kind": "oracle",
+            "sample": f"1 of {wl.B} sequences of {wl.name}, all {wl.H} heads, first {Tp} of {wl.T} "
+                      f"tokens (addressing of both branches + EQ4 forward and backward), {ts:.1f} s wall",
+            "host_cpu": host_cpu()}
+
+
+def train_bench(a, wl, x, dev):
+    """Training: one step = table init, addressing of both branches, the forward
+    that stores pre-images, zeroing dL/dM of the final state, the backward that
+    undoes the forward, and the initial state's gradient (sum over sequences)."""
+    import torch
+    import sparse_memory_linear_amd as sdm
+
+    g = {k: v.to(dev) for k, v in x.items()}
+    B, H, T, N, dv, W, R = wl.B, wl.H, wl.T, wl.N, wl.d_v, wl.W, wl.R
+    gen = torch.Generator().manual_seed(1234)
+    dy_host = torch.randn((B, H, T, dv), generator=gen)
+    dy = dy_host.to(dev)
+    f32 = lambda *shape: torch.empty(shape, dtype=torch.float32, device=dev)
+    addr_out = (torch.empty((B, H, T, W), dtype=torch.int32, device=dev), f32(B, H, T, W),
+                torch.empty((B, H, T, R), dtype=torch.int32, device=dev), f32(B, H, T, R))
+    M, dM, y, snap = f32(B, H, N, dv), f32(B, H, N, dv), f32(B, H, T, dv), f32(B, H, T, W, dv)
+    grads = {"dv": f32(B, H, T, dv), "dalpha": f32(B, H, T), "dbeta": f32(B, H, T),
+             "dwt_w": f32(B, H, T, W), "dwt_r": f32(B, H, T, R)}
+    dM0 = f32(H, N, dv)
+    ws_f = torch.empty((sdm.sdm_scan_workspace_bytes(B, H, T, W, R, dv),), dtype=torch.uint8, device=dev)
+    ws_b = torch.empty((sdm.sdm_scan_backward_workspace_bytes(B, H, T, W, R, dv),), dtype=torch.uint8,
+                       device=dev)
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    NM = 7
+
+    def step(marks=None):
+        rec = (lambda i: marks[i].record()) if marks else (lambda i: None)
+        rec(0)
+        sdm.sdm_state_init(g["M0"], B, out=M)
+        rec(1)
+        iw, ww, ir, wr = sdm.sdm_address(g["q_w"], g["q_r"], g["subkeys"], g["subkeys"], W, R, out=addr_out)
+        rec(2)
+        args = (iw, ww, ir, wr, g["alpha"], g["beta"], g["v"])
+        sdm.sdm_scan_forward_save(*args, M, a.form, y=y, snap=snap, workspace=ws_f)
+        rec(3)
+        dM.zero_()
+        rec(4)
+        sdm.sdm_scan_backward(*args, snap, dy, M, dM, a.form, out=grads, workspace=ws_b)
+        rec(5)
+        sdm.sdm_state_init_backward(dM, out=dM0)
+        rec(6)
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    marks = [[ev() for _ in range(NM)] for _ in range(a.steps)]
+    t0 = time.perf_counter()
+    for i in range(a.steps):
+        step(marks[i])
+    torch.cuda.synchronize()
+    ms_step = 1e3 * (time.perf_counter() - t0) / a.steps
+    part = lambda i: sum(m[i].elapsed_time(m[i + 1]) for m in marks) / a.steps
+    names = ["state_init", "address", "forward_save", "dM_zero", "backward", "state_init_backward"]
+    br = {n: part(i) for i, n in enumerate(names)}
+    th = B * H * T
+    fwd_bytes = th * (3 * W + R) * dv * 4     # gather W, scatter W, store W pre-images, gather R
+    bwd_bytes = th * (4 * W + 3 * R) * dv * 4  # G, pre-image in and G, M out per write; M, G in, G out per read
+    bwd_gbps = bwd_bytes / (br["backward"] * 1e-3) / 1e9
+    rec = {
+        "metric": "SDM training tokens/s (addressing + forward with pre-images + backward with undo) "
+                  "at N=65536,W=R=64,d_v=128",
+        "value": B * T / (ms_step * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": a.steps,
+        "warmup": a.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": wl.name, "B": B, "H": H, "T": T, "N": N, "W": W, "R": R, "d_v": dv,
+                   "d_h": wl.d_h, "form": a.form, "mode": "train",
+                   "inputs": "bf16 q/v/subkeys, fp32 table/gates/gradients" if wl.bf16_inputs else "fp32"},
+        "breakdown_ms": br,
+        "forward_save_GBps": fwd_bytes / (br["forward_save"] * 1e-3) / 1e9,
+        "roofline": {"bound": "hbm", "achieved": bwd_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": bwd_gbps / HBM_PEAK_GBPS, "traffic": None,
+                     "kernel": "sdm_scan_backward (scan_backward_kernel + bwd_partials_reduce)",
+                     "algorithmic_bytes_per_launch": bwd_bytes},
+    }
+    if not a.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline_train(wl, x, dy_host.numpy(), a.cpu_seconds)
+    print(json.dumps(rec), flush=True)
 
 
 def decode_bench(a, wl, x, dev):
@@ -197,6 +307,8 @@ def main():
     x = inputs.make_inputs(wl)
     if wl.name == "decode":
         return decode_bench(a, wl, x, dev)
+    if a.train:
+        return train_bench(a, wl, x, dev)
     g = {k: v.to(dev) for k, v in x.items()}
     B, H, T, N, dv, W, R = wl.B, wl.H, wl.T, wl.N, wl.d_v, wl.W, wl.R
     addr_out = (torch.empty((B, H, T, W), dtype=torch.int32, device=dev),

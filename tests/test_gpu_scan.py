@@ -208,19 +208,30 @@ def test_state_init_broadcasts_M0():
 @pytest.mark.parametrize("name,streams", [("gdn_matched", [(0, 0), (3, 7)]), ("long_context", [(0, 5)])])
 def test_full_pipeline_full_size_sampled_streams(name, streams):
     """The whole hot path at full size, in the benchmark's launch configuration
-    (state init, addressing, scan); sampled (b, h) streams are checked in full
-    against the oracle scan fed with the GPU's slots and weights."""
+    (state init, addressing, scan). The sampled (b, h) streams take the oracle's
+    own slots and weights (written over the GPU's before the scan), so both
+    sides scan identical inputs that come from the oracle; those streams are
+    checked in full against the oracle scan."""
     wl = inputs.get(name)
     say(f"[pipeline full size] {name} B={wl.B} H={wl.H} T={wl.T} streams={streams}")
     x = inputs.make_inputs(wl)
     g = {k: v.to(DEV) for k, v in x.items()}
     iw, ww, ir, wr = sdm.sdm_address(g["q_w"], g["q_r"], g["subkeys"], g["subkeys"], wl.W, wl.R)
+    orc = {}
+    for (b, h) in streams:
+        q = lambda k: x[k][b:b + 1, h:h + 1]
+        oi, ow, _, _ = oracle.address(q("q_w"), x["subkeys"][h:h + 1], wl.W)
+        ri, rw, _, _ = oracle.address(q("q_r"), x["subkeys"][h:h + 1], wl.R)
+        orc[(b, h)] = (oi, ow, ri, rw)
+        for dst, src in ((iw, oi), (ww, ow), (ir, ri), (wr, rw)):
+            dst[b, h] = torch.from_numpy(src[0, 0]).to(DEV)
     M = sdm.sdm_state_init(g["M0"], wl.B)
     y = sdm.sdm_scan_forward(iw, ww, ir, wr, g["alpha"], g["beta"], g["v"], M, "eq4")
     torch.cuda.synchronize()
     for (b, h) in streams:
         sl = lambda t: t[b:b + 1, h:h + 1].cpu()
-        Mo, yo = oracle.scan(sl(iw), sl(ww), sl(ir), sl(wr), sl(x["alpha"]), sl(x["beta"]), sl(x["v"]),
+        oi, ow, ri, rw = orc[(b, h)]
+        Mo, yo = oracle.scan(oi, ow, ri, rw, sl(x["alpha"]), sl(x["beta"]), sl(x["v"]),
                              x["M0"][h:h + 1][None].numpy(), oracle.EQ4)
         _check(f"stream ({b},{h})", sl(M).numpy(), sl(y).numpy(), Mo, yo,
-               x["M0"][h:h + 1][None].numpy(), sl(iw).numpy(), TOL_BF16)
+               x["M0"][h:h + 1][None].numpy(), oi, TOL_BF16)
