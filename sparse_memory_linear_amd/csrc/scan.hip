@@ -150,6 +150,7 @@ struct PlanArgs {
     int64_t Tc, TS, N;
     int D, G, NWW, NWR, TT, pb, P, pshift;
     int64_t ntile;
+    int wpos;   // writer entries of the per-slot training forward: (packed, beta*w, alpha, write position)
 };
 
 // Rank of this lane's access among the valid accesses of its partition at
@@ -280,7 +281,10 @@ __global__ __launch_bounds__(PLAN_THREADS) __attribute__((amdgpu_waves_per_eu(4)
                     const uint32_t packed =
                         (uint32_t)row[u] | fwd_bits(ht, bm, (uint32_t)row[u], cur, cur - D, cur - (isw ? 1 : 0), pb);
                     uint8_t* rec = Ps + ((int64_t)part * T + tt) * REC;
-                    if (isw)
+                    if (isw && a.wpos)
+                        *reinterpret_cast<int4*>(rec + (int64_t)rank * 16) = make_int4(
+                            (int)packed, __float_as_int(be[tt] * w[u]), __float_as_int(al[tt]), c + lane);
+                    else if (isw)
                         *reinterpret_cast<int4*>(rec + (int64_t)rank * 16) = make_int4(
                             (int)packed, __float_as_int(w[u]), __float_as_int(al[tt]), __float_as_int(be[tt]));
                     else
@@ -357,8 +361,11 @@ struct ScanKArgs {
 
 // SAVE (training forward): every write also stores its row as it was before
 // this token's decay (the pre-image M_{t-1}[i]) at [t][write position][col],
-// which the backward uses to undo the write. It runs with one row partition,
-// so a writer's rank in its token is the write position.
+// which the backward uses to undo the write. The per-slot form's writer
+// entries then carry beta*w (the one product the update uses, rounded as the
+// kernel would round it) and the write position in place of w and beta; the
+// shared-residual form runs with one row partition, where a writer's rank in
+// its token is the write position.
 template <int S, int FORM, bool VBF16, bool SAVE>
 __global__ __launch_bounds__(SlabCfg<S>::NWMAX * 64) void scan_kernel(ScanKArgs a) {
     constexpr int L = S / 4, G = 64 / L;
@@ -453,8 +460,12 @@ __global__ __launch_bounds__(SlabCfg<S>::NWMAX * 64) void scan_kernel(ScanKArgs 
     auto write_token = [&](int t, int slot, int4 e, float4 pre, V4 vt) {
         const uint32_t pk = (uint32_t)e.x;
         const float w = __int_as_float(e.y), al = __int_as_float(e.z), be = __int_as_float(e.w);
+        constexpr bool WPOS = SAVE && FORM == 0;  // entry = (packed, beta*w, alpha, write position)
         const float4 old = source(slot, pk, pre);
-        if constexpr (SAVE) st_f4(old, Rs, (pk & ENT_INVALID) ? OOB : s_lane, (uint32_t)t * sstride);
+        if constexpr (SAVE) {
+            const uint32_t so = WPOS ? __umul24((uint32_t)e.w, dv4) + col4 : s_lane;
+            st_f4(old, Rs, (pk & ENT_INVALID) ? OOB : so, (uint32_t)t * sstride);
+        }
         const float4 mt = f4_scale(al, old);
         float4 pred = mt;
         if constexpr (FORM == 1) {
@@ -466,7 +477,7 @@ __global__ __launch_bounds__(SlabCfg<S>::NWMAX * 64) void scan_kernel(ScanKArgs 
             for (int q = 1; q < NWMAX; ++q)
                 if (q < NWW) pred = f4_add(pred, vbuf[q * L + cc]);
         }
-        const float4 nv = f4_fma(be * w, f4_sub(VL::f(vt), pred), mt);
+        const float4 nv = f4_fma(WPOS ? w : be * w, f4_sub(VL::f(vt), pred), mt);
         st_f4(nv, Rm, row_off(pk), 0u);
         ring_at(slot, pos) = nv;
         __syncthreads();
@@ -757,6 +768,7 @@ hipError_t launch_scan_slab(const ScanArgs& a, const Cfg& c, hipStream_t st) {
         p.Tc = Tn; p.TS = a.T; p.N = a.N;
         p.D = D; p.G = g.G; p.NWW = g.NWW; p.NWR = g.NWR; p.TT = TT; p.pb = pb; p.P = c.P; p.pshift = psh;
         p.ntile = (Tn + TT - 1) / TT;
+        p.wpos = save && a.form == 0;
         hipLaunchKernelGGL(plan_kernel, dim3((unsigned)(p.ntile * a.NS)), dim3(PLAN_THREADS), bm_bytes, st, p);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -886,11 +898,9 @@ int pick_slab(int64_t NS, int W, int R, int dv, int forced) {
 // more than the extra padding lanes of a partitioned record. The shared-residual
 // form (FIG2) couples all rows of a token and keeps P = 1.
 // SDM_SCAN_SLAB and SDM_SCAN_PARTS force a width and a partition count.
-// The training forward (snapshots) keeps P = 1 for both forms, so that a
-// writer's rank is its write position.
-Cfg choose_cfg(int64_t NS, int W, int R, int dv, int form, bool save = false) {
+Cfg choose_cfg(int64_t NS, int W, int R, int dv, int form) {
     Cfg c;
-    const int fs = env_int("SDM_SCAN_SLAB"), fp = save ? 1 : env_int("SDM_SCAN_PARTS");
+    const int fs = env_int("SDM_SCAN_SLAB"), fp = env_int("SDM_SCAN_PARTS");
     if (form == 0 && (fs == 0 || fs == 32) && slab_fits(32, W, R, dv) && fp != 1) {
         c.S = 32;
     } else {
@@ -949,7 +959,7 @@ hipError_t launch_scan(const ScanArgs& a, hipStream_t st) {
             default: break;
         }
     }
-    const Cfg c = choose_cfg(a.NS, a.W, a.R, a.dv, a.form, a.snap != nullptr);
+    const Cfg c = choose_cfg(a.NS, a.W, a.R, a.dv, a.form);
     switch (c.S) {
         case 32: return launch_scan_slab<32>(a, c, st);
         case 16: return launch_scan_slab<16>(a, c, st);

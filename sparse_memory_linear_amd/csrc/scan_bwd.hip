@@ -33,6 +33,15 @@
 // one memory round trip. The gradients of the weights and gates are column
 // sums: each workgroup writes its slab's partial sums and a second kernel adds
 // them over the slabs in slab order (deterministic).
+//
+// Row partitions (per-slot form). The per-slot write never couples two rows,
+// so, as in the forward, the rows of a stream's table are split into P
+// partitions by a hash of the row index and each partition is walked by its
+// own workgroups: a token costs each of them the same round trip, and P times
+// as many workgroups keep P times as many rows in flight. A workgroup takes the
+// accesses of its partition and leaves the others' lanes idle (a wavefront
+// with no access of its partition in a token skips it). dv_t and the gate
+// gradients are then partial sums per partition, added in partition order.
 #include "sdm_buffer.h"
 #include "sdm_internal.h"
 
@@ -40,6 +49,13 @@ namespace sdm {
 namespace {
 
 constexpr int BWD_NWMAX = 16;   // wavefronts per workgroup (1024 threads, 128 VGPRs)
+#ifndef SDM_BWD_DEPTH
+#define SDM_BWD_DEPTH 6
+#endif
+// tokens of streamed inputs in flight per wavefront (fp32 v takes two more
+// registers per token, so its ring is shorter)
+template <bool VBF16>
+constexpr int ring_depth() { return VBF16 ? SDM_BWD_DEPTH : SDM_BWD_DEPTH - 2; }
 constexpr int HS = 512;         // LDS hash slots per token parity: R <= 256 keeps the load <= 1/2
 constexpr int HS_BITS = 9;
 
@@ -51,20 +67,27 @@ struct BwdKArgs {
     const float* alpha; const float* beta;
     const void* v; const float* snap; const float* dy;
     float* M; float* G; float* dvo;
-    float* pw; float* pr; float* pab;   // partial sums of this launch: [nslab][NS][T][W | R | 2]
+    float* pw; float* pr;               // partial sums of this launch: [nslab][NS][T][W], [nslab][NS][T][R]
+    float* pab;                         // [nslab * P][NS][T][2]
+    float* pdv;                         // P > 1: [P][NS][T][dv]
     int64_t TS, t0;                     // tokens per stream; first token of this launch
     int T, W, R;
     int64_t N;
-    int dv, nslab;
+    int dv, nslab, P, pshift;
     int64_t NS;
     int NWW, NWR;
 };
+
+__device__ __forceinline__ int row_part(uint32_t row, int pshift) {
+    return pshift == 0 ? 0 : (int)((row * 0x9E3779B1u) >> (32 - pshift));
+}
 
 template <int S, int FORM, bool VBF16>
 __global__ __launch_bounds__(BWD_NWMAX * 64) void scan_backward_kernel(BwdKArgs a) {
     constexpr int L = S / 4, G = 64 / L;
     using VL = VLoad<VBF16>;
     using V4 = typename VL::T4;
+    constexpr int DP = ring_depth<VBF16>();
     __shared__ int hkey[2][HS];                 // read rows of the token (parity t & 1), -1 = empty
     __shared__ int hpos[2][HS];                 // their read positions
     __shared__ float4 rg[BWD_NWMAX * 64];       // readers' new G segments [read position][L]
@@ -72,10 +95,15 @@ __global__ __launch_bounds__(BWD_NWMAX * 64) void scan_backward_kernel(BwdKArgs 
     __shared__ float ab[BWD_NWMAX][2];          // per writer wavefront: dalpha, dbeta partials
 
     const int NWW = a.NWW, T = a.T, dv = a.dv, W = a.W, R = a.R;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane / L, cc = lane % L;
-    const int b = blockIdx.x, xcd = b & 7, kq = b >> 3;
-    const int64_t s = (int64_t)(kq / a.nslab) * 8 + xcd;
-    const int slab = kq % a.nslab;
+    // the wavefront index through readfirstlane: the compiler then knows it is
+    // uniform, so role branches stay scalar (no per-lane descriptor loops)
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63, r = lane / L,
+              cc = lane % L;
+    // workgroups are dealt to the 8 XCDs round-robin: all slabs and partitions
+    // of a stream go to the same XCD (they share its L2)
+    const int b = blockIdx.x, xcd = b & 7, kq = b >> 3, units = a.nslab * a.P;
+    const int64_t s = (int64_t)(kq / units) * 8 + xcd;
+    const int slab = kq % a.nslab, part = (kq % units) / a.nslab;
     if (s >= a.NS) return;  // uniform over the workgroup
     const int col = slab * S + cc * 4;
     const bool writer = wave < NWW;
@@ -93,7 +121,8 @@ __global__ __launch_bounds__(BWD_NWMAX * 64) void scan_backward_kernel(BwdKArgs 
     const rsrc_t Rv = make_rsrc(static_cast<const char*>(a.v) + tok0 * dv * VL::ESZ, (int64_t)T * dv * VL::ESZ);
     const rsrc_t Rd = make_rsrc(a.dy + tok0 * dv, (int64_t)T * dv * 4);
     const rsrc_t Rs = make_rsrc(a.snap + tok0 * W * dv, (int64_t)T * W * dv * 4);
-    const rsrc_t Ro = make_rsrc(a.dvo + tok0 * dv, (int64_t)T * dv * 4);
+    const rsrc_t Ro = a.P > 1 ? make_rsrc(a.pdv + ((int64_t)part * a.NS + s) * T * dv, (int64_t)T * dv * 4)
+                              : make_rsrc(a.dvo + tok0 * dv, (int64_t)T * dv * 4);
     const uint32_t dv4 = (uint32_t)dv * 4u, col4 = (uint32_t)col * 4u;
     const uint32_t vstride = (uint32_t)dv * VL::ESZ, v_off = (uint32_t)col * VL::ESZ;
     const uint32_t sstride = (uint32_t)W * dv4;                  // pre-image bytes per token
@@ -101,53 +130,96 @@ __global__ __launch_bounds__(BWD_NWMAX * 64) void scan_backward_kernel(BwdKArgs 
     const int64_t ps = (int64_t)slab * a.NS + s;
     float* pw = a.pw + ps * T * W;
     float* pr = a.pr + ps * T * R;
-    float* pab = a.pab + ps * T * 2;
+    float* pab = a.pab + ((int64_t)(slab * a.P + part) * a.NS + s) * T * 2;
 
     for (int i = threadIdx.x; i < 2 * HS; i += blockDim.x) (&hkey[0][0])[i] = -1;
+    for (int i = threadIdx.x; i < 2 * BWD_NWMAX * L; i += blockDim.x)
+        (&xb[0][0][0])[i] = make_float4(0.f, 0.f, 0.f, 0.f);
     __syncthreads();
 
+    // the lane's access, if its row is valid and in this workgroup's partition
     auto off_of = [&](int32_t row) -> uint32_t {
-        return (row >= 0 && row < a.N) ? __umul24((uint32_t)row, dv4) + col4 : OOB;
+        return (row >= 0 && row < a.N && row_part((uint32_t)row, a.pshift) == part)
+                   ? __umul24((uint32_t)row, dv4) + col4 : OOB;
     };
-    // token T-1's inputs; writers take v and their pre-images, readers dy
-    int tl = T - 1;
-    int32_t row_n = has ? ix[(int64_t)tl * K + pos] : -1;
-    float w_n = has ? wx[(int64_t)tl * K + pos] : 0.f;
-    float al_n = alp[tl], be_n = bep[tl];
-    V4 v_n{};
-    float4 x_n;
-    if (writer) {
-        v_n = VL::load(Rv, v_off, (uint32_t)tl * vstride);
-        x_n = ld_f4(Rs, s_lane, (uint32_t)tl * sstride);
-    } else {
-        x_n = ld_f4(Rd, col4, (uint32_t)tl * dv4);
-    }
+    // partition 0 writes the (zero) weight gradients of positions whose row is out of range
+    auto owns_pos = [&](int32_t row, uint32_t off) -> bool {
+        return off != OOB || (part == 0 && has && !(row >= 0 && row < a.N));
+    };
+    // The inputs no write changes (index, weight, gates; v and the pre-image for
+    // writers, dy for readers) come DP tokens ahead, from a register ring that
+    // the unrolled loop indexes statically. A token first issues its table-row
+    // loads, then the ring refill: the memory counters complete in order, so
+    // waiting for the rows does not wait for the refill.
+    struct In {
+        int32_t row;
+        float w, al, be;
+        V4 v;
+        float4 x;
+    };
+    auto fetch = [&](int tk) -> In {
+        In d;
+        const int64_t o = (int64_t)tk * K + pos;
+        d.row = has ? ix[o] : -1;
+        d.w = has ? wx[o] : 0.f;
+        d.al = alp[tk];
+        d.be = bep[tk];
+        if (writer) {
+            d.v = VL::load(Rv, v_off, (uint32_t)tk * vstride);
+            d.x = ld_f4(Rs, s_lane, (uint32_t)tk * sstride);
+        } else {
+            d.v = V4{};
+            d.x = ld_f4(Rd, col4, (uint32_t)tk * dv4);
+        }
+        return d;
+    };
+    In ring[DP];
+#pragma unroll
+    for (int j = 0; j < DP; ++j)
+        if (T - 1 - j >= 0) ring[j] = fetch(T - 1 - j);
     int ins = -1;  // readers: the hash slot of this lane's row in the previous token's table
 
-    for (; tl >= 0; --tl) {
-        const int32_t row = row_n;
-        const uint32_t off = off_of(row);
-        const float w = off == OOB ? 0.f : w_n, al = al_n, be = be_n;
-        const V4 vt = v_n;
-        const float4 xt = x_n;
-        const int tb = tl & 1;
-        if (tl > 0) {  // uniform: the next token's inputs
-            const int64_t o = (int64_t)(tl - 1) * K + pos;
-            row_n = has ? ix[o] : -1;
-            w_n = has ? wx[o] : 0.f;
-            al_n = alp[tl - 1];
-            be_n = bep[tl - 1];
-            if (writer) {
-                v_n = VL::load(Rv, v_off, (uint32_t)(tl - 1) * vstride);
-                x_n = ld_f4(Rs, s_lane, (uint32_t)(tl - 1) * sstride);
-            } else {
-                x_n = ld_f4(Rd, col4, (uint32_t)(tl - 1) * dv4);
-            }
+    // wavefront 0: token tk's dv (per-slot form: the writers' partial sums) and
+    // gate partial sums. Called once the next token's row loads are issued, so
+    // its LDS reads overlap them; the writers overwrite xb and ab only after
+    // the next token's first barrier.
+    auto finish = [&](int tk) {
+        if constexpr (FORM == 0) {
+            float acc = 0.f;
+#pragma unroll
+            for (int q = 0; q < BWD_NWMAX; ++q)  // xb of absent wavefronts holds zeros
+                acc += reinterpret_cast<const float*>(xb[0][q])[lane < S ? lane : 0];
+            st_f1(acc, Ro, lane < S ? (uint32_t)(slab * S + lane) * 4u : OOB, (uint32_t)tk * dv4);
         }
+        const float sa = wave_sum(lane < NWW ? ab[lane][0] : 0.f), sb = wave_sum(lane < NWW ? ab[lane][1] : 0.f);
+        if (lane == 0) {
+            pab[2 * (int64_t)tk] = sa;
+            pab[2 * (int64_t)tk + 1] = sb;
+        }
+    };
+
+    for (int t0 = T - 1; t0 >= 0; t0 -= DP) {
+#pragma unroll
+    for (int j = 0; j < DP; ++j) {
+        const int tl = t0 - j;
+        if (tl < 0) break;  // uniform
+        const In cur = ring[j];
+        auto refill = [&]() {
+            if (tl - DP >= 0) ring[j] = fetch(tl - DP);  // uniform
+        };
+        const int32_t row = cur.row;
+        const uint32_t off = off_of(row);
+        const float w = off == OOB ? 0.f : cur.w, al = cur.al, be = cur.be;
+        const V4 vt = cur.v;
+        const float4 xt = cur.x;
+        const int tb = tl & 1;
+        const bool run = __ballot(off != OOB) != 0ull;  // wavefront has an access of this partition
         if (writer) {
-            float4 g = ld_f4(Rg, off, 0u);  // after the barrier that closed token tl + 1
-            const float4 m = xt;            // the pre-image M_{t-1}[i]
-            __syncthreads();                // B1: the readers' new G values are in LDS
+            float4 g = ld_f4(Rg, run ? off : OOB, 0u);  // after the barrier that closed token tl + 1
+            refill();
+            const float4 m = xt;                         // the pre-image M_{t-1}[i]
+            if (wave == 0 && tl + 1 < T) finish(tl + 1);
+            __syncthreads();                             // B1: the readers' new G values are in LDS
             if (off != OOB) {               // a row this token also reads: its G after the reads
                 int h = hslot((uint32_t)row), k;
                 while ((k = hkey[tb][h]) != -1) {
@@ -163,15 +235,21 @@ __global__ __launch_bounds__(BWD_NWMAX * 64) void scan_backward_kernel(BwdKArgs 
                 const float4 u = f4_sub(VL::f(vt), f4_scale(al, m));
                 const float part = rows_reduce<L>(f4_scale(bw, g));
                 if ((lane & 15) < L) reinterpret_cast<float*>(xb[0][wave])[4 * (lane & 15) + (lane >> 4)] = part;
-                const float gm = dot4(g, m), gu = dot4(g, u);
-                const float gur = group_sum<L>(gu);
-                if (off != OOB && cc == 0) pw[(int64_t)tl * W + pos] = be * gur;
-                const float da = wave_sum(c1 * gm), db = wave_sum(w * gu);
+                float da = 0.f, db = 0.f;
+                if (run) {  // uniform per wavefront
+                    const float gm = dot4(g, m), gu = dot4(g, u);
+                    const float gur = group_sum<L>(gu);
+                    if (owns_pos(row, off) && cc == 0) pw[(int64_t)tl * W + pos] = off == OOB ? 0.f : be * gur;
+                    da = wave_sum(c1 * gm);
+                    db = wave_sum(w * gu);
+                    st_f4(f4_scale(al * c1, g), Rg, off, 0u);
+                } else if (owns_pos(row, off) && cc == 0) {
+                    pw[(int64_t)tl * W + pos] = 0.f;
+                }
                 if (lane == 0) {
                     ab[wave][0] = da;
                     ab[wave][1] = db;
                 }
-                st_f4(f4_scale(al * c1, g), Rg, off, 0u);
             } else {
                 const float pg = rows_reduce<L>(f4_scale(w, g)), pm = rows_reduce<L>(f4_scale(w, m));
                 if ((lane & 15) < L) {
@@ -187,7 +265,8 @@ __global__ __launch_bounds__(BWD_NWMAX * 64) void scan_backward_kernel(BwdKArgs 
                 const float4 u = f4_sub(VL::f(vt), f4_scale(al, sm));
                 const float gm = dot4(g, m), gu = dot4(g, u), hm = dot4(gh, m);
                 const float gur = group_sum<L>(gu), hmr = group_sum<L>(hm);
-                if (off != OOB && cc == 0) pw[(int64_t)tl * W + pos] = be * gur - al * be * hmr;
+                if (owns_pos(row, off) && cc == 0)
+                    pw[(int64_t)tl * W + pos] = off == OOB ? 0.f : be * gur - al * be * hmr;
                 float xa = gm, xc = 0.f;
                 if (wave == 0 && r == 0) {  // the per-slab terms, once
                     xa -= be * dot4(gh, sm);
@@ -201,56 +280,54 @@ __global__ __launch_bounds__(BWD_NWMAX * 64) void scan_backward_kernel(BwdKArgs 
                 }
                 st_f4(f4_sub(f4_scale(al, g), f4_scale(al * be * w, gh)), Rg, off, 0u);
             }
-            st_f4(m, Rm, off, 0u);  // the undo
-            __syncthreads();        // B2
-            if (wave == 0) {
-                if constexpr (FORM == 0) {
-                    if (lane < S) {
-                        float acc = 0.f;
-                        for (int q = 0; q < NWW; ++q) acc += reinterpret_cast<const float*>(xb[0][q])[lane];
-                        st_f1(acc, Ro, (uint32_t)(slab * S + lane) * 4u, (uint32_t)tl * dv4);
-                    }
-                }
-                if (lane == 0) {
-                    float sa = 0.f, sb = 0.f;
-                    for (int q = 0; q < NWW; ++q) {
-                        sa += ab[q][0];
-                        sb += ab[q][1];
-                    }
-                    pab[2 * (int64_t)tl] = sa;
-                    pab[2 * (int64_t)tl + 1] = sb;
-                }
-            }
+            if (run) st_f4(m, Rm, off, 0u);  // the undo
+            __syncthreads();                 // B2
         } else {
-            const float4 m = ld_f4(Rm, off, 0u);  // M_t: rows of later tokens are already undone
-            const float4 g = ld_f4(Rg, off, 0u);
             if (ins >= 0) hkey[tb ^ 1][ins] = -1;  // the previous token's writers are done with it
             ins = -1;
-            const float dr = group_sum<L>(dot4(xt, m));
-            const float4 gn = f4_fma(w, xt, g);
-            st_f4(gn, Rg, off, 0u);
-            rg[pos * L + cc] = gn;
-            if (off != OOB && cc == 0) {
-                pr[(int64_t)tl * R + pos] = dr;
-                int h = hslot((uint32_t)row);
-                while (atomicCAS(&hkey[tb][h], -1, row) != -1) h = (h + 1) & (HS - 1);
-                hpos[tb][h] = pos;
-                ins = h;
+            float4 m = make_float4(0.f, 0.f, 0.f, 0.f), g = m;
+            if (run) {  // uniform per wavefront
+                m = ld_f4(Rm, off, 0u);  // M_t: rows of later tokens are already undone
+                g = ld_f4(Rg, off, 0u);
+            }
+            refill();
+            if (run) {
+                if (off != OOB && cc == 0) {  // publish the row while the loads are in flight
+                    int h = hslot((uint32_t)row);
+                    while (atomicCAS(&hkey[tb][h], -1, row) != -1) h = (h + 1) & (HS - 1);
+                    hpos[tb][h] = pos;
+                    ins = h;
+                }
+                const float dr = group_sum<L>(dot4(xt, m));
+                const float4 gn = f4_fma(w, xt, g);
+                st_f4(gn, Rg, off, 0u);
+                rg[pos * L + cc] = gn;
+                if (owns_pos(row, off) && cc == 0) pr[(int64_t)tl * R + pos] = off == OOB ? 0.f : dr;
+            } else if (owns_pos(row, off) && cc == 0) {
+                pr[(int64_t)tl * R + pos] = 0.f;
             }
             __syncthreads();                           // B1
             if constexpr (FORM == 1) __syncthreads();  // BX
             __syncthreads();                           // B2
         }
     }
+    }
+    if (wave == 0) finish(0);  // writers' last partial sums are complete since the last B2
 }
 
 // dwt_w, dwt_r, dalpha, dbeta of one launch: the slabs' partial sums added in
 // slab order.
+// With P > 1 row partitions, the gate gradients also add the partitions'
+// partial sums (slab-major, then partition) and dv_t those of the partitions.
 __global__ __launch_bounds__(256) void bwd_partials_reduce(const float* __restrict__ pw, const float* __restrict__ pr,
-                                                           const float* __restrict__ pab, int nslab, int64_t NS,
-                                                           int64_t T, int W, int R, int64_t TS, int64_t t0,
-                                                           float* dwt_w, float* dwt_r, float* dalpha, float* dbeta) {
-    const int64_t nw = NS * T * W, nr = NS * T * R, na = NS * T * 2, n = nw + nr + na;
+                                                           const float* __restrict__ pab,
+                                                           const float* __restrict__ pdv, int nslab, int P,
+                                                           int64_t NS, int64_t T, int W, int R, int dv, int64_t TS,
+                                                           int64_t t0, float* dwt_w, float* dwt_r, float* dalpha,
+                                                           float* dbeta, float* dv_out) {
+    const int64_t nw = NS * T * W, nr = NS * T * R, na = NS * T * 2, nd = P > 1 ? NS * T * dv : 0;
+    const int64_t n = nw + nr + na + nd;
+    const int nab = nslab * P;
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
         if (i < nw) {
             float acc = pw[i];
@@ -263,12 +340,18 @@ __global__ __launch_bounds__(256) void bwd_partials_reduce(const float* __restri
             for (int k = 1; k < nslab; ++k) acc += pr[k * nr + j];
             const int64_t st = j / (T * R), rem = j - st * T * R;
             dwt_r[(st * TS + t0) * R + rem] = acc;
-        } else {
+        } else if (i < nw + nr + na) {
             const int64_t j = i - nw - nr;
             float acc = pab[j];
-            for (int k = 1; k < nslab; ++k) acc += pab[k * na + j];
+            for (int k = 1; k < nab; ++k) acc += pab[k * na + j];
             const int64_t st = j / (T * 2), rem = j - st * T * 2;
             (rem & 1 ? dbeta : dalpha)[st * TS + t0 + rem / 2] = acc;
+        } else {
+            const int64_t j = i - nw - nr - na;
+            float acc = pdv[j];
+            for (int q = 1; q < P; ++q) acc += pdv[q * nd + j];
+            const int64_t st = j / (T * dv), rem = j - st * T * dv;
+            dv_out[(st * TS + t0) * dv + rem] = acc;
         }
     }
 }
@@ -290,22 +373,48 @@ bool bwd_fits(int S, int W, int R, int dv) {
     return g.NWW + g.NWR <= BWD_NWMAX;
 }
 
-// Slab width: the widest that still gives 256 workgroups (one per CU), else
-// the one with the most workgroups; SDM_BWD_SLAB forces one.
-int bwd_slab(int64_t NS, int W, int R, int dv) {
-    const char* e = getenv("SDM_BWD_SLAB");
-    const int forced = e ? atoi(e) : 0;
-    int best = 0;
-    int64_t best_units = 0;
-    for (int S : {32, 16, 8, 4}) {
-        if ((forced && forced != S) || !bwd_fits(S, W, R, dv)) continue;
-        const int64_t units = NS * (dv / S);
-        if (best == 0 || (best_units < 256 && units > best_units)) {
-            best = S;
-            best_units = units;
+int env_int(const char* name) {
+    const char* e = getenv(name);
+    return e ? atoi(e) : 0;
+}
+
+constexpr int BWD_MAX_PARTS = 16;
+
+// Slab width and row partitions. The per-slot form takes whole 128-byte lines
+// (32-column slabs) and the smallest power-of-two P (<= 16) that gives 256
+// workgroups (one per CU: a second workgroup on a CU stretches every token of
+// both, measured); the shared-residual form, which cannot split rows,
+// takes the widest slab that still gives 256 workgroups, else the one with the
+// most. SDM_BWD_SLAB and SDM_BWD_PARTS force a choice.
+struct BCfg {
+    int S = 0, P = 1;
+};
+BCfg bwd_cfg(int64_t NS, int W, int R, int dv, int form) {
+    BCfg c;
+    const int fs = env_int("SDM_BWD_SLAB"), fp = env_int("SDM_BWD_PARTS");
+    if (form == 0 && (fs == 0 || fs == 32) && fp != 1 && bwd_fits(32, W, R, dv)) {
+        c.S = 32;
+    } else {
+        int64_t best_units = 0;
+        for (int S : {32, 16, 8, 4}) {
+            if ((fs && fs != S) || !bwd_fits(S, W, R, dv)) continue;
+            const int64_t units = NS * (dv / S);
+            if (c.S == 0 || (best_units < 256 && units > best_units)) {
+                c.S = S;
+                best_units = units;
+            }
+        }
+        if (c.S == 0) return c;
+    }
+    if (form == 0) {
+        if (fp == 1 || fp == 2 || fp == 4 || fp == 8 || fp == 16) {
+            c.P = fp;
+        } else {
+            const int64_t units = (NS > 0 ? NS : 1) * (dv / c.S);
+            while (c.P < BWD_MAX_PARTS && units * c.P < 256) c.P *= 2;
         }
     }
-    return best;
+    return c;
 }
 
 int64_t bwd_chunk_tokens(int64_t T, int W, int dv) {
@@ -314,13 +423,22 @@ int64_t bwd_chunk_tokens(int64_t T, int W, int dv) {
     return T < cap ? T : cap;
 }
 
+// Workspace of one launch of Tn tokens: pw, pr, pab, then (P > 1) pdv.
+int64_t bwd_ws_floats(const BCfg& c, int64_t NS, int64_t Tn, int W, int R, int dv) {
+    const int nslab = dv / c.S;
+    return (int64_t)nslab * NS * Tn * (W + R) + (int64_t)nslab * c.P * NS * Tn * 2 +
+           (c.P > 1 ? (int64_t)c.P * NS * Tn * dv : 0);
+}
+
 template <int S>
-hipError_t launch_bwd_slab(const BwdArgs& a, hipStream_t st) {
+hipError_t launch_bwd_slab(const BwdArgs& a, const BCfg& c, hipStream_t st) {
     const BGeom g = bwd_geom(S, a.W, a.R);
     const int nslab = a.dv / S;
     const int64_t Tc = bwd_chunk_tokens(a.T, a.W, a.dv);
     float* pw = static_cast<float*>(a.workspace);
-    const int64_t nblk = ((a.NS + 7) / 8) * 8 * nslab;
+    int psh = 0;
+    while ((1 << psh) < c.P) ++psh;
+    const int64_t nblk = ((a.NS + 7) / 8) * 8 * nslab * c.P;
     const int esz = a.v_bf16 ? 2 : 4;
     const int64_t nchunk = (a.T + Tc - 1) / Tc;
     for (int64_t ci = nchunk - 1; ci >= 0; --ci) {  // the chunks in reverse
@@ -333,8 +451,10 @@ hipError_t launch_bwd_slab(const BwdArgs& a, hipStream_t st) {
         k.pw = pw;
         k.pr = pw + nslab * a.NS * Tn * a.W;
         k.pab = k.pr + nslab * a.NS * Tn * a.R;
+        k.pdv = k.pab + (int64_t)nslab * c.P * a.NS * Tn * 2;
         k.TS = a.T; k.t0 = c0; k.T = (int)Tn; k.W = a.W; k.R = a.R;
-        k.N = a.N; k.dv = a.dv; k.nslab = nslab; k.NS = a.NS; k.NWW = g.NWW; k.NWR = g.NWR;
+        k.N = a.N; k.dv = a.dv; k.nslab = nslab; k.P = c.P; k.pshift = psh;
+        k.NS = a.NS; k.NWW = g.NWW; k.NWR = g.NWR;
         (void)esz;
         dim3 grid((unsigned)nblk), block((unsigned)((g.NWW + g.NWR) * 64));
         const int sel = (a.form ? 2 : 0) | (a.v_bf16 ? 1 : 0);
@@ -346,10 +466,11 @@ hipError_t launch_bwd_slab(const BwdArgs& a, hipStream_t st) {
         }
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        const int64_t n = a.NS * Tn * (a.W + a.R + 2);
-        const int64_t nb = (n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096;
-        hipLaunchKernelGGL(bwd_partials_reduce, dim3((unsigned)nb), dim3(256), 0, st, k.pw, k.pr, k.pab, nslab,
-                           a.NS, Tn, a.W, a.R, a.T, c0, a.dwt_w, a.dwt_r, a.dalpha, a.dbeta);
+        const int64_t n = a.NS * Tn * (a.W + a.R + 2 + (c.P > 1 ? a.dv : 0));
+        const int64_t nb = (n + 255) / 256 < 8192 ? (n + 255) / 256 : 8192;
+        hipLaunchKernelGGL(bwd_partials_reduce, dim3((unsigned)nb), dim3(256), 0, st, k.pw, k.pr, k.pab, k.pdv,
+                           nslab, c.P, a.NS, Tn, a.W, a.R, a.dv, a.T, c0, a.dwt_w, a.dwt_r, a.dalpha, a.dbeta,
+                           a.dv_out);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -358,20 +479,28 @@ hipError_t launch_bwd_slab(const BwdArgs& a, hipStream_t st) {
 
 }  // namespace
 
-bool scan_backward_geometry(int64_t NS, int W, int R, int dv) { return bwd_slab(NS, W, R, dv) != 0; }
+bool scan_backward_geometry(int64_t NS, int W, int R, int dv) {
+    return bwd_cfg(NS, W, R, dv, 0).S != 0 && bwd_cfg(NS, W, R, dv, 1).S != 0;
+}
 
 int64_t scan_backward_workspace_bytes(int64_t NS, int64_t T, int W, int R, int dv) {
-    const int S = bwd_slab(NS, W, R, dv);
-    if (S == 0) return -1;
-    return (int64_t)(dv / S) * NS * bwd_chunk_tokens(T, W, dv) * (W + R + 2) * 4;
+    int64_t need = 0;
+    for (int form = 0; form < 2; ++form) {
+        const BCfg c = bwd_cfg(NS, W, R, dv, form);
+        if (c.S == 0) return -1;
+        const int64_t b = bwd_ws_floats(c, NS, bwd_chunk_tokens(T, W, dv), W, R, dv) * 4;
+        if (b > need) need = b;
+    }
+    return need;
 }
 
 hipError_t launch_scan_backward(const BwdArgs& a, hipStream_t st) {
-    switch (bwd_slab(a.NS, a.W, a.R, a.dv)) {
-        case 32: return launch_bwd_slab<32>(a, st);
-        case 16: return launch_bwd_slab<16>(a, st);
-        case 8: return launch_bwd_slab<8>(a, st);
-        case 4: return launch_bwd_slab<4>(a, st);
+    const BCfg c = bwd_cfg(a.NS, a.W, a.R, a.dv, a.form);
+    switch (c.S) {
+        case 32: return launch_bwd_slab<32>(a, c, st);
+        case 16: return launch_bwd_slab<16>(a, c, st);
+        case 8: return launch_bwd_slab<8>(a, c, st);
+        case 4: return launch_bwd_slab<4>(a, c, st);
         default: return hipErrorInvalidValue;
     }
 }

@@ -117,25 +117,36 @@ def test_backward_hazard_stress(case, form, oform):
     assert np.array_equal(M_back.view(np.uint32), c["M_in"].view(np.uint32))
 
 
-@pytest.mark.parametrize("slab", [32, 16, 8, 4])
-@pytest.mark.parametrize("form,oform", FORMS, ids=["eq4", "fig2"])
-def test_backward_slab_widths(slab, form, oform, monkeypatch):
+BWD_SWEEP = [("eq4", 32, 1), ("eq4", 32, 2), ("eq4", 32, 4), ("eq4", 32, 16), ("eq4", 16, 8), ("eq4", 8, 2),
+             ("eq4", 4, 1), ("fig2", 32, 1), ("fig2", 16, 1), ("fig2", 8, 1), ("fig2", 4, 1)]
+
+
+@pytest.mark.parametrize("form,slab,parts", BWD_SWEEP, ids=[f"{f}-S{s}P{p}" for f, s, p in BWD_SWEEP])
+def test_backward_slabs_and_row_partitions(form, slab, parts, monkeypatch):
     monkeypatch.setenv("SDM_BWD_SLAB", str(slab))
+    monkeypatch.setenv("SDM_BWD_PARTS", str(parts))
+    oform = oracle.EQ4 if form == "eq4" else oracle.FIG2
     case = dict(B=1, H=2, T=250, N=4096, dv=128, W=64, R=64, bf16=True)
-    say(f"[backward slab {slab}] form={form}")
+    say(f"[backward S={slab} P={parts}] form={form}")
     c = _random_case(4, **case)
     dy, dM = _cotangents(5, 1, 2, 250, 4096, 128)
     ref = oracle.scan_backward(**c, dy=dy, dM_out=dM, form=oform)
     _, _, _, got, M_back = _gpu_train(c, dy, dM, form)
-    _check_grads(f"S{slab}", got, ref, TOL_F32)
+    _check_grads(f"S{slab}P{parts}", got, ref, TOL_F32)
     assert np.array_equal(M_back.view(np.uint32), c["M_in"].view(np.uint32))
 
 
-@pytest.mark.parametrize("form,oform", FORMS, ids=["eq4", "fig2"])
-def test_forward_save_table_and_pre_images(form, oform):
+SAVE_CFG = [("eq4", 0), ("eq4", 1), ("eq4", 2), ("fig2", 0)]
+
+
+@pytest.mark.parametrize("form,parts", SAVE_CFG, ids=[f"{f}-P{p or 'auto'}" for f, p in SAVE_CFG])
+def test_forward_save_table_and_pre_images(form, parts, monkeypatch):
     """The training forward's table equals sdm_scan_forward's bit for bit, its
     y agrees to rounding, and every stored row is the oracle's table row before
-    that token's write."""
+    that token's write (row partitions: the default 8, forced 1 and 2)."""
+    if parts:
+        monkeypatch.setenv("SDM_SCAN_PARTS", str(parts))
+    oform = oracle.EQ4 if form == "eq4" else oracle.FIG2
     c = _random_case(6, B=1, H=2, T=48, N=128, dv=32, W=16, R=8)
     a = {k: _t(v) for k, v in c.items()}
     args = (a["idx_w"], a["wt_w"], a["idx_r"], a["wt_r"], a["alpha"], a["beta"], a["v"])
