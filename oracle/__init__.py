@@ -45,13 +45,14 @@ def _load():
         lib = ctypes.CDLL(LIB_PATH)
         P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
         lib.oracle_half_scores.argtypes = [P, P, I64, I64, I64, I64, I64, P, I]
+        lib.oracle_half_scores_idw.argtypes = [P, P, I64, I64, I64, I64, I64, P, I]
         lib.oracle_select.argtypes = [P, I64, I64, I64, I64, I64, P, P, P, P, I]
         lib.oracle_scan.argtypes = [P, P, I64, P, P, I64, P, P, P, P, P,
                                     I64, I64, I64, I64, I64, I, I]
         lib.oracle_scan_backward.argtypes = [P, P, I64, P, P, I64, P, P, P, P, P, P,
                                              P, P, P, P, P, P, I64, I64, I64, I64, I64, I, I]
-        for f in (lib.oracle_half_scores, lib.oracle_select, lib.oracle_scan,
-                  lib.oracle_scan_backward):
+        for f in (lib.oracle_half_scores, lib.oracle_half_scores_idw, lib.oracle_select,
+                  lib.oracle_scan, lib.oracle_scan_backward):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -90,15 +91,24 @@ def default_threads() -> int:
     return max(1, min(16, os.cpu_count() or 1))
 
 
-def half_scores(q, subkeys, nthreads: Optional[int] = None) -> np.ndarray:
-    """A1: q [B,H,T,2,dh], subkeys [H,2,n,dh] -> half-scores [B,H,T,2,n] fp32."""
+SCORINGS = ("dot", "idw")
+
+
+def half_scores(q, subkeys, nthreads: Optional[int] = None, scoring: str = "dot") -> np.ndarray:
+    """A1: q [B,H,T,2,dh], subkeys [H,2,n,dh] -> half-scores [B,H,T,2,n] fp32.
+
+    scoring "dot": <q_j, K_j[a]> (SDM notes §2.3); "idw": -log(1e-3 + ||q_j - K_j[a]||^2)
+    (FwPKM notes §2.2, inverse-distance weighting).
+    """
+    if scoring not in SCORINGS:
+        raise ValueError(f"unknown scoring {scoring!r}")
     q = _f32(q); K = _f32(subkeys)
     B, H, T, two, dh = q.shape
     assert two == 2 and K.shape[0] == H and K.shape[1] == 2 and K.shape[3] == dh
     n = K.shape[2]
     out = np.empty((B, H, T, 2, n), np.float32)
-    _check(_load().oracle_half_scores(_p(q), _p(K), B, H, T, n, dh, _p(out),
-                                      nthreads or default_threads()), "half_scores")
+    fn = _load().oracle_half_scores if scoring == "dot" else _load().oracle_half_scores_idw
+    _check(fn(_p(q), _p(K), B, H, T, n, dh, _p(out), nthreads or default_threads()), "half_scores")
     return out
 
 
@@ -117,9 +127,9 @@ def select(half, k: int, nthreads: Optional[int] = None
     return idx, wt, sc, nxt
 
 
-def address(q, subkeys, k: int, nthreads: Optional[int] = None):
+def address(q, subkeys, k: int, nthreads: Optional[int] = None, scoring: str = "dot"):
     """A1-A4: product-key addressing of one branch. Returns (idx, wt, score, score_next)."""
-    return select(half_scores(q, subkeys, nthreads), k, nthreads)
+    return select(half_scores(q, subkeys, nthreads, scoring), k, nthreads)
 
 
 def scan(idx_w, wt_w, idx_r, wt_r, alpha, beta, v, M_in, form: int = EQ4,

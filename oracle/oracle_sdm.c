@@ -26,7 +26,7 @@
 #include <stdlib.h>
 #include <string.h>
 
-int oracle_version(void) { return 2; }
+int oracle_version(void) { return 3; }
 
 /* ------------------------------------------------------------------ */
 /* a tiny "run f(i) for i in [0, count) on nthreads threads" helper.   */
@@ -93,6 +93,41 @@ int oracle_half_scores(const float* q, const float* subkeys, int64_t B, int64_t 
     if (B < 0 || H < 0 || T < 0 || n < 1 || dh < 1) return -2;
     hs_ctx c = {q, subkeys, H, T, n, dh, out};
     parallel_for(hs_item, &c, B * H * T, nthreads);
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* A1, inverse-distance variant [FwPKM §2.2]: the default FwPKM score of */
+/* a subkey is s = -log(1e-3 + ||q - K_a||^2), so a near subkey scores   */
+/* high; the selection that follows is the same outer sum and top-k.    */
+/* The squared distance is summed in double over the componentwise      */
+/* differences (no expansion into norms and a dot product).             */
+/* ------------------------------------------------------------------ */
+#define ORACLE_IDW_EPS 1e-3   /* the constant FwPKM §2.2 adds to the squared distance */
+
+static void hs_idw_item(void* p, int64_t bht) {
+    hs_ctx* c = (hs_ctx*)p;
+    int64_t h = (bht / c->T) % c->H;
+    for (int j = 0; j < 2; ++j) {
+        const float* qj = c->q + (bht * 2 + j) * c->dh;
+        for (int64_t a = 0; a < c->n; ++a) {
+            const float* ka = c->K + ((h * 2 + j) * c->n + a) * c->dh;
+            double d2 = 0.0;
+            for (int64_t i = 0; i < c->dh; ++i) {
+                double d = (double)qj[i] - (double)ka[i];
+                d2 += d * d;
+            }
+            c->out[(bht * 2 + j) * c->n + a] = (float)(-log(ORACLE_IDW_EPS + d2));
+        }
+    }
+}
+
+int oracle_half_scores_idw(const float* q, const float* subkeys, int64_t B, int64_t H,
+                           int64_t T, int64_t n, int64_t dh, float* out, int nthreads) {
+    if (!q || !subkeys || !out) return -1;
+    if (B < 0 || H < 0 || T < 0 || n < 1 || dh < 1) return -2;
+    hs_ctx c = {q, subkeys, H, T, n, dh, out};
+    parallel_for(hs_idw_item, &c, B * H * T, nthreads);
     return 0;
 }
 

@@ -12,7 +12,8 @@
  *           §2.4 Eq. (3)-(5) write / read, §2.5 Fig. 2 shared-residual form
  *           and the worked counter-example, §2.1 Eq. (2) gated delta rule.
  *   [FwPKM] "Fast-weight Product Key Memory：中文精读笔记", §2.2
- *           (per-half top-k, k^2 candidates, softmax over the selection).
+ *           (per-half top-k, k^2 candidates, softmax over the selection;
+ *           the inverse-distance subkey score).
  *
  * Conventions: all arrays are host memory, row-major and contiguous, fp32 for
  * every floating-point tensor (bf16 inputs are widened exactly by the
@@ -20,7 +21,7 @@
  * fp32. Functions return 0 on success and a negative code on invalid
  * arguments (nothing is written then).
  *
- * Every function has a pin in tests/test_oracle_pins.py; none is unpinned.
+ * Every function has pins in tests/test_oracle_*pins.py; none is unpinned.
  */
 #ifndef ORACLE_SDM_H
 #define ORACLE_SDM_H
@@ -37,6 +38,12 @@ extern "C" {
  * out[..,j,a] = fp32( sum_c q[..,j,c] * K[h,j,a,c] ), summed in double in c order. */
 int oracle_half_scores(const float* q, const float* subkeys, int64_t B, int64_t H,
                        int64_t T, int64_t n, int64_t dh, float* out, int nthreads);
+
+/* A1, inverse-distance variant ([FwPKM] §2.2, FwPKM's default scoring):
+ * out[..,j,a] = fp32( -log(1e-3 + sum_c (q[..,j,c] - K[h,j,a,c])^2) ), the
+ * squared distance summed in double in c order. Same shapes as above. */
+int oracle_half_scores_idw(const float* q, const float* subkeys, int64_t B, int64_t H,
+                           int64_t T, int64_t n, int64_t dh, float* out, int nthreads);
 
 /* A2-A4 from given half-scores half [B,H,T,2,n], for k selected slots.
  * idx/wt/score [B,H,T,k]: slots ordered by (score desc, slot asc), softmax
