@@ -38,6 +38,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default="gdn_matched")
     p.add_argument("--form", default="eq4", choices=["eq4", "fig2"])
+    p.add_argument("--scoring", default="dot", choices=["dot", "idw"],
+                   help="subkey score of the addressing: dot product, or FwPKM's inverse distance")
     p.add_argument("--cpu-seconds", type=float, default=20.0,
                    help="target CPU time of the oracle baseline sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -74,7 +76,7 @@ def measured_traffic():
     return None
 
 
-def cpu_baseline(wl, x, target_s: float):
+def cpu_baseline(wl, x, target_s: float, scoring: str = "dot"):
     """The oracle as it is (addressing of both branches + scan) on a bounded
     sample of the same workload: the first B' sequences with all H heads, or
     the first T' tokens of one sequence when a whole one already exceeds the
@@ -87,8 +89,8 @@ def cpu_baseline(wl, x, target_s: float):
     def run(nb, Tp):
         sl = lambda t: t[:nb, :, :Tp].contiguous()
         t0 = time.perf_counter()
-        iw, ww, _, _ = oracle.address(sl(x["q_w"]), x["subkeys"], wl.W, nthreads)
-        ir, wr, _, _ = oracle.address(sl(x["q_r"]), x["subkeys"], wl.R, nthreads)
+        iw, ww, _, _ = oracle.address(sl(x["q_w"]), x["subkeys"], wl.W, nthreads, scoring)
+        ir, wr, _, _ = oracle.address(sl(x["q_r"]), x["subkeys"], wl.R, nthreads, scoring)
         oracle.scan(iw, ww, ir, wr, sl(x["alpha"]), sl(x["beta"]), sl(x["v"]),
                     oracle.broadcast_state(x["M0"].numpy(), nb), oracle.EQ4, nthreads)
         return time.perf_counter() - t0
@@ -105,11 +107,11 @@ def cpu_baseline(wl, x, target_s: float):
     ts = run(nb, Tp) if (nb, Tp) != (1, T2) else t2
     return {"value": nb * Tp / ts, "unit": "tokens/s", "cores": nthreads, "kind": "oracle",
             "sample": f"{nb} of {wl.B} sequences of {wl.name}, all {wl.H} heads, first {Tp} of "
-                      f"{wl.T} tokens (addressing of both branches + EQ4 scan), {ts:.1f} s wall",
+                      f"{wl.T} tokens ({scoring} addressing of both branches + EQ4 scan), {ts:.1f} s wall",
             "host_cpu": host_cpu()}
 
 
-def cpu_baseline_train(wl, x, dy, target_s: float):
+def cpu_baseline_train(wl, x, dy, target_s: float, scoring: str = "dot"):
     """The oracle's training step (addressing of both branches + its backward,
     which runs its forward first) on a bounded sample: the first T' tokens of
     the first sequence, all heads, T' sized from a calibration run."""
@@ -120,8 +122,8 @@ def cpu_baseline_train(wl, x, dy, target_s: float):
     def run(Tp):
         sl = lambda t: t[:1, :, :Tp].contiguous()
         t0 = time.perf_counter()
-        iw, ww, _, _ = oracle.address(sl(x["q_w"]), x["subkeys"], wl.W, nthreads)
-        ir, wr, _, _ = oracle.address(sl(x["q_r"]), x["subkeys"], wl.R, nthreads)
+        iw, ww, _, _ = oracle.address(sl(x["q_w"]), x["subkeys"], wl.W, nthreads, scoring)
+        ir, wr, _, _ = oracle.address(sl(x["q_r"]), x["subkeys"], wl.R, nthreads, scoring)
         oracle.scan_backward(iw, ww, ir, wr, sl(x["alpha"]), sl(x["beta"]), sl(x["v"]),
                              oracle.broadcast_state(x["M0"].numpy(), 1), dy[:1, :, :Tp],
                              None, oracle.EQ4, nthreads)
@@ -134,7 +136,7 @@ def cpu_baseline_train(wl, x, dy, target_s: float):
     ts = run(Tp) if Tp != T2 else t2
     return {"value": Tp / ts, "unit": "tokens/s", "cores": nthreads, "kind": "oracle",
             "sample": f"1 of {wl.B} sequences of {wl.name}, all {wl.H} heads, first {Tp} of {wl.T} "
-                      f"tokens (addressing of both branches + EQ4 forward and backward), {ts:.1f} s wall",
+                      f"tokens ({scoring} addressing of both branches + EQ4 forward and backward), {ts:.1f} s wall",
             "host_cpu": host_cpu()}
 
 
@@ -168,7 +170,8 @@ def train_bench(a, wl, x, dev):
         rec(0)
         sdm.sdm_state_init(g["M0"], B, out=M)
         rec(1)
-        iw, ww, ir, wr = sdm.sdm_address(g["q_w"], g["q_r"], g["subkeys"], g["subkeys"], W, R, out=addr_out)
+        iw, ww, ir, wr = sdm.sdm_address(g["q_w"], g["q_r"], g["subkeys"], g["subkeys"], W, R, out=addr_out,
+                                         scoring=a.scoring)
         rec(2)
         args = (iw, ww, ir, wr, g["alpha"], g["beta"], g["v"])
         sdm.sdm_scan_forward_save(*args, M, a.form, y=y, snap=snap, workspace=ws_f)
@@ -203,7 +206,7 @@ def train_bench(a, wl, x, dev):
         "warmup": a.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": wl.name, "B": B, "H": H, "T": T, "N": N, "W": W, "R": R, "d_v": dv,
-                   "d_h": wl.d_h, "form": a.form, "mode": "train",
+                   "d_h": wl.d_h, "form": a.form, "scoring": a.scoring, "mode": "train",
                    "inputs": "bf16 q/v/subkeys, fp32 table/gates/gradients" if wl.bf16_inputs else "fp32"},
         "breakdown_ms": br,
         "forward_save_GBps": fwd_bytes / (br["forward_save"] * 1e-3) / 1e9,
@@ -213,7 +216,7 @@ def train_bench(a, wl, x, dev):
                      "algorithmic_bytes_per_launch": bwd_bytes},
     }
     if not a.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline_train(wl, x, dy_host.numpy(), a.cpu_seconds)
+        rec["cpu_baseline"] = cpu_baseline_train(wl, x, dy_host.numpy(), a.cpu_seconds, a.scoring)
     print(json.dumps(rec), flush=True)
 
 
@@ -243,7 +246,7 @@ def decode_bench(a, wl, x, dev):
         i = per[k]
         if marks:
             marks[0].record()
-        iw, ww, ir, wr = sdm.sdm_address(i["q_w"], i["q_r"], sub, sub, W, R, out=addr_out)
+        iw, ww, ir, wr = sdm.sdm_address(i["q_w"], i["q_r"], sub, sub, W, R, out=addr_out, scoring=a.scoring)
         if marks:
             marks[1].record()
         sdm.sdm_scan_forward(iw, ww, ir, wr, i["alpha"], i["beta"], i["v"], M, a.form, y=y, workspace=ws)
@@ -269,7 +272,8 @@ def decode_bench(a, wl, x, dev):
         "warmup": a.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": wl.name, "B": B, "H": H, "T_per_step": 1, "N": N, "W": W, "R": R, "d_v": dv,
-                   "d_h": wl.d_h, "form": a.form, "inputs": "bf16 q/v/subkeys, fp32 table/gates",
+                   "d_h": wl.d_h, "form": a.form, "scoring": a.scoring,
+                   "inputs": "bf16 q/v/subkeys, fp32 table/gates",
                    "state_GiB": B * H * N * dv * 4 / 2**30},
         "breakdown_ms": {"address": addr_ms, "scan": scan_ms},
         "slot_row_GBps": gbps,
@@ -279,7 +283,7 @@ def decode_bench(a, wl, x, dev):
                      "algorithmic_bytes_per_launch": row_bytes},
     }
     if not a.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(wl, x, a.cpu_seconds)
+        rec["cpu_baseline"] = cpu_baseline(wl, x, a.cpu_seconds, a.scoring)
     print(json.dumps(rec), flush=True)
 
 
@@ -326,7 +330,8 @@ def main():
         sdm.sdm_state_init(g["M0"], B, out=M)
         if marks:
             marks[1].record()
-        iw, ww, ir, wr = sdm.sdm_address(g["q_w"], g["q_r"], g["subkeys"], g["subkeys"], W, R, out=addr_out)
+        iw, ww, ir, wr = sdm.sdm_address(g["q_w"], g["q_r"], g["subkeys"], g["subkeys"], W, R, out=addr_out,
+                                         scoring=a.scoring)
         if marks:
             marks[2].record()
         sdm.sdm_scan_forward(iw, ww, ir, wr, g["alpha"], g["beta"], g["v"], M, a.form, y=y, workspace=ws)
@@ -363,9 +368,11 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": wl.name, "B": B, "H": H, "T": T, "N": N, "W": W, "R": R,
-                   "d_v": dv, "d_h": wl.d_h, "form": a.form,
+                   "d_v": dv, "d_h": wl.d_h, "form": a.form, "scoring": a.scoring,
                    "inputs": "bf16 q/v/subkeys, fp32 table/gates" if wl.bf16_inputs else "fp32"},
         "breakdown_ms": {"state_init": init_ms, "address": addr_ms, "scan": scan_ms},
+        # the half-score contraction of both branches: 2 halves x n_sub x d_h MACs per token-branch
+        "address_mfma_TFLOPs": 2 * B * H * T * 2 * (2 * wl.n_sub * wl.d_h) / (addr_ms * 1e-3) / 1e12,
         "scan_tokens_per_s": B * T / (scan_ms * 1e-3),
         "slot_row_GBps": scan_gbps,
         "roofline": {"bound": "hbm", "achieved": scan_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
@@ -374,7 +381,7 @@ def main():
                      "algorithmic_bytes_per_launch": row_bytes},
     }
     if not a.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(wl, x, a.cpu_seconds)
+        rec["cpu_baseline"] = cpu_baseline(wl, x, a.cpu_seconds, a.scoring)
     print(json.dumps(rec), flush=True)
 
 

@@ -32,7 +32,7 @@
 extern "C" {
 #endif
 
-#define SDM_ABI_VERSION 2
+#define SDM_ABI_VERSION 3
 
 typedef enum sdm_status {
     SDM_OK = 0,
@@ -100,6 +100,32 @@ int sdm_address(const void* q_w, const void* q_r, int q_dtype,
 int sdm_debug_half_scores(const void* q, int q_dtype, const void* subkeys, int k_dtype,
                           int64_t B, int64_t H, int64_t T, int64_t n_sub, int64_t dh,
                           float* half, void* stream);
+
+/*
+ * sdm_address_idw -- sdm_address with FwPKM's inverse-distance subkey score
+ * ([FwPKM] §2.2, FwPKM's default scoring) in place of the dot product:
+ *   half-scores  s_j[a] = -log(1e-3 + ||q[.., j, :] - subkeys[h, j, a, :]||^2)
+ * (computed as ||q||^2 + ||K_a||^2 - 2 <q, K_a>, the inner product on MFMA with
+ * fp32 accumulation). Per-half top-k, the outer sum, the selection and the
+ * softmax are those of sdm_address, so the weights of the selected slots are
+ * the normalised products 1 / ((1e-3 + d_0)(1e-3 + d_1)) of the two halves'
+ * squared distances. Arguments, layouts, errors and support as sdm_address.
+ */
+int sdm_address_idw(const void* q_w, const void* q_r, int q_dtype,
+                    const void* subkeys_w, const void* subkeys_r, int k_dtype,
+                    int64_t B, int64_t H, int64_t T, int64_t n_sub, int64_t dh,
+                    int64_t W, int64_t R,
+                    int32_t* idx_w, float* wt_w, int32_t* idx_r, float* wt_r,
+                    float* score_w, float* score_r, void* stream);
+
+/*
+ * sdm_debug_half_scores_idw -- test hook: the inverse-distance half-scores of
+ * sdm_address_idw alone (same kernel code), for one branch. Arguments as
+ * sdm_debug_half_scores.
+ */
+int sdm_debug_half_scores_idw(const void* q, int q_dtype, const void* subkeys, int k_dtype,
+                              int64_t B, int64_t H, int64_t T, int64_t n_sub, int64_t dh,
+                              float* half, void* stream);
 
 /*
  * sdm_state_init -- per-sequence initial table from the (learned) initial

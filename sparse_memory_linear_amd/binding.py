@@ -29,6 +29,9 @@ _SIGS = {
     "sdm_address": (_I, [_P, _P, _I, _P, _P, _I, _I64, _I64, _I64, _I64, _I64, _I64, _I64,
                          _P, _P, _P, _P, _P, _P, _P]),
     "sdm_debug_half_scores": (_I, [_P, _I, _P, _I, _I64, _I64, _I64, _I64, _I64, _P, _P]),
+    "sdm_address_idw": (_I, [_P, _P, _I, _P, _P, _I, _I64, _I64, _I64, _I64, _I64, _I64, _I64,
+                             _P, _P, _P, _P, _P, _P, _P]),
+    "sdm_debug_half_scores_idw": (_I, [_P, _I, _P, _I, _I64, _I64, _I64, _I64, _I64, _P, _P]),
     "sdm_state_init": (_I, [_P, _P, _I64, _I64, _I64, _I64, _P]),
     "sdm_scan_workspace_bytes": (_I64, [_I64, _I64, _I64, _I64, _I64, _I64]),
     "sdm_scan_forward": (_I, [_P, _P, _I64, _P, _P, _I64, _P, _P, _P, _I, _P, _P,
@@ -110,15 +113,22 @@ def sdm_last_error() -> str:
     return lib().sdm_last_error().decode()
 
 
+SCORINGS = ("dot", "idw")
+
+
 def sdm_address(q_w: torch.Tensor, q_r: torch.Tensor, subkeys_w: torch.Tensor,
                 subkeys_r: torch.Tensor, W: int, R: int, return_scores: bool = False,
-                out: Optional[Tuple[torch.Tensor, ...]] = None):
+                out: Optional[Tuple[torch.Tensor, ...]] = None, scoring: str = "dot"):
     """Product-key addressing of both branches.
 
     q_w, q_r [B,H,T,2,dh]; subkeys [H,2,n_sub,dh] (same dtype, fp32 or bf16).
     Returns (idx_w, wt_w, idx_r, wt_r) and, with return_scores, (score_w, score_r).
-    ``out`` may pass preallocated (idx_w, wt_w, idx_r, wt_r) tensors.
+    ``out`` may pass preallocated (idx_w, wt_w, idx_r, wt_r) tensors. ``scoring``
+    "dot" calls sdm_address, "idw" sdm_address_idw (inverse-distance half-scores).
     """
+    if scoring not in SCORINGS:
+        raise ValueError(f"unknown scoring {scoring!r}")
+    fn = "sdm_address" if scoring == "dot" else "sdm_address_idw"
     d = _dev(q_w, q_r, subkeys_w, subkeys_r)
     B, H, T, two, dh = q_w.shape
     n = subkeys_w.shape[2]
@@ -140,7 +150,7 @@ def sdm_address(q_w: torch.Tensor, q_r: torch.Tensor, subkeys_w: torch.Tensor,
         wt_r = torch.empty((B, H, T, R), dtype=torch.float32, **kw)
     sc_w = torch.empty((B, H, T, W), dtype=torch.float32, **kw) if return_scores else None
     sc_r = torch.empty((B, H, T, R), dtype=torch.float32, **kw) if return_scores else None
-    _check("sdm_address", lib().sdm_address(
+    _check(fn, getattr(lib(), fn)(
         _ptr(q_w), _ptr(q_r), _dtype_code(q_w), _ptr(subkeys_w), _ptr(subkeys_r),
         _dtype_code(subkeys_w), B, H, T, n, dh, W, R, _ptr(idx_w), _ptr(wt_w), _ptr(idx_r),
         _ptr(wt_r), _ptr(sc_w), _ptr(sc_r), _stream(d)))
@@ -148,13 +158,17 @@ def sdm_address(q_w: torch.Tensor, q_r: torch.Tensor, subkeys_w: torch.Tensor,
     return out + (sc_w, sc_r) if return_scores else out
 
 
-def sdm_debug_half_scores(q: torch.Tensor, subkeys: torch.Tensor) -> torch.Tensor:
-    """Half-scores [B,H,T,2,n_sub] fp32 of one branch (the contraction of sdm_address)."""
+def sdm_debug_half_scores(q: torch.Tensor, subkeys: torch.Tensor, scoring: str = "dot") -> torch.Tensor:
+    """Half-scores [B,H,T,2,n_sub] fp32 of one branch (the contraction of sdm_address,
+    or with scoring "idw" the inverse-distance scores of sdm_address_idw)."""
+    if scoring not in SCORINGS:
+        raise ValueError(f"unknown scoring {scoring!r}")
+    fn = "sdm_debug_half_scores" if scoring == "dot" else "sdm_debug_half_scores_idw"
     d = _dev(q, subkeys)
     B, H, T, _, dh = q.shape
     n = subkeys.shape[2]
     half = torch.empty((B, H, T, 2, n), dtype=torch.float32, device=d)
-    _check("sdm_debug_half_scores", lib().sdm_debug_half_scores(
+    _check(fn, getattr(lib(), fn)(
         _ptr(q), _dtype_code(q), _ptr(subkeys), _dtype_code(subkeys), B, H, T, n, dh,
         _ptr(half), _stream(d)))
     return half

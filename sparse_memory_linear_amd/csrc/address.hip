@@ -26,6 +26,12 @@
 //       score (a tie that the slot order could decide differently), the token
 //       is redone over the full k_h x k_h grid.
 //   a4  softmax in fp32 (max-subtracted, expf), butterfly sum.
+// Inverse-distance scores ("Fast-weight Product Key Memory：中文精读笔记" §2.2,
+// FwPKM's default): s = -log(1e-3 + ||q - K_a||^2). The squared distance is
+// ||q||^2 + ||K_a||^2 - 2 <q, K_a>, so the contraction stays on MFMA; each lane
+// also sums the squares of the q and subkey elements it loads for the MFMA, a
+// 4-lane butterfly completes the norms, and the epilogue of a1 turns the dot
+// products into scores. Everything after a1 is the same for both scorings.
 // The wavefronts share the MFMA tiles of a1; then each selects TG = 2 tokens.
 // The selection is a chain of dependent wave-wide steps, so the 2 tokens are
 // carried through it together (independent chains interleave), and every
@@ -268,7 +274,23 @@ __device__ __forceinline__ uint64_t composite(uint32_t key, uint32_t id) {
     return ((uint64_t)key << 32) | (uint64_t)(0xFFFFFFFFu - id);
 }
 
-template <bool BF16, int EH>
+// Sum of squares of the 8 bf16 (packed in a uint4) or 2 fp32 elements a lane loads.
+__device__ __forceinline__ float sumsq(const uint4& x) {
+    float s = 0.f;
+    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float lo = __uint_as_float(w[i] << 16), hi = __uint_as_float(w[i] & 0xFFFF0000u);
+        s = fmaf(lo, lo, s);
+        s = fmaf(hi, hi, s);
+    }
+    return s;
+}
+__device__ __forceinline__ float sumsq(const float2& x) { return fmaf(x.y, x.y, x.x * x.x); }
+
+constexpr float IDW_EPS = 1e-3f;  // the constant FwPKM adds to the squared distance
+
+template <bool BF16, int EH, bool IDW>
 __global__ __launch_bounds__(NWA * 64) void address_kernel(AddressArgs a) {
     extern __shared__ __align__(16) uint32_t smem[];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -313,10 +335,12 @@ __global__ __launch_bounds__(NWA * 64) void address_kernel(AddressArgs a) {
     const int64_t tq = u0 + m16;
     const bool tok_ok = tq < UT;
     f32x4_t acc[TPW];
+    float qsq[2] = {0.f, 0.f}, ksq[TPW];  // IDW: partial squared norms of what this lane loads
     int64_t krow[TPW];  // element offset of this lane's subkey row of each tile
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
         acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        ksq[i] = 0.f;
         const int tile = wave + i * NWA, j = tile / nt16, a0 = (tile % nt16) * 16;
         krow[i] = (((int64_t)h * 2 + j) * n + a0 + m16) * dh;
     }
@@ -332,6 +356,13 @@ __global__ __launch_bounds__(NWA * 64) void address_kernel(AddressArgs a) {
 #pragma unroll
             for (int i = 0; i < TPW; ++i)
                 if (wave + i * NWA < ntiles) kb[i] = *reinterpret_cast<const uint4*>(kp + krow[i] + c0 + g4 * 8);
+            if constexpr (IDW) {
+                qsq[0] += sumsq(qa[0]);
+                qsq[1] += sumsq(qa[1]);
+#pragma unroll
+                for (int i = 0; i < TPW; ++i)
+                    if (wave + i * NWA < ntiles) ksq[i] += sumsq(kb[i]);
+            }
 #pragma unroll
             for (int i = 0; i < TPW; ++i) {
                 const int tile = wave + i * NWA;
@@ -352,6 +383,13 @@ __global__ __launch_bounds__(NWA * 64) void address_kernel(AddressArgs a) {
 #pragma unroll
             for (int i = 0; i < TPW; ++i)
                 if (wave + i * NWA < ntiles) kb[i] = *reinterpret_cast<const float2*>(kp + krow[i] + c0 + g4 * 2);
+            if constexpr (IDW) {
+                qsq[0] += sumsq(qa[0]);
+                qsq[1] += sumsq(qa[1]);
+#pragma unroll
+                for (int i = 0; i < TPW; ++i)
+                    if (wave + i * NWA < ntiles) ksq[i] += sumsq(kb[i]);
+            }
 #pragma unroll
             for (int i = 0; i < TPW; ++i) {
                 const int tile = wave + i * NWA;
@@ -364,13 +402,37 @@ __global__ __launch_bounds__(NWA * 64) void address_kernel(AddressArgs a) {
         }
     }
     // D layout: lane holds tokens 4*(lane/16)+i of subkey column lane%16
+    float qn[2][4];  // IDW: ||q||^2 of the 4 tokens of this lane's D rows, per half
+    if constexpr (IDW) {
+        // lanes m16 + 16 g4 (g4 = 0..3) loaded disjoint chunks of token m16 / subkey row m16
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+            float t = qsq[jj];
+            t += xlanef<16>(t, lane);
+            t += xlanef<32>(t, lane);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) qn[jj][r] = __shfl(t, g4 * 4 + r);
+        }
+#pragma unroll
+        for (int i = 0; i < TPW; ++i) {
+            ksq[i] += xlanef<16>(ksq[i], lane);
+            ksq[i] += xlanef<32>(ksq[i], lane);
+        }
+    }
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
         const int tile = wave + i * NWA;
         if (tile < ntiles) {
             const int j = tile / nt16, a0 = (tile % nt16) * 16;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) sc_tok(g4 * 4 + r)[j * n + a0 + m16] = acc[i][r];
+            for (int r = 0; r < 4; ++r) {
+                float sc = acc[i][r];
+                if constexpr (IDW) {
+                    const float d2 = fmaf(-2.f, sc, (j ? qn[1][r] : qn[0][r]) + ksq[i]);
+                    sc = -logf(IDW_EPS + fmaxf(d2, 0.f));
+                }
+                sc_tok(g4 * 4 + r)[j * n + a0 + m16] = sc;
+            }
         }
     }
     __syncthreads();
@@ -526,7 +588,10 @@ hipError_t launch_inst(const AddressArgs& a, hipStream_t st) {
     const int64_t ntile = (a.B * a.T + TOK - 1) / TOK;
     const size_t lds = (size_t)NWA * block_floats(a.n) * 4 + EC * 64 * 4;
     dim3 grid((unsigned)(ntile * a.H), (unsigned)a.nbranch);
-    hipLaunchKernelGGL((address_kernel<BF16, EH>), grid, dim3(NWA * 64), lds, st, a);
+    if (a.idw)
+        hipLaunchKernelGGL((address_kernel<BF16, EH, true>), grid, dim3(NWA * 64), lds, st, a);
+    else
+        hipLaunchKernelGGL((address_kernel<BF16, EH, false>), grid, dim3(NWA * 64), lds, st, a);
     return hipGetLastError();
 }
 

@@ -73,10 +73,10 @@ const char* sdm_status_string(int s) {
 
 const char* sdm_last_error(void) { return g_err; }
 
-int sdm_address(const void* q_w, const void* q_r, int q_dtype, const void* subkeys_w, const void* subkeys_r,
-                int k_dtype, int64_t B, int64_t H, int64_t T, int64_t n_sub, int64_t dh, int64_t W, int64_t R,
-                int32_t* idx_w, float* wt_w, int32_t* idx_r, float* wt_r, float* score_w, float* score_r,
-                void* stream) {
+static int address_impl(const char* fn, bool idw, const void* q_w, const void* q_r, int q_dtype,
+                        const void* subkeys_w, const void* subkeys_r, int k_dtype, int64_t B, int64_t H, int64_t T,
+                        int64_t n_sub, int64_t dh, int64_t W, int64_t R, int32_t* idx_w, float* wt_w,
+                        int32_t* idx_r, float* wt_r, float* score_w, float* score_r, void* stream) {
     int rc = check_address_sizes(q_dtype, k_dtype, B, H, T, n_sub, dh);
     if (rc) return rc;
     const int64_t N = n_sub * n_sub;
@@ -87,12 +87,12 @@ int sdm_address(const void* q_w, const void* q_r, int q_dtype, const void* subke
                                       (long long)W, (long long)R);
     if (B == 0 || H == 0 || T == 0) return ok();  // empty tensors may have NULL data
     if (!q_w || !q_r || !subkeys_w || !subkeys_r || !idx_w || !wt_w || !idx_r || !wt_r)
-        return fail(SDM_ERR_NULL, "sdm_address: a required pointer is NULL");
+        return fail(SDM_ERR_NULL, "%s: a required pointer is NULL", fn);
     const void* ptrs[] = {q_w, q_r, subkeys_w, subkeys_r, idx_w, wt_w, idx_r, wt_r};
     for (const void* p : ptrs)
-        if (!aligned16(p)) return fail(SDM_ERR_ALIGN, "sdm_address: pointer %p not 16-byte aligned", p);
+        if (!aligned16(p)) return fail(SDM_ERR_ALIGN, "%s: pointer %p not 16-byte aligned", fn, p);
     if ((score_w && !aligned16(score_w)) || (score_r && !aligned16(score_r)))
-        return fail(SDM_ERR_ALIGN, "sdm_address: score pointer not 16-byte aligned");
+        return fail(SDM_ERR_ALIGN, "%s: score pointer not 16-byte aligned", fn);
     sdm::AddressArgs a{};
     a.q[0] = q_w; a.q[1] = q_r;
     a.K[0] = subkeys_w; a.K[1] = subkeys_r;
@@ -104,19 +104,20 @@ int sdm_address(const void* q_w, const void* q_r, int q_dtype, const void* subke
     a.B = B; a.H = H; a.T = T; a.n = (int)n_sub; a.dh = (int)dh;
     a.nbranch = 2;
     a.bf16 = q_dtype == SDM_BF16;
+    a.idw = idw;
     hipError_t e = sdm::launch_address(a, static_cast<hipStream_t>(stream));
-    if (e != hipSuccess) return hip_fail(e, "sdm_address launch");
+    if (e != hipSuccess) return hip_fail(e, fn);
     return ok();
 }
 
-int sdm_debug_half_scores(const void* q, int q_dtype, const void* subkeys, int k_dtype, int64_t B, int64_t H,
-                          int64_t T, int64_t n_sub, int64_t dh, float* half, void* stream) {
+static int half_scores_impl(const char* fn, bool idw, const void* q, int q_dtype, const void* subkeys, int k_dtype,
+                            int64_t B, int64_t H, int64_t T, int64_t n_sub, int64_t dh, float* half, void* stream) {
     int rc = check_address_sizes(q_dtype, k_dtype, B, H, T, n_sub, dh);
     if (rc) return rc;
     if (B == 0 || H == 0 || T == 0) return ok();
-    if (!q || !subkeys || !half) return fail(SDM_ERR_NULL, "sdm_debug_half_scores: NULL pointer");
+    if (!q || !subkeys || !half) return fail(SDM_ERR_NULL, "%s: NULL pointer", fn);
     if (!aligned16(q) || !aligned16(subkeys) || !aligned16(half))
-        return fail(SDM_ERR_ALIGN, "sdm_debug_half_scores: pointer not 16-byte aligned");
+        return fail(SDM_ERR_ALIGN, "%s: pointer not 16-byte aligned", fn);
     sdm::AddressArgs a{};
     a.q[0] = q; a.K[0] = subkeys;
     a.k[0] = 1;
@@ -124,9 +125,38 @@ int sdm_debug_half_scores(const void* q, int q_dtype, const void* subkeys, int k
     a.B = B; a.H = H; a.T = T; a.n = (int)n_sub; a.dh = (int)dh;
     a.nbranch = 1;
     a.bf16 = q_dtype == SDM_BF16;
+    a.idw = idw;
     hipError_t e = sdm::launch_address(a, static_cast<hipStream_t>(stream));
-    if (e != hipSuccess) return hip_fail(e, "sdm_debug_half_scores launch");
+    if (e != hipSuccess) return hip_fail(e, fn);
     return ok();
+}
+
+int sdm_address(const void* q_w, const void* q_r, int q_dtype, const void* subkeys_w, const void* subkeys_r,
+                int k_dtype, int64_t B, int64_t H, int64_t T, int64_t n_sub, int64_t dh, int64_t W, int64_t R,
+                int32_t* idx_w, float* wt_w, int32_t* idx_r, float* wt_r, float* score_w, float* score_r,
+                void* stream) {
+    return address_impl("sdm_address", false, q_w, q_r, q_dtype, subkeys_w, subkeys_r, k_dtype, B, H, T, n_sub, dh,
+                        W, R, idx_w, wt_w, idx_r, wt_r, score_w, score_r, stream);
+}
+
+int sdm_address_idw(const void* q_w, const void* q_r, int q_dtype, const void* subkeys_w, const void* subkeys_r,
+                    int k_dtype, int64_t B, int64_t H, int64_t T, int64_t n_sub, int64_t dh, int64_t W, int64_t R,
+                    int32_t* idx_w, float* wt_w, int32_t* idx_r, float* wt_r, float* score_w, float* score_r,
+                    void* stream) {
+    return address_impl("sdm_address_idw", true, q_w, q_r, q_dtype, subkeys_w, subkeys_r, k_dtype, B, H, T, n_sub,
+                        dh, W, R, idx_w, wt_w, idx_r, wt_r, score_w, score_r, stream);
+}
+
+int sdm_debug_half_scores(const void* q, int q_dtype, const void* subkeys, int k_dtype, int64_t B, int64_t H,
+                          int64_t T, int64_t n_sub, int64_t dh, float* half, void* stream) {
+    return half_scores_impl("sdm_debug_half_scores", false, q, q_dtype, subkeys, k_dtype, B, H, T, n_sub, dh, half,
+                            stream);
+}
+
+int sdm_debug_half_scores_idw(const void* q, int q_dtype, const void* subkeys, int k_dtype, int64_t B, int64_t H,
+                              int64_t T, int64_t n_sub, int64_t dh, float* half, void* stream) {
+    return half_scores_impl("sdm_debug_half_scores_idw", true, q, q_dtype, subkeys, k_dtype, B, H, T, n_sub, dh,
+                            half, stream);
 }
 
 int sdm_state_init(const float* M0, float* M, int64_t B, int64_t H, int64_t N, int64_t dv, void* stream) {

@@ -18,6 +18,7 @@ struct AddressArgs {
     int n, dh;
     int nbranch;             // 1 or 2
     bool bf16;
+    bool idw;                // inverse-distance half-scores instead of dot products
 };
 hipError_t launch_address(const AddressArgs& a, hipStream_t st);
 
