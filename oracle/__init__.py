@@ -49,10 +49,12 @@ def _load():
         lib.oracle_select.argtypes = [P, I64, I64, I64, I64, I64, P, P, P, P, I]
         lib.oracle_scan.argtypes = [P, P, I64, P, P, I64, P, P, P, P, P,
                                     I64, I64, I64, I64, I64, I, I]
+        lib.oracle_scan_bf16.argtypes = [P, P, I64, P, P, I64, P, P, P, P, P,
+                                         I64, I64, I64, I64, I64, I, I]
         lib.oracle_scan_backward.argtypes = [P, P, I64, P, P, I64, P, P, P, P, P, P,
                                              P, P, P, P, P, P, I64, I64, I64, I64, I64, I, I]
         for f in (lib.oracle_half_scores, lib.oracle_half_scores_idw, lib.oracle_select,
-                  lib.oracle_scan, lib.oracle_scan_backward):
+                  lib.oracle_scan, lib.oracle_scan_bf16, lib.oracle_scan_backward):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -150,6 +152,47 @@ def scan(idx_w, wt_w, idx_r, wt_r, alpha, beta, v, M_in, form: int = EQ4,
                                _p(M), _p(y), B, H, T, N, dv, form,
                                nthreads or default_threads()), "scan")
     return M, y
+
+
+def bf16_bits(x) -> np.ndarray:
+    """The raw 16-bit patterns of a bfloat16 tensor (or a uint16 array as is)."""
+    import torch
+    if isinstance(x, torch.Tensor):
+        if x.dtype != torch.bfloat16:
+            raise ValueError("expected a bfloat16 tensor")
+        return np.ascontiguousarray(x.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16))
+    x = np.asarray(x)
+    if x.dtype != np.uint16:
+        raise ValueError("expected bfloat16 bits as uint16")
+    return np.ascontiguousarray(x)
+
+
+def bits_to_bf16(bits: np.ndarray):
+    """uint16 bit patterns -> a CPU bfloat16 tensor (no rounding: the same bits)."""
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16).copy()).view(torch.bfloat16)
+
+
+def scan_bf16(idx_w, wt_w, idx_r, wt_r, alpha, beta, v, M_in, form: int = EQ4,
+              nthreads: Optional[int] = None):
+    """A5-A6 with the table stored in bfloat16 (each stored element rounded once,
+    to nearest even, from the double-precision update). M_in [B,H,N,dv] is a
+    bfloat16 tensor (or its uint16 bits) and is not modified.
+
+    Returns (M_out as a CPU bfloat16 tensor, y [B,H,T,dv] fp32).
+    """
+    iw = _i32(idx_w); ww = _f32(wt_w); ir = _i32(idx_r); wr = _f32(wt_r)
+    a = _f32(alpha); b = _f32(beta); vv = _f32(v)
+    Mb = np.array(bf16_bits(M_in), dtype=np.uint16, copy=True, order="C")
+    B, H, T, W = iw.shape
+    R = ir.shape[3]
+    N, dv = Mb.shape[2], Mb.shape[3]
+    assert Mb.shape[:2] == (B, H) and vv.shape == (B, H, T, dv)
+    y = np.empty((B, H, T, dv), np.float32)
+    _check(_load().oracle_scan_bf16(_p(iw), _p(ww), W, _p(ir), _p(wr), R, _p(a), _p(b), _p(vv),
+                                    _p(Mb), _p(y), B, H, T, N, dv, form,
+                                    nthreads or default_threads()), "scan_bf16")
+    return bits_to_bf16(Mb), y
 
 
 def scan_backward(idx_w, wt_w, idx_r, wt_r, alpha, beta, v, M_in, dy, dM_out=None,

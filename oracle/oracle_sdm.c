@@ -235,12 +235,47 @@ typedef struct {
     float *M, *y;
     int64_t T, N, dv;
     int form;
+    uint16_t* Mb;        /* non-NULL: the table is stored in bfloat16 instead of M */
 } scan_ctx;
+
+/* Round x to the nearest bfloat16 (8 significant bits, the fp32 exponent
+ * range), ties to even; returns its 16 bits. x = m 2^e with 0.5 <= |m| < 1
+ * lies where bfloat16 values are 2^(e-8) apart (below the normal range the
+ * spacing stays 2^-133). Used only for the bf16-table variant of the scan. */
+static uint16_t bf16_round(double x) {
+    int e;
+    if (x == 0.0) return signbit(x) ? 0x8000u : 0u;
+    frexp(x, &e);
+    if (e < -125) e = -125;
+    double q = ldexp(1.0, e - 8);
+    float f = (float)(nearbyint(x / q) * q);   /* exact: at most 8 significant bits */
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    return (uint16_t)(u >> 16);
+}
+
+static double bf16_value(uint16_t h) {
+    uint32_t u = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return (double)f;
+}
+
+/* element (row, col) of stream s's table, and its update (one rounding to
+   the storage type: fp32, or bfloat16 for the bf16-table variant) */
+static double tab_get(const scan_ctx* c, int64_t s, int64_t row, int64_t col) {
+    int64_t o = (s * c->N + row) * c->dv + col;
+    return c->Mb ? bf16_value(c->Mb[o]) : (double)c->M[o];
+}
+static void tab_put(scan_ctx* c, int64_t s, int64_t row, int64_t col, double x) {
+    int64_t o = (s * c->N + row) * c->dv + col;
+    if (c->Mb) c->Mb[o] = bf16_round(x);
+    else c->M[o] = (float)x;
+}
 
 static void scan_item(void* p, int64_t s) {      /* s = b*H + h: one sequence-head */
     scan_ctx* c = (scan_ctx*)p;
     int64_t W = c->W, R = c->R, dv = c->dv;
-    float* Ms = c->M + s * c->N * dv;
     double* vhat = (double*)malloc((size_t)dv * sizeof(double));
     for (int64_t t = 0; t < c->T; ++t) {
         int64_t st = s * c->T + t;
@@ -255,21 +290,18 @@ static void scan_item(void* p, int64_t s) {      /* s = b*H + h: one sequence-he
             /* shared prediction from the decayed pre-token rows:
                vhat = sum_j k^(j) * alpha * M[j] */
             for (int64_t col = 0; col < dv; ++col) vhat[col] = 0.0;
-            for (int64_t j = 0; j < W; ++j) {
-                const float* row = Ms + (int64_t)iw[j] * dv;
+            for (int64_t j = 0; j < W; ++j)
                 for (int64_t col = 0; col < dv; ++col)
-                    vhat[col] += (double)ww[j] * (a * (double)row[col]);
-            }
+                    vhat[col] += (double)ww[j] * (a * tab_get(c, s, iw[j], col));
         }
         /* Eq. (3): decay the selected rows; Eq. (4) or Fig. 2: delta-correct them.
            Unselected rows are not touched at all. */
         for (int64_t j = 0; j < W; ++j) {
-            float* row = Ms + (int64_t)iw[j] * dv;
             double kw = (double)ww[j];
             for (int64_t col = 0; col < dv; ++col) {
-                double mt = a * (double)row[col];
+                double mt = a * tab_get(c, s, iw[j], col);
                 double pred = (c->form == ORACLE_FIG2) ? vhat[col] : mt;
-                row[col] = (float)(mt + b * kw * ((double)vt[col] - pred));
+                tab_put(c, s, iw[j], col, mt + b * kw * ((double)vt[col] - pred));
             }
         }
         /* Eq. (5): weighted read of the R selected rows of the updated table */
@@ -277,7 +309,7 @@ static void scan_item(void* p, int64_t s) {      /* s = b*H + h: one sequence-he
         for (int64_t col = 0; col < dv; ++col) {
             double acc = 0.0;
             for (int64_t j = 0; j < R; ++j)
-                acc += (double)wr[j] * (double)Ms[(int64_t)ir[j] * dv + col];
+                acc += (double)wr[j] * tab_get(c, s, ir[j], col);
             yt[col] = (float)acc;
         }
     }
@@ -314,7 +346,22 @@ int oracle_scan(const int32_t* idx_w, const float* wt_w, int64_t W,
     if (form != ORACLE_EQ4 && form != ORACLE_FIG2) return -2;
     int rc = check_indices(idx_w, W, idx_r, R, B * H * T, N);
     if (rc) return rc;
-    scan_ctx c = {idx_w, wt_w, W, idx_r, wt_r, R, alpha, beta, v, M, y, T, N, dv, form};
+    scan_ctx c = {idx_w, wt_w, W, idx_r, wt_r, R, alpha, beta, v, M, y, T, N, dv, form, NULL};
+    parallel_for(scan_item, &c, B * H, nthreads);
+    return 0;
+}
+
+int oracle_scan_bf16(const int32_t* idx_w, const float* wt_w, int64_t W,
+                     const int32_t* idx_r, const float* wt_r, int64_t R,
+                     const float* alpha, const float* beta, const float* v,
+                     uint16_t* Mb, float* y, int64_t B, int64_t H, int64_t T, int64_t N,
+                     int64_t dv, int form, int nthreads) {
+    if (!idx_w || !wt_w || !idx_r || !wt_r || !alpha || !beta || !v || !Mb || !y) return -1;
+    if (B < 0 || H < 0 || T < 0 || N < 1 || dv < 1 || W < 1 || R < 1 || W > N || R > N) return -2;
+    if (form != ORACLE_EQ4 && form != ORACLE_FIG2) return -2;
+    int rc = check_indices(idx_w, W, idx_r, R, B * H * T, N);
+    if (rc) return rc;
+    scan_ctx c = {idx_w, wt_w, W, idx_r, wt_r, R, alpha, beta, v, NULL, y, T, N, dv, form, Mb};
     parallel_for(scan_item, &c, B * H, nthreads);
     return 0;
 }

@@ -64,6 +64,18 @@ int oracle_scan(const int32_t* idx_w, const float* wt_w, int64_t W,
                 float* M, float* y, int64_t B, int64_t H, int64_t T, int64_t N,
                 int64_t dv, int form, int nthreads);
 
+/* A5-A6 with the table stored in bfloat16 (a storage variant: the pages'
+ * per-layer state size implies 2-byte elements, [SDM] §4.5 Table 3 with the
+ * element count of §2.8). Same recurrence, in double, as oracle_scan; every
+ * stored table element is rounded once to the nearest bfloat16 (ties to even)
+ * instead of to fp32; reads widen the stored bits exactly. Mb [B,H,N,dv]
+ * holds the bfloat16 bits (in/out); y [B,H,T,dv] is fp32. Same return codes. */
+int oracle_scan_bf16(const int32_t* idx_w, const float* wt_w, int64_t W,
+                     const int32_t* idx_r, const float* wt_r, int64_t R,
+                     const float* alpha, const float* beta, const float* v,
+                     uint16_t* Mb, float* y, int64_t B, int64_t H, int64_t T, int64_t N,
+                     int64_t dv, int form, int nthreads);
+
 /* Backward of A5-A6 by reverse-mode differentiation of the whole scan, the
  * tokens walked in reverse with each written row restored from its pre-image
  * ([SDM] §2.9 Appendix A, backward memory). Same index/weight/gate/v inputs as
