@@ -38,6 +38,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default="gdn_matched")
     p.add_argument("--form", default="eq4", choices=["eq4", "fig2"])
+    p.add_argument("--table", default="f32", choices=["f32", "bf16"],
+                   help="element type of the state table (bf16 halves every row access)")
     p.add_argument("--scoring", default="dot", choices=["dot", "idw"],
                    help="subkey score of the addressing: dot product, or FwPKM's inverse distance")
     p.add_argument("--cpu-seconds", type=float, default=20.0,
@@ -76,7 +78,7 @@ def measured_traffic():
     return None
 
 
-def cpu_baseline(wl, x, target_s: float, scoring: str = "dot"):
+def cpu_baseline(wl, x, target_s: float, scoring: str = "dot", table: str = "f32"):
     """The oracle as it is (addressing of both branches + scan) on a bounded
     sample of the same workload: the first B' sequences with all H heads, or
     the first T' tokens of one sequence when a whole one already exceeds the
@@ -91,8 +93,13 @@ def cpu_baseline(wl, x, target_s: float, scoring: str = "dot"):
         t0 = time.perf_counter()
         iw, ww, _, _ = oracle.address(sl(x["q_w"]), x["subkeys"], wl.W, nthreads, scoring)
         ir, wr, _, _ = oracle.address(sl(x["q_r"]), x["subkeys"], wl.R, nthreads, scoring)
-        oracle.scan(iw, ww, ir, wr, sl(x["alpha"]), sl(x["beta"]), sl(x["v"]),
-                    oracle.broadcast_state(x["M0"].numpy(), nb), oracle.EQ4, nthreads)
+        M_in = oracle.broadcast_state(x["M0"].numpy(), nb)
+        if table == "bf16":
+            import torch
+            oracle.scan_bf16(iw, ww, ir, wr, sl(x["alpha"]), sl(x["beta"]), sl(x["v"]),
+                             torch.from_numpy(M_in.copy()).to(torch.bfloat16), oracle.EQ4, nthreads)
+        else:
+            oracle.scan(iw, ww, ir, wr, sl(x["alpha"]), sl(x["beta"]), sl(x["v"]), M_in, oracle.EQ4, nthreads)
         return time.perf_counter() - t0
 
     # two calibration points separate the per-call fixed cost from the per-token cost
@@ -107,7 +114,8 @@ def cpu_baseline(wl, x, target_s: float, scoring: str = "dot"):
     ts = run(nb, Tp) if (nb, Tp) != (1, T2) else t2
     return {"value": nb * Tp / ts, "unit": "tokens/s", "cores": nthreads, "kind": "oracle",
             "sample": f"{nb} of {wl.B} sequences of {wl.name}, all {wl.H} heads, first {Tp} of "
-                      f"{wl.T} tokens ({scoring} addressing of both branches + EQ4 scan), {ts:.1f} s wall",
+                      f"{wl.T} tokens ({scoring} addressing of both branches + EQ4 scan, {table} table), "
+                      f"{ts:.1f} s wall",
             "host_cpu": host_cpu()}
 
 
@@ -233,7 +241,8 @@ def decode_bench(a, wl, x, dev):
     sub = x["subkeys"].to(dev)
     tok = lambda key, k: x[key][:, :, k:k + 1].contiguous().to(dev)
     per = [{key: tok(key, k) for key in ("q_w", "q_r", "alpha", "beta", "v")} for k in range(nsteps)]
-    M = sdm.sdm_state_init(x["M0"].to(dev), B)
+    tdt = torch.bfloat16 if a.table == "bf16" else torch.float32
+    M = sdm.sdm_state_init(x["M0"].to(dev), B, dtype=tdt)
     addr_out = (torch.empty((B, H, 1, W), dtype=torch.int32, device=dev),
                 torch.empty((B, H, 1, W), dtype=torch.float32, device=dev),
                 torch.empty((B, H, 1, R), dtype=torch.int32, device=dev),
@@ -264,7 +273,7 @@ def decode_bench(a, wl, x, dev):
     ms_step = 1e3 * (time.perf_counter() - t0) / a.steps
     addr_ms = sum(m[0].elapsed_time(m[1]) for m in marks) / a.steps
     scan_ms = sum(m[1].elapsed_time(m[2]) for m in marks) / a.steps
-    row_bytes = B * H * (2 * W + R) * dv * 4
+    row_bytes = B * H * (2 * W + R) * dv * (2 if a.table == "bf16" else 4)
     gbps = row_bytes / (scan_ms * 1e-3) / 1e9
     rec = {
         "metric": "SDM decode tokens/s at N=65536,W=R=64,d_v=128 (one token per sequence per step)",
@@ -272,9 +281,9 @@ def decode_bench(a, wl, x, dev):
         "warmup": a.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": wl.name, "B": B, "H": H, "T_per_step": 1, "N": N, "W": W, "R": R, "d_v": dv,
-                   "d_h": wl.d_h, "form": a.form, "scoring": a.scoring,
-                   "inputs": "bf16 q/v/subkeys, fp32 table/gates",
-                   "state_GiB": B * H * N * dv * 4 / 2**30},
+                   "d_h": wl.d_h, "form": a.form, "scoring": a.scoring, "table": a.table,
+                   "inputs": f"bf16 q/v/subkeys, {a.table} table, fp32 gates",
+                   "state_GiB": B * H * N * dv * (2 if a.table == "bf16" else 4) / 2**30},
         "breakdown_ms": {"address": addr_ms, "scan": scan_ms},
         "slot_row_GBps": gbps,
         "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
@@ -283,7 +292,7 @@ def decode_bench(a, wl, x, dev):
                      "algorithmic_bytes_per_launch": row_bytes},
     }
     if not a.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(wl, x, a.cpu_seconds, a.scoring)
+        rec["cpu_baseline"] = cpu_baseline(wl, x, a.cpu_seconds, a.scoring, a.table)
     print(json.dumps(rec), flush=True)
 
 
@@ -312,6 +321,8 @@ def main():
     if wl.name == "decode":
         return decode_bench(a, wl, x, dev)
     if a.train:
+        if a.table != "f32":
+            sys.exit("training keeps an fp32 table (the backward restores fp32 pre-images)")
         return train_bench(a, wl, x, dev)
     g = {k: v.to(dev) for k, v in x.items()}
     B, H, T, N, dv, W, R = wl.B, wl.H, wl.T, wl.N, wl.d_v, wl.W, wl.R
@@ -319,7 +330,8 @@ def main():
                 torch.empty((B, H, T, W), dtype=torch.float32, device=dev),
                 torch.empty((B, H, T, R), dtype=torch.int32, device=dev),
                 torch.empty((B, H, T, R), dtype=torch.float32, device=dev))
-    M = torch.empty((B, H, N, dv), dtype=torch.float32, device=dev)
+    esz = 2 if a.table == "bf16" else 4
+    M = torch.empty((B, H, N, dv), dtype=torch.bfloat16 if a.table == "bf16" else torch.float32, device=dev)
     y = torch.empty((B, H, T, dv), dtype=torch.float32, device=dev)
     ws = torch.empty((sdm.sdm_scan_workspace_bytes(B, H, T, W, R, dv),), dtype=torch.uint8, device=dev)
     ev = lambda: torch.cuda.Event(enable_timing=True)
@@ -352,7 +364,7 @@ def main():
     addr_ms = sum(m[1].elapsed_time(m[2]) for m in marks) / a.steps
     scan_ms = sum(m[2].elapsed_time(m[3]) for m in marks) / a.steps
 
-    row_bytes = B * H * T * (2 * W + R) * dv * 4
+    row_bytes = B * H * T * (2 * W + R) * dv * esz
     scan_gbps = row_bytes / (scan_ms * 1e-3) / 1e9
     rec = {
         "metric": METRIC,
@@ -368,20 +380,23 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": wl.name, "B": B, "H": H, "T": T, "N": N, "W": W, "R": R,
-                   "d_v": dv, "d_h": wl.d_h, "form": a.form, "scoring": a.scoring,
-                   "inputs": "bf16 q/v/subkeys, fp32 table/gates" if wl.bf16_inputs else "fp32"},
+                   "d_v": dv, "d_h": wl.d_h, "form": a.form, "scoring": a.scoring, "table": a.table,
+                   "inputs": (f"bf16 q/v/subkeys, {a.table} table, fp32 gates" if wl.bf16_inputs
+                              else f"fp32 inputs, {a.table} table")},
         "breakdown_ms": {"state_init": init_ms, "address": addr_ms, "scan": scan_ms},
         # the half-score contraction of both branches: 2 halves x n_sub x d_h MACs per token-branch
         "address_mfma_TFLOPs": 2 * B * H * T * 2 * (2 * wl.n_sub * wl.d_h) / (addr_ms * 1e-3) / 1e12,
         "scan_tokens_per_s": B * T / (scan_ms * 1e-3),
         "slot_row_GBps": scan_gbps,
         "roofline": {"bound": "hbm", "achieved": scan_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": scan_gbps / HBM_PEAK_GBPS, "traffic": measured_traffic(),
+                     "frac": scan_gbps / HBM_PEAK_GBPS,
+                     "traffic": measured_traffic() if (a.table, a.form, wl.name) == ("f32", "eq4", "gdn_matched")
+                     else None,
                      "kernel": "sdm_scan_forward (plan_kernel + scan_kernel + ypart_reduce)",
                      "algorithmic_bytes_per_launch": row_bytes},
     }
     if not a.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(wl, x, a.cpu_seconds, a.scoring)
+        rec["cpu_baseline"] = cpu_baseline(wl, x, a.cpu_seconds, a.scoring, a.table)
     print(json.dumps(rec), flush=True)
 
 

@@ -32,7 +32,7 @@
 extern "C" {
 #endif
 
-#define SDM_ABI_VERSION 3
+#define SDM_ABI_VERSION 4
 
 typedef enum sdm_status {
     SDM_OK = 0,
@@ -130,9 +130,11 @@ int sdm_debug_half_scores_idw(const void* q, int q_dtype, const void* subkeys, i
 /*
  * sdm_state_init -- per-sequence initial table from the (learned) initial
  * state M0 ([SDM] §2.6): M[b] = M0 for every b.
- *   M0 [H, N, dv] fp32, M [B, H, N, dv] fp32 (out). dv must be a multiple of 4.
+ *   M0 [H, N, dv] fp32, M [B, H, N, dv] (out) in m_dtype: SDM_F32 (a copy) or
+ *   SDM_BF16 (each element rounded to nearest-even bfloat16). dv must be a
+ *   multiple of 4.
  */
-int sdm_state_init(const float* M0, float* M, int64_t B, int64_t H, int64_t N,
+int sdm_state_init(const float* M0, void* M, int m_dtype, int64_t B, int64_t H, int64_t N,
                    int64_t dv, void* stream);
 
 /*
@@ -155,8 +157,13 @@ int64_t sdm_scan_workspace_bytes(int64_t B, int64_t H, int64_t T, int64_t W, int
  *   idx_w, wt_w  [B, H, T, W]   int32 / fp32     idx_r, wt_r [B, H, T, R]
  *   alpha, beta  [B, H, T]      fp32 gates
  *   v            [B, H, T, dv]  v_dtype (SDM_F32 or SDM_BF16)
- *   M            [B, H, N, dv]  fp32, in: state before token 0, out: after token T-1
+ *   M            [B, H, N, dv]  m_dtype, in: state before token 0, out: after token T-1
  *   y            [B, H, T, dv]  fp32 (out)
+ *   m_dtype      SDM_F32, or SDM_BF16: the table is stored in bfloat16 (the
+ *                2-byte state elements the notes' per-layer state size implies,
+ *                [SDM] §4.5 Table 3 with §2.8's element count); each update is
+ *                computed in fp32 from the widened row and stored rounded to
+ *                nearest even, halving the bytes of every row access
  *   workspace    device buffer of >= sdm_scan_workspace_bytes(B,H,T,W,R,dv) bytes,
  *                16-byte aligned; its contents on entry do not matter.
  *
@@ -165,14 +172,14 @@ int64_t sdm_scan_workspace_bytes(int64_t B, int64_t H, int64_t T, int64_t W, int
  * of one token distinct (sdm_address guarantees both). Entries that break the
  * first are skipped (memory-safe, result unspecified); the second gives an
  * unspecified result. Weights are used as given.
- * Supported: 1 <= W, R <= 256, N <= 2^18, dv a multiple of 4, N * dv * 4 < 2^31
- * (one stream's table below 2 GiB).
+ * Supported: 1 <= W, R <= 256, N <= 2^18, dv a multiple of 4 (of 8 for a bf16
+ * table), N * dv * 4 < 2^31.
  */
 int sdm_scan_forward(const int32_t* idx_w, const float* wt_w, int64_t W,
                      const int32_t* idx_r, const float* wt_r, int64_t R,
                      const float* alpha, const float* beta,
                      const void* v, int v_dtype,
-                     float* M, float* y,
+                     void* M, int m_dtype, float* y,
                      int64_t B, int64_t H, int64_t T, int64_t N, int64_t dv,
                      int form, void* workspace, int64_t workspace_bytes, void* stream);
 
@@ -191,8 +198,9 @@ int sdm_scan_forward(const int32_t* idx_w, const float* wt_w, int64_t W,
 int64_t sdm_scan_snapshot_bytes(int64_t B, int64_t H, int64_t T, int64_t W, int64_t dv);
 
 /*
- * sdm_scan_forward_save -- sdm_scan_forward (same arguments; M bit-identical
- * to it, y equal up to the order in which the read rows are added) that also
+ * sdm_scan_forward_save -- sdm_scan_forward on an fp32 table (same arguments
+ * but m_dtype; M bit-identical to it, y equal up to the order in which the read
+ * rows are added) that also
  * stores, for every write, the row as it was before this token's decay:
  *   snap [B, H, T, W, dv] fp32 (out): snap[b,h,t,p,:] = M_{t-1}[b,h,idx_w[b,h,t,p],:]
  * The workspace is the one sdm_scan_workspace_bytes gives. Same support as

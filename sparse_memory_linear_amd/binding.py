@@ -32,9 +32,9 @@ _SIGS = {
     "sdm_address_idw": (_I, [_P, _P, _I, _P, _P, _I, _I64, _I64, _I64, _I64, _I64, _I64, _I64,
                              _P, _P, _P, _P, _P, _P, _P]),
     "sdm_debug_half_scores_idw": (_I, [_P, _I, _P, _I, _I64, _I64, _I64, _I64, _I64, _P, _P]),
-    "sdm_state_init": (_I, [_P, _P, _I64, _I64, _I64, _I64, _P]),
+    "sdm_state_init": (_I, [_P, _P, _I, _I64, _I64, _I64, _I64, _P]),
     "sdm_scan_workspace_bytes": (_I64, [_I64, _I64, _I64, _I64, _I64, _I64]),
-    "sdm_scan_forward": (_I, [_P, _P, _I64, _P, _P, _I64, _P, _P, _P, _I, _P, _P,
+    "sdm_scan_forward": (_I, [_P, _P, _I64, _P, _P, _I64, _P, _P, _P, _I, _P, _I, _P,
                               _I64, _I64, _I64, _I64, _I64, _I, _P, _I64, _P]),
     "sdm_scan_snapshot_bytes": (_I64, [_I64, _I64, _I64, _I64, _I64]),
     "sdm_scan_forward_save": (_I, [_P, _P, _I64, _P, _P, _I64, _P, _P, _P, _I, _P, _P, _P,
@@ -174,15 +174,20 @@ def sdm_debug_half_scores(q: torch.Tensor, subkeys: torch.Tensor, scoring: str =
     return half
 
 
-def sdm_state_init(M0: torch.Tensor, B: int, out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Per-sequence table [B,H,N,dv] initialised from M0 [H,N,dv]."""
+def sdm_state_init(M0: torch.Tensor, B: int, out: Optional[torch.Tensor] = None,
+                   dtype: torch.dtype = torch.float32) -> torch.Tensor:
+    """Per-sequence table [B,H,N,dv] initialised from M0 [H,N,dv] fp32, stored in
+    ``dtype`` (float32, or bfloat16: rounded to nearest even)."""
     d = _dev(M0)
     H, N, dv = M0.shape
-    M = out if out is not None else torch.empty((B, H, N, dv), dtype=torch.float32, device=d)
-    if M.shape != (B, H, N, dv) or M.dtype != torch.float32:
+    if M0.dtype != torch.float32:
+        raise ValueError("M0 must be fp32")
+    M = out if out is not None else torch.empty((B, H, N, dv), dtype=dtype, device=d)
+    if M.shape != (B, H, N, dv) or M.dtype not in (torch.float32, torch.bfloat16):
         raise ValueError("state tensor has the wrong shape or dtype")
     _dev(M0, M)
-    _check("sdm_state_init", lib().sdm_state_init(_ptr(M0), _ptr(M), B, H, N, dv, _stream(d)))
+    _check("sdm_state_init", lib().sdm_state_init(_ptr(M0), _ptr(M), _dtype_code(M), B, H, N, dv,
+                                                  _stream(d)))
     return M
 
 
@@ -193,7 +198,7 @@ def sdm_scan_workspace_bytes(B: int, H: int, T: int, W: int, R: int, dv: int) ->
     return n
 
 
-def _scan_inputs(fn, idx_w, wt_w, idx_r, wt_r, alpha, beta, v, M):
+def _scan_inputs(fn, idx_w, wt_w, idx_r, wt_r, alpha, beta, v, M, table_dtypes=(torch.float32,)):
     d = _dev(idx_w, wt_w, idx_r, wt_r, alpha, beta, v, M)
     B, H, T, W = idx_w.shape
     R = idx_r.shape[3]
@@ -206,7 +211,7 @@ def _scan_inputs(fn, idx_w, wt_w, idx_r, wt_r, alpha, beta, v, M):
             raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {shp}")
     if idx_w.dtype != torch.int32 or idx_r.dtype != torch.int32 or wt_w.dtype != torch.float32 \
             or wt_r.dtype != torch.float32 or alpha.dtype != torch.float32 \
-            or beta.dtype != torch.float32 or M.dtype != torch.float32:
+            or beta.dtype != torch.float32 or M.dtype not in table_dtypes:
         raise ValueError(f"dtype mismatch in {fn}")
     return d, (B, H, T, W, R, N, dv)
 
@@ -236,17 +241,18 @@ def sdm_scan_forward(idx_w: torch.Tensor, wt_w: torch.Tensor, idx_r: torch.Tenso
                      v: torch.Tensor, M: torch.Tensor, form: str = "eq4",
                      y: Optional[torch.Tensor] = None,
                      workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Sparse gated delta scan over all T tokens; M [B,H,N,dv] is updated in place.
+    """Sparse gated delta scan over all T tokens; M [B,H,N,dv] (float32 or
+    bfloat16 storage) is updated in place.
 
     Returns y [B,H,T,dv] fp32.
     """
     d, (B, H, T, W, R, N, dv) = _scan_inputs("sdm_scan_forward", idx_w, wt_w, idx_r, wt_r,
-                                             alpha, beta, v, M)
+                                             alpha, beta, v, M, (torch.float32, torch.bfloat16))
     y = _f32_out(y, (B, H, T, dv), d, "y")
     workspace = _workspace(workspace, sdm_scan_workspace_bytes(B, H, T, W, R, dv), d)
     _check("sdm_scan_forward", lib().sdm_scan_forward(
         _ptr(idx_w), _ptr(wt_w), W, _ptr(idx_r), _ptr(wt_r), R, _ptr(alpha), _ptr(beta),
-        _ptr(v), _dtype_code(v), _ptr(M), _ptr(y), B, H, T, N, dv, FORMS[form],
+        _ptr(v), _dtype_code(v), _ptr(M), _dtype_code(M), _ptr(y), B, H, T, N, dv, FORMS[form],
         _ptr(workspace), workspace.numel(), _stream(d)))
     return y
 

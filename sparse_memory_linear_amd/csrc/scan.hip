@@ -345,7 +345,7 @@ struct ScanKArgs {
     const uint8_t* plan;  // [NS][P][T][rec]
     const uint32_t* maxc; // [NS][P][2]: most writes / reads of one token in a partition
     const void* v;
-    float* M;
+    void* M;              // fp32 or bfloat16 elements
     float* y;       // y of (stream s, partition p) at y + s * ys + p * yp
     int64_t ys, yp;
     int T;          // tokens in this launch
@@ -366,10 +366,18 @@ struct ScanKArgs {
 // kernel would round it) and the write position in place of w and beta; the
 // shared-residual form runs with one row partition, where a writer's rank in
 // its token is the write position.
-template <int S, int FORM, bool VBF16, bool SAVE>
-__global__ __launch_bounds__(SlabCfg<S>::NWMAX * 64) void scan_kernel(ScanKArgs a) {
-    constexpr int L = S / 4, G = 64 / L;
-    constexpr int D = SlabCfg<S>::D, NWMAX = SlabCfg<S>::NWMAX, NRMAX = nrmax<S>();
+// MBF16: the table is stored in bfloat16. A lane's 16 bytes of a row then hold
+// 8 columns instead of 4, so the same lane layout covers twice the columns
+// (slab width S = 2 * SL) and every row access moves half the bytes; rows are
+// unpacked to fp32 for the update and rounded to nearest-even bfloat16 on the
+// store (and in the LDS ring, which holds the stored bytes).
+// SL = 4 * (lanes per row segment): the slab width in columns of an fp32 table.
+template <int SL, int FORM, bool VBF16, bool SAVE, bool MBF16>
+__global__ __launch_bounds__(SlabCfg<SL>::NWMAX * 64) void scan_kernel(ScanKArgs a) {
+    static_assert(!(SAVE && MBF16), "pre-images are taken of fp32 tables only");
+    using RF = RowFmt<MBF16>;
+    constexpr int L = SL / 4, G = 64 / L, NQ = RF::NQ, CPL = RF::CPL, S = L * CPL;
+    constexpr int D = SlabCfg<SL>::D, NWMAX = SlabCfg<SL>::NWMAX, NRMAX = nrmax<SL>();
     constexpr int DM = D + 1;       // plan-entry lead beyond D
     constexpr int UP = D + 1;       // row / value register rings: D in flight + the one in use
     constexpr int U = D + DM + 1;   // plan-entry ring = unroll factor (a multiple of UP, so
@@ -377,24 +385,24 @@ __global__ __launch_bounds__(SlabCfg<S>::NWMAX * 64) void scan_kernel(ScanKArgs 
     static_assert(U % UP == 0, "ring sizes");
     constexpr int UR = U;           // LDS ring of written rows: token t uses slot t % U, a
                                     // constant in the unrolled loop (reuse needs UR >= D + 2)
-    using VL = VLoad<VBF16>;
-    using V4 = typename VL::T4;
+    using VL = VLoadN<VBF16, NQ>;
+    using V4 = typename VL::T;
     const int NWW = a.NWW, NWR = a.NWR, T = a.T, dv = a.dv;
     extern __shared__ float4 lds[];
     float4* ring = lds;                                              // [UR][NWW*G][L]
     float* ybuf = reinterpret_cast<float*>(lds + UR * NWW * G * L);  // [2][NRMAX][S]
-    float4* vbuf = reinterpret_cast<float4*>(ybuf + 2 * NRMAX * S);  // [NWW][L] (FIG2)
+    float4* vbuf = reinterpret_cast<float4*>(ybuf + 2 * NRMAX * S);  // [NWW][S/4] (FIG2)
 
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane / L, cc = lane % L;
     const int b = blockIdx.x, xcd = b & 7, kq = b >> 3, units = a.nslab * a.P;
     const int64_t s = (int64_t)(kq / units) * 8 + xcd;
     const int slab = kq % a.nslab, part = (kq % units) / a.nslab;
     if (s >= a.NS) return;  // uniform over the workgroup
-    const int col = slab * S + cc * 4;
-    const Geom geo{S, G, NWW, NWR};
+    const int col = slab * S + cc * CPL;
+    const Geom geo{SL, G, NWW, NWR};
     const uint32_t REC = (uint32_t)geo.rec();
     const rsrc_t Rp = make_rsrc(a.plan + (s * a.P + part) * (int64_t)T * REC, (int64_t)T * REC);
-    const rsrc_t Rm = make_rsrc(a.M + s * a.N * dv, a.N * dv * 4);
+    const rsrc_t Rm = make_rsrc(static_cast<char*>(a.M) + s * a.N * dv * RF::ESZ, a.N * dv * RF::ESZ);
     const rsrc_t Rv = make_rsrc(static_cast<const char*>(a.v) + s * a.TS * dv * VL::ESZ, (int64_t)T * dv * VL::ESZ);
     const rsrc_t Ry = make_rsrc(a.y + s * a.ys + part * a.yp, (int64_t)T * dv * 4);
     const rsrc_t Rs = make_rsrc(SAVE ? a.snap + s * a.snap_s : a.M, SAVE ? (int64_t)T * a.W * dv * 4 : 0);
@@ -402,7 +410,8 @@ __global__ __launch_bounds__(SlabCfg<S>::NWMAX * 64) void scan_kernel(ScanKArgs 
     const int pos = wave * G + r;                        // write position of a writer lane
     const int rw = wave - NWW;                           // reader index
     const uint32_t e_off = writer ? (uint32_t)pos * 16u : (uint32_t)geo.wbytes() + (uint32_t)(rw * G + r) * 8u;
-    const uint32_t dv4 = (uint32_t)dv * 4u, col4 = (uint32_t)col * 4u;
+    const uint32_t dv4 = (uint32_t)dv * 4u, col4 = (uint32_t)col * 4u;          // fp32 rows (y, snapshots)
+    const uint32_t mrow = (uint32_t)dv * RF::ESZ, colb = (uint32_t)col * RF::ESZ;  // table rows
     const uint32_t v_off = (uint32_t)col * VL::ESZ;
     const uint32_t vstride = (uint32_t)dv * VL::ESZ;
     const uint32_t sstride = (uint32_t)a.W * dv4;                    // snapshot bytes per token
@@ -437,7 +446,7 @@ __global__ __launch_bounds__(SlabCfg<S>::NWMAX * 64) void scan_kernel(ScanKArgs 
     }
 
     auto row_off = [&](uint32_t pk) -> uint32_t {
-        return (pk & ENT_INVALID) ? OOB : __umul24(pk & ROW_MASK, dv4) + col4;
+        return (pk & ENT_INVALID) ? OOB : __umul24(pk & ROW_MASK, mrow) + colb;
     };
     auto load_went = [&](int t) -> int4 { return ld_i4(Rp, e_off, (uint32_t)t * REC); };
     auto load_rent = [&](int t) -> int2 { return ld_i2(Rp, e_off, (uint32_t)t * REC); };
@@ -466,20 +475,35 @@ __global__ __launch_bounds__(SlabCfg<S>::NWMAX * 64) void scan_kernel(ScanKArgs 
             const uint32_t so = WPOS ? __umul24((uint32_t)e.w, dv4) + col4 : s_lane;
             st_f4(old, Rs, (pk & ENT_INVALID) ? OOB : so, (uint32_t)t * sstride);
         }
-        const float4 mt = f4_scale(al, old);
-        float4 pred = mt;
-        if constexpr (FORM == 1) {
-            const float part = rows_reduce<L>(f4_scale(w, mt));
-            if ((lane & 15) < L) reinterpret_cast<float*>(vbuf)[wave * S + 4 * (lane & 15) + (lane >> 4)] = part;
-            __syncthreads();
-            pred = vbuf[cc];
+        float4 mt[NQ], pred[NQ], vf[NQ], nv[NQ];
+        RF::unpack(old, mt);
 #pragma unroll
-            for (int q = 1; q < NWMAX; ++q)
-                if (q < NWW) pred = f4_add(pred, vbuf[q * L + cc]);
+        for (int i = 0; i < NQ; ++i) {
+            mt[i] = f4_scale(al, mt[i]);
+            pred[i] = mt[i];
         }
-        const float4 nv = f4_fma(WPOS ? w : be * w, f4_sub(VL::f(vt), pred), mt);
-        st_f4(nv, Rm, row_off(pk), 0u);
-        ring_at(slot, pos) = nv;
+        if constexpr (FORM == 1) {
+#pragma unroll
+            for (int i = 0; i < NQ; ++i) {
+                const float part = rows_reduce<L>(f4_scale(w, mt[i]));
+                if ((lane & 15) < L)
+                    reinterpret_cast<float*>(vbuf)[wave * S + CPL * (lane & 15) + 4 * i + (lane >> 4)] = part;
+            }
+            __syncthreads();
+#pragma unroll
+            for (int i = 0; i < NQ; ++i) {
+                pred[i] = vbuf[NQ * cc + i];
+#pragma unroll
+                for (int q = 1; q < NWMAX; ++q)
+                    if (q < NWW) pred[i] = f4_add(pred[i], vbuf[q * (S / 4) + NQ * cc + i]);
+            }
+        }
+        VL::f(vt, vf);
+#pragma unroll
+        for (int i = 0; i < NQ; ++i) nv[i] = f4_fma(WPOS ? w : be * w, f4_sub(vf[i], pred[i]), mt[i]);
+        const float4 st = RF::pack(nv);
+        st_f4(st, Rm, row_off(pk), 0u);
+        ring_at(slot, pos) = st;
         __syncthreads();
     };
     // one token of a reader wavefront (barriers: [B'_t], B_t); the partial sums
@@ -493,8 +517,13 @@ __global__ __launch_bounds__(SlabCfg<S>::NWMAX * 64) void scan_kernel(ScanKArgs 
         if (rw == 0)  // uniform per wavefront; no memory operation inside
             acc = readers_sum<NRMAX, S>(ybuf + ((t - 1) & 1) * NRMAX * S + ylane, nra);
         const uint32_t pk = (uint32_t)e.x;
-        const float part = rows_reduce<L>(f4_scale(__int_as_float(e.y), source(slot, pk, pre)));
-        if ((lane & 15) < L) ybuf[((t & 1) * NRMAX + rw) * S + 4 * (lane & 15) + (lane >> 4)] = part;
+        float4 cur[NQ];
+        RF::unpack(source(slot, pk, pre), cur);
+#pragma unroll
+        for (int i = 0; i < NQ; ++i) {
+            const float part = rows_reduce<L>(f4_scale(__int_as_float(e.y), cur[i]));
+            if ((lane & 15) < L) ybuf[((t & 1) * NRMAX + rw) * S + CPL * (lane & 15) + 4 * i + (lane >> 4)] = part;
+        }
         st_f1(acc, Ry, t > 0 ? y_off : OOB, (uint32_t)(t > 0 ? t - 1 : 0) * dv4);
     };
 
@@ -581,7 +610,7 @@ struct DirectArgs {
     const int32_t* idx_r; const float* wt_r; int R;
     const float* alpha; const float* beta;
     const void* v;
-    float* M;
+    void* M;        // fp32 or bfloat16 elements
     float* y;
     int T;
     int64_t N;
@@ -591,22 +620,24 @@ struct DirectArgs {
     float* snap;    // SAVE: [NS][T][W][dv] pre-images
 };
 
-template <int S, int FORM, bool VBF16, bool SAVE>
-__global__ __launch_bounds__(SlabCfg<S>::NWMAX * 64) void scan_direct_kernel(DirectArgs a) {
-    constexpr int L = S / 4, G = 64 / L;
-    constexpr int NWMAX = SlabCfg<S>::NWMAX, NRMAX = nrmax<S>();
-    using VL = VLoad<VBF16>;
-    using V4 = typename VL::T4;
+template <int SL, int FORM, bool VBF16, bool SAVE, bool MBF16>
+__global__ __launch_bounds__(SlabCfg<SL>::NWMAX * 64) void scan_direct_kernel(DirectArgs a) {
+    static_assert(!(SAVE && MBF16), "pre-images are taken of fp32 tables only");
+    using RF = RowFmt<MBF16>;
+    constexpr int L = SL / 4, G = 64 / L, NQ = RF::NQ, CPL = RF::CPL, S = L * CPL;
+    constexpr int NWMAX = SlabCfg<SL>::NWMAX, NRMAX = nrmax<SL>();
+    using VL = VLoadN<VBF16, NQ>;
+    using V4 = typename VL::T;
     const int NWW = a.NWW, NWR = a.NWR, T = a.T, dv = a.dv, W = a.W, R = a.R;
     __shared__ float ybuf[NRMAX * S];
-    __shared__ float4 vbuf[NWMAX * L];
+    __shared__ float4 vbuf[NWMAX * S / 4];
 
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane / L, cc = lane % L;
     const int b = blockIdx.x, xcd = b & 7, kq = b >> 3;
     const int64_t s = (int64_t)(kq / a.nslab) * 8 + xcd;
     const int slab = kq % a.nslab;
     if (s >= a.NS) return;  // uniform over the workgroup
-    const int col = slab * S + cc * 4;
+    const int col = slab * S + cc * CPL;
     const bool writer = wave < NWW;
     const int rw = wave - NWW;
     const int pos = writer ? wave * G + r : rw * G + r;  // access position of this lane's row
@@ -614,12 +645,13 @@ __global__ __launch_bounds__(SlabCfg<S>::NWMAX * 64) void scan_direct_kernel(Dir
     const bool has = pos < K;
     const int32_t* ix = (writer ? a.idx_w : a.idx_r) + s * (int64_t)T * K;
     const float* wx = (writer ? a.wt_w : a.wt_r) + s * (int64_t)T * K;
-    const rsrc_t Rm = make_rsrc(a.M + s * a.N * dv, a.N * dv * 4);
+    const rsrc_t Rm = make_rsrc(static_cast<char*>(a.M) + s * a.N * dv * RF::ESZ, a.N * dv * RF::ESZ);
     const rsrc_t Rv = make_rsrc(static_cast<const char*>(a.v) + s * (int64_t)T * dv * VL::ESZ,
                                 (int64_t)T * dv * VL::ESZ);
     const rsrc_t Ry = make_rsrc(a.y + s * (int64_t)T * dv, (int64_t)T * dv * 4);
     const rsrc_t Rs = make_rsrc(SAVE ? a.snap + s * (int64_t)T * W * dv : a.M, SAVE ? (int64_t)T * W * dv * 4 : 0);
-    const uint32_t dv4 = (uint32_t)dv * 4u, col4 = (uint32_t)col * 4u;
+    const uint32_t dv4 = (uint32_t)dv * 4u, col4 = (uint32_t)col * 4u;          // fp32 rows (y, snapshots)
+    const uint32_t mrow = (uint32_t)dv * RF::ESZ, colb = (uint32_t)col * RF::ESZ;  // table rows
     const uint32_t y_off = (!writer && rw == 0 && lane < S) ? (uint32_t)(slab * S + lane) * 4u : OOB;
     const int ylane = lane < S ? lane : 0;
     int nra = 1;
@@ -628,7 +660,7 @@ __global__ __launch_bounds__(SlabCfg<S>::NWMAX * 64) void scan_direct_kernel(Dir
     __syncthreads();
 
     auto off_of = [&](int32_t row) -> uint32_t {
-        return (row >= 0 && row < a.N) ? __umul24((uint32_t)row, dv4) + col4 : OOB;
+        return (row >= 0 && row < a.N) ? __umul24((uint32_t)row, mrow) + colb : OOB;
     };
     // this lane's access of token t: row offset and weight (0 when absent)
     int32_t row_n = has ? ix[pos] : -1;
@@ -651,24 +683,43 @@ __global__ __launch_bounds__(SlabCfg<S>::NWMAX * 64) void scan_direct_kernel(Dir
             const float4 pre = ld_f4(Rm, off, 0u);  // after the barrier that closed token t-1
             if constexpr (SAVE)
                 st_f4(pre, Rs, off == OOB ? OOB : (uint32_t)pos * dv4 + col4, (uint32_t)t * (uint32_t)W * dv4);
-            const float4 mt = f4_scale(al, pre);
-            float4 pred = mt;
-            if constexpr (FORM == 1) {
-                const float part = rows_reduce<L>(f4_scale(w, mt));
-                if ((lane & 15) < L) reinterpret_cast<float*>(vbuf)[wave * S + 4 * (lane & 15) + (lane >> 4)] = part;
-                __syncthreads();
-                pred = vbuf[cc];
-                for (int q = 1; q < NWW; ++q) pred = f4_add(pred, vbuf[q * L + cc]);
+            float4 mt[NQ], pred[NQ], vf[NQ], nv[NQ];
+            RF::unpack(pre, mt);
+#pragma unroll
+            for (int i = 0; i < NQ; ++i) {
+                mt[i] = f4_scale(al, mt[i]);
+                pred[i] = mt[i];
             }
-            st_f4(f4_fma(be * w, f4_sub(VL::f(vt), pred), mt), Rm, off, 0u);
+            if constexpr (FORM == 1) {
+#pragma unroll
+                for (int i = 0; i < NQ; ++i) {
+                    const float part = rows_reduce<L>(f4_scale(w, mt[i]));
+                    if ((lane & 15) < L)
+                        reinterpret_cast<float*>(vbuf)[wave * S + CPL * (lane & 15) + 4 * i + (lane >> 4)] = part;
+                }
+                __syncthreads();
+#pragma unroll
+                for (int i = 0; i < NQ; ++i) {
+                    pred[i] = vbuf[NQ * cc + i];
+                    for (int q = 1; q < NWW; ++q) pred[i] = f4_add(pred[i], vbuf[q * (S / 4) + NQ * cc + i]);
+                }
+            }
+            VL::f(vt, vf);
+#pragma unroll
+            for (int i = 0; i < NQ; ++i) nv[i] = f4_fma(be * w, f4_sub(vf[i], pred[i]), mt[i]);
+            st_f4(RF::pack(nv), Rm, off, 0u);
             __syncthreads();  // B1: this token's rows are written
             __syncthreads();  // B2
         } else {
             if constexpr (FORM == 1) __syncthreads();
             __syncthreads();  // B1
-            const float4 cur = ld_f4(Rm, off, 0u);  // the rows after this token's writes
-            const float part = rows_reduce<L>(f4_scale(w, cur));
-            if ((lane & 15) < L) ybuf[rw * S + 4 * (lane & 15) + (lane >> 4)] = part;
+            float4 cur[NQ];
+            RF::unpack(ld_f4(Rm, off, 0u), cur);  // the rows after this token's writes
+#pragma unroll
+            for (int i = 0; i < NQ; ++i) {
+                const float part = rows_reduce<L>(f4_scale(w, cur[i]));
+                if ((lane & 15) < L) ybuf[rw * S + CPL * (lane & 15) + 4 * i + (lane >> 4)] = part;
+            }
             __syncthreads();  // B2: all partial sums are in
             float acc = 0.f;
             if (rw == 0) acc = readers_sum<NRMAX, S>(ybuf + ylane, nra);
@@ -682,10 +733,11 @@ __global__ __launch_bounds__(SlabCfg<S>::NWMAX * 64) void scan_direct_kernel(Dir
 // wavefront passed barrier B_{t-1}, which needs t - UR + D <= t - 2, i.e.
 // UR >= D + 2 (here UR = 2D + 2).
 
-template <int S>
-size_t scan_lds_bytes(const Geom& g) {
-    constexpr int D = SlabCfg<S>::D, UR = 2 * D + 2, L = S / 4;
-    return (size_t)UR * g.NWW * g.G * L * 16 + (size_t)2 * nrmax<S>() * S * 4 + (size_t)g.NWW * L * 16;
+template <int SL>
+size_t scan_lds_bytes(const Geom& g, int cpl) {
+    constexpr int D = SlabCfg<SL>::D, UR = 2 * D + 2, L = SL / 4;
+    const int S = L * cpl;
+    return (size_t)UR * g.NWW * g.G * L * 16 + (size_t)2 * nrmax<SL>() * S * 4 + (size_t)g.NWW * S * 4;
 }
 
 // Partial y of P row partitions summed in partition order: y[s, t] = sum_p yp[p, s, t].
@@ -729,9 +781,32 @@ WsLayout ws_layout(const Cfg& c, int64_t NS, int64_t Tc, int dv) {
     return w;
 }
 
-template <int S>
+// One instance of the token-loop kernel per (slab, form, v dtype, pre-image
+// stores, table dtype); pre-images are taken only of fp32 tables.
+template <int SL>
+void launch_scan_inst(int form, bool vb, bool save, bool mb, dim3 grid, dim3 block, size_t lds, hipStream_t st,
+                      const ScanKArgs& k) {
+    const int sel = (form ? 8 : 0) | (vb ? 4 : 0) | (save ? 2 : 0) | (mb ? 1 : 0);
+    switch (sel) {
+        case 0: hipLaunchKernelGGL((scan_kernel<SL, 0, false, false, false>), grid, block, lds, st, k); break;
+        case 1: hipLaunchKernelGGL((scan_kernel<SL, 0, false, false, true>), grid, block, lds, st, k); break;
+        case 2: hipLaunchKernelGGL((scan_kernel<SL, 0, false, true, false>), grid, block, lds, st, k); break;
+        case 4: hipLaunchKernelGGL((scan_kernel<SL, 0, true, false, false>), grid, block, lds, st, k); break;
+        case 5: hipLaunchKernelGGL((scan_kernel<SL, 0, true, false, true>), grid, block, lds, st, k); break;
+        case 6: hipLaunchKernelGGL((scan_kernel<SL, 0, true, true, false>), grid, block, lds, st, k); break;
+        case 8: hipLaunchKernelGGL((scan_kernel<SL, 1, false, false, false>), grid, block, lds, st, k); break;
+        case 9: hipLaunchKernelGGL((scan_kernel<SL, 1, false, false, true>), grid, block, lds, st, k); break;
+        case 10: hipLaunchKernelGGL((scan_kernel<SL, 1, false, true, false>), grid, block, lds, st, k); break;
+        case 12: hipLaunchKernelGGL((scan_kernel<SL, 1, true, false, false>), grid, block, lds, st, k); break;
+        case 13: hipLaunchKernelGGL((scan_kernel<SL, 1, true, false, true>), grid, block, lds, st, k); break;
+        case 14: hipLaunchKernelGGL((scan_kernel<SL, 1, true, true, false>), grid, block, lds, st, k); break;
+        default: break;  // pre-images of a bf16 table: rejected by the C ABI before any launch
+    }
+}
+
+template <int SL>
 hipError_t launch_scan_slab(const ScanArgs& a, const Cfg& c, hipStream_t st) {
-    constexpr int D = SlabCfg<S>::D;
+    constexpr int D = SlabCfg<SL>::D;
     static_assert(D <= 15, "the plan stores forward distances in 4 bits");
     const Geom& g = c.g;
     // planner: tiles of TT tokens; the hash table holds the writes of TT + D tokens
@@ -747,9 +822,10 @@ hipError_t launch_scan_slab(const ScanArgs& a, const Cfg& c, hipStream_t st) {
     const bool save = a.snap != nullptr;
     const int64_t Tc = chunk_tokens(a.T, g, a.dv, save ? a.W : 0);
     const WsLayout wl = ws_layout(c, a.NS, Tc, a.dv);
-    const int nslab = a.dv / S;
+    const int cpl = a.m_bf16 ? 8 : 4;
+    const int nslab = a.dv / (SL / 4 * cpl);
     const int64_t nblk = ((a.NS + 7) / 8) * 8 * nslab * c.P;
-    const size_t lds = scan_lds_bytes<S>(g);
+    const size_t lds = scan_lds_bytes<SL>(g, cpl);
     const size_t bm_bytes = (size_t)((a.N + 31) / 32) * 4;
     const int esz = a.v_bf16 ? 2 : 4;
     uint8_t* plan = static_cast<uint8_t*>(a.workspace);
@@ -788,17 +864,7 @@ hipError_t launch_scan_slab(const ScanArgs& a, const Cfg& c, hipStream_t st) {
         k.snap = save ? a.snap + c0 * a.W * a.dv : nullptr;
         k.snap_s = a.T * a.W * a.dv;
         dim3 grid((unsigned)nblk), block((unsigned)(g.nw() * 64));
-        const int sel = (a.form ? 4 : 0) | (a.v_bf16 ? 2 : 0) | (save ? 1 : 0);
-        switch (sel) {
-            case 0: hipLaunchKernelGGL((scan_kernel<S, 0, false, false>), grid, block, lds, st, k); break;
-            case 1: hipLaunchKernelGGL((scan_kernel<S, 0, false, true>), grid, block, lds, st, k); break;
-            case 2: hipLaunchKernelGGL((scan_kernel<S, 0, true, false>), grid, block, lds, st, k); break;
-            case 3: hipLaunchKernelGGL((scan_kernel<S, 0, true, true>), grid, block, lds, st, k); break;
-            case 4: hipLaunchKernelGGL((scan_kernel<S, 1, false, false>), grid, block, lds, st, k); break;
-            case 5: hipLaunchKernelGGL((scan_kernel<S, 1, false, true>), grid, block, lds, st, k); break;
-            case 6: hipLaunchKernelGGL((scan_kernel<S, 1, true, false>), grid, block, lds, st, k); break;
-            default: hipLaunchKernelGGL((scan_kernel<S, 1, true, true>), grid, block, lds, st, k); break;
-        }
+        launch_scan_inst<SL>(a.form, a.v_bf16, save, a.m_bf16, grid, block, lds, st, k);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
         if (c.P > 1) {
@@ -814,40 +880,49 @@ hipError_t launch_scan_slab(const ScanArgs& a, const Cfg& c, hipStream_t st) {
     return hipSuccess;
 }
 
-template <int S>
+template <int SL>
 hipError_t launch_scan_direct(const ScanArgs& a, hipStream_t st) {
-    const Geom g = make_geom(S, a.W, a.R);
+    const Geom g = make_geom(SL, a.W, a.R);
     DirectArgs d{};
     d.idx_w = a.idx_w; d.wt_w = a.wt_w; d.W = a.W;
     d.idx_r = a.idx_r; d.wt_r = a.wt_r; d.R = a.R;
     d.alpha = a.alpha; d.beta = a.beta; d.v = a.v; d.M = a.M; d.y = a.y;
-    d.T = (int)a.T; d.N = a.N; d.dv = a.dv; d.nslab = a.dv / S; d.NS = a.NS;
+    d.T = (int)a.T; d.N = a.N; d.dv = a.dv; d.nslab = a.dv / (SL / 4 * (a.m_bf16 ? 8 : 4)); d.NS = a.NS;
     d.NWW = g.NWW; d.NWR = g.NWR;
     d.snap = a.snap;
     const int64_t nblk = ((a.NS + 7) / 8) * 8 * d.nslab;
     dim3 grid((unsigned)nblk), block((unsigned)(g.nw() * 64));
-    const int sel = (a.form ? 4 : 0) | (a.v_bf16 ? 2 : 0) | (a.snap ? 1 : 0);
+    const int sel = (a.form ? 8 : 0) | (a.v_bf16 ? 4 : 0) | (a.snap ? 2 : 0) | (a.m_bf16 ? 1 : 0);
     switch (sel) {
-        case 0: hipLaunchKernelGGL((scan_direct_kernel<S, 0, false, false>), grid, block, 0, st, d); break;
-        case 1: hipLaunchKernelGGL((scan_direct_kernel<S, 0, false, true>), grid, block, 0, st, d); break;
-        case 2: hipLaunchKernelGGL((scan_direct_kernel<S, 0, true, false>), grid, block, 0, st, d); break;
-        case 3: hipLaunchKernelGGL((scan_direct_kernel<S, 0, true, true>), grid, block, 0, st, d); break;
-        case 4: hipLaunchKernelGGL((scan_direct_kernel<S, 1, false, false>), grid, block, 0, st, d); break;
-        case 5: hipLaunchKernelGGL((scan_direct_kernel<S, 1, false, true>), grid, block, 0, st, d); break;
-        case 6: hipLaunchKernelGGL((scan_direct_kernel<S, 1, true, false>), grid, block, 0, st, d); break;
-        default: hipLaunchKernelGGL((scan_direct_kernel<S, 1, true, true>), grid, block, 0, st, d); break;
+        case 0: hipLaunchKernelGGL((scan_direct_kernel<SL, 0, false, false, false>), grid, block, 0, st, d); break;
+        case 1: hipLaunchKernelGGL((scan_direct_kernel<SL, 0, false, false, true>), grid, block, 0, st, d); break;
+        case 2: hipLaunchKernelGGL((scan_direct_kernel<SL, 0, false, true, false>), grid, block, 0, st, d); break;
+        case 4: hipLaunchKernelGGL((scan_direct_kernel<SL, 0, true, false, false>), grid, block, 0, st, d); break;
+        case 5: hipLaunchKernelGGL((scan_direct_kernel<SL, 0, true, false, true>), grid, block, 0, st, d); break;
+        case 6: hipLaunchKernelGGL((scan_direct_kernel<SL, 0, true, true, false>), grid, block, 0, st, d); break;
+        case 8: hipLaunchKernelGGL((scan_direct_kernel<SL, 1, false, false, false>), grid, block, 0, st, d); break;
+        case 9: hipLaunchKernelGGL((scan_direct_kernel<SL, 1, false, false, true>), grid, block, 0, st, d); break;
+        case 10: hipLaunchKernelGGL((scan_direct_kernel<SL, 1, false, true, false>), grid, block, 0, st, d); break;
+        case 12: hipLaunchKernelGGL((scan_direct_kernel<SL, 1, true, false, false>), grid, block, 0, st, d); break;
+        case 13: hipLaunchKernelGGL((scan_direct_kernel<SL, 1, true, false, true>), grid, block, 0, st, d); break;
+        case 14: hipLaunchKernelGGL((scan_direct_kernel<SL, 1, true, true, false>), grid, block, 0, st, d); break;
+        default: return hipErrorInvalidValue;  // pre-images of a bf16 table: rejected by the C ABI
     }
     return hipGetLastError();
 }
 
+// Slab widths are named by SL = 4 * (lanes per row segment), which fixes the
+// wavefront layout (G = 64 / (SL / 4) rows per wavefront) and the plan
+// records; a slab holds SL columns of an fp32 table and 2 * SL of a bf16 one
+// (cpl = 4 or 8 columns per 16-byte lane).
 int slab_nwmax(int S) {
     return S == 32 ? SlabCfg<32>::NWMAX : S == 16 ? SlabCfg<16>::NWMAX : S == 8 ? SlabCfg<8>::NWMAX : SlabCfg<4>::NWMAX;
 }
 int slab_nrmax(int S) {
     return S == 32 ? nrmax<32>() : S == 16 ? nrmax<16>() : S == 8 ? nrmax<8>() : nrmax<4>();
 }
-bool slab_fits(int S, int W, int R, int dv) {
-    if (dv % S != 0) return false;
+bool slab_fits(int S, int W, int R, int dv, int cpl) {
+    if (dv % (S / 4 * cpl) != 0) return false;
     const Geom g = make_geom(S, W, R);
     return g.nw() <= slab_nwmax(S) && g.NWR <= slab_nrmax(S);
 }
@@ -860,20 +935,22 @@ int env_int(const char* name) {
 // Slab width without row partitions: among the widths whose groups of G rows
 // tile W and R without padding and that need at most 8 wavefronts (the
 // 16-wavefront form has a shallower pipeline), the widest one that still gives
-// at least 128 workgroups (half the CUs): wider slabs move longer row segments,
-// narrower ones give more independent workgroups. Failing that, the width with
-// the most workgroups, then the one with the least padding. (Measured on the
-// N=65536, W=R=64, d_v=128 shapes: 32 streams -> 16 columns, 8 streams -> 8.)
-int pick_slab(int64_t NS, int W, int R, int dv, int forced) {
+// at least 128 workgroups (half the CUs; 256 for a bf16 table): wider slabs
+// move longer row segments, narrower ones give more independent workgroups.
+// Failing that, the width with the most workgroups, then the one with the least
+// padding. (Measured on the N=65536, W=R=64, d_v=128 shapes: fp32, 32 streams
+// -> 16 columns, 8 streams -> 8; bf16, 32 streams -> 16 columns (SL = 8).)
+int pick_slab(int64_t NS, int W, int R, int dv, int cpl, int forced) {
+    const long enough = cpl == 8 ? 256 : 128;
     struct Cand {
         int S;
         long waste, units;
         int nw;
     };
-    auto better = [](const Cand& a, const Cand& b) {
+    auto better = [enough](const Cand& a, const Cand& b) {
         if ((a.waste == 0) != (b.waste == 0)) return a.waste == 0;
         if ((a.nw <= 8) != (b.nw <= 8)) return a.nw <= 8;
-        const bool ea = a.units >= 128, eb = b.units >= 128;
+        const bool ea = a.units >= enough, eb = b.units >= enough;
         if (ea != eb) return ea;
         if (ea) return a.S > b.S;
         if (a.units != b.units) return a.units > b.units;
@@ -881,9 +958,9 @@ int pick_slab(int64_t NS, int W, int R, int dv, int forced) {
     };
     Cand best{0, 0, 0, 0};
     for (int S : {32, 16, 8, 4}) {
-        if ((forced && forced != S) || !slab_fits(S, W, R, dv)) continue;
+        if ((forced && forced != S) || !slab_fits(S, W, R, dv, cpl)) continue;
         const Geom g = make_geom(S, W, R);
-        const Cand c{S, (long)g.NWW * g.G - W + (long)g.NWR * g.G - R, (long)NS * (dv / S), g.nw()};
+        const Cand c{S, (long)g.NWW * g.G - W + (long)g.NWR * g.G - R, (long)NS * (dv / (S / 4 * cpl)), g.nw()};
         if (best.S == 0 || better(c, best)) best = c;
     }
     return best.S;
@@ -891,28 +968,41 @@ int pick_slab(int64_t NS, int W, int R, int dv, int forced) {
 
 // The per-slot form (EQ4) never couples two rows, so it may split the rows into
 // partitions; then every workgroup reads and writes whole 128-byte lines
-// (32-column slabs) and the partitions supply the workgroups that narrower
-// slabs would: P is the smallest power of two (at most 8) that gives 256
-// workgroups. The per-CU count of outstanding line misses is what bounds the
-// scan, so a line that carries 128 useful bytes instead of 32 or 64 is worth
-// more than the extra padding lanes of a partitioned record. The shared-residual
-// form (FIG2) couples all rows of a token and keeps P = 1.
-// SDM_SCAN_SLAB and SDM_SCAN_PARTS force a width and a partition count.
-Cfg choose_cfg(int64_t NS, int W, int R, int dv, int form) {
+// (8 lanes of 16 bytes per row: 32 fp32 or 64 bf16 columns) and the partitions
+// supply the workgroups that narrower slabs would: P is the smallest power of
+// two (at most 8) that gives 256 workgroups. The per-CU count of outstanding
+// line misses is what bounds the scan, so a line that carries 128 useful bytes
+// instead of 32 or 64 is worth more than the extra padding lanes of a
+// partitioned record. The shared-residual form (FIG2) couples all rows of a
+// token and keeps P = 1.
+// A bf16 table halves the bytes of every access, so its loop is bound by the
+// per-token work of a workgroup rather than by line misses: there the 8-wavefront
+// layouts with their deeper prefetch win. Measured (N=65536, W=R=64, d_v=128):
+// 32 streams -> 32-column slabs (SL = 16), P = 2 (3.9 ms against 4.4 for whole
+// lines at P = 4); 8 streams -> 16-column slabs (SL = 8), P = 8 (512 workgroups:
+// 41 ms against 51 at 256).
+// SDM_SCAN_SLAB (an SL value) and SDM_SCAN_PARTS force a width and a partition count.
+Cfg choose_cfg(int64_t NS, int W, int R, int dv, int form, int cpl) {
     Cfg c;
     const int fs = env_int("SDM_SCAN_SLAB"), fp = env_int("SDM_SCAN_PARTS");
-    if (form == 0 && (fs == 0 || fs == 32) && slab_fits(32, W, R, dv) && fp != 1) {
+    const int64_t ns = NS > 0 ? NS : 1;
+    int want = 256;  // workgroups the partitions should reach
+    if (form == 0 && cpl == 4 && (fs == 0 || fs == 32) && slab_fits(32, W, R, dv, cpl) && fp != 1) {
         c.S = 32;
+    } else if (form == 0 && cpl == 8 && fs == 0 && slab_fits(16, W, R, dv, cpl) && slab_fits(8, W, R, dv, cpl)) {
+        const bool many = ns * (dv / 32) >= 128;
+        c.S = many ? 16 : 8;
+        want = many ? 256 : 512;
     } else {
-        c.S = pick_slab(NS, W, R, dv, fs);
+        c.S = pick_slab(NS, W, R, dv, cpl, fs);
         if (c.S == 0) return c;
     }
     if (form == 0) {
         if (fp == 1 || fp == 2 || fp == 4 || fp == 8) {
             c.P = fp;
         } else {
-            const int64_t units = (NS > 0 ? NS : 1) * (dv / c.S);
-            while (c.P < MAX_PARTS && units * c.P < 256) c.P *= 2;
+            const int64_t units = ns * (dv / (c.S / 4 * cpl));
+            while (c.P < MAX_PARTS && units * c.P < want) c.P *= 2;
         }
     }
     c.g = make_geom(c.S, W, R);
@@ -921,22 +1011,31 @@ Cfg choose_cfg(int64_t NS, int W, int R, int dv, int form) {
 
 }  // namespace
 
-bool scan_geometry(int64_t NS, int W, int R, int dv, int* slab, int* rec) {
+bool scan_geometry(int64_t NS, int W, int R, int dv, bool m_bf16, int* slab, int* rec) {
+    const int cpl = m_bf16 ? 8 : 4;
     for (int form = 0; form < 2; ++form)
-        if (choose_cfg(NS, W, R, dv, form).S == 0) return false;
-    const Cfg c = choose_cfg(NS, W, R, dv, 0);
+        if (choose_cfg(NS, W, R, dv, form, cpl).S == 0) return false;
+    const Cfg c = choose_cfg(NS, W, R, dv, 0, cpl);
     if (slab) *slab = c.S;
     if (rec) *rec = (int)c.g.rec();
     return true;
 }
 
+// The workspace covers both forms and both table dtypes (where a dtype's
+// slabs fit dv), so one size serves every call with these sizes.
 int64_t scan_workspace_bytes(int64_t NS, int64_t T, int W, int R, int dv) {
     int64_t need = 0;
-    for (int form = 0; form < 2; ++form) {
-        const Cfg c = choose_cfg(NS, W, R, dv, form);
-        if (c.S == 0) return -1;
-        const int64_t b = ws_layout(c, NS, chunk_tokens(T, c.g, dv), dv).total;
-        if (b > need) need = b;
+    for (int cpl : {4, 8}) {
+        if (cpl == 8 && dv % 8 != 0) continue;
+        for (int form = 0; form < 2; ++form) {
+            const Cfg c = choose_cfg(NS, W, R, dv, form, cpl);
+            if (c.S == 0) {
+                if (cpl == 4) return -1;
+                continue;
+            }
+            const int64_t b = ws_layout(c, NS, chunk_tokens(T, c.g, dv), dv).total;
+            if (b > need) need = b;
+        }
     }
     return need;
 }
@@ -949,9 +1048,10 @@ int64_t direct_max_tokens() {
 }
 
 hipError_t launch_scan(const ScanArgs& a, hipStream_t st) {
+    const int cpl = a.m_bf16 ? 8 : 4;
     const int64_t per_tok = (int64_t)a.dv * 4 * (a.snap ? (a.W > 1 ? a.W : 1) : 1);
     if (a.T <= direct_max_tokens() && a.T * per_tok < 0x7FFFFFFF) {
-        switch (pick_slab(a.NS, a.W, a.R, a.dv, env_int("SDM_SCAN_SLAB"))) {
+        switch (pick_slab(a.NS, a.W, a.R, a.dv, cpl, env_int("SDM_SCAN_SLAB"))) {
             case 32: return launch_scan_direct<32>(a, st);
             case 16: return launch_scan_direct<16>(a, st);
             case 8: return launch_scan_direct<8>(a, st);
@@ -959,7 +1059,7 @@ hipError_t launch_scan(const ScanArgs& a, hipStream_t st) {
             default: break;
         }
     }
-    const Cfg c = choose_cfg(a.NS, a.W, a.R, a.dv, a.form);
+    const Cfg c = choose_cfg(a.NS, a.W, a.R, a.dv, a.form, cpl);
     switch (c.S) {
         case 32: return launch_scan_slab<32>(a, c, st);
         case 16: return launch_scan_slab<16>(a, c, st);

@@ -159,13 +159,16 @@ int sdm_debug_half_scores_idw(const void* q, int q_dtype, const void* subkeys, i
                             half, stream);
 }
 
-int sdm_state_init(const float* M0, float* M, int64_t B, int64_t H, int64_t N, int64_t dv, void* stream) {
+int sdm_state_init(const float* M0, void* M, int m_dtype, int64_t B, int64_t H, int64_t N, int64_t dv,
+                   void* stream) {
+    if (m_dtype != SDM_F32 && m_dtype != SDM_BF16) return fail(SDM_ERR_DTYPE, "unknown table dtype %d", m_dtype);
     if (B < 0 || H < 0 || N < 1 || dv < 1) return fail(SDM_ERR_SHAPE, "sdm_state_init: invalid sizes");
     if (dv % 4 != 0) return fail(SDM_ERR_UNSUPPORTED, "sdm_state_init: dv must be a multiple of 4");
     if (B == 0 || H == 0) return ok();
     if (!M0 || !M) return fail(SDM_ERR_NULL, "sdm_state_init: NULL pointer");
     if (!aligned16(M0) || !aligned16(M)) return fail(SDM_ERR_ALIGN, "sdm_state_init: pointer not 16-byte aligned");
-    hipError_t e = sdm::launch_state_init(M0, M, B, H * N * dv, static_cast<hipStream_t>(stream));
+    hipError_t e = sdm::launch_state_init(M0, M, m_dtype == SDM_BF16, B, H * N * dv,
+                                          static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "sdm_state_init launch");
     return ok();
 }
@@ -186,8 +189,9 @@ namespace {
 constexpr int NO_WORK = -1;
 int check_scan(const char* fn, const int32_t* idx_w, const float* wt_w, int64_t W, const int32_t* idx_r,
                const float* wt_r, int64_t R, const float* alpha, const float* beta, const void* v, int v_dtype,
-               int64_t B, int64_t H, int64_t T, int64_t N, int64_t dv, int form) {
+               int64_t B, int64_t H, int64_t T, int64_t N, int64_t dv, int form, int m_dtype = SDM_F32) {
     if (v_dtype != SDM_F32 && v_dtype != SDM_BF16) return fail(SDM_ERR_DTYPE, "unknown v dtype %d", v_dtype);
+    if (m_dtype != SDM_F32 && m_dtype != SDM_BF16) return fail(SDM_ERR_DTYPE, "unknown table dtype %d", m_dtype);
     if (form != SDM_DELTA_EQ4 && form != SDM_DELTA_FIG2) return fail(SDM_ERR_DTYPE, "unknown delta form %d", form);
     if (B < 0 || H < 0 || T < 0 || N < 1 || dv < 1) return fail(SDM_ERR_SHAPE, "%s: invalid sizes", fn);
     if (W < 1 || R < 1 || W > N || R > N)
@@ -196,10 +200,13 @@ int check_scan(const char* fn, const int32_t* idx_w, const float* wt_w, int64_t 
     if (W > 256 || R > 256) return fail(SDM_ERR_UNSUPPORTED, "W, R <= 256 on the GPU");
     if (N > (1 << 18)) return fail(SDM_ERR_UNSUPPORTED, "N=%lld: at most 2^18 slots", (long long)N);
     if (dv % 4 != 0) return fail(SDM_ERR_UNSUPPORTED, "dv=%lld must be a multiple of 4", (long long)dv);
+    if (m_dtype == SDM_BF16 && dv % 8 != 0)
+        return fail(SDM_ERR_UNSUPPORTED, "dv=%lld must be a multiple of 8 for a bf16 table", (long long)dv);
     if (N * dv * 4 >= (1ll << 31))
         return fail(SDM_ERR_UNSUPPORTED, "one stream's table (N*dv*4 = %lld bytes) must stay below 2 GiB",
                     (long long)(N * dv * 4));
-    if (!sdm::scan_geometry(B * H > 0 ? B * H : 1, (int)W, (int)R, (int)dv, nullptr, nullptr))
+    if (!sdm::scan_geometry(B * H > 0 ? B * H : 1, (int)W, (int)R, (int)dv, m_dtype == SDM_BF16, nullptr,
+                            nullptr))
         return fail(SDM_ERR_UNSUPPORTED, "no scan kernel covers W=%lld, R=%lld, dv=%lld", (long long)W,
                     (long long)R, (long long)dv);
     if ((B * H + 7) / 8 * 8 * (dv / 4) > 0x7FFFFFFFll)
@@ -231,9 +238,11 @@ int check_workspace(void* workspace, int64_t workspace_bytes, int64_t need) {
 
 int scan_forward_impl(const char* fn, const int32_t* idx_w, const float* wt_w, int64_t W, const int32_t* idx_r,
                       const float* wt_r, int64_t R, const float* alpha, const float* beta, const void* v,
-                      int v_dtype, float* M, float* y, float* snap, bool save, int64_t B, int64_t H, int64_t T,
-                      int64_t N, int64_t dv, int form, void* workspace, int64_t workspace_bytes, void* stream) {
-    int rc = check_scan(fn, idx_w, wt_w, W, idx_r, wt_r, R, alpha, beta, v, v_dtype, B, H, T, N, dv, form);
+                      int v_dtype, void* M, int m_dtype, float* y, float* snap, bool save, int64_t B, int64_t H,
+                      int64_t T, int64_t N, int64_t dv, int form, void* workspace, int64_t workspace_bytes,
+                      void* stream) {
+    int rc = check_scan(fn, idx_w, wt_w, W, idx_r, wt_r, R, alpha, beta, v, v_dtype, B, H, T, N, dv, form,
+                        m_dtype);
     if (rc == NO_WORK) return ok();
     if (rc) return rc;
     if ((rc = check_buffers(fn, {M, y}))) return rc;
@@ -246,7 +255,7 @@ int scan_forward_impl(const char* fn, const int32_t* idx_w, const float* wt_w, i
     a.idx_r = idx_r; a.wt_r = wt_r; a.R = (int)R;
     a.alpha = alpha; a.beta = beta;
     a.v = v; a.v_bf16 = v_dtype == SDM_BF16;
-    a.M = M; a.y = y;
+    a.M = M; a.m_bf16 = m_dtype == SDM_BF16; a.y = y;
     a.NS = B * H; a.T = T; a.N = N; a.dv = (int)dv;
     a.form = form;
     a.workspace = workspace;
@@ -261,11 +270,11 @@ int scan_forward_impl(const char* fn, const int32_t* idx_w, const float* wt_w, i
 extern "C" {
 
 int sdm_scan_forward(const int32_t* idx_w, const float* wt_w, int64_t W, const int32_t* idx_r, const float* wt_r,
-                     int64_t R, const float* alpha, const float* beta, const void* v, int v_dtype, float* M,
-                     float* y, int64_t B, int64_t H, int64_t T, int64_t N, int64_t dv, int form, void* workspace,
-                     int64_t workspace_bytes, void* stream) {
-    return scan_forward_impl("sdm_scan_forward", idx_w, wt_w, W, idx_r, wt_r, R, alpha, beta, v, v_dtype, M, y,
-                             nullptr, false, B, H, T, N, dv, form, workspace, workspace_bytes, stream);
+                     int64_t R, const float* alpha, const float* beta, const void* v, int v_dtype, void* M,
+                     int m_dtype, float* y, int64_t B, int64_t H, int64_t T, int64_t N, int64_t dv, int form,
+                     void* workspace, int64_t workspace_bytes, void* stream) {
+    return scan_forward_impl("sdm_scan_forward", idx_w, wt_w, W, idx_r, wt_r, R, alpha, beta, v, v_dtype, M,
+                             m_dtype, y, nullptr, false, B, H, T, N, dv, form, workspace, workspace_bytes, stream);
 }
 
 int64_t sdm_scan_snapshot_bytes(int64_t B, int64_t H, int64_t T, int64_t W, int64_t dv) {
@@ -278,7 +287,7 @@ int sdm_scan_forward_save(const int32_t* idx_w, const float* wt_w, int64_t W, co
                           int v_dtype, float* M, float* y, float* snap, int64_t B, int64_t H, int64_t T, int64_t N,
                           int64_t dv, int form, void* workspace, int64_t workspace_bytes, void* stream) {
     return scan_forward_impl("sdm_scan_forward_save", idx_w, wt_w, W, idx_r, wt_r, R, alpha, beta, v, v_dtype, M,
-                             y, snap, true, B, H, T, N, dv, form, workspace, workspace_bytes, stream);
+                             SDM_F32, y, snap, true, B, H, T, N, dv, form, workspace, workspace_bytes, stream);
 }
 
 int64_t sdm_scan_backward_workspace_bytes(int64_t B, int64_t H, int64_t T, int64_t W, int64_t R, int64_t dv) {

@@ -62,6 +62,84 @@ struct VLoad<true> {
     }
 };
 
+// v_t of this lane's 8 columns (a lane of a bf16-table row holds 8 columns).
+template <bool BF16>
+struct VLoad8;
+template <>
+struct VLoad8<false> {
+    struct T4 { float4 a, b; };
+    static constexpr int ESZ = 4;
+    __device__ static T4 load(rsrc_t r, uint32_t vo, uint32_t so) { return {ld_f4(r, vo, so), ld_f4(r, vo + 16u, so)}; }
+    __device__ static void f(const T4& x, float4 (&o)[2]) { o[0] = x.a; o[1] = x.b; }
+};
+template <>
+struct VLoad8<true> {
+    using T4 = int4;
+    static constexpr int ESZ = 2;
+    __device__ static T4 load(rsrc_t r, uint32_t vo, uint32_t so) { return ld_i4(r, vo, so); }
+    __device__ static void f(const T4& x, float4 (&o)[2]) {
+        o[0] = VLoad<true>::f(make_int2(x.x, x.y));
+        o[1] = VLoad<true>::f(make_int2(x.z, x.w));
+    }
+};
+// v of a lane's CPL columns as NQ = CPL / 4 float4
+template <bool VBF16, int NQ>
+struct VLoadN;
+template <bool VBF16>
+struct VLoadN<VBF16, 1> {
+    using VL = VLoad<VBF16>;
+    using T = typename VL::T4;
+    static constexpr int ESZ = VL::ESZ;
+    __device__ static T load(rsrc_t r, uint32_t vo, uint32_t so) { return VL::load(r, vo, so); }
+    __device__ static void f(const T& x, float4 (&o)[1]) { o[0] = VL::f(x); }
+};
+template <bool VBF16>
+struct VLoadN<VBF16, 2> {
+    using VL = VLoad8<VBF16>;
+    using T = typename VL::T4;
+    static constexpr int ESZ = VL::ESZ;
+    __device__ static T load(rsrc_t r, uint32_t vo, uint32_t so) { return VL::load(r, vo, so); }
+    __device__ static void f(const T& x, float4 (&o)[2]) { VL::f(x, o); }
+};
+
+// Nearest-even bfloat16 of a finite fp32 value, as its 16 bits.
+__device__ __forceinline__ uint32_t bf16_rne(float f) {
+    const uint32_t u = __float_as_uint(f);
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// A lane's 16-byte piece of a table row: 4 fp32 columns (NQ = 1) or 8
+// bfloat16 columns (NQ = 2), unpacked to NQ float4 for the arithmetic and
+// packed back (bfloat16: rounded to nearest even) for the store. The packed
+// 16 bytes are exactly what the table holds, so they are also what an LDS
+// copy of a written row keeps.
+template <bool MBF16>
+struct RowFmt;
+template <>
+struct RowFmt<false> {
+    static constexpr int NQ = 1, CPL = 4, ESZ = 4;
+    __device__ static void unpack(float4 m, float4 (&x)[1]) { x[0] = m; }
+    __device__ static float4 pack(const float4 (&x)[1]) { return x[0]; }
+};
+template <>
+struct RowFmt<true> {
+    static constexpr int NQ = 2, CPL = 8, ESZ = 2;
+    __device__ static void unpack(float4 m, float4 (&x)[2]) {
+        const uint32_t a = __float_as_uint(m.x), b = __float_as_uint(m.y);
+        const uint32_t c = __float_as_uint(m.z), d = __float_as_uint(m.w);
+        x[0] = make_float4(__uint_as_float(a << 16), __uint_as_float(a & 0xFFFF0000u),
+                           __uint_as_float(b << 16), __uint_as_float(b & 0xFFFF0000u));
+        x[1] = make_float4(__uint_as_float(c << 16), __uint_as_float(c & 0xFFFF0000u),
+                           __uint_as_float(d << 16), __uint_as_float(d & 0xFFFF0000u));
+    }
+    __device__ static float4 pack(const float4 (&x)[2]) {
+        return make_float4(__uint_as_float(bf16_rne(x[0].x) | (bf16_rne(x[0].y) << 16)),
+                           __uint_as_float(bf16_rne(x[0].z) | (bf16_rne(x[0].w) << 16)),
+                           __uint_as_float(bf16_rne(x[1].x) | (bf16_rne(x[1].y) << 16)),
+                           __uint_as_float(bf16_rne(x[1].z) | (bf16_rne(x[1].w) << 16)));
+    }
+};
+
 __device__ __forceinline__ float4 f4_scale(float s, float4 a) {
     return make_float4(s * a.x, s * a.y, s * a.z, s * a.w);
 }

@@ -27,7 +27,8 @@ struct ScanArgs {
     const int32_t* idx_r; const float* wt_r; int R;
     const float* alpha; const float* beta;
     const void* v; bool v_bf16;
-    float* M; float* y;
+    void* M; bool m_bf16;    // table elements: fp32, or bfloat16 (no pre-images then)
+    float* y;
     int64_t NS;              // B*H streams
     int64_t T, N;
     int dv;
@@ -36,7 +37,7 @@ struct ScanArgs {
     float* snap;             // optional [NS][T][W][dv]: pre-image of every write (training forward)
 };
 // Chooses the kernel instance; returns false if no instance covers (W, R, dv).
-bool scan_geometry(int64_t NS, int W, int R, int dv, int* slab, int* rec_bytes);
+bool scan_geometry(int64_t NS, int W, int R, int dv, bool m_bf16, int* slab, int* rec_bytes);
 int64_t scan_workspace_bytes(int64_t NS, int64_t T, int W, int R, int dv);
 hipError_t launch_scan(const ScanArgs& a, hipStream_t st);
 
@@ -62,6 +63,6 @@ bool scan_backward_geometry(int64_t NS, int W, int R, int dv);
 hipError_t launch_scan_backward(const BwdArgs& a, hipStream_t st);
 hipError_t launch_state_init_backward(const float* dM, float* dM0, int64_t B, int64_t per_seq, hipStream_t st);
 
-hipError_t launch_state_init(const float* M0, float* M, int64_t B, int64_t per_seq, hipStream_t st);
+hipError_t launch_state_init(const float* M0, void* M, bool m_bf16, int64_t B, int64_t per_seq, hipStream_t st);
 
 }  // namespace sdm

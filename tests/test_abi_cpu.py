@@ -43,7 +43,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert binding.sdm_abi_version() == 3
+    assert binding.sdm_abi_version() == 4
     assert binding.sdm_status_string(0) == "ok"
     assert binding.sdm_status_string(7).startswith("workspace")
     assert binding.sdm_status_string(99) == "unknown status"
@@ -57,6 +57,8 @@ def test_workspace_size_is_pure_host_logic(lib):
     # two partitions' partial y. The shared-residual form (16-column slabs, one
     # partition) needs less, and the workspace covers both.
     # and the largest per-token count of each (stream, partition, branch)
+    # The workspace also covers a bf16 table (32-column slabs, 2 partitions for
+    # 32 streams; 16-column slabs, 8 partitions for 8): the same sizes here.
     rec = 64 * 16 + 64 * 8
     assert binding.sdm_scan_workspace_bytes(4, 8, 8192, 64, 64, 128) == \
         32 * 2 * 8192 * rec + 2 * 32 * 8192 * 128 * 4 + 32 * 2 * 2 * 4
@@ -92,12 +94,15 @@ def test_address_rejects_bad_arguments_before_launch(lib):
 def test_scan_rejects_bad_arguments_before_launch(lib):
     fake = P(4096)
     base = dict(iw=fake, ww=fake, W=64, ir=fake, wr=fake, R=64, a=fake, b=fake, v=fake, vd=1,
-                M=fake, y=fake, B=1, H=1, T=8, N=65536, dv=128, form=0, ws=fake, wsb=1 << 30,
+                M=fake, md=0, y=fake, B=1, H=1, T=8, N=65536, dv=128, form=0, ws=fake, wsb=1 << 30,
                 st=None)
     call = lambda **kw: lib.sdm_scan_forward(*dict(base, **kw).values())
     assert call(iw=None) == 1
     assert call(iw=None, ww=None, M=None, T=0) == 0                     # empty: valid no-op
     assert call(vd=2) == 3
+    assert call(md=2) == 3                       # unknown table dtype
+    assert call(md=1, dv=132) == 5               # a bf16 table needs dv % 8 == 0
+    assert call(md=1, M=None) == 1
     assert call(form=2) == 3
     assert call(W=65537) == 2                    # W > N
     assert call(N=(1 << 18) + 1, W=64) == 5
@@ -162,10 +167,12 @@ def test_training_calls_reject_bad_arguments_before_launch(lib):
 
 def test_state_init_rejects_bad_arguments(lib):
     fake = P(4096)
-    assert lib.sdm_state_init(None, fake, 1, 1, 16, 16, None) == 1
-    assert lib.sdm_state_init(None, None, 0, 1, 16, 16, None) == 0      # empty: no storage needed
-    assert lib.sdm_state_init(fake, fake, 1, 1, 16, 18, None) == 5
-    assert lib.sdm_state_init(fake, fake, -1, 1, 16, 16, None) == 2
+    assert lib.sdm_state_init(None, fake, 0, 1, 1, 16, 16, None) == 1
+    assert lib.sdm_state_init(None, None, 0, 0, 1, 16, 16, None) == 0   # empty: no storage needed
+    assert lib.sdm_state_init(fake, fake, 0, 1, 1, 16, 18, None) == 5
+    assert lib.sdm_state_init(fake, fake, 1, 1, 1, 16, 18, None) == 5
+    assert lib.sdm_state_init(fake, fake, 0, -1, 1, 16, 16, None) == 2
+    assert lib.sdm_state_init(fake, fake, 3, 1, 1, 16, 16, None) == 3   # unknown table dtype
 
 
 def test_binding_refuses_cpu_tensors(lib):

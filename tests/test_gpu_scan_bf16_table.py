@@ -1,0 +1,210 @@
+"""GPU parity of the scan with a bfloat16 table against the oracle's bf16-table
+scan, through the C ABI.
+
+Both sides get identical indices, weights, gates, values and initial table
+bits. The oracle computes each update in double and rounds it once to
+bfloat16; the GPU computes it in fp32 and rounds that to bfloat16, so an
+element may land one bfloat16 ulp away where the exact value sits next to a
+rounding boundary; such differences then decay with the row. Tolerance: the
+bf16 configuration's 2e-2 (max relative error per vector); most elements
+must also be bit-identical. Rows no token writes stay bit-identical to M0.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_memory_linear_amd as sdm
+from sparse_memory_linear_amd import inputs
+from parity import TOL_BF16, max_rel_err, say
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+FORMS = [("eq4", oracle.EQ4), ("fig2", oracle.FIG2)]
+
+
+def _t(a):
+    return (a if isinstance(a, torch.Tensor) else torch.from_numpy(np.ascontiguousarray(a))).to(DEV)
+
+
+def _run_gpu(idx_w, wt_w, idx_r, wt_r, alpha, beta, v, M_in, form):
+    M = _t(M_in).contiguous().clone()
+    assert M.dtype == torch.bfloat16
+    y = sdm.sdm_scan_forward(_t(idx_w).int(), _t(wt_w).float(), _t(idx_r).int(), _t(wt_r).float(),
+                             _t(alpha).float(), _t(beta).float(), _t(v), M, form)
+    torch.cuda.synchronize()
+    return M.cpu(), y.cpu().numpy()
+
+
+def _check(name, Mg, yg, Mo, yo, M_in, idx_w, min_same=0.99):
+    ey, em = max_rel_err(yg, yo), max_rel_err(Mg.float().numpy(), Mo.float().numpy())
+    same = float((Mg.view(torch.int16) == Mo.view(torch.int16)).float().mean())
+    say(f"  {name}: max rel err y {ey:.2e}, M {em:.2e}; table elements bit-identical {same:.6f}")
+    assert ey <= TOL_BF16 and em <= TOL_BF16
+    assert same >= min_same
+    iw = np.asarray(idx_w)
+    B, H = iw.shape[:2]
+    for b in range(B):
+        for h in range(H):
+            written = np.zeros(M_in.shape[2], bool)
+            written[iw[b, h].reshape(-1)] = True
+            keep = torch.from_numpy(~written)
+            assert torch.equal(Mg[b, h][keep], M_in[b, h][keep])
+
+
+def _random_case(seed, B, H, T, N, dv, W, R, bf16=False):
+    rng = np.random.default_rng(seed)
+    iw = np.stack([rng.permutation(N)[:W] for _ in range(B * H * T)]).reshape(B, H, T, W).astype(np.int32)
+    ir = np.stack([rng.permutation(N)[:R] for _ in range(B * H * T)]).reshape(B, H, T, R).astype(np.int32)
+    ww = rng.dirichlet(np.ones(W), size=(B, H, T)).astype(np.float32)
+    wr = rng.dirichlet(np.ones(R), size=(B, H, T)).astype(np.float32)
+    a = (1 / (1 + np.exp(-rng.normal(2, .5, (B, H, T))))).astype(np.float32)
+    b = (1 / (1 + np.exp(-rng.normal(0, 1, (B, H, T))))).astype(np.float32)
+    v = torch.from_numpy(rng.standard_normal((B, H, T, dv)).astype(np.float32))
+    if bf16:
+        v = v.to(torch.bfloat16)
+    M0 = torch.from_numpy((rng.standard_normal((B, H, N, dv)) * 0.02).astype(np.float32)).to(torch.bfloat16)
+    return dict(idx_w=iw, wt_w=ww, idx_r=ir, wt_r=wr, alpha=a, beta=b, v=v, M_in=M0)
+
+
+CASES = [("tiny", {}), ("tiny_dense", {}), ("small", dict(B=2)),
+         ("gdn_matched", dict(B=1, H=2, T=1000)), ("long_context", dict(H=2, T=3000)),
+         ("large_table", dict(T=1500))]
+
+
+@pytest.mark.parametrize("name,over", CASES, ids=[c[0] for c in CASES])
+@pytest.mark.parametrize("form,oform", FORMS, ids=["eq4", "fig2"])
+def test_bf16_table_scan_matches_oracle(name, over, form, oform):
+    say(f"[bf16 table scan] {name} {over} form={form}")
+    wl = inputs.get(name, **over)
+    x = inputs.make_inputs(wl)
+    iw, ww, _, _ = oracle.address(x["q_w"], x["subkeys"], wl.W)
+    ir, wr, _, _ = oracle.address(x["q_r"], x["subkeys"], wl.R)
+    M_in = torch.from_numpy(oracle.broadcast_state(x["M0"], wl.B).copy()).to(torch.bfloat16)
+    Mo, yo = oracle.scan_bf16(iw, ww, ir, wr, x["alpha"], x["beta"], x["v"], M_in, oform)
+    Mg, yg = _run_gpu(iw, ww, ir, wr, x["alpha"], x["beta"], x["v"], M_in, form)
+    _check(name, Mg, yg, Mo, yo, M_in, iw)
+
+
+HAZARD = [
+    dict(B=1, H=3, T=700, N=256, dv=128, W=64, R=64, bf16=True),
+    dict(B=2, H=1, T=400, N=64, dv=32, W=16, R=16),
+    dict(B=1, H=1, T=300, N=16, dv=512, W=8, R=8),
+    dict(B=1, H=2, T=500, N=300, dv=16, W=200, R=256),
+]
+
+
+@pytest.mark.parametrize("case", HAZARD, ids=[f"N{c['N']}W{c['W']}dv{c['dv']}" for c in HAZARD])
+@pytest.mark.parametrize("form,oform", FORMS, ids=["eq4", "fig2"])
+def test_bf16_table_hazard_stress(case, form, oform):
+    """Heavy row reuse: forwarded rows must be the stored (rounded) values."""
+    say(f"[bf16 table hazards] {case} form={form}")
+    c = _random_case(1, **case)
+    Mo, yo = oracle.scan_bf16(**c, form=oform)
+    Mg, yg = _run_gpu(**c, form=form)
+    _check("hazard", Mg, yg, Mo, yo, c["M_in"], c["idx_w"], min_same=0.98)
+
+
+SWEEP = [(32, 1), (32, 2), (32, 4), (32, 8), (16, 2), (16, 8), (8, 4), (4, 8)]
+
+
+@pytest.mark.parametrize("slab,parts", SWEEP, ids=[f"SL{s}P{p}" for s, p in SWEEP])
+def test_bf16_table_slabs_and_row_partitions(slab, parts, monkeypatch):
+    monkeypatch.setenv("SDM_SCAN_SLAB", str(slab))
+    monkeypatch.setenv("SDM_SCAN_PARTS", str(parts))
+    say(f"[bf16 table slab/partitions] SL={slab} P={parts}")
+    for case in (HAZARD[0], dict(B=2, H=1, T=300, N=64, dv=64, W=16, R=16),
+                 dict(B=1, H=2, T=77, N=4096, dv=128, W=64, R=32)):
+        if case["dv"] % (2 * slab):
+            continue
+        c = _random_case(7, **case)
+        Mo, yo = oracle.scan_bf16(**c, form=oracle.EQ4)
+        Mg, yg = _run_gpu(**c, form="eq4")
+        _check(f"SL={slab} P={parts} N={case['N']}", Mg, yg, Mo, yo, c["M_in"], c["idx_w"], min_same=0.98)
+        M2, y2 = _run_gpu(**c, form="eq4")
+        assert torch.equal(M2, Mg) and np.array_equal(y2, yg)
+
+
+@pytest.mark.parametrize("case", HAZARD[:3] + [dict(B=8, H=2, T=40, N=4096, dv=128, W=64, R=64, bf16=True)],
+                         ids=[f"N{c['N']}W{c['W']}dv{c['dv']}" for c in HAZARD[:3]] + ["N4096dv128"])
+@pytest.mark.parametrize("form,oform", FORMS, ids=["eq4", "fig2"])
+def test_bf16_table_direct_short_scan(case, form, oform, monkeypatch):
+    """The planner-free short-call form (decoding), forced for whole sequences."""
+    monkeypatch.setenv("SDM_SCAN_DIRECT_T", "100000")
+    say(f"[bf16 table direct] {case} form={form}")
+    c = _random_case(5, **case)
+    Mo, yo = oracle.scan_bf16(**c, form=oform)
+    Mg, yg = _run_gpu(**c, form=form)
+    _check("direct", Mg, yg, Mo, yo, c["M_in"], c["idx_w"], min_same=0.98)
+
+
+@pytest.mark.parametrize("T", [1, 2, 7, 13, 61])
+def test_bf16_table_short_and_ragged(T):
+    for case in (dict(B=3, H=1, N=128, dv=128, W=64, R=64), dict(B=1, H=5, N=64, dv=64, W=16, R=16)):
+        c = _random_case(T, T=T, **case)
+        for form, oform in FORMS:
+            Mo, yo = oracle.scan_bf16(**c, form=oform)
+            Mg, yg = _run_gpu(**c, form=form)
+            _check(f"T={T} {form}", Mg, yg, Mo, yo, c["M_in"], c["idx_w"], min_same=0.98)
+
+
+def test_bf16_table_deterministic_split_and_decode_loop():
+    c = _random_case(3, B=2, H=2, T=300, N=512, dv=128, W=64, R=64, bf16=True)
+    for form in ("eq4", "fig2"):
+        M1, y1 = _run_gpu(**c, form=form)
+        M2, y2 = _run_gpu(**c, form=form)
+        assert torch.equal(M1, M2) and np.array_equal(y1, y2)
+        t1 = 113
+        first = {k: (v[:, :, :t1] if k != "M_in" else v) for k, v in c.items()}
+        Ma, ya = _run_gpu(**first, form=form)
+        second = {k: (v[:, :, t1:] if k != "M_in" else Ma) for k, v in c.items()}
+        Mb, yb = _run_gpu(**second, form=form)
+        assert torch.equal(Mb, M1) and np.array_equal(np.concatenate([ya, yb], 2), y1)
+    # one token per call (the direct form) against the oracle over the sequence
+    Mo, yo = oracle.scan_bf16(**c, form=oracle.EQ4)
+    M = _t(c["M_in"]).clone()
+    ys = []
+    for k in range(c["idx_w"].shape[2]):
+        sl = lambda a: _t(a)[:, :, k:k + 1].contiguous()
+        ys.append(sdm.sdm_scan_forward(sl(c["idx_w"]).int(), sl(c["wt_w"]).float(), sl(c["idx_r"]).int(),
+                                       sl(c["wt_r"]).float(), sl(c["alpha"]).float(), sl(c["beta"]).float(),
+                                       sl(c["v"]), M, "eq4"))
+    torch.cuda.synchronize()
+    _check("decode loop", M.cpu(), torch.cat(ys, 2).cpu().numpy(), Mo, yo, c["M_in"], c["idx_w"], min_same=0.98)
+
+
+def test_state_init_rounds_M0_to_bf16():
+    M0 = torch.randn(3, 1000, 64)
+    M0[0, 0, :4] = torch.tensor([1 + 2 ** -8, 1 + 3 * 2 ** -8, -(2 + 2 ** -7), 5 * 2.0 ** -136])
+    M = sdm.sdm_state_init(M0.to(DEV), 5, dtype=torch.bfloat16).cpu()
+    ref = M0.to(torch.bfloat16)
+    assert M.dtype == torch.bfloat16 and all(torch.equal(M[b], ref) for b in range(5))
+
+
+def test_bf16_table_full_pipeline_full_size_sampled_streams():
+    """The benchmark's bf16-table configuration at full size (gdn_matched:
+    state init into bf16, addressing, scan); the sampled streams take the
+    oracle's own slots and weights and are checked in full."""
+    wl = inputs.get("gdn_matched")
+    streams = [(0, 0), (2, 5)]
+    say(f"[bf16 table pipeline full size] B={wl.B} H={wl.H} T={wl.T} streams={streams}")
+    x = inputs.make_inputs(wl)
+    g = {k: v.to(DEV) for k, v in x.items()}
+    iw, ww, ir, wr = sdm.sdm_address(g["q_w"], g["q_r"], g["subkeys"], g["subkeys"], wl.W, wl.R)
+    orc = {}
+    for (b, h) in streams:
+        q = lambda k: x[k][b:b + 1, h:h + 1]
+        oi, ow, _, _ = oracle.address(q("q_w"), x["subkeys"][h:h + 1], wl.W)
+        ri, rw, _, _ = oracle.address(q("q_r"), x["subkeys"][h:h + 1], wl.R)
+        orc[(b, h)] = (oi, ow, ri, rw)
+        for dst, src in ((iw, oi), (ww, ow), (ir, ri), (wr, rw)):
+            dst[b, h] = torch.from_numpy(src[0, 0]).to(DEV)
+    M = sdm.sdm_state_init(g["M0"], wl.B, dtype=torch.bfloat16)
+    y = sdm.sdm_scan_forward(iw, ww, ir, wr, g["alpha"], g["beta"], g["v"], M, "eq4")
+    torch.cuda.synchronize()
+    for (b, h) in streams:
+        sl = lambda t: t[b:b + 1, h:h + 1].cpu()
+        oi, ow, ri, rw = orc[(b, h)]
+        M_in = x["M0"][h:h + 1][None].to(torch.bfloat16)
+        Mo, yo = oracle.scan_bf16(oi, ow, ri, rw, sl(x["alpha"]), sl(x["beta"]), sl(x["v"]), M_in, oracle.EQ4)
+        _check(f"stream ({b},{h})", sl(M), sl(y).numpy(), Mo, yo, M_in, oi)
