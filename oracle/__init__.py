@@ -51,10 +51,13 @@ def _load():
                                     I64, I64, I64, I64, I64, I, I]
         lib.oracle_scan_bf16.argtypes = [P, P, I64, P, P, I64, P, P, P, P, P,
                                          I64, I64, I64, I64, I64, I, I]
+        lib.oracle_gates.argtypes = [P, P, P, P, P, I64, I64, I64, I64, P, P, I]
+        lib.oracle_output_gate.argtypes = [P, P, P, ctypes.c_double, I64, I64, I64, I64, P, I]
         lib.oracle_scan_backward.argtypes = [P, P, I64, P, P, I64, P, P, P, P, P, P,
                                              P, P, P, P, P, P, I64, I64, I64, I64, I64, I, I]
         for f in (lib.oracle_half_scores, lib.oracle_half_scores_idw, lib.oracle_select,
-                  lib.oracle_scan, lib.oracle_scan_bf16, lib.oracle_scan_backward):
+                  lib.oracle_scan, lib.oracle_scan_bf16, lib.oracle_scan_backward,
+                  lib.oracle_gates, lib.oracle_output_gate):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -222,6 +225,31 @@ def scan_backward(idx_w, wt_w, idx_r, wt_r, alpha, beta, v, M_in, dy, dM_out=Non
         _p(out["dwt_w"]), _p(out["dwt_r"]), _p(out["dM_in"]), B, H, T, N, dv, form,
         nthreads or default_threads()), "scan_backward")
     return out
+
+
+def gates(x, W_a, W_b, b_dt, A, nthreads: Optional[int] = None) -> Tuple[np.ndarray, np.ndarray]:
+    """alpha, beta [B,H,T] from the layer input x [B,T,d] (SDM notes §2.4):
+    alpha = exp(-A softplus(W_a x + b_dt)), beta = sigmoid(W_b x); W_a, W_b [H,d];
+    b_dt, A [H]."""
+    x = _f32(x); Wa = _f32(W_a); Wb = _f32(W_b); bd = _f32(b_dt); Af = _f32(A)
+    B, T, d = x.shape
+    H = Wa.shape[0]
+    assert Wa.shape == (H, d) and Wb.shape == (H, d) and bd.shape == (H,) and Af.shape == (H,)
+    al = np.empty((B, H, T), np.float32); be = np.empty((B, H, T), np.float32)
+    _check(_load().oracle_gates(_p(x), _p(Wa), _p(Wb), _p(bd), _p(Af), B, T, d, H, _p(al), _p(be),
+                                nthreads or default_threads()), "gates")
+    return al, be
+
+
+def output_gate(y, gamma, g, eps: float, nthreads: Optional[int] = None) -> np.ndarray:
+    """o = y / sqrt(mean(y^2) + eps) * gamma[h] * sigmoid(g), per row of y [B,H,T,dv]."""
+    yy = _f32(y); gm = _f32(gamma); gg = _f32(g)
+    B, H, T, dv = yy.shape
+    assert gm.shape == (H, dv) and gg.shape == yy.shape
+    o = np.empty_like(yy)
+    _check(_load().oracle_output_gate(_p(yy), _p(gm), _p(gg), float(eps), B, H, T, dv, _p(o),
+                                      nthreads or default_threads()), "output_gate")
+    return o
 
 
 def broadcast_state(M0, B: int) -> np.ndarray:

@@ -531,3 +531,77 @@ int oracle_scan_backward(const int32_t* idx_w, const float* wt_w, int64_t W,
     parallel_for(bwd_item, &c, B * H, nthreads);
     return 0;
 }
+
+/* ------------------------------------------------------------------ */
+/* Glue either side of the scan [SDM §2.4]: the per-head scalar gates   */
+/*   alpha_t = exp(-A softplus(W_a x_t + b_dt)),  beta_t = sigma(W_b x_t) */
+/* and, after the read, the per-head RMS-Norm with an elementwise       */
+/* output gate (reading: o = y / sqrt(mean(y^2) + eps) * gamma *         */
+/* sigmoid(g), the gate's activation being the sigmoid FwPKM §2.3 uses). */
+/* ------------------------------------------------------------------ */
+typedef struct {
+    const float *x, *Wa, *Wb, *bdt, *A;
+    int64_t T, d, H;
+    float *alpha, *beta;
+} gates_ctx;
+
+static double softplus(double z) {    /* log(1 + e^z), without overflow for large z */
+    return z > 0.0 ? z + log1p(exp(-z)) : log1p(exp(z));
+}
+
+static void gates_item(void* p, int64_t bt) {   /* bt = b*T + t: one token, all heads */
+    gates_ctx* c = (gates_ctx*)p;
+    int64_t b = bt / c->T, t = bt % c->T;
+    const float* xt = c->x + bt * c->d;
+    for (int64_t h = 0; h < c->H; ++h) {
+        double za = 0.0, zb = 0.0;
+        for (int64_t i = 0; i < c->d; ++i) {
+            za += (double)c->Wa[h * c->d + i] * (double)xt[i];
+            zb += (double)c->Wb[h * c->d + i] * (double)xt[i];
+        }
+        za += (double)c->bdt[h];
+        int64_t o = (b * c->H + h) * c->T + t;    /* [B, H, T] */
+        c->alpha[o] = (float)exp(-(double)c->A[h] * softplus(za));
+        c->beta[o] = (float)(1.0 / (1.0 + exp(-zb)));
+    }
+}
+
+int oracle_gates(const float* x, const float* W_a, const float* W_b, const float* b_dt,
+                 const float* A, int64_t B, int64_t T, int64_t d, int64_t H,
+                 float* alpha, float* beta, int nthreads) {
+    if (!x || !W_a || !W_b || !b_dt || !A || !alpha || !beta) return -1;
+    if (B < 0 || T < 0 || d < 1 || H < 1) return -2;
+    gates_ctx c = {x, W_a, W_b, b_dt, A, T, d, H, alpha, beta};
+    parallel_for(gates_item, &c, B * T, nthreads);
+    return 0;
+}
+
+typedef struct {
+    const float *y, *gamma, *g;
+    double eps;
+    int64_t H, T, dv;
+    float* o;
+} outg_ctx;
+
+static void outg_item(void* p, int64_t bht) {   /* one (b, h, t) row of d_v values */
+    outg_ctx* c = (outg_ctx*)p;
+    int64_t h = (bht / c->T) % c->H;
+    const float* yr = c->y + bht * c->dv;
+    const float* gr = c->g + bht * c->dv;
+    double ss = 0.0;
+    for (int64_t i = 0; i < c->dv; ++i) ss += (double)yr[i] * (double)yr[i];
+    double r = 1.0 / sqrt(ss / (double)c->dv + c->eps);
+    for (int64_t i = 0; i < c->dv; ++i) {
+        double gate = 1.0 / (1.0 + exp(-(double)gr[i]));
+        c->o[bht * c->dv + i] = (float)((double)yr[i] * r * (double)c->gamma[h * c->dv + i] * gate);
+    }
+}
+
+int oracle_output_gate(const float* y, const float* gamma, const float* g, double eps,
+                       int64_t B, int64_t H, int64_t T, int64_t dv, float* o, int nthreads) {
+    if (!y || !gamma || !g || !o) return -1;
+    if (B < 0 || H < 1 || T < 0 || dv < 1 || !(eps >= 0.0)) return -2;
+    outg_ctx c = {y, gamma, g, eps, H, T, dv, o};
+    parallel_for(outg_item, &c, B * H * T, nthreads);
+    return 0;
+}

@@ -13,7 +13,7 @@
  *           and the worked counter-example, §2.1 Eq. (2) gated delta rule.
  *   [FwPKM] "Fast-weight Product Key Memory：中文精读笔记", §2.2
  *           (per-half top-k, k^2 candidates, softmax over the selection;
- *           the inverse-distance subkey score).
+ *           the inverse-distance subkey score), §2.3 (the sigmoid gate).
  *
  * Conventions: all arrays are host memory, row-major and contiguous, fp32 for
  * every floating-point tensor (bf16 inputs are widened exactly by the
@@ -92,6 +92,22 @@ int oracle_scan_backward(const int32_t* idx_w, const float* wt_w, int64_t W,
                          float* dv_, float* dalpha, float* dbeta, float* dwt_w, float* dwt_r,
                          float* dM_in, int64_t B, int64_t H, int64_t T, int64_t N, int64_t dv,
                          int form, int nthreads);
+
+/* Gates of the scan from the layer input ([SDM] §2.4, the definitions under
+ * Eq. (3)-(4)): per token and head, with sums in double,
+ *   alpha[b,h,t] = fp32( exp(-A[h] * softplus(sum_i W_a[h,i] x[b,t,i] + b_dt[h])) )
+ *   beta[b,h,t]  = fp32( sigmoid(sum_i W_b[h,i] x[b,t,i]) )
+ * x [B,T,d], W_a and W_b [H,d], b_dt and A [H]; alpha, beta [B,H,T]. */
+int oracle_gates(const float* x, const float* W_a, const float* W_b, const float* b_dt,
+                 const float* A, int64_t B, int64_t T, int64_t d, int64_t H,
+                 float* alpha, float* beta, int nthreads);
+
+/* The per-head output after the read ([SDM] §2.4: RMS-Norm, then an
+ * elementwise output gate; the gate's activation is read as the sigmoid of
+ * [FwPKM] §2.3): o = fp32( y / sqrt(mean_i y_i^2 + eps) * gamma[h] * sigmoid(g) )
+ * per row, in double. y, g, o [B,H,T,dv]; gamma [H,dv]. */
+int oracle_output_gate(const float* y, const float* gamma, const float* g, double eps,
+                       int64_t B, int64_t H, int64_t T, int64_t dv, float* o, int nthreads);
 
 int oracle_version(void);
 

@@ -130,6 +130,45 @@ def make_inputs(wl: Workload, seed: Optional[int] = None) -> Dict[str, torch.Ten
             "M0": M0.contiguous()}
 
 
+def d_model(wl: Workload) -> int:
+    """Model width d of the layer around the path: d = H * d_v, the relation of
+    the SDM notes' own configuration (§2.8: d = 1920 with H = 2, d_v = 960)."""
+    return wl.H * wl.d_v
+
+
+def make_glue_inputs(wl: Workload, d: Optional[int] = None, seed: Optional[int] = None
+                     ) -> Dict[str, torch.Tensor]:
+    """Inputs of the glue either side of the scan (own generator, seed + 1000, so
+    the scan inputs above are unchanged). Draw order (fp32 draws):
+
+    1. x ``[B, T, d]`` ~ N(0, 1)                       (layer input)
+    2. W_a ``[H, d]``, 3. W_b ``[H, d]`` ~ N(0, 1/d)   (gate projections)
+    4. b_dt ``[H]`` = -2.5 + 0.1 N(0, 1)               (mean alpha ~ 0.9)
+    5. A ``[H]`` = exp(0.1 N(0, 1))                    (positive decay rates)
+    6. g ``[B, H, T, d_v]`` ~ N(0, 1)                  (output-gate pre-activation)
+    7. gamma ``[H, d_v]`` = 1 + 0.1 N(0, 1)            (RMS-Norm scale)
+
+    x, W_a, W_b and g are rounded to bf16 where the workload's inputs are bf16.
+    """
+    d = d_model(wl) if d is None else d
+    g = torch.Generator(device="cpu")
+    g.manual_seed((wl.seed if seed is None else seed) + 1000)
+    B, H, T, dv = wl.B, wl.H, wl.T, wl.d_v
+    f32 = torch.float32
+    x = torch.randn((B, T, d), generator=g, dtype=f32)
+    W_a = torch.randn((H, d), generator=g, dtype=f32) / d ** 0.5
+    W_b = torch.randn((H, d), generator=g, dtype=f32) / d ** 0.5
+    b_dt = -2.5 + 0.1 * torch.randn((H,), generator=g, dtype=f32)
+    A = torch.exp(0.1 * torch.randn((H,), generator=g, dtype=f32))
+    gate = torch.randn((B, H, T, dv), generator=g, dtype=f32)
+    gamma = 1.0 + 0.1 * torch.randn((H, dv), generator=g, dtype=f32)
+    if wl.bf16_inputs:
+        x, W_a, W_b, gate = (t.to(torch.bfloat16) for t in (x, W_a, W_b, gate))
+    return {"x": x.contiguous(), "W_a": W_a.contiguous(), "W_b": W_b.contiguous(),
+            "b_dt": b_dt.contiguous(), "A": A.contiguous(), "g": gate.contiguous(),
+            "gamma": gamma.contiguous()}
+
+
 def input_recipe(wl: Workload) -> Dict[str, object]:
     """Plain description of a workload's input recipe (for result records)."""
     d = dataclasses.asdict(wl)
