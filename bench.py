@@ -45,6 +45,9 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=20.0,
                    help="target CPU time of the oracle baseline sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--glue", action="store_true",
+                   help="layer step: gates from the layer input, then addressing and scan, then the "
+                        "per-head RMS-Norm and output gate")
     p.add_argument("--train", action="store_true",
                    help="training step: addressing, forward with pre-images, backward with undo")
     p.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
@@ -78,7 +81,7 @@ def measured_traffic():
     return None
 
 
-def cpu_baseline(wl, x, target_s: float, scoring: str = "dot", table: str = "f32"):
+def cpu_baseline(wl, x, target_s: float, scoring: str = "dot", table: str = "f32", gx=None):
     """The oracle as it is (addressing of both branches + scan) on a bounded
     sample of the same workload: the first B' sequences with all H heads, or
     the first T' tokens of one sequence when a whole one already exceeds the
@@ -91,15 +94,20 @@ def cpu_baseline(wl, x, target_s: float, scoring: str = "dot", table: str = "f32
     def run(nb, Tp):
         sl = lambda t: t[:nb, :, :Tp].contiguous()
         t0 = time.perf_counter()
+        al, be = sl(x["alpha"]), sl(x["beta"])
+        if gx is not None:
+            al, be = oracle.gates(gx["x"][:nb, :Tp].contiguous(), gx["W_a"], gx["W_b"], gx["b_dt"], gx["A"], nthreads)
         iw, ww, _, _ = oracle.address(sl(x["q_w"]), x["subkeys"], wl.W, nthreads, scoring)
         ir, wr, _, _ = oracle.address(sl(x["q_r"]), x["subkeys"], wl.R, nthreads, scoring)
         M_in = oracle.broadcast_state(x["M0"].numpy(), nb)
         if table == "bf16":
             import torch
-            oracle.scan_bf16(iw, ww, ir, wr, sl(x["alpha"]), sl(x["beta"]), sl(x["v"]),
-                             torch.from_numpy(M_in.copy()).to(torch.bfloat16), oracle.EQ4, nthreads)
+            _, y = oracle.scan_bf16(iw, ww, ir, wr, al, be, sl(x["v"]),
+                                    torch.from_numpy(M_in.copy()).to(torch.bfloat16), oracle.EQ4, nthreads)
         else:
-            oracle.scan(iw, ww, ir, wr, sl(x["alpha"]), sl(x["beta"]), sl(x["v"]), M_in, oracle.EQ4, nthreads)
+            _, y = oracle.scan(iw, ww, ir, wr, al, be, sl(x["v"]), M_in, oracle.EQ4, nthreads)
+        if gx is not None:
+            oracle.output_gate(y, gx["gamma"], sl(gx["g"]), 1e-6, nthreads)
         return time.perf_counter() - t0
 
     # two calibration points separate the per-call fixed cost from the per-token cost
@@ -114,7 +122,8 @@ def cpu_baseline(wl, x, target_s: float, scoring: str = "dot", table: str = "f32
     ts = run(nb, Tp) if (nb, Tp) != (1, T2) else t2
     return {"value": nb * Tp / ts, "unit": "tokens/s", "cores": nthreads, "kind": "oracle",
             "sample": f"{nb} of {wl.B} sequences of {wl.name}, all {wl.H} heads, first {Tp} of "
-                      f"{wl.T} tokens ({scoring} addressing of both branches + EQ4 scan, {table} table), "
+                      f"{wl.T} tokens ({'gates + ' if gx is not None else ''}{scoring} addressing of both "
+                      f"branches + EQ4 scan, {table} table{' + output gate' if gx is not None else ''}), "
                       f"{ts:.1f} s wall",
             "host_cpu": host_cpu()}
 
@@ -335,25 +344,36 @@ def main():
     y = torch.empty((B, H, T, dv), dtype=torch.float32, device=dev)
     ws = torch.empty((sdm.sdm_scan_workspace_bytes(B, H, T, W, R, dv),), dtype=torch.uint8, device=dev)
     ev = lambda: torch.cuda.Event(enable_timing=True)
+    if a.glue:
+        gx = {k: v.to(dev) for k, v in inputs.make_glue_inputs(wl).items()}
+        gates_out = (torch.empty((B, H, T), dtype=torch.float32, device=dev),
+                     torch.empty((B, H, T), dtype=torch.float32, device=dev))
+        o = torch.empty((B, H, T, dv), dtype=torch.float32, device=dev)
+    NM = 6 if a.glue else 4
 
     def step(marks=None):
-        if marks:
-            marks[0].record()
+        rec = (lambda i: marks[i].record()) if marks else (lambda i: None)
+        rec(0)
         sdm.sdm_state_init(g["M0"], B, out=M)
-        if marks:
-            marks[1].record()
+        rec(1)
+        if a.glue:
+            al, be = sdm.sdm_gates(gx["x"], gx["W_a"], gx["W_b"], gx["b_dt"], gx["A"], out=gates_out)
+            rec(4)
+        else:
+            al, be = g["alpha"], g["beta"]
         iw, ww, ir, wr = sdm.sdm_address(g["q_w"], g["q_r"], g["subkeys"], g["subkeys"], W, R, out=addr_out,
                                          scoring=a.scoring)
-        if marks:
-            marks[2].record()
-        sdm.sdm_scan_forward(iw, ww, ir, wr, g["alpha"], g["beta"], g["v"], M, a.form, y=y, workspace=ws)
-        if marks:
-            marks[3].record()
+        rec(2)
+        sdm.sdm_scan_forward(iw, ww, ir, wr, al, be, g["v"], M, a.form, y=y, workspace=ws)
+        rec(3)
+        if a.glue:
+            sdm.sdm_output_gate(y, gx["gamma"], gx["g"], 1e-6, out=o)
+            rec(5)
 
     for _ in range(a.warmup):
         step()
     torch.cuda.synchronize()
-    marks = [[ev() for _ in range(4)] for _ in range(a.steps)]
+    marks = [[ev() for _ in range(NM)] for _ in range(a.steps)]
     t0 = time.perf_counter()
     for i in range(a.steps):
         step(marks[i])
@@ -361,8 +381,22 @@ def main():
     wall = time.perf_counter() - t0
     ms_step = 1e3 * wall / a.steps
     init_ms = sum(m[0].elapsed_time(m[1]) for m in marks) / a.steps
-    addr_ms = sum(m[1].elapsed_time(m[2]) for m in marks) / a.steps
+    addr_ms = sum(m[4 if a.glue else 1].elapsed_time(m[2]) for m in marks) / a.steps
     scan_ms = sum(m[2].elapsed_time(m[3]) for m in marks) / a.steps
+    breakdown = {"state_init": init_ms, "address": addr_ms, "scan": scan_ms}
+    glue = None
+    if a.glue:
+        gates_ms = sum(m[1].elapsed_time(m[4]) for m in marks) / a.steps
+        out_ms = sum(m[3].elapsed_time(m[5]) for m in marks) / a.steps
+        breakdown.update(gates=gates_ms, output_gate=out_ms)
+        dm = inputs.d_model(wl)
+        xb = 2 if wl.bf16_inputs else 4
+        gate_bytes = B * T * dm * xb + 2 * B * H * T * 4          # x in, alpha and beta out
+        out_bytes = B * H * T * dv * (4 + xb + 4)                   # y and g in, o out
+        glue = {"d_model": dm,
+                "gates_GBps": gate_bytes / (gates_ms * 1e-3) / 1e9,
+                "gates_mfma_TFLOPs": 2 * B * T * dm * 2 * H / (gates_ms * 1e-3) / 1e12,
+                "output_gate_GBps": out_bytes / (out_ms * 1e-3) / 1e9}
 
     row_bytes = B * H * T * (2 * W + R) * dv * esz
     scan_gbps = row_bytes / (scan_ms * 1e-3) / 1e9
@@ -383,7 +417,7 @@ def main():
                    "d_v": dv, "d_h": wl.d_h, "form": a.form, "scoring": a.scoring, "table": a.table,
                    "inputs": (f"bf16 q/v/subkeys, {a.table} table, fp32 gates" if wl.bf16_inputs
                               else f"fp32 inputs, {a.table} table")},
-        "breakdown_ms": {"state_init": init_ms, "address": addr_ms, "scan": scan_ms},
+        "breakdown_ms": breakdown,
         # the half-score contraction of both branches: 2 halves x n_sub x d_h MACs per token-branch
         "address_mfma_TFLOPs": 2 * B * H * T * 2 * (2 * wl.n_sub * wl.d_h) / (addr_ms * 1e-3) / 1e12,
         "scan_tokens_per_s": B * T / (scan_ms * 1e-3),
@@ -395,8 +429,12 @@ def main():
                      "kernel": "sdm_scan_forward (plan_kernel + scan_kernel + ypart_reduce)",
                      "algorithmic_bytes_per_launch": row_bytes},
     }
+    if glue:
+        rec["glue"] = glue
+        rec["config"]["mode"] = "layer (gates + addressing + scan + output gate)"
     if not a.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(wl, x, a.cpu_seconds, a.scoring, a.table)
+        rec["cpu_baseline"] = cpu_baseline(wl, x, a.cpu_seconds, a.scoring, a.table,
+                                           inputs.make_glue_inputs(wl) if a.glue else None)
     print(json.dumps(rec), flush=True)
 
 

@@ -32,7 +32,7 @@
 extern "C" {
 #endif
 
-#define SDM_ABI_VERSION 4
+#define SDM_ABI_VERSION 5
 
 typedef enum sdm_status {
     SDM_OK = 0,
@@ -258,6 +258,36 @@ int sdm_scan_backward(const int32_t* idx_w, const float* wt_w, int64_t W,
  */
 int sdm_state_init_backward(const float* dM, float* dM0, int64_t B, int64_t H, int64_t N,
                             int64_t dv, void* stream);
+
+/*
+ * The steps either side of the scan ([SDM] §2.4).
+ *
+ * sdm_gates -- the scan's per-head scalar gates from the layer input:
+ *   alpha[b,h,t] = exp(-A[h] * softplus(<W_a[h,:], x[b,t,:]> + b_dt[h]))
+ *   beta[b,h,t]  = sigmoid(<W_b[h,:], x[b,t,:]>)
+ * The projections of all heads are one MFMA contraction over d with fp32
+ * accumulation (bf16 or fp32 operands); softplus, exp and sigmoid in fp32.
+ *   x [B, T, d] x_dtype; W_a, W_b [H, d] w_dtype == x_dtype; b_dt, A [H] fp32;
+ *   alpha, beta [B, H, T] fp32 (out): the layout sdm_scan_forward reads.
+ * Supported: d a multiple of 32 (bf16) or 8 (fp32) up to 2^20, H <= 4096.
+ */
+int sdm_gates(const void* x, int x_dtype, const void* W_a, const void* W_b, int w_dtype,
+              const float* b_dt, const float* A, int64_t B, int64_t T, int64_t d, int64_t H,
+              float* alpha, float* beta, void* stream);
+
+/*
+ * sdm_output_gate -- each head's output after the read: RMS-Norm of the row
+ * y[b,h,t,:], then the elementwise output gate; the gate's activation is taken
+ * to be the sigmoid ([FwPKM] §2.3's output gate; the SDM notes name the gate
+ * without its activation):
+ *   o[b,h,t,i] = y[b,h,t,i] / sqrt(mean_j y[b,h,t,j]^2 + eps) * gamma[h,i] * sigmoid(g[b,h,t,i])
+ *   y, o [B, H, T, dv] fp32; g [B, H, T, dv] g_dtype (gate pre-activation);
+ *   gamma [H, dv] fp32; eps >= 0. o may not alias y. dv a multiple of 4.
+ * The head-mixing projection W_o that follows is a plain dense layer and is
+ * not part of this library.
+ */
+int sdm_output_gate(const float* y, const float* gamma, const void* g, int g_dtype, float eps,
+                    int64_t B, int64_t H, int64_t T, int64_t dv, float* o, void* stream);
 
 #ifdef __cplusplus
 }

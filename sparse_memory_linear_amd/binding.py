@@ -43,6 +43,8 @@ _SIGS = {
     "sdm_scan_backward": (_I, [_P, _P, _I64, _P, _P, _I64, _P, _P, _P, _I, _P, _P, _P, _P,
                                _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I, _P, _I64, _P]),
     "sdm_state_init_backward": (_I, [_P, _P, _I64, _I64, _I64, _I64, _P]),
+    "sdm_gates": (_I, [_P, _I, _P, _P, _I, _P, _P, _I64, _I64, _I64, _I64, _P, _P, _P]),
+    "sdm_output_gate": (_I, [_P, _P, _P, _I, ctypes.c_float, _I64, _I64, _I64, _I64, _P, _P]),
 }
 
 _lib = None
@@ -322,6 +324,45 @@ def sdm_scan_backward(idx_w: torch.Tensor, wt_w: torch.Tensor, idx_r: torch.Tens
         _ptr(out["dalpha"]), _ptr(out["dbeta"]), _ptr(out["dwt_w"]), _ptr(out["dwt_r"]),
         B, H, T, N, dv, FORMS[form], _ptr(workspace), workspace.numel(), _stream(d)))
     return out
+
+
+def sdm_gates(x: torch.Tensor, W_a: torch.Tensor, W_b: torch.Tensor, b_dt: torch.Tensor,
+              A: torch.Tensor, out: Optional[Tuple[torch.Tensor, torch.Tensor]] = None
+              ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Scan gates from the layer input: alpha = exp(-A softplus(W_a x + b_dt)),
+    beta = sigmoid(W_b x). x [B,T,d], W_a/W_b [H,d] (same dtype, fp32 or bf16),
+    b_dt/A [H] fp32. Returns (alpha, beta) [B,H,T] fp32."""
+    d_ = _dev(x, W_a, W_b, b_dt, A)
+    B, T, d = x.shape
+    H = W_a.shape[0]
+    if W_a.shape != (H, d) or W_b.shape != (H, d) or b_dt.shape != (H,) or A.shape != (H,):
+        raise ValueError("shape mismatch in sdm_gates")
+    if b_dt.dtype != torch.float32 or A.dtype != torch.float32:
+        raise ValueError("b_dt and A must be fp32")
+    al, be = out if out is not None else (None, None)
+    al = _f32_out(al, (B, H, T), d_, "alpha")
+    be = _f32_out(be, (B, H, T), d_, "beta")
+    _check("sdm_gates", lib().sdm_gates(
+        _ptr(x), _dtype_code(x), _ptr(W_a), _ptr(W_b), _dtype_code(W_a), _ptr(b_dt), _ptr(A),
+        B, T, d, H, _ptr(al), _ptr(be), _stream(d_)))
+    return al, be
+
+
+def sdm_output_gate(y: torch.Tensor, gamma: torch.Tensor, g: torch.Tensor, eps: float = 1e-6,
+                    out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Per-head RMS-Norm of y [B,H,T,dv] times gamma [H,dv] and sigmoid(g) (g
+    [B,H,T,dv], fp32 or bf16). Returns o [B,H,T,dv] fp32."""
+    d_ = _dev(y, gamma, g)
+    B, H, T, dv = y.shape
+    if gamma.shape != (H, dv) or g.shape != y.shape or y.dtype != torch.float32 \
+            or gamma.dtype != torch.float32:
+        raise ValueError("shape or dtype mismatch in sdm_output_gate")
+    o = _f32_out(out, (B, H, T, dv), d_, "o")
+    if o.data_ptr() == y.data_ptr() and o.numel() > 0:
+        raise ValueError("o may not alias y")
+    _check("sdm_output_gate", lib().sdm_output_gate(
+        _ptr(y), _ptr(gamma), _ptr(g), _dtype_code(g), float(eps), B, H, T, dv, _ptr(o), _stream(d_)))
+    return o
 
 
 def sdm_state_init_backward(dM: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:

@@ -11,7 +11,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libsdm.so")
 OBJ = os.path.join(PKG, "_build")
-SOURCES = ["sdm_api.hip", "address.hip", "scan.hip", "scan_bwd.hip", "state_init.hip"]
+SOURCES = ["sdm_api.hip", "address.hip", "scan.hip", "scan_bwd.hip", "state_init.hip", "glue.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -327,6 +327,45 @@ int sdm_scan_backward(const int32_t* idx_w, const float* wt_w, int64_t W, const 
     return ok();
 }
 
+int sdm_gates(const void* x, int x_dtype, const void* W_a, const void* W_b, int w_dtype, const float* b_dt,
+              const float* A, int64_t B, int64_t T, int64_t d, int64_t H, float* alpha, float* beta, void* stream) {
+    const char* fn = "sdm_gates";
+    if (x_dtype != SDM_F32 && x_dtype != SDM_BF16) return fail(SDM_ERR_DTYPE, "unknown x dtype %d", x_dtype);
+    if (w_dtype != x_dtype) return fail(SDM_ERR_DTYPE, "weight dtype %d differs from x dtype %d", w_dtype, x_dtype);
+    if (B < 0 || T < 0 || d < 1 || H < 1) return fail(SDM_ERR_SHAPE, "%s: invalid sizes", fn);
+    const int64_t step = x_dtype == SDM_BF16 ? 32 : 8;
+    if (d % step != 0 || d > (1 << 20))
+        return fail(SDM_ERR_UNSUPPORTED, "d=%lld: a multiple of %lld up to 2^20", (long long)d, (long long)step);
+    if (H > 4096) return fail(SDM_ERR_UNSUPPORTED, "H=%lld: at most 4096 heads", (long long)H);
+    if ((B * T + 63) / 64 > 0x7FFFFFFFll) return fail(SDM_ERR_UNSUPPORTED, "too many tokens for one launch");
+    if (B == 0 || T == 0) return ok();
+    int rc = check_buffers(fn, {x, W_a, W_b, b_dt, A, alpha, beta});
+    if (rc) return rc;
+    sdm::GatesArgs a{};
+    a.x = x; a.Wa = W_a; a.Wb = W_b; a.bdt = b_dt; a.A = A; a.alpha = alpha; a.beta = beta;
+    a.B = B; a.T = T; a.d = (int)d; a.H = (int)H; a.bf16 = x_dtype == SDM_BF16;
+    hipError_t e = sdm::launch_gates(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, fn);
+    return ok();
+}
+
+int sdm_output_gate(const float* y, const float* gamma, const void* g, int g_dtype, float eps, int64_t B,
+                    int64_t H, int64_t T, int64_t dv, float* o, void* stream) {
+    const char* fn = "sdm_output_gate";
+    if (g_dtype != SDM_F32 && g_dtype != SDM_BF16) return fail(SDM_ERR_DTYPE, "unknown gate dtype %d", g_dtype);
+    if (B < 0 || H < 1 || T < 0 || dv < 1 || !(eps >= 0.f)) return fail(SDM_ERR_SHAPE, "%s: invalid sizes or eps", fn);
+    if (dv % 4 != 0) return fail(SDM_ERR_UNSUPPORTED, "dv=%lld must be a multiple of 4", (long long)dv);
+    if (B == 0 || T == 0) return ok();
+    int rc = check_buffers(fn, {y, gamma, g, o});
+    if (rc) return rc;
+    sdm::OutGateArgs a{};
+    a.y = y; a.gamma = gamma; a.g = g; a.o = o; a.eps = eps;
+    a.rows = B * H * T; a.T = T; a.H = H; a.dv = (int)dv; a.g_bf16 = g_dtype == SDM_BF16;
+    hipError_t e = sdm::launch_output_gate(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, fn);
+    return ok();
+}
+
 int sdm_state_init_backward(const float* dM, float* dM0, int64_t B, int64_t H, int64_t N, int64_t dv,
                             void* stream) {
     if (B < 0 || H < 0 || N < 1 || dv < 1) return fail(SDM_ERR_SHAPE, "sdm_state_init_backward: invalid sizes");

@@ -65,4 +65,29 @@ hipError_t launch_state_init_backward(const float* dM, float* dM0, int64_t B, in
 
 hipError_t launch_state_init(const float* M0, void* M, bool m_bf16, int64_t B, int64_t per_seq, hipStream_t st);
 
+struct GatesArgs {
+    const void* x;           // [B,T,d]
+    const void* Wa;          // [H,d]
+    const void* Wb;          // [H,d]
+    const float* bdt;        // [H]
+    const float* A;          // [H]
+    float* alpha; float* beta;  // [B,H,T]
+    int64_t B, T;
+    int d, H;
+    bool bf16;
+};
+hipError_t launch_gates(const GatesArgs& a, hipStream_t st);
+
+struct OutGateArgs {
+    const float* y;          // [B,H,T,dv]
+    const float* gamma;      // [H,dv]
+    const void* g;           // [B,H,T,dv]
+    float* o;                // [B,H,T,dv]
+    float eps;
+    int64_t rows, T, H;      // rows = B*H*T
+    int dv, lg;
+    bool g_bf16;
+};
+hipError_t launch_output_gate(OutGateArgs a, hipStream_t st);
+
 }  // namespace sdm

@@ -32,7 +32,7 @@ def test_header_declares_the_hot_path_calls():
               "sdm_scan_workspace_bytes", "sdm_status_string", "sdm_last_error", "sdm_abi_version",
               "sdm_scan_forward_save", "sdm_scan_snapshot_bytes", "sdm_scan_backward",
               "sdm_scan_backward_workspace_bytes", "sdm_state_init_backward", "sdm_address_idw",
-              "sdm_debug_half_scores_idw"):
+              "sdm_debug_half_scores_idw", "sdm_gates", "sdm_output_gate"):
         assert f in names
 
 
@@ -43,7 +43,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert binding.sdm_abi_version() == 4
+    assert binding.sdm_abi_version() == 5
     assert binding.sdm_status_string(0) == "ok"
     assert binding.sdm_status_string(7).startswith("workspace")
     assert binding.sdm_status_string(99) == "unknown status"
