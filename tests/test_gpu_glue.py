@@ -125,3 +125,22 @@ def test_layer_gates_scan_output_match_oracle(name, over, form):
     e_o, e_m = max_rel_err(o.cpu().numpy(), oo), max_rel_err(M.cpu().numpy(), Mo)
     say(f"  max rel err o {e_o:.2e}, M {e_m:.2e}")
     assert e_o <= tol and e_m <= tol
+
+
+def test_glue_full_size_gdn_matched():
+    """The glue at the benchmark's full size (gdn_matched: 32768 tokens, d = 1024,
+    8 heads; y of 33.5 M values)."""
+    wl = inputs.get("gdn_matched")
+    say(f"[glue full size] B={wl.B} H={wl.H} T={wl.T} d={inputs.d_model(wl)}")
+    gx = inputs.make_glue_inputs(wl)
+    g = {k: v.to(DEV) for k, v in gx.items()}
+    al, be = sdm.sdm_gates(g["x"], g["W_a"], g["W_b"], g["b_dt"], g["A"])
+    y = torch.randn((wl.B, wl.H, wl.T, wl.d_v), generator=torch.Generator().manual_seed(8)) * 0.3
+    o = sdm.sdm_output_gate(y.to(DEV), g["gamma"], g["g"], 1e-6)
+    torch.cuda.synchronize()
+    oa, ob = oracle.gates(gx["x"], gx["W_a"], gx["W_b"], gx["b_dt"], gx["A"])
+    ea = max_rel_err(al.cpu().numpy()[..., None], oa[..., None])
+    eb = max_rel_err(be.cpu().numpy()[..., None], ob[..., None])
+    eo = max_rel_err(o.cpu().numpy(), oracle.output_gate(y, gx["gamma"], gx["g"], 1e-6))
+    say(f"  max rel err alpha {ea:.2e}, beta {eb:.2e}, o {eo:.2e}")
+    assert ea <= TOL_BF16 and eb <= TOL_BF16 and eo <= 1e-5

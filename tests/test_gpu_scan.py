@@ -11,7 +11,7 @@ import torch
 import oracle
 import sparse_memory_linear_amd as sdm
 from sparse_memory_linear_amd import inputs
-from parity import TOL_BF16, TOL_F32, max_rel_err, say
+from parity import TOL_BF16, TOL_F32, compare_slots, max_rel_err, say
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
@@ -235,3 +235,26 @@ def test_full_pipeline_full_size_sampled_streams(name, streams):
                              x["M0"][h:h + 1][None].numpy(), oracle.EQ4)
         _check(f"stream ({b},{h})", sl(M).numpy(), sl(y).numpy(), Mo, yo,
                x["M0"][h:h + 1][None].numpy(), oi, TOL_BF16)
+
+
+@pytest.mark.parametrize("form,oform", FORMS, ids=["eq4", "fig2"])
+def test_large_table_full_size(form, oform):
+    """The FwPKM-sized workload at full size (one stream, T=65536, N=262144,
+    d_v=512, W=R=8, fp32): GPU addressing end to end against the oracle (near-
+    tie accounting), then both scans fed the oracle's slots, the whole y and
+    table checked."""
+    wl = inputs.get("large_table")
+    say(f"[large_table full size] T={wl.T} N={wl.N} d_v={wl.d_v} form={form}")
+    x = inputs.make_inputs(wl)
+    g = {k: v.to(DEV) for k, v in x.items()}
+    iw, ww, ir, wr = sdm.sdm_address(g["q_w"], g["q_r"], g["subkeys"], g["subkeys"], wl.W, wl.R)
+    oiw, oww, osw, onw = oracle.address(x["q_w"], x["subkeys"], wl.W)
+    oir, owr, osr, onr = oracle.address(x["q_r"], x["subkeys"], wl.R)
+    for gi, oi, osc, onx in ((iw, oiw, osw, onw), (ir, oir, osr, onr)):
+        res = compare_slots(gi.cpu().numpy(), oi, osc, onx)
+        say(f"  slots: {res}")
+        assert res["violating"] == 0
+    M_in = oracle.broadcast_state(x["M0"], wl.B)
+    Mo, yo = oracle.scan(oiw, oww, oir, owr, x["alpha"], x["beta"], x["v"], M_in, oform)
+    Mg, yg = _run_gpu(oiw, oww, oir, owr, x["alpha"], x["beta"], x["v"], M_in, form)
+    _check("large_table", Mg, yg, Mo, yo, M_in, oiw, TOL_F32)
