@@ -229,7 +229,7 @@ def train_bench(a, wl, x, dev):
         "forward_save_GBps": fwd_bytes / (br["forward_save"] * 1e-3) / 1e9,
         "roofline": {"bound": "hbm", "achieved": bwd_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": bwd_gbps / HBM_PEAK_GBPS, "traffic": None,
-                     "kernel": "sdm_scan_backward (scan_backward_kernel + bwd_partials_reduce)",
+                     "kernel": "sdm_scan_backward (bwd_plan_kernel + scan_backward_kernel + bwd_partials_reduce)",
                      "algorithmic_bytes_per_launch": bwd_bytes},
     }
     if not a.no_cpu_baseline:

@@ -22,26 +22,26 @@
 //
 // Design. As in the forward, one workgroup owns one (stream, column slab of S
 // floats): writer wavefronts hold the W write rows of a token (G rows each, one
-// 16-byte segment per lane), reader wavefronts the R read rows. What no write
-// changes (indices, weights, gates, v, dy, pre-images) is loaded one token
-// ahead. The table rows (M and G of the reads, G of the writes) are loaded
-// after the barrier that closes the previous token, so they see every earlier
-// store of the workgroup (same CU) and nothing is forwarded across tokens.
-// Within a token, readers and writers load at the same time; a write row that
-// the token also reads takes the readers' new G value from LDS (the readers
-// publish row -> read position in a small LDS hash table), so a token costs
-// one memory round trip. The gradients of the weights and gates are column
+// 16-byte segment per lane), reader wavefronts the R read rows. Each token's
+// loads (index words, weights, gates, v or dy, pre-images and the table rows)
+// are issued D = 2 tokens before the token is processed, so the walk is not one
+// memory round trip per token. Rows that a token of that window will still
+// change are not taken from memory: a planner kernel resolves, from the
+// indices alone, where each access finds its row instead (the adjoint row from
+// an LDS ring of the rows the nearest later toucher produced; a read's table
+// row from the pre-image of the nearest later write). Every load and store in
+// the token loop is a buffer access that every lane issues (out-of-range
+// offsets where a lane has none), so the number of memory operations in flight
+// is the same on every path and the compiler's counter waits drain only the
+// token being consumed. The gradients of the weights and gates are column
 // sums: each workgroup writes its slab's partial sums and a second kernel adds
 // them over the slabs in slab order (deterministic).
 //
-// Row partitions (per-slot form). The per-slot write never couples two rows,
-// so, as in the forward, the rows of a stream's table are split into P
-// partitions by a hash of the row index and each partition is walked by its
-// own workgroups: a token costs each of them the same round trip, and P times
-// as many workgroups keep P times as many rows in flight. A workgroup takes the
-// accesses of its partition and leaves the others' lanes idle (a wavefront
-// with no access of its partition in a token skips it). dv_t and the gate
-// gradients are then partial sums per partition, added in partition order.
+// Row partitions (per-slot form, on request). The per-slot write never couples
+// two rows, so the rows of a stream's table can be split into P partitions by a
+// hash of the row index, each walked by its own workgroups, which take the
+// accesses of their partition and leave the other lanes idle. dv_t and the
+// gate gradients are then partial sums per partition, added in partition order.
 #include "sdm_buffer.h"
 #include "sdm_internal.h"
 
@@ -49,17 +49,6 @@ namespace sdm {
 namespace {
 
 constexpr int BWD_NWMAX = 16;   // wavefronts per workgroup (1024 threads, 128 VGPRs)
-#ifndef SDM_BWD_DEPTH
-#define SDM_BWD_DEPTH 6
-#endif
-// tokens of streamed inputs in flight per wavefront (fp32 v takes two more
-// registers per token, so its ring is shorter)
-template <bool VBF16>
-constexpr int ring_depth() { return VBF16 ? SDM_BWD_DEPTH : SDM_BWD_DEPTH - 2; }
-constexpr int HS = 512;         // LDS hash slots per token parity: R <= 256 keeps the load <= 1/2
-constexpr int HS_BITS = 9;
-
-__device__ __forceinline__ int hslot(uint32_t row) { return (int)((row * 2654435761u) >> (32 - HS_BITS)); }
 
 struct BwdKArgs {
     const int32_t* idx_w; const float* wt_w;
@@ -70,6 +59,7 @@ struct BwdKArgs {
     float* pw; float* pr;               // partial sums of this launch: [nslab][NS][T][W], [nslab][NS][T][R]
     float* pab;                         // [nslab * P][NS][T][2]
     float* pdv;                         // P > 1: [P][NS][T][dv]
+    const uint32_t* plan;               // prefetching form: [NS][T][W + 2R] source words of this launch
     int64_t TS, t0;                     // tokens per stream; first token of this launch
     int T, W, R;
     int64_t N;
@@ -82,25 +72,157 @@ __device__ __forceinline__ int row_part(uint32_t row, int pshift) {
     return pshift == 0 ? 0 : (int)((row * 0x9E3779B1u) >> (32 - pshift));
 }
 
+// ------------------------------------------------------------------ planner
+// The prefetching backward issues a token's table-row loads D tokens before the
+// token is processed (processing runs t = T-1 .. 0), so a load of token u does
+// not see what tokens u+1 .. u+D will store. All indices are known, so for
+// every access of token u a planner finds, from the indices alone:
+//   G source: the token of (u, u+D] nearest to u that touches the row; the
+//     row's adjoint after that token (its writer's new G if it writes the row,
+//     else its reader's) comes from an LDS ring. A write whose row the same
+//     token also reads takes that reader's new G (distance 0).
+//   M source (reads): the token of (u, u+D] nearest to u that writes the row;
+//     the row's state after token u is that write's pre-image, read from the
+//     forward's stored pre-images (which nothing modifies) instead of the table.
+// Without a source in the window, the table in memory is already right.
+// Word layout: bit 31 = from the ring / from the pre-images, bits 9-11 =
+// distance d, bits 0-8 = source position (writer p < W, reader W + q).
+constexpr uint32_t BSRC_ON = 1u << 31;
+constexpr int BSRC_DSHIFT = 9;
+constexpr uint32_t BSRC_POS = 511u;
+constexpr int BHT_BITS = 13;
+constexpr int BHT_CAP = 1 << BHT_BITS;     // 64-bit LDS hash entries (64 KiB)
+constexpr uint64_t BHT_EMPTY = ~0ull;
+constexpr int BPLAN_THREADS = 512;
+
+struct BPlanArgs {
+    const int32_t* idx_w; const int32_t* idx_r;   // the launch's first token of stream 0; stream stride TS
+    uint32_t* plan;                               // [NS][Tn][W + 2R]
+    int64_t Tn, TS, N;
+    int W, R, D, TT;
+    int64_t ntile;
+};
+
+__device__ __forceinline__ uint32_t bht_hash(uint32_t row) { return (row * 2654435761u) >> (32 - BHT_BITS); }
+
+// One workgroup per (stream, tile of TT tokens [u0, u1)): an LDS hash holds every
+// access of tokens [u0, u1 + D) as (row << 32 | token - u0 << 10 | is_write << 9 |
+// position), at most half full; each access of the tile then walks its row's
+// entries and keeps the nearest later touch and write.
+__global__ __launch_bounds__(BPLAN_THREADS) void bwd_plan_kernel(BPlanArgs a) {
+    __shared__ uint64_t ht[BHT_CAP];
+    const int tid = threadIdx.x;
+    const int W = a.W, R = a.R, D = a.D, K = W + R, RW = W + 2 * R;
+    const int64_t s = blockIdx.x / a.ntile;
+    const int64_t u0 = (blockIdx.x % a.ntile) * a.TT;
+    const int64_t u1 = u0 + a.TT < a.Tn ? u0 + a.TT : a.Tn;
+    const int64_t h1 = u1 + D < a.Tn ? u1 + D : a.Tn;
+    const int32_t* iw = a.idx_w + s * a.TS * W;
+    const int32_t* ir = a.idx_r + s * a.TS * R;
+    uint32_t* Ps = a.plan + s * a.Tn * RW;
+    for (int i = tid; i < BHT_CAP; i += BPLAN_THREADS) ht[i] = BHT_EMPTY;
+    __syncthreads();
+    const int n1 = (int)(h1 - u0) * K;
+    for (int e = tid; e < n1; e += BPLAN_THREADS) {
+        const int tk = e / K, pos = e - tk * K;
+        const bool isw = pos < W;
+        const int q = isw ? pos : pos - W;
+        const int32_t row = isw ? iw[(u0 + tk) * W + q] : ir[(u0 + tk) * R + q];
+        if (row < 0 || row >= a.N) continue;
+        const uint64_t ent = ((uint64_t)(uint32_t)row << 32) | ((uint64_t)tk << 10) | ((uint64_t)isw << 9) |
+                             (uint64_t)q;
+        uint32_t h = bht_hash((uint32_t)row);
+        while (atomicCAS((unsigned long long*)&ht[h], (unsigned long long)BHT_EMPTY, (unsigned long long)ent) !=
+               (unsigned long long)BHT_EMPTY)
+            h = (h + 1) & (BHT_CAP - 1);
+    }
+    __syncthreads();
+    const int n2 = (int)(u1 - u0) * K;
+    for (int e = tid; e < n2; e += BPLAN_THREADS) {
+        const int tk = e / K, pos = e - tk * K;
+        const bool isw = pos < W;
+        const int q = isw ? pos : pos - W;
+        const int32_t row = isw ? iw[(u0 + tk) * W + q] : ir[(u0 + tk) * R + q];
+        uint32_t gs = 0u, ms = 0u;
+        if (row >= 0 && row < a.N) {
+            int gd = D + 1, md = D + 1;
+            bool gw = false, own = false;
+            uint32_t gp = 0u, mp = 0u, op = 0u;
+            uint32_t h = bht_hash((uint32_t)row);
+            uint64_t ent;
+            while ((ent = ht[h]) != BHT_EMPTY) {
+                if ((uint32_t)(ent >> 32) == (uint32_t)row) {
+                    const int d = (int)((ent >> 10) & 1023u) - tk;
+                    const bool ew = (ent >> 9) & 1u;
+                    const uint32_t ep = (uint32_t)(ent & 511u);
+                    if (d == 0 && isw && !ew) {
+                        own = true;
+                        op = ep;
+                    }
+                    if (d >= 1 && d <= D) {
+                        if (d < gd || (d == gd && ew && !gw)) {
+                            gd = d;
+                            gw = ew;
+                            gp = ew ? ep : (uint32_t)W + ep;
+                        }
+                        if (ew && d < md) {
+                            md = d;
+                            mp = ep;
+                        }
+                    }
+                }
+                h = (h + 1) & (BHT_CAP - 1);
+            }
+            if (own) gs = BSRC_ON | ((uint32_t)W + op);
+            else if (gd <= D) gs = BSRC_ON | ((uint32_t)gd << BSRC_DSHIFT) | gp;
+            if (!isw && md <= D) ms = BSRC_ON | ((uint32_t)md << BSRC_DSHIFT) | mp;
+        }
+        uint32_t* rec = Ps + (u0 + tk) * RW;
+        if (isw) {
+            rec[q] = gs;
+        } else {
+            rec[W + q] = gs;
+            rec[W + R + q] = ms;
+        }
+    }
+}
+
+// ------------------------------------------------------------------ prefetching backward
+// The backward above with each token's rows loaded D tokens early. Per token,
+// in the reverse walk: address words (index and the planner's source words)
+// come D + DM tokens early; values (weight, gates, v or dy, pre-image) and
+// table rows (G of every access, M of the reads, or the pre-image a read's M
+// comes from) D tokens early, issued right after the barrier that closed the
+// previous token. Every token leaves the adjoint rows it produced (writers' and
+// readers' new G) in an LDS ring of D + 1 token slots [slot][W + R][L], where
+// later-processed tokens of the window find them.
+// D = 2 measured best on MI355X: D = 1 is as fast for the per-slot form and 5 %
+// slower for the shared-residual one; D = 3 no longer fits 128 VGPRs (spills)
+// and runs about twice as long.
+constexpr int BWD_D = 2;
+
+__device__ __forceinline__ uint32_t ld_u1(rsrc_t r, uint32_t vo, uint32_t so) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, (int)vo, (int)so, 0);
+}
+
 template <int S, int FORM, bool VBF16>
 __global__ __launch_bounds__(BWD_NWMAX * 64) void scan_backward_kernel(BwdKArgs a) {
     constexpr int L = S / 4, G = 64 / L;
     using VL = VLoad<VBF16>;
     using V4 = typename VL::T4;
-    constexpr int DP = ring_depth<VBF16>();
-    __shared__ int hkey[2][HS];                 // read rows of the token (parity t & 1), -1 = empty
-    __shared__ int hpos[2][HS];                 // their read positions
-    __shared__ float4 rg[BWD_NWMAX * 64];       // readers' new G segments [read position][L]
-    __shared__ float4 xb[2][BWD_NWMAX][L];      // per writer wavefront: dv (EQ4) or gh and s (FIG2) partials
-    __shared__ float ab[BWD_NWMAX][2];          // per writer wavefront: dalpha, dbeta partials
+    constexpr int D = BWD_D;
+    constexpr int DM = D + 1;
+    constexpr int UP = D + 1;          // value/row ring
+    constexpr int U = D + DM + 1;      // address ring = unroll factor (a multiple of UP)
+    static_assert(U % UP == 0, "ring sizes");
+    constexpr int UR = D + 1;          // LDS ring slots
+    extern __shared__ float4 lring[];  // [UR][W + R][L]
+    __shared__ float4 xb[2][BWD_NWMAX][L];
+    __shared__ float ab[BWD_NWMAX][2];
 
-    const int NWW = a.NWW, T = a.T, dv = a.dv, W = a.W, R = a.R;
-    // the wavefront index through readfirstlane: the compiler then knows it is
-    // uniform, so role branches stay scalar (no per-lane descriptor loops)
+    const int NWW = a.NWW, T = a.T, dv = a.dv, W = a.W, R = a.R, KR = W + R, RW = W + 2 * R;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63, r = lane / L,
               cc = lane % L;
-    // workgroups are dealt to the 8 XCDs round-robin: all slabs and partitions
-    // of a stream go to the same XCD (they share its L2)
     const int b = blockIdx.x, xcd = b & 7, kq = b >> 3, units = a.nslab * a.P;
     const int64_t s = (int64_t)(kq / units) * 8 + xcd;
     const int slab = kq % a.nslab, part = (kq % units) / a.nslab;
@@ -108,14 +230,16 @@ __global__ __launch_bounds__(BWD_NWMAX * 64) void scan_backward_kernel(BwdKArgs 
     const int col = slab * S + cc * 4;
     const bool writer = wave < NWW;
     const int rw = wave - NWW;
-    const int pos = writer ? wave * G + r : rw * G + r;  // access position of this lane's row
+    const int pos = writer ? wave * G + r : rw * G + r;
     const int K = writer ? W : R;
     const bool has = pos < K;
-    const int64_t tok0 = s * a.TS + a.t0;               // stream s's first token of this launch
+    const int64_t tok0 = s * a.TS + a.t0;
     const int32_t* ix = (writer ? a.idx_w : a.idx_r) + tok0 * K;
     const float* wx = (writer ? a.wt_w : a.wt_r) + tok0 * K;
     const float* alp = a.alpha + tok0;
     const float* bep = a.beta + tok0;
+    const uint32_t* pl = a.plan + s * (int64_t)T * RW;
+    const int pg_off = writer ? pos : W + pos;    // this lane's G-source word in a token record
     const rsrc_t Rm = make_rsrc(a.M + s * a.N * dv, a.N * dv * 4);
     const rsrc_t Rg = make_rsrc(a.G + s * a.N * dv, a.N * dv * 4);
     const rsrc_t Rv = make_rsrc(static_cast<const char*>(a.v) + tok0 * dv * VL::ESZ, (int64_t)T * dv * VL::ESZ);
@@ -125,126 +249,133 @@ __global__ __launch_bounds__(BWD_NWMAX * 64) void scan_backward_kernel(BwdKArgs 
                               : make_rsrc(a.dvo + tok0 * dv, (int64_t)T * dv * 4);
     const uint32_t dv4 = (uint32_t)dv * 4u, col4 = (uint32_t)col * 4u;
     const uint32_t vstride = (uint32_t)dv * VL::ESZ, v_off = (uint32_t)col * VL::ESZ;
-    const uint32_t sstride = (uint32_t)W * dv4;                  // pre-image bytes per token
+    const uint32_t sstride = (uint32_t)W * dv4;
     const uint32_t s_lane = has ? (uint32_t)pos * dv4 + col4 : OOB;
     const int64_t ps = (int64_t)slab * a.NS + s;
     float* pw = a.pw + ps * T * W;
     float* pr = a.pr + ps * T * R;
     float* pab = a.pab + ((int64_t)(slab * a.P + part) * a.NS + s) * T * 2;
 
-    for (int i = threadIdx.x; i < 2 * HS; i += blockDim.x) (&hkey[0][0])[i] = -1;
     for (int i = threadIdx.x; i < 2 * BWD_NWMAX * L; i += blockDim.x)
         (&xb[0][0][0])[i] = make_float4(0.f, 0.f, 0.f, 0.f);
     __syncthreads();
 
-    // the lane's access, if its row is valid and in this workgroup's partition
     auto off_of = [&](int32_t row) -> uint32_t {
         return (row >= 0 && row < a.N && row_part((uint32_t)row, a.pshift) == part)
                    ? __umul24((uint32_t)row, dv4) + col4 : OOB;
     };
-    // partition 0 writes the (zero) weight gradients of positions whose row is out of range
     auto owns_pos = [&](int32_t row, uint32_t off) -> bool {
         return off != OOB || (part == 0 && has && !(row >= 0 && row < a.N));
     };
-    // The inputs no write changes (index, weight, gates; v and the pre-image for
-    // writers, dy for readers) come DP tokens ahead, from a register ring that
-    // the unrolled loop indexes statically. A token first issues its table-row
-    // loads, then the ring refill: the memory counters complete in order, so
-    // waiting for the rows does not wait for the refill.
-    struct In {
+    auto ring_at = [&](int slot, int p) -> float4& { return lring[((int64_t)slot * KR + p) * L + cc]; };
+
+    const rsrc_t Rix = make_rsrc(ix, (int64_t)T * K * 4);
+    const rsrc_t Rwx = make_rsrc(wx, (int64_t)T * K * 4);
+    const rsrc_t Rpl = make_rsrc(pl, (int64_t)T * RW * 4);
+    const rsrc_t Ral = make_rsrc(alp, (int64_t)T * 4);
+    const rsrc_t Rbe = make_rsrc(bep, (int64_t)T * 4);
+    const rsrc_t Rpw = make_rsrc(pw, (int64_t)T * W * 4);
+    const rsrc_t Rpr = make_rsrc(pr, (int64_t)T * R * 4);
+    const rsrc_t Rpab = make_rsrc(pab, (int64_t)T * 8);
+    const uint32_t lane_k = has ? (uint32_t)pos * 4u : OOB;
+    const uint32_t lane_pg = has ? (uint32_t)pg_off * 4u : OOB;
+    const uint32_t lane_pm = (has && !writer) ? (uint32_t)(W + R + pos) * 4u : OOB;
+
+    struct Ad {
         int32_t row;
-        float w, al, be;
-        V4 v;
-        float4 x;
+        uint32_t gs, ms;
     };
-    auto fetch = [&](int tk) -> In {
-        In d;
-        const int64_t o = (int64_t)tk * K + pos;
-        d.row = has ? ix[o] : -1;
-        d.w = has ? wx[o] : 0.f;
-        d.al = alp[tk];
-        d.be = bep[tk];
-        if (writer) {
-            d.v = VL::load(Rv, v_off, (uint32_t)tk * vstride);
-            d.x = ld_f4(Rs, s_lane, (uint32_t)tk * sstride);
-        } else {
-            d.v = V4{};
-            d.x = ld_f4(Rd, col4, (uint32_t)tk * dv4);
-        }
+    struct Va {
+        float w, al, be;
+        float4 x;   // writers: the pre-image of the write; readers: dy
+        float4 g;   // the adjoint row (unless it comes from the ring)
+        float4 y;   // writers: v_t (its raw bits); readers: M_t of the row (table or pre-image)
+    };
+    auto v_of = [&](const float4& y) -> V4 {
+        if constexpr (VBF16) return make_int2(__float_as_int(y.x), __float_as_int(y.y));
+        else return y;
+    };
+    // Every load below is issued by every lane of both wavefront roles (a lane
+    // without the access gets an out-of-range offset), so the loads in flight
+    // per token are the same on every path.
+    auto fetch_ad = [&](int tk) -> Ad {
+        Ad d;
+        const int32_t row = (int32_t)ld_u1(Rix, lane_k, (uint32_t)tk * (uint32_t)K * 4u);
+        d.row = has ? row : -1;
+        d.gs = ld_u1(Rpl, lane_pg, (uint32_t)tk * (uint32_t)RW * 4u);
+        d.ms = ld_u1(Rpl, lane_pm, (uint32_t)tk * (uint32_t)RW * 4u);
         return d;
     };
-    In ring[DP];
-#pragma unroll
-    for (int j = 0; j < DP; ++j)
-        if (T - 1 - j >= 0) ring[j] = fetch(T - 1 - j);
-    int ins = -1;  // readers: the hash slot of this lane's row in the previous token's table
+    auto fetch_va = [&](int tk, const Ad& d) -> Va {
+        Va x;
+        const uint32_t off = off_of(d.row);
+        x.w = __uint_as_float(ld_u1(Rwx, lane_k, (uint32_t)tk * (uint32_t)K * 4u));
+        x.al = __uint_as_float(ld_u1(Ral, 0u, (uint32_t)tk * 4u));
+        x.be = __uint_as_float(ld_u1(Rbe, 0u, (uint32_t)tk * 4u));
+        x.g = ld_f4(Rg, (d.gs & BSRC_ON) ? OOB : off, 0u);
+        const V4 vv = VL::load(Rv, writer ? v_off : OOB, (uint32_t)tk * vstride);
+        const float4 sn = ld_f4(Rs, writer ? s_lane : OOB, (uint32_t)tk * sstride);
+        const float4 dy = ld_f4(Rd, writer ? OOB : col4, (uint32_t)tk * dv4);
+        // a read's M_t: from the table, or from a later write's pre-image (the
+        // other load's offset is out of range: it is dropped)
+        const bool from_pre = !writer && (d.ms & BSRC_ON) && off != OOB;
+        const uint32_t dd = (d.ms >> BSRC_DSHIFT) & 7u, sp = d.ms & BSRC_POS;
+        const float4 mt = ld_f4(Rm, (writer || from_pre) ? OOB : off, 0u);
+        const float4 mp = ld_f4(Rs, from_pre ? (uint32_t)(tk + (int)dd) * sstride + sp * dv4 + col4 : OOB, 0u);
+        float4 vf;
+        if constexpr (VBF16) vf = make_float4(__int_as_float(vv.x), __int_as_float(vv.y), 0.f, 0.f);
+        else vf = vv;
+        x.x = writer ? sn : dy;
+        x.y = writer ? vf : (from_pre ? mp : mt);
+        return x;
+    };
 
-    // wavefront 0: token tk's dv (per-slot form: the writers' partial sums) and
-    // gate partial sums. Called once the next token's row loads are issued, so
-    // its LDS reads overlap them; the writers overwrite xb and ab only after
-    // the next token's first barrier.
+    // wavefront 0: token tk's dv (per-slot form) and gate partial sums
     auto finish = [&](int tk) {
         if constexpr (FORM == 0) {
             float acc = 0.f;
 #pragma unroll
-            for (int q = 0; q < BWD_NWMAX; ++q)  // xb of absent wavefronts holds zeros
+            for (int q = 0; q < BWD_NWMAX; ++q)
                 acc += reinterpret_cast<const float*>(xb[0][q])[lane < S ? lane : 0];
             st_f1(acc, Ro, lane < S ? (uint32_t)(slab * S + lane) * 4u : OOB, (uint32_t)tk * dv4);
         }
         const float sa = wave_sum(lane < NWW ? ab[lane][0] : 0.f), sb = wave_sum(lane < NWW ? ab[lane][1] : 0.f);
-        if (lane == 0) {
-            pab[2 * (int64_t)tk] = sa;
-            pab[2 * (int64_t)tk + 1] = sb;
-        }
+        st_f1(lane == 0 ? sa : sb, Rpab, lane < 2 ? (uint32_t)lane * 4u : OOB, (uint32_t)tk * 8u);
     };
 
-    for (int t0 = T - 1; t0 >= 0; t0 -= DP) {
-#pragma unroll
-    for (int j = 0; j < DP; ++j) {
-        const int tl = t0 - j;
-        if (tl < 0) break;  // uniform
-        const In cur = ring[j];
-        auto refill = [&]() {
-            if (tl - DP >= 0) ring[j] = fetch(tl - DP);  // uniform
-        };
-        const int32_t row = cur.row;
+    int slot = (T - 1) % UR;  // LDS ring slot of the token being processed
+    auto process = [&](int tl, const Ad& d, const Va& x) {
+        const int32_t row = d.row;
         const uint32_t off = off_of(row);
-        const float w = off == OOB ? 0.f : cur.w, al = cur.al, be = cur.be;
-        const V4 vt = cur.v;
-        const float4 xt = cur.x;
-        const int tb = tl & 1;
-        const bool run = __ballot(off != OOB) != 0ull;  // wavefront has an access of this partition
+        const float w = off == OOB ? 0.f : x.w, al = x.al, be = x.be;
+        const bool run = __ballot(off != OOB) != 0ull;  // else every lane's offset is out of range
+        const bool fwd = (d.gs & BSRC_ON) && off != OOB;
+        int fslot = slot + (int)((d.gs >> BSRC_DSHIFT) & 7u);
+        if (fslot >= UR) fslot -= UR;
+        const int fpos = (int)(d.gs & BSRC_POS);
+        const bool own = owns_pos(row, off) && cc == 0;
         if (writer) {
-            float4 g = ld_f4(Rg, run ? off : OOB, 0u);  // after the barrier that closed token tl + 1
-            refill();
-            const float4 m = xt;                         // the pre-image M_{t-1}[i]
+            const float4 m = x.x;  // the pre-image M_{t-1}[i]
             if (wave == 0 && tl + 1 < T) finish(tl + 1);
-            __syncthreads();                             // B1: the readers' new G values are in LDS
-            if (off != OOB) {               // a row this token also reads: its G after the reads
-                int h = hslot((uint32_t)row), k;
-                while ((k = hkey[tb][h]) != -1) {
-                    if (k == row) {
-                        g = rg[hpos[tb][h] * L + cc];
-                        break;
-                    }
-                    h = (h + 1) & (HS - 1);
-                }
-            }
+            __syncthreads();       // B1: this token's readers' new G values are in the ring
+            float4 g = x.g;
+            if (fwd) g = ring_at(fslot, fpos);
+            float4 gn = make_float4(0.f, 0.f, 0.f, 0.f);
+            float pwv = 0.f;
             if constexpr (FORM == 0) {
                 const float bw = be * w, c1 = 1.f - bw;
-                const float4 u = f4_sub(VL::f(vt), f4_scale(al, m));
+                const float4 u = f4_sub(VL::f(v_of(x.y)), f4_scale(al, m));
                 const float part = rows_reduce<L>(f4_scale(bw, g));
                 if ((lane & 15) < L) reinterpret_cast<float*>(xb[0][wave])[4 * (lane & 15) + (lane >> 4)] = part;
                 float da = 0.f, db = 0.f;
-                if (run) {  // uniform per wavefront
+                if (run) {
                     const float gm = dot4(g, m), gu = dot4(g, u);
                     const float gur = group_sum<L>(gu);
-                    if (owns_pos(row, off) && cc == 0) pw[(int64_t)tl * W + pos] = off == OOB ? 0.f : be * gur;
+                    pwv = off == OOB ? 0.f : be * gur;
                     da = wave_sum(c1 * gm);
                     db = wave_sum(w * gu);
-                    st_f4(f4_scale(al * c1, g), Rg, off, 0u);
-                } else if (owns_pos(row, off) && cc == 0) {
-                    pw[(int64_t)tl * W + pos] = 0.f;
+                    gn = f4_scale(al * c1, g);
+                    if (off != OOB) ring_at(slot, pos) = gn;
                 }
                 if (lane == 0) {
                     ab[wave][0] = da;
@@ -262,57 +393,72 @@ __global__ __launch_bounds__(BWD_NWMAX * 64) void scan_backward_kernel(BwdKArgs 
                     gh = f4_add(gh, xb[0][q][cc]);
                     sm = f4_add(sm, xb[1][q][cc]);
                 }
-                const float4 u = f4_sub(VL::f(vt), f4_scale(al, sm));
+                const float4 u = f4_sub(VL::f(v_of(x.y)), f4_scale(al, sm));
                 const float gm = dot4(g, m), gu = dot4(g, u), hm = dot4(gh, m);
                 const float gur = group_sum<L>(gu), hmr = group_sum<L>(hm);
-                if (owns_pos(row, off) && cc == 0)
-                    pw[(int64_t)tl * W + pos] = off == OOB ? 0.f : be * gur - al * be * hmr;
-                float xa = gm, xc = 0.f;
-                if (wave == 0 && r == 0) {  // the per-slab terms, once
-                    xa -= be * dot4(gh, sm);
-                    xc = dot4(gh, u);
-                    st_f4(f4_scale(be, gh), Ro, col4, (uint32_t)tl * dv4);  // dv_t = b gh
-                }
+                pwv = off == OOB ? 0.f : be * gur - al * be * hmr;
+                const bool lead = wave == 0 && r == 0;
+                const float xa = lead ? gm - be * dot4(gh, sm) : gm, xc = lead ? dot4(gh, u) : 0.f;
+                st_f4(f4_scale(be, gh), Ro, lead ? col4 : OOB, (uint32_t)tl * dv4);
                 const float da = wave_sum(xa), db = wave_sum(xc);
                 if (lane == 0) {
                     ab[wave][0] = da;
                     ab[wave][1] = db;
                 }
-                st_f4(f4_sub(f4_scale(al, g), f4_scale(al * be * w, gh)), Rg, off, 0u);
+                gn = f4_sub(f4_scale(al, g), f4_scale(al * be * w, gh));
+                if (off != OOB) ring_at(slot, pos) = gn;
             }
-            if (run) st_f4(m, Rm, off, 0u);  // the undo
-            __syncthreads();                 // B2
+            st_f1(pwv, Rpw, own ? (uint32_t)pos * 4u : OOB, (uint32_t)tl * (uint32_t)W * 4u);
+            st_f4(gn, Rg, off, 0u);
+            st_f4(m, Rm, off, 0u);  // the undo
+            __syncthreads();        // B2
         } else {
-            if (ins >= 0) hkey[tb ^ 1][ins] = -1;  // the previous token's writers are done with it
-            ins = -1;
-            float4 m = make_float4(0.f, 0.f, 0.f, 0.f), g = m;
-            if (run) {  // uniform per wavefront
-                m = ld_f4(Rm, off, 0u);  // M_t: rows of later tokens are already undone
-                g = ld_f4(Rg, off, 0u);
-            }
-            refill();
+            float4 gn = make_float4(0.f, 0.f, 0.f, 0.f);
+            float dr = 0.f;
             if (run) {
-                if (off != OOB && cc == 0) {  // publish the row while the loads are in flight
-                    int h = hslot((uint32_t)row);
-                    while (atomicCAS(&hkey[tb][h], -1, row) != -1) h = (h + 1) & (HS - 1);
-                    hpos[tb][h] = pos;
-                    ins = h;
-                }
-                const float dr = group_sum<L>(dot4(xt, m));
-                const float4 gn = f4_fma(w, xt, g);
-                st_f4(gn, Rg, off, 0u);
-                rg[pos * L + cc] = gn;
-                if (owns_pos(row, off) && cc == 0) pr[(int64_t)tl * R + pos] = off == OOB ? 0.f : dr;
-            } else if (owns_pos(row, off) && cc == 0) {
-                pr[(int64_t)tl * R + pos] = 0.f;
+                float4 g = x.g;
+                if (fwd) g = ring_at(fslot, fpos);
+                dr = group_sum<L>(dot4(x.x, x.y));
+                gn = f4_fma(w, x.x, g);
+                if (off != OOB) ring_at(slot, W + pos) = gn;
             }
+            st_f4(gn, Rg, off, 0u);
+            st_f1(off == OOB ? 0.f : dr, Rpr, own ? (uint32_t)pos * 4u : OOB, (uint32_t)tl * (uint32_t)R * 4u);
             __syncthreads();                           // B1
             if constexpr (FORM == 1) __syncthreads();  // BX
             __syncthreads();                           // B2
         }
+        slot = slot == 0 ? UR - 1 : slot - 1;
+    };
+
+    // Main loop: U tokens per trip, fully unrolled so the register rings are
+    // statically indexed; the token being processed is tl = T - 1 - k.
+    int k_done = 0;
+    if (T >= U) {
+        Ad ad[U];
+        Va va[UP];
+#pragma unroll
+        for (int q = 0; q < D + DM; ++q) ad[q] = fetch_ad(T - 1 - q);
+#pragma unroll
+        for (int q = 0; q < D; ++q) va[q] = fetch_va(T - 1 - q, ad[q]);
+        for (int k0 = 0; k0 + U <= T; k0 += U) {
+#pragma unroll
+            for (int j = 0; j < U; ++j) {
+                const int tl = T - 1 - (k0 + j);
+                // early loads of tokens before 0 fetch token 0 again, unused
+                ad[(j + D + DM) % U] = fetch_ad(tl - D - DM >= 0 ? tl - D - DM : 0);
+                va[(j + D) % UP] = fetch_va(tl - D >= 0 ? tl - D : 0, ad[(j + D) % U]);
+                process(tl, ad[j], va[j % UP]);
+            }
+        }
+        k_done = (T / U) * U;
     }
+    for (int k = k_done; k < T; ++k) {  // the rest: loads right before use
+        const int tl = T - 1 - k;
+        const Ad d = fetch_ad(tl);
+        process(tl, d, fetch_va(tl, d));
     }
-    if (wave == 0) finish(0);  // writers' last partial sums are complete since the last B2
+    if (wave == 0) finish(0);
 }
 
 // dwt_w, dwt_r, dalpha, dbeta of one launch: the slabs' partial sums added in
@@ -367,10 +513,15 @@ BGeom bwd_geom(int S, int W, int R) {
     g.NWR = (R + g.G - 1) / g.G;
     return g;
 }
+// LDS of the prefetching form: the ring of D + 1 token slots of W + R rows.
+size_t bwd_ring_bytes(int S, int W, int R) {
+    return (size_t)(BWD_D + 1) * (W + R) * (S / 4) * 16;
+}
+
 bool bwd_fits(int S, int W, int R, int dv) {
     if (dv % S != 0) return false;
     const BGeom g = bwd_geom(S, W, R);
-    return g.NWW + g.NWR <= BWD_NWMAX;
+    return g.NWW + g.NWR <= BWD_NWMAX && bwd_ring_bytes(S, W, R) <= 128 * 1024;
 }
 
 int env_int(const char* name) {
@@ -378,42 +529,32 @@ int env_int(const char* name) {
     return e ? atoi(e) : 0;
 }
 
-constexpr int BWD_MAX_PARTS = 16;
-
-// Slab width and row partitions. The per-slot form takes whole 128-byte lines
-// (32-column slabs) and the smallest power-of-two P (<= 16) that gives 256
-// workgroups (one per CU: a second workgroup on a CU stretches every token of
-// both, measured); the shared-residual form, which cannot split rows,
-// takes the widest slab that still gives 256 workgroups, else the one with the
-// most. SDM_BWD_SLAB and SDM_BWD_PARTS force a choice.
+// Slab width and row partitions. Both forms take the widest slab that still
+// gives 256 workgroups (one per CU: a second workgroup on a CU stretches every
+// token of both), else the one with the most, and one partition: partitions
+// multiply the wavefronts that step through every token, and with the token
+// loop's loads issued ahead that costs more than the extra rows in flight
+// bring (measured on the per-slot form: 16-column slabs without partitions
+// 16.4 ms against 19.2 ms for 32-column slabs in 2 partitions on 32 streams of
+// 8192 tokens). SDM_BWD_SLAB and SDM_BWD_PARTS (per-slot form only) force a
+// choice.
 struct BCfg {
     int S = 0, P = 1;
 };
 BCfg bwd_cfg(int64_t NS, int W, int R, int dv, int form) {
     BCfg c;
     const int fs = env_int("SDM_BWD_SLAB"), fp = env_int("SDM_BWD_PARTS");
-    if (form == 0 && (fs == 0 || fs == 32) && fp != 1 && bwd_fits(32, W, R, dv)) {
-        c.S = 32;
-    } else {
-        int64_t best_units = 0;
-        for (int S : {32, 16, 8, 4}) {
-            if ((fs && fs != S) || !bwd_fits(S, W, R, dv)) continue;
-            const int64_t units = NS * (dv / S);
-            if (c.S == 0 || (best_units < 256 && units > best_units)) {
-                c.S = S;
-                best_units = units;
-            }
-        }
-        if (c.S == 0) return c;
-    }
-    if (form == 0) {
-        if (fp == 1 || fp == 2 || fp == 4 || fp == 8 || fp == 16) {
-            c.P = fp;
-        } else {
-            const int64_t units = (NS > 0 ? NS : 1) * (dv / c.S);
-            while (c.P < BWD_MAX_PARTS && units * c.P < 256) c.P *= 2;
+    int64_t best_units = 0;
+    for (int S : {32, 16, 8, 4}) {
+        if ((fs && fs != S) || !bwd_fits(S, W, R, dv)) continue;
+        const int64_t units = NS * (dv / S);
+        if (c.S == 0 || (best_units < 256 && units > best_units)) {
+            c.S = S;
+            best_units = units;
         }
     }
+    if (c.S == 0) return c;
+    if (form == 0 && (fp == 2 || fp == 4 || fp == 8 || fp == 16)) c.P = fp;
     return c;
 }
 
@@ -423,11 +564,11 @@ int64_t bwd_chunk_tokens(int64_t T, int W, int dv) {
     return T < cap ? T : cap;
 }
 
-// Workspace of one launch of Tn tokens: pw, pr, pab, then (P > 1) pdv.
+// Workspace of one launch of Tn tokens: pw, pr, pab, (P > 1) pdv, then the plan.
 int64_t bwd_ws_floats(const BCfg& c, int64_t NS, int64_t Tn, int W, int R, int dv) {
     const int nslab = dv / c.S;
     return (int64_t)nslab * NS * Tn * (W + R) + (int64_t)nslab * c.P * NS * Tn * 2 +
-           (c.P > 1 ? (int64_t)c.P * NS * Tn * dv : 0);
+           (c.P > 1 ? (int64_t)c.P * NS * Tn * dv : 0) + NS * Tn * (W + 2 * R);
 }
 
 template <int S>
@@ -439,7 +580,6 @@ hipError_t launch_bwd_slab(const BwdArgs& a, const BCfg& c, hipStream_t st) {
     int psh = 0;
     while ((1 << psh) < c.P) ++psh;
     const int64_t nblk = ((a.NS + 7) / 8) * 8 * nslab * c.P;
-    const int esz = a.v_bf16 ? 2 : 4;
     const int64_t nchunk = (a.T + Tc - 1) / Tc;
     for (int64_t ci = nchunk - 1; ci >= 0; --ci) {  // the chunks in reverse
         const int64_t c0 = ci * Tc, Tn = a.T - c0 < Tc ? a.T - c0 : Tc;
@@ -455,16 +595,31 @@ hipError_t launch_bwd_slab(const BwdArgs& a, const BCfg& c, hipStream_t st) {
         k.TS = a.T; k.t0 = c0; k.T = (int)Tn; k.W = a.W; k.R = a.R;
         k.N = a.N; k.dv = a.dv; k.nslab = nslab; k.P = c.P; k.pshift = psh;
         k.NS = a.NS; k.NWW = g.NWW; k.NWR = g.NWR;
-        (void)esz;
         dim3 grid((unsigned)nblk), block((unsigned)((g.NWW + g.NWR) * 64));
         const int sel = (a.form ? 2 : 0) | (a.v_bf16 ? 1 : 0);
-        switch (sel) {
-            case 0: hipLaunchKernelGGL((scan_backward_kernel<S, 0, false>), grid, block, 0, st, k); break;
-            case 1: hipLaunchKernelGGL((scan_backward_kernel<S, 0, true>), grid, block, 0, st, k); break;
-            case 2: hipLaunchKernelGGL((scan_backward_kernel<S, 1, false>), grid, block, 0, st, k); break;
-            default: hipLaunchKernelGGL((scan_backward_kernel<S, 1, true>), grid, block, 0, st, k); break;
-        }
+        // the planner, then the reverse walk
+        uint32_t* plan = reinterpret_cast<uint32_t*>(k.pdv + (c.P > 1 ? (int64_t)c.P * a.NS * Tn * a.dv : 0));
+        BPlanArgs pa{};
+        pa.idx_w = a.idx_w + c0 * a.W; pa.idx_r = a.idx_r + c0 * a.R; pa.plan = plan;
+        pa.Tn = Tn; pa.TS = a.T; pa.N = a.N; pa.W = a.W; pa.R = a.R; pa.D = BWD_D;
+        // the hash holds (TT + D) * (W + R) entries at load <= 1/2 (W, R <= 256
+        // keeps TT >= 6); token fields have 10 bits
+        pa.TT = (BHT_CAP / 2) / (a.W + a.R) - BWD_D;
+        if (pa.TT > 1000) pa.TT = 1000;
+        if (pa.TT < 1) pa.TT = 1;
+        pa.ntile = (Tn + pa.TT - 1) / pa.TT;
+        hipLaunchKernelGGL(bwd_plan_kernel, dim3((unsigned)(pa.ntile * a.NS)), dim3(BPLAN_THREADS), 0, st, pa);
         hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        k.plan = plan;
+        const size_t lds = bwd_ring_bytes(S, a.W, a.R);
+        switch (sel) {
+            case 0: hipLaunchKernelGGL((scan_backward_kernel<S, 0, false>), grid, block, lds, st, k); break;
+            case 1: hipLaunchKernelGGL((scan_backward_kernel<S, 0, true>), grid, block, lds, st, k); break;
+            case 2: hipLaunchKernelGGL((scan_backward_kernel<S, 1, false>), grid, block, lds, st, k); break;
+            default: hipLaunchKernelGGL((scan_backward_kernel<S, 1, true>), grid, block, lds, st, k); break;
+        }
+        e = hipGetLastError();
         if (e != hipSuccess) return e;
         const int64_t n = a.NS * Tn * (a.W + a.R + 2 + (c.P > 1 ? a.dv : 0));
         const int64_t nb = (n + 255) / 256 < 8192 ? (n + 255) / 256 : 8192;

@@ -119,21 +119,20 @@ def test_training_sizes_are_pure_host_logic(lib):
     assert binding.sdm_scan_snapshot_bytes(4, 8, 8192, 64, 128) == 4 * 8 * 8192 * 64 * 128 * 4
     assert lib.sdm_scan_snapshot_bytes(1, 1, 1, 0, 16) == -1
     # backward partial sums: per (slab, stream, token) W + R weight gradients, per
-    # (slab, partition, stream, token) 2 gate gradients, and with P > 1 row
-    # partitions a partial dv per partition; the workspace covers both forms.
+    # (slab, partition, stream, token) 2 gate gradients, with P > 1 row
+    # partitions a partial dv per partition, and per (stream, token) the
+    # prefetch plan's W + 2R source words; the workspace covers both forms.
     def bwd(NS, T, S, P, W=64, R=64, dv=128):
         nslab = dv // S
-        return 4 * (nslab * NS * T * (W + R) + nslab * P * NS * T * 2 + (P * NS * T * dv if P > 1 else 0))
-    # 32 streams: per-slot form 32-column slabs with 2 partitions (256 workgroups);
-    # shared-residual form 16-column slabs (the widest with 256 workgroups)
-    assert binding.sdm_scan_backward_workspace_bytes(4, 8, 8192, 64, 64, 128) == \
-        max(bwd(32, 8192, 32, 2), bwd(32, 8192, 16, 1))
-    # 8 streams: 8 partitions / 4-column slabs; chunks of at most 2^31 / (W dv 4) tokens
-    assert binding.sdm_scan_backward_workspace_bytes(1, 8, 1000, 64, 64, 128) == \
-        max(bwd(8, 1000, 32, 8), bwd(8, 1000, 4, 1))
+        return 4 * (nslab * NS * T * (W + R) + nslab * P * NS * T * 2 + (P * NS * T * dv if P > 1 else 0)
+                    + NS * T * (W + 2 * R))
+    # both forms take the widest slab with 256 workgroups and one partition:
+    # 32 streams -> 16-column slabs; 8 streams -> 4-column slabs; chunks of at
+    # most 2^31 / (W dv 4) tokens
+    assert binding.sdm_scan_backward_workspace_bytes(4, 8, 8192, 64, 64, 128) == bwd(32, 8192, 16, 1)
+    assert binding.sdm_scan_backward_workspace_bytes(1, 8, 1000, 64, 64, 128) == bwd(8, 1000, 4, 1)
     Tc = 0x7FFFFFFF // (64 * 128 * 4)
-    assert binding.sdm_scan_backward_workspace_bytes(1, 8, 131072, 64, 64, 128) == \
-        max(bwd(8, Tc, 32, 8), bwd(8, Tc, 4, 1))
+    assert binding.sdm_scan_backward_workspace_bytes(1, 8, 131072, 64, 64, 128) == bwd(8, Tc, 4, 1)
     assert binding.sdm_scan_backward_workspace_bytes(0, 8, 100, 64, 64, 128) == 0
     assert lib.sdm_scan_backward_workspace_bytes(1, 1, 1, 300, 1, 16) == -1
 
