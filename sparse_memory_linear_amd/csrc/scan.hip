@@ -119,15 +119,18 @@ constexpr int nrmax() {
 //
 // One workgroup per (stream, tile of TT tokens). An LDS hash table holds every
 // write of tokens [t0 - D, t0 + TT) as a 32-bit entry (row << 14 | tok << pb |
-// rank) with tok the token relative to t0 - D; the table is kept at most half
-// full. A bitmap over all N rows marks the rows written anywhere in the tile,
+// rank) with tok the token relative to t0 - D; the table is kept at most a
+// quarter full. A bitmap over all N rows marks the rows written anywhere in the tile,
 // so the common access (no writer nearby) is settled by one LDS read; the
 // others look up the latest writer of their row inside their window. Each
 // wavefront handles whole tokens (lanes = access positions, ranks by ballot)
 // and issues the index loads of PNB tokens together.
 constexpr int HT_CAP = 16384;              // LDS hash table entries (32-bit): 64 KiB
 constexpr int HT_BITS = 14;
-constexpr int HT_WRITES = HT_CAP / 2;      // writes held per tile (load factor <= 1/2)
+constexpr int HT_WRITES = HT_CAP / 4;      // writes held per tile: at load <= 1/4 the probe chains,
+                                           // which a wavefront walks as long as its longest lane's,
+                                           // stay short (planner 550 -> 422 us against load 1/2 on
+                                           // 32 streams x 8192 tokens; load 1/8: 447 us)
 constexpr uint32_t HT_EMPTY = ~0u;         // never a valid entry (see the launch)
 constexpr int PLAN_WAVES = 8;
 constexpr int PLAN_THREADS = PLAN_WAVES * 64;
@@ -810,9 +813,9 @@ hipError_t launch_scan_slab(const ScanArgs& a, const Cfg& c, hipStream_t st) {
     static_assert(D <= 15, "the plan stores forward distances in 4 bits");
     const Geom& g = c.g;
     // planner: tiles of TT tokens; the hash table holds the writes of TT + D tokens
-    // at load <= 1/2. With pb = ceil(log2 W) (so 2^pb < 2W), the entry ids
-    // tok << pb | rank stay below (TT + D) << pb < 2 * HT_WRITES = 2^14, and the
-    // largest one is at most 2^14 - 2, so no entry equals HT_EMPTY.
+    // at load <= 1/4. With pb = ceil(log2 W) (so 2^pb < 2W), the entry ids
+    // tok << pb | rank stay below (TT + D) << pb < 2 * HT_WRITES = 2^13 < 2^14, so
+    // no entry equals HT_EMPTY.
     int pb = 0;
     while ((1 << pb) < a.W) ++pb;
     int psh = 0;

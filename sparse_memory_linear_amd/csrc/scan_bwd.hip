@@ -107,7 +107,7 @@ __device__ __forceinline__ uint32_t bht_hash(uint32_t row) { return (row * 26544
 
 // One workgroup per (stream, tile of TT tokens [u0, u1)): an LDS hash holds every
 // access of tokens [u0, u1 + D) as (row << 32 | token - u0 << 10 | is_write << 9 |
-// position), at most half full; each access of the tile then walks its row's
+// position), at most a quarter full; each access of the tile then walks its row's
 // entries and keeps the nearest later touch and write.
 __global__ __launch_bounds__(BPLAN_THREADS) void bwd_plan_kernel(BPlanArgs a) {
     __shared__ uint64_t ht[BHT_CAP];
@@ -602,9 +602,10 @@ hipError_t launch_bwd_slab(const BwdArgs& a, const BCfg& c, hipStream_t st) {
         BPlanArgs pa{};
         pa.idx_w = a.idx_w + c0 * a.W; pa.idx_r = a.idx_r + c0 * a.R; pa.plan = plan;
         pa.Tn = Tn; pa.TS = a.T; pa.N = a.N; pa.W = a.W; pa.R = a.R; pa.D = BWD_D;
-        // the hash holds (TT + D) * (W + R) entries at load <= 1/2 (W, R <= 256
-        // keeps TT >= 6); token fields have 10 bits
-        pa.TT = (BHT_CAP / 2) / (a.W + a.R) - BWD_D;
+        // the hash holds (TT + D) * (W + R) entries at load <= 1/4, which keeps the
+        // probe chains a wavefront walks short (W, R <= 256 keeps TT >= 2); token
+        // fields have 10 bits
+        pa.TT = (BHT_CAP / 4) / (a.W + a.R) - BWD_D;
         if (pa.TT > 1000) pa.TT = 1000;
         if (pa.TT < 1) pa.TT = 1;
         pa.ntile = (Tn + pa.TT - 1) / pa.TT;
