@@ -12,6 +12,9 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libsdm.so")
 OBJ = os.path.join(PKG, "_build")
 SOURCES = ["sdm_api.hip", "address.hip", "scan.hip", "scan_bwd.hip", "state_init.hip", "glue.hip"]
+# the measurement aid behind `bench.py --gather-probe`, in a library of its own
+PROBE_LIB = os.path.join(PKG, "libsdm_probe.so")
+PROBE_SOURCES = ["probe_gather.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
@@ -29,18 +32,24 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    os.makedirs(OBJ, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=4) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, out: str) -> None:
+    tmp = out + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = True) -> str:
+    os.makedirs(OBJ, exist_ok=True)
+    with concurrent.futures.ThreadPoolExecutor(max_workers=4) as ex:
+        objs = list(ex.map(_compile, SOURCES + PROBE_SOURCES))
+    n = len(SOURCES)
+    _link(objs[:n], LIB)
+    _link(objs[n:], PROBE_LIB)
     if verbose:
-        print(f"built {LIB}", file=sys.stderr)
+        print(f"built {LIB} and {PROBE_LIB}", file=sys.stderr)
     return LIB
 
 
