@@ -144,6 +144,33 @@ def test_direct_short_scan_matches_oracle(case, form, oform, monkeypatch):
     _check("direct", Mg, yg, Mo, yo, c["M_in"], c["idx_w"], TOL_F32)
 
 
+@pytest.mark.parametrize("overlap", ["all", "half"])
+@pytest.mark.parametrize("form,oform", FORMS, ids=["eq4", "fig2"])
+def test_direct_reads_of_rows_the_token_writes(overlap, form, oform, monkeypatch):
+    """Direct form with reads on the rows the same token writes: every read
+    (read set a permutation of the write set) or half of them. The reader
+    loads its row with the writers, before they store, so each such read must
+    take the token's new row from the writers instead (read-after-write within
+    a token, SDM notes §2.4)."""
+    monkeypatch.setenv("SDM_SCAN_DIRECT_T", "100000")
+    say(f"[scan direct, reads on written rows] overlap={overlap} form={form}")
+    rng = np.random.default_rng(11)
+    c = _random_case(12, B=2, H=2, T=60, N=512, dv=64, W=32, R=32)
+    B, H, T, W = c["idx_w"].shape
+    for b in range(B):
+        for h in range(H):
+            for t in range(T):
+                w = c["idx_w"][b, h, t]
+                if overlap == "all":
+                    c["idx_r"][b, h, t] = rng.permutation(w)
+                else:
+                    others = np.setdiff1d(np.arange(512), w)
+                    c["idx_r"][b, h, t] = rng.permutation(np.concatenate([w[:16], rng.choice(others, 16, False)]))
+    Mo, yo = oracle.scan(**c, form=oform)
+    Mg, yg = _run_gpu(**c, form=form)
+    _check("direct read-on-write", Mg, yg, Mo, yo, c["M_in"], c["idx_w"], TOL_F32)
+
+
 def test_decode_one_token_per_call_matches_one_scan():
     """Decoding: T = 1 per call, the table carried between calls, equals the
     oracle's scan over the whole sequence."""
