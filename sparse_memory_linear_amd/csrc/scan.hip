@@ -34,9 +34,10 @@
 // its buffer, which the hardware drops (loads return 0). Writer entries carry
 // alpha and beta next to the weight, so a writer issues one plan load per token.
 //
-// Placement: workgroups are dealt to the 8 XCDs round-robin, so blockIdx is
-// remapped to put every slab of a stream on the same XCD; the slabs of a row
-// then share that XCD's L2 lines.
+// Placement: workgroups are dealt to the 8 XCDs round-robin, so with at least
+// 8 streams blockIdx is remapped to put every slab of a stream on the same XCD
+// (the slabs of a row then share that XCD's L2 lines and the plan records);
+// with fewer streams a stream's slabs are spread over all XCDs.
 #include "sdm_buffer.h"
 #include "sdm_internal.h"
 
@@ -397,9 +398,10 @@ __global__ __launch_bounds__(SlabCfg<SL>::NWMAX * 64) void scan_kernel(ScanKArgs
     float4* vbuf = reinterpret_cast<float4*>(ybuf + 2 * NRMAX * S);  // [NWW][S/4] (FIG2)
 
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane / L, cc = lane % L;
-    const int b = blockIdx.x, xcd = b & 7, kq = b >> 3, units = a.nslab * a.P;
-    const int64_t s = (int64_t)(kq / units) * 8 + xcd;
-    const int slab = kq % a.nslab, part = (kq % units) / a.nslab;
+    int64_t s;
+    int kq;
+    block_unit(blockIdx.x, a.NS, a.nslab * a.P, s, kq);
+    const int slab = kq % a.nslab, part = kq / a.nslab;
     if (s >= a.NS) return;  // uniform over the workgroup
     const int col = slab * S + cc * CPL;
     const Geom geo{SL, G, NWW, NWR};
@@ -636,9 +638,9 @@ __global__ __launch_bounds__(SlabCfg<SL>::NWMAX * 64) void scan_direct_kernel(Di
     __shared__ float4 vbuf[NWMAX * S / 4];
 
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane / L, cc = lane % L;
-    const int b = blockIdx.x, xcd = b & 7, kq = b >> 3;
-    const int64_t s = (int64_t)(kq / a.nslab) * 8 + xcd;
-    const int slab = kq % a.nslab;
+    int64_t s;
+    int slab;
+    block_unit(blockIdx.x, a.NS, a.nslab, s, slab);
     if (s >= a.NS) return;  // uniform over the workgroup
     const int col = slab * S + cc * CPL;
     const bool writer = wave < NWW;
@@ -827,7 +829,7 @@ hipError_t launch_scan_slab(const ScanArgs& a, const Cfg& c, hipStream_t st) {
     const WsLayout wl = ws_layout(c, a.NS, Tc, a.dv);
     const int cpl = a.m_bf16 ? 8 : 4;
     const int nslab = a.dv / (SL / 4 * cpl);
-    const int64_t nblk = ((a.NS + 7) / 8) * 8 * nslab * c.P;
+    const int64_t nblk = unit_grid(a.NS, (int64_t)nslab * c.P);
     const size_t lds = scan_lds_bytes<SL>(g, cpl);
     const size_t bm_bytes = (size_t)((a.N + 31) / 32) * 4;
     const int esz = a.v_bf16 ? 2 : 4;
@@ -893,7 +895,7 @@ hipError_t launch_scan_direct(const ScanArgs& a, hipStream_t st) {
     d.T = (int)a.T; d.N = a.N; d.dv = a.dv; d.nslab = a.dv / (SL / 4 * (a.m_bf16 ? 8 : 4)); d.NS = a.NS;
     d.NWW = g.NWW; d.NWR = g.NWR;
     d.snap = a.snap;
-    const int64_t nblk = ((a.NS + 7) / 8) * 8 * d.nslab;
+    const int64_t nblk = unit_grid(a.NS, d.nslab);
     dim3 grid((unsigned)nblk), block((unsigned)(g.nw() * 64));
     const int sel = (a.form ? 8 : 0) | (a.v_bf16 ? 4 : 0) | (a.snap ? 2 : 0) | (a.m_bf16 ? 1 : 0);
     switch (sel) {
@@ -970,13 +972,18 @@ int pick_slab(int64_t NS, int W, int R, int dv, int cpl, int forced) {
 }
 
 // The per-slot form (EQ4) never couples two rows, so it may split the rows into
-// partitions; then every workgroup reads and writes whole 128-byte lines
-// (8 lanes of 16 bytes per row: 32 fp32 or 64 bf16 columns) and the partitions
-// supply the workgroups that narrower slabs would: P is the smallest power of
-// two (at most 8) that gives 256 workgroups. The per-CU count of outstanding
-// line misses is what bounds the scan, so a line that carries 128 useful bytes
-// instead of 32 or 64 is worth more than the extra padding lanes of a
-// partitioned record. The shared-residual form (FIG2) couples all rows of a
+// partitions, each walked by its own workgroups. With an fp32 table it takes
+// whole 128-byte lines (32-column slabs) when at most 2 partitions give 256
+// workgroups (many streams: the per-CU line misses in flight bound the scan,
+// and a line that carries 128 useful bytes is worth more than the padding
+// lanes of a partitioned record), else 16-column slabs (the 8-wavefront layout
+// with its deeper prefetch) and the smallest power-of-two P <= 4 towards 256
+// workgroups: with few streams the per-token chain of a workgroup bounds the
+// loop. Measured on MI355X, scan call in ms (32-col/P against 16-col/P):
+// 32 streams, W=R=64, d_v=128: 5.56 (32/2) against 6.70 (16/1); 8 streams x
+// 131072 tokens: 39.5 (32/8) against 38.2 (16/4); one stream, W=R=8, d_v=512:
+// 29.1 (32/8) against 11.3 (16/4); 16 streams, W=R=16, d_v=64: 2.11 (32/8)
+// against 0.94 (16/4). The shared-residual form (FIG2) couples all rows of a
 // token and keeps P = 1.
 // A bf16 table halves the bytes of every access, so its loop is bound by the
 // per-token work of a workgroup rather than by line misses: there the 8-wavefront
@@ -990,8 +997,12 @@ Cfg choose_cfg(int64_t NS, int W, int R, int dv, int form, int cpl) {
     const int fs = env_int("SDM_SCAN_SLAB"), fp = env_int("SDM_SCAN_PARTS");
     const int64_t ns = NS > 0 ? NS : 1;
     int want = 256;  // workgroups the partitions should reach
-    if (form == 0 && cpl == 4 && (fs == 0 || fs == 32) && slab_fits(32, W, R, dv, cpl) && fp != 1) {
+    int pcap = MAX_PARTS;
+    if (form == 0 && cpl == 4 && fs == 0 && slab_fits(32, W, R, dv, cpl) && ns * (dv / 32) * 2 >= 256) {
         c.S = 32;
+    } else if (form == 0 && cpl == 4 && fs == 0 && slab_fits(16, W, R, dv, cpl)) {
+        c.S = 16;
+        pcap = 4;
     } else if (form == 0 && cpl == 8 && fs == 0 && slab_fits(16, W, R, dv, cpl) && slab_fits(8, W, R, dv, cpl)) {
         const bool many = ns * (dv / 32) >= 128;
         c.S = many ? 16 : 8;
@@ -1005,7 +1016,7 @@ Cfg choose_cfg(int64_t NS, int W, int R, int dv, int form, int cpl) {
             c.P = fp;
         } else {
             const int64_t units = ns * (dv / (c.S / 4 * cpl));
-            while (c.P < MAX_PARTS && units * c.P < want) c.P *= 2;
+            while (c.P < pcap && units * c.P < want) c.P *= 2;
         }
     }
     c.g = make_geom(c.S, W, R);

@@ -223,9 +223,10 @@ __global__ __launch_bounds__(BWD_NWMAX * 64) void scan_backward_kernel(BwdKArgs 
     const int NWW = a.NWW, T = a.T, dv = a.dv, W = a.W, R = a.R, KR = W + R, RW = W + 2 * R;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63, r = lane / L,
               cc = lane % L;
-    const int b = blockIdx.x, xcd = b & 7, kq = b >> 3, units = a.nslab * a.P;
-    const int64_t s = (int64_t)(kq / units) * 8 + xcd;
-    const int slab = kq % a.nslab, part = (kq % units) / a.nslab;
+    int64_t s;
+    int kq;
+    block_unit(blockIdx.x, a.NS, a.nslab * a.P, s, kq);
+    const int slab = kq % a.nslab, part = kq / a.nslab;
     if (s >= a.NS) return;  // uniform over the workgroup
     const int col = slab * S + cc * 4;
     const bool writer = wave < NWW;
@@ -579,7 +580,7 @@ hipError_t launch_bwd_slab(const BwdArgs& a, const BCfg& c, hipStream_t st) {
     float* pw = static_cast<float*>(a.workspace);
     int psh = 0;
     while ((1 << psh) < c.P) ++psh;
-    const int64_t nblk = ((a.NS + 7) / 8) * 8 * nslab * c.P;
+    const int64_t nblk = unit_grid(a.NS, (int64_t)nslab * c.P);
     const int64_t nchunk = (a.T + Tc - 1) / Tc;
     for (int64_t ci = nchunk - 1; ci >= 0; --ci) {  // the chunks in reverse
         const int64_t c0 = ci * Tc, Tn = a.T - c0 < Tc ? a.T - c0 : Tc;

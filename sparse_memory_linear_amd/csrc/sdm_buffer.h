@@ -40,6 +40,25 @@ __device__ __forceinline__ void st_f1(float v, rsrc_t r, uint32_t vo, uint32_t s
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, (int)vo, (int)so, 0);
 }
 
+// Workgroup -> (stream, unit of that stream: a column slab, or a slab and row
+// partition). The hardware deals workgroups to the 8 XCDs round-robin
+// (blockIdx mod 8). With at least 8 streams, all units of a stream go to one
+// XCD, so its slabs share that XCD's L2 for the rows' lines and for the plan
+// records they all read; with fewer, a stream's units are dealt over all 8
+// XCDs, since one XCD's 32 CUs would otherwise carry every workgroup.
+__device__ __forceinline__ void block_unit(int b, int64_t NS, int units, int64_t& s, int& u) {
+    if (NS >= 8) {
+        s = (int64_t)((b >> 3) / units) * 8 + (b & 7);
+        u = (b >> 3) % units;
+    } else {
+        s = b / units;
+        u = b % units;
+    }
+}
+// Workgroups to launch for NS streams of `units` units each (with at least 8
+// streams, rounded up to whole XCD rounds; the extra ones return at once).
+inline int64_t unit_grid(int64_t NS, int64_t units) { return NS >= 8 ? ((NS + 7) / 8) * 8 * units : NS * units; }
+
 // v_t of this lane's 4 columns.
 template <bool BF16>
 struct VLoad;
