@@ -196,29 +196,36 @@ __global__ __launch_bounds__(BPLAN_THREADS) void bwd_plan_kernel(BPlanArgs a) {
 // previous token. Every token leaves the adjoint rows it produced (writers' and
 // readers' new G) in an LDS ring of D + 1 token slots [slot][W + R][L], where
 // later-processed tokens of the window find them.
-// D = 2 measured best on MI355X: D = 1 is as fast for the per-slot form and 5 %
-// slower for the shared-residual one; D = 3 no longer fits 128 VGPRs (spills)
-// and runs about twice as long.
+// Two instantiations: up to 16 wavefronts per workgroup (128 VGPRs) with
+// D = 2, and up to 8 wavefronts (256 VGPRs) with D = 4, which every layout of
+// at most 8 wavefronts takes. Measured on MI355X: with 16 wavefronts, D = 1 is
+// as fast as D = 2 for the per-slot form and 5 % slower for the shared-residual
+// one, and D = 3 no longer fits 128 VGPRs (spills) and runs about twice as
+// long; with 8 wavefronts, D = 4 against D = 2 takes one stream of 65536 tokens
+// (W = R = 8, d_v = 512) from 75 to 65 ms and 16 streams of 4096 tokens from
+// 4.8 to 4.2 ms, while D = 6 spills with fp32 v and is slower there (88, 5.5).
 constexpr int BWD_D = 2;
+constexpr int BWD_D_DEEP = 4;
+constexpr int BWD_NW_DEEP = 8;
+static_assert(BWD_D_DEEP <= 7, "plan words keep the distance in 3 bits");
 
 __device__ __forceinline__ uint32_t ld_u1(rsrc_t r, uint32_t vo, uint32_t so) {
     return __builtin_amdgcn_raw_buffer_load_b32(r, (int)vo, (int)so, 0);
 }
 
-template <int S, int FORM, bool VBF16>
-__global__ __launch_bounds__(BWD_NWMAX * 64) void scan_backward_kernel(BwdKArgs a) {
+template <int S, int FORM, bool VBF16, int D, int NWM>
+__global__ __launch_bounds__(NWM * 64) void scan_backward_kernel(BwdKArgs a) {
     constexpr int L = S / 4, G = 64 / L;
     using VL = VLoad<VBF16>;
     using V4 = typename VL::T4;
-    constexpr int D = BWD_D;
     constexpr int DM = D + 1;
     constexpr int UP = D + 1;          // value/row ring
     constexpr int U = D + DM + 1;      // address ring = unroll factor (a multiple of UP)
     static_assert(U % UP == 0, "ring sizes");
     constexpr int UR = D + 1;          // LDS ring slots
     extern __shared__ float4 lring[];  // [UR][W + R][L]
-    __shared__ float4 xb[2][BWD_NWMAX][L];
-    __shared__ float ab[BWD_NWMAX][2];
+    __shared__ float4 xb[2][NWM][L];
+    __shared__ float ab[NWM][2];
 
     const int NWW = a.NWW, T = a.T, dv = a.dv, W = a.W, R = a.R, KR = W + R, RW = W + 2 * R;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63, r = lane / L,
@@ -257,7 +264,7 @@ __global__ __launch_bounds__(BWD_NWMAX * 64) void scan_backward_kernel(BwdKArgs 
     float* pr = a.pr + ps * T * R;
     float* pab = a.pab + ((int64_t)(slab * a.P + part) * a.NS + s) * T * 2;
 
-    for (int i = threadIdx.x; i < 2 * BWD_NWMAX * L; i += blockDim.x)
+    for (int i = threadIdx.x; i < 2 * NWM * L; i += blockDim.x)
         (&xb[0][0][0])[i] = make_float4(0.f, 0.f, 0.f, 0.f);
     __syncthreads();
 
@@ -336,7 +343,7 @@ __global__ __launch_bounds__(BWD_NWMAX * 64) void scan_backward_kernel(BwdKArgs 
         if constexpr (FORM == 0) {
             float acc = 0.f;
 #pragma unroll
-            for (int q = 0; q < BWD_NWMAX; ++q)
+            for (int q = 0; q < NWM; ++q)
                 acc += reinterpret_cast<const float*>(xb[0][q])[lane < S ? lane : 0];
             st_f1(acc, Ro, lane < S ? (uint32_t)(slab * S + lane) * 4u : OOB, (uint32_t)tk * dv4);
         }
@@ -515,14 +522,20 @@ BGeom bwd_geom(int S, int W, int R) {
     return g;
 }
 // LDS of the prefetching form: the ring of D + 1 token slots of W + R rows.
-size_t bwd_ring_bytes(int S, int W, int R) {
-    return (size_t)(BWD_D + 1) * (W + R) * (S / 4) * 16;
+size_t bwd_ring_bytes(int S, int W, int R, int D) {
+    return (size_t)(D + 1) * (W + R) * (S / 4) * 16;
 }
 
 bool bwd_fits(int S, int W, int R, int dv) {
     if (dv % S != 0) return false;
     const BGeom g = bwd_geom(S, W, R);
-    return g.NWW + g.NWR <= BWD_NWMAX && bwd_ring_bytes(S, W, R) <= 128 * 1024;
+    return g.NWW + g.NWR <= BWD_NWMAX && bwd_ring_bytes(S, W, R, BWD_D) <= 128 * 1024;
+}
+
+// The deeper instantiation: at most 8 wavefronts and its ring within 128 KiB.
+bool bwd_deep(int S, int W, int R) {
+    const BGeom g = bwd_geom(S, W, R);
+    return g.NWW + g.NWR <= BWD_NW_DEEP && bwd_ring_bytes(S, W, R, BWD_D_DEEP) <= 128 * 1024;
 }
 
 int env_int(const char* name) {
@@ -602,11 +615,14 @@ hipError_t launch_bwd_slab(const BwdArgs& a, const BCfg& c, hipStream_t st) {
         uint32_t* plan = reinterpret_cast<uint32_t*>(k.pdv + (c.P > 1 ? (int64_t)c.P * a.NS * Tn * a.dv : 0));
         BPlanArgs pa{};
         pa.idx_w = a.idx_w + c0 * a.W; pa.idx_r = a.idx_r + c0 * a.R; pa.plan = plan;
-        pa.Tn = Tn; pa.TS = a.T; pa.N = a.N; pa.W = a.W; pa.R = a.R; pa.D = BWD_D;
+        const bool deep = bwd_deep(S, a.W, a.R);
+        const int D = deep ? BWD_D_DEEP : BWD_D;
+        pa.Tn = Tn; pa.TS = a.T; pa.N = a.N; pa.W = a.W; pa.R = a.R; pa.D = D;
         // the hash holds (TT + D) * (W + R) entries at load <= 1/4, which keeps the
-        // probe chains a wavefront walks short (W, R <= 256 keeps TT >= 2); token
-        // fields have 10 bits
-        pa.TT = (BHT_CAP / 4) / (a.W + a.R) - BWD_D;
+        // probe chains a wavefront walks short; with TT clamped to 1 (W + R > 292
+        // at D = 6) it holds at most 7 * 512 of its 8192 entries; token fields
+        // have 10 bits
+        pa.TT = (BHT_CAP / 4) / (a.W + a.R) - D;
         if (pa.TT > 1000) pa.TT = 1000;
         if (pa.TT < 1) pa.TT = 1;
         pa.ntile = (Tn + pa.TT - 1) / pa.TT;
@@ -614,12 +630,17 @@ hipError_t launch_bwd_slab(const BwdArgs& a, const BCfg& c, hipStream_t st) {
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         k.plan = plan;
-        const size_t lds = bwd_ring_bytes(S, a.W, a.R);
-        switch (sel) {
-            case 0: hipLaunchKernelGGL((scan_backward_kernel<S, 0, false>), grid, block, lds, st, k); break;
-            case 1: hipLaunchKernelGGL((scan_backward_kernel<S, 0, true>), grid, block, lds, st, k); break;
-            case 2: hipLaunchKernelGGL((scan_backward_kernel<S, 1, false>), grid, block, lds, st, k); break;
-            default: hipLaunchKernelGGL((scan_backward_kernel<S, 1, true>), grid, block, lds, st, k); break;
+        const size_t lds = bwd_ring_bytes(S, a.W, a.R, D);
+        constexpr int DD = BWD_D_DEEP, D2 = BWD_D, N8 = BWD_NW_DEEP, N16 = BWD_NWMAX;
+        switch (sel | (deep ? 4 : 0)) {
+            case 0: hipLaunchKernelGGL((scan_backward_kernel<S, 0, false, D2, N16>), grid, block, lds, st, k); break;
+            case 1: hipLaunchKernelGGL((scan_backward_kernel<S, 0, true, D2, N16>), grid, block, lds, st, k); break;
+            case 2: hipLaunchKernelGGL((scan_backward_kernel<S, 1, false, D2, N16>), grid, block, lds, st, k); break;
+            case 3: hipLaunchKernelGGL((scan_backward_kernel<S, 1, true, D2, N16>), grid, block, lds, st, k); break;
+            case 4: hipLaunchKernelGGL((scan_backward_kernel<S, 0, false, DD, N8>), grid, block, lds, st, k); break;
+            case 5: hipLaunchKernelGGL((scan_backward_kernel<S, 0, true, DD, N8>), grid, block, lds, st, k); break;
+            case 6: hipLaunchKernelGGL((scan_backward_kernel<S, 1, false, DD, N8>), grid, block, lds, st, k); break;
+            default: hipLaunchKernelGGL((scan_backward_kernel<S, 1, true, DD, N8>), grid, block, lds, st, k); break;
         }
         e = hipGetLastError();
         if (e != hipSuccess) return e;
