@@ -267,3 +267,19 @@ def test_backward_full_size_sampled_streams():
         got["dM_in"] = sl(dM).cpu().numpy()
         _check_grads(f"stream ({b},{h})", got, ref, TOL_BF16)
         assert np.array_equal(sl(M).cpu().numpy(), M0)
+
+
+@pytest.mark.parametrize("B,H", [(5, 1), (7, 1), (3, 3), (3, 4)], ids=["NS5", "NS7", "NS9", "NS12"])
+@pytest.mark.parametrize("form,oform", [("eq4", oracle.EQ4), ("fig2", oracle.FIG2)], ids=["eq4", "fig2"])
+def test_backward_stream_counts_around_one_round_of_xcds(B, H, form, oform):
+    """Fewer than 8 streams deal each stream's workgroups over all XCDs; 8 or
+    more keep a stream on one XCD and round the grid up to whole rounds of 8:
+    stream counts on both sides of that boundary, every stream checked."""
+    say(f"[backward streams] B={B} H={H} form={form}")
+    case = dict(B=B, H=H, T=90, N=512, dv=64, W=16, R=16)
+    c = _random_case(21, **case)
+    dy, dM = _cotangents(22, B, H, 90, 512, 64)
+    ref = oracle.scan_backward(**c, dy=dy, dM_out=dM, form=oform)
+    _, _, _, got, M_back = _gpu_train(c, dy, dM, form)
+    _check_grads(f"NS={B * H}", got, ref, TOL_F32)
+    assert np.array_equal(M_back.view(np.uint32), c["M_in"].view(np.uint32))

@@ -171,6 +171,25 @@ def test_direct_reads_of_rows_the_token_writes(overlap, form, oform, monkeypatch
     _check("direct read-on-write", Mg, yg, Mo, yo, c["M_in"], c["idx_w"], TOL_F32)
 
 
+@pytest.mark.parametrize("B,H", [(5, 1), (7, 1), (3, 3), (3, 4)], ids=["NS5", "NS7", "NS9", "NS12"])
+@pytest.mark.parametrize("form,oform", FORMS, ids=["eq4", "fig2"])
+def test_stream_counts_around_one_round_of_xcds(B, H, form, oform):
+    """Fewer than 8 streams deal each stream's workgroups over all XCDs; 8 or
+    more keep a stream on one XCD and round the grid up to whole rounds of 8:
+    stream counts on both sides of that boundary, every stream checked, for the
+    pipelined scan and the direct short-call form."""
+    say(f"[scan streams] B={B} H={H} form={form}")
+    c = _random_case(23, B=B, H=H, T=120, N=512, dv=64, W=16, R=16)
+    Mo, yo = oracle.scan(**c, form=oform)
+    Mg, yg = _run_gpu(**c, form=form)
+    _check(f"NS={B * H}", Mg, yg, Mo, yo, c["M_in"], c["idx_w"], TOL_F32)
+    c2 = {k: v if k == "M_in" else (v[:, :, :6].contiguous() if isinstance(v, torch.Tensor) else
+                                     np.ascontiguousarray(v[:, :, :6])) for k, v in c.items()}
+    Mo2, yo2 = oracle.scan(**c2, form=oform)
+    Mg2, yg2 = _run_gpu(**c2, form=form)   # 6 tokens: the direct form
+    _check(f"NS={B * H} direct", Mg2, yg2, Mo2, yo2, c2["M_in"], c2["idx_w"], TOL_F32)
+
+
 def test_decode_one_token_per_call_matches_one_scan():
     """Decoding: T = 1 per call, the table carried between calls, equals the
     oracle's scan over the whole sequence."""
