@@ -224,8 +224,10 @@ __global__ __launch_bounds__(NWM * 64) void scan_backward_kernel(BwdKArgs a) {
     static_assert(U % UP == 0, "ring sizes");
     constexpr int UR = D + 1;          // LDS ring slots
     extern __shared__ float4 lring[];  // [UR][W + R][L]
+    // per-slot form: each writer's dv partial, by token parity; shared-residual
+    // form: the writers' partials of gh (0) and s (1) within a token
     __shared__ float4 xb[2][NWM][L];
-    __shared__ float ab[NWM][2];
+    __shared__ float ab[2][NWM][2];  // each writer's gate-gradient partials, by token parity
 
     const int NWW = a.NWW, T = a.T, dv = a.dv, W = a.W, R = a.R, KR = W + R, RW = W + 2 * R;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63, r = lane / L,
@@ -338,16 +340,20 @@ __global__ __launch_bounds__(NWM * 64) void scan_backward_kernel(BwdKArgs a) {
         return x;
     };
 
-    // wavefront 0: token tk's dv (per-slot form) and gate partial sums
+    // the first reader wavefront, while the writers work on the next token: token
+    // tk's dv (per-slot form) and gate-gradient sums over the writers' partials
+    // (kept by token parity, so the next token's writers do not overwrite them)
     auto finish = [&](int tk) {
+        const int par = tk & 1;
         if constexpr (FORM == 0) {
             float acc = 0.f;
 #pragma unroll
             for (int q = 0; q < NWM; ++q)
-                acc += reinterpret_cast<const float*>(xb[0][q])[lane < S ? lane : 0];
+                acc += reinterpret_cast<const float*>(xb[par][q])[lane < S ? lane : 0];
             st_f1(acc, Ro, lane < S ? (uint32_t)(slab * S + lane) * 4u : OOB, (uint32_t)tk * dv4);
         }
-        const float sa = wave_sum(lane < NWW ? ab[lane][0] : 0.f), sb = wave_sum(lane < NWW ? ab[lane][1] : 0.f);
+        const float sa = wave_sum(lane < NWW ? ab[par][lane][0] : 0.f);
+        const float sb = wave_sum(lane < NWW ? ab[par][lane][1] : 0.f);
         st_f1(lane == 0 ? sa : sb, Rpab, lane < 2 ? (uint32_t)lane * 4u : OOB, (uint32_t)tk * 8u);
     };
 
@@ -364,7 +370,7 @@ __global__ __launch_bounds__(NWM * 64) void scan_backward_kernel(BwdKArgs a) {
         const bool own = owns_pos(row, off) && cc == 0;
         if (writer) {
             const float4 m = x.x;  // the pre-image M_{t-1}[i]
-            if (wave == 0 && tl + 1 < T) finish(tl + 1);
+            const int par = tl & 1;
             __syncthreads();       // B1: this token's readers' new G values are in the ring
             float4 g = x.g;
             if (fwd) g = ring_at(fslot, fpos);
@@ -374,7 +380,7 @@ __global__ __launch_bounds__(NWM * 64) void scan_backward_kernel(BwdKArgs a) {
                 const float bw = be * w, c1 = 1.f - bw;
                 const float4 u = f4_sub(VL::f(v_of(x.y)), f4_scale(al, m));
                 const float part = rows_reduce<L>(f4_scale(bw, g));
-                if ((lane & 15) < L) reinterpret_cast<float*>(xb[0][wave])[4 * (lane & 15) + (lane >> 4)] = part;
+                if ((lane & 15) < L) reinterpret_cast<float*>(xb[par][wave])[4 * (lane & 15) + (lane >> 4)] = part;
                 float da = 0.f, db = 0.f;
                 if (run) {
                     const float gm = dot4(g, m), gu = dot4(g, u);
@@ -386,8 +392,8 @@ __global__ __launch_bounds__(NWM * 64) void scan_backward_kernel(BwdKArgs a) {
                     if (off != OOB) ring_at(slot, pos) = gn;
                 }
                 if (lane == 0) {
-                    ab[wave][0] = da;
-                    ab[wave][1] = db;
+                    ab[par][wave][0] = da;
+                    ab[par][wave][1] = db;
                 }
             } else {
                 const float pg = rows_reduce<L>(f4_scale(w, g)), pm = rows_reduce<L>(f4_scale(w, m));
@@ -410,8 +416,8 @@ __global__ __launch_bounds__(NWM * 64) void scan_backward_kernel(BwdKArgs a) {
                 st_f4(f4_scale(be, gh), Ro, lead ? col4 : OOB, (uint32_t)tl * dv4);
                 const float da = wave_sum(xa), db = wave_sum(xc);
                 if (lane == 0) {
-                    ab[wave][0] = da;
-                    ab[wave][1] = db;
+                    ab[par][wave][0] = da;
+                    ab[par][wave][1] = db;
                 }
                 gn = f4_sub(f4_scale(al, g), f4_scale(al * be * w, gh));
                 if (off != OOB) ring_at(slot, pos) = gn;
@@ -434,6 +440,7 @@ __global__ __launch_bounds__(NWM * 64) void scan_backward_kernel(BwdKArgs a) {
             st_f1(off == OOB ? 0.f : dr, Rpr, own ? (uint32_t)pos * 4u : OOB, (uint32_t)tl * (uint32_t)R * 4u);
             __syncthreads();                           // B1
             if constexpr (FORM == 1) __syncthreads();  // BX
+            if (rw == 0 && tl + 1 < T) finish(tl + 1);
             __syncthreads();                           // B2
         }
         slot = slot == 0 ? UR - 1 : slot - 1;
@@ -466,7 +473,7 @@ __global__ __launch_bounds__(NWM * 64) void scan_backward_kernel(BwdKArgs a) {
         const Ad d = fetch_ad(tl);
         process(tl, d, fetch_va(tl, d));
     }
-    if (wave == 0) finish(0);
+    if (wave == NWW) finish(0);
 }
 
 // dwt_w, dwt_r, dalpha, dbeta of one launch: the slabs' partial sums added in
