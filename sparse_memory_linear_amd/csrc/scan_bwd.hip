@@ -227,7 +227,7 @@ __global__ __launch_bounds__(NWM * 64) void scan_backward_kernel(BwdKArgs a) {
     // per-slot form: each writer's dv partial, by token parity; shared-residual
     // form: the writers' partials of gh (0) and s (1) within a token
     __shared__ float4 xb[2][NWM][L];
-    __shared__ float ab[2][NWM][2];  // each writer's gate-gradient partials, by token parity
+    __shared__ float ab[2][NWM][2][64];  // each writer lane's gate-gradient terms, by token parity
 
     const int NWW = a.NWW, T = a.T, dv = a.dv, W = a.W, R = a.R, KR = W + R, RW = W + 2 * R;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63, r = lane / L,
@@ -352,8 +352,12 @@ __global__ __launch_bounds__(NWM * 64) void scan_backward_kernel(BwdKArgs a) {
                 acc += reinterpret_cast<const float*>(xb[par][q])[lane < S ? lane : 0];
             st_f1(acc, Ro, lane < S ? (uint32_t)(slab * S + lane) * 4u : OOB, (uint32_t)tk * dv4);
         }
-        const float sa = wave_sum(lane < NWW ? ab[par][lane][0] : 0.f);
-        const float sb = wave_sum(lane < NWW ? ab[par][lane][1] : 0.f);
+        float pa = 0.f, pb = 0.f;
+        for (int q = 0; q < NWW; ++q) {
+            pa += ab[par][q][0][lane];
+            pb += ab[par][q][1][lane];
+        }
+        const float sa = wave_sum(pa), sb = wave_sum(pb);
         st_f1(lane == 0 ? sa : sb, Rpab, lane < 2 ? (uint32_t)lane * 4u : OOB, (uint32_t)tk * 8u);
     };
 
@@ -381,20 +385,18 @@ __global__ __launch_bounds__(NWM * 64) void scan_backward_kernel(BwdKArgs a) {
                 const float4 u = f4_sub(VL::f(v_of(x.y)), f4_scale(al, m));
                 const float part = rows_reduce<L>(f4_scale(bw, g));
                 if ((lane & 15) < L) reinterpret_cast<float*>(xb[par][wave])[4 * (lane & 15) + (lane >> 4)] = part;
-                float da = 0.f, db = 0.f;
+                float da = 0.f, db = 0.f;  // this lane's terms; the finishing wavefront sums them
                 if (run) {
                     const float gm = dot4(g, m), gu = dot4(g, u);
                     const float gur = group_sum<L>(gu);
                     pwv = off == OOB ? 0.f : be * gur;
-                    da = wave_sum(c1 * gm);
-                    db = wave_sum(w * gu);
+                    da = c1 * gm;
+                    db = w * gu;
                     gn = f4_scale(al * c1, g);
                     if (off != OOB) ring_at(slot, pos) = gn;
                 }
-                if (lane == 0) {
-                    ab[par][wave][0] = da;
-                    ab[par][wave][1] = db;
-                }
+                ab[par][wave][0][lane] = da;
+                ab[par][wave][1][lane] = db;
             } else {
                 const float pg = rows_reduce<L>(f4_scale(w, g)), pm = rows_reduce<L>(f4_scale(w, m));
                 if ((lane & 15) < L) {
@@ -414,11 +416,8 @@ __global__ __launch_bounds__(NWM * 64) void scan_backward_kernel(BwdKArgs a) {
                 const bool lead = wave == 0 && r == 0;
                 const float xa = lead ? gm - be * dot4(gh, sm) : gm, xc = lead ? dot4(gh, u) : 0.f;
                 st_f4(f4_scale(be, gh), Ro, lead ? col4 : OOB, (uint32_t)tl * dv4);
-                const float da = wave_sum(xa), db = wave_sum(xc);
-                if (lane == 0) {
-                    ab[par][wave][0] = da;
-                    ab[par][wave][1] = db;
-                }
+                ab[par][wave][0][lane] = xa;  // summed by the finishing wavefront
+                ab[par][wave][1][lane] = xc;
                 gn = f4_sub(f4_scale(al, g), f4_scale(al * be * w, gh));
                 if (off != OOB) ring_at(slot, pos) = gn;
             }
