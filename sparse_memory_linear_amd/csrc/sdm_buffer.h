@@ -121,11 +121,9 @@ struct VLoadN<VBF16, 2> {
     __device__ static void f(const T& x, float4 (&o)[2]) { VL::f(x, o); }
 };
 
-// Nearest-even bfloat16 of a finite fp32 value, as its 16 bits.
-__device__ __forceinline__ uint32_t bf16_rne(float f) {
-    const uint32_t u = __float_as_uint(f);
-    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
 
 // A lane's 16-byte piece of a table row: 4 fp32 columns (NQ = 1) or 8
 // bfloat16 columns (NQ = 2), unpacked to NQ float4 for the arithmetic and
@@ -151,11 +149,16 @@ struct RowFmt<true> {
         x[1] = make_float4(__uint_as_float(c << 16), __uint_as_float(c & 0xFFFF0000u),
                            __uint_as_float(d << 16), __uint_as_float(d & 0xFFFF0000u));
     }
+    // two values per v_cvt_pk_bf16_f32, gfx950's round-to-nearest-even
+    // conversion: for finite values bit for bit (u + 0x7FFF + lsb) >> 16 of the
+    // fp32 bits u (checked on MI355X over every exponent with tie and near-tie
+    // low bits, both signs, denormals, and 2^26 random values)
+    __device__ static uint32_t pk(float a, float b) {
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t));
+    }
     __device__ static float4 pack(const float4 (&x)[2]) {
-        return make_float4(__uint_as_float(bf16_rne(x[0].x) | (bf16_rne(x[0].y) << 16)),
-                           __uint_as_float(bf16_rne(x[0].z) | (bf16_rne(x[0].w) << 16)),
-                           __uint_as_float(bf16_rne(x[1].x) | (bf16_rne(x[1].y) << 16)),
-                           __uint_as_float(bf16_rne(x[1].z) | (bf16_rne(x[1].w) << 16)));
+        return make_float4(__uint_as_float(pk(x[0].x, x[0].y)), __uint_as_float(pk(x[0].z, x[0].w)),
+                           __uint_as_float(pk(x[1].x, x[1].y)), __uint_as_float(pk(x[1].z, x[1].w)));
     }
 };
 
