@@ -28,7 +28,16 @@ sys.path.insert(0, ROOT)
 METRIC = "SDM scan tokens/s and slot-row HBM GB/s at N=65536,W=R=64,d_v=128"
 HBM_PEAK_GBPS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scan_traffic_gdn_matched.json")
-SCAN_SRC = os.path.join(ROOT, "sparse_memory_linear_amd", "csrc", "scan.hip")
+# the sources the scan kernels are compiled from: the counter summary holds for them only
+SCAN_SRCS = [os.path.join(ROOT, "sparse_memory_linear_amd", "csrc", f) for f in ("scan.hip", "sdm_buffer.h")]
+
+
+def scan_source_sha256() -> str:
+    h = hashlib.sha256()
+    for path in SCAN_SRCS:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def parse():
@@ -114,8 +123,7 @@ def measured_traffic():
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)
-        sha = hashlib.sha256(open(SCAN_SRC, "rb").read()).hexdigest()
-        if rec.get("scan_source_sha256") == sha:
+        if rec.get("scan_source_sha256") == scan_source_sha256():
             return rec.get("traffic_bytes_per_launch")
     except (OSError, ValueError):
         pass

@@ -59,7 +59,7 @@ struct BwdKArgs {
     float* pw; float* pr;               // partial sums of this launch: [nslab][NS][T][W], [nslab][NS][T][R]
     float* pab;                         // [nslab * P][NS][T][2]
     float* pdv;                         // P > 1: [P][NS][T][dv]
-    const uint32_t* plan;               // prefetching form: [NS][T][W + 2R] source words of this launch
+    const uint32_t* plan;               // [NS][T][W + 2R] source words of this launch (bwd_plan_kernel)
     int64_t TS, t0;                     // tokens per stream; first token of this launch
     int T, W, R;
     int64_t N;
@@ -527,7 +527,7 @@ BGeom bwd_geom(int S, int W, int R) {
     g.NWR = (R + g.G - 1) / g.G;
     return g;
 }
-// LDS of the prefetching form: the ring of D + 1 token slots of W + R rows.
+// LDS of the reverse walk: the ring of D + 1 token slots of W + R rows.
 size_t bwd_ring_bytes(int S, int W, int R, int D) {
     return (size_t)(D + 1) * (W + R) * (S / 4) * 16;
 }
