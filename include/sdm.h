@@ -216,8 +216,10 @@ int sdm_scan_forward_save(const int32_t* idx_w, const float* wt_w, int64_t W,
 
 /*
  * sdm_scan_backward_workspace_bytes -- device workspace sdm_scan_backward needs
- * (per-slab partial sums of the weight and gate gradients); 0 when there is no
- * work, -1 when the sizes are invalid.
+ * (per-slab partial sums of the weight and gate gradients, and the planner's
+ * W + 2R source words per token and stream that let the reverse walk load a
+ * token's rows several tokens early); 0 when there is no work, -1 when the
+ * sizes are invalid.
  */
 int64_t sdm_scan_backward_workspace_bytes(int64_t B, int64_t H, int64_t T, int64_t W, int64_t R,
                                           int64_t dv);
