@@ -73,7 +73,7 @@ __device__ __forceinline__ int row_part(uint32_t row, int pshift) {
 }
 
 // ------------------------------------------------------------------ planner
-// The prefetching backward issues a token's table-row loads D tokens before the
+// The reverse walk issues a token's table-row loads D tokens before the
 // token is processed (processing runs t = T-1 .. 0), so a load of token u does
 // not see what tokens u+1 .. u+D will store. All indices are known, so for
 // every access of token u a planner finds, from the indices alone:
@@ -187,9 +187,9 @@ __global__ __launch_bounds__(BPLAN_THREADS) void bwd_plan_kernel(BPlanArgs a) {
     }
 }
 
-// ------------------------------------------------------------------ prefetching backward
-// The backward above with each token's rows loaded D tokens early. Per token,
-// in the reverse walk: address words (index and the planner's source words)
+// ------------------------------------------------------------------ reverse walk
+// The backward of the header with each token's rows loaded D tokens early.
+// Per token, in the reverse walk: address words (index and the planner's source words)
 // come D + DM tokens early; values (weight, gates, v or dy, pre-image) and
 // table rows (G of every access, M of the reads, or the pre-image a read's M
 // comes from) D tokens early, issued right after the barrier that closed the
