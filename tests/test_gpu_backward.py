@@ -283,3 +283,20 @@ def test_backward_stream_counts_around_one_round_of_xcds(B, H, form, oform):
     _, _, _, got, M_back = _gpu_train(c, dy, dM, form)
     _check_grads(f"NS={B * H}", got, ref, TOL_F32)
     assert np.array_equal(M_back.view(np.uint32), c["M_in"].view(np.uint32))
+
+
+@pytest.mark.parametrize("form,oform", [("eq4", oracle.EQ4), ("fig2", oracle.FIG2)], ids=["eq4", "fig2"])
+def test_training_call_split_into_launch_chunks(form, oform):
+    """W = 256 write rows of d_v = 512 fp32 values: 512 KiB of pre-images per
+    token, so the training forward and the backward each split the call into
+    launches of at most 2^31 bytes of pre-images (4095 + 105 tokens); the
+    backward walks the chunks last to first and must match the oracle across
+    the boundary, with the table restored bit for bit."""
+    say(f"[backward launch chunks] W=256 d_v=512 T=4200 form={form}")
+    case = dict(B=1, H=1, T=4200, N=2048, dv=512, W=256, R=16)
+    c = _random_case(31, **case)
+    dy, dM = _cotangents(32, 1, 1, 4200, 2048, 512)
+    ref = oracle.scan_backward(**c, dy=dy, dM_out=dM, form=oform)
+    _, _, _, got, M_back = _gpu_train(c, dy, dM, form)
+    _check_grads(f"chunks {form}", got, ref, TOL_F32)
+    assert np.array_equal(M_back.view(np.uint32), c["M_in"].view(np.uint32))
