@@ -300,3 +300,18 @@ def test_training_call_split_into_launch_chunks(form, oform):
     _, _, _, got, M_back = _gpu_train(c, dy, dM, form)
     _check_grads(f"chunks {form}", got, ref, TOL_F32)
     assert np.array_equal(M_back.view(np.uint32), c["M_in"].view(np.uint32))
+
+
+@pytest.mark.parametrize("T", [1, 6])
+@pytest.mark.parametrize("form,oform", [("eq4", oracle.EQ4), ("fig2", oracle.FIG2)], ids=["eq4", "fig2"])
+def test_training_short_calls(T, form, oform):
+    """Calls of at most 8 tokens take the direct form, also for the training
+    forward (its pre-image stores); the backward then runs with fewer tokens
+    than its unrolled loop holds (its tail loop only). Both against the oracle."""
+    say(f"[backward short call] T={T} form={form}")
+    c = _random_case(41 + T, B=2, H=3, T=T, N=512, dv=64, W=16, R=16)
+    dy, dM = _cotangents(42 + T, 2, 3, T, 512, 64)
+    ref = oracle.scan_backward(**c, dy=dy, dM_out=dM, form=oform)
+    _, _, _, got, M_back = _gpu_train(c, dy, dM, form)
+    _check_grads(f"T={T} {form}", got, ref, TOL_F32)
+    assert np.array_equal(M_back.view(np.uint32), c["M_in"].view(np.uint32))
