@@ -549,9 +549,13 @@ int env_int(const char* name) {
     return e ? atoi(e) : 0;
 }
 
-// Slab width and row partitions. Both forms take the widest slab that still
-// gives 256 workgroups (one per CU: a second workgroup on a CU stretches every
-// token of both), else the one with the most, and one partition: partitions
+// Slab width and row partitions. Both forms take the widest slab whose layout
+// has at most 8 wavefronts (the deeper window) and gives at least 128
+// workgroups (8 streams x 131072 tokens: 8-column slabs 167 ms against 177 for
+// 4-column ones with 256 workgroups; 32 streams: 16-column slabs as before),
+// else the widest that still gives 256 workgroups (one per CU: a second
+// workgroup on a CU stretches every token of both), else the one with the
+// most, and one partition: partitions
 // multiply the wavefronts that step through every token, and with the token
 // loop's loads issued ahead that costs more than the extra rows in flight
 // bring (measured on the per-slot form: 16-column slabs without partitions
@@ -564,7 +568,14 @@ struct BCfg {
 BCfg bwd_cfg(int64_t NS, int W, int R, int dv, int form) {
     BCfg c;
     const int fs = env_int("SDM_BWD_SLAB"), fp = env_int("SDM_BWD_PARTS");
-    int64_t best_units = 0;
+    // first choice: the widest slab whose layout takes the deeper-window
+    // instantiation (at most 8 wavefronts) with at least 128 workgroups
+    for (int S : {32, 16, 8, 4}) {
+        if (fs || !bwd_fits(S, W, R, dv) || !bwd_deep(S, W, R) || NS * (dv / S) < 128) continue;
+        c.S = S;
+        break;
+    }
+    int64_t best_units = c.S ? 1 << 30 : 0;
     for (int S : {32, 16, 8, 4}) {
         if ((fs && fs != S) || !bwd_fits(S, W, R, dv)) continue;
         const int64_t units = NS * (dv / S);

@@ -126,13 +126,15 @@ def test_training_sizes_are_pure_host_logic(lib):
         nslab = dv // S
         return 4 * (nslab * NS * T * (W + R) + nslab * P * NS * T * 2 + (P * NS * T * dv if P > 1 else 0)
                     + NS * T * (W + 2 * R))
-    # both forms take the widest slab with 256 workgroups and one partition:
-    # 32 streams -> 16-column slabs; 8 streams -> 4-column slabs; chunks of at
-    # most 2^31 / (W dv 4) tokens
+    # both forms take the widest slab with at most 8 wavefronts and at least 128
+    # workgroups, one partition: 32 streams -> 16-column slabs; 8 streams ->
+    # 8-column slabs; chunks of at most 2^31 / (W dv 4) tokens
     assert binding.sdm_scan_backward_workspace_bytes(4, 8, 8192, 64, 64, 128) == bwd(32, 8192, 16, 1)
-    assert binding.sdm_scan_backward_workspace_bytes(1, 8, 1000, 64, 64, 128) == bwd(8, 1000, 4, 1)
+    assert binding.sdm_scan_backward_workspace_bytes(1, 8, 1000, 64, 64, 128) == bwd(8, 1000, 8, 1)
     Tc = 0x7FFFFFFF // (64 * 128 * 4)
-    assert binding.sdm_scan_backward_workspace_bytes(1, 8, 131072, 64, 64, 128) == bwd(8, Tc, 4, 1)
+    assert binding.sdm_scan_backward_workspace_bytes(1, 8, 131072, 64, 64, 128) == bwd(8, Tc, 8, 1)
+    # one stream of d_v = 512, W = R = 8: only 4-column slabs reach 128 workgroups
+    assert binding.sdm_scan_backward_workspace_bytes(1, 1, 500, 8, 8, 512) == bwd(1, 500, 4, 1, W=8, R=8, dv=512)
     assert binding.sdm_scan_backward_workspace_bytes(0, 8, 100, 64, 64, 128) == 0
     assert lib.sdm_scan_backward_workspace_bytes(1, 1, 1, 300, 1, 16) == -1
 
