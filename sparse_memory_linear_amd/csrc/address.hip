@@ -299,14 +299,17 @@ __global__ __launch_bounds__(NWA * 64) void address_kernel(AddressArgs a) {
     // order, u = b * T + t: within a sequence for long calls, across sequences
     // when a call carries few tokens per sequence (decoding). Every token of a
     // tile uses the same subkeys.
+    // token numbers u = b * T + t stay below 2^32 (checked by the C ABI), so
+    // the tile and row arithmetic is 32-bit (64-bit division is a long
+    // software sequence on the GPU)
     const int64_t UT = a.B * a.T;
-    const int64_t ntile = (UT + TOK - 1) / TOK;
+    const uint32_t ntile = (uint32_t)((UT + TOK - 1) / TOK), T32 = (uint32_t)a.T;
     const int h = (int)(blockIdx.x / ntile);
-    const int64_t u0 = (blockIdx.x % ntile) * TOK;
+    const int64_t u0 = (int64_t)(blockIdx.x - (uint32_t)h * ntile) * TOK;
     const int br = blockIdx.y;
     auto row_of = [&](int64_t u) -> int64_t {  // row of token u in the [B, H, T] layout
-        const int64_t b = u / a.T;
-        return (b * a.H + h) * a.T + (u - b * a.T);
+        const uint32_t uu = (uint32_t)u, b = uu / T32;
+        return ((int64_t)b * a.H + h) * a.T + (uu - b * T32);
     };
 
     // LDS: one block of pw floats per wavefront, then the pruned rank pairs. A

@@ -48,6 +48,9 @@ int check_address_sizes(int q_dtype, int k_dtype, int64_t B, int64_t H, int64_t 
                     (long long)step);
     const int64_t ntile = (B * T + 15) / 16;
     if (ntile * H > 0x7FFFFFFFll) return fail(SDM_ERR_UNSUPPORTED, "too many token tiles for one launch");
+    // token numbers b * T + t are kept in 32 bits on the GPU
+    if (B * T > 0xFFFFFFFFll) return fail(SDM_ERR_UNSUPPORTED, "B*T=%lld: at most 2^32 - 1 tokens per call",
+                                          (long long)(B * T));
     return SDM_OK;
 }
 

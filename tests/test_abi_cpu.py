@@ -89,6 +89,8 @@ def test_address_rejects_bad_arguments_before_launch(lib):
     assert call(args(W=65)) == 5                 # GPU covers k <= 64
     assert call(args(iw=P(4100))) == 4           # misaligned
     assert "aligned" in binding.sdm_last_error()
+    assert call(args(B=1 << 16, T=1 << 16)) == 5  # 2^32 tokens: token numbers are 32-bit on the GPU
+    assert "2^32" in binding.sdm_last_error()
 
 
 def test_scan_rejects_bad_arguments_before_launch(lib):
