@@ -82,7 +82,8 @@ const char* sdm_last_error(void);
  *   score_w, score_r     [B, H, T, W|R]     optional (NULL): fp32 slot scores
  *
  * Supported: q_dtype in {SDM_F32, SDM_BF16}; n_sub a multiple of 16 up to 512;
- * dh a multiple of 8 (fp32) or 32 (bf16) up to 256; 1 <= W, R <= min(64, n_sub^2).
+ * dh a multiple of 8 (fp32) or 32 (bf16) up to 256; 1 <= W, R <= min(64, n_sub^2);
+ * B * T < 2^32 tokens per call.
  */
 int sdm_address(const void* q_w, const void* q_r, int q_dtype,
                 const void* subkeys_w, const void* subkeys_r, int k_dtype,
