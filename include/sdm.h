@@ -272,7 +272,8 @@ int sdm_state_init_backward(const float* dM, float* dM0, int64_t B, int64_t H, i
  * accumulation (bf16 or fp32 operands); softplus, exp and sigmoid in fp32.
  *   x [B, T, d] x_dtype; W_a, W_b [H, d] w_dtype == x_dtype; b_dt, A [H] fp32;
  *   alpha, beta [B, H, T] fp32 (out): the layout sdm_scan_forward reads.
- * Supported: d a multiple of 32 (bf16) or 8 (fp32) up to 2^20, H <= 4096.
+ * Supported: d a multiple of 32 (bf16) or 8 (fp32) up to 2^20, H <= 4096,
+ * B * T < 2^32 tokens per call.
  */
 int sdm_gates(const void* x, int x_dtype, const void* W_a, const void* W_b, int w_dtype,
               const float* b_dt, const float* A, int64_t B, int64_t T, int64_t d, int64_t H,
@@ -285,7 +286,8 @@ int sdm_gates(const void* x, int x_dtype, const void* W_a, const void* W_b, int 
  * without its activation):
  *   o[b,h,t,i] = y[b,h,t,i] / sqrt(mean_j y[b,h,t,j]^2 + eps) * gamma[h,i] * sigmoid(g[b,h,t,i])
  *   y, o [B, H, T, dv] fp32; g [B, H, T, dv] g_dtype (gate pre-activation);
- *   gamma [H, dv] fp32; eps >= 0. o may not alias y. dv a multiple of 4.
+ *   gamma [H, dv] fp32; eps >= 0. o may not alias y. dv a multiple of 4;
+ *   B * H * T < 2^32 rows per call.
  * The head-mixing projection W_o that follows is a plain dense layer and is
  * not part of this library.
  */

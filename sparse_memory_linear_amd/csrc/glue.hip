@@ -78,7 +78,7 @@ __global__ __launch_bounds__(GW * 64) void gates_kernel(GatesArgs a) {
         for (int i = 0; i < 4; ++i) {
             const int64_t u = u0 + 4 * g4 + i;
             if (u >= UT) break;
-            const int64_t b = u / a.T, t = u - b * a.T;
+            const uint32_t uu = (uint32_t)u, b = uu / (uint32_t)a.T, t = uu - b * (uint32_t)a.T;  // u < 2^32
             const int64_t o = (b * H + hrow) * a.T + t;
             if (is_a) a.alpha[o] = expf(-Ah * softplusf(acc[i] + bias));
             else a.beta[o] = 1.f / (1.f + expf(-acc[i]));
@@ -98,7 +98,7 @@ __global__ __launch_bounds__(256) void output_gate_kernel(OutGateArgs a) {
     for (int64_t r0 = wave_g * rows_per_wave; r0 < a.rows; r0 += nwaves * rows_per_wave) {
         const int64_t row = r0 + lane / LG;
         const bool ok = row < a.rows;
-        const int64_t h = ok ? (row / a.T) % a.H : 0;
+        const int64_t h = ok ? ((uint32_t)row / (uint32_t)a.T) % (uint32_t)a.H : 0;  // rows < 2^32
         const float4* y4 = reinterpret_cast<const float4*>(a.y) + (ok ? row : 0) * nq;
         float ss = 0.f;
         for (int q = sub; q < nq; q += LG) {

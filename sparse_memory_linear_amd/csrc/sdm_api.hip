@@ -340,7 +340,8 @@ int sdm_gates(const void* x, int x_dtype, const void* W_a, const void* W_b, int 
     if (d % step != 0 || d > (1 << 20))
         return fail(SDM_ERR_UNSUPPORTED, "d=%lld: a multiple of %lld up to 2^20", (long long)d, (long long)step);
     if (H > 4096) return fail(SDM_ERR_UNSUPPORTED, "H=%lld: at most 4096 heads", (long long)H);
-    if ((B * T + 63) / 64 > 0x7FFFFFFFll) return fail(SDM_ERR_UNSUPPORTED, "too many tokens for one launch");
+    if (B * T > 0xFFFFFFFFll) return fail(SDM_ERR_UNSUPPORTED, "B*T=%lld: at most 2^32 - 1 tokens per call",
+                                          (long long)(B * T));
     if (B == 0 || T == 0) return ok();
     int rc = check_buffers(fn, {x, W_a, W_b, b_dt, A, alpha, beta});
     if (rc) return rc;
@@ -358,6 +359,8 @@ int sdm_output_gate(const float* y, const float* gamma, const void* g, int g_dty
     if (g_dtype != SDM_F32 && g_dtype != SDM_BF16) return fail(SDM_ERR_DTYPE, "unknown gate dtype %d", g_dtype);
     if (B < 0 || H < 1 || T < 0 || dv < 1 || !(eps >= 0.f)) return fail(SDM_ERR_SHAPE, "%s: invalid sizes or eps", fn);
     if (dv % 4 != 0) return fail(SDM_ERR_UNSUPPORTED, "dv=%lld must be a multiple of 4", (long long)dv);
+    if (B * H * T > 0xFFFFFFFFll)
+        return fail(SDM_ERR_UNSUPPORTED, "B*H*T=%lld: at most 2^32 - 1 rows per call", (long long)(B * H * T));
     if (B == 0 || T == 0) return ok();
     int rc = check_buffers(fn, {y, gamma, g, o});
     if (rc) return rc;

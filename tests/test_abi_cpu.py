@@ -203,3 +203,21 @@ def test_probe_library_exports_its_declared_symbol_and_rejects_bad_arguments(lib
     assert f(fake, 16, 96, 10, 4, fake, None) == 1             # piece size not 64/128/256/512
     assert f(fake, 16, 128, 10, 0, fake, None) == 1            # empty grid
     assert f(fake, 1 << 31, 128, 10, 4, fake, None) == 1       # more rows than 32-bit indices reach
+
+
+def test_glue_calls_reject_bad_arguments_before_launch(lib):
+    fake = P(4096)  # never dereferenced: every call below fails validation first
+    g = lambda x_dtype=1, w_dtype=1, B=2, T=16, d=1024, H=8: lib.sdm_gates(
+        fake, x_dtype, fake, fake, w_dtype, fake, fake, B, T, d, H, fake, fake, None)
+    assert g(x_dtype=5) == 3
+    assert g(w_dtype=0) == 3                      # weights in the dtype of x
+    assert g(d=1000) == 5                         # bf16 needs d % 32 == 0
+    assert g(H=5000) == 5
+    assert g(B=1 << 16, T=1 << 16) == 5           # 2^32 tokens: token numbers are 32-bit on the GPU
+    assert "2^32" in binding.sdm_last_error()
+    og = lambda B=2, H=8, T=16, dv=128, eps=1e-6: lib.sdm_output_gate(
+        fake, fake, fake, 0, ctypes.c_float(eps), B, H, T, dv, fake, None)
+    assert og(dv=130) == 5
+    assert og(eps=-1.0) == 2
+    assert og(B=1 << 12, H=1 << 10, T=1 << 10) == 5   # 2^32 rows
+    assert "2^32" in binding.sdm_last_error()
