@@ -103,7 +103,7 @@ Geom make_geom(int S, int W, int R) {
     return g;
 }
 
-// Readers summed by reader 0 per token: the largest reader count a slab width
+// Readers whose partial sums are added per token: the largest reader count a slab width
 // can have (R <= 256, at most NWMAX wavefronts in all); partial-sum slots of
 // absent readers stay zero.
 template <int S>
@@ -421,8 +421,6 @@ __global__ __launch_bounds__(SlabCfg<SL>::NWMAX * 64) void scan_kernel(ScanKArgs
     const uint32_t vstride = (uint32_t)dv * VL::ESZ;
     const uint32_t sstride = (uint32_t)a.W * dv4;                    // snapshot bytes per token
     const uint32_t s_lane = (uint32_t)pos * dv4 + col4;
-    // reader 0's first S lanes store y[t-1] (one column each); every other y store is dropped
-    const uint32_t y_off = (!writer && rw == 0 && lane < S) ? (uint32_t)(slab * S + lane) * 4u : OOB;
     const int ylane = lane < S ? lane : 0;
 
     // partial sums of absent readers stay zero (made visible by the first barrier)
@@ -431,23 +429,42 @@ __global__ __launch_bounds__(SlabCfg<SL>::NWMAX * 64) void scan_kernel(ScanKArgs
     // The planner packs a partition's accesses to the front of its records, so
     // wavefronts whose slots no token of this launch reaches have nothing to do:
     // they only keep the barrier count (one barrier per token, one at the end).
-    // Reader 0 always runs (it stores y); the shared-residual form uses all
-    // writers' partial sums and runs every wavefront.
-    // nra: reader wavefronts whose partial sums reader 0 adds (a power of two)
+    // Reader 0 always runs. The readers' partial sums of a token are added, and
+    // y stored, by the last reader wavefront when it is such an idle one (then
+    // the running readers only scan rows), else by reader 0. The shared-residual
+    // form uses all writers' partial sums and runs every wavefront.
+    // nra: reader wavefronts whose partial sums are added (a power of two)
     int nra = NWR;
+    bool sum0 = true;  // reader 0 adds the partial sums
     if constexpr (FORM == 0) {
         const uint32_t* mc = a.maxc + (s * a.P + part) * 2;
+        nra = ((int)mc[1] + G - 1) / G;
+        sum0 = !(NWR >= 2 && nra < NWR);
         const bool idle = writer ? (uint32_t)(wave * G) >= mc[0] : (rw > 0 && (uint32_t)(rw * G) >= mc[1]);
-        if (idle) {
+        if (idle && (sum0 || rw != NWR - 1)) {
             for (int t = 0; t <= T; ++t) __syncthreads();
             return;
         }
-        nra = ((int)mc[1] + G - 1) / G;
     }
     {
         int q = 1;
         while (q < nra) q *= 2;
         nra = q;
+    }
+    // the summing wavefront's first S lanes store y[t-1] (one column each); every
+    // other y store is dropped
+    const bool ysum = !writer && rw == (sum0 ? 0 : NWR - 1);
+    const uint32_t y_off = (ysum && lane < S) ? (uint32_t)(slab * S + lane) * 4u : OOB;
+    if (FORM == 0 && ysum && !sum0) {
+        // an idle reader wavefront: token t - 1's partial sums are complete at
+        // token t's barrier and are not overwritten before token t + 1's
+        for (int t = 0; t < T; ++t) {
+            __syncthreads();
+            if (t > 0) st_f1(readers_sum<NRMAX, S>(ybuf + ((t - 1) & 1) * NRMAX * S + ylane, nra), Ry, y_off, (uint32_t)(t - 1) * dv4);
+        }
+        __syncthreads();
+        if (T > 0) st_f1(readers_sum<NRMAX, S>(ybuf + ((T - 1) & 1) * NRMAX * S + ylane, nra), Ry, y_off, (uint32_t)(T - 1) * dv4);
+        return;
     }
 
     auto row_off = [&](uint32_t pk) -> uint32_t {
@@ -512,14 +529,15 @@ __global__ __launch_bounds__(SlabCfg<SL>::NWMAX * 64) void scan_kernel(ScanKArgs
         __syncthreads();
     };
     // one token of a reader wavefront (barriers: [B'_t], B_t); the partial sums
-    // of token t are combined by reader 0 after the next barrier
+    // of token t are added by the summing wavefront after the next barrier
     auto read_token = [&](int t, int slot, int2 e, float4 pre) {
         if constexpr (FORM == 1) __syncthreads();
         __syncthreads();
-        // reader 0 first sums the previous token's partials (complete since
-        // this token's barrier), so their LDS reads overlap the row sum below
+        // when it sums, reader 0 first adds the previous token's partials
+        // (complete since this token's barrier), so their LDS reads overlap
+        // the row sum below
         float acc = 0.f;
-        if (rw == 0)  // uniform per wavefront; no memory operation inside
+        if (ysum)  // uniform per wavefront; no memory operation inside
             acc = readers_sum<NRMAX, S>(ybuf + ((t - 1) & 1) * NRMAX * S + ylane, nra);
         const uint32_t pk = (uint32_t)e.x;
         float4 cur[NQ];
@@ -595,7 +613,7 @@ __global__ __launch_bounds__(SlabCfg<SL>::NWMAX * 64) void scan_kernel(ScanKArgs
     }
     // the last token's partial sums
     __syncthreads();
-    if (!writer && rw == 0 && T > 0) {
+    if (ysum && T > 0) {
         const float acc = readers_sum<NRMAX, S>(ybuf + ((T - 1) & 1) * NRMAX * S + ylane, nra);
         st_f1(acc, Ry, y_off, (uint32_t)(T - 1) * dv4);
     }
