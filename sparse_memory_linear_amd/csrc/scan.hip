@@ -436,12 +436,16 @@ __global__ __launch_bounds__(SlabCfg<SL>::NWMAX * 64) void scan_kernel(ScanKArgs
     // nra: reader wavefronts whose partial sums are added (a power of two)
     int nra = NWR;
     bool sum0 = true;  // reader 0 adds the partial sums
+    int sw = 0;        // else this reader wavefront does
     if constexpr (FORM == 0) {
         const uint32_t* mc = a.maxc + (s * a.P + part) * 2;
         nra = ((int)mc[1] + G - 1) / G;
-        sum0 = !(NWR >= 2 && nra < NWR);
+        // summing candidate: the extra wavefront the launch adds to a layout
+        // with one reader wavefront, else the last reader wavefront
+        sw = (int)(blockDim.x >> 6) > NWW + NWR ? NWR : NWR - 1;
+        sum0 = !(sw >= 1 && nra <= sw);
         const bool idle = writer ? (uint32_t)(wave * G) >= mc[0] : (rw > 0 && (uint32_t)(rw * G) >= mc[1]);
-        if (idle && (sum0 || rw != NWR - 1)) {
+        if (idle && (sum0 || rw != sw)) {
             for (int t = 0; t <= T; ++t) __syncthreads();
             return;
         }
@@ -453,7 +457,7 @@ __global__ __launch_bounds__(SlabCfg<SL>::NWMAX * 64) void scan_kernel(ScanKArgs
     }
     // the summing wavefront's first S lanes store y[t-1] (one column each); every
     // other y store is dropped
-    const bool ysum = !writer && rw == (sum0 ? 0 : NWR - 1);
+    const bool ysum = !writer && rw == (sum0 ? 0 : sw);
     const uint32_t y_off = (ysum && lane < S) ? (uint32_t)(slab * S + lane) * 4u : OOB;
     if (FORM == 0 && ysum && !sum0) {
         // an idle reader wavefront: token t - 1's partial sums are complete at
@@ -886,7 +890,10 @@ hipError_t launch_scan_slab(const ScanArgs& a, const Cfg& c, hipStream_t st) {
         k.W = a.W;
         k.snap = save ? a.snap + c0 * a.W * a.dv : nullptr;
         k.snap_s = a.T * a.W * a.dv;
-        dim3 grid((unsigned)nblk), block((unsigned)(g.nw() * 64));
+        // per-slot form with one reader wavefront: one more wavefront adds the
+        // readers' partial sums and stores y
+        const int xw = (a.form == 0 && g.NWR == 1 && g.nw() < SlabCfg<SL>::NWMAX && g.NWR < nrmax<SL>()) ? 1 : 0;
+        dim3 grid((unsigned)nblk), block((unsigned)((g.nw() + xw) * 64));
         launch_scan_inst<SL>(a.form, a.v_bf16, save, a.m_bf16, grid, block, lds, st, k);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
