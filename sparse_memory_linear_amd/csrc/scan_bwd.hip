@@ -361,6 +361,21 @@ __global__ __launch_bounds__(NWM * 64) void scan_backward_kernel(BwdKArgs a) {
         st_f1(lane == 0 ? sa : sb, Rpab, lane < 2 ? (uint32_t)lane * 4u : OOB, (uint32_t)tk * 8u);
     };
 
+    // a wavefront the launch adds beyond the writers and readers (when the
+    // layout leaves room) does nothing but the finishing sums, off the readers'
+    // path; it keeps the barrier count of the others
+    const bool xf = (int)(blockDim.x >> 6) > NWW + a.NWR;
+    if (wave == NWW + a.NWR) {
+        for (int tl = T - 1; tl >= 0; --tl) {
+            __syncthreads();                           // B1
+            if constexpr (FORM == 1) __syncthreads();  // BX
+            if (tl + 1 < T) finish(tl + 1);
+            __syncthreads();                           // B2
+        }
+        finish(0);
+        return;
+    }
+
     int slot = (T - 1) % UR;  // LDS ring slot of the token being processed
     auto process = [&](int tl, const Ad& d, const Va& x) {
         const int32_t row = d.row;
@@ -439,7 +454,7 @@ __global__ __launch_bounds__(NWM * 64) void scan_backward_kernel(BwdKArgs a) {
             st_f1(off == OOB ? 0.f : dr, Rpr, own ? (uint32_t)pos * 4u : OOB, (uint32_t)tl * (uint32_t)R * 4u);
             __syncthreads();                           // B1
             if constexpr (FORM == 1) __syncthreads();  // BX
-            if (rw == 0 && tl + 1 < T) finish(tl + 1);
+            if (rw == 0 && !xf && tl + 1 < T) finish(tl + 1);
             __syncthreads();                           // B2
         }
         slot = slot == 0 ? UR - 1 : slot - 1;
@@ -472,7 +487,7 @@ __global__ __launch_bounds__(NWM * 64) void scan_backward_kernel(BwdKArgs a) {
         const Ad d = fetch_ad(tl);
         process(tl, d, fetch_va(tl, d));
     }
-    if (wave == NWW) finish(0);
+    if (wave == NWW && !xf) finish(0);
 }
 
 // dwt_w, dwt_r, dalpha, dbeta of one launch: the slabs' partial sums added in
@@ -626,13 +641,15 @@ hipError_t launch_bwd_slab(const BwdArgs& a, const BCfg& c, hipStream_t st) {
         k.TS = a.T; k.t0 = c0; k.T = (int)Tn; k.W = a.W; k.R = a.R;
         k.N = a.N; k.dv = a.dv; k.nslab = nslab; k.P = c.P; k.pshift = psh;
         k.NS = a.NS; k.NWW = g.NWW; k.NWR = g.NWR;
-        dim3 grid((unsigned)nblk), block((unsigned)((g.NWW + g.NWR) * 64));
+        const bool deep = bwd_deep(S, a.W, a.R);
+        // one more wavefront for the finishing sums where the instantiation has room
+        const int xw = g.NWW + g.NWR < (deep ? BWD_NW_DEEP : BWD_NWMAX) ? 1 : 0;
+        dim3 grid((unsigned)nblk), block((unsigned)((g.NWW + g.NWR + xw) * 64));
         const int sel = (a.form ? 2 : 0) | (a.v_bf16 ? 1 : 0);
         // the planner, then the reverse walk
         uint32_t* plan = reinterpret_cast<uint32_t*>(k.pdv + (c.P > 1 ? (int64_t)c.P * a.NS * Tn * a.dv : 0));
         BPlanArgs pa{};
         pa.idx_w = a.idx_w + c0 * a.W; pa.idx_r = a.idx_r + c0 * a.R; pa.plan = plan;
-        const bool deep = bwd_deep(S, a.W, a.R);
         const int D = deep ? BWD_D_DEEP : BWD_D;
         pa.Tn = Tn; pa.TS = a.T; pa.N = a.N; pa.W = a.W; pa.R = a.R; pa.D = D;
         // the hash holds (TT + D) * (W + R) entries at load <= 1/4, which keeps the
