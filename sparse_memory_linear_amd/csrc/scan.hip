@@ -951,10 +951,17 @@ int slab_nwmax(int S) {
 int slab_nrmax(int S) {
     return S == 32 ? nrmax<32>() : S == 16 ? nrmax<16>() : S == 8 ? nrmax<8>() : nrmax<4>();
 }
+// LDS of one workgroup of the prefetching loop (its ring grows with W)
+size_t slab_lds(int S, const Geom& g, int cpl) {
+    return S == 32 ? scan_lds_bytes<32>(g, cpl) : S == 16 ? scan_lds_bytes<16>(g, cpl)
+         : S == 8 ? scan_lds_bytes<8>(g, cpl) : scan_lds_bytes<4>(g, cpl);
+}
+constexpr size_t LDS_MAX = 160 * 1024;  // per workgroup on gfx950
+
 bool slab_fits(int S, int W, int R, int dv, int cpl) {
     if (dv % (S / 4 * cpl) != 0) return false;
     const Geom g = make_geom(S, W, R);
-    return g.nw() <= slab_nwmax(S) && g.NWR <= slab_nrmax(S);
+    return g.nw() <= slab_nwmax(S) && g.NWR <= slab_nrmax(S) && slab_lds(S, g, cpl) <= LDS_MAX;
 }
 
 int env_int(const char* name) {

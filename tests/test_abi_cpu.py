@@ -66,6 +66,12 @@ def test_workspace_size_is_pure_host_logic(lib):
     assert binding.sdm_scan_workspace_bytes(1, 8, 1000, 64, 64, 128) == \
         8 * 8 * 1000 * rec + 8 * 8 * 1000 * 128 * 4 + 8 * 8 * 2 * 4
     assert binding.sdm_scan_workspace_bytes(0, 8, 8192, 64, 64, 128) == 0
+    # W = 120, R = 8, 32 streams: 32-column slabs would fit 16 wavefronts, but
+    # their forwarding ring (14 tokens x 120 rows x 128 B) exceeds the 160 KiB of
+    # LDS, and 16-column ones need 9 wavefronts; every form and table dtype takes
+    # 8-column slabs (4 writer + 1 reader wavefronts of 32 rows), one partition
+    assert binding.sdm_scan_workspace_bytes(4, 8, 1000, 120, 8, 128) == \
+        32 * 1000 * (4 * 32 * 16 + 32 * 8) + 32 * 2 * 4
     assert lib.sdm_scan_workspace_bytes(1, 1, 1, 0, 1, 16) == -1
     assert lib.sdm_scan_workspace_bytes(1, 1, 1, 300, 1, 16) == -1
 

@@ -129,6 +129,44 @@ def test_scan_slabs_and_row_partitions_match_oracle(slab, parts, monkeypatch):
         assert np.array_equal(M2, Mg) and np.array_equal(y2, yg)       # bit-exact rerun
 
 
+# Who adds the reader wavefronts' partial sums of a token and stores y:
+# reader 0 when every reader runs, the last reader when the planner's counts
+# leave it idle, an added wavefront when the layout has one reader wavefront
+# and room for another, reader 0 again when it has no room.
+SUMMERS = [
+    ("reader0_all_run", 32, 1, dict(B=1, H=2, T=200, N=4096, dv=64, W=64, R=64)),
+    ("idle_last_reader", 32, 4, dict(B=1, H=2, T=200, N=4096, dv=64, W=64, R=64)),
+    ("added_wavefront", 16, 1, dict(B=2, H=1, T=300, N=512, dv=64, W=16, R=16)),
+    ("added_wavefront_partitioned", 16, 4, dict(B=2, H=1, T=300, N=512, dv=64, W=16, R=16)),
+    ("one_reader_no_room", 16, 1, dict(B=1, H=1, T=200, N=1024, dv=64, W=112, R=16)),
+]
+
+
+@pytest.mark.parametrize("label,slab,parts,case", SUMMERS, ids=[c[0] for c in SUMMERS])
+def test_partial_sum_wavefront_arrangements(label, slab, parts, case, monkeypatch):
+    monkeypatch.setenv("SDM_SCAN_SLAB", str(slab))
+    monkeypatch.setenv("SDM_SCAN_PARTS", str(parts))
+    say(f"[partial sums] {label} S={slab} P={parts}")
+    c = _random_case(11, **case)
+    Mo, yo = oracle.scan(**c, form=oracle.EQ4)
+    Mg, yg = _run_gpu(**c, form="eq4")
+    _check(label, Mg, yg, Mo, yo, c["M_in"], c["idx_w"], TOL_F32)
+    M2, y2 = _run_gpu(**c, form="eq4")
+    assert np.array_equal(M2, Mg) and np.array_equal(y2, yg)
+
+
+def test_wide_writer_sets_take_a_slab_whose_ring_fits_lds():
+    # W = 120 with 32 streams: the 32-column layout fits 16 wavefronts but its
+    # forwarding ring would need 210 KiB of LDS; the rule must pick a narrower
+    # slab (and the call must succeed) for both forms
+    c = _random_case(13, B=4, H=8, T=40, N=2048, dv=128, W=120, R=8)
+    for form, oform in FORMS:
+        say(f"[wide W] form={form}")
+        Mo, yo = oracle.scan(**c, form=oform)
+        Mg, yg = _run_gpu(**c, form=form)
+        _check(f"W=120 {form}", Mg, yg, Mo, yo, c["M_in"], c["idx_w"], TOL_F32)
+
+
 @pytest.mark.parametrize("case", HAZARD + [dict(B=2, H=2, T=130, N=4096, dv=64, W=64, R=32, bf16=True)],
                          ids=[f"N{c['N']}W{c['W']}dv{c['dv']}" for c in HAZARD] + ["N4096W64dv64"])
 @pytest.mark.parametrize("form,oform", FORMS, ids=["eq4", "fig2"])
