@@ -62,48 +62,7 @@ def parse():
     p.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                    help="run one plain device copy of BYTES bytes before the benchmark "
                         "(a known-size kernel that calibrates HBM byte counters)")
-    p.add_argument("--gather-probe", action="store_true",
-                   help="instead of the benchmark: the rate of random in-place row-piece traffic "
-                        "(the scan's access pattern) on a 1 GiB table, per piece size and grid")
     return p.parse_args()
-
-
-def gather_probe(dev) -> None:
-    """Practical ceiling of the scan's access pattern: random pieces of 512-byte
-    rows read, and half of them written back, over a 1 GiB table (libsdm_probe.so,
-    timed with HIP events on the stream the kernel runs on)."""
-    import ctypes
-    import torch
-    lib = ctypes.CDLL(os.path.join(ROOT, "sparse_memory_linear_amd", "libsdm_probe.so"))
-    lib.sdm_probe_gather.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int64, ctypes.c_int,
-                                     ctypes.c_void_p, ctypes.c_void_p]
-    lib.sdm_probe_gather.restype = ctypes.c_int
-    rows = 1 << 21
-    tab = torch.zeros((rows, 128), dtype=torch.float32, device=dev)
-    grids = (1024, 4096, 16384)
-    sink = torch.empty((max(grids) * 256,), dtype=torch.float32, device=dev)
-    st = torch.cuda.current_stream()
-    out = []
-    for grid in grids:
-        for piece in (64, 128, 256, 512):
-            n = (8 << 30) // piece
-            call = lambda: lib.sdm_probe_gather(ctypes.c_void_p(tab.data_ptr()), rows, piece, n, grid,
-                                                ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(st.cuda_stream))
-            if call() != 0:
-                sys.exit("sdm_probe_gather failed")
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(st)
-            for _ in range(5):
-                call()
-            e1.record(st)
-            e1.synchronize()
-            ms = e0.elapsed_time(e1) / 5
-            out.append({"piece_bytes": piece, "workgroups": grid, "ms": round(ms, 4),
-                        "TBps": round(n * piece * 1.5 / ms / 1e9, 3)})
-            print(json.dumps(out[-1]), file=sys.stderr, flush=True)
-    print(json.dumps({"probe": "random in-place row-piece traffic, 1 GiB table of 512-byte rows, "
-                               "half of the pieces written back", "results": out,
-                      "best_TBps": max(r["TBps"] for r in out)}))
 
 
 def host_cpu() -> str:
@@ -368,8 +327,6 @@ def main():
     from sparse_memory_linear_amd import inputs
 
     dev = torch.device("cuda:0")
-    if a.gather_probe:
-        return gather_probe(dev)
     if a.copy_probe > 0:
         src = torch.ones(a.copy_probe // 4, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)

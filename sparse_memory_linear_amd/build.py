@@ -12,9 +12,6 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libsdm.so")
 OBJ = os.path.join(PKG, "_build")
 SOURCES = ["sdm_api.hip", "address.hip", "scan.hip", "scan_bwd.hip", "state_init.hip", "glue.hip"]
-# the measurement aid behind `bench.py --gather-probe`, in a library of its own
-PROBE_LIB = os.path.join(PKG, "libsdm_probe.so")
-PROBE_SOURCES = ["probe_gather.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
@@ -44,12 +41,10 @@ def _link(objs, out: str) -> None:
 def build(verbose: bool = True) -> str:
     os.makedirs(OBJ, exist_ok=True)
     with concurrent.futures.ThreadPoolExecutor(max_workers=4) as ex:
-        objs = list(ex.map(_compile, SOURCES + PROBE_SOURCES))
-    n = len(SOURCES)
-    _link(objs[:n], LIB)
-    _link(objs[n:], PROBE_LIB)
+        objs = list(ex.map(_compile, SOURCES))
+    _link(objs, LIB)
     if verbose:
-        print(f"built {LIB} and {PROBE_LIB}", file=sys.stderr)
+        print(f"built {LIB}", file=sys.stderr)
     return LIB
 
 

@@ -79,7 +79,7 @@ __global__ __launch_bounds__(GW * 64) void gates_kernel(GatesArgs a) {
             const int64_t u = u0 + 4 * g4 + i;
             if (u >= UT) break;
             const uint32_t uu = (uint32_t)u, b = uu / (uint32_t)a.T, t = uu - b * (uint32_t)a.T;  // u < 2^32
-            const int64_t o = (b * H + hrow) * a.T + t;
+            const int64_t o = ((int64_t)b * H + hrow) * a.T + t;  // B * H may pass 2^32
             if (is_a) a.alpha[o] = expf(-Ah * softplusf(acc[i] + bias));
             else a.beta[o] = 1.f / (1.f + expf(-acc[i]));
         }

@@ -48,6 +48,12 @@ namespace {
 constexpr uint32_t ENT_INVALID = 1u << 31;  // padding or out-of-range index: no access
 constexpr uint32_t ENT_FWD = 1u << 30;      // value comes from the LDS ring
 constexpr uint32_t ROW_MASK = (1u << 18) - 1u;
+constexpr uint32_t OFF_MASK = (1u << 30) - 1u;
+// The forward source of a shared-residual writer entry: token distance and
+// write position in the entry word. Reader entries and per-slot writer entries
+// carry the LDS byte offset of the source row in the ring instead (reader: in
+// the entry word, which then needs no row; writer: in the last word), so the
+// scan adds its lane's offset and reads.
 constexpr int POS_SHIFT = 18;               // write position of the source (8 bits)
 constexpr int DIST_SHIFT = 26;              // token distance of the source (4 bits)
 
@@ -154,7 +160,12 @@ struct PlanArgs {
     int64_t Tc, TS, N;
     int D, G, NWW, NWR, TT, pb, P, pshift;
     int64_t ntile;
-    int wpos;   // writer entries of the per-slot training forward: (packed, beta*w, alpha, write position)
+    int wpos;   // per-slot training forward: writer entries carry the write position
+    int form;   // 0: per-slot writer entries (packed, c, b, position | ring offset << 8), c = alpha (1 - beta w),
+                // b = beta w; 1: shared-residual writer entries (packed, w, alpha, beta)
+    int ur;     // LDS ring of the scan: slots (token t uses slot t % ur), write positions per slot,
+    int rpos;   // bytes per position (16 per lane of a row segment)
+    int rlane;
 };
 
 // Rank of this lane's access among the valid accesses of its partition at
@@ -172,13 +183,13 @@ __device__ __forceinline__ int part_rank(bool ok, int part, int P, uint64_t belo
     return rank;
 }
 
-// Forward bits of an access of `row` at token cur (relative to the window
-// start): the latest write of the row at a token in [lo, hi], or 0.
-__device__ __forceinline__ uint32_t fwd_bits(const uint32_t* ht, const uint32_t* bm, uint32_t row, int cur,
-                                             int lo, int hi, int pb) {
-    if (!((bm[row >> 5] >> (row & 31)) & 1u)) return 0u;
+// The latest write of `row` at a token in [lo, hi] (relative to the window
+// start): returns its token (or -1) and its rank in its partition.
+__device__ __forceinline__ int fwd_src(const uint32_t* ht, const uint32_t* bm, uint32_t row, int lo, int hi,
+                                       int pb, uint32_t& bp) {
+    bp = 0;
+    if (!((bm[row >> 5] >> (row & 31)) & 1u)) return -1;
     int best = -1;
-    uint32_t bp = 0;
     uint32_t h = ht_hash(row), ent;
     while ((ent = ht[h]) != HT_EMPTY) {
         if ((ent >> HT_BITS) == row) {
@@ -190,7 +201,7 @@ __device__ __forceinline__ uint32_t fwd_bits(const uint32_t* ht, const uint32_t*
         }
         h = (h + 1) & (HT_CAP - 1);
     }
-    return best < 0 ? 0u : ENT_FWD | ((uint32_t)(cur - best) << DIST_SHIFT) | (bp << POS_SHIFT);
+    return best;
 }
 
 __global__ __launch_bounds__(PLAN_THREADS) __attribute__((amdgpu_waves_per_eu(4))) void plan_kernel(PlanArgs a) {
@@ -282,18 +293,29 @@ __global__ __launch_bounds__(PLAN_THREADS) __attribute__((amdgpu_waves_per_eu(4)
                     if (!ok) continue;
                     // latest writer of this row in [tt-D, tt-1] (writes) or [tt-D, tt] (reads)
                     const int cur = (int)(tt - h0);
-                    const uint32_t packed =
-                        (uint32_t)row[u] | fwd_bits(ht, bm, (uint32_t)row[u], cur, cur - D, cur - (isw ? 1 : 0), pb);
+                    uint32_t bp;
+                    const int src = fwd_src(ht, bm, (uint32_t)row[u], cur - D, cur - (isw ? 1 : 0), pb, bp);
+                    // LDS byte offset of the source row in the scan's ring (slot of its token, its rank)
+                    const uint32_t roff =
+                        src < 0 ? 0u
+                                : ((uint32_t)(h0 + src) % (uint32_t)a.ur * (uint32_t)a.rpos + bp) * (uint32_t)a.rlane;
                     uint8_t* rec = Ps + ((int64_t)part * T + tt) * REC;
-                    if (isw && a.wpos)
+                    if (isw && a.form == 0) {
+                        const float b = be[tt] * w[u], cw = al[tt] * (1.f - b);
+                        const uint32_t w4 = (a.wpos ? (uint32_t)(c + lane) : 0u) | (roff << 8);
+                        *reinterpret_cast<int4*>(rec + (int64_t)rank * 16) =
+                            make_int4((int)((uint32_t)row[u] | (src < 0 ? 0u : ENT_FWD)), __float_as_int(cw),
+                                      __float_as_int(b), (int)w4);
+                    } else if (isw) {
+                        const uint32_t fb =
+                            src < 0 ? 0u : ENT_FWD | ((uint32_t)(cur - src) << DIST_SHIFT) | (bp << POS_SHIFT);
                         *reinterpret_cast<int4*>(rec + (int64_t)rank * 16) = make_int4(
-                            (int)packed, __float_as_int(be[tt] * w[u]), __float_as_int(al[tt]), c + lane);
-                    else if (isw)
-                        *reinterpret_cast<int4*>(rec + (int64_t)rank * 16) = make_int4(
-                            (int)packed, __float_as_int(w[u]), __float_as_int(al[tt]), __float_as_int(be[tt]));
-                    else
+                            (int)((uint32_t)row[u] | fb), __float_as_int(w[u]), __float_as_int(al[tt]),
+                            __float_as_int(be[tt]));
+                    } else {
                         *reinterpret_cast<int2*>(rec + WB + (int64_t)rank * 8) =
-                            make_int2((int)packed, __float_as_int(w[u]));
+                            make_int2((int)(src < 0 ? (uint32_t)row[u] : ENT_FWD | roff), __float_as_int(w[u]));
+                    }
                 }
             }
             // padding: slots past each partition's count
@@ -471,17 +493,19 @@ __global__ __launch_bounds__(SlabCfg<SL>::NWMAX * 64) void scan_kernel(ScanKArgs
         return;
     }
 
+    // A forwarded access loads nothing (its value comes from the ring); the
+    // store of a written row goes to its table offset. Token offsets sit in the
+    // per-lane offset, which the hardware range-checks, so a prefetch past the
+    // last token is dropped and needs no clamp.
     auto row_off = [&](uint32_t pk) -> uint32_t {
         return (pk & ENT_INVALID) ? OOB : __umul24(pk & ROW_MASK, mrow) + colb;
     };
-    auto load_went = [&](int t) -> int4 { return ld_i4(Rp, e_off, (uint32_t)t * REC); };
-    auto load_rent = [&](int t) -> int2 { return ld_i2(Rp, e_off, (uint32_t)t * REC); };
-    auto load_row = [&](uint32_t pk) -> float4 { return ld_f4(Rm, row_off(pk), 0u); };
-    auto load_v = [&](int t) -> V4 { return VL::load(Rv, v_off, (uint32_t)t * vstride); };
+    auto load_row = [&](uint32_t pk) -> float4 { return ld_f4(Rm, (pk & ENT_FWD) ? OOB : row_off(pk), 0u); };
     auto ring_at = [&](int slot, int p) -> float4& { return ring[((int64_t)slot * NWW * G + p) * L + cc]; };
-    auto source = [&](int slot, uint32_t pk, float4 pre) -> float4 {
-        // forwarded rows come from the LDS ring; the ballot keeps the common
-        // no-forward case free of LDS traffic
+    const char* ring_b = reinterpret_cast<const char*>(ring) + cc * 16;
+    // forwarded rows come from the LDS ring; the ballot keeps the common
+    // no-forward case free of LDS traffic
+    auto source = [&](int slot, uint32_t pk, float4 pre) -> float4 {  // shared-residual writers
         const bool f = (pk & (ENT_FWD | ENT_INVALID)) == ENT_FWD;
         if (__ballot(f) != 0ull && f) {
             int sl = slot - (int)((pk >> DIST_SHIFT) & 15u);
@@ -490,27 +514,38 @@ __global__ __launch_bounds__(SlabCfg<SL>::NWMAX * 64) void scan_kernel(ScanKArgs
         }
         return pre;
     };
+    auto source_at = [&](uint32_t pk, uint32_t off, float4 pre) -> float4 {  // readers, per-slot writers
+        const bool f = (pk & (ENT_FWD | ENT_INVALID)) == ENT_FWD;
+        if (__ballot(f) != 0ull && f) pre = *reinterpret_cast<const float4*>(ring_b + off);
+        return pre;
+    };
 
     // one token of a writer wavefront (barriers: [B'_t], B_t)
-    auto write_token = [&](int t, int slot, int4 e, float4 pre, V4 vt) {
+    auto write_token = [&](int t, int slot, int4 e, float4 pre, V4 vt, uint32_t soff) {
         const uint32_t pk = (uint32_t)e.x;
-        const float w = __int_as_float(e.y), al = __int_as_float(e.z), be = __int_as_float(e.w);
-        constexpr bool WPOS = SAVE && FORM == 0;  // entry = (packed, beta*w, alpha, write position)
-        const float4 old = source(slot, pk, pre);
+        float4 old;
+        if constexpr (FORM == 0) old = source_at(pk, (uint32_t)e.w >> 8, pre);
+        else old = source(slot, pk, pre);
         if constexpr (SAVE) {
-            const uint32_t so = WPOS ? __umul24((uint32_t)e.w, dv4) + col4 : s_lane;
+            // per-slot entries carry the write position (partitions reorder them)
+            const uint32_t so = FORM == 0 ? __umul24((uint32_t)e.w & 255u, dv4) + col4 : s_lane;
             st_f4(old, Rs, (pk & ENT_INVALID) ? OOB : so, (uint32_t)t * sstride);
         }
-        float4 mt[NQ], pred[NQ], vf[NQ], nv[NQ];
+        float4 mt[NQ], vf[NQ], nv[NQ];
         RF::unpack(old, mt);
+        VL::f(vt, vf);
+        if constexpr (FORM == 0) {
+            // entry = (packed, c, b, ...): M[i] = c M[i] + b v, c = alpha (1 - beta w), b = beta w
+            const float cw = __int_as_float(e.y), b = __int_as_float(e.z);
 #pragma unroll
-        for (int i = 0; i < NQ; ++i) {
-            mt[i] = f4_scale(al, mt[i]);
-            pred[i] = mt[i];
-        }
-        if constexpr (FORM == 1) {
+            for (int i = 0; i < NQ; ++i) nv[i] = f4_fma(cw, mt[i], f4_scale(b, vf[i]));
+        } else {
+            // entry = (packed, w, alpha, beta): M[i] = alpha M[i] + beta w (v - sum_j w_j alpha M[j])
+            const float w = __int_as_float(e.y), al = __int_as_float(e.z), be = __int_as_float(e.w);
+            float4 pred[NQ];
 #pragma unroll
             for (int i = 0; i < NQ; ++i) {
+                mt[i] = f4_scale(al, mt[i]);
                 const float part = rows_reduce<L>(f4_scale(w, mt[i]));
                 if ((lane & 15) < L)
                     reinterpret_cast<float*>(vbuf)[wave * S + CPL * (lane & 15) + 4 * i + (lane >> 4)] = part;
@@ -523,18 +558,17 @@ __global__ __launch_bounds__(SlabCfg<SL>::NWMAX * 64) void scan_kernel(ScanKArgs
                 for (int q = 1; q < NWMAX; ++q)
                     if (q < NWW) pred[i] = f4_add(pred[i], vbuf[q * (S / 4) + NQ * cc + i]);
             }
-        }
-        VL::f(vt, vf);
 #pragma unroll
-        for (int i = 0; i < NQ; ++i) nv[i] = f4_fma(WPOS ? w : be * w, f4_sub(vf[i], pred[i]), mt[i]);
+            for (int i = 0; i < NQ; ++i) nv[i] = f4_fma(be * w, f4_sub(vf[i], pred[i]), mt[i]);
+        }
         const float4 st = RF::pack(nv);
-        st_f4(st, Rm, row_off(pk), 0u);
+        st_f4(st, Rm, soff, 0u);
         ring_at(slot, pos) = st;
         __syncthreads();
     };
     // one token of a reader wavefront (barriers: [B'_t], B_t); the partial sums
     // of token t are added by the summing wavefront after the next barrier
-    auto read_token = [&](int t, int slot, int2 e, float4 pre) {
+    auto read_token = [&](int t, int2 e, float4 pre, uint32_t yv, uint32_t ys) {
         if constexpr (FORM == 1) __syncthreads();
         __syncthreads();
         // when it sums, reader 0 first adds the previous token's partials
@@ -545,13 +579,13 @@ __global__ __launch_bounds__(SlabCfg<SL>::NWMAX * 64) void scan_kernel(ScanKArgs
             acc = readers_sum<NRMAX, S>(ybuf + ((t - 1) & 1) * NRMAX * S + ylane, nra);
         const uint32_t pk = (uint32_t)e.x;
         float4 cur[NQ];
-        RF::unpack(source(slot, pk, pre), cur);
+        RF::unpack(source_at(pk, pk & OFF_MASK, pre), cur);
 #pragma unroll
         for (int i = 0; i < NQ; ++i) {
             const float part = rows_reduce<L>(f4_scale(__int_as_float(e.y), cur[i]));
             if ((lane & 15) < L) ybuf[((t & 1) * NRMAX + rw) * S + CPL * (lane & 15) + 4 * i + (lane >> 4)] = part;
         }
-        st_f1(acc, Ry, t > 0 ? y_off : OOB, (uint32_t)(t > 0 ? t - 1 : 0) * dv4);
+        st_f1(acc, Ry, yv, ys);  // y of token t - 1: dropped at t = 0 and for all but the summing lanes
     };
 
     // Main loop: U tokens per trip, fully unrolled so that the register rings
@@ -559,47 +593,67 @@ __global__ __launch_bounds__(SlabCfg<SL>::NWMAX * 64) void scan_kernel(ScanKArgs
     // steady-state sequence of memory operations (with a dropped store standing
     // in for each token's store), so that the loop header merges like states and
     // the compiler's memory waits stay D tokens deep.
+    // the table offset of each prefetched write is kept for its store where
+    // the VGPR budget allows (layouts of at most 8 wavefronts)
+    constexpr bool KEEP_OFF = NWMAX <= 8;
     int t_done = 0;
     if (T >= U) {
         float4 pre[UP];
+        uint32_t ve = e_off;  // per-lane offset of the next plan entry to load
         if (writer) {
             int4 ent[U];
             V4 vv[UP];
+            uint32_t so[KEEP_OFF ? UP : 1];
+            uint32_t vo = v_off;  // per-lane offset of the next v to load
+            auto prefetch = [&](int q, int k) {  // entry of token q + D + DM, row and v of token q + D
+                const uint32_t pk = (uint32_t)ent[k].x;
+                const uint32_t ro = row_off(pk);
+                if constexpr (KEEP_OFF) so[q % UP] = ro;
+                pre[q % UP] = ld_f4(Rm, (pk & ENT_FWD) ? OOB : ro, 0u);
+                vv[q % UP] = VL::load(Rv, vo, 0u);
+                vo += vstride;
+            };
 #pragma unroll
             for (int q = 0; q < D + DM; ++q) {
-                ent[q] = load_went(q);
-                if (q >= DM) {
-                    pre[q - DM] = load_row((uint32_t)ent[q - DM].x);
-                    vv[q - DM] = load_v(q - DM);
-                }
-                st_f4(make_float4(0.f, 0.f, 0.f, 0.f), Rm, OOB, 0u);
-                if constexpr (SAVE) st_f4(make_float4(0.f, 0.f, 0.f, 0.f), Rs, OOB, 0u);
+                ent[q] = ld_i4(Rp, ve, 0u);
+                ve += REC;
+                if (q >= DM) prefetch(q - DM, q - DM);
+                // the dropped stores get distinct offsets (identical ones would be
+                // merged away) and the scheduling barrier keeps this order, so
+                // the counter state entering the loop is the steady-state one
+                st_f4(make_float4(0.f, 0.f, 0.f, 0.f), Rm, OOB, (uint32_t)q * 16u);
+                if constexpr (SAVE) st_f4(make_float4(0.f, 0.f, 0.f, 0.f), Rs, OOB, (uint32_t)q * 16u);
+                __builtin_amdgcn_sched_barrier(0);
             }
             for (int t0 = 0; t0 + U <= T; t0 += U) {
 #pragma unroll
                 for (int j = 0; j < U; ++j) {
-                    const int t = t0 + j;
-                    ent[(j + D + DM) % U] = load_went(t + D + DM < T ? t + D + DM : T - 1);
-                    pre[(j + D) % UP] = load_row((uint32_t)ent[(j + D) % U].x);
-                    vv[(j + D) % UP] = load_v(t + D < T ? t + D : T - 1);
-                    write_token(t, j, ent[j], pre[j % UP], vv[j % UP]);
+                    ent[(j + D + DM) % U] = ld_i4(Rp, ve, 0u);
+                    ve += REC;
+                    prefetch(j + D, (j + D) % U);
+                    write_token(t0 + j, j, ent[j], pre[j % UP], vv[j % UP],
+                                KEEP_OFF ? so[j % UP] : row_off((uint32_t)ent[j].x));
                 }
             }
         } else {
             int2 ent[U];
+            uint32_t ys = 0u - dv4;  // y of token t - 1
 #pragma unroll
             for (int q = 0; q < D + DM; ++q) {
-                ent[q] = load_rent(q);
+                ent[q] = ld_i2(Rp, ve, 0u);
+                ve += REC;
                 if (q >= DM) pre[q - DM] = load_row((uint32_t)ent[q - DM].x);
-                st_f1(0.f, Ry, OOB, 0u);
+                st_f1(0.f, Ry, OOB, (uint32_t)q * 4u);
+                __builtin_amdgcn_sched_barrier(0);
             }
             for (int t0 = 0; t0 + U <= T; t0 += U) {
 #pragma unroll
                 for (int j = 0; j < U; ++j) {
-                    const int t = t0 + j;
-                    ent[(j + D + DM) % U] = load_rent(t + D + DM < T ? t + D + DM : T - 1);
+                    ent[(j + D + DM) % U] = ld_i2(Rp, ve, 0u);
+                    ve += REC;
                     pre[(j + D) % UP] = load_row((uint32_t)ent[(j + D) % U].x);
-                    read_token(t, j, ent[j], pre[j % UP]);
+                    read_token(t0 + j, ent[j], pre[j % UP], (j > 0 || t0 > 0) ? y_off : OOB, ys);
+                    ys += dv4;
                 }
             }
         }
@@ -608,11 +662,12 @@ __global__ __launch_bounds__(SlabCfg<SL>::NWMAX * 64) void scan_kernel(ScanKArgs
     // tail (and short sequences): loads right before use; forwarding stays valid
     for (int t = t_done; t < T; ++t) {
         if (writer) {
-            const int4 e = load_went(t);
-            write_token(t, t % U, e, load_row((uint32_t)e.x), load_v(t));
+            const int4 e = ld_i4(Rp, e_off + (uint32_t)t * REC, 0u);
+            write_token(t, t % U, e, load_row((uint32_t)e.x), VL::load(Rv, v_off + (uint32_t)t * vstride, 0u),
+                        row_off((uint32_t)e.x));
         } else {
-            const int2 e = load_rent(t);
-            read_token(t, t % U, e, load_row((uint32_t)e.x));
+            const int2 e = ld_i2(Rp, e_off + (uint32_t)t * REC, 0u);
+            read_token(t, e, load_row((uint32_t)e.x), t > 0 ? y_off : OOB, (uint32_t)(t - 1) * dv4);
         }
     }
     // the last token's partial sums
@@ -712,12 +767,20 @@ __global__ __launch_bounds__(SlabCfg<SL>::NWMAX * 64) void scan_direct_kernel(Di
                 st_f4(pre, Rs, off == OOB ? OOB : (uint32_t)pos * dv4 + col4, (uint32_t)t * (uint32_t)W * dv4);
             float4 mt[NQ], pred[NQ], vf[NQ], nv[NQ];
             RF::unpack(pre, mt);
+            VL::f(vt, vf);
+            if constexpr (FORM == 0) {
+                // M[i] = c M[i] + b v with c = alpha (1 - beta w), b = beta w: the
+                // pipelined form's arithmetic, so a sequence split over both forms
+                // gives the same bits
+                const float b = be * w, cw = al * (1.f - b);
 #pragma unroll
-            for (int i = 0; i < NQ; ++i) {
-                mt[i] = f4_scale(al, mt[i]);
-                pred[i] = mt[i];
-            }
-            if constexpr (FORM == 1) {
+                for (int i = 0; i < NQ; ++i) nv[i] = f4_fma(cw, mt[i], f4_scale(b, vf[i]));
+            } else {
+#pragma unroll
+                for (int i = 0; i < NQ; ++i) {
+                    mt[i] = f4_scale(al, mt[i]);
+                    pred[i] = mt[i];
+                }
 #pragma unroll
                 for (int i = 0; i < NQ; ++i) {
                     const float part = rows_reduce<L>(f4_scale(w, mt[i]));
@@ -730,10 +793,9 @@ __global__ __launch_bounds__(SlabCfg<SL>::NWMAX * 64) void scan_direct_kernel(Di
                     pred[i] = vbuf[NQ * cc + i];
                     for (int q = 1; q < NWW; ++q) pred[i] = f4_add(pred[i], vbuf[q * (S / 4) + NQ * cc + i]);
                 }
-            }
-            VL::f(vt, vf);
 #pragma unroll
-            for (int i = 0; i < NQ; ++i) nv[i] = f4_fma(be * w, f4_sub(vf[i], pred[i]), mt[i]);
+                for (int i = 0; i < NQ; ++i) nv[i] = f4_fma(be * w, f4_sub(vf[i], pred[i]), mt[i]);
+            }
             st_f4(RF::pack(nv), Rm, off, 0u);
             __syncthreads();  // B1: this token's rows are written
             __syncthreads();  // B2
@@ -872,6 +934,10 @@ hipError_t launch_scan_slab(const ScanArgs& a, const Cfg& c, hipStream_t st) {
         p.D = D; p.G = g.G; p.NWW = g.NWW; p.NWR = g.NWR; p.TT = TT; p.pb = pb; p.P = c.P; p.pshift = psh;
         p.ntile = (Tn + TT - 1) / TT;
         p.wpos = save && a.form == 0;
+        p.form = a.form;
+        p.ur = 2 * D + 2;            // the scan kernel's ring: U = 2D + 2 token slots
+        p.rpos = g.NWW * g.G;        // write positions per slot
+        p.rlane = (SL / 4) * 16;     // bytes per position: 16 per lane of a row segment
         hipLaunchKernelGGL(plan_kernel, dim3((unsigned)(p.ntile * a.NS)), dim3(PLAN_THREADS), bm_bytes, st, p);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;

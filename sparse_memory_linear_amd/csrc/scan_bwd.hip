@@ -604,8 +604,14 @@ BCfg bwd_cfg(int64_t NS, int W, int R, int dv, int form) {
     return c;
 }
 
-int64_t bwd_chunk_tokens(int64_t T, int W, int dv) {
-    const int64_t per_tok = (int64_t)(W > 1 ? W : 1) * dv * 4;
+// Tokens per launch: every buffer one stream spans in a launch stays below
+// 2 GiB, so its 32-bit offsets and the dropped-access offset work. Per token a
+// stream holds W pre-image rows, one row of v, dy and dv, W + R index and
+// weight words, W + 2R planner words and W + R partial sums per slab.
+int64_t bwd_chunk_tokens(int64_t T, int W, int R, int dv) {
+    int64_t per_tok = (int64_t)(W > 1 ? W : 1) * dv * 4;
+    if ((int64_t)(W + 2 * R) * 4 > per_tok) per_tok = (int64_t)(W + 2 * R) * 4;
+    if ((int64_t)dv * 4 > per_tok) per_tok = (int64_t)dv * 4;
     const int64_t cap = (int64_t)0x7FFFFFFF / per_tok;
     return T < cap ? T : cap;
 }
@@ -621,7 +627,7 @@ template <int S>
 hipError_t launch_bwd_slab(const BwdArgs& a, const BCfg& c, hipStream_t st) {
     const BGeom g = bwd_geom(S, a.W, a.R);
     const int nslab = a.dv / S;
-    const int64_t Tc = bwd_chunk_tokens(a.T, a.W, a.dv);
+    const int64_t Tc = bwd_chunk_tokens(a.T, a.W, a.R, a.dv);
     float* pw = static_cast<float*>(a.workspace);
     int psh = 0;
     while ((1 << psh) < c.P) ++psh;
@@ -700,7 +706,7 @@ int64_t scan_backward_workspace_bytes(int64_t NS, int64_t T, int W, int R, int d
     for (int form = 0; form < 2; ++form) {
         const BCfg c = bwd_cfg(NS, W, R, dv, form);
         if (c.S == 0) return -1;
-        const int64_t b = bwd_ws_floats(c, NS, bwd_chunk_tokens(T, W, dv), W, R, dv) * 4;
+        const int64_t b = bwd_ws_floats(c, NS, bwd_chunk_tokens(T, W, R, dv), W, R, dv) * 4;
         if (b > need) need = b;
     }
     return need;

@@ -192,25 +192,6 @@ def test_binding_refuses_cpu_tensors(lib):
         binding.sdm_address(x, x, k, k, 8, 8)
 
 
-def test_probe_library_exports_its_declared_symbol_and_rejects_bad_arguments(lib):
-    """The measurement aid (include/sdm_probe.h) ships as its own library; bad
-    arguments return 1 before any launch."""
-    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "sdm_probe.h")).read(), flags=re.S)
-    names = sorted(set(re.findall(r"\b(sdm_[a-z_0-9]+)\s*\(", text)))
-    assert names == ["sdm_probe_gather"]
-    probe = ctypes.CDLL(os.path.join(ROOT, "sparse_memory_linear_amd", "libsdm_probe.so"))
-    f = probe.sdm_probe_gather
-    f.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p,
-                  ctypes.c_void_p]
-    f.restype = ctypes.c_int
-    fake = ctypes.c_void_p(4096)
-    assert f(None, 16, 128, 10, 4, fake, None) == 1            # no table
-    assert f(fake, 0, 128, 10, 4, fake, None) == 1             # no rows
-    assert f(fake, 16, 96, 10, 4, fake, None) == 1             # piece size not 64/128/256/512
-    assert f(fake, 16, 128, 10, 0, fake, None) == 1            # empty grid
-    assert f(fake, 1 << 31, 128, 10, 4, fake, None) == 1       # more rows than 32-bit indices reach
-
-
 def test_glue_calls_reject_bad_arguments_before_launch(lib):
     fake = P(4096)  # never dereferenced: every call below fails validation first
     g = lambda x_dtype=1, w_dtype=1, B=2, T=16, d=1024, H=8: lib.sdm_gates(
