@@ -349,6 +349,11 @@ __global__ void zero_u32(uint32_t* p, int n) {
 }
 
 // ------------------------------------------------------------------ scan
+template <bool B>
+struct BoolC {
+    static constexpr bool value = B;
+};
+
 // Sum of the first Q partial-sum slots (stride S) as a balanced tree. Slots of
 // readers that do not run hold zero, so any power of two Q >= the number of
 // running readers gives the same sum: the tree over 2Q adds a zero subtree.
@@ -515,8 +520,8 @@ __global__ __launch_bounds__(SlabCfg<SL>::NWMAX * 64) void scan_kernel(ScanKArgs
         return pre;
     };
     auto source_at = [&](uint32_t pk, uint32_t off, float4 pre) -> float4 {  // readers, per-slot writers
-        const bool f = (pk & (ENT_FWD | ENT_INVALID)) == ENT_FWD;
-        if (__ballot(f) != 0ull && f) pre = *reinterpret_cast<const float4*>(ring_b + off);
+        // a divergent branch: the hardware skips it when no lane forwards
+        if ((pk & (ENT_FWD | ENT_INVALID)) == ENT_FWD) pre = *reinterpret_cast<const float4*>(ring_b + off);
         return pre;
     };
 
@@ -568,15 +573,19 @@ __global__ __launch_bounds__(SlabCfg<SL>::NWMAX * 64) void scan_kernel(ScanKArgs
     };
     // one token of a reader wavefront (barriers: [B'_t], B_t); the partial sums
     // of token t are added by the summing wavefront after the next barrier
-    auto read_token = [&](int t, int2 e, float4 pre, uint32_t yv, uint32_t ys) {
+    auto read_barrier = [&]() {
         if constexpr (FORM == 1) __syncthreads();
         __syncthreads();
+    };
+    // YS: this wavefront adds the readers' partial sums and stores y (a
+    // separate copy of the loop, so the other readers issue no y store)
+    auto read_token = [&](auto ys_c, int t, int2 e, float4 pre, uint32_t yv, uint32_t ys) {
+        constexpr bool YS = decltype(ys_c)::value;
         // when it sums, reader 0 first adds the previous token's partials
         // (complete since this token's barrier), so their LDS reads overlap
         // the row sum below
         float acc = 0.f;
-        if (ysum)  // uniform per wavefront; no memory operation inside
-            acc = readers_sum<NRMAX, S>(ybuf + ((t - 1) & 1) * NRMAX * S + ylane, nra);
+        if constexpr (YS) acc = readers_sum<NRMAX, S>(ybuf + ((t - 1) & 1) * NRMAX * S + ylane, nra);
         const uint32_t pk = (uint32_t)e.x;
         float4 cur[NQ];
         RF::unpack(source_at(pk, pk & OFF_MASK, pre), cur);
@@ -585,7 +594,7 @@ __global__ __launch_bounds__(SlabCfg<SL>::NWMAX * 64) void scan_kernel(ScanKArgs
             const float part = rows_reduce<L>(f4_scale(__int_as_float(e.y), cur[i]));
             if ((lane & 15) < L) ybuf[((t & 1) * NRMAX + rw) * S + CPL * (lane & 15) + 4 * i + (lane >> 4)] = part;
         }
-        st_f1(acc, Ry, yv, ys);  // y of token t - 1: dropped at t = 0 and for all but the summing lanes
+        if constexpr (YS) st_f1(acc, Ry, yv, ys);  // y of token t - 1: dropped at t = 0 and beyond S lanes
     };
 
     // Main loop: U tokens per trip, fully unrolled so that the register rings
@@ -636,26 +645,32 @@ __global__ __launch_bounds__(SlabCfg<SL>::NWMAX * 64) void scan_kernel(ScanKArgs
                 }
             }
         } else {
-            int2 ent[U];
-            uint32_t ys = 0u - dv4;  // y of token t - 1
+            auto reader_loop = [&](auto ys_c) {
+                constexpr bool YS = decltype(ys_c)::value;
+                int2 ent[U];
+                uint32_t ys = 0u - dv4;  // y of token t - 1
 #pragma unroll
-            for (int q = 0; q < D + DM; ++q) {
-                ent[q] = ld_i2(Rp, ve, 0u);
-                ve += REC;
-                if (q >= DM) pre[q - DM] = load_row((uint32_t)ent[q - DM].x);
-                st_f1(0.f, Ry, OOB, (uint32_t)q * 4u);
-                __builtin_amdgcn_sched_barrier(0);
-            }
-            for (int t0 = 0; t0 + U <= T; t0 += U) {
-#pragma unroll
-                for (int j = 0; j < U; ++j) {
-                    ent[(j + D + DM) % U] = ld_i2(Rp, ve, 0u);
+                for (int q = 0; q < D + DM; ++q) {
+                    ent[q] = ld_i2(Rp, ve, 0u);
                     ve += REC;
-                    pre[(j + D) % UP] = load_row((uint32_t)ent[(j + D) % U].x);
-                    read_token(t0 + j, ent[j], pre[j % UP], (j > 0 || t0 > 0) ? y_off : OOB, ys);
-                    ys += dv4;
+                    if (q >= DM) pre[q - DM] = load_row((uint32_t)ent[q - DM].x);
+                    if constexpr (YS) st_f1(0.f, Ry, OOB, (uint32_t)q * 4u);
+                    __builtin_amdgcn_sched_barrier(0);
                 }
-            }
+                for (int t0 = 0; t0 + U <= T; t0 += U) {
+#pragma unroll
+                    for (int j = 0; j < U; ++j) {
+                        ent[(j + D + DM) % U] = ld_i2(Rp, ve, 0u);
+                        ve += REC;
+                        pre[(j + D) % UP] = load_row((uint32_t)ent[(j + D) % U].x);
+                        read_barrier();
+                        read_token(ys_c, t0 + j, ent[j], pre[j % UP], (j > 0 || t0 > 0) ? y_off : OOB, ys);
+                        ys += dv4;
+                    }
+                }
+            };
+            if (ysum) reader_loop(BoolC<true>{});
+            else reader_loop(BoolC<false>{});
         }
         t_done = (T / U) * U;
     }
@@ -667,7 +682,10 @@ __global__ __launch_bounds__(SlabCfg<SL>::NWMAX * 64) void scan_kernel(ScanKArgs
                         row_off((uint32_t)e.x));
         } else {
             const int2 e = ld_i2(Rp, e_off + (uint32_t)t * REC, 0u);
-            read_token(t, e, load_row((uint32_t)e.x), t > 0 ? y_off : OOB, (uint32_t)(t - 1) * dv4);
+            const float4 pr = load_row((uint32_t)e.x);
+            read_barrier();
+            if (ysum) read_token(BoolC<true>{}, t, e, pr, t > 0 ? y_off : OOB, (uint32_t)(t - 1) * dv4);
+            else read_token(BoolC<false>{}, t, e, pr, OOB, 0u);
         }
     }
     // the last token's partial sums
