@@ -61,31 +61,43 @@ constexpr int DIST_SHIFT = 26;              // token distance of the source (4 b
 // entries lead by another D + 1 tokens (memory counters complete in order, so
 // waiting on an entry also waits on every older row load: a lead >= D keeps D
 // tokens of rows in flight); NWMAX = wavefronts per workgroup (sets the VGPR
-// budget: 8 -> 256, 16 -> 128).
-#ifndef SDM_SCAN_DEPTH
-#define SDM_SCAN_DEPTH 10
-#endif
-#ifndef SDM_SCAN_DEPTH32
-#define SDM_SCAN_DEPTH32 6
-#endif
+// budget: 8 -> 256, 16 -> 128). The token loop is unrolled U times so that
+// every register ring index is static: U is a multiple of D + 1 (row and
+// entry rings), of UR (the LDS ring of written rows, token t in slot t % UR,
+// reuse needs UR >= D + 2) and of NBT (the ring of loaded entry blocks; a
+// lane loads the entries of BT <= 4 consecutive tokens at once, and a block
+// stays until the row loads of its tokens are issued).
 template <int S>
 struct SlabCfg {
-    static constexpr int D = SDM_SCAN_DEPTH, NWMAX = 8;
+    static constexpr int D = 7, NWMAX = 8, U = 24, UR = 12, NBT = 12, BT = 4;
 };
-#ifndef SDM_SCAN_DEPTH8
-#define SDM_SCAN_DEPTH8 SDM_SCAN_DEPTH
-#endif
-#ifndef SDM_SCAN_NW8
-#define SDM_SCAN_NW8 8
-#endif
+// 16-column slabs: one entry per load. This layout serves the few-stream
+// shapes, whose per-token chain of dependent steps sets the pace; there the
+// broadcasts cost more than the saved loads (8 streams x 131072 tokens:
+// 30.4 ms with one entry per load, 31.3 with four, 31.5 with two).
 template <>
-struct SlabCfg<8> {
-    static constexpr int D = SDM_SCAN_DEPTH8, NWMAX = SDM_SCAN_NW8;
+struct SlabCfg<16> {
+    static constexpr int D = 7, NWMAX = 8, U = 24, UR = 12, NBT = 12, BT = 1;
 };
 template <>
 struct SlabCfg<32> {
-    static constexpr int D = SDM_SCAN_DEPTH32, NWMAX = 16;
+    static constexpr int D = 5, NWMAX = 16, U = 12, UR = 12, NBT = 12, BT = 4;
 };
+// tokens whose plan entries one lane load fetches: the lanes of a row segment
+// (in groups of at most 4, a DPP quad) take consecutive tokens
+template <int S>
+constexpr int entry_batch() {
+    constexpr int l = S / 4 >= 4 ? 4 : S / 4;
+    return SlabCfg<S>::BT < l ? SlabCfg<S>::BT : l;
+}
+template <int S>
+constexpr bool slab_cfg_ok() {
+    constexpr int D = SlabCfg<S>::D, U = SlabCfg<S>::U, UR = SlabCfg<S>::UR, NBT = SlabCfg<S>::NBT;
+    constexpr int BT = entry_batch<S>();
+    return U % (D + 1) == 0 && U % UR == 0 && U % NBT == 0 && NBT % BT == 0 && UR >= D + 2 &&
+           NBT / BT >= 1 + (BT + D) / BT && D <= 15;
+}
+static_assert(slab_cfg_ok<4>() && slab_cfg_ok<8>() && slab_cfg_ok<16>() && slab_cfg_ok<32>(), "ring sizes");
 
 // Geometry of a slab of S fp32 columns: L = S/4 lanes per row segment (16 B
 // each), G = 64/L rows per wavefront; NWW = ceil(W/G) writer and NWR = ceil(R/G)
@@ -166,6 +178,8 @@ struct PlanArgs {
     int ur;     // LDS ring of the scan: slots (token t uses slot t % ur), write positions per slot,
     int rpos;   // bytes per position (16 per lane of a row segment)
     int rlane;
+    int bt;     // records in blocks of bt tokens: [writer positions][bt] entries, then [reader positions][bt]
+    int64_t tp; // tokens of a (stream, partition) record region (Tc rounded up to bt)
 };
 
 // Rank of this lane's access among the valid accesses of its partition at
@@ -224,7 +238,13 @@ __global__ __launch_bounds__(PLAN_THREADS) __attribute__((amdgpu_waves_per_eu(4)
     const float* wr = a.wt_r + s * a.TS * R;
     const float* al = a.alpha + s * a.TS;
     const float* be = a.beta + s * a.TS;
-    uint8_t* Ps = a.plan + s * P * T * REC;   // this stream's records [P][Tc][rec]
+    uint8_t* Ps = a.plan + s * P * a.tp * REC;   // this stream's records [P][tp][rec]
+    const int BT = a.bt;
+    // byte offset of the entry of token tt at writer / reader position k in a partition's records
+    auto w_at = [&](int64_t tt, int k) -> int64_t { return (tt / BT) * BT * REC + ((int64_t)k * BT + tt % BT) * 16; };
+    auto r_at = [&](int64_t tt, int k) -> int64_t {
+        return (tt / BT) * BT * REC + WB * BT + ((int64_t)k * BT + tt % BT) * 8;
+    };
 
     for (int i = tid; i < HT_CAP / 4; i += PLAN_THREADS)
         reinterpret_cast<uint4*>(ht)[i] = make_uint4(HT_EMPTY, HT_EMPTY, HT_EMPTY, HT_EMPTY);
@@ -299,21 +319,21 @@ __global__ __launch_bounds__(PLAN_THREADS) __attribute__((amdgpu_waves_per_eu(4)
                     const uint32_t roff =
                         src < 0 ? 0u
                                 : ((uint32_t)(h0 + src) % (uint32_t)a.ur * (uint32_t)a.rpos + bp) * (uint32_t)a.rlane;
-                    uint8_t* rec = Ps + ((int64_t)part * T + tt) * REC;
+                    uint8_t* rec = Ps + (int64_t)part * a.tp * REC;
                     if (isw && a.form == 0) {
                         const float b = be[tt] * w[u], cw = al[tt] * (1.f - b);
                         const uint32_t w4 = (a.wpos ? (uint32_t)(c + lane) : 0u) | (roff << 8);
-                        *reinterpret_cast<int4*>(rec + (int64_t)rank * 16) =
+                        *reinterpret_cast<int4*>(rec + w_at(tt, rank)) =
                             make_int4((int)((uint32_t)row[u] | (src < 0 ? 0u : ENT_FWD)), __float_as_int(cw),
                                       __float_as_int(b), (int)w4);
                     } else if (isw) {
                         const uint32_t fb =
                             src < 0 ? 0u : ENT_FWD | ((uint32_t)(cur - src) << DIST_SHIFT) | (bp << POS_SHIFT);
-                        *reinterpret_cast<int4*>(rec + (int64_t)rank * 16) = make_int4(
+                        *reinterpret_cast<int4*>(rec + w_at(tt, rank)) = make_int4(
                             (int)((uint32_t)row[u] | fb), __float_as_int(w[u]), __float_as_int(al[tt]),
                             __float_as_int(be[tt]));
                     } else {
-                        *reinterpret_cast<int2*>(rec + WB + (int64_t)rank * 8) =
+                        *reinterpret_cast<int2*>(rec + r_at(tt, rank)) =
                             make_int2((int)(src < 0 ? (uint32_t)row[u] : ENT_FWD | roff), __float_as_int(w[u]));
                     }
                 }
@@ -329,12 +349,12 @@ __global__ __launch_bounds__(PLAN_THREADS) __attribute__((amdgpu_waves_per_eu(4)
                 for (int q = 0; q < MAX_PARTS; ++q) {
                     if (q >= P) break;
                     if (lane == 0) atomicMax(&smax[br][q], (uint32_t)cnt[u][q]);
-                    uint8_t* rec = Ps + ((int64_t)q * T + tt) * REC;
+                    uint8_t* rec = Ps + (int64_t)q * a.tp * REC;
                     for (int k = cnt[u][q] + lane; k < cap; k += 64) {
                         if (isw)
-                            *reinterpret_cast<int4*>(rec + (int64_t)k * 16) = make_int4((int)ENT_INVALID, 0, 0, 0);
+                            *reinterpret_cast<int4*>(rec + w_at(tt, k)) = make_int4((int)ENT_INVALID, 0, 0, 0);
                         else
-                            *reinterpret_cast<int2*>(rec + WB + (int64_t)k * 8) = make_int2((int)ENT_INVALID, 0);
+                            *reinterpret_cast<int2*>(rec + r_at(tt, k)) = make_int2((int)ENT_INVALID, 0);
                     }
                 }
             }
@@ -353,6 +373,28 @@ template <bool B>
 struct BoolC {
     static constexpr bool value = B;
 };
+
+// Entry of token i (0 <= i < BT) of a block: the lanes of a row segment hold
+// consecutive tokens' entries (lane l holds token l % BT), a DPP quad
+// permutation hands token i's to every lane of the segment.
+template <int BT, int I>
+__device__ __forceinline__ int ent_bcast_c(int x) {
+    if constexpr (BT == 2) return __builtin_amdgcn_mov_dpp(x, I | (I << 2) | ((2 + I) << 4) | ((2 + I) << 6), 0xF, 0xF, false);
+    else return __builtin_amdgcn_mov_dpp(x, I | (I << 2) | (I << 4) | (I << 6), 0xF, 0xF, false);
+}
+template <int BT>
+__device__ __forceinline__ int ent_bcast(int x, int i) {
+    if constexpr (BT == 1) return x;
+    else if constexpr (BT == 2) return i == 0 ? ent_bcast_c<2, 0>(x) : ent_bcast_c<2, 1>(x);
+    else {
+        switch (i) {
+            case 0: return ent_bcast_c<4, 0>(x);
+            case 1: return ent_bcast_c<4, 1>(x);
+            case 2: return ent_bcast_c<4, 2>(x);
+            default: return ent_bcast_c<4, 3>(x);
+        }
+    }
+}
 
 // Sum of the first Q partial-sum slots (stride S) as a balanced tree. Slots of
 // readers that do not run hold zero, so any power of two Q >= the number of
@@ -409,13 +451,12 @@ __global__ __launch_bounds__(SlabCfg<SL>::NWMAX * 64) void scan_kernel(ScanKArgs
     using RF = RowFmt<MBF16>;
     constexpr int L = SL / 4, G = 64 / L, NQ = RF::NQ, CPL = RF::CPL, S = L * CPL;
     constexpr int D = SlabCfg<SL>::D, NWMAX = SlabCfg<SL>::NWMAX, NRMAX = nrmax<SL>();
-    constexpr int DM = D + 1;       // plan-entry lead beyond D
-    constexpr int UP = D + 1;       // row / value register rings: D in flight + the one in use
-    constexpr int U = D + DM + 1;   // plan-entry ring = unroll factor (a multiple of UP, so
-                                    // every ring index is static in the unrolled loop)
-    static_assert(U % UP == 0, "ring sizes");
-    constexpr int UR = U;           // LDS ring of written rows: token t uses slot t % U, a
-                                    // constant in the unrolled loop (reuse needs UR >= D + 2)
+    constexpr int DM = D + 1;                   // plan-entry lead beyond D
+    constexpr int UP = D + 1;                   // row / value / entry rings: D in flight + the one in use
+    constexpr int U = SlabCfg<SL>::U;           // unroll factor: every ring index is static
+    constexpr int UR = SlabCfg<SL>::UR;         // LDS ring of written rows: token t in slot t % UR
+    constexpr int BT = entry_batch<SL>();       // tokens whose entries one lane load fetches
+    constexpr int NB = SlabCfg<SL>::NBT / BT;   // ring of loaded entry blocks
     using VL = VLoadN<VBF16, NQ>;
     using V4 = typename VL::T;
     const int NWW = a.NWW, NWR = a.NWR, T = a.T, dv = a.dv;
@@ -433,7 +474,10 @@ __global__ __launch_bounds__(SlabCfg<SL>::NWMAX * 64) void scan_kernel(ScanKArgs
     const int col = slab * S + cc * CPL;
     const Geom geo{SL, G, NWW, NWR};
     const uint32_t REC = (uint32_t)geo.rec();
-    const rsrc_t Rp = make_rsrc(a.plan + (s * a.P + part) * (int64_t)T * REC, (int64_t)T * REC);
+    // plan records of this (stream, partition): blocks of BT tokens, each block
+    // [writer positions][BT tokens] entries then [reader positions][BT tokens]
+    const int64_t TP = ((int64_t)T + BT - 1) / BT * BT;
+    const rsrc_t Rp = make_rsrc(a.plan + (s * a.P + part) * TP * REC, TP * REC);
     const rsrc_t Rm = make_rsrc(static_cast<char*>(a.M) + s * a.N * dv * RF::ESZ, a.N * dv * RF::ESZ);
     const rsrc_t Rv = make_rsrc(static_cast<const char*>(a.v) + s * a.TS * dv * VL::ESZ, (int64_t)T * dv * VL::ESZ);
     const rsrc_t Ry = make_rsrc(a.y + s * a.ys + part * a.yp, (int64_t)T * dv * 4);
@@ -441,7 +485,9 @@ __global__ __launch_bounds__(SlabCfg<SL>::NWMAX * 64) void scan_kernel(ScanKArgs
     const bool writer = wave < NWW;
     const int pos = wave * G + r;                        // write position of a writer lane
     const int rw = wave - NWW;                           // reader index
-    const uint32_t e_off = writer ? (uint32_t)pos * 16u : (uint32_t)geo.wbytes() + (uint32_t)(rw * G + r) * 8u;
+    const uint32_t e_off = writer ? ((uint32_t)pos * BT + (uint32_t)(cc % BT)) * 16u
+                                  : (uint32_t)geo.wbytes() * BT + ((uint32_t)(rw * G + r) * BT + (uint32_t)(cc % BT)) * 8u;
+    const uint32_t BREC = (uint32_t)BT * REC;  // bytes of one block of entries
     const uint32_t dv4 = (uint32_t)dv * 4u, col4 = (uint32_t)col * 4u;          // fp32 rows (y, snapshots)
     const uint32_t mrow = (uint32_t)dv * RF::ESZ, colb = (uint32_t)col * RF::ESZ;  // table rows
     const uint32_t v_off = (uint32_t)col * VL::ESZ;
@@ -507,7 +553,6 @@ __global__ __launch_bounds__(SlabCfg<SL>::NWMAX * 64) void scan_kernel(ScanKArgs
     };
     auto load_row = [&](uint32_t pk) -> float4 { return ld_f4(Rm, (pk & ENT_FWD) ? OOB : row_off(pk), 0u); };
     auto ring_at = [&](int slot, int p) -> float4& { return ring[((int64_t)slot * NWW * G + p) * L + cc]; };
-    const char* ring_b = reinterpret_cast<const char*>(ring) + cc * 16;
     // forwarded rows come from the LDS ring; the ballot keeps the common
     // no-forward case free of LDS traffic
     auto source = [&](int slot, uint32_t pk, float4 pre) -> float4 {  // shared-residual writers
@@ -520,8 +565,16 @@ __global__ __launch_bounds__(SlabCfg<SL>::NWMAX * 64) void scan_kernel(ScanKArgs
         return pre;
     };
     auto source_at = [&](uint32_t pk, uint32_t off, float4 pre) -> float4 {  // readers, per-slot writers
-        // a divergent branch: the hardware skips it when no lane forwards
-        if ((pk & (ENT_FWD | ENT_INVALID)) == ENT_FWD) pre = *reinterpret_cast<const float4*>(ring_b + off);
+        // a uniform branch around one 16-byte read of every lane (off is a
+        // multiple of 16; lanes that do not forward read slot 0 and keep pre)
+        const bool f = (pk & (ENT_FWD | ENT_INVALID)) == ENT_FWD;
+        if (__ballot(f) != 0ull) {
+            const float4 x = ring[(f ? off >> 4 : 0u) + cc];
+            pre.x = f ? x.x : pre.x;  // per component (a float4 select goes through memory)
+            pre.y = f ? x.y : pre.y;
+            pre.z = f ? x.z : pre.z;
+            pre.w = f ? x.w : pre.w;
+        }
         return pre;
     };
 
@@ -608,14 +661,22 @@ __global__ __launch_bounds__(SlabCfg<SL>::NWMAX * 64) void scan_kernel(ScanKArgs
     int t_done = 0;
     if (T >= U) {
         float4 pre[UP];
-        uint32_t ve = e_off;  // per-lane offset of the next plan entry to load
+        uint32_t ve = e_off;  // per-lane offset of the next block of entries
         if (writer) {
-            int4 ent[U];
+            int4 blk[NB], ent[UP];
             V4 vv[UP];
             uint32_t so[KEEP_OFF ? UP : 1];
             uint32_t vo = v_off;  // per-lane offset of the next v to load
-            auto prefetch = [&](int q, int k) {  // entry of token q + D + DM, row and v of token q + D
-                const uint32_t pk = (uint32_t)ent[k].x;
+            auto load_block = [&](int q) {  // entries of tokens q .. q + BT - 1
+                blk[(q / BT) % NB] = ld_i4(Rp, ve, 0u);
+                ve += BREC;
+            };
+            auto prefetch = [&](int q) {  // token q: its entry, row and v
+                const int4 b = blk[(q / BT) % NB];
+                const int4 e = make_int4(ent_bcast<BT>(b.x, q % BT), ent_bcast<BT>(b.y, q % BT),
+                                         ent_bcast<BT>(b.z, q % BT), ent_bcast<BT>(b.w, q % BT));
+                ent[q % UP] = e;
+                const uint32_t pk = (uint32_t)e.x;
                 const uint32_t ro = row_off(pk);
                 if constexpr (KEEP_OFF) so[q % UP] = ro;
                 pre[q % UP] = ld_f4(Rm, (pk & ENT_FWD) ? OOB : ro, 0u);
@@ -623,48 +684,54 @@ __global__ __launch_bounds__(SlabCfg<SL>::NWMAX * 64) void scan_kernel(ScanKArgs
                 vo += vstride;
             };
 #pragma unroll
-            for (int q = 0; q < D + DM; ++q) {
-                ent[q] = ld_i4(Rp, ve, 0u);
-                ve += REC;
-                if (q >= DM) prefetch(q - DM, q - DM);
+            for (int p = 0; p < D + DM; ++p) {
+                if (p % BT == 0) load_block(p);
+                if (p >= DM) prefetch(p - DM);
                 // the dropped stores get distinct offsets (identical ones would be
                 // merged away) and the scheduling barrier keeps this order, so
                 // the counter state entering the loop is the steady-state one
-                st_f4(make_float4(0.f, 0.f, 0.f, 0.f), Rm, OOB, (uint32_t)q * 16u);
-                if constexpr (SAVE) st_f4(make_float4(0.f, 0.f, 0.f, 0.f), Rs, OOB, (uint32_t)q * 16u);
+                st_f4(make_float4(0.f, 0.f, 0.f, 0.f), Rm, OOB, (uint32_t)p * 16u);
+                if constexpr (SAVE) st_f4(make_float4(0.f, 0.f, 0.f, 0.f), Rs, OOB, (uint32_t)p * 16u);
                 __builtin_amdgcn_sched_barrier(0);
             }
             for (int t0 = 0; t0 + U <= T; t0 += U) {
 #pragma unroll
                 for (int j = 0; j < U; ++j) {
-                    ent[(j + D + DM) % U] = ld_i4(Rp, ve, 0u);
-                    ve += REC;
-                    prefetch(j + D, (j + D) % U);
-                    write_token(t0 + j, j, ent[j], pre[j % UP], vv[j % UP],
-                                KEEP_OFF ? so[j % UP] : row_off((uint32_t)ent[j].x));
+                    if ((j + D + DM) % BT == 0) load_block(j + D + DM);
+                    prefetch(j + D);
+                    write_token(t0 + j, j % UR, ent[j % UP], pre[j % UP], vv[j % UP],
+                                KEEP_OFF ? so[j % UP] : row_off((uint32_t)ent[j % UP].x));
                 }
             }
         } else {
             auto reader_loop = [&](auto ys_c) {
                 constexpr bool YS = decltype(ys_c)::value;
-                int2 ent[U];
+                int2 blk[NB], ent[UP];
                 uint32_t ys = 0u - dv4;  // y of token t - 1
+                auto load_block = [&](int q) {
+                    blk[(q / BT) % NB] = ld_i2(Rp, ve, 0u);
+                    ve += BREC;
+                };
+                auto prefetch = [&](int q) {
+                    const int2 b = blk[(q / BT) % NB];
+                    const int2 e = make_int2(ent_bcast<BT>(b.x, q % BT), ent_bcast<BT>(b.y, q % BT));
+                    ent[q % UP] = e;
+                    pre[q % UP] = load_row((uint32_t)e.x);
+                };
 #pragma unroll
-                for (int q = 0; q < D + DM; ++q) {
-                    ent[q] = ld_i2(Rp, ve, 0u);
-                    ve += REC;
-                    if (q >= DM) pre[q - DM] = load_row((uint32_t)ent[q - DM].x);
-                    if constexpr (YS) st_f1(0.f, Ry, OOB, (uint32_t)q * 4u);
+                for (int p = 0; p < D + DM; ++p) {
+                    if (p % BT == 0) load_block(p);
+                    if (p >= DM) prefetch(p - DM);
+                    if constexpr (YS) st_f1(0.f, Ry, OOB, (uint32_t)p * 4u);
                     __builtin_amdgcn_sched_barrier(0);
                 }
                 for (int t0 = 0; t0 + U <= T; t0 += U) {
 #pragma unroll
                     for (int j = 0; j < U; ++j) {
-                        ent[(j + D + DM) % U] = ld_i2(Rp, ve, 0u);
-                        ve += REC;
-                        pre[(j + D) % UP] = load_row((uint32_t)ent[(j + D) % U].x);
+                        if ((j + D + DM) % BT == 0) load_block(j + D + DM);
+                        prefetch(j + D);
                         read_barrier();
-                        read_token(ys_c, t0 + j, ent[j], pre[j % UP], (j > 0 || t0 > 0) ? y_off : OOB, ys);
+                        read_token(ys_c, t0 + j, ent[j % UP], pre[j % UP], (j > 0 || t0 > 0) ? y_off : OOB, ys);
                         ys += dv4;
                     }
                 }
@@ -676,12 +743,17 @@ __global__ __launch_bounds__(SlabCfg<SL>::NWMAX * 64) void scan_kernel(ScanKArgs
     }
     // tail (and short sequences): loads right before use; forwarding stays valid
     for (int t = t_done; t < T; ++t) {
+        const uint32_t bo = e_off + (uint32_t)(t / BT) * BREC;
+        const int i = t % BT;
         if (writer) {
-            const int4 e = ld_i4(Rp, e_off + (uint32_t)t * REC, 0u);
-            write_token(t, t % U, e, load_row((uint32_t)e.x), VL::load(Rv, v_off + (uint32_t)t * vstride, 0u),
+            const int4 b = ld_i4(Rp, bo, 0u);
+            const int4 e = make_int4(ent_bcast<BT>(b.x, i), ent_bcast<BT>(b.y, i), ent_bcast<BT>(b.z, i),
+                                     ent_bcast<BT>(b.w, i));
+            write_token(t, t % UR, e, load_row((uint32_t)e.x), VL::load(Rv, v_off + (uint32_t)t * vstride, 0u),
                         row_off((uint32_t)e.x));
         } else {
-            const int2 e = ld_i2(Rp, e_off + (uint32_t)t * REC, 0u);
+            const int2 b = ld_i2(Rp, bo, 0u);
+            const int2 e = make_int2(ent_bcast<BT>(b.x, i), ent_bcast<BT>(b.y, i));
             const float4 pr = load_row((uint32_t)e.x);
             read_barrier();
             if (ysum) read_token(BoolC<true>{}, t, e, pr, t > 0 ? y_off : OOB, (uint32_t)(t - 1) * dv4);
@@ -838,11 +910,11 @@ __global__ __launch_bounds__(SlabCfg<SL>::NWMAX * 64) void scan_direct_kernel(Di
 // Ring reuse: the writer of token t overwrites slot t % UR, last used by token
 // t - UR; its readers (tokens up to t - UR + D) have finished once every
 // wavefront passed barrier B_{t-1}, which needs t - UR + D <= t - 2, i.e.
-// UR >= D + 2 (here UR = 2D + 2).
+// UR >= D + 2 (checked for every slab configuration).
 
 template <int SL>
 size_t scan_lds_bytes(const Geom& g, int cpl) {
-    constexpr int D = SlabCfg<SL>::D, UR = 2 * D + 2, L = SL / 4;
+    constexpr int UR = SlabCfg<SL>::UR, L = SL / 4;
     const int S = L * cpl;
     return (size_t)UR * g.NWW * g.G * L * 16 + (size_t)2 * nrmax<SL>() * S * 4 + (size_t)g.NWW * S * 4;
 }
@@ -864,9 +936,13 @@ __global__ __launch_bounds__(256) void ypart_reduce(const float4* __restrict__ y
 int64_t chunk_tokens(int64_t T, const Geom& g, int dv, int save_w = 0) {
     int64_t per_tok = g.rec() > (int64_t)dv * 4 ? g.rec() : (int64_t)dv * 4;
     if ((int64_t)save_w * dv * 4 > per_tok) per_tok = (int64_t)save_w * dv * 4;
-    const int64_t cap = (int64_t)0x7FFFFFFF / per_tok;
+    const int64_t cap = (int64_t)0x7FFFFFFF / per_tok - 4;  // room for the records' block padding
     return T < cap ? T : cap;
 }
+
+// Tokens of a launch's plan record region: rounded up to a whole block of
+// entries (at most 4 tokens a block)
+inline int64_t plan_tokens(int64_t Tc) { return (Tc + 3) / 4 * 4; }
 
 // A scan configuration: slab width S, row partitions P and the wavefront layout.
 struct Cfg {
@@ -880,7 +956,7 @@ struct WsLayout {
 };
 WsLayout ws_layout(const Cfg& c, int64_t NS, int64_t Tc, int dv) {
     WsLayout w;
-    w.plan_bytes = NS * c.P * Tc * c.g.rec();
+    w.plan_bytes = NS * c.P * plan_tokens(Tc) * c.g.rec();
     w.ypart_off = (w.plan_bytes + 255) / 256 * 256;
     const int64_t yend = c.P > 1 ? w.ypart_off + (int64_t)c.P * NS * Tc * dv * 4 : w.plan_bytes;
     w.maxc_off = (yend + 255) / 256 * 256;
@@ -953,7 +1029,9 @@ hipError_t launch_scan_slab(const ScanArgs& a, const Cfg& c, hipStream_t st) {
         p.ntile = (Tn + TT - 1) / TT;
         p.wpos = save && a.form == 0;
         p.form = a.form;
-        p.ur = 2 * D + 2;            // the scan kernel's ring: U = 2D + 2 token slots
+        p.ur = SlabCfg<SL>::UR;      // the scan kernel's ring of written rows: token slots
+        p.bt = entry_batch<SL>();    // tokens per block of entries
+        p.tp = (Tn + p.bt - 1) / p.bt * p.bt;
         p.rpos = g.NWW * g.G;        // write positions per slot
         p.rlane = (SL / 4) * 16;     // bytes per position: 16 per lane of a row segment
         hipLaunchKernelGGL(plan_kernel, dim3((unsigned)(p.ntile * a.NS)), dim3(PLAN_THREADS), bm_bytes, st, p);
