@@ -78,9 +78,10 @@ def test_slots_match_oracle_end_to_end(name, over):
     g = _gpu(x)
     idx_w, wt_w, idx_r, wt_r = sdm.sdm_address(g["q_w"], g["q_r"], g["subkeys"], g["subkeys"],
                                                wl.W, wl.R)
-    for q, k, gi in ((x["q_w"], wl.W, idx_w), (x["q_r"], wl.R, idx_r)):
-        oi, ow, osc, onext = oracle.address(q, x["subkeys"], k)
-        res = compare_slots(gi.cpu().numpy(), oi, osc, onext)
+    for br, q, k, gi in (("write", x["q_w"], wl.W, idx_w), ("read", x["q_r"], wl.R, idx_r)):
+        ohalf = oracle.half_scores(q, x["subkeys"])
+        oi, ow, osc, onext = oracle.select(ohalf, k)
+        res = compare_slots(gi.cpu().numpy(), oi, osc, onext, ohalf, label=f"dot {name} {over} {br}")
         say(f"  k={k}: {res}")
         assert res["violating"] == 0
 
@@ -178,7 +179,7 @@ def test_full_size_sampled_tokens(name):
     iw, ww, ir, wr = sdm.sdm_address(g["q_w"], g["q_r"], g["subkeys"], g["subkeys"], wl.W, wl.R)
     torch.cuda.synchronize()
     rng = np.random.default_rng(11)
-    nb = 256
+    nb = 2048
     bs = torch.from_numpy(rng.integers(0, wl.B, nb)); hs = torch.from_numpy(rng.integers(0, wl.H, nb))
     ts = torch.from_numpy(rng.integers(0, wl.T, nb)); ar = torch.arange(nb)
     for qn, k, gi in (("q_w", wl.W, iw), ("q_r", wl.R, ir)):
@@ -192,8 +193,10 @@ def test_full_size_sampled_tokens(name):
         assert np.array_equal(gsel, oi2[0, 0])
         qq = torch.zeros((1, wl.H, nb, 2, wl.d_h), dtype=torch.float32)
         qq[0, hs, ar] = qs.float()
-        oi, ow, osc, onext = oracle.address(qq, x["subkeys"], k)
+        ohalf = oracle.half_scores(qq, x["subkeys"])
+        oi, ow, osc, onext = oracle.select(ohalf, k)
         sel = (0, hs.numpy(), ar.numpy())
-        res = compare_slots(gsel, oi[sel], osc[sel], onext[sel])
+        res = compare_slots(gsel, oi[sel], osc[sel], onext[sel], ohalf[sel],
+                            label=f"dot {name} full size, {nb} sampled token-branches, {qn}")
         say(f"  {qn}: {res}")
         assert res["violating"] == 0

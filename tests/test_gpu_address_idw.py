@@ -92,10 +92,11 @@ def test_idw_slots_match_oracle_end_to_end(name, over):
     g = _gpu(x)
     idx_w, wt_w, idx_r, wt_r = sdm.sdm_address(g["q_w"], g["q_r"], g["subkeys"], g["subkeys"],
                                                wl.W, wl.R, scoring="idw")
-    for q, k, gi, gw in ((x["q_w"], wl.W, idx_w, wt_w), (x["q_r"], wl.R, idx_r, wt_r)):
-        oi, ow, osc, onext = oracle.address(q, x["subkeys"], k, scoring="idw")
+    for br, q, k, gi, gw in (("write", x["q_w"], wl.W, idx_w, wt_w), ("read", x["q_r"], wl.R, idx_r, wt_r)):
+        ohalf = oracle.half_scores(q, x["subkeys"], scoring="idw")
+        oi, ow, osc, onext = oracle.select(ohalf, k)
         gi = gi.cpu().numpy()
-        res = compare_slots(gi, oi, osc, onext)
+        res = compare_slots(gi, oi, osc, onext, ohalf, label=f"idw {name} {over} {br}")
         say(f"  k={k}: {res}")
         assert res["violating"] == 0
         same = (gi == oi).all(-1)
@@ -154,7 +155,7 @@ def test_idw_full_size_sampled_tokens(name):
                                      scoring="idw")
     torch.cuda.synchronize()
     rng = np.random.default_rng(12)
-    nb = 256
+    nb = 2048
     bs = torch.from_numpy(rng.integers(0, wl.B, nb)); hs = torch.from_numpy(rng.integers(0, wl.H, nb))
     ts = torch.from_numpy(rng.integers(0, wl.T, nb)); ar = torch.arange(nb)
     for qn, k, gi in (("q_w", wl.W, iw), ("q_r", wl.R, ir)):
@@ -167,8 +168,10 @@ def test_idw_full_size_sampled_tokens(name):
         assert np.array_equal(gsel, oi2[0, 0])
         qq = torch.zeros((1, wl.H, nb, 2, wl.d_h), dtype=torch.float32)
         qq[0, hs, ar] = qs.float()
-        oi, ow, osc, onext = oracle.address(qq, x["subkeys"], k, scoring="idw")
+        ohalf = oracle.half_scores(qq, x["subkeys"], scoring="idw")
+        oi, ow, osc, onext = oracle.select(ohalf, k)
         sel = (0, hs.numpy(), ar.numpy())
-        res = compare_slots(gsel, oi[sel], osc[sel], onext[sel])
+        res = compare_slots(gsel, oi[sel], osc[sel], onext[sel], ohalf[sel],
+                            label=f"idw {name} full size, {nb} sampled token-branches, {qn}")
         say(f"  {qn}: {res}")
         assert res["violating"] == 0

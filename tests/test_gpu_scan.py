@@ -11,7 +11,7 @@ import torch
 import oracle
 import sparse_memory_linear_amd as sdm
 from sparse_memory_linear_amd import inputs
-from parity import TOL_BF16, TOL_F32, compare_slots, max_rel_err, say
+from parity import TOL_BF16, TOL_F32, TOL_SAME_INPUTS, compare_slots, max_rel_err, say
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
@@ -27,10 +27,15 @@ def _run_gpu(idx_w, wt_w, idx_r, wt_r, alpha, beta, v, M_in, form):
     return M.cpu().numpy(), y.cpu().numpy()
 
 
-def _check(name, Mg, yg, Mo, yo, M_in, idx_w, tol):
+def _check(name, Mg, yg, Mo, yo, M_in, idx_w, tol, tight=None):
+    """tight: a second, smaller bound asserted where both sides scan identical
+    inputs (only fp32 rounding order differs); the result is reported against tol."""
     ey, em = max_rel_err(yg, yo), max_rel_err(Mg, Mo)
-    say(f"  {name}: max rel err y {ey:.2e}, M {em:.2e}")
+    say(f"  {name}: max rel err y {ey:.2e}, M {em:.2e} (tolerance {tol:g}"
+        + (f", asserted {tight:g})" if tight is not None else ")"))
     assert ey <= tol and em <= tol
+    if tight is not None:
+        assert ey <= tight and em <= tight
     # rows never selected for writing are bit-identical to the initial table
     M_in = np.asarray(M_in)
     iw = np.asarray(idx_w)
@@ -289,15 +294,20 @@ def test_state_init_broadcasts_M0():
     assert all(torch.equal(M[b], M0) for b in range(5))
 
 
-@pytest.mark.parametrize("name,streams", [("gdn_matched", [(0, 0), (3, 7)]), ("long_context", [(0, 5)])])
-def test_full_pipeline_full_size_sampled_streams(name, streams):
+FULL = [("gdn_matched", "eq4", [(0, 0), (1, 3), (2, 5), (3, 7)]), ("gdn_matched", "fig2", [(0, 2), (3, 6)]),
+        ("long_context", "eq4", [(0, 5), (0, 2)])]
+
+
+@pytest.mark.parametrize("name,form,streams", FULL, ids=[f"{n}-{f}" for n, f, _ in FULL])
+def test_full_pipeline_full_size_sampled_streams(name, form, streams):
     """The whole hot path at full size, in the benchmark's launch configuration
     (state init, addressing, scan). The sampled (b, h) streams take the oracle's
     own slots and weights (written over the GPU's before the scan), so both
     sides scan identical inputs that come from the oracle; those streams are
-    checked in full against the oracle scan."""
+    checked in full against the oracle scan, to the workload's tolerance and to
+    the fp32-rounding bound of identical inputs."""
     wl = inputs.get(name)
-    say(f"[pipeline full size] {name} B={wl.B} H={wl.H} T={wl.T} streams={streams}")
+    say(f"[pipeline full size] {name} {form} B={wl.B} H={wl.H} T={wl.T} streams={streams}")
     x = inputs.make_inputs(wl)
     g = {k: v.to(DEV) for k, v in x.items()}
     iw, ww, ir, wr = sdm.sdm_address(g["q_w"], g["q_r"], g["subkeys"], g["subkeys"], wl.W, wl.R)
@@ -310,15 +320,15 @@ def test_full_pipeline_full_size_sampled_streams(name, streams):
         for dst, src in ((iw, oi), (ww, ow), (ir, ri), (wr, rw)):
             dst[b, h] = torch.from_numpy(src[0, 0]).to(DEV)
     M = sdm.sdm_state_init(g["M0"], wl.B)
-    y = sdm.sdm_scan_forward(iw, ww, ir, wr, g["alpha"], g["beta"], g["v"], M, "eq4")
+    y = sdm.sdm_scan_forward(iw, ww, ir, wr, g["alpha"], g["beta"], g["v"], M, form)
     torch.cuda.synchronize()
     for (b, h) in streams:
         sl = lambda t: t[b:b + 1, h:h + 1].cpu()
         oi, ow, ri, rw = orc[(b, h)]
         Mo, yo = oracle.scan(oi, ow, ri, rw, sl(x["alpha"]), sl(x["beta"]), sl(x["v"]),
-                             x["M0"][h:h + 1][None].numpy(), oracle.EQ4)
+                             x["M0"][h:h + 1][None].numpy(), oracle.EQ4 if form == "eq4" else oracle.FIG2)
         _check(f"stream ({b},{h})", sl(M).numpy(), sl(y).numpy(), Mo, yo,
-               x["M0"][h:h + 1][None].numpy(), oi, TOL_BF16)
+               x["M0"][h:h + 1][None].numpy(), oi, TOL_BF16, TOL_SAME_INPUTS)
 
 
 @pytest.mark.parametrize("form,oform", FORMS, ids=["eq4", "fig2"])
@@ -332,13 +342,15 @@ def test_large_table_full_size(form, oform):
     x = inputs.make_inputs(wl)
     g = {k: v.to(DEV) for k, v in x.items()}
     iw, ww, ir, wr = sdm.sdm_address(g["q_w"], g["q_r"], g["subkeys"], g["subkeys"], wl.W, wl.R)
-    oiw, oww, osw, onw = oracle.address(x["q_w"], x["subkeys"], wl.W)
-    oir, owr, osr, onr = oracle.address(x["q_r"], x["subkeys"], wl.R)
-    for gi, oi, osc, onx in ((iw, oiw, osw, onw), (ir, oir, osr, onr)):
-        res = compare_slots(gi.cpu().numpy(), oi, osc, onx)
-        say(f"  slots: {res}")
-        assert res["violating"] == 0
+    hw, hr = oracle.half_scores(x["q_w"], x["subkeys"]), oracle.half_scores(x["q_r"], x["subkeys"])
+    oiw, oww, osw, onw = oracle.select(hw, wl.W)
+    oir, owr, osr, onr = oracle.select(hr, wl.R)
+    if form == "eq4":  # the addressing does not depend on the form: account for it once
+        for br, gi, oi, osc, onx, oh in (("write", iw, oiw, osw, onw, hw), ("read", ir, oir, osr, onr, hr)):
+            res = compare_slots(gi.cpu().numpy(), oi, osc, onx, oh, label=f"dot large_table full size {br}")
+            say(f"  slots: {res}")
+            assert res["violating"] == 0
     M_in = oracle.broadcast_state(x["M0"], wl.B)
     Mo, yo = oracle.scan(oiw, oww, oir, owr, x["alpha"], x["beta"], x["v"], M_in, oform)
     Mg, yg = _run_gpu(oiw, oww, oir, owr, x["alpha"], x["beta"], x["v"], M_in, form)
-    _check("large_table", Mg, yg, Mo, yo, M_in, oiw, TOL_F32)
+    _check("large_table", Mg, yg, Mo, yo, M_in, oiw, TOL_F32, TOL_SAME_INPUTS)
