@@ -59,6 +59,9 @@ def parse():
                         "per-head RMS-Norm and output gate")
     p.add_argument("--train", action="store_true",
                    help="training step: addressing, forward with pre-images, backward with undo")
+    p.add_argument("--no-extras", action="store_true",
+                   help="skip the extra entries of the default line (shared-residual scan, long-context scan "
+                        "and its slot-reuse statistics)")
     p.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                    help="run one plain device copy of BYTES bytes before the benchmark "
                         "(a known-size kernel that calibrates HBM byte counters)")
@@ -76,6 +79,57 @@ def host_cpu() -> str:
     return platform.processor() or "unknown"
 
 
+def host_facts() -> dict:
+    """What the host reports: nproc (the CPUs this process may use), os.cpu_count()
+    and the lscpu model name."""
+    try:
+        nproc = int(subprocess.run(["nproc"], capture_output=True, text=True).stdout.strip())
+    except Exception:
+        nproc = None
+    lscpu = {}
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True).stdout
+        for line in out.splitlines():
+            k, _, v = line.partition(":")
+            if k.strip() in ("Model name", "CPU family", "Model", "Thread(s) per core", "Core(s) per socket",
+                             "Socket(s)", "CPU max MHz", "L3 cache"):
+                lscpu[k.strip()] = v.strip()
+    except Exception:
+        pass
+    return {"nproc": nproc, "cpu_count": os.cpu_count(), "host_cpu": host_cpu(), "lscpu": lscpu}
+
+
+def pct(xs, q: float) -> float:
+    """q-th percentile (nearest rank) of a list of timings."""
+    xs = sorted(xs)
+    return xs[min(len(xs) - 1, max(0, int(round(q / 100.0 * (len(xs) - 1)))))]
+
+
+def stats(xs) -> dict:
+    return {"median": pct(xs, 50), "p10": pct(xs, 10), "p90": pct(xs, 90), "n": len(xs)}
+
+
+def slot_reuse(idx, N: int, window: int = 32768) -> dict:
+    """Slot-reuse statistics of one branch's slots idx [B, H, T, k] with FwPKM's
+    definitions (its ablation table: per 32K-token window, then averaged):
+    coverage = fraction of the N slots accessed; collision = fraction of the
+    accesses that land on a slot accessed more than once; KLD = KL divergence of
+    the access distribution from the uniform one (natural log)."""
+    import numpy as np
+    idx = idx.reshape(-1, idx.shape[-2], idx.shape[-1])  # [streams, T, k]
+    cov, col, kld = [], [], []
+    for st in range(idx.shape[0]):
+        for t0 in range(0, idx.shape[1], window):
+            c = np.bincount(idx[st, t0:t0 + window].reshape(-1).astype(np.int64), minlength=N)
+            n = c.sum()
+            p = c[c > 0] / n
+            cov.append((c > 0).mean())
+            col.append(c[c > 1].sum() / n)
+            kld.append(float((p * np.log(p * N)).sum()))
+    f = lambda v: {"mean": float(np.mean(v)), "min": float(np.min(v)), "max": float(np.max(v))}
+    return {"window_tokens": window, "windows": len(cov), "coverage": f(cov), "collision": f(col), "kld": f(kld)}
+
+
 def measured_traffic():
     """HBM bytes per scan launch from the committed counter summary, if it was
     taken on the current scan kernel source."""
@@ -89,7 +143,8 @@ def measured_traffic():
     return None
 
 
-def cpu_baseline(wl, x, target_s: float, scoring: str = "dot", table: str = "f32", gx=None):
+def cpu_baseline(wl, x, target_s: float, scoring: str = "dot", table: str = "f32", gx=None,
+                 single_s: float = 0.0):
     """The oracle as it is (addressing of both branches + scan) on a bounded
     sample of the same workload: the first B' sequences with all H heads, or
     the first T' tokens of one sequence when a whole one already exceeds the
@@ -128,12 +183,26 @@ def cpu_baseline(wl, x, target_s: float, scoring: str = "dot", table: str = "f32
     else:
         nb, Tp = min(wl.B, max(1, math.ceil(want / wl.T))), wl.T
     ts = run(nb, Tp) if (nb, Tp) != (1, T2) else t2
-    return {"value": nb * Tp / ts, "unit": "tokens/s", "cores": nthreads, "kind": "oracle",
-            "sample": f"{nb} of {wl.B} sequences of {wl.name}, all {wl.H} heads, first {Tp} of "
-                      f"{wl.T} tokens ({'gates + ' if gx is not None else ''}{scoring} addressing of both "
-                      f"branches + EQ4 scan, {table} table{' + output gate' if gx is not None else ''}), "
-                      f"{ts:.1f} s wall",
-            "host_cpu": host_cpu()}
+    rec = {"value": nb * Tp / ts, "unit": "tokens/s", "cores": nthreads, "kind": "oracle",
+           "sample": f"{nb} of {wl.B} sequences of {wl.name}, all {wl.H} heads, first {Tp} of "
+                     f"{wl.T} tokens ({'gates + ' if gx is not None else ''}{scoring} addressing of both "
+                     f"branches + EQ4 scan, {table} table{' + output gate' if gx is not None else ''}), "
+                     f"{ts:.1f} s wall",
+           "threads_note": "the pool takes the GPU box's CPU share for one GPU (16 threads), "
+                           "whatever nproc reports",
+           **host_facts()}
+    if single_s > 0:
+        # the same oracle on one thread, first T1 tokens of one sequence sized to ~single_s
+        nthreads_saved = nthreads
+        nthreads = 1
+        t1s = run(1, T1)
+        per1 = max(t1s / T1, 1e-6)
+        T1p = int(min(wl.T, max(T1, single_s / per1)))
+        t1p = run(1, T1p) if T1p != T1 else t1s
+        nthreads = nthreads_saved
+        rec["single_thread"] = {"value": T1p / t1p, "unit": "tokens/s", "cores": 1,
+                                "sample": f"1 sequence, all {wl.H} heads, first {T1p} tokens, {t1p:.1f} s wall"}
+    return rec
 
 
 def cpu_baseline_train(wl, x, dy, target_s: float, scoring: str = "dot"):
@@ -162,7 +231,7 @@ def cpu_baseline_train(wl, x, dy, target_s: float, scoring: str = "dot"):
     return {"value": Tp / ts, "unit": "tokens/s", "cores": nthreads, "kind": "oracle",
             "sample": f"1 of {wl.B} sequences of {wl.name}, all {wl.H} heads, first {Tp} of {wl.T} "
                       f"tokens ({scoring} addressing of both branches + EQ4 forward and backward), {ts:.1f} s wall",
-            "host_cpu": host_cpu()}
+            **host_facts()}
 
 
 def train_bench(a, wl, x, dev):
@@ -390,7 +459,8 @@ def main():
     ms_step = 1e3 * wall / a.steps
     init_ms = sum(m[0].elapsed_time(m[1]) for m in marks) / a.steps
     addr_ms = sum(m[4 if a.glue else 1].elapsed_time(m[2]) for m in marks) / a.steps
-    scan_ms = sum(m[2].elapsed_time(m[3]) for m in marks) / a.steps
+    scan_each = [m[2].elapsed_time(m[3]) for m in marks]
+    scan_ms = sum(scan_each) / a.steps
     breakdown = {"state_init": init_ms, "address": addr_ms, "scan": scan_ms}
     glue = None
     if a.glue:
@@ -429,6 +499,7 @@ def main():
         # the half-score contraction of both branches: 2 halves x n_sub x d_h MACs per token-branch
         "address_mfma_TFLOPs": 2 * B * H * T * 2 * (2 * wl.n_sub * wl.d_h) / (addr_ms * 1e-3) / 1e12,
         "scan_tokens_per_s": B * T / (scan_ms * 1e-3),
+        "scan_ms_per_step": stats(scan_each),
         "slot_row_GBps": scan_gbps,
         "roofline": {"bound": "hbm", "achieved": scan_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": scan_gbps / HBM_PEAK_GBPS,
@@ -442,10 +513,76 @@ def main():
     if glue:
         rec["glue"] = glue
         rec["config"]["mode"] = "layer (gates + addressing + scan + output gate)"
+    default_line = (wl.name, a.form, a.table, a.scoring, a.glue) == ("gdn_matched", "eq4", "f32", "dot", False)
+    if default_line and not a.no_extras:
+        # the shared-residual form on the same slots, then the long-context workload
+        rec["fig2_scan"] = scan_entry(sdm, g, M, y, ws, addr_out, "fig2", row_bytes, reps=7)
+        del g, M, y, ws, addr_out
+        torch.cuda.empty_cache()
+        rec["long_context_scan"] = long_context_entry(sdm, inputs, dev)
     if not a.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(wl, x, a.cpu_seconds, a.scoring, a.table,
-                                           inputs.make_glue_inputs(wl) if a.glue else None)
+                                           inputs.make_glue_inputs(wl) if a.glue else None,
+                                           single_s=8.0 if default_line else 0.0)
     print(json.dumps(rec), flush=True)
+
+
+def scan_entry(sdm, g, M, y, ws, addr_out, form: str, row_bytes: int, reps: int) -> dict:
+    """sdm_scan_forward on resident inputs: reps calls after one warm-up, each on a
+    fresh table from M0 (untimed), timed with HIP events on the current stream."""
+    import torch
+    iw, ww, ir, wr = addr_out
+    B = M.shape[0]
+    times = []
+    for i in range(reps + 1):
+        sdm.sdm_state_init(g["M0"], B, out=M)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        sdm.sdm_scan_forward(iw, ww, ir, wr, g["alpha"], g["beta"], g["v"], M, form, y=y, workspace=ws)
+        e1.record()
+        e1.synchronize()
+        if i:
+            times.append(e0.elapsed_time(e1))
+    st = stats(times)
+    gbps = row_bytes / (st["median"] * 1e-3) / 1e9
+    return {"form": form, "ms": st, "slot_row_GBps": gbps, "frac": gbps / HBM_PEAK_GBPS,
+            "algorithmic_bytes_per_launch": row_bytes}
+
+
+def long_context_entry(sdm, inputs, dev) -> dict:
+    """The long-context workload (B=1, H=8, T=131072, N=65536, W=R=64, d_v=128,
+    mixture keys, EQ4, fp32 table): addressing once, then the scan timed like the
+    default line's, and the slot-reuse statistics of both branches' slots."""
+    import torch
+    wl = inputs.get("long_context")
+    x = inputs.make_inputs(wl)
+    g = {k: v.to(dev) for k, v in x.items()}
+    del x
+    B, H, T, N, dv, W, R = wl.B, wl.H, wl.T, wl.N, wl.d_v, wl.W, wl.R
+    out = (torch.empty((B, H, T, W), dtype=torch.int32, device=dev),
+           torch.empty((B, H, T, W), dtype=torch.float32, device=dev),
+           torch.empty((B, H, T, R), dtype=torch.int32, device=dev),
+           torch.empty((B, H, T, R), dtype=torch.float32, device=dev))
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    sdm.sdm_address(g["q_w"], g["q_r"], g["subkeys"], g["subkeys"], W, R, out=out)
+    e0.record()
+    sdm.sdm_address(g["q_w"], g["q_r"], g["subkeys"], g["subkeys"], W, R, out=out)
+    e1.record()
+    e1.synchronize()
+    addr_ms = e0.elapsed_time(e1)
+    M = torch.empty((B, H, N, dv), dtype=torch.float32, device=dev)
+    y = torch.empty((B, H, T, dv), dtype=torch.float32, device=dev)
+    ws = torch.empty((sdm.sdm_scan_workspace_bytes(B, H, T, W, R, dv),), dtype=torch.uint8, device=dev)
+    row_bytes = B * H * T * (2 * W + R) * dv * 4
+    ent = scan_entry(sdm, g, M, y, ws, out, "eq4", row_bytes, reps=5)
+    ent.update({"workload": "long_context", "B": B, "H": H, "T": T, "N": N, "W": W, "R": R, "d_v": dv,
+                "keys": f"{wl.n_centroids}-centroid Gaussian mixture, sigma={wl.sigma}",
+                "scan_tokens_per_s": B * T / (ent["ms"]["median"] * 1e-3), "address_ms": addr_ms,
+                "slot_reuse": {"write": slot_reuse(out[0].cpu().numpy(), N),
+                               "read": slot_reuse(out[2].cpu().numpy(), N)}})
+    del g, M, y, ws, out
+    torch.cuda.empty_cache()
+    return ent
 
 
 if __name__ == "__main__":
