@@ -32,7 +32,7 @@
 extern "C" {
 #endif
 
-#define SDM_ABI_VERSION 5
+#define SDM_ABI_VERSION 6
 
 typedef enum sdm_status {
     SDM_OK = 0,
@@ -183,6 +183,32 @@ int sdm_scan_forward(const int32_t* idx_w, const float* wt_w, int64_t W,
                      void* M, int m_dtype, float* y,
                      int64_t B, int64_t H, int64_t T, int64_t N, int64_t dv,
                      int form, void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
+ * sdm_scan_forward_noalloc -- sdm_scan_forward without a workspace argument, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc). Arguments, layouts,
+ * results and support as sdm_scan_forward (the table and y are bit-identical
+ * to it), except:
+ *   - the scan's scratch (plan records, partial sums, counters) is one array of
+ *     64 MiB per GPU inside the library, held from the first call on that GPU
+ *     until the process ends; the call allocates and frees nothing;
+ *   - calls of more tokens than that scratch holds at once are run as several
+ *     launch chunks in order (the same result: the state carries over exactly);
+ *     a call whose streams need more than 64 MiB for even one token per launch
+ *     (B*H in the thousands) returns SDM_ERR_UNSUPPORTED;
+ *   - every call on a GPU uses that GPU's one array, so calls that overlap in
+ *     time on one GPU (on different streams or from different threads) race and
+ *     give unspecified results; calls on one stream are ordered and safe;
+ *   - `stream` selects the GPU (its device), else the current device.
+ */
+int sdm_scan_forward_noalloc(const int32_t* idx_w, const float* wt_w, int64_t W,
+                             const int32_t* idx_r, const float* wt_r, int64_t R,
+                             const float* alpha, const float* beta,
+                             const void* v, int v_dtype,
+                             void* M, int m_dtype, float* y,
+                             int64_t B, int64_t H, int64_t T, int64_t N, int64_t dv,
+                             int form, void* stream);
 
 /*
  * Training: the forward with pre-images, then the backward that undoes it.

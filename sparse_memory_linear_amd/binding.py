@@ -36,6 +36,8 @@ _SIGS = {
     "sdm_scan_workspace_bytes": (_I64, [_I64, _I64, _I64, _I64, _I64, _I64]),
     "sdm_scan_forward": (_I, [_P, _P, _I64, _P, _P, _I64, _P, _P, _P, _I, _P, _I, _P,
                               _I64, _I64, _I64, _I64, _I64, _I, _P, _I64, _P]),
+    "sdm_scan_forward_noalloc": (_I, [_P, _P, _I64, _P, _P, _I64, _P, _P, _P, _I, _P, _I, _P,
+                                      _I64, _I64, _I64, _I64, _I64, _I, _P]),
     "sdm_scan_snapshot_bytes": (_I64, [_I64, _I64, _I64, _I64, _I64]),
     "sdm_scan_forward_save": (_I, [_P, _P, _I64, _P, _P, _I64, _P, _P, _P, _I, _P, _P, _P,
                                    _I64, _I64, _I64, _I64, _I64, _I, _P, _I64, _P]),
@@ -256,6 +258,23 @@ def sdm_scan_forward(idx_w: torch.Tensor, wt_w: torch.Tensor, idx_r: torch.Tenso
         _ptr(idx_w), _ptr(wt_w), W, _ptr(idx_r), _ptr(wt_r), R, _ptr(alpha), _ptr(beta),
         _ptr(v), _dtype_code(v), _ptr(M), _dtype_code(M), _ptr(y), B, H, T, N, dv, FORMS[form],
         _ptr(workspace), workspace.numel(), _stream(d)))
+    return y
+
+
+def sdm_scan_forward_noalloc(idx_w: torch.Tensor, wt_w: torch.Tensor, idx_r: torch.Tensor,
+                             wt_r: torch.Tensor, alpha: torch.Tensor, beta: torch.Tensor,
+                             v: torch.Tensor, M: torch.Tensor, form: str = "eq4",
+                             y: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """sdm_scan_forward with the library's own per-GPU scratch instead of a
+    workspace (the C call allocates nothing; pass y to keep this binding from
+    allocating it). M is updated in place. Returns y [B,H,T,dv] fp32."""
+    d, (B, H, T, W, R, N, dv) = _scan_inputs("sdm_scan_forward_noalloc", idx_w, wt_w, idx_r, wt_r,
+                                             alpha, beta, v, M, (torch.float32, torch.bfloat16))
+    y = _f32_out(y, (B, H, T, dv), d, "y")
+    _check("sdm_scan_forward_noalloc", lib().sdm_scan_forward_noalloc(
+        _ptr(idx_w), _ptr(wt_w), W, _ptr(idx_r), _ptr(wt_r), R, _ptr(alpha), _ptr(beta),
+        _ptr(v), _dtype_code(v), _ptr(M), _dtype_code(M), _ptr(y), B, H, T, N, dv, FORMS[form],
+        _stream(d)))
     return y
 
 

@@ -1003,7 +1003,8 @@ hipError_t launch_scan_slab(const ScanArgs& a, const Cfg& c, hipStream_t st) {
     int TT = HT_WRITES / a.W - D;
     if (TT < 1) TT = 1;
     const bool save = a.snap != nullptr;
-    const int64_t Tc = chunk_tokens(a.T, g, a.dv, save ? a.W : 0);
+    int64_t Tc = chunk_tokens(a.T, g, a.dv, save ? a.W : 0);
+    if (a.max_tokens > 0 && Tc > a.max_tokens) Tc = a.max_tokens;
     const WsLayout wl = ws_layout(c, a.NS, Tc, a.dv);
     const int cpl = a.m_bf16 ? 8 : 4;
     const int nslab = a.dv / (SL / 4 * cpl);
@@ -1257,6 +1258,22 @@ int64_t scan_workspace_bytes(int64_t NS, int64_t T, int W, int R, int dv) {
 int64_t direct_max_tokens() {
     const char* e = getenv("SDM_SCAN_DIRECT_T");
     return e ? atoll(e) : 8;
+}
+
+int64_t scan_tokens_within(int64_t NS, int64_t T, int W, int R, int dv, bool m_bf16, int form, int64_t bytes) {
+    if (T <= direct_max_tokens()) return T;  // the short-call form needs no workspace
+    const Cfg c = choose_cfg(NS, W, R, dv, form, m_bf16 ? 8 : 4);
+    if (c.S == 0) return 0;
+    const int64_t cap = chunk_tokens(T, c.g, dv);
+    auto fits = [&](int64_t tc) { return ws_layout(c, NS, tc, dv).total <= bytes; };
+    if (!fits(1)) return 0;
+    int64_t lo = 1, hi = cap;  // fits(lo); the answer lies in [lo, hi]
+    while (lo < hi) {
+        const int64_t mid = lo + (hi - lo + 1) / 2;
+        if (fits(mid)) lo = mid;
+        else hi = mid - 1;
+    }
+    return lo;
 }
 
 hipError_t launch_scan(const ScanArgs& a, hipStream_t st) {

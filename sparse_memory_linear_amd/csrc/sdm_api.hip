@@ -6,6 +6,7 @@
 #include <string.h>
 
 #include <initializer_list>
+#include <mutex>
 
 #include "sdm.h"
 #include "sdm_internal.h"
@@ -278,6 +279,80 @@ int sdm_scan_forward(const int32_t* idx_w, const float* wt_w, int64_t W, const i
                      void* workspace, int64_t workspace_bytes, void* stream) {
     return scan_forward_impl("sdm_scan_forward", idx_w, wt_w, W, idx_r, wt_r, R, alpha, beta, v, v_dtype, M,
                              m_dtype, y, nullptr, false, B, H, T, N, dv, form, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+// The scan's scratch (plan records, partial y, counters) for callers that cannot
+// allocate: one array per GPU, kept until the process ends. Host code uses its
+// device address from hipGetSymbolAddress, taken once per device.
+constexpr int64_t SCRATCH_BYTES = 64ll << 20;
+__device__ __align__(256) unsigned char scratch[SCRATCH_BYTES];
+
+constexpr int MAX_DEVICES = 64;
+std::once_flag g_scratch_once[MAX_DEVICES];
+void* g_scratch_ptr[MAX_DEVICES];
+hipError_t g_scratch_err[MAX_DEVICES];
+
+// Device address of this GPU's scratch array (nullptr and the error on failure).
+void* scratch_of(int dev, hipError_t* err) {
+    std::call_once(g_scratch_once[dev], [dev] {
+        int cur = 0;
+        hipError_t e = hipGetDevice(&cur);
+        if (e == hipSuccess && cur != dev) e = hipSetDevice(dev);
+        void* p = nullptr;
+        if (e == hipSuccess) e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (cur != dev) (void)hipSetDevice(cur);
+        g_scratch_err[dev] = e;
+        g_scratch_ptr[dev] = e == hipSuccess ? p : nullptr;
+    });
+    *err = g_scratch_err[dev];
+    return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+int sdm_scan_forward_noalloc(const int32_t* idx_w, const float* wt_w, int64_t W, const int32_t* idx_r,
+                             const float* wt_r, int64_t R, const float* alpha, const float* beta, const void* v,
+                             int v_dtype, void* M, int m_dtype, float* y, int64_t B, int64_t H, int64_t T,
+                             int64_t N, int64_t dv, int form, void* stream) {
+    const char* fn = "sdm_scan_forward_noalloc";
+    int rc = check_scan(fn, idx_w, wt_w, W, idx_r, wt_r, R, alpha, beta, v, v_dtype, B, H, T, N, dv, form,
+                        m_dtype);
+    if (rc == NO_WORK) return ok();
+    if (rc) return rc;
+    if ((rc = check_buffers(fn, {M, y}))) return rc;
+    const int64_t tc = sdm::scan_tokens_within(B * H, T, (int)W, (int)R, (int)dv, m_dtype == SDM_BF16, form,
+                                               SCRATCH_BYTES);
+    if (tc < 1)
+        return fail(SDM_ERR_UNSUPPORTED,
+                    "%s: B*H=%lld streams need more than the %lld-byte scratch for even one token per launch",
+                    fn, (long long)(B * H), (long long)SCRATCH_BYTES);
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess && stream) e = hipStreamGetDevice(static_cast<hipStream_t>(stream), &dev);
+    if (e != hipSuccess) return hip_fail(e, fn);
+    if (dev < 0 || dev >= MAX_DEVICES) return fail(SDM_ERR_UNSUPPORTED, "%s: device %d out of range", fn, dev);
+    void* ws = scratch_of(dev, &e);
+    if (!ws) return hip_fail(e, "sdm_scan_forward_noalloc (scratch address)");
+    sdm::ScanArgs a{};
+    a.idx_w = idx_w; a.wt_w = wt_w; a.W = (int)W;
+    a.idx_r = idx_r; a.wt_r = wt_r; a.R = (int)R;
+    a.alpha = alpha; a.beta = beta;
+    a.v = v; a.v_bf16 = v_dtype == SDM_BF16;
+    a.M = M; a.m_bf16 = m_dtype == SDM_BF16; a.y = y;
+    a.NS = B * H; a.T = T; a.N = N; a.dv = (int)dv;
+    a.form = form;
+    a.workspace = ws;
+    a.snap = nullptr;
+    a.max_tokens = tc;
+    e = sdm::launch_scan(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, fn);
+    return ok();
 }
 
 int64_t sdm_scan_snapshot_bytes(int64_t B, int64_t H, int64_t T, int64_t W, int64_t dv) {

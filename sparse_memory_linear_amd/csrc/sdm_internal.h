@@ -35,10 +35,15 @@ struct ScanArgs {
     int form;                // 0 = per-slot Eq. (4), 1 = Fig. 2 shared residual
     void* workspace;
     float* snap;             // optional [NS][T][W][dv]: pre-image of every write (training forward)
+    int64_t max_tokens = 0;  // > 0: tokens per launch chunk at most this (a bounded workspace)
 };
 // Chooses the kernel instance; returns false if no instance covers (W, R, dv).
 bool scan_geometry(int64_t NS, int W, int R, int dv, bool m_bf16, int* slab, int* rec_bytes);
 int64_t scan_workspace_bytes(int64_t NS, int64_t T, int W, int R, int dv);
+// The most tokens per launch chunk (at most T) whose workspace fits in `bytes`
+// for this table dtype and form; T itself when the call takes the short-call
+// form (no workspace); 0 when not even one token fits.
+int64_t scan_tokens_within(int64_t NS, int64_t T, int W, int R, int dv, bool m_bf16, int form, int64_t bytes);
 hipError_t launch_scan(const ScanArgs& a, hipStream_t st);
 
 struct BwdArgs {

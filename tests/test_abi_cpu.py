@@ -32,7 +32,7 @@ def test_header_declares_the_hot_path_calls():
               "sdm_scan_workspace_bytes", "sdm_status_string", "sdm_last_error", "sdm_abi_version",
               "sdm_scan_forward_save", "sdm_scan_snapshot_bytes", "sdm_scan_backward",
               "sdm_scan_backward_workspace_bytes", "sdm_state_init_backward", "sdm_address_idw",
-              "sdm_debug_half_scores_idw", "sdm_gates", "sdm_output_gate"):
+              "sdm_debug_half_scores_idw", "sdm_gates", "sdm_output_gate", "sdm_scan_forward_noalloc"):
         assert f in names
 
 
@@ -43,7 +43,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert binding.sdm_abi_version() == 5
+    assert binding.sdm_abi_version() == 6
     assert binding.sdm_status_string(0) == "ok"
     assert binding.sdm_status_string(7).startswith("workspace")
     assert binding.sdm_status_string(99) == "unknown status"
@@ -208,3 +208,20 @@ def test_glue_calls_reject_bad_arguments_before_launch(lib):
     assert og(eps=-1.0) == 2
     assert og(B=1 << 12, H=1 << 10, T=1 << 10) == 5   # 2^32 rows
     assert "2^32" in binding.sdm_last_error()
+
+
+def test_noalloc_scan_rejects_bad_arguments_before_launch(lib):
+    """The scan entry point without a workspace validates like sdm_scan_forward
+    and rejects stream counts whose scan needs more than its 64 MiB scratch for
+    a single token per launch, all before any HIP call."""
+    fake = P(4096)
+    base = dict(iw=fake, ww=fake, W=64, ir=fake, wr=fake, R=64, a=fake, b=fake, v=fake, vd=1,
+                M=fake, md=0, y=fake, B=1, H=1, T=100, N=4096, dv=128, form=0, st=None)
+    call = lambda **kw: lib.sdm_scan_forward_noalloc(*dict(base, **kw).values())
+    assert call(iw=None) == 1
+    assert call(iw=None, ww=None, M=None, T=0) == 0                     # empty: valid no-op
+    assert call(form=2) == 3
+    assert call(y=P(4104)) == 4
+    # 65536 streams: one token's plan records alone take 65536 x 1536 bytes
+    assert call(B=65536) == 5
+    assert "scratch" in binding.sdm_last_error()
