@@ -17,7 +17,10 @@ from typing import Optional, Tuple
 import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "liboracle_sdm.so")
+# SDM_ORACLE_SANITIZE=1 loads a build with AddressSanitizer and UBSan instead
+# (the process must then preload the ASan runtime, see tests/test_oracle_sanitized.py)
+SANITIZE = os.environ.get("SDM_ORACLE_SANITIZE") == "1"
+LIB_PATH = os.path.join(HERE, "liboracle_sdm_san.so" if SANITIZE else "liboracle_sdm.so")
 SRC = os.path.join(HERE, "oracle_sdm.c")
 
 EQ4 = 0
@@ -27,10 +30,14 @@ _lib = None
 
 
 def build(force: bool = True) -> str:
-    """Compile liboracle_sdm.so with gcc (no fast-math, no FMA contraction)."""
+    """Compile liboracle_sdm.so with gcc (no fast-math, no FMA contraction), or
+    with SDM_ORACLE_SANITIZE=1 the same source with AddressSanitizer and
+    UndefinedBehaviorSanitizer (every UB report aborts) into liboracle_sdm_san.so."""
     if force or not os.path.exists(LIB_PATH):
         tmp = LIB_PATH + ".tmp"
-        cmd = ["gcc", "-O2", "-std=c11", "-Wall", "-ffp-contract=off", "-fno-fast-math",
+        san = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer", "-g"] \
+            if SANITIZE else []
+        cmd = ["gcc", "-O2", "-std=c11", "-Wall", "-ffp-contract=off", "-fno-fast-math", *san,
                "-fPIC", "-shared", "-pthread", SRC, "-o", tmp, "-lm"]
         subprocess.run(cmd, check=True)
         os.replace(tmp, LIB_PATH)
