@@ -965,26 +965,39 @@ WsLayout ws_layout(const Cfg& c, int64_t NS, int64_t Tc, int dv) {
 }
 
 // One instance of the token-loop kernel per (slab, form, v dtype, pre-image
-// stores, table dtype); pre-images are taken only of fp32 tables.
+// stores, table dtype); pre-images are taken only of fp32 tables, and a bf16
+// table never takes SL = 32 slabs in the loop (slab_fits), so neither has an
+// instance.
 template <int SL>
-void launch_scan_inst(int form, bool vb, bool save, bool mb, dim3 grid, dim3 block, size_t lds, hipStream_t st,
-                      const ScanKArgs& k) {
+hipError_t launch_scan_inst(int form, bool vb, bool save, bool mb, dim3 grid, dim3 block, size_t lds,
+                            hipStream_t st, const ScanKArgs& k) {
     const int sel = (form ? 8 : 0) | (vb ? 4 : 0) | (save ? 2 : 0) | (mb ? 1 : 0);
+    if constexpr (SL == 32) {
+        if (mb) return hipErrorInvalidValue;
+    }
     switch (sel) {
         case 0: hipLaunchKernelGGL((scan_kernel<SL, 0, false, false, false>), grid, block, lds, st, k); break;
-        case 1: hipLaunchKernelGGL((scan_kernel<SL, 0, false, false, true>), grid, block, lds, st, k); break;
         case 2: hipLaunchKernelGGL((scan_kernel<SL, 0, false, true, false>), grid, block, lds, st, k); break;
         case 4: hipLaunchKernelGGL((scan_kernel<SL, 0, true, false, false>), grid, block, lds, st, k); break;
-        case 5: hipLaunchKernelGGL((scan_kernel<SL, 0, true, false, true>), grid, block, lds, st, k); break;
         case 6: hipLaunchKernelGGL((scan_kernel<SL, 0, true, true, false>), grid, block, lds, st, k); break;
         case 8: hipLaunchKernelGGL((scan_kernel<SL, 1, false, false, false>), grid, block, lds, st, k); break;
-        case 9: hipLaunchKernelGGL((scan_kernel<SL, 1, false, false, true>), grid, block, lds, st, k); break;
         case 10: hipLaunchKernelGGL((scan_kernel<SL, 1, false, true, false>), grid, block, lds, st, k); break;
         case 12: hipLaunchKernelGGL((scan_kernel<SL, 1, true, false, false>), grid, block, lds, st, k); break;
-        case 13: hipLaunchKernelGGL((scan_kernel<SL, 1, true, false, true>), grid, block, lds, st, k); break;
         case 14: hipLaunchKernelGGL((scan_kernel<SL, 1, true, true, false>), grid, block, lds, st, k); break;
-        default: break;  // pre-images of a bf16 table: rejected by the C ABI before any launch
+        default:
+            if constexpr (SL != 32) {
+                switch (sel) {
+                    case 1: hipLaunchKernelGGL((scan_kernel<SL, 0, false, false, true>), grid, block, lds, st, k); break;
+                    case 5: hipLaunchKernelGGL((scan_kernel<SL, 0, true, false, true>), grid, block, lds, st, k); break;
+                    case 9: hipLaunchKernelGGL((scan_kernel<SL, 1, false, false, true>), grid, block, lds, st, k); break;
+                    case 13: hipLaunchKernelGGL((scan_kernel<SL, 1, true, false, true>), grid, block, lds, st, k); break;
+                    default: return hipErrorInvalidValue;  // pre-images of a bf16 table: rejected by the C ABI
+                }
+            } else {
+                return hipErrorInvalidValue;
+            }
     }
+    return hipSuccess;
 }
 
 template <int SL>
@@ -1057,8 +1070,8 @@ hipError_t launch_scan_slab(const ScanArgs& a, const Cfg& c, hipStream_t st) {
         // readers' partial sums and stores y
         const int xw = (a.form == 0 && g.NWR == 1 && g.nw() < SlabCfg<SL>::NWMAX && g.NWR < nrmax<SL>()) ? 1 : 0;
         dim3 grid((unsigned)nblk), block((unsigned)((g.nw() + xw) * 64));
-        launch_scan_inst<SL>(a.form, a.v_bf16, save, a.m_bf16, grid, block, lds, st, k);
-        e = hipGetLastError();
+        e = launch_scan_inst<SL>(a.form, a.v_bf16, save, a.m_bf16, grid, block, lds, st, k);
+        if (e == hipSuccess) e = hipGetLastError();
         if (e != hipSuccess) return e;
         if (c.P > 1) {
             const int64_t n4 = a.NS * Tn * (a.dv / 4);
@@ -1121,8 +1134,13 @@ size_t slab_lds(int S, const Geom& g, int cpl) {
 }
 constexpr size_t LDS_MAX = 160 * 1024;  // per workgroup on gfx950
 
-bool slab_fits(int S, int W, int R, int dv, int cpl) {
+// The token loop does not take a bf16 table in SL = 32 slabs (64 columns): with
+// its two float4 of widened values per row it needs more than the 128 VGPRs of
+// a 16-wavefront workgroup and spills; such tables take narrower slabs there.
+// The direct form (loop = false) keeps them.
+bool slab_fits(int S, int W, int R, int dv, int cpl, bool loop = true) {
     if (dv % (S / 4 * cpl) != 0) return false;
+    if (loop && S == 32 && cpl == 8) return false;
     const Geom g = make_geom(S, W, R);
     return g.nw() <= slab_nwmax(S) && g.NWR <= slab_nrmax(S) && slab_lds(S, g, cpl) <= LDS_MAX;
 }
@@ -1140,12 +1158,12 @@ int env_int(const char* name) {
 // Failing that, the width with the most workgroups, then the one with the least
 // padding. (Measured on the N=65536, W=R=64, d_v=128 shapes: fp32, 32 streams
 // -> 16 columns, 8 streams -> 8; bf16, 32 streams -> 16 columns (SL = 8).)
-int pick_slab(int64_t NS, int W, int R, int dv, int cpl, int forced) {
+int pick_slab(int64_t NS, int W, int R, int dv, int cpl, int forced, bool loop = true) {
     const long enough = cpl == 8 ? 256 : 128;
     // fp32 table, few streams: the 8-wavefront 16-column layout and its deeper
     // prefetch (one stream, W = R = 8, d_v = 512, shared-residual form: 19.8 ms
     // against 35.3 for 32-column slabs)
-    if (!forced && cpl == 4 && (long)NS * (dv / 32) < enough && slab_fits(16, W, R, dv, cpl)) return 16;
+    if (!forced && cpl == 4 && (long)NS * (dv / 32) < enough && slab_fits(16, W, R, dv, cpl, loop)) return 16;
     struct Cand {
         int S;
         long waste, units;
@@ -1162,7 +1180,7 @@ int pick_slab(int64_t NS, int W, int R, int dv, int cpl, int forced) {
     };
     Cand best{0, 0, 0, 0};
     for (int S : {32, 16, 8, 4}) {
-        if ((forced && forced != S) || !slab_fits(S, W, R, dv, cpl)) continue;
+        if ((forced && forced != S) || !slab_fits(S, W, R, dv, cpl, loop)) continue;
         const Geom g = make_geom(S, W, R);
         const Cand c{S, (long)g.NWW * g.G - W + (long)g.NWR * g.G - R, (long)NS * (dv / (S / 4 * cpl)), g.nw()};
         if (best.S == 0 || better(c, best)) best = c;
@@ -1280,7 +1298,7 @@ hipError_t launch_scan(const ScanArgs& a, hipStream_t st) {
     const int cpl = a.m_bf16 ? 8 : 4;
     const int64_t per_tok = (int64_t)a.dv * 4 * (a.snap ? (a.W > 1 ? a.W : 1) : 1);
     if (a.T <= direct_max_tokens() && a.T * per_tok < 0x7FFFFFFF) {
-        switch (pick_slab(a.NS, a.W, a.R, a.dv, cpl, env_int("SDM_SCAN_SLAB"))) {
+        switch (pick_slab(a.NS, a.W, a.R, a.dv, cpl, env_int("SDM_SCAN_SLAB"), false)) {
             case 32: return launch_scan_direct<32>(a, st);
             case 16: return launch_scan_direct<16>(a, st);
             case 8: return launch_scan_direct<8>(a, st);

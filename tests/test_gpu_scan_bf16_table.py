@@ -105,7 +105,16 @@ def test_bf16_table_hazard_stress(case, form, oform):
     _check("hazard", Mg, yg, Mo, yo, c["M_in"], c["idx_w"], min_same=0.98)
 
 
-SWEEP = [(32, 1), (32, 2), (32, 4), (32, 8), (16, 2), (16, 8), (8, 4), (4, 8)]
+# SL = 32 (64 bf16 columns) is not a width of the token loop for a bf16 table
+# (it would spill registers); forcing it is rejected before any launch.
+SWEEP = [(16, 1), (16, 2), (16, 4), (16, 8), (8, 2), (8, 4), (8, 8), (4, 8)]
+
+
+def test_bf16_table_rejects_forced_64_column_slabs(monkeypatch):
+    monkeypatch.setenv("SDM_SCAN_SLAB", "32")
+    c = _random_case(7, **HAZARD[0])
+    with pytest.raises(RuntimeError):
+        _run_gpu(**c, form="eq4")
 
 
 @pytest.mark.parametrize("slab,parts", SWEEP, ids=[f"SL{s}P{p}" for s, p in SWEEP])
