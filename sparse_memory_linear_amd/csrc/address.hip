@@ -71,8 +71,9 @@ __device__ __forceinline__ int lanes_below(uint64_t m) {
                                           __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
-// Value of lane (lane ^ M), without LDS: DPP quad permutes (1, 2), DPP row
-// shifts (4), DPP row rotate (8), gfx950 permlane swaps (16, 32).
+// Value of lane (lane ^ M), without LDS: DPP quad permutes (1, 2), DPP
+// half-row mirror + quad permute (4), DPP row rotate (8), gfx950 permlane
+// swaps (16, 32).
 template <int M>
 __device__ __forceinline__ uint32_t xlane(uint32_t x, int lane) {
     if constexpr (M == 1) {
@@ -80,9 +81,9 @@ __device__ __forceinline__ uint32_t xlane(uint32_t x, int lane) {
     } else if constexpr (M == 2) {
         return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x4E, 0xF, 0xF, false);  // quad_perm 2,3,0,1
     } else if constexpr (M == 4) {
-        const uint32_t up = (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x104, 0xF, 0xF, false);  // row_shl:4
-        const uint32_t dn = (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x114, 0xF, 0xF, false);  // row_shr:4
-        return (lane & 4) ? dn : up;
+        // lane ^ 4 = (lane ^ 7) ^ 3: row_half_mirror, then quad_perm 3,2,1,0
+        const int m = __builtin_amdgcn_mov_dpp((int)x, 0x141, 0xF, 0xF, false);
+        return (uint32_t)__builtin_amdgcn_mov_dpp(m, 0x1B, 0xF, 0xF, false);
     } else if constexpr (M == 8) {
         return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x128, 0xF, 0xF, false);  // row_ror:8
     } else if constexpr (M == 16) {
@@ -114,116 +115,159 @@ __device__ __forceinline__ float wave_sum(float v, int lane) {
     return v;  // the butterfly adds the same pairs on every lane: identical on all lanes
 }
 
+// Select output rows: OSTR words per token-chain; a winner goes to one of the
+// first k words, every other lane stores to word OSTR / 2 + lane (unused), so
+// the compaction stores need no lane mask.
+constexpr int OSTR = 128;
+
+// f(e) for e < NCH (compile-time, unrolled) or e < nch (run time).
+template <int NCH, typename F>
+__device__ __forceinline__ void for_chunks(int nch, F f) {
+    if constexpr (NCH > 0) {
+#pragma unroll
+        for (int e = 0; e < NCH; ++e) f(e);
+    } else {
+        for (int e = 0; e < nch; ++e) f(e);
+    }
+}
+
 // Select, for each of the NT token-chains g, the k best candidates (larger key
 // first, then smaller id) among candidates c = e*64 + lane, e < nch, read
 // through get(g, e, key, id). Key 0 marks an absent candidate; ids are below
 // 2^18. Exactly k winners (k <= number of present candidates) are written in
-// candidate order to okey/oid[g*64 + 0..k).
+// candidate order to okey/oid[g*OSTR + 0..k).
 template <int NT, int NCH, typename Get>
 __device__ __forceinline__ void wave_select(Get get, int nch_rt, int k, uint32_t* okey, uint32_t* oid,
                                             int lane) {
-    const int nch = NCH > 0 ? NCH : nch_rt;
     // Radix select of the k-th largest key, most significant bit first: tau
-    // keeps the bits fixed so far with count(key >= tau) >= k. As soon as some
-    // prefix has exactly k keys at or above it, the winners are known and the
-    // lower bits cannot change them, so a token stops there (the loop ends when
-    // every token has); with distinct keys that happens once the prefix
-    // separates the k-th from the (k+1)-th key, after about half the bits.
+    // keeps the bits fixed so far, cur = count(key >= tau) >= k. A bit is taken
+    // when the count at tau with the bit set still reaches k. Once cur == k the
+    // winners are the keys at or above tau, and taking further bits keeps
+    // exactly those k keys at or above it (a bit is only taken while the count
+    // stays >= k, and it cannot exceed cur), so a finished token needs no
+    // branch of its own; the loop ends when every token has cur == k (with
+    // distinct keys, once the prefix separates the k-th from the (k+1)-th key).
     uint32_t tau[NT];
-    bool done[NT];
+    int cur[NT];
 #pragma unroll
     for (int g = 0; g < NT; ++g) {
         tau[g] = 0u;
-        done[g] = false;
+        cur[g] = -1;  // unknown, >= k
     }
-    for (int bit = 31; bit >= 0; --bit) {
+    for (uint32_t b = 0x80000000u; b != 0u; b >>= 1) {
         int cnt[NT];
+        uint32_t t[NT];
 #pragma unroll
-        for (int g = 0; g < NT; ++g) cnt[g] = 0;
-#pragma unroll
-        for (int e = 0; e < nch; ++e) {
+        for (int g = 0; g < NT; ++g) {
+            cnt[g] = 0;
+            t[g] = tau[g] | b;
+        }
+        for_chunks<NCH>(nch_rt, [&](int e) {
 #pragma unroll
             for (int g = 0; g < NT; ++g) {
                 uint32_t kk, ii;
                 get(g, e, kk, ii);
-                cnt[g] += popc(__ballot(kk >= (tau[g] | (1u << bit))));
+                cnt[g] += popc(__ballot(kk >= t[g]));
             }
-        }
-        bool all = true;
+        });
+        uint32_t left = 0u;
 #pragma unroll
         for (int g = 0; g < NT; ++g) {
-            if (!done[g] && cnt[g] >= k) {
-                tau[g] |= 1u << bit;
-                done[g] = cnt[g] == k;
+            const bool take = cnt[g] >= k;
+            tau[g] = take ? t[g] : tau[g];
+            cur[g] = take ? cnt[g] : cur[g];
+            left |= (uint32_t)(cur[g] ^ k);
+        }
+        if (left == 0u) break;
+    }
+    uint32_t open = 0u;
+#pragma unroll
+    for (int g = 0; g < NT; ++g) open |= (cur[g] != k ? 1u : 0u) << g;
+    // compaction: the winners are the keys at or above tau (with cut: of the
+    // keys equal to tau, those whose inverted id reaches sig)
+    auto compact = [&](const uint32_t (&th)[NT], uint32_t cutm, const uint32_t (&sig)[NT]) {
+#pragma unroll
+        for (int g = 0; g < NT; ++g) {
+            const bool cut = (cutm >> g) & 1u;
+            int base = 0;
+            for_chunks<NCH>(nch_rt, [&](int e) {
+                uint32_t kk, ii;
+                get(g, e, kk, ii);
+                const bool sel = kk > th[g] || (kk == th[g] && (!cut || (0x3FFFFu - ii) >= sig[g]));
+                const uint64_t m = __ballot(sel);
+                const int pos = sel ? base + lanes_below(m) : OSTR / 2 + lane;
+                okey[g * OSTR + pos] = kk;
+                oid[g * OSTR + pos] = ii;
+                base += popc(m);
+            });
+        }
+    };
+    if (open != 0u) {
+        // Rare: a token went through bit 0, so its tau is the k-th key itself,
+        // and more keys may equal it than places are left (exact ties): those
+        // keep the lowest ids, by a second radix pass over the inverted id.
+        // The thresholds pass through readfirstlane (a no-op on a uniform
+        // value) so that none of this path's compares is hoisted into the
+        // common one.
+        uint32_t th[NT], sig[NT], cutm = 0u;
+        int need[NT];
+#pragma unroll
+        for (int g = 0; g < NT; ++g) {
+            th[g] = (uint32_t)__builtin_amdgcn_readfirstlane((int)tau[g]);
+            sig[g] = 0u;
+            int gt = 0;
+            for_chunks<NCH>(nch_rt, [&](int e) {
+                uint32_t kk, ii;
+                get(g, e, kk, ii);
+                gt += popc(__ballot(kk > th[g]));
+            });
+            need[g] = k - gt;
+            // cur = count(key >= tau), so cur - gt keys equal tau
+            if (((open >> g) & 1u) && cur[g] - gt > need[g]) cutm |= 1u << g;
+        }
+        if (cutm != 0u) {
+            for (int bit = 17; bit >= 0; --bit) {
+                int cnt[NT];
+#pragma unroll
+                for (int g = 0; g < NT; ++g) cnt[g] = 0;
+                for_chunks<NCH>(nch_rt, [&](int e) {
+#pragma unroll
+                    for (int g = 0; g < NT; ++g) {
+                        uint32_t kk, ii;
+                        get(g, e, kk, ii);
+                        cnt[g] += popc(__ballot(kk == th[g] && (0x3FFFFu - ii) >= (sig[g] | (1u << bit))));
+                    }
+                });
+#pragma unroll
+                for (int g = 0; g < NT; ++g)
+                    if (cnt[g] >= need[g]) sig[g] |= 1u << bit;
             }
-            all = all && done[g];
         }
-        if (all) break;
+        compact(th, cutm, sig);
+        return;
     }
-    int need[NT];
-    bool cut[NT], any_cut = false;
-#pragma unroll
-    for (int g = 0; g < NT; ++g) {
-        int gt = 0, eq = 0;
-#pragma unroll
-        for (int e = 0; e < nch; ++e) {
-            uint32_t kk, ii;
-            get(g, e, kk, ii);
-            gt += popc(__ballot(kk > tau[g]));
-            eq += popc(__ballot(kk == tau[g]));
-        }
-        need[g] = k - gt;
-        cut[g] = eq > need[g];  // more ties at the threshold than places left
-        any_cut |= cut[g];
-    }
-    uint32_t sig[NT];
-#pragma unroll
-    for (int g = 0; g < NT; ++g) sig[g] = 0u;
-    if (any_cut) {  // rare: exact ties at the threshold; keep the lowest ids
-        for (int bit = 17; bit >= 0; --bit) {
-            int cnt[NT];
-#pragma unroll
-            for (int g = 0; g < NT; ++g) cnt[g] = 0;
-#pragma unroll
-            for (int e = 0; e < nch; ++e) {
-#pragma unroll
-                for (int g = 0; g < NT; ++g) {
-                    uint32_t kk, ii;
-                    get(g, e, kk, ii);
-                    cnt[g] += popc(__ballot(kk == tau[g] && (0x3FFFFu - ii) >= (sig[g] | (1u << bit))));
-                }
-            }
-#pragma unroll
-            for (int g = 0; g < NT; ++g)
-                if (cnt[g] >= need[g]) sig[g] |= 1u << bit;
-        }
-    }
-#pragma unroll
-    for (int g = 0; g < NT; ++g) {
-        int base = 0;
-#pragma unroll
-        for (int e = 0; e < nch; ++e) {
-            uint32_t kk, ii;
-            get(g, e, kk, ii);
-            const bool sel = kk > tau[g] || (kk == tau[g] && (!cut[g] || (0x3FFFFu - ii) >= sig[g]));
-            const uint64_t m = __ballot(sel);
-            if (sel) {
-                const int pos = base + lanes_below(m);
-                okey[g * 64 + pos] = kk;
-                oid[g * 64 + pos] = ii;
-            }
-            base += popc(m);
-        }
-    }
+    const uint32_t nosig[NT] = {};
+    compact(tau, 0u, nosig);
 }
 
-template <int J, int NT>
-__device__ __forceinline__ void sort_stage(uint64_t (&x)[NT], int lane, int k) {
+// Lanes of a bitonic stage (partner distance J, merge size K) that keep the
+// smaller of the pair: bit l of the mask. A compile-time constant, so each
+// stage applies it to the compare mask with two scalar XORs on literals.
+template <int J, int K>
+constexpr uint64_t keep_min_lanes() {
+    uint64_t m = 0;
+    for (int l = 0; l < 64; ++l)
+        if (((l & J) == 0) != ((l & K) == 0)) m |= 1ull << l;
+    return m;
+}
+
+template <int J, int K, int NT>
+__device__ __forceinline__ void sort_stage(uint64_t (&x)[NT], int lane) {
+    constexpr uint64_t KMIN = keep_min_lanes<J, K>();
 #pragma unroll
     for (int g = 0; g < NT; ++g) {
         // keep the larger of (x, partner) where the lane keeps the maximum, the
-        // smaller elsewhere: one compare, one mask operation, one select
-        const bool keep_max = (((lane & J) == 0) == ((lane & k) == 0));
+        // smaller elsewhere: one compare, one scalar mask operation, one select
         if constexpr (J >= 16) {
             // a permlane swap of (v, v) returns {v, partner's v} in an order that
             // depends only on the lane half, the same order for both words; max
@@ -240,10 +284,12 @@ __device__ __forceinline__ void sort_stage(uint64_t (&x)[NT], int lane, int k) {
                 l0 = pl[0]; l1 = pl[1]; h0 = ph[0]; h1 = ph[1];
             }
             const uint64_t a0 = ((uint64_t)h0 << 32) | l0, a1 = ((uint64_t)h1 << 32) | l1;
-            x[g] = ((a0 > a1) == keep_max) ? a0 : a1;
+            const bool take0 = __builtin_amdgcn_inverse_ballot_w64(__ballot(a0 > a1) ^ KMIN);
+            x[g] = take0 ? a0 : a1;
         } else {
             const uint64_t o = xlane64<J>(x[g], lane);
-            x[g] = ((x[g] > o) == keep_max) ? x[g] : o;
+            const bool keep = __builtin_amdgcn_inverse_ballot_w64(__ballot(x[g] > o) ^ KMIN);
+            x[g] = keep ? x[g] : o;
         }
     }
 }
@@ -252,21 +298,21 @@ __device__ __forceinline__ void sort_stage(uint64_t (&x)[NT], int lane, int k) {
 // NT independent sequences at once.
 template <int NT>
 __device__ __forceinline__ void wave_sort_desc(uint64_t (&x)[NT], int lane) {
-    sort_stage<1>(x, lane, 2);
-    sort_stage<2>(x, lane, 4); sort_stage<1>(x, lane, 4);
-    sort_stage<4>(x, lane, 8); sort_stage<2>(x, lane, 8); sort_stage<1>(x, lane, 8);
-    sort_stage<8>(x, lane, 16); sort_stage<4>(x, lane, 16); sort_stage<2>(x, lane, 16);
-    sort_stage<1>(x, lane, 16);
-    sort_stage<16>(x, lane, 32); sort_stage<8>(x, lane, 32); sort_stage<4>(x, lane, 32);
-    sort_stage<2>(x, lane, 32); sort_stage<1>(x, lane, 32);
-    sort_stage<32>(x, lane, 64); sort_stage<16>(x, lane, 64); sort_stage<8>(x, lane, 64);
-    sort_stage<4>(x, lane, 64); sort_stage<2>(x, lane, 64); sort_stage<1>(x, lane, 64);
+    sort_stage<1, 2>(x, lane);
+    sort_stage<2, 4>(x, lane); sort_stage<1, 4>(x, lane);
+    sort_stage<4, 8>(x, lane); sort_stage<2, 8>(x, lane); sort_stage<1, 8>(x, lane);
+    sort_stage<8, 16>(x, lane); sort_stage<4, 16>(x, lane); sort_stage<2, 16>(x, lane);
+    sort_stage<1, 16>(x, lane);
+    sort_stage<16, 32>(x, lane); sort_stage<8, 32>(x, lane); sort_stage<4, 32>(x, lane);
+    sort_stage<2, 32>(x, lane); sort_stage<1, 32>(x, lane);
+    sort_stage<32, 64>(x, lane); sort_stage<16, 64>(x, lane); sort_stage<8, 64>(x, lane);
+    sort_stage<4, 64>(x, lane); sort_stage<2, 64>(x, lane); sort_stage<1, 64>(x, lane);
 }
 
 // Floats per wavefront block of LDS: the half-scores of TG tokens or the sorted
 // lists + select buffers, whichever is larger.
 __host__ __device__ inline int block_floats(int n) {
-    const int scores = TG * 2 * n, lists = TG * (128 * 2 + 64 * 2);
+    const int scores = TG * 2 * n, lists = TG * (128 * 2 + OSTR * 2);
     return scores > lists ? scores : lists;
 }
 
@@ -325,8 +371,8 @@ __global__ __launch_bounds__(NWA * 64) void address_kernel(AddressArgs a) {
     uint32_t* pairs = reinterpret_cast<uint32_t*>(smf + NWA * pw);  // [EC*64] pruned rank pairs
     float* ls = smf + wave * pw;                      // [TG][2][64] sorted half scores
     uint32_t* lid = reinterpret_cast<uint32_t*>(ls + TG * 128);  // [TG][2][64] their sub-indices
-    uint32_t* bkey = lid + TG * 128;                  // [TG][64] select output
-    uint32_t* bid = bkey + TG * 64;                   // [TG][64]
+    uint32_t* bkey = lid + TG * 128;                  // [TG][OSTR] select output
+    uint32_t* bid = bkey + TG * OSTR;                 // [TG][OSTR]
 
     // ---------------- a1: half-scores on MFMA ----------------
     // The 2 * n/16 subkey tiles are dealt round-robin to the wavefronts. For each
@@ -500,7 +546,8 @@ __global__ __launch_bounds__(NWA * 64) void address_kernel(AddressArgs a) {
                 EH, kh, bkey, bid, lane);
             uint64_t x[TG];
 #pragma unroll
-            for (int g = 0; g < TG; ++g) x[g] = lane < kh ? composite(bkey[g * 64 + lane], bid[g * 64 + lane]) : 0ull;
+            for (int g = 0; g < TG; ++g)
+                x[g] = lane < kh ? composite(bkey[g * OSTR + lane], bid[g * OSTR + lane]) : 0ull;
             wave_sort_desc<TG>(x, lane);
 #pragma unroll
             for (int g = 0; g < TG; ++g)
@@ -531,7 +578,7 @@ __global__ __launch_bounds__(NWA * 64) void address_kernel(AddressArgs a) {
             EC, k, bkey, bid, lane);
         uint64_t x[TG];
 #pragma unroll
-        for (int g = 0; g < TG; ++g) x[g] = lane < k ? composite(bkey[g * 64 + lane], bid[g * 64 + lane]) : 0ull;
+        for (int g = 0; g < TG; ++g) x[g] = lane < k ? composite(bkey[g * OSTR + lane], bid[g * OSTR + lane]) : 0ull;
         wave_sort_desc<TG>(x, lane);
 
         // certificate: every pruned pair must score strictly below the k-th winner
@@ -560,8 +607,8 @@ __global__ __launch_bounds__(NWA * 64) void address_kernel(AddressArgs a) {
                             ii = i0[i] * (uint32_t)n + i1[jj];
                         }
                     },
-                    (full + 63) / 64, k, bkey + g * 64, bid + g * 64, lane);
-                uint64_t y1[1] = {lane < k ? composite(bkey[g * 64 + lane], bid[g * 64 + lane]) : 0ull};
+                    (full + 63) / 64, k, bkey + g * OSTR, bid + g * OSTR, lane);
+                uint64_t y1[1] = {lane < k ? composite(bkey[g * OSTR + lane], bid[g * OSTR + lane]) : 0ull};
                 wave_sort_desc<1>(y1, lane);
                 x[g] = y1[0];
             }
