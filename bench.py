@@ -426,7 +426,8 @@ def main():
         gates_out = (torch.empty((B, H, T), dtype=torch.float32, device=dev),
                      torch.empty((B, H, T), dtype=torch.float32, device=dev))
         o = torch.empty((B, H, T, dv), dtype=torch.float32, device=dev)
-    NM = 6 if a.glue else 4
+        wsg = torch.empty((sdm.sdm_scan_gated_workspace_bytes(B, H, T, W, R, dv),), dtype=torch.uint8, device=dev)
+    NM = 5 if a.glue else 4
 
     def step(marks=None):
         rec = (lambda i: marks[i].record()) if marks else (lambda i: None)
@@ -441,11 +442,12 @@ def main():
         iw, ww, ir, wr = sdm.sdm_address(g["q_w"], g["q_r"], g["subkeys"], g["subkeys"], W, R, out=addr_out,
                                          scoring=a.scoring)
         rec(2)
-        sdm.sdm_scan_forward(iw, ww, ir, wr, al, be, g["v"], M, a.form, y=y, workspace=ws)
+        if a.glue:  # the scan with the output step (RMS-Norm + gate) fused into its last pass
+            sdm.sdm_scan_forward_gated(iw, ww, ir, wr, al, be, g["v"], M, gx["gamma"], gx["g"], 1e-6, a.form,
+                                       out=o, workspace=wsg)
+        else:
+            sdm.sdm_scan_forward(iw, ww, ir, wr, al, be, g["v"], M, a.form, y=y, workspace=ws)
         rec(3)
-        if a.glue:
-            sdm.sdm_output_gate(y, gx["gamma"], gx["g"], 1e-6, out=o)
-            rec(5)
 
     for _ in range(a.warmup):
         step()
@@ -465,16 +467,15 @@ def main():
     glue = None
     if a.glue:
         gates_ms = sum(m[1].elapsed_time(m[4]) for m in marks) / a.steps
-        out_ms = sum(m[3].elapsed_time(m[5]) for m in marks) / a.steps
-        breakdown.update(gates=gates_ms, output_gate=out_ms)
+        breakdown["gates"] = gates_ms
+        breakdown["scan_gated"] = breakdown.pop("scan")
         dm = inputs.d_model(wl)
         xb = 2 if wl.bf16_inputs else 4
         gate_bytes = B * T * dm * xb + 2 * B * H * T * 4          # x in, alpha and beta out
-        out_bytes = B * H * T * dv * (4 + xb + 4)                   # y and g in, o out
         glue = {"d_model": dm,
                 "gates_GBps": gate_bytes / (gates_ms * 1e-3) / 1e9,
                 "gates_mfma_TFLOPs": 2 * B * T * dm * 2 * H / (gates_ms * 1e-3) / 1e12,
-                "output_gate_GBps": out_bytes / (out_ms * 1e-3) / 1e9}
+                "output_step": output_step_entry(sdm, g, gx, M, y, o, ws, wsg, addr_out, a.form)}
 
     row_bytes = B * H * T * (2 * W + R) * dv * esz
     scan_gbps = row_bytes / (scan_ms * 1e-3) / 1e9
@@ -512,7 +513,7 @@ def main():
     }
     if glue:
         rec["glue"] = glue
-        rec["config"]["mode"] = "layer (gates + addressing + scan + output gate)"
+        rec["config"]["mode"] = "layer (gates + addressing + scan with the output gate fused)"
     default_line = (wl.name, a.form, a.table, a.scoring, a.glue) == ("gdn_matched", "eq4", "f32", "dot", False)
     if default_line and not a.no_extras:
         # the shared-residual form on the same slots, then the long-context workload
@@ -525,6 +526,38 @@ def main():
                                            inputs.make_glue_inputs(wl) if a.glue else None,
                                            single_s=8.0 if default_line else 0.0)
     print(json.dumps(rec), flush=True)
+
+
+def output_step_entry(sdm, g, gx, M, y, o, ws, wsg, addr_out, form: str, reps: int = 5) -> dict:
+    """What the output step (RMS-Norm + gate) adds to the scan, fused into the
+    scan's last pass and as a separate kernel after it: medians of reps calls on
+    a fresh table each, HIP events on the current stream."""
+    import torch
+    iw, ww, ir, wr = addr_out
+    B = M.shape[0]
+    calls = {
+        "scan": lambda: sdm.sdm_scan_forward(iw, ww, ir, wr, g["alpha"], g["beta"], g["v"], M, form, y=y,
+                                             workspace=ws),
+        "scan_gated": lambda: sdm.sdm_scan_forward_gated(iw, ww, ir, wr, g["alpha"], g["beta"], g["v"], M,
+                                                         gx["gamma"], gx["g"], 1e-6, form, out=o, workspace=wsg),
+        "scan_then_output_gate": lambda: (calls["scan"](), sdm.sdm_output_gate(y, gx["gamma"], gx["g"], 1e-6,
+                                                                               out=o)),
+    }
+    med = {}
+    for name, fn in calls.items():
+        times = []
+        for i in range(reps + 1):
+            sdm.sdm_state_init(g["M0"], B, out=M)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            e1.synchronize()
+            if i:
+                times.append(e0.elapsed_time(e1))
+        med[name] = stats(times)["median"]
+    return {"ms": med, "fused_extra_ms": med["scan_gated"] - med["scan"],
+            "separate_extra_ms": med["scan_then_output_gate"] - med["scan"]}
 
 
 def scan_entry(sdm, g, M, y, ws, addr_out, form: str, row_bytes: int, reps: int) -> dict:

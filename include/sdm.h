@@ -32,7 +32,7 @@
 extern "C" {
 #endif
 
-#define SDM_ABI_VERSION 6
+#define SDM_ABI_VERSION 7
 
 typedef enum sdm_status {
     SDM_OK = 0,
@@ -183,6 +183,42 @@ int sdm_scan_forward(const int32_t* idx_w, const float* wt_w, int64_t W,
                      void* M, int m_dtype, float* y,
                      int64_t B, int64_t H, int64_t T, int64_t N, int64_t dv,
                      int form, void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
+ * sdm_scan_gated_workspace_bytes -- device workspace sdm_scan_forward_gated
+ * needs: sdm_scan_workspace_bytes rounded up to 256, plus B*H*T*dv*4 bytes for
+ * y in the calls that keep it themselves (0 when there is no work, -1 when the
+ * sizes are invalid).
+ */
+int64_t sdm_scan_gated_workspace_bytes(int64_t B, int64_t H, int64_t T, int64_t W, int64_t R,
+                                       int64_t dv);
+
+/*
+ * sdm_scan_forward_gated -- sdm_scan_forward followed by the head's output step
+ * of the SDM layer ([SDM] §2.4: the read, then RMS-Norm and the output gate;
+ * the same step as sdm_output_gate):
+ *   o[b,h,t,i] = y[b,h,t,i] / sqrt(mean_j y[b,h,t,j]^2 + eps) * gamma[h,i] * sigmoid(g[b,h,t,i])
+ * Arguments as sdm_scan_forward and sdm_output_gate, except:
+ *   y          [B, H, T, dv] fp32 (out), or NULL: then y is not returned
+ *   gamma      [H, dv] fp32; g [B, H, T, dv] g_dtype (SDM_F32 or SDM_BF16);
+ *   eps >= 0;  o [B, H, T, dv] fp32 (out), not aliasing y
+ *   workspace  >= sdm_scan_gated_workspace_bytes(B,H,T,W,R,dv) bytes, 16-byte aligned
+ * The table M and y are bit-identical to sdm_scan_forward's, and o to
+ * sdm_output_gate applied to that y. Where the scan splits the table rows into
+ * partitions whose partial sums of y a last pass adds (long calls: the usual
+ * case), that pass also normalises and gates each row while it holds it in
+ * registers (d_v <= 1024), so y is stored only if requested and never read
+ * back; otherwise y is stored (to `y`, or the workspace) and the output step
+ * runs after the scan. Same support as sdm_scan_forward, and B*H*T < 2^32.
+ */
+int sdm_scan_forward_gated(const int32_t* idx_w, const float* wt_w, int64_t W,
+                           const int32_t* idx_r, const float* wt_r, int64_t R,
+                           const float* alpha, const float* beta,
+                           const void* v, int v_dtype,
+                           void* M, int m_dtype, float* y,
+                           const float* gamma, const void* g, int g_dtype, float eps, float* o,
+                           int64_t B, int64_t H, int64_t T, int64_t N, int64_t dv,
+                           int form, void* workspace, int64_t workspace_bytes, void* stream);
 
 /*
  * sdm_scan_forward_noalloc -- sdm_scan_forward without a workspace argument, for

@@ -36,6 +36,10 @@ _SIGS = {
     "sdm_scan_workspace_bytes": (_I64, [_I64, _I64, _I64, _I64, _I64, _I64]),
     "sdm_scan_forward": (_I, [_P, _P, _I64, _P, _P, _I64, _P, _P, _P, _I, _P, _I, _P,
                               _I64, _I64, _I64, _I64, _I64, _I, _P, _I64, _P]),
+    "sdm_scan_gated_workspace_bytes": (_I64, [_I64, _I64, _I64, _I64, _I64, _I64]),
+    "sdm_scan_forward_gated": (_I, [_P, _P, _I64, _P, _P, _I64, _P, _P, _P, _I, _P, _I, _P,
+                                    _P, _P, _I, ctypes.c_float, _P,
+                                    _I64, _I64, _I64, _I64, _I64, _I, _P, _I64, _P]),
     "sdm_scan_forward_noalloc": (_I, [_P, _P, _I64, _P, _P, _I64, _P, _P, _P, _I, _P, _I, _P,
                                       _I64, _I64, _I64, _I64, _I64, _I, _P]),
     "sdm_scan_snapshot_bytes": (_I64, [_I64, _I64, _I64, _I64, _I64]),
@@ -259,6 +263,39 @@ def sdm_scan_forward(idx_w: torch.Tensor, wt_w: torch.Tensor, idx_r: torch.Tenso
         _ptr(v), _dtype_code(v), _ptr(M), _dtype_code(M), _ptr(y), B, H, T, N, dv, FORMS[form],
         _ptr(workspace), workspace.numel(), _stream(d)))
     return y
+
+
+def sdm_scan_gated_workspace_bytes(B: int, H: int, T: int, W: int, R: int, dv: int) -> int:
+    n = lib().sdm_scan_gated_workspace_bytes(B, H, T, W, R, dv)
+    if n < 0:
+        raise ValueError("invalid sizes for the gated scan workspace")
+    return n
+
+
+def sdm_scan_forward_gated(idx_w: torch.Tensor, wt_w: torch.Tensor, idx_r: torch.Tensor,
+                           wt_r: torch.Tensor, alpha: torch.Tensor, beta: torch.Tensor,
+                           v: torch.Tensor, M: torch.Tensor, gamma: torch.Tensor, g: torch.Tensor,
+                           eps: float = 1e-6, form: str = "eq4", y: Optional[torch.Tensor] = None,
+                           keep_y: bool = False, out: Optional[torch.Tensor] = None,
+                           workspace: Optional[torch.Tensor] = None):
+    """The scan followed by the output step (RMS-Norm, gamma, sigmoid gate).
+    M is updated in place. Returns o [B,H,T,dv] fp32, or (o, y) when y is given
+    or keep_y is set (otherwise y is not stored where the scan need not)."""
+    d, (B, H, T, W, R, N, dv) = _scan_inputs("sdm_scan_forward_gated", idx_w, wt_w, idx_r, wt_r,
+                                             alpha, beta, v, M, (torch.float32, torch.bfloat16))
+    if gamma.shape != (H, dv) or gamma.dtype != torch.float32 or g.shape != (B, H, T, dv):
+        raise ValueError("shape or dtype mismatch of gamma or g in sdm_scan_forward_gated")
+    _dev(idx_w, gamma, g)
+    if y is not None or keep_y:
+        y = _f32_out(y, (B, H, T, dv), d, "y")
+    o = _f32_out(out, (B, H, T, dv), d, "o")
+    workspace = _workspace(workspace, sdm_scan_gated_workspace_bytes(B, H, T, W, R, dv), d)
+    _check("sdm_scan_forward_gated", lib().sdm_scan_forward_gated(
+        _ptr(idx_w), _ptr(wt_w), W, _ptr(idx_r), _ptr(wt_r), R, _ptr(alpha), _ptr(beta),
+        _ptr(v), _dtype_code(v), _ptr(M), _dtype_code(M), _ptr(y),
+        _ptr(gamma), _ptr(g), _dtype_code(g), float(eps), _ptr(o), B, H, T, N, dv, FORMS[form],
+        _ptr(workspace), workspace.numel(), _stream(d)))
+    return (o, y) if y is not None else o
 
 
 def sdm_scan_forward_noalloc(idx_w: torch.Tensor, wt_w: torch.Tensor, idx_r: torch.Tensor,

@@ -19,6 +19,13 @@
 // row of d_v values in 16-byte pieces; the sum of squares is a butterfly over
 // the group, then each lane scales, multiplies by gamma and the gate, and
 // stores. HBM-bound: y and g in, o out.
+//
+// ypart_gate_kernel: the same step fused into the scan's last pass where the
+// scan splits the table rows into P partitions: a lane adds its pieces' P
+// partial sums (in partition order, as the plain partial-sum pass does), keeps
+// them in registers for the norm and the gate, and stores y only on request.
+// Against partial sums + output gate it saves storing y and reading it back:
+// per row P * d_v * 4 + g in, o (+ y) out.
 #include "sdm_buffer.h"
 #include "sdm_internal.h"
 
@@ -128,7 +135,84 @@ __global__ __launch_bounds__(256) void output_gate_kernel(OutGateArgs a) {
     }
 }
 
+// o for one row held by a group of LG lanes: pieces v[j] (q = sub + j * LG < nq)
+template <bool GBF16, int NJ>
+__device__ __forceinline__ void gate_row(const float4 (&v)[NJ], int sub, int LG, int nq, int dv, float eps,
+                                         const float4* gm4, const void* g, int64_t row, float4* o4, bool ok) {
+    float ss = 0.f;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+        const int q = sub + j * LG;
+        if (ok && q < nq) ss = fmaf(v[j].x, v[j].x, fmaf(v[j].y, v[j].y, fmaf(v[j].z, v[j].z, fmaf(v[j].w, v[j].w, ss))));
+    }
+    for (int m = 1; m < LG; m <<= 1) ss += __shfl_xor(ss, m);  // the same sum on every lane of the group
+    const float r = 1.f / sqrtf(ss / (float)dv + eps);
+    if (!ok) return;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+        const int q = sub + j * LG;
+        if (q >= nq) break;
+        const float4 gm = gm4[q];
+        float4 gt;
+        if constexpr (GBF16) {
+            const uint2 p = reinterpret_cast<const uint2*>(g)[row * nq + q];
+            gt = make_float4(__uint_as_float(p.x << 16), __uint_as_float(p.x & 0xFFFF0000u),
+                             __uint_as_float(p.y << 16), __uint_as_float(p.y & 0xFFFF0000u));
+        } else {
+            gt = reinterpret_cast<const float4*>(g)[row * nq + q];
+        }
+        auto sg = [](float z) { return 1.f / (1.f + expf(-z)); };
+        o4[q] = make_float4(v[j].x * r * gm.x * sg(gt.x), v[j].y * r * gm.y * sg(gt.y), v[j].z * r * gm.z * sg(gt.z),
+                            v[j].w * r * gm.w * sg(gt.w));
+    }
+}
+
+template <bool GBF16>
+__global__ __launch_bounds__(256) void ypart_gate_kernel(YGateArgs a) {
+    constexpr int NJ = GATE_FUSED_PIECES;
+    const int LG = output_gate_lanes(a.dv);
+    const int lane = threadIdx.x & 63;
+    const int sub = lane & (LG - 1);
+    const int rows_per_wave = 64 / LG;
+    const int64_t wave_g = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 6;
+    const int64_t nwaves = ((int64_t)gridDim.x * 256) >> 6;
+    const int nq = a.dv / 4;
+    const int64_t rows = a.NS * a.Tc, n = rows * nq;  // float4 per partition
+    const float4* yp = reinterpret_cast<const float4*>(a.yp);
+    for (int64_t r0 = wave_g * rows_per_wave; r0 < rows; r0 += nwaves * rows_per_wave) {
+        const int64_t rl = r0 + lane / LG;  // row of the chunk: stream s, token t0 + t
+        const bool ok = rl < rows;
+        const int64_t s = ok ? rl / a.Tc : 0, grow = s * a.TS + a.t0 + (ok ? rl - s * a.Tc : 0);
+        float4 v[NJ];
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            const int q = sub + j * LG;
+            v[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (!ok || q >= nq) continue;
+            float4 acc = yp[rl * nq + q];
+            for (int p = 1; p < a.P; ++p) acc = f4_add(acc, yp[p * n + rl * nq + q]);
+            v[j] = acc;
+            if (a.y) reinterpret_cast<float4*>(a.y)[grow * nq + q] = acc;
+        }
+        const float4* gm4 = reinterpret_cast<const float4*>(a.gate.gamma) + (s % a.gate.H) * nq;
+        gate_row<GBF16, NJ>(v, sub, LG, nq, a.dv, a.gate.eps, gm4, a.gate.g, grow,
+                            reinterpret_cast<float4*>(a.gate.o) + grow * nq, ok);
+    }
+}
+
 }  // namespace
+
+hipError_t launch_ypart_gate(const YGateArgs& a, hipStream_t st) {
+    const int lg = output_gate_lanes(a.dv);
+    const int64_t waves = (a.NS * a.Tc + (64 / lg) - 1) / (64 / lg);
+    int64_t blocks = (waves + 3) / 4;
+    if (blocks > 16384) blocks = 16384;
+    if (a.gate.g_bf16)
+        hipLaunchKernelGGL(ypart_gate_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, st, a);
+    else
+        hipLaunchKernelGGL(ypart_gate_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, st, a);
+    return hipGetLastError();
+}
 
 hipError_t launch_gates(const GatesArgs& a, hipStream_t st) {
     const int64_t tiles = (a.B * a.T + 15) / 16;
@@ -141,8 +225,7 @@ hipError_t launch_gates(const GatesArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_output_gate(OutGateArgs a, hipStream_t st) {
-    int lg = 1;
-    while (lg < 64 && lg < a.dv / 4) lg <<= 1;
+    const int lg = output_gate_lanes(a.dv);
     a.lg = lg;
     const int64_t waves = (a.rows + (64 / lg) - 1) / (64 / lg);
     int64_t blocks = (waves + 3) / 4;

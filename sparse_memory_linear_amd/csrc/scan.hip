@@ -1000,6 +1000,9 @@ hipError_t launch_scan_inst(int form, bool vb, bool save, bool mb, dim3 grid, di
     return hipSuccess;
 }
 
+// the fused output step keeps a lane's pieces of a row in registers
+bool gate_fusable(int dv) { return dv / 4 <= GATE_FUSED_PIECES * output_gate_lanes(dv); }
+
 template <int SL>
 hipError_t launch_scan_slab(const ScanArgs& a, const Cfg& c, hipStream_t st) {
     constexpr int D = SlabCfg<SL>::D;
@@ -1073,7 +1076,13 @@ hipError_t launch_scan_slab(const ScanArgs& a, const Cfg& c, hipStream_t st) {
         e = launch_scan_inst<SL>(a.form, a.v_bf16, save, a.m_bf16, grid, block, lds, st, k);
         if (e == hipSuccess) e = hipGetLastError();
         if (e != hipSuccess) return e;
-        if (c.P > 1) {
+        if (c.P > 1 && a.gate && gate_fusable(a.dv)) {
+            YGateArgs ga{};
+            ga.yp = ypart; ga.y = a.y; ga.gate = *a.gate; ga.P = c.P;
+            ga.NS = a.NS; ga.Tc = Tn; ga.TS = a.T; ga.t0 = c0; ga.dv = a.dv;
+            e = launch_ypart_gate(ga, st);
+            if (e != hipSuccess) return e;
+        } else if (c.P > 1) {
             const int64_t n4 = a.NS * Tn * (a.dv / 4);
             const int64_t nb = (n4 + 255) / 256 < 4096 ? (n4 + 255) / 256 : 4096;
             hipLaunchKernelGGL(ypart_reduce, dim3((unsigned)nb), dim3(256), 0, st,
@@ -1292,6 +1301,14 @@ int64_t scan_tokens_within(int64_t NS, int64_t T, int W, int R, int dv, bool m_b
         else hi = mid - 1;
     }
     return lo;
+}
+
+bool scan_fuses_gate(int64_t NS, int64_t T, int W, int R, int dv, bool m_bf16, int form) {
+    const int cpl = m_bf16 ? 8 : 4;
+    if (T <= direct_max_tokens() && T * (int64_t)dv * 4 < 0x7FFFFFFF &&
+        pick_slab(NS, W, R, dv, cpl, env_int("SDM_SCAN_SLAB"), false) != 0)
+        return false;  // the short-call form: no partial sums
+    return choose_cfg(NS, W, R, dv, form, cpl).P > 1 && gate_fusable(dv);
 }
 
 hipError_t launch_scan(const ScanArgs& a, hipStream_t st) {

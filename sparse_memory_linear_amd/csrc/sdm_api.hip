@@ -281,6 +281,61 @@ int sdm_scan_forward(const int32_t* idx_w, const float* wt_w, int64_t W, const i
                              m_dtype, y, nullptr, false, B, H, T, N, dv, form, workspace, workspace_bytes, stream);
 }
 
+int64_t sdm_scan_gated_workspace_bytes(int64_t B, int64_t H, int64_t T, int64_t W, int64_t R, int64_t dv) {
+    const int64_t b = sdm_scan_workspace_bytes(B, H, T, W, R, dv);
+    if (b <= 0) return b;
+    return (b + 255) / 256 * 256 + B * H * T * dv * 4;  // + y, where the call keeps it itself
+}
+
+int sdm_scan_forward_gated(const int32_t* idx_w, const float* wt_w, int64_t W, const int32_t* idx_r,
+                           const float* wt_r, int64_t R, const float* alpha, const float* beta, const void* v,
+                           int v_dtype, void* M, int m_dtype, float* y, const float* gamma, const void* g,
+                           int g_dtype, float eps, float* o, int64_t B, int64_t H, int64_t T, int64_t N,
+                           int64_t dv, int form, void* workspace, int64_t workspace_bytes, void* stream) {
+    const char* fn = "sdm_scan_forward_gated";
+    int rc = check_scan(fn, idx_w, wt_w, W, idx_r, wt_r, R, alpha, beta, v, v_dtype, B, H, T, N, dv, form,
+                        m_dtype);
+    if (g_dtype != SDM_F32 && g_dtype != SDM_BF16) return fail(SDM_ERR_DTYPE, "unknown gate dtype %d", g_dtype);
+    if (!(eps >= 0.f)) return fail(SDM_ERR_SHAPE, "%s: eps must be >= 0", fn);
+    if (rc == NO_WORK) return ok();
+    if (rc) return rc;
+    if (B * H * T > 0xFFFFFFFFll)
+        return fail(SDM_ERR_UNSUPPORTED, "B*H*T=%lld: at most 2^32 - 1 rows per call", (long long)(B * H * T));
+    if ((rc = check_buffers(fn, {M, gamma, g, o}))) return rc;
+    if (y && !aligned16(y)) return fail(SDM_ERR_ALIGN, "%s: pointer %p not 16-byte aligned", fn, (void*)y);
+    if (o == y) return fail(SDM_ERR_SHAPE, "%s: o may not alias y", fn);
+    const int64_t scan_ws = sdm::scan_workspace_bytes(B * H, T, (int)W, (int)R, (int)dv);
+    if ((rc = check_workspace(workspace, workspace_bytes, (scan_ws + 255) / 256 * 256 + B * H * T * dv * 4)))
+        return rc;
+    sdm::GateArgs ga{};
+    ga.gamma = gamma; ga.g = g; ga.o = o; ga.eps = eps; ga.H = H; ga.g_bf16 = g_dtype == SDM_BF16;
+    const bool fused = sdm::scan_fuses_gate(B * H, T, (int)W, (int)R, (int)dv, m_dtype == SDM_BF16, form);
+    // where the scan stores y itself and the caller passed none, y goes to the workspace's tail
+    float* yy = y ? y : reinterpret_cast<float*>(static_cast<char*>(workspace) + (scan_ws + 255) / 256 * 256);
+    sdm::ScanArgs a{};
+    a.idx_w = idx_w; a.wt_w = wt_w; a.W = (int)W;
+    a.idx_r = idx_r; a.wt_r = wt_r; a.R = (int)R;
+    a.alpha = alpha; a.beta = beta;
+    a.v = v; a.v_bf16 = v_dtype == SDM_BF16;
+    a.M = M; a.m_bf16 = m_dtype == SDM_BF16;
+    a.y = fused ? y : yy;
+    a.NS = B * H; a.T = T; a.N = N; a.dv = (int)dv;
+    a.form = form;
+    a.workspace = workspace;
+    a.gate = fused ? &ga : nullptr;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e = sdm::launch_scan(a, st);
+    if (e != hipSuccess) return hip_fail(e, fn);
+    if (!fused) {
+        sdm::OutGateArgs og{};
+        og.y = yy; og.gamma = gamma; og.g = g; og.o = o; og.eps = eps;
+        og.rows = B * H * T; og.T = T; og.H = H; og.dv = (int)dv; og.g_bf16 = ga.g_bf16;
+        e = sdm::launch_output_gate(og, st);
+        if (e != hipSuccess) return hip_fail(e, fn);
+    }
+    return ok();
+}
+
 }  // extern "C"
 
 namespace {

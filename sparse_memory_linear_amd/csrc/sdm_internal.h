@@ -22,6 +22,17 @@ struct AddressArgs {
 };
 hipError_t launch_address(const AddressArgs& a, hipStream_t st);
 
+// The output step fused into the scan's last pass (partial sums of the row
+// partitions -> y -> RMS-Norm and output gate -> o): see sdm_scan_forward_gated.
+struct GateArgs {
+    const float* gamma;      // [H,dv]
+    const void* g;           // [B,H,T,dv] gate pre-activation
+    float* o;                // [B,H,T,dv]
+    float eps;
+    int64_t H;
+    bool g_bf16;
+};
+
 struct ScanArgs {
     const int32_t* idx_w; const float* wt_w; int W;
     const int32_t* idx_r; const float* wt_r; int R;
@@ -36,7 +47,14 @@ struct ScanArgs {
     void* workspace;
     float* snap;             // optional [NS][T][W][dv]: pre-image of every write (training forward)
     int64_t max_tokens = 0;  // > 0: tokens per launch chunk at most this (a bounded workspace)
+    // optional: the output step; where the scan sums row-partition partials it
+    // runs in that pass (y is then stored only if y != nullptr), else the caller
+    // runs the output gate on y
+    const GateArgs* gate = nullptr;
 };
+// Whether launch_scan with a.gate set fuses the output step for these sizes
+// (else y is stored and the caller applies the gate).
+bool scan_fuses_gate(int64_t NS, int64_t T, int W, int R, int dv, bool m_bf16, int form);
 // Chooses the kernel instance; returns false if no instance covers (W, R, dv).
 bool scan_geometry(int64_t NS, int W, int R, int dv, bool m_bf16, int* slab, int* rec_bytes);
 int64_t scan_workspace_bytes(int64_t NS, int64_t T, int W, int R, int dv);
@@ -94,5 +112,27 @@ struct OutGateArgs {
     bool g_bf16;
 };
 hipError_t launch_output_gate(OutGateArgs a, hipStream_t st);
+
+// Lanes per row of the output step: a power of two covering the row's 16-byte
+// pieces, at most 64 (the same in the plain and the fused kernel, so both add
+// the squares in the same order).
+__host__ __device__ inline int output_gate_lanes(int dv) {
+    int lg = 1;
+    while (lg < 64 && lg < dv / 4) lg <<= 1;
+    return lg;
+}
+// The fused form holds a lane's pieces in registers: at most this many.
+constexpr int GATE_FUSED_PIECES = 4;
+// The partial sums of P row partitions of one launch chunk (Tc of TS tokens
+// from t0) -> y (if y != nullptr) and the output step -> o.
+struct YGateArgs {
+    const float* yp;         // [P][NS][Tc][dv]
+    float* y;                // [NS][TS][dv] or nullptr
+    GateArgs gate;
+    int P;
+    int64_t NS, Tc, TS, t0;
+    int dv;
+};
+hipError_t launch_ypart_gate(const YGateArgs& a, hipStream_t st);
 
 }  // namespace sdm

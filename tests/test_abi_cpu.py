@@ -32,7 +32,8 @@ def test_header_declares_the_hot_path_calls():
               "sdm_scan_workspace_bytes", "sdm_status_string", "sdm_last_error", "sdm_abi_version",
               "sdm_scan_forward_save", "sdm_scan_snapshot_bytes", "sdm_scan_backward",
               "sdm_scan_backward_workspace_bytes", "sdm_state_init_backward", "sdm_address_idw",
-              "sdm_debug_half_scores_idw", "sdm_gates", "sdm_output_gate", "sdm_scan_forward_noalloc"):
+              "sdm_debug_half_scores_idw", "sdm_gates", "sdm_output_gate", "sdm_scan_forward_noalloc",
+              "sdm_scan_forward_gated", "sdm_scan_gated_workspace_bytes"):
         assert f in names
 
 
@@ -43,7 +44,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert binding.sdm_abi_version() == 6
+    assert binding.sdm_abi_version() == 7
     assert binding.sdm_status_string(0) == "ok"
     assert binding.sdm_status_string(7).startswith("workspace")
     assert binding.sdm_status_string(99) == "unknown status"
@@ -225,3 +226,29 @@ def test_noalloc_scan_rejects_bad_arguments_before_launch(lib):
     # 65536 streams: one token's plan records alone take 65536 x 1536 bytes
     assert call(B=65536) == 5
     assert "scratch" in binding.sdm_last_error()
+
+
+def test_gated_scan_rejects_bad_arguments_before_launch(lib):
+    """The scan with the output step validates the scan's arguments like
+    sdm_scan_forward, then its own (gate dtype, eps, gamma/g/o, o not aliasing
+    y, the larger workspace), all before any HIP call; y may be NULL."""
+    fake = P(4096)
+    B, H, T, dv = 1, 2, 100, 128
+    need = binding.sdm_scan_gated_workspace_bytes(B, H, T, 64, 64, dv)
+    assert need >= binding.sdm_scan_workspace_bytes(B, H, T, 64, 64, dv) + B * H * T * dv * 4
+    assert binding.sdm_scan_gated_workspace_bytes(0, H, T, 64, 64, dv) == 0
+    assert lib.sdm_scan_gated_workspace_bytes(B, H, T, 64, 64, 6) == -1
+    base = dict(iw=fake, ww=fake, W=64, ir=fake, wr=fake, R=64, a=fake, b=fake, v=fake, vd=1, M=fake, md=0,
+                y=None, gamma=fake, g=fake, gd=1, eps=ctypes.c_float(1e-6), o=P(8192), B=B, H=H, T=T, N=4096,
+                dv=dv, form=0, ws=fake, wsb=need, st=None)
+    call = lambda **kw: lib.sdm_scan_forward_gated(*dict(base, **kw).values())
+    assert call(iw=None) == 1                                  # SDM_ERR_NULL
+    assert call(gamma=None) == 1
+    assert call(o=None) == 1
+    assert call(iw=None, ww=None, M=None, T=0) == 0           # empty: valid no-op
+    assert call(gd=5) == 3                                     # SDM_ERR_DTYPE
+    assert call(form=2) == 3
+    assert call(eps=ctypes.c_float(-1.0)) == 2                 # SDM_ERR_SHAPE
+    assert call(y=P(8192)) == 2                                # o aliases y
+    assert call(o=P(8200)) == 4                                # SDM_ERR_ALIGN
+    assert call(wsb=need - 16) == 7                            # SDM_ERR_WORKSPACE

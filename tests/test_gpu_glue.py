@@ -144,3 +144,83 @@ def test_glue_full_size_gdn_matched():
     eo = max_rel_err(o.cpu().numpy(), oracle.output_gate(y, gx["gamma"], gx["g"], 1e-6))
     say(f"  max rel err alpha {ea:.2e}, beta {eb:.2e}, o {eo:.2e}")
     assert ea <= TOL_BF16 and eb <= TOL_BF16 and eo <= 1e-5
+
+
+GATED = [("gdn_matched", dict(B=1, H=2, T=500), "eq4", "f32"),     # row partitions: the fused pass
+         ("gdn_matched", dict(B=1, H=2, T=300), "fig2", "f32"),    # one partition: y, then the gate
+         ("gdn_matched", dict(B=3, H=2, T=5), "eq4", "f32"),       # the short-call form
+         ("gdn_matched", dict(B=1, H=2, T=400), "eq4", "bf16"),    # bf16 table, row partitions
+         ("small", dict(B=2, H=2, T=333), "eq4", "f32"),           # fp32 gate input
+         ("large_table", dict(T=200), "eq4", "f32")]               # d_v = 512: 2 pieces a lane
+
+
+@pytest.mark.parametrize("name,over,form,table", GATED, ids=[f"{c[0]}-{c[2]}-{c[3]}-T{c[1]['T']}" for c in GATED])
+def test_gated_scan_equals_scan_then_output_gate(name, over, form, table):
+    """sdm_scan_forward_gated against sdm_scan_forward followed by
+    sdm_output_gate: table, y and o bit-identical, with y returned or not."""
+    wl = inputs.get(name, **over)
+    say(f"[gated scan] {name} {over} {form} table={table}")
+    x = inputs.make_inputs(wl)
+    gx = inputs.make_glue_inputs(wl)
+    g = {k: v.to(DEV) for k, v in x.items()}
+    gg = {k: v.to(DEV) for k, v in gx.items()}
+    iw, ww, ir, wr = sdm.sdm_address(g["q_w"], g["q_r"], g["subkeys"], g["subkeys"], wl.W, wl.R)
+    M0 = sdm.sdm_state_init(g["M0"], wl.B)
+    if table == "bf16":
+        M0 = M0.to(torch.bfloat16)
+    M1, M2, M3 = M0.clone(), M0.clone(), M0.clone()
+    y1 = sdm.sdm_scan_forward(iw, ww, ir, wr, g["alpha"], g["beta"], g["v"], M1, form)
+    o1 = sdm.sdm_output_gate(y1, gg["gamma"], gg["g"], 1e-6)
+    o2, y2 = sdm.sdm_scan_forward_gated(iw, ww, ir, wr, g["alpha"], g["beta"], g["v"], M2, gg["gamma"], gg["g"],
+                                        1e-6, form, keep_y=True)
+    o3 = sdm.sdm_scan_forward_gated(iw, ww, ir, wr, g["alpha"], g["beta"], g["v"], M3, gg["gamma"], gg["g"],
+                                    1e-6, form)
+    torch.cuda.synchronize()
+    assert torch.equal(M1, M2) and torch.equal(M1, M3)
+    assert torch.equal(y1, y2)
+    assert torch.equal(o1, o2) and torch.equal(o1, o3)
+
+
+def test_gated_scan_layer_matches_oracle():
+    """The whole layer step through the gated call against the oracle chain
+    (addressing, gates, scan, RMS-Norm and gate), both sides on the oracle's
+    slots and weights."""
+    wl = inputs.get("gdn_matched", B=1, H=2, T=600)
+    say("[gated scan vs oracle] gdn_matched B=1 H=2 T=600")
+    x = inputs.make_inputs(wl)
+    gx = inputs.make_glue_inputs(wl)
+    iw, ww, _, _ = oracle.address(x["q_w"], x["subkeys"], wl.W)
+    ir, wr, _, _ = oracle.address(x["q_r"], x["subkeys"], wl.R)
+    oa, ob = oracle.gates(gx["x"], gx["W_a"], gx["W_b"], gx["b_dt"], gx["A"])
+    Mo, yo = oracle.scan(iw, ww, ir, wr, oa, ob, x["v"], oracle.broadcast_state(x["M0"], wl.B), oracle.EQ4)
+    oo = oracle.output_gate(yo, gx["gamma"], gx["g"], 1e-6)
+    g = {k: v.to(DEV) for k, v in gx.items()}
+    al, be = sdm.sdm_gates(g["x"], g["W_a"], g["W_b"], g["b_dt"], g["A"])
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    M = sdm.sdm_state_init(x["M0"].to(DEV), wl.B)
+    o = sdm.sdm_scan_forward_gated(t(iw), t(ww), t(ir), t(wr), al, be, x["v"].to(DEV), M, g["gamma"], g["g"],
+                                   1e-6, "eq4")
+    torch.cuda.synchronize()
+    e_o, e_m = max_rel_err(o.cpu().numpy(), oo), max_rel_err(M.cpu().numpy(), Mo)
+    say(f"  max rel err o {e_o:.2e}, M {e_m:.2e}")
+    assert e_o <= TOL_BF16 and e_m <= TOL_BF16
+
+
+def test_gated_scan_full_size_gdn_matched():
+    """The gated call in the benchmark's launch configuration (32 streams of
+    8192 tokens: two row partitions, the fused pass) equals scan + output gate."""
+    wl = inputs.get("gdn_matched")
+    say(f"[gated scan full size] B={wl.B} H={wl.H} T={wl.T}")
+    x = inputs.make_inputs(wl)
+    gx = inputs.make_glue_inputs(wl)
+    g = {k: v.to(DEV) for k, v in x.items()}
+    gg = {k: v.to(DEV) for k, v in gx.items()}
+    iw, ww, ir, wr = sdm.sdm_address(g["q_w"], g["q_r"], g["subkeys"], g["subkeys"], wl.W, wl.R)
+    M1 = sdm.sdm_state_init(g["M0"], wl.B)
+    M2 = M1.clone()
+    y1 = sdm.sdm_scan_forward(iw, ww, ir, wr, g["alpha"], g["beta"], g["v"], M1, "eq4")
+    o1 = sdm.sdm_output_gate(y1, gg["gamma"], gg["g"], 1e-6)
+    del y1
+    o2 = sdm.sdm_scan_forward_gated(iw, ww, ir, wr, g["alpha"], g["beta"], g["v"], M2, gg["gamma"], gg["g"], 1e-6)
+    torch.cuda.synchronize()
+    assert torch.equal(M1, M2) and torch.equal(o1, o2)
