@@ -27,7 +27,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "SDM scan tokens/s and slot-row HBM GB/s at N=65536,W=R=64,d_v=128"
 HBM_PEAK_GBPS = 8000.0
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scan_traffic_gdn_matched.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scan_traffic_{}.json")
 # the sources the scan kernels are compiled from: the counter summary holds for them only
 SCAN_SRCS = [os.path.join(ROOT, "sparse_memory_linear_amd", "csrc", f) for f in ("scan.hip", "sdm_buffer.h")]
 
@@ -130,11 +130,11 @@ def slot_reuse(idx, N: int, window: int = 32768) -> dict:
     return {"window_tokens": window, "windows": len(cov), "coverage": f(cov), "collision": f(col), "kld": f(kld)}
 
 
-def measured_traffic():
-    """HBM bytes per scan launch from the committed counter summary, if it was
-    taken on the current scan kernel source."""
+def measured_traffic(workload: str = "gdn_matched"):
+    """HBM bytes per scan launch from the committed counter summary of this
+    workload, if it was taken on the current scan kernel source."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(TRAFFIC_FILE.format(workload)) as f:
             rec = json.load(f)
         if rec.get("scan_source_sha256") == scan_source_sha256():
             return rec.get("traffic_bytes_per_launch")
@@ -611,6 +611,7 @@ def long_context_entry(sdm, inputs, dev) -> dict:
     ent.update({"workload": "long_context", "B": B, "H": H, "T": T, "N": N, "W": W, "R": R, "d_v": dv,
                 "keys": f"{wl.n_centroids}-centroid Gaussian mixture, sigma={wl.sigma}",
                 "scan_tokens_per_s": B * T / (ent["ms"]["median"] * 1e-3), "address_ms": addr_ms,
+                "traffic": measured_traffic("long_context"),
                 "slot_reuse": {"write": slot_reuse(out[0].cpu().numpy(), N),
                                "read": slot_reuse(out[2].cpu().numpy(), N)}})
     del g, M, y, ws, out
