@@ -33,10 +33,15 @@ SCAN_SRCS = [os.path.join(ROOT, "sparse_memory_linear_amd", "csrc", f) for f in 
 
 
 def scan_source_sha256() -> str:
+    """SHA-256 of the scan sources' code: each line with its // comment and
+    trailing blanks removed, blank lines dropped (comment edits keep the hash)."""
     h = hashlib.sha256()
     for path in SCAN_SRCS:
-        with open(path, "rb") as f:
-            h.update(f.read())
+        with open(path, encoding="utf-8") as f:
+            for line in f:
+                code = line.split("//", 1)[0].rstrip()
+                if code:
+                    h.update(code.encode() + b"\n")
     return h.hexdigest()
 
 

@@ -31,8 +31,10 @@
 // memory access is a buffer instruction with a 32-bit lane offset and the
 // token's offset in a scalar register; an access that must not happen (padding
 // lanes, the y store of all but one wavefront) gets an offset past the end of
-// its buffer, which the hardware drops (loads return 0). Writer entries carry
-// alpha and beta next to the weight, so a writer issues one plan load per token.
+// its buffer, which the hardware drops (loads return 0). A writer entry carries
+// the token's gate values with the row (per-slot form: the update's two
+// coefficients c = alpha (1 - beta w) and b = beta w, so M[i] = c M[i] + b v is
+// one multiply-add per element), so a writer issues one plan load per token.
 //
 // Placement: workgroups are dealt to the 8 XCDs round-robin, so with at least
 // 8 streams blockIdx is remapped to put every slab of a stream on the same XCD
@@ -102,9 +104,12 @@ static_assert(slab_cfg_ok<4>() && slab_cfg_ok<8>() && slab_cfg_ok<16>() && slab_
 // Geometry of a slab of S fp32 columns: L = S/4 lanes per row segment (16 B
 // each), G = 64/L rows per wavefront; NWW = ceil(W/G) writer and NWR = ceil(R/G)
 // reader wavefronts. Plan record per token: writer entries [NWW][G] of 16 bytes
-// (packed word, weight, alpha, beta), then reader entries [NWR][G] of 8 bytes
-// (packed word, weight): writer wave w, lane row r -> write access w*G + r,
-// reader wave w -> read access w*G + r.
+// (per-slot form: packed word, c, b, write position | ring offset << 8;
+// shared-residual form: packed word, weight, alpha, beta), then reader entries
+// [NWR][G] of 8 bytes (packed word, weight): writer wave w, lane row r -> write
+// access w*G + r, reader wave w -> read access w*G + r. Records come in blocks
+// of BT tokens, entry-major within a block, so that one lane load fetches an
+// entry of BT consecutive tokens.
 struct Geom {
     int S, G, NWW, NWR;
     __host__ __device__ int nw() const { return NWW + NWR; }
@@ -435,10 +440,8 @@ struct ScanKArgs {
 // SAVE (training forward): every write also stores its row as it was before
 // this token's decay (the pre-image M_{t-1}[i]) at [t][write position][col],
 // which the backward uses to undo the write. The per-slot form's writer
-// entries then carry beta*w (the one product the update uses, rounded as the
-// kernel would round it) and the write position in place of w and beta; the
-// shared-residual form runs with one row partition, where a writer's rank in
-// its token is the write position.
+// entries carry the write position for it; the shared-residual form runs with
+// one row partition, where a writer's rank in its token is the write position.
 // MBF16: the table is stored in bfloat16. A lane's 16 bytes of a row then hold
 // 8 columns instead of 4, so the same lane layout covers twice the columns
 // (slab width S = 2 * SL) and every row access moves half the bytes; rows are
