@@ -97,7 +97,7 @@ constexpr bool slab_cfg_ok() {
     constexpr int D = SlabCfg<S>::D, U = SlabCfg<S>::U, UR = SlabCfg<S>::UR, NBT = SlabCfg<S>::NBT;
     constexpr int BT = entry_batch<S>();
     return U % (D + 1) == 0 && U % UR == 0 && U % NBT == 0 && NBT % BT == 0 && UR >= D + 2 &&
-           NBT / BT >= 1 + (BT + D) / BT && D <= 15;
+           NBT / BT >= 1 + (BT + D) / BT && D <= 15 && (BT & (BT - 1)) == 0 && UR <= 31;
 }
 static_assert(slab_cfg_ok<4>() && slab_cfg_ok<8>() && slab_cfg_ok<16>() && slab_cfg_ok<32>(), "ring sizes");
 
@@ -184,6 +184,8 @@ struct PlanArgs {
     int rpos;   // bytes per position (16 per lane of a row segment)
     int rlane;
     int bt;     // records in blocks of bt tokens: [writer positions][bt] entries, then [reader positions][bt]
+    int bts;    // log2(bt): bt is a power of two
+    uint32_t urm;  // ceil(2^32 / ur): x % ur = x - ur * umulhi(x, urm) for x < 2^32 / ur
     int64_t tp; // tokens of a (stream, partition) record region (Tc rounded up to bt)
 };
 
@@ -244,12 +246,24 @@ __global__ __launch_bounds__(PLAN_THREADS) __attribute__((amdgpu_waves_per_eu(4)
     const float* al = a.alpha + s * a.TS;
     const float* be = a.beta + s * a.TS;
     uint8_t* Ps = a.plan + s * P * a.tp * REC;   // this stream's records [P][tp][rec]
-    const int BT = a.bt;
+    const int BT = a.bt, BTS = a.bts;
     // byte offset of the entry of token tt at writer / reader position k in a partition's records
-    auto w_at = [&](int64_t tt, int k) -> int64_t { return (tt / BT) * BT * REC + ((int64_t)k * BT + tt % BT) * 16; };
-    auto r_at = [&](int64_t tt, int k) -> int64_t {
-        return (tt / BT) * BT * REC + WB * BT + ((int64_t)k * BT + tt % BT) * 8;
+    // (blocks of BT tokens, a power of two: shifts, not divisions)
+    // (32-bit: the launch's chunking keeps a partition's records below 2 GiB)
+    const uint32_t REC32 = (uint32_t)REC, WB32 = (uint32_t)WB;
+    auto w_at = [&](int64_t tt, int k) -> uint32_t {
+        const uint32_t t = (uint32_t)tt;
+        return ((t >> BTS) << BTS) * REC32 + (((uint32_t)k << BTS) + (t & (uint32_t)(BT - 1))) * 16u;
     };
+    auto r_at = [&](int64_t tt, int k) -> uint32_t {
+        const uint32_t t = (uint32_t)tt;
+        return ((t >> BTS) << BTS) * REC32 + (WB32 << BTS) + (((uint32_t)k << BTS) + (t & (uint32_t)(BT - 1))) * 8u;
+    };
+    // ring slot of a token: x % ur by a multiply-high with ceil(2^32 / ur), exact for x < 2^32 / ur
+    // (x = a token of the launch: below 2^27, since the chunking keeps 16+ bytes per token of a
+    // stream's region below 2 GiB, and ur <= 31)
+    const uint32_t UR = (uint32_t)a.ur, URM = a.urm;
+    auto slot_of = [&](uint32_t x) -> uint32_t { return x - UR * __umulhi(x, URM); };
 
     for (int i = tid; i < HT_CAP / 4; i += PLAN_THREADS)
         reinterpret_cast<uint4*>(ht)[i] = make_uint4(HT_EMPTY, HT_EMPTY, HT_EMPTY, HT_EMPTY);
@@ -322,8 +336,7 @@ __global__ __launch_bounds__(PLAN_THREADS) __attribute__((amdgpu_waves_per_eu(4)
                     const int src = fwd_src(ht, bm, (uint32_t)row[u], cur - D, cur - (isw ? 1 : 0), pb, bp);
                     // LDS byte offset of the source row in the scan's ring (slot of its token, its rank)
                     const uint32_t roff =
-                        src < 0 ? 0u
-                                : ((uint32_t)(h0 + src) % (uint32_t)a.ur * (uint32_t)a.rpos + bp) * (uint32_t)a.rlane;
+                        src < 0 ? 0u : (slot_of((uint32_t)(h0 + src)) * (uint32_t)a.rpos + bp) * (uint32_t)a.rlane;
                     uint8_t* rec = Ps + (int64_t)part * a.tp * REC;
                     if (isw && a.form == 0) {
                         const float b = be[tt] * w[u], cw = al[tt] * (1.f - b);
@@ -1051,6 +1064,8 @@ hipError_t launch_scan_slab(const ScanArgs& a, const Cfg& c, hipStream_t st) {
         p.form = a.form;
         p.ur = SlabCfg<SL>::UR;      // the scan kernel's ring of written rows: token slots
         p.bt = entry_batch<SL>();    // tokens per block of entries
+        p.bts = p.bt == 4 ? 2 : p.bt == 2 ? 1 : 0;
+        p.urm = (uint32_t)((((uint64_t)1 << 32) + (uint64_t)p.ur - 1) / (uint64_t)p.ur);
         p.tp = (Tn + p.bt - 1) / p.bt * p.bt;
         p.rpos = g.NWW * g.G;        // write positions per slot
         p.rlane = (SL / 4) * 16;     // bytes per position: 16 per lane of a row segment
