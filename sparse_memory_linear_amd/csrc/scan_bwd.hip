@@ -572,13 +572,14 @@ int env_int(const char* name) {
 // 4-column ones with 256 workgroups; 32 streams: 16-column slabs as before),
 // else the widest that still gives 256 workgroups (one per CU: a second
 // workgroup on a CU stretches every token of both), else the one with the
-// most, and one partition: partitions
+// most, and one partition where that fills the CUs: partitions
 // multiply the wavefronts that step through every token, and with the token
 // loop's loads issued ahead that costs more than the extra rows in flight
 // bring (measured on the per-slot form: 16-column slabs without partitions
-// 16.4 ms against 19.2 ms for 32-column slabs in 2 partitions on 32 streams of
-// 8192 tokens). SDM_BWD_SLAB and SDM_BWD_PARTS (per-slot form only) force a
-// choice.
+// 16.2 ms against 20.4 ms for 32-column slabs in 2 partitions and 22.2 for
+// 16-column slabs in 2 on 32 streams of 8192 tokens). The exception, below:
+// half the CUs idle and two or more writer wavefronts. SDM_BWD_SLAB and
+// SDM_BWD_PARTS (per-slot form only) force a choice.
 struct BCfg {
     int S = 0, P = 1;
 };
@@ -602,7 +603,19 @@ BCfg bwd_cfg(int64_t NS, int W, int R, int dv, int form) {
         }
     }
     if (c.S == 0) return c;
-    if (form == 0 && (fp == 2 || fp == 4 || fp == 8 || fp == 16)) c.P = fp;
+    if (form == 0 && (fp == 2 || fp == 4 || fp == 8 || fp == 16)) {
+        c.P = fp;
+    } else if (form == 0 && fp == 0 && !fs) {
+        // few streams: where the layout has two or more writer wavefronts and
+        // half the CUs would idle, 2 row partitions fill them (long_context,
+        // 8-column slabs: 128 workgroups 160 ms, 2 partitions 123 ms; 4
+        // partitions 226 ms). With one writer wavefront the walk is bound by
+        // its fixed per-token steps and partitions do not help (large_table
+        // 46.9 against 47.1 ms, small 3.00 against 3.04 ms).
+        const BGeom g = bwd_geom(c.S, W, R);
+        const int64_t units = NS * (dv / c.S);
+        if (g.NWW >= 2 && units * 2 <= 256) c.P = 2;
+    }
     return c;
 }
 
