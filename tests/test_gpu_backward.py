@@ -320,3 +320,43 @@ def test_training_short_calls(T, form, oform):
     _, _, _, got, M_back = _gpu_train(c, dy, dM, form)
     _check_grads(f"T={T} {form}", got, ref, TOL_F32)
     assert np.array_equal(M_back.view(np.uint32), c["M_in"].view(np.uint32))
+
+
+def test_backward_long_context_layout():
+    """The long-context shape's backward layout (8 streams: 8-column slabs in 2
+    row partitions): with T = 8192 one stream takes the oracle's own slots and
+    is checked in full against the oracle; at the full T = 131072 (the launch
+    the training bench times) the undo must give back the initial table bit
+    for bit on every stream, with finite gradients."""
+    for T in (8192, 131072):
+        wl = inputs.get("long_context", T=T)
+        say(f"[backward long_context layout] B={wl.B} H={wl.H} T={wl.T}")
+        x = inputs.make_inputs(wl)
+        g = {k: v.to(DEV) for k, v in x.items()}
+        iw, ww, ir, wr = sdm.sdm_address(g["q_w"], g["q_r"], g["subkeys"], g["subkeys"], wl.W, wl.R)
+        b, h = 0, 5
+        if T == 8192:
+            q = lambda k: x[k][b:b + 1, h:h + 1]
+            oi, ow, _, _ = oracle.address(q("q_w"), x["subkeys"][h:h + 1], wl.W)
+            ri, rw, _, _ = oracle.address(q("q_r"), x["subkeys"][h:h + 1], wl.R)
+            iw[b, h] = _t(oi[0, 0]); ww[b, h] = _t(ow[0, 0]); ir[b, h] = _t(ri[0, 0]); wr[b, h] = _t(rw[0, 0])
+        dy, dM_out = _cotangents(17, wl.B, wl.H, wl.T, wl.N, wl.d_v)
+        M = sdm.sdm_state_init(g["M0"], wl.B)
+        M_in = M.cpu()
+        args = (iw, ww, ir, wr, g["alpha"], g["beta"], g["v"])
+        y, snap = sdm.sdm_scan_forward_save(*args, M, "eq4")
+        dM = _t(dM_out)
+        grads = sdm.sdm_scan_backward(*args, snap, _t(dy), M, dM, "eq4")
+        torch.cuda.synchronize()
+        del snap, y
+        assert torch.equal(M.cpu(), M_in)
+        assert all(bool(torch.isfinite(v).all()) for v in grads.values()) and bool(torch.isfinite(dM).all())
+        if T == 8192:
+            sl = lambda t: t[b:b + 1, h:h + 1]
+            ref = oracle.scan_backward(oi, ow, ri, rw, sl(x["alpha"]), sl(x["beta"]), sl(x["v"]),
+                                       x["M0"][h:h + 1][None].numpy(), sl(dy), sl(dM_out), form=oracle.EQ4)
+            got = {k: sl(v).cpu().numpy() for k, v in grads.items()}
+            got["dM_in"] = sl(dM).cpu().numpy()
+            _check_grads(f"long_context T={T} stream ({b},{h})", got, ref, TOL_BF16, TOL_SAME_INPUTS)
+        del grads, dM, M, g
+        torch.cuda.empty_cache()
