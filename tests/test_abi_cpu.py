@@ -136,12 +136,18 @@ def test_training_sizes_are_pure_host_logic(lib):
         return 4 * (nslab * NS * T * (W + R) + nslab * P * NS * T * 2 + (P * NS * T * dv if P > 1 else 0)
                     + NS * T * (W + 2 * R))
     # both forms take the widest slab with at most 8 wavefronts and at least 128
-    # workgroups, one partition: 32 streams -> 16-column slabs; 8 streams ->
-    # 8-column slabs; chunks of at most 2^31 / (W dv 4) tokens
+    # workgroups: 32 streams -> 16-column slabs, one partition; 8 streams ->
+    # 8-column slabs (128 workgroups, two writer wavefronts), where the per-slot
+    # form takes 2 row partitions; chunks of at most 2^31 / (W dv 4) tokens
     assert binding.sdm_scan_backward_workspace_bytes(4, 8, 8192, 64, 64, 128) == bwd(32, 8192, 16, 1)
-    assert binding.sdm_scan_backward_workspace_bytes(1, 8, 1000, 64, 64, 128) == bwd(8, 1000, 8, 1)
+    assert binding.sdm_scan_backward_workspace_bytes(1, 8, 1000, 64, 64, 128) == bwd(8, 1000, 8, 2)
     Tc = 0x7FFFFFFF // (64 * 128 * 4)
-    assert binding.sdm_scan_backward_workspace_bytes(1, 8, 131072, 64, 64, 128) == bwd(8, Tc, 8, 1)
+    assert binding.sdm_scan_backward_workspace_bytes(1, 8, 131072, 64, 64, 128) == bwd(8, Tc, 8, 2)
+    # small W, large R: the chunk is bounded by the W + 2R plan words per token, not
+    # by the pre-images (1 x 4 x 4 bytes): 2^31 / ((1 + 512) x 4) tokens
+    Tc = 0x7FFFFFFF // ((1 + 2 * 256) * 4)
+    assert binding.sdm_scan_backward_workspace_bytes(1, 1, 2_000_000, 1, 256, 4) == \
+        bwd(1, Tc, 4, 1, W=1, R=256, dv=4)
     # one stream of d_v = 512, W = R = 8: only 4-column slabs reach 128 workgroups
     assert binding.sdm_scan_backward_workspace_bytes(1, 1, 500, 8, 8, 512) == bwd(1, 500, 4, 1, W=8, R=8, dv=512)
     assert binding.sdm_scan_backward_workspace_bytes(0, 8, 100, 64, 64, 128) == 0
