@@ -136,9 +136,15 @@ __device__ __forceinline__ void for_chunks(int nch, F f) {
 // through get(g, e, key, id). Key 0 marks an absent candidate; ids are below
 // 2^18. Exactly k winners (k <= number of present candidates) are written in
 // candidate order to okey/oid[g*OSTR + 0..k).
+// tau0 / b0 (optional): bits of the k-th key known before the search — for
+// each token, its bits above some position equal tau0[g]'s (and tau0[g]'s lower
+// bits are 0); b0 is one bit at or above every token's first unknown bit. The
+// walk then starts at b0. (Walking a token's known bits again changes nothing:
+// a known 1 is taken at once, a known 0 would leave fewer than k keys.)
 template <int NT, int NCH, typename Get>
 __device__ __forceinline__ void wave_select(Get get, int nch_rt, int k, uint32_t* okey, uint32_t* oid,
-                                            int lane) {
+                                            int lane, const uint32_t* tau0 = nullptr,
+                                            uint32_t b0 = 0x80000000u) {
     // Radix select of the k-th largest key, most significant bit first: tau
     // keeps the bits fixed so far, cur = count(key >= tau) >= k. A bit is taken
     // when the count at tau with the bit set still reaches k. Once cur == k the
@@ -151,10 +157,10 @@ __device__ __forceinline__ void wave_select(Get get, int nch_rt, int k, uint32_t
     int cur[NT];
 #pragma unroll
     for (int g = 0; g < NT; ++g) {
-        tau[g] = 0u;
+        tau[g] = tau0 ? tau0[g] : 0u;
         cur[g] = -1;  // unknown, >= k
     }
-    for (uint32_t b = 0x80000000u; b != 0u; b >>= 1) {
+    for (uint32_t b = b0; b != 0u; b >>= 1) {
         int cnt[NT];
         uint32_t t[NT];
 #pragma unroll
@@ -215,15 +221,15 @@ __device__ __forceinline__ void wave_select(Get get, int nch_rt, int k, uint32_t
         for (int g = 0; g < NT; ++g) {
             th[g] = (uint32_t)__builtin_amdgcn_readfirstlane((int)tau[g]);
             sig[g] = 0u;
-            int gt = 0;
+            int gt = 0, eq = 0;
             for_chunks<NCH>(nch_rt, [&](int e) {
                 uint32_t kk, ii;
                 get(g, e, kk, ii);
                 gt += popc(__ballot(kk > th[g]));
+                eq += popc(__ballot(kk == th[g]));
             });
             need[g] = k - gt;
-            // cur = count(key >= tau), so cur - gt keys equal tau
-            if (((open >> g) & 1u) && cur[g] - gt > need[g]) cutm |= 1u << g;
+            if (((open >> g) & 1u) && eq > need[g]) cutm |= 1u << g;
         }
         if (cutm != 0u) {
             for (int bit = 17; bit >= 0; --bit) {
@@ -570,12 +576,37 @@ __global__ __launch_bounds__(NWA * 64) void address_kernel(AddressArgs a) {
                 ci[g][e] = __umul24(lid[(g * 2) * 64 + i], (uint32_t)n) + lid[(g * 2 + 1) * 64 + jj];
             }
         }
+        // Known leading bits of each token's k-th candidate key S_k: the pairs
+        // (i, 0), i < k, are all candidates, so S_k >= s_0[k-1] + s_1[0]
+        // (likewise s_0[0] + s_1[k-1]), and S_k <= s_0[0] + s_1[0]; the bits
+        // above the highest one where these two bounds differ are S_k's. (Only
+        // when k <= n: else fewer than k pairs have rank 0 in a half.)
+        uint32_t tau0[TG], bx = 0u;
+#pragma unroll
+        for (int g = 0; g < TG; ++g) {
+            tau0[g] = 0u;
+            if (k <= n) {
+                const float* l0 = ls + (g * 2) * 64;
+                const float* l1 = ls + (g * 2 + 1) * 64;
+                const uint32_t lo_a = ord_key(l0[k - 1] + l1[0]), lo_b = ord_key(l0[0] + l1[k - 1]);
+                const uint32_t lo = lo_a > lo_b ? lo_a : lo_b, hi = ord_key(l0[0] + l1[0]);
+                const uint32_t d = lo ^ hi;                             // lo <= hi
+                const uint32_t top = d ? 0x80000000u >> __clz(d) : 0u;  // highest differing bit
+                tau0[g] = lo & (top ? ~((top << 1) - 1u) : ~0u);         // the bits above it (all if none)
+                bx |= top ? top : 1u;
+                tau0[g] = (uint32_t)__builtin_amdgcn_readfirstlane((int)tau0[g]);
+            } else {
+                bx |= 0x80000000u;
+            }
+        }
+        bx = (uint32_t)__builtin_amdgcn_readfirstlane((int)bx);
+        const uint32_t b0 = 0x80000000u >> __clz(bx);  // the highest start bit of the tokens
         wave_select<TG, EC>(
             [&](int g, int e, uint32_t& kk, uint32_t& ii) {
                 kk = ck[g][e];
                 ii = ci[g][e];
             },
-            EC, k, bkey, bid, lane);
+            EC, k, bkey, bid, lane, tau0, b0);
         uint64_t x[TG];
 #pragma unroll
         for (int g = 0; g < TG; ++g) x[g] = lane < k ? composite(bkey[g * OSTR + lane], bid[g * OSTR + lane]) : 0ull;
