@@ -542,19 +542,54 @@ __global__ __launch_bounds__(NWA * 64) void address_kernel(AddressArgs a) {
                     keys[j][g][e] = aa < n ? ord_key(s[aa]) : 0u;
                 }
             }
+        uint32_t kth0[TG];  // half 0's k_h-th key, per token
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
+            // Half 1's scores come from the same subkey distribution and a
+            // half-query of similar norm, so its k_h-th key is usually near half
+            // 0's: two counts test the bracket [0.75 x, 1.35 x) around it (x the
+            // half-0 value) and, when it holds, the select starts below the
+            // bracket's common leading bits (else, for that token, at bit 31).
+            uint32_t tau0[TG], b0 = 0x80000000u;
+            if (j == 1) {
+                uint32_t bx = 0u;
+#pragma unroll
+                for (int g = 0; g < TG; ++g) {
+                    const float f = key_float(kth0[g]), m = fabsf(f);
+                    const uint32_t klo = ord_key(f - 0.25f * m), khi = ord_key(f + 0.35f * m);
+                    int clo = 0, chi = 0;
+#pragma unroll
+                    for (int e = 0; e < EH; ++e) {
+                        clo += popc(__ballot(keys[1][g][e] >= klo));
+                        chi += popc(__ballot(keys[1][g][e] >= khi));
+                    }
+                    tau0[g] = 0u;
+                    uint32_t top = 0x80000000u;
+                    if (clo >= kh && chi < kh && khi > klo) {  // klo <= S_k <= khi - 1
+                        const uint32_t d = klo ^ (khi - 1u);
+                        top = d ? 0x80000000u >> __clz(d) : 1u;
+                        tau0[g] = klo & (d ? ~((top << 1) - 1u) : ~0u);
+                    }
+                    bx |= top;
+                }
+                b0 = 0x80000000u >> __clz(bx);
+            }
             wave_select<TG, EH>(
                 [&](int g, int e, uint32_t& kk, uint32_t& ii) {
                     kk = keys[j][g][e];
                     ii = (uint32_t)(e * 64 + lane);
                 },
-                EH, kh, bkey, bid, lane);
+                EH, kh, bkey, bid, lane, j == 1 ? tau0 : nullptr, b0);
             uint64_t x[TG];
 #pragma unroll
             for (int g = 0; g < TG; ++g)
                 x[g] = lane < kh ? composite(bkey[g * OSTR + lane], bid[g * OSTR + lane]) : 0ull;
             wave_sort_desc<TG>(x, lane);
+            if (j == 0) {
+#pragma unroll
+                for (int g = 0; g < TG; ++g)
+                    kth0[g] = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(x[g] >> 32), kh - 1);
+            }
 #pragma unroll
             for (int g = 0; g < TG; ++g)
                 if (lane < kh) {
