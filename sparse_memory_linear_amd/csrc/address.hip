@@ -315,6 +315,83 @@ __device__ __forceinline__ void wave_sort_desc(uint64_t (&x)[NT], int lane) {
     sort_stage<4, 64>(x, lane); sort_stage<2, 64>(x, lane); sort_stage<1, 64>(x, lane);
 }
 
+// The same network on one 32-bit word per lane.
+template <int J, int K, int NT>
+__device__ __forceinline__ void sort_stage32(uint32_t (&x)[NT], int lane) {
+    constexpr uint64_t KMIN = keep_min_lanes<J, K>();
+#pragma unroll
+    for (int g = 0; g < NT; ++g) {
+        if constexpr (J >= 16) {
+            uint32_t a0, a1;
+            if constexpr (J == 16) {
+                const auto p = __builtin_amdgcn_permlane16_swap(x[g], x[g], false, false);
+                a0 = p[0]; a1 = p[1];
+            } else {
+                const auto p = __builtin_amdgcn_permlane32_swap(x[g], x[g], false, false);
+                a0 = p[0]; a1 = p[1];
+            }
+            const bool take0 = __builtin_amdgcn_inverse_ballot_w64(__ballot(a0 > a1) ^ KMIN);
+            x[g] = take0 ? a0 : a1;
+        } else {
+            const uint32_t o = xlane<J>(x[g], lane);
+            const bool keep = __builtin_amdgcn_inverse_ballot_w64(__ballot(x[g] > o) ^ KMIN);
+            x[g] = keep ? x[g] : o;
+        }
+    }
+}
+
+template <int NT>
+__device__ __forceinline__ void wave_sort_desc32(uint32_t (&x)[NT], int lane) {
+    sort_stage32<1, 2>(x, lane);
+    sort_stage32<2, 4>(x, lane); sort_stage32<1, 4>(x, lane);
+    sort_stage32<4, 8>(x, lane); sort_stage32<2, 8>(x, lane); sort_stage32<1, 8>(x, lane);
+    sort_stage32<8, 16>(x, lane); sort_stage32<4, 16>(x, lane); sort_stage32<2, 16>(x, lane);
+    sort_stage32<1, 16>(x, lane);
+    sort_stage32<16, 32>(x, lane); sort_stage32<8, 32>(x, lane); sort_stage32<4, 32>(x, lane);
+    sort_stage32<2, 32>(x, lane); sort_stage32<1, 32>(x, lane);
+    sort_stage32<32, 64>(x, lane); sort_stage32<16, 64>(x, lane); sort_stage32<8, 64>(x, lane);
+    sort_stage32<4, 64>(x, lane); sort_stage32<2, 64>(x, lane); sort_stage32<1, 64>(x, lane);
+}
+
+__device__ __forceinline__ uint64_t composite(uint32_t key, uint32_t id) {
+    return ((uint64_t)key << 32) | (uint64_t)(0xFFFFFFFFu - id);
+}
+
+// The k winners of a select (okey/oid rows, in candidate order) sorted by (key
+// desc, id asc) into x[g] (composite words, lanes >= k zero). A 32-bit network
+// sorts the keys with their low 6 bits replaced by 63 - (candidate position):
+// that orders every pair whose keys differ above those bits, and equal
+// truncated keys by position. The full (key, id) words, gathered by position,
+// are then checked to be strictly descending over the lanes; a token where some
+// neighbours are not (keys equal in their top 26 bits but not below, or equal
+// keys whose ids run against the candidate order) is sorted again with the
+// 64-bit network.
+template <int NT>
+__device__ __forceinline__ void sort_winners(uint64_t (&x)[NT], const uint32_t* okey, const uint32_t* oid, int k,
+                                             int lane) {
+    uint32_t v[NT];
+#pragma unroll
+    for (int g = 0; g < NT; ++g) v[g] = lane < k ? (okey[g * OSTR + lane] & ~63u) | (63u - (uint32_t)lane) : 0u;
+    wave_sort_desc32<NT>(v, lane);
+#pragma unroll
+    for (int g = 0; g < NT; ++g) {
+        const uint32_t p = 63u - (v[g] & 63u);
+        x[g] = lane < k ? composite(okey[g * OSTR + p], oid[g * OSTR + p]) : 0ull;
+        // lane - 1's word (DPP wave shift right by one; lane 0 keeps its own)
+        const uint32_t plo = (uint32_t)__builtin_amdgcn_update_dpp((int)(uint32_t)x[g], (int)(uint32_t)x[g], 0x138,
+                                                                   0xF, 0xF, false);
+        const uint32_t phi = (uint32_t)__builtin_amdgcn_update_dpp((int)(uint32_t)(x[g] >> 32),
+                                                                   (int)(uint32_t)(x[g] >> 32), 0x138, 0xF, 0xF,
+                                                                   false);
+        const uint64_t prev = ((uint64_t)phi << 32) | plo;
+        if (__ballot(lane >= 1 && lane < k && !(prev > x[g])) != 0ull) {
+            uint64_t y1[1] = {lane < k ? composite(okey[g * OSTR + lane], oid[g * OSTR + lane]) : 0ull};
+            wave_sort_desc<1>(y1, lane);
+            x[g] = y1[0];
+        }
+    }
+}
+
 // Floats per wavefront block of LDS: the half-scores of TG tokens or the sorted
 // lists + select buffers, whichever is larger.
 __host__ __device__ inline int block_floats(int n) {
@@ -322,9 +399,6 @@ __host__ __device__ inline int block_floats(int n) {
     return scores > lists ? scores : lists;
 }
 
-__device__ __forceinline__ uint64_t composite(uint32_t key, uint32_t id) {
-    return ((uint64_t)key << 32) | (uint64_t)(0xFFFFFFFFu - id);
-}
 
 // Sum of squares of the 8 bf16 (packed in a uint4) or 2 fp32 elements a lane loads.
 __device__ __forceinline__ float sumsq(const uint4& x) {
@@ -581,10 +655,7 @@ __global__ __launch_bounds__(NWA * 64) void address_kernel(AddressArgs a) {
                 },
                 EH, kh, bkey, bid, lane, j == 1 ? tau0 : nullptr, b0);
             uint64_t x[TG];
-#pragma unroll
-            for (int g = 0; g < TG; ++g)
-                x[g] = lane < kh ? composite(bkey[g * OSTR + lane], bid[g * OSTR + lane]) : 0ull;
-            wave_sort_desc<TG>(x, lane);
+            sort_winners<TG>(x, bkey, bid, kh, lane);
             if (j == 0) {
 #pragma unroll
                 for (int g = 0; g < TG; ++g)
@@ -643,9 +714,7 @@ __global__ __launch_bounds__(NWA * 64) void address_kernel(AddressArgs a) {
             },
             EC, k, bkey, bid, lane, tau0, b0);
         uint64_t x[TG];
-#pragma unroll
-        for (int g = 0; g < TG; ++g) x[g] = lane < k ? composite(bkey[g * OSTR + lane], bid[g * OSTR + lane]) : 0ull;
-        wave_sort_desc<TG>(x, lane);
+        sort_winners<TG>(x, bkey, bid, k, lane);
 
         // certificate: every pruned pair must score strictly below the k-th winner
 #pragma unroll
