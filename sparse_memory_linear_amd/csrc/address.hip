@@ -416,8 +416,14 @@ __device__ __forceinline__ float sumsq(const float2& x) { return fmaf(x.y, x.y, 
 
 constexpr float IDW_EPS = 1e-3f;  // the constant FwPKM adds to the squared distance
 
+// Up to n = 256: 8 wavefronts per SIMD (four workgroups per CU). The selection
+// is bound by instruction issue, and more wavefronts keep both issue ports
+// busier (gdn_matched 1.18 -> 1.11 ms against the register budget of 6 per
+// SIMD). At n = 512 the contraction (d_h up to 256, 8 tiles a wavefront) takes
+// most of the time and keeps all its tiles in flight instead (large_table:
+// 2.24 ms, against 3.57 ms with tiles in groups of 2 for 8 per SIMD).
 template <bool BF16, int EH, bool IDW>
-__global__ __launch_bounds__(NWA * 64) void address_kernel(AddressArgs a) {
+__global__ __launch_bounds__(NWA * 64) __attribute__((amdgpu_waves_per_eu(EH <= 4 ? 8 : 1))) void address_kernel(AddressArgs a) {
     extern __shared__ __align__(16) uint32_t smem[];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int n = a.n, dh = a.dh;
@@ -455,112 +461,123 @@ __global__ __launch_bounds__(NWA * 64) void address_kernel(AddressArgs a) {
     uint32_t* bid = bkey + TG * OSTR;                 // [TG][OSTR]
 
     // ---------------- a1: half-scores on MFMA ----------------
-    // The 2 * n/16 subkey tiles are dealt round-robin to the wavefronts. For each
-    // k-step a wavefront loads its tokens' half-queries once and the subkeys of
-    // all its tiles together, so the loads of a step are in flight at once.
+    // The 2 * n/16 subkey tiles are dealt round-robin to the wavefronts. A
+    // wavefront takes its tiles in groups of TPG: for each k-step it loads its
+    // tokens' half-queries and the subkeys of the group's tiles together, so the
+    // loads of a step are in flight at once; up to n = 256, groups of 2 keep the
+    // accumulators and subkey registers of only 2 tiles live, which keeps the
+    // kernel within the 64 VGPRs of 8 wavefronts per SIMD.
     constexpr int TPW = (2 * (64 * EH / 16) + NWA - 1) / NWA;  // most tiles per wavefront
+    constexpr int TPG = EH > 4 || TPW < 2 ? TPW : 2;           // tiles per group
     const int nt16 = n / 16, ntiles = 2 * nt16;
     const int m16 = lane & 15, g4 = lane >> 4;
     const int64_t tq = u0 + m16;
     const bool tok_ok = tq < UT;
-    f32x4_t acc[TPW];
-    float qsq[2] = {0.f, 0.f}, ksq[TPW];  // IDW: partial squared norms of what this lane loads
-    int64_t krow[TPW];  // element offset of this lane's subkey row of each tile
-#pragma unroll
-    for (int i = 0; i < TPW; ++i) {
-        acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        ksq[i] = 0.f;
-        const int tile = wave + i * NWA, j = tile / nt16, a0 = (tile % nt16) * 16;
-        krow[i] = (((int64_t)h * 2 + j) * n + a0 + m16) * dh;
-    }
     const int64_t qrow = row_of(tok_ok ? tq : 0) * 2 * dh;  // half 0; half 1 follows
-    if constexpr (BF16) {
-        const uint16_t* q = static_cast<const uint16_t*>(a.q[br]) + qrow;
-        const uint16_t* kp = static_cast<const uint16_t*>(a.K[br]);
-        for (int c0 = 0; c0 < dh; c0 += 32) {
-            uint4 qa[2], kb[TPW];
 #pragma unroll
-            for (int jj = 0; jj < 2; ++jj)
-                qa[jj] = tok_ok ? *reinterpret_cast<const uint4*>(q + jj * dh + c0 + g4 * 8) : make_uint4(0u, 0u, 0u, 0u);
+    for (int grp = 0; grp < TPW; grp += TPG) {  // tiles past ntiles are skipped inside
+        f32x4_t acc[TPG];
+        float qsq[2] = {0.f, 0.f}, ksq[TPG];  // IDW: partial squared norms of what this lane loads
+        uint32_t krow[TPG];  // element offset of this lane's subkey row of each tile within the head's table
 #pragma unroll
-            for (int i = 0; i < TPW; ++i)
-                if (wave + i * NWA < ntiles) kb[i] = *reinterpret_cast<const uint4*>(kp + krow[i] + c0 + g4 * 8);
-            if constexpr (IDW) {
-                qsq[0] += sumsq(qa[0]);
-                qsq[1] += sumsq(qa[1]);
-#pragma unroll
-                for (int i = 0; i < TPW; ++i)
-                    if (wave + i * NWA < ntiles) ksq[i] += sumsq(kb[i]);
-            }
-#pragma unroll
-            for (int i = 0; i < TPW; ++i) {
-                const int tile = wave + i * NWA;
-                if (tile < ntiles)
-                    acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        __builtin_bit_cast(bf16x8_t, tile < nt16 ? qa[0] : qa[1]), __builtin_bit_cast(bf16x8_t, kb[i]),
-                        acc[i], 0, 0, 0);
-            }
+        for (int i = 0; i < TPG; ++i) {
+            acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            ksq[i] = 0.f;
+            const int tile = wave + (grp + i) * NWA, j = tile / nt16, a0 = (tile % nt16) * 16;
+            krow[i] = (uint32_t)((j * n + a0 + m16) * dh);  // < 2 * 512 * 256
         }
-    } else {
-        const float* q = static_cast<const float*>(a.q[br]) + qrow;
-        const float* kp = static_cast<const float*>(a.K[br]);
-        for (int c0 = 0; c0 < dh; c0 += 8) {
-            float2 qa[2], kb[TPW];
+        if constexpr (BF16) {
+            const uint16_t* q = static_cast<const uint16_t*>(a.q[br]) + qrow;
+            const uint16_t* kp = static_cast<const uint16_t*>(a.K[br]) + (int64_t)h * 2 * n * dh;  // this head's
+            for (int c0 = 0; c0 < dh; c0 += 32) {
+                uint4 qa[2], kb[TPG];
 #pragma unroll
-            for (int jj = 0; jj < 2; ++jj)
-                qa[jj] = tok_ok ? *reinterpret_cast<const float2*>(q + jj * dh + c0 + g4 * 2) : make_float2(0.f, 0.f);
+                for (int jj = 0; jj < 2; ++jj)
+                    qa[jj] = tok_ok ? *reinterpret_cast<const uint4*>(q + jj * dh + c0 + g4 * 8)
+                                    : make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
-            for (int i = 0; i < TPW; ++i)
-                if (wave + i * NWA < ntiles) kb[i] = *reinterpret_cast<const float2*>(kp + krow[i] + c0 + g4 * 2);
-            if constexpr (IDW) {
-                qsq[0] += sumsq(qa[0]);
-                qsq[1] += sumsq(qa[1]);
-#pragma unroll
-                for (int i = 0; i < TPW; ++i)
-                    if (wave + i * NWA < ntiles) ksq[i] += sumsq(kb[i]);
-            }
-#pragma unroll
-            for (int i = 0; i < TPW; ++i) {
-                const int tile = wave + i * NWA;
-                if (tile < ntiles) {
-                    const float2 qv = tile < nt16 ? qa[0] : qa[1];
-                    acc[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(qv.x, kb[i].x, acc[i], 0, 0, 0);
-                    acc[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(qv.y, kb[i].y, acc[i], 0, 0, 0);
-                }
-            }
-        }
-    }
-    // D layout: lane holds tokens 4*(lane/16)+i of subkey column lane%16
-    float qn[2][4];  // IDW: ||q||^2 of the 4 tokens of this lane's D rows, per half
-    if constexpr (IDW) {
-        // lanes m16 + 16 g4 (g4 = 0..3) loaded disjoint chunks of token m16 / subkey row m16
-#pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-            float t = qsq[jj];
-            t += xlanef<16>(t, lane);
-            t += xlanef<32>(t, lane);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) qn[jj][r] = __shfl(t, g4 * 4 + r);
-        }
-#pragma unroll
-        for (int i = 0; i < TPW; ++i) {
-            ksq[i] += xlanef<16>(ksq[i], lane);
-            ksq[i] += xlanef<32>(ksq[i], lane);
-        }
-    }
-#pragma unroll
-    for (int i = 0; i < TPW; ++i) {
-        const int tile = wave + i * NWA;
-        if (tile < ntiles) {
-            const int j = tile / nt16, a0 = (tile % nt16) * 16;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                float sc = acc[i][r];
+                for (int i = 0; i < TPG; ++i)
+                    if (wave + (grp + i) * NWA < ntiles)
+                        kb[i] = *reinterpret_cast<const uint4*>(kp + krow[i] + c0 + g4 * 8);
                 if constexpr (IDW) {
-                    const float d2 = fmaf(-2.f, sc, (j ? qn[1][r] : qn[0][r]) + ksq[i]);
-                    sc = -logf(IDW_EPS + fmaxf(d2, 0.f));
+                    qsq[0] += sumsq(qa[0]);
+                    qsq[1] += sumsq(qa[1]);
+#pragma unroll
+                    for (int i = 0; i < TPG; ++i)
+                        if (wave + (grp + i) * NWA < ntiles) ksq[i] += sumsq(kb[i]);
                 }
-                sc_tok(g4 * 4 + r)[j * n + a0 + m16] = sc;
+#pragma unroll
+                for (int i = 0; i < TPG; ++i) {
+                    const int tile = wave + (grp + i) * NWA;
+                    if (tile < ntiles)
+                        acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            __builtin_bit_cast(bf16x8_t, tile < nt16 ? qa[0] : qa[1]),
+                            __builtin_bit_cast(bf16x8_t, kb[i]), acc[i], 0, 0, 0);
+                }
+            }
+        } else {
+            const float* q = static_cast<const float*>(a.q[br]) + qrow;
+            const float* kp = static_cast<const float*>(a.K[br]) + (int64_t)h * 2 * n * dh;  // this head's table
+            for (int c0 = 0; c0 < dh; c0 += 8) {
+                float2 qa[2], kb[TPG];
+#pragma unroll
+                for (int jj = 0; jj < 2; ++jj)
+                    qa[jj] = tok_ok ? *reinterpret_cast<const float2*>(q + jj * dh + c0 + g4 * 2)
+                                    : make_float2(0.f, 0.f);
+#pragma unroll
+                for (int i = 0; i < TPG; ++i)
+                    if (wave + (grp + i) * NWA < ntiles)
+                        kb[i] = *reinterpret_cast<const float2*>(kp + krow[i] + c0 + g4 * 2);
+                if constexpr (IDW) {
+                    qsq[0] += sumsq(qa[0]);
+                    qsq[1] += sumsq(qa[1]);
+#pragma unroll
+                    for (int i = 0; i < TPG; ++i)
+                        if (wave + (grp + i) * NWA < ntiles) ksq[i] += sumsq(kb[i]);
+                }
+#pragma unroll
+                for (int i = 0; i < TPG; ++i) {
+                    const int tile = wave + (grp + i) * NWA;
+                    if (tile < ntiles) {
+                        const float2 qv = tile < nt16 ? qa[0] : qa[1];
+                        acc[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(qv.x, kb[i].x, acc[i], 0, 0, 0);
+                        acc[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(qv.y, kb[i].y, acc[i], 0, 0, 0);
+                    }
+                }
+            }
+        }
+        // D layout: lane holds tokens 4*(lane/16)+i of subkey column lane%16
+        float qn[2][4];  // IDW: ||q||^2 of the 4 tokens of this lane's D rows, per half
+        if constexpr (IDW) {
+            // lanes m16 + 16 g4 (g4 = 0..3) loaded disjoint chunks of token m16 / subkey row m16
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj) {
+                float t = qsq[jj];
+                t += xlanef<16>(t, lane);
+                t += xlanef<32>(t, lane);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) qn[jj][r] = __shfl(t, g4 * 4 + r);
+            }
+#pragma unroll
+            for (int i = 0; i < TPG; ++i) {
+                ksq[i] += xlanef<16>(ksq[i], lane);
+                ksq[i] += xlanef<32>(ksq[i], lane);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < TPG; ++i) {
+            const int tile = wave + (grp + i) * NWA;
+            if (tile < ntiles) {
+                const int j = tile / nt16, a0 = (tile % nt16) * 16;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    float sc = acc[i][r];
+                    if constexpr (IDW) {
+                        const float d2 = fmaf(-2.f, sc, (j ? qn[1][r] : qn[0][r]) + ksq[i]);
+                        sc = -logf(IDW_EPS + fmaxf(d2, 0.f));
+                    }
+                    sc_tok(g4 * 4 + r)[j * n + a0 + m16] = sc;
+                }
             }
         }
     }
