@@ -211,6 +211,11 @@ constexpr int BWD_D_DEEP = 4;
 constexpr int BWD_NW_DEEP = 8;
 static_assert(BWD_D_DEEP <= 7, "plan words keep the distance in 3 bits");
 
+template <bool B>
+struct BRole {
+    static constexpr bool value = B;
+};
+
 __device__ __forceinline__ uint32_t ld_u1(rsrc_t r, uint32_t vo, uint32_t so) {
     return __builtin_amdgcn_raw_buffer_load_b32(r, (int)vo, (int)so, 0);
 }
@@ -307,38 +312,45 @@ __global__ __launch_bounds__(NWM * 64) void scan_backward_kernel(BwdKArgs a) {
         if constexpr (VBF16) return make_int2(__float_as_int(y.x), __float_as_int(y.y));
         else return y;
     };
-    // Every load below is issued by every lane of both wavefront roles (a lane
-    // without the access gets an out-of-range offset), so the loads in flight
-    // per token are the same on every path.
-    auto fetch_ad = [&](int tk) -> Ad {
+    // Each role (WR: writer wavefronts) issues only the loads it uses, the same
+    // ones for every token, so the loads in flight per token are the same on
+    // every path of that role's loop (a lane without the access gets an
+    // out-of-range offset).
+    auto fetch_ad = [&](auto wr_c, int tk) -> Ad {
+        constexpr bool WR = decltype(wr_c)::value;
         Ad d;
         const int32_t row = (int32_t)ld_u1(Rix, lane_k, (uint32_t)tk * (uint32_t)K * 4u);
         d.row = has ? row : -1;
         d.gs = ld_u1(Rpl, lane_pg, (uint32_t)tk * (uint32_t)RW * 4u);
-        d.ms = ld_u1(Rpl, lane_pm, (uint32_t)tk * (uint32_t)RW * 4u);
+        if constexpr (WR) d.ms = 0u;
+        else d.ms = ld_u1(Rpl, lane_pm, (uint32_t)tk * (uint32_t)RW * 4u);
         return d;
     };
-    auto fetch_va = [&](int tk, const Ad& d) -> Va {
+    auto fetch_va = [&](auto wr_c, int tk, const Ad& d) -> Va {
+        constexpr bool WR = decltype(wr_c)::value;
         Va x;
         const uint32_t off = off_of(d.row);
         x.w = __uint_as_float(ld_u1(Rwx, lane_k, (uint32_t)tk * (uint32_t)K * 4u));
-        x.al = __uint_as_float(ld_u1(Ral, 0u, (uint32_t)tk * 4u));
-        x.be = __uint_as_float(ld_u1(Rbe, 0u, (uint32_t)tk * 4u));
         x.g = ld_f4(Rg, (d.gs & BSRC_ON) ? OOB : off, 0u);
-        const V4 vv = VL::load(Rv, writer ? v_off : OOB, (uint32_t)tk * vstride);
-        const float4 sn = ld_f4(Rs, writer ? s_lane : OOB, (uint32_t)tk * sstride);
-        const float4 dy = ld_f4(Rd, writer ? OOB : col4, (uint32_t)tk * dv4);
-        // a read's M_t: from the table, or from a later write's pre-image (the
-        // other load's offset is out of range: it is dropped)
-        const bool from_pre = !writer && (d.ms & BSRC_ON) && off != OOB;
-        const uint32_t dd = (d.ms >> BSRC_DSHIFT) & 7u, sp = d.ms & BSRC_POS;
-        const float4 mt = ld_f4(Rm, (writer || from_pre) ? OOB : off, 0u);
-        const float4 mp = ld_f4(Rs, from_pre ? (uint32_t)(tk + (int)dd) * sstride + sp * dv4 + col4 : OOB, 0u);
-        float4 vf;
-        if constexpr (VBF16) vf = make_float4(__int_as_float(vv.x), __int_as_float(vv.y), 0.f, 0.f);
-        else vf = vv;
-        x.x = writer ? sn : dy;
-        x.y = writer ? vf : (from_pre ? mp : mt);
+        if constexpr (WR) {
+            x.al = __uint_as_float(ld_u1(Ral, 0u, (uint32_t)tk * 4u));
+            x.be = __uint_as_float(ld_u1(Rbe, 0u, (uint32_t)tk * 4u));
+            const V4 vv = VL::load(Rv, v_off, (uint32_t)tk * vstride);
+            x.x = ld_f4(Rs, s_lane, (uint32_t)tk * sstride);
+            if constexpr (VBF16) x.y = make_float4(__int_as_float(vv.x), __int_as_float(vv.y), 0.f, 0.f);
+            else x.y = vv;
+        } else {
+            x.al = 0.f;
+            x.be = 0.f;
+            x.x = ld_f4(Rd, col4, (uint32_t)tk * dv4);
+            // a read's M_t: from the table, or from a later write's pre-image (the
+            // other load's offset is out of range: it is dropped)
+            const bool from_pre = (d.ms & BSRC_ON) && off != OOB;
+            const uint32_t dd = (d.ms >> BSRC_DSHIFT) & 7u, sp = d.ms & BSRC_POS;
+            const float4 mt = ld_f4(Rm, from_pre ? OOB : off, 0u);
+            const float4 mp = ld_f4(Rs, from_pre ? (uint32_t)(tk + (int)dd) * sstride + sp * dv4 + col4 : OOB, 0u);
+            x.y = from_pre ? mp : mt;
+        }
         return x;
     };
 
@@ -379,7 +391,8 @@ __global__ __launch_bounds__(NWM * 64) void scan_backward_kernel(BwdKArgs a) {
     }
 
     int slot = (T - 1) % UR;  // LDS ring slot of the token being processed
-    auto process = [&](int tl, const Ad& d, const Va& x) {
+    auto process = [&](auto wr_c, int tl, const Ad& d, const Va& x) {
+        constexpr bool WR = decltype(wr_c)::value;
         const int32_t row = d.row;
         const uint32_t off = off_of(row);
         const float w = off == OOB ? 0.f : x.w, al = x.al, be = x.be;
@@ -389,7 +402,7 @@ __global__ __launch_bounds__(NWM * 64) void scan_backward_kernel(BwdKArgs a) {
         if (fslot >= UR) fslot -= UR;
         const int fpos = (int)(d.gs & BSRC_POS);
         const bool own = owns_pos(row, off) && cc == 0;
-        if (writer) {
+        if constexpr (WR) {
             const float4 m = x.x;  // the pre-image M_{t-1}[i]
             const int par = tl & 1;
             __syncthreads();       // B1: this token's readers' new G values are in the ring
@@ -463,32 +476,37 @@ __global__ __launch_bounds__(NWM * 64) void scan_backward_kernel(BwdKArgs a) {
     };
 
     // Main loop: U tokens per trip, fully unrolled so the register rings are
-    // statically indexed; the token being processed is tl = T - 1 - k.
-    int k_done = 0;
-    if (T >= U) {
-        Ad ad[U];
-        Va va[UP];
+    // statically indexed; the token being processed is tl = T - 1 - k. Each role
+    // runs its own copy.
+    auto run = [&](auto wr_c) {
+        int k_done = 0;
+        if (T >= U) {
+            Ad ad[U];
+            Va va[UP];
 #pragma unroll
-        for (int q = 0; q < D + DM; ++q) ad[q] = fetch_ad(T - 1 - q);
+            for (int q = 0; q < D + DM; ++q) ad[q] = fetch_ad(wr_c, T - 1 - q);
 #pragma unroll
-        for (int q = 0; q < D; ++q) va[q] = fetch_va(T - 1 - q, ad[q]);
-        for (int k0 = 0; k0 + U <= T; k0 += U) {
+            for (int q = 0; q < D; ++q) va[q] = fetch_va(wr_c, T - 1 - q, ad[q]);
+            for (int k0 = 0; k0 + U <= T; k0 += U) {
 #pragma unroll
-            for (int j = 0; j < U; ++j) {
-                const int tl = T - 1 - (k0 + j);
-                // early loads of tokens before 0 fetch token 0 again, unused
-                ad[(j + D + DM) % U] = fetch_ad(tl - D - DM >= 0 ? tl - D - DM : 0);
-                va[(j + D) % UP] = fetch_va(tl - D >= 0 ? tl - D : 0, ad[(j + D) % U]);
-                process(tl, ad[j], va[j % UP]);
+                for (int j = 0; j < U; ++j) {
+                    const int tl = T - 1 - (k0 + j);
+                    // early loads of tokens before 0 fetch token 0 again, unused
+                    ad[(j + D + DM) % U] = fetch_ad(wr_c, tl - D - DM >= 0 ? tl - D - DM : 0);
+                    va[(j + D) % UP] = fetch_va(wr_c, tl - D >= 0 ? tl - D : 0, ad[(j + D) % U]);
+                    process(wr_c, tl, ad[j], va[j % UP]);
+                }
             }
+            k_done = (T / U) * U;
         }
-        k_done = (T / U) * U;
-    }
-    for (int k = k_done; k < T; ++k) {  // the rest: loads right before use
-        const int tl = T - 1 - k;
-        const Ad d = fetch_ad(tl);
-        process(tl, d, fetch_va(tl, d));
-    }
+        for (int k = k_done; k < T; ++k) {  // the rest: loads right before use
+            const int tl = T - 1 - k;
+            const Ad d = fetch_ad(wr_c, tl);
+            process(wr_c, tl, d, fetch_va(wr_c, tl, d));
+        }
+    };
+    if (writer) run(BRole<true>{});
+    else run(BRole<false>{});
     if (wave == NWW && !xf) finish(0);
 }
 
