@@ -24,8 +24,11 @@
 // floats): writer wavefronts hold the W write rows of a token (G rows each, one
 // 16-byte segment per lane), reader wavefronts the R read rows. Each token's
 // loads (index words, weights, gates, v or dy, pre-images and the table rows)
-// are issued D = 2 tokens before the token is processed, so the walk is not one
-// memory round trip per token. Rows that a token of that window will still
+// are issued D tokens before the token is processed, so the walk is not one
+// memory round trip per token. A write whose row the same token reads adds
+// that read's term itself, so the reads and writes of one token run side by
+// side and one workgroup barrier per token (two for the shared-residual form)
+// orders the walk. Rows that a token of that window will still
 // change are not taken from memory: a planner kernel resolves, from the
 // indices alone, where each access finds its row instead (the adjoint row from
 // an LDS ring of the rows the nearest later toucher produced; a read's table
@@ -37,7 +40,7 @@
 // sums: each workgroup writes its slab's partial sums and a second kernel adds
 // them over the slabs in slab order (deterministic).
 //
-// Row partitions (per-slot form, on request). The per-slot write never couples
+// Row partitions (per-slot form). The per-slot write never couples
 // two rows, so the rows of a stream's table can be split into P partitions by a
 // hash of the row index, each walked by its own workgroups, which take the
 // accesses of their partition and leave the other lanes idle. dv_t and the
@@ -79,16 +82,27 @@ __device__ __forceinline__ int row_part(uint32_t row, int pshift) {
 // every access of token u a planner finds, from the indices alone:
 //   G source: the token of (u, u+D] nearest to u that touches the row; the
 //     row's adjoint after that token (its writer's new G if it writes the row,
-//     else its reader's) comes from an LDS ring. A write whose row the same
-//     token also reads takes that reader's new G (distance 0).
-//   M source (reads): the token of (u, u+D] nearest to u that writes the row;
-//     the row's state after token u is that write's pre-image, read from the
-//     forward's stored pre-images (which nothing modifies) instead of the table.
+//     else its reader's) comes from an LDS ring.
+//   Same-token pairs: a write whose row the same token also reads adds that
+//     read's r_q dy_u itself (the read position q is in its word), and that
+//     read's new G is marked superseded (the write's replaces it), so the
+//     reads and writes of one token need no ordering between them.
+//   M source (reads): the token of (u, u+D+1] nearest to u that writes the
+//     row; the row's state after token u is that write's pre-image, read from
+//     the forward's stored pre-images (which nothing modifies) instead of the
+//     table. (The walk stores a token's undo one token late, so that a read of
+//     the same token has taken the row before it changes; the window is one
+//     token longer for that.)
 // Without a source in the window, the table in memory is already right.
 // Word layout: bit 31 = from the ring / from the pre-images, bits 9-11 =
-// distance d, bits 0-8 = source position (writer p < W, reader W + q).
+// distance d, bits 0-8 = source position (writer p < W, reader W + q); G words
+// also: bit 30 = a write the same token reads (read position in bits 12-19),
+// bit 29 = a read the same token writes.
 constexpr uint32_t BSRC_ON = 1u << 31;
+constexpr uint32_t BSRC_OWN = 1u << 30;
+constexpr uint32_t BSRC_DEAD = 1u << 29;
 constexpr int BSRC_DSHIFT = 9;
+constexpr int BSRC_QSHIFT = 12;
 constexpr uint32_t BSRC_POS = 511u;
 constexpr int BHT_BITS = 13;
 constexpr int BHT_CAP = 1 << BHT_BITS;     // 64-bit LDS hash entries (64 KiB)
@@ -106,7 +120,7 @@ struct BPlanArgs {
 __device__ __forceinline__ uint32_t bht_hash(uint32_t row) { return (row * 2654435761u) >> (32 - BHT_BITS); }
 
 // One workgroup per (stream, tile of TT tokens [u0, u1)): an LDS hash holds every
-// access of tokens [u0, u1 + D) as (row << 32 | token - u0 << 10 | is_write << 9 |
+// access of tokens [u0, u1 + D + 1) as (row << 32 | token - u0 << 10 | is_write << 9 |
 // position), at most a quarter full; each access of the tile then walks its row's
 // entries and keeps the nearest later touch and write.
 __global__ __launch_bounds__(BPLAN_THREADS) void bwd_plan_kernel(BPlanArgs a) {
@@ -116,7 +130,7 @@ __global__ __launch_bounds__(BPLAN_THREADS) void bwd_plan_kernel(BPlanArgs a) {
     const int64_t s = blockIdx.x / a.ntile;
     const int64_t u0 = (blockIdx.x % a.ntile) * a.TT;
     const int64_t u1 = u0 + a.TT < a.Tn ? u0 + a.TT : a.Tn;
-    const int64_t h1 = u1 + D < a.Tn ? u1 + D : a.Tn;
+    const int64_t h1 = u1 + D + 1 < a.Tn ? u1 + D + 1 : a.Tn;
     const int32_t* iw = a.idx_w + s * a.TS * W;
     const int32_t* ir = a.idx_r + s * a.TS * R;
     uint32_t* Ps = a.plan + s * a.Tn * RW;
@@ -145,8 +159,8 @@ __global__ __launch_bounds__(BPLAN_THREADS) void bwd_plan_kernel(BPlanArgs a) {
         const int32_t row = isw ? iw[(u0 + tk) * W + q] : ir[(u0 + tk) * R + q];
         uint32_t gs = 0u, ms = 0u;
         if (row >= 0 && row < a.N) {
-            int gd = D + 1, md = D + 1;
-            bool gw = false, own = false;
+            int gd = D + 1, md = D + 2;
+            bool gw = false, own = false, dead = false;
             uint32_t gp = 0u, mp = 0u, op = 0u;
             uint32_t h = bht_hash((uint32_t)row);
             uint64_t ent;
@@ -159,23 +173,23 @@ __global__ __launch_bounds__(BPLAN_THREADS) void bwd_plan_kernel(BPlanArgs a) {
                         own = true;
                         op = ep;
                     }
-                    if (d >= 1 && d <= D) {
-                        if (d < gd || (d == gd && ew && !gw)) {
-                            gd = d;
-                            gw = ew;
-                            gp = ew ? ep : (uint32_t)W + ep;
-                        }
-                        if (ew && d < md) {
-                            md = d;
-                            mp = ep;
-                        }
+                    if (d == 0 && !isw && ew) dead = true;
+                    if (d >= 1 && d <= D && (d < gd || (d == gd && ew && !gw))) {
+                        gd = d;
+                        gw = ew;
+                        gp = ew ? ep : (uint32_t)W + ep;
+                    }
+                    if (d >= 1 && d <= D + 1 && ew && d < md) {
+                        md = d;
+                        mp = ep;
                     }
                 }
                 h = (h + 1) & (BHT_CAP - 1);
             }
-            if (own) gs = BSRC_ON | ((uint32_t)W + op);
-            else if (gd <= D) gs = BSRC_ON | ((uint32_t)gd << BSRC_DSHIFT) | gp;
-            if (!isw && md <= D) ms = BSRC_ON | ((uint32_t)md << BSRC_DSHIFT) | mp;
+            if (gd <= D) gs = BSRC_ON | ((uint32_t)gd << BSRC_DSHIFT) | gp;
+            if (own) gs |= BSRC_OWN | (op << BSRC_QSHIFT);
+            if (dead) gs |= BSRC_DEAD;
+            if (!isw && md <= D + 1) ms = BSRC_ON | ((uint32_t)md << BSRC_DSHIFT) | mp;
         }
         uint32_t* rec = Ps + (u0 + tk) * RW;
         if (isw) {
@@ -195,7 +209,7 @@ __global__ __launch_bounds__(BPLAN_THREADS) void bwd_plan_kernel(BPlanArgs a) {
 // comes from) D tokens early, issued right after the barrier that closed the
 // previous token. Every token leaves the adjoint rows it produced (writers' and
 // readers' new G) in an LDS ring of D + 1 token slots [slot][W + R][L], where
-// later-processed tokens of the window find them.
+// later-processed tokens of the window find them after the token's barrier.
 // Two instantiations: up to 16 wavefronts per workgroup (128 VGPRs) with
 // D = 1, and up to 8 wavefronts (256 VGPRs) with D = 4, which every layout of
 // at most 8 wavefronts takes. With 16 wavefronts D = 2 no longer fits 128 VGPRs
@@ -209,7 +223,7 @@ __global__ __launch_bounds__(BPLAN_THREADS) void bwd_plan_kernel(BPlanArgs a) {
 constexpr int BWD_D = 1;
 constexpr int BWD_D_DEEP = 4;
 constexpr int BWD_NW_DEEP = 8;
-static_assert(BWD_D_DEEP <= 7, "plan words keep the distance in 3 bits");
+static_assert(BWD_D_DEEP + 1 <= 7, "plan words keep the distance in 3 bits");
 
 template <bool B>
 struct BRole {
@@ -288,6 +302,7 @@ __global__ __launch_bounds__(NWM * 64) void scan_backward_kernel(BwdKArgs a) {
 
     const rsrc_t Rix = make_rsrc(ix, (int64_t)T * K * 4);
     const rsrc_t Rwx = make_rsrc(wx, (int64_t)T * K * 4);
+    const rsrc_t Rwr = make_rsrc(a.wt_r + tok0 * R, (int64_t)T * R * 4);  // writers: same-token read weights
     const rsrc_t Rpl = make_rsrc(pl, (int64_t)T * RW * 4);
     const rsrc_t Ral = make_rsrc(alp, (int64_t)T * 4);
     const rsrc_t Rbe = make_rsrc(bep, (int64_t)T * 4);
@@ -307,6 +322,8 @@ __global__ __launch_bounds__(NWM * 64) void scan_backward_kernel(BwdKArgs a) {
         float4 x;   // writers: the pre-image of the write; readers: dy
         float4 g;   // the adjoint row (unless it comes from the ring)
         float4 y;   // writers: v_t (its raw bits); readers: M_t of the row (table or pre-image)
+        float4 dy;  // writers: dy_t
+        float wr;   // writers: the weight of this token's read of the row (0 if none)
     };
     auto v_of = [&](const float4& y) -> V4 {
         if constexpr (VBF16) return make_int2(__float_as_int(y.x), __float_as_int(y.y));
@@ -335,6 +352,10 @@ __global__ __launch_bounds__(NWM * 64) void scan_backward_kernel(BwdKArgs a) {
         if constexpr (WR) {
             x.al = __uint_as_float(ld_u1(Ral, 0u, (uint32_t)tk * 4u));
             x.be = __uint_as_float(ld_u1(Rbe, 0u, (uint32_t)tk * 4u));
+            const uint32_t oq = (d.gs >> BSRC_QSHIFT) & 255u;
+            x.wr = __uint_as_float(ld_u1(Rwr, (d.gs & BSRC_OWN) && off != OOB ? oq * 4u : OOB,
+                                         (uint32_t)tk * (uint32_t)R * 4u));
+            x.dy = ld_f4(Rd, col4, (uint32_t)tk * dv4);
             const V4 vv = VL::load(Rv, v_off, (uint32_t)tk * vstride);
             x.x = ld_f4(Rs, s_lane, (uint32_t)tk * sstride);
             if constexpr (VBF16) x.y = make_float4(__int_as_float(vv.x), __int_as_float(vv.y), 0.f, 0.f);
@@ -342,6 +363,8 @@ __global__ __launch_bounds__(NWM * 64) void scan_backward_kernel(BwdKArgs a) {
         } else {
             x.al = 0.f;
             x.be = 0.f;
+            x.wr = 0.f;
+            x.dy = make_float4(0.f, 0.f, 0.f, 0.f);
             x.x = ld_f4(Rd, col4, (uint32_t)tk * dv4);
             // a read's M_t: from the table, or from a later write's pre-image (the
             // other load's offset is out of range: it is dropped)
@@ -381,16 +404,19 @@ __global__ __launch_bounds__(NWM * 64) void scan_backward_kernel(BwdKArgs a) {
     const bool xf = (int)(blockDim.x >> 6) > NWW + a.NWR;
     if (wave == NWW + a.NWR) {
         for (int tl = T - 1; tl >= 0; --tl) {
-            __syncthreads();                           // B1
             if constexpr (FORM == 1) __syncthreads();  // BX
             if (tl + 1 < T) finish(tl + 1);
-            __syncthreads();                           // B2
+            __syncthreads();                           // B
         }
         finish(0);
         return;
     }
 
     int slot = (T - 1) % UR;  // LDS ring slot of the token being processed
+    // a writer's undo, stored one token late: this token's reads of the row
+    // (other wavefronts, loads issued tokens ago) have taken it by then
+    float4 undo_m = make_float4(0.f, 0.f, 0.f, 0.f);
+    uint32_t undo_off = OOB;
     auto process = [&](auto wr_c, int tl, const Ad& d, const Va& x) {
         constexpr bool WR = decltype(wr_c)::value;
         const int32_t row = d.row;
@@ -405,9 +431,12 @@ __global__ __launch_bounds__(NWM * 64) void scan_backward_kernel(BwdKArgs a) {
         if constexpr (WR) {
             const float4 m = x.x;  // the pre-image M_{t-1}[i]
             const int par = tl & 1;
-            __syncthreads();       // B1: this token's readers' new G values are in the ring
+            st_f4(undo_m, Rm, undo_off, 0u);  // the previous token's undo
+            undo_m = m;
+            undo_off = off;
             float4 g = x.g;
             if (fwd) g = ring_at(fslot, fpos);
+            g = f4_fma(x.wr, x.dy, g);  // G after this token's reads
             float4 gn = make_float4(0.f, 0.f, 0.f, 0.f);
             float pwv = 0.f;
             if constexpr (FORM == 0) {
@@ -453,8 +482,7 @@ __global__ __launch_bounds__(NWM * 64) void scan_backward_kernel(BwdKArgs a) {
             }
             st_f1(pwv, Rpw, own ? (uint32_t)pos * 4u : OOB, (uint32_t)tl * (uint32_t)W * 4u);
             st_f4(gn, Rg, off, 0u);
-            st_f4(m, Rm, off, 0u);  // the undo
-            __syncthreads();        // B2
+            __syncthreads();  // B: this token's new G rows are in the ring
         } else {
             float4 gn = make_float4(0.f, 0.f, 0.f, 0.f);
             float dr = 0.f;
@@ -465,12 +493,11 @@ __global__ __launch_bounds__(NWM * 64) void scan_backward_kernel(BwdKArgs a) {
                 gn = f4_fma(w, x.x, g);
                 if (off != OOB) ring_at(slot, W + pos) = gn;
             }
-            st_f4(gn, Rg, off, 0u);
+            st_f4(gn, Rg, (d.gs & BSRC_DEAD) ? OOB : off, 0u);  // a same-token write replaces it
             st_f1(off == OOB ? 0.f : dr, Rpr, own ? (uint32_t)pos * 4u : OOB, (uint32_t)tl * (uint32_t)R * 4u);
-            __syncthreads();                           // B1
             if constexpr (FORM == 1) __syncthreads();  // BX
             if (rw == 0 && !xf && tl + 1 < T) finish(tl + 1);
-            __syncthreads();                           // B2
+            __syncthreads();                           // B
         }
         slot = slot == 0 ? UR - 1 : slot - 1;
     };
@@ -505,8 +532,12 @@ __global__ __launch_bounds__(NWM * 64) void scan_backward_kernel(BwdKArgs a) {
             process(wr_c, tl, d, fetch_va(wr_c, tl, d));
         }
     };
-    if (writer) run(BRole<true>{});
-    else run(BRole<false>{});
+    if (writer) {
+        run(BRole<true>{});
+        st_f4(undo_m, Rm, undo_off, 0u);  // token 0's undo
+    } else {
+        run(BRole<false>{});
+    }
     if (wave == NWW && !xf) finish(0);
 }
 
@@ -584,19 +615,21 @@ int env_int(const char* name) {
     return e ? atoi(e) : 0;
 }
 
-// Slab width and row partitions. Both forms take the widest slab whose layout
+// Slab width and row partitions. The per-slot form takes the widest slab that
+// fills the CUs (256 workgroups) in one row partition, or in two where the
+// layout has two or more writer wavefronts. Every workgroup of a partition
+// steps through every token, so more partitions cost more than they bring (8
+// streams of 131072 tokens, 8-column slabs in 2 / 4 partitions: 112.8 / 162
+// ms), while wider slabs pay off because a random row piece costs the DRAM a
+// whole 128-byte line (32 streams of 8192 tokens: 32-column slabs in 2
+// partitions 15.1 ms against 16.5 for 16-column slabs in one; 16 streams of
+// 4096 tokens, W = R = 16, d_v = 64: 4-column slabs 2.01 ms against 2.13 for
+// 8-column ones on half the CUs). Where no layout fills the CUs that way, and
+// for the shared-residual form (no partitions): the widest slab whose layout
 // has at most 8 wavefronts (the deeper window) and gives at least 128
-// workgroups (8 streams x 131072 tokens: 8-column slabs 167 ms against 177 for
-// 4-column ones with 256 workgroups; 32 streams: 16-column slabs as before),
-// else the widest that still gives 256 workgroups (one per CU: a second
-// workgroup on a CU stretches every token of both), else the one with the
-// most, and one partition where that fills the CUs: partitions
-// multiply the wavefronts that step through every token, and with the token
-// loop's loads issued ahead that costs more than the extra rows in flight
-// bring (measured on the per-slot form: 16-column slabs without partitions
-// 16.2 ms against 20.4 ms for 32-column slabs in 2 partitions and 22.2 for
-// 16-column slabs in 2 on 32 streams of 8192 tokens). The exception, below:
-// half the CUs idle and two or more writer wavefronts. SDM_BWD_SLAB and
+// workgroups, else the widest that still gives 256, else the one with the
+// most; the per-slot form then takes 2 partitions where half the CUs would
+// idle and the layout has two or more writer wavefronts. SDM_BWD_SLAB and
 // SDM_BWD_PARTS (per-slot form only) force a choice.
 struct BCfg {
     int S = 0, P = 1;
@@ -604,6 +637,18 @@ struct BCfg {
 BCfg bwd_cfg(int64_t NS, int W, int R, int dv, int form) {
     BCfg c;
     const int fs = env_int("SDM_BWD_SLAB"), fp = env_int("SDM_BWD_PARTS");
+    if (form == 0 && !fs && !fp) {  // 256 workgroups with the widest slab
+        for (int S : {32, 16, 8, 4}) {
+            if (!bwd_fits(S, W, R, dv)) continue;
+            const int64_t units = NS * (dv / S);
+            const int P = units >= 256 ? 1 : (bwd_geom(S, W, R).NWW >= 2 && units * 2 >= 256) ? 2 : 0;
+            if (P) {
+                c.S = S;
+                c.P = P;
+                return c;
+            }
+        }
+    }
     // first choice: the widest slab whose layout takes the deeper-window
     // instantiation (at most 8 wavefronts) with at least 128 workgroups
     for (int S : {32, 16, 8, 4}) {
@@ -624,12 +669,11 @@ BCfg bwd_cfg(int64_t NS, int W, int R, int dv, int form) {
     if (form == 0 && (fp == 2 || fp == 4 || fp == 8 || fp == 16)) {
         c.P = fp;
     } else if (form == 0 && fp == 0 && !fs) {
-        // few streams: where the layout has two or more writer wavefronts and
-        // half the CUs would idle, 2 row partitions fill them (long_context,
-        // 8-column slabs: 128 workgroups 160 ms, 2 partitions 123 ms; 4
-        // partitions 226 ms). With one writer wavefront the walk is bound by
-        // its fixed per-token steps and partitions do not help (large_table
-        // 46.9 against 47.1 ms, small 3.00 against 3.04 ms).
+        // few streams, where no layout fills the CUs: 2 row partitions where
+        // half of them would idle and there are two or more writer wavefronts;
+        // with one, the walk is bound by its fixed per-token steps (one stream
+        // of 65536 tokens, W = R = 8, d_v = 512, 4-column slabs: 30.6 ms in one
+        // partition, 30.4 in two)
         const BGeom g = bwd_geom(c.S, W, R);
         const int64_t units = NS * (dv / c.S);
         if (g.NWW >= 2 && units * 2 <= 256) c.P = 2;
@@ -691,11 +735,11 @@ hipError_t launch_bwd_slab(const BwdArgs& a, const BCfg& c, hipStream_t st) {
         pa.idx_w = a.idx_w + c0 * a.W; pa.idx_r = a.idx_r + c0 * a.R; pa.plan = plan;
         const int D = deep ? BWD_D_DEEP : BWD_D;
         pa.Tn = Tn; pa.TS = a.T; pa.N = a.N; pa.W = a.W; pa.R = a.R; pa.D = D;
-        // the hash holds (TT + D) * (W + R) entries at load <= 1/4, which keeps the
-        // probe chains a wavefront walks short; with TT clamped to 1 (W + R > 292
-        // at D = 6) it holds at most 7 * 512 of its 8192 entries; token fields
-        // have 10 bits
-        pa.TT = (BHT_CAP / 4) / (a.W + a.R) - D;
+        // the hash holds (TT + D + 1) * (W + R) entries at load <= 1/4, which
+        // keeps the probe chains a wavefront walks short; with TT clamped to 1
+        // (W + R > 256 at D = 6) it holds at most 8 * 512 of its 8192 entries;
+        // token fields have 10 bits
+        pa.TT = (BHT_CAP / 4) / (a.W + a.R) - D - 1;
         if (pa.TT > 1000) pa.TT = 1000;
         if (pa.TT < 1) pa.TT = 1;
         pa.ntile = (Tn + pa.TT - 1) / pa.TT;
