@@ -271,13 +271,6 @@ __global__ __launch_bounds__(NWM * 64) void scan_backward_kernel(BwdKArgs a) {
     const float* bep = a.beta + tok0;
     const uint32_t* pl = a.plan + s * (int64_t)T * RW;
     const int pg_off = writer ? pos : W + pos;    // this lane's G-source word in a token record
-    const rsrc_t Rm = make_rsrc(a.M + s * a.N * dv, a.N * dv * 4);
-    const rsrc_t Rg = make_rsrc(a.G + s * a.N * dv, a.N * dv * 4);
-    const rsrc_t Rv = make_rsrc(static_cast<const char*>(a.v) + tok0 * dv * VL::ESZ, (int64_t)T * dv * VL::ESZ);
-    const rsrc_t Rd = make_rsrc(a.dy + tok0 * dv, (int64_t)T * dv * 4);
-    const rsrc_t Rs = make_rsrc(a.snap + tok0 * W * dv, (int64_t)T * W * dv * 4);
-    const rsrc_t Ro = a.P > 1 ? make_rsrc(a.pdv + ((int64_t)part * a.NS + s) * T * dv, (int64_t)T * dv * 4)
-                              : make_rsrc(a.dvo + tok0 * dv, (int64_t)T * dv * 4);
     const uint32_t dv4 = (uint32_t)dv * 4u, col4 = (uint32_t)col * 4u;
     const uint32_t vstride = (uint32_t)dv * VL::ESZ, v_off = (uint32_t)col * VL::ESZ;
     const uint32_t sstride = (uint32_t)W * dv4;
@@ -291,24 +284,47 @@ __global__ __launch_bounds__(NWM * 64) void scan_backward_kernel(BwdKArgs a) {
         (&xb[0][0][0])[i] = make_float4(0.f, 0.f, 0.f, 0.f);
     __syncthreads();
 
+    const uint32_t N32 = (uint32_t)(a.N < 0x7FFFFFFF ? a.N : 0x7FFFFFFF);
     auto off_of = [&](int32_t row) -> uint32_t {
-        return (row >= 0 && row < a.N && row_part((uint32_t)row, a.pshift) == part)
-                   ? __umul24((uint32_t)row, dv4) + col4 : OOB;
+        return ((uint32_t)row < N32 && row_part((uint32_t)row, a.pshift) == part) ? __umul24((uint32_t)row, dv4) + col4
+                                                                                   : OOB;
     };
     auto owns_pos = [&](int32_t row, uint32_t off) -> bool {
-        return off != OOB || (part == 0 && has && !(row >= 0 && row < a.N));
+        return off != OOB || (part == 0 && has && !((uint32_t)row < N32));
     };
-    auto ring_at = [&](int slot, int p) -> float4& { return lring[((int64_t)slot * KR + p) * L + cc]; };
+    auto ring_at = [&](int slot, int p) -> float4& { return lring[(slot * KR + p) * L + cc]; };
 
-    const rsrc_t Rix = make_rsrc(ix, (int64_t)T * K * 4);
-    const rsrc_t Rwx = make_rsrc(wx, (int64_t)T * K * 4);
-    const rsrc_t Rwr = make_rsrc(a.wt_r + tok0 * R, (int64_t)T * R * 4);  // writers: same-token read weights
-    const rsrc_t Rpl = make_rsrc(pl, (int64_t)T * RW * 4);
-    const rsrc_t Ral = make_rsrc(alp, (int64_t)T * 4);
-    const rsrc_t Rbe = make_rsrc(bep, (int64_t)T * 4);
-    const rsrc_t Rpw = make_rsrc(pw, (int64_t)T * W * 4);
-    const rsrc_t Rpr = make_rsrc(pr, (int64_t)T * R * 4);
-    const rsrc_t Rpab = make_rsrc(pab, (int64_t)T * 8);
+    // Buffer descriptors are made in each role's own path (and the finishing
+    // sums' in theirs), so that scalar registers hold only one role's set.
+    auto make_ro = [&]() {
+        return a.P > 1 ? make_rsrc(a.pdv + ((int64_t)part * a.NS + s) * T * dv, (int64_t)T * dv * 4)
+                       : make_rsrc(a.dvo + tok0 * dv, (int64_t)T * dv * 4);
+    };
+    struct BD {
+        rsrc_t ix, wx, pl, g, m, s, d, v, al, be, wr, pw, pr, o;
+    };
+    auto make_desc = [&](auto wr_c) -> BD {
+        constexpr bool WR = decltype(wr_c)::value;
+        BD d;
+        d.ix = make_rsrc(ix, (int64_t)T * K * 4);
+        d.wx = make_rsrc(wx, (int64_t)T * K * 4);
+        d.pl = make_rsrc(pl, (int64_t)T * RW * 4);
+        d.g = make_rsrc(a.G + s * a.N * dv, a.N * dv * 4);
+        d.m = make_rsrc(a.M + s * a.N * dv, a.N * dv * 4);
+        d.s = make_rsrc(a.snap + tok0 * W * dv, (int64_t)T * W * dv * 4);
+        d.d = make_rsrc(a.dy + tok0 * dv, (int64_t)T * dv * 4);
+        if constexpr (WR) {
+            d.v = make_rsrc(static_cast<const char*>(a.v) + tok0 * dv * VL::ESZ, (int64_t)T * dv * VL::ESZ);
+            d.al = make_rsrc(alp, (int64_t)T * 4);
+            d.be = make_rsrc(bep, (int64_t)T * 4);
+            d.wr = make_rsrc(a.wt_r + tok0 * R, (int64_t)T * R * 4);  // same-token read weights
+            d.pw = make_rsrc(pw, (int64_t)T * W * 4);
+            if constexpr (FORM == 1) d.o = make_ro();
+        } else {
+            d.pr = make_rsrc(pr, (int64_t)T * R * 4);
+        }
+        return d;
+    };
     const uint32_t lane_k = has ? (uint32_t)pos * 4u : OOB;
     const uint32_t lane_pg = has ? (uint32_t)pg_off * 4u : OOB;
     const uint32_t lane_pm = (has && !writer) ? (uint32_t)(W + R + pos) * 4u : OOB;
@@ -324,6 +340,7 @@ __global__ __launch_bounds__(NWM * 64) void scan_backward_kernel(BwdKArgs a) {
         float4 y;   // writers: v_t (its raw bits); readers: M_t of the row (table or pre-image)
         float4 dy;  // writers: dy_t
         float wr;   // writers: the weight of this token's read of the row (0 if none)
+        uint32_t off;  // the row's byte offset in the tables (OOB if none here)
     };
     auto v_of = [&](const float4& y) -> V4 {
         if constexpr (VBF16) return make_int2(__float_as_int(y.x), __float_as_int(y.y));
@@ -333,31 +350,32 @@ __global__ __launch_bounds__(NWM * 64) void scan_backward_kernel(BwdKArgs a) {
     // ones for every token, so the loads in flight per token are the same on
     // every path of that role's loop (a lane without the access gets an
     // out-of-range offset).
-    auto fetch_ad = [&](auto wr_c, int tk) -> Ad {
+    auto fetch_ad = [&](auto wr_c, const BD& D_, int tk) -> Ad {
         constexpr bool WR = decltype(wr_c)::value;
         Ad d;
-        const int32_t row = (int32_t)ld_u1(Rix, lane_k, (uint32_t)tk * (uint32_t)K * 4u);
+        const int32_t row = (int32_t)ld_u1(D_.ix, lane_k, (uint32_t)tk * (uint32_t)K * 4u);
         d.row = has ? row : -1;
-        d.gs = ld_u1(Rpl, lane_pg, (uint32_t)tk * (uint32_t)RW * 4u);
+        d.gs = ld_u1(D_.pl, lane_pg, (uint32_t)tk * (uint32_t)RW * 4u);
         if constexpr (WR) d.ms = 0u;
-        else d.ms = ld_u1(Rpl, lane_pm, (uint32_t)tk * (uint32_t)RW * 4u);
+        else d.ms = ld_u1(D_.pl, lane_pm, (uint32_t)tk * (uint32_t)RW * 4u);
         return d;
     };
-    auto fetch_va = [&](auto wr_c, int tk, const Ad& d) -> Va {
+    auto fetch_va = [&](auto wr_c, const BD& D_, int tk, const Ad& d) -> Va {
         constexpr bool WR = decltype(wr_c)::value;
         Va x;
         const uint32_t off = off_of(d.row);
-        x.w = __uint_as_float(ld_u1(Rwx, lane_k, (uint32_t)tk * (uint32_t)K * 4u));
-        x.g = ld_f4(Rg, (d.gs & BSRC_ON) ? OOB : off, 0u);
+        x.off = off;
+        x.w = __uint_as_float(ld_u1(D_.wx, lane_k, (uint32_t)tk * (uint32_t)K * 4u));
+        x.g = ld_f4(D_.g, (d.gs & BSRC_ON) ? OOB : off, 0u);
         if constexpr (WR) {
-            x.al = __uint_as_float(ld_u1(Ral, 0u, (uint32_t)tk * 4u));
-            x.be = __uint_as_float(ld_u1(Rbe, 0u, (uint32_t)tk * 4u));
+            x.al = __uint_as_float(ld_u1(D_.al, 0u, (uint32_t)tk * 4u));
+            x.be = __uint_as_float(ld_u1(D_.be, 0u, (uint32_t)tk * 4u));
             const uint32_t oq = (d.gs >> BSRC_QSHIFT) & 255u;
-            x.wr = __uint_as_float(ld_u1(Rwr, (d.gs & BSRC_OWN) && off != OOB ? oq * 4u : OOB,
+            x.wr = __uint_as_float(ld_u1(D_.wr, (d.gs & BSRC_OWN) && off != OOB ? oq * 4u : OOB,
                                          (uint32_t)tk * (uint32_t)R * 4u));
-            x.dy = ld_f4(Rd, col4, (uint32_t)tk * dv4);
-            const V4 vv = VL::load(Rv, v_off, (uint32_t)tk * vstride);
-            x.x = ld_f4(Rs, s_lane, (uint32_t)tk * sstride);
+            x.dy = ld_f4(D_.d, col4, (uint32_t)tk * dv4);
+            const V4 vv = VL::load(D_.v, v_off, (uint32_t)tk * vstride);
+            x.x = ld_f4(D_.s, s_lane, (uint32_t)tk * sstride);
             if constexpr (VBF16) x.y = make_float4(__int_as_float(vv.x), __int_as_float(vv.y), 0.f, 0.f);
             else x.y = vv;
         } else {
@@ -365,13 +383,14 @@ __global__ __launch_bounds__(NWM * 64) void scan_backward_kernel(BwdKArgs a) {
             x.be = 0.f;
             x.wr = 0.f;
             x.dy = make_float4(0.f, 0.f, 0.f, 0.f);
-            x.x = ld_f4(Rd, col4, (uint32_t)tk * dv4);
+            x.x = ld_f4(D_.d, col4, (uint32_t)tk * dv4);
             // a read's M_t: from the table, or from a later write's pre-image (the
             // other load's offset is out of range: it is dropped)
             const bool from_pre = (d.ms & BSRC_ON) && off != OOB;
             const uint32_t dd = (d.ms >> BSRC_DSHIFT) & 7u, sp = d.ms & BSRC_POS;
-            const float4 mt = ld_f4(Rm, from_pre ? OOB : off, 0u);
-            const float4 mp = ld_f4(Rs, from_pre ? (uint32_t)(tk + (int)dd) * sstride + sp * dv4 + col4 : OOB, 0u);
+            const float4 mt = ld_f4(D_.m, from_pre ? OOB : off, 0u);
+            const float4 mp = ld_f4(D_.s, from_pre ? __umul24(dd, sstride) + __umul24(sp, dv4) + col4 : OOB,
+                                    (uint32_t)tk * sstride);
             x.y = from_pre ? mp : mt;
         }
         return x;
@@ -382,6 +401,7 @@ __global__ __launch_bounds__(NWM * 64) void scan_backward_kernel(BwdKArgs a) {
     // (kept by token parity, so the next token's writers do not overwrite them)
     auto finish = [&](int tk) {
         const int par = tk & 1;
+        const rsrc_t Ro = make_ro(), Rpab = make_rsrc(pab, (int64_t)T * 8);
         if constexpr (FORM == 0) {
             float acc = 0.f;
 #pragma unroll
@@ -417,10 +437,10 @@ __global__ __launch_bounds__(NWM * 64) void scan_backward_kernel(BwdKArgs a) {
     // (other wavefronts, loads issued tokens ago) have taken it by then
     float4 undo_m = make_float4(0.f, 0.f, 0.f, 0.f);
     uint32_t undo_off = OOB;
-    auto process = [&](auto wr_c, int tl, const Ad& d, const Va& x) {
+    auto process = [&](auto wr_c, const BD& D_, int tl, const Ad& d, const Va& x) {
         constexpr bool WR = decltype(wr_c)::value;
         const int32_t row = d.row;
-        const uint32_t off = off_of(row);
+        const uint32_t off = x.off;
         const float w = off == OOB ? 0.f : x.w, al = x.al, be = x.be;
         const bool run = __ballot(off != OOB) != 0ull;  // else every lane's offset is out of range
         const bool fwd = (d.gs & BSRC_ON) && off != OOB;
@@ -431,7 +451,7 @@ __global__ __launch_bounds__(NWM * 64) void scan_backward_kernel(BwdKArgs a) {
         if constexpr (WR) {
             const float4 m = x.x;  // the pre-image M_{t-1}[i]
             const int par = tl & 1;
-            st_f4(undo_m, Rm, undo_off, 0u);  // the previous token's undo
+            st_f4(undo_m, D_.m, undo_off, 0u);  // the previous token's undo
             undo_m = m;
             undo_off = off;
             float4 g = x.g;
@@ -474,14 +494,14 @@ __global__ __launch_bounds__(NWM * 64) void scan_backward_kernel(BwdKArgs a) {
                 pwv = off == OOB ? 0.f : be * gur - al * be * hmr;
                 const bool lead = wave == 0 && r == 0;
                 const float xa = lead ? gm - be * dot4(gh, sm) : gm, xc = lead ? dot4(gh, u) : 0.f;
-                st_f4(f4_scale(be, gh), Ro, lead ? col4 : OOB, (uint32_t)tl * dv4);
+                st_f4(f4_scale(be, gh), D_.o, lead ? col4 : OOB, (uint32_t)tl * dv4);
                 ab[par][wave][0][lane] = xa;  // summed by the finishing wavefront
                 ab[par][wave][1][lane] = xc;
                 gn = f4_sub(f4_scale(al, g), f4_scale(al * be * w, gh));
                 if (off != OOB) ring_at(slot, pos) = gn;
             }
-            st_f1(pwv, Rpw, own ? (uint32_t)pos * 4u : OOB, (uint32_t)tl * (uint32_t)W * 4u);
-            st_f4(gn, Rg, off, 0u);
+            st_f1(pwv, D_.pw, own ? (uint32_t)pos * 4u : OOB, (uint32_t)tl * (uint32_t)W * 4u);
+            st_f4(gn, D_.g, off, 0u);
             __syncthreads();  // B: this token's new G rows are in the ring
         } else {
             float4 gn = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -493,8 +513,8 @@ __global__ __launch_bounds__(NWM * 64) void scan_backward_kernel(BwdKArgs a) {
                 gn = f4_fma(w, x.x, g);
                 if (off != OOB) ring_at(slot, W + pos) = gn;
             }
-            st_f4(gn, Rg, (d.gs & BSRC_DEAD) ? OOB : off, 0u);  // a same-token write replaces it
-            st_f1(off == OOB ? 0.f : dr, Rpr, own ? (uint32_t)pos * 4u : OOB, (uint32_t)tl * (uint32_t)R * 4u);
+            st_f4(gn, D_.g, (d.gs & BSRC_DEAD) ? OOB : off, 0u);  // a same-token write replaces it
+            st_f1(off == OOB ? 0.f : dr, D_.pr, own ? (uint32_t)pos * 4u : OOB, (uint32_t)tl * (uint32_t)R * 4u);
             if constexpr (FORM == 1) __syncthreads();  // BX
             if (rw == 0 && !xf && tl + 1 < T) finish(tl + 1);
             __syncthreads();                           // B
@@ -506,38 +526,37 @@ __global__ __launch_bounds__(NWM * 64) void scan_backward_kernel(BwdKArgs a) {
     // statically indexed; the token being processed is tl = T - 1 - k. Each role
     // runs its own copy.
     auto run = [&](auto wr_c) {
+        constexpr bool WR = decltype(wr_c)::value;
+        const BD R_ = make_desc(wr_c);
         int k_done = 0;
         if (T >= U) {
             Ad ad[U];
             Va va[UP];
 #pragma unroll
-            for (int q = 0; q < D + DM; ++q) ad[q] = fetch_ad(wr_c, T - 1 - q);
+            for (int q = 0; q < D + DM; ++q) ad[q] = fetch_ad(wr_c, R_, T - 1 - q);
 #pragma unroll
-            for (int q = 0; q < D; ++q) va[q] = fetch_va(wr_c, T - 1 - q, ad[q]);
+            for (int q = 0; q < D; ++q) va[q] = fetch_va(wr_c, R_, T - 1 - q, ad[q]);
             for (int k0 = 0; k0 + U <= T; k0 += U) {
 #pragma unroll
                 for (int j = 0; j < U; ++j) {
                     const int tl = T - 1 - (k0 + j);
                     // early loads of tokens before 0 fetch token 0 again, unused
-                    ad[(j + D + DM) % U] = fetch_ad(wr_c, tl - D - DM >= 0 ? tl - D - DM : 0);
-                    va[(j + D) % UP] = fetch_va(wr_c, tl - D >= 0 ? tl - D : 0, ad[(j + D) % U]);
-                    process(wr_c, tl, ad[j], va[j % UP]);
+                    ad[(j + D + DM) % U] = fetch_ad(wr_c, R_, tl - D - DM >= 0 ? tl - D - DM : 0);
+                    va[(j + D) % UP] = fetch_va(wr_c, R_, tl - D >= 0 ? tl - D : 0, ad[(j + D) % U]);
+                    process(wr_c, R_, tl, ad[j], va[j % UP]);
                 }
             }
             k_done = (T / U) * U;
         }
         for (int k = k_done; k < T; ++k) {  // the rest: loads right before use
             const int tl = T - 1 - k;
-            const Ad d = fetch_ad(wr_c, tl);
-            process(wr_c, tl, d, fetch_va(wr_c, tl, d));
+            const Ad d = fetch_ad(wr_c, R_, tl);
+            process(wr_c, R_, tl, d, fetch_va(wr_c, R_, tl, d));
         }
+        if constexpr (WR) st_f4(undo_m, R_.m, undo_off, 0u);  // token 0's undo
     };
-    if (writer) {
-        run(BRole<true>{});
-        st_f4(undo_m, Rm, undo_off, 0u);  // token 0's undo
-    } else {
-        run(BRole<false>{});
-    }
+    if (writer) run(BRole<true>{});
+    else run(BRole<false>{});
     if (wave == NWW && !xf) finish(0);
 }
 
@@ -599,7 +618,8 @@ size_t bwd_ring_bytes(int S, int W, int R, int D) {
 }
 
 bool bwd_fits(int S, int W, int R, int dv) {
-    if (dv % S != 0) return false;
+    // (a token's pre-images span W * dv * 4 bytes, multiplied in 24 bits)
+    if (dv % S != 0 || (int64_t)W * dv * 4 >= (1 << 24)) return false;
     const BGeom g = bwd_geom(S, W, R);
     return g.NWW + g.NWR <= BWD_NWMAX && bwd_ring_bytes(S, W, R, BWD_D) <= 128 * 1024;
 }
