@@ -135,10 +135,13 @@ def test_training_sizes_are_pure_host_logic(lib):
         nslab = dv // S
         return 4 * (nslab * NS * T * (W + R) + nslab * P * NS * T * 2 + (P * NS * T * dv if P > 1 else 0)
                     + NS * T * (W + 2 * R))
-    # both forms take the widest slab with at most 8 wavefronts and at least 128
-    # workgroups: 32 streams -> 16-column slabs, one partition; 8 streams ->
-    # 8-column slabs (128 workgroups, two writer wavefronts), where the per-slot
-    # form takes 2 row partitions; chunks of at most 2^31 / (W dv 4) tokens
+    # the per-slot form takes the widest slab that fills 256 workgroups in at most
+    # 2 partitions (32 streams: 32-column slabs in 2; 8 streams: 8-column slabs in
+    # 2), the shared-residual form the widest with at most 8 wavefronts and at
+    # least 128 workgroups (32 streams: 16-column slabs; 8 streams: 8-column
+    # slabs), and the workspace is the larger of the two; chunks of at most
+    # 2^31 / (W dv 4) tokens
+    assert bwd(32, 8192, 16, 1) > bwd(32, 8192, 32, 2)
     assert binding.sdm_scan_backward_workspace_bytes(4, 8, 8192, 64, 64, 128) == bwd(32, 8192, 16, 1)
     assert binding.sdm_scan_backward_workspace_bytes(1, 8, 1000, 64, 64, 128) == bwd(8, 1000, 8, 2)
     Tc = 0x7FFFFFFF // (64 * 128 * 4)
