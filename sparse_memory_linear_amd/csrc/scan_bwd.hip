@@ -211,15 +211,14 @@ __global__ __launch_bounds__(BPLAN_THREADS) void bwd_plan_kernel(BPlanArgs a) {
 // readers' new G) in an LDS ring of D + 1 token slots [slot][W + R][L], where
 // later-processed tokens of the window find them after the token's barrier.
 // Two instantiations: up to 16 wavefronts per workgroup (128 VGPRs) with
-// D = 1, and up to 8 wavefronts (256 VGPRs) with D = 4, which every layout of
-// at most 8 wavefronts takes. With 16 wavefronts D = 2 no longer fits 128 VGPRs
-// (8 to 40 bytes of spills per lane; D = 3 spills more and ran about twice as
-// long), and D = 1 measured as fast as D = 2 for the per-slot form and 5 %
-// slower for the shared-residual one; only layouts of more than 8 wavefronts
-// (W + R above 128 rows at 16-column slabs) take it. With 8 wavefronts, D = 4
-// against D = 2 takes one stream of 65536 tokens (W = R = 8, d_v = 512) from
-// 75 to 65 ms and 16 streams of 4096 tokens from 4.8 to 4.2 ms, while D = 6
-// spills with fp32 v and is slower there (88, 5.5).
+// D = 1, which the layouts of more than 8 wavefronts take (32 streams of 8192
+// tokens, W = R = 64, d_v = 128: 32-column slabs), and up to 8 wavefronts (256
+// VGPRs) with D = 4, which every layout of at most 8 wavefronts takes. With 16
+// wavefronts D = 2 fits 128 VGPRs but runs slower (that shape: 16.2 against
+// 15.1 ms; D = 3 spills). With 8 wavefronts, D = 4 against D = 2 took one
+// stream of 65536 tokens (W = R = 8, d_v = 512) from 75 to 65 ms and 16
+// streams of 4096 tokens from 4.8 to 4.2 ms; D = 6 is slower on the first (58.9
+// against 30.6 ms) and no faster on the others.
 constexpr int BWD_D = 1;
 constexpr int BWD_D_DEEP = 4;
 constexpr int BWD_NW_DEEP = 8;
